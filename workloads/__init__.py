@@ -1,0 +1,14 @@
+"""Seeded synthetic inputs shared by the oracle tests, the GPU parity tests and
+the benchmark.  This package holds input preparation only (random draws,
+bf16 rounding of inputs, packing offsets); none of the method's arithmetic.
+"""
+from .gen import (  # noqa: F401
+    CONFIGS,
+    bf16_bits_to_f32,
+    f32_to_bf16_bits,
+    as_f64,
+    make_markov,
+    make_rnn,
+    make_verify_only,
+    packed_offsets,
+)
