@@ -1,0 +1,20 @@
+"""MI355X-native DSpark draft sampling and lossless verification.
+
+The compute path is the HIP library libspecdec.so (include/specdec.h); this
+package only marshals torch device tensors into its C ABI.  Importing the
+package does not load the library; the first call does, and fails loudly if
+the library is missing.
+"""
+from .api import (  # noqa: F401
+    SPEC_BF16,
+    SPEC_F32,
+    SpecError,
+    library_path,
+    load_library,
+    spec_draft_sample_markov,
+    spec_draft_sample_rnn,
+    spec_philox_uniforms,
+    spec_verify,
+    spec_version,
+    workspace_bytes,
+)

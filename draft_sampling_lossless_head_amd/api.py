@@ -1,0 +1,235 @@
+"""ctypes binding of libspecdec.so with the C ABI's names.
+
+Argument marshalling only: shape checks, output/workspace allocation when the
+caller does not pass them, and the current torch stream.  Every step of the
+method runs in the library's HIP kernels.
+"""
+import ctypes
+import os
+
+import torch
+
+SPEC_F32 = 0
+SPEC_BF16 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libspecdec.so")
+_lib = None
+
+
+class SpecError(RuntimeError):
+    pass
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libspecdec.so (built by __graft_entry__.build()).  Raises if it is
+    missing: there is no fallback path."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise SpecError(f"{_LIB_PATH} is missing: build the HIP library first "
+                        "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, u64, u32, f32, sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64,
+                                  ctypes.c_uint32, ctypes.c_float, ctypes.c_size_t)
+    lib.spec_version.restype = i32
+    lib.spec_last_error.restype = ctypes.c_char_p
+    lib.spec_philox_uniforms.argtypes = [u64, u32, u32, i32, i32, vp, vp]
+    lib.spec_philox_uniforms.restype = i32
+    lib.spec_draft_markov_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.spec_draft_markov_workspace_size.restype = sz
+    lib.spec_draft_sample_markov.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, f32,
+                                             vp, u64, u32, vp, vp, vp, vp, vp, sz, vp]
+    lib.spec_draft_sample_markov.restype = i32
+    lib.spec_draft_rnn_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    lib.spec_draft_rnn_workspace_size.restype = sz
+    lib.spec_draft_sample_rnn.argtypes = [vp, i32, vp, vp, i32, i32, vp, vp, vp, vp, vp, i32, i32,
+                                          i32, i32, i32, f32, vp, u64, u32, vp, vp, vp, vp, vp,
+                                          sz, vp]
+    lib.spec_draft_sample_rnn.restype = i32
+    lib.spec_verify_workspace_size.argtypes = [i32, i32, i32]
+    lib.spec_verify_workspace_size.restype = sz
+    lib.spec_verify.argtypes = [vp, i32, vp, i32, vp, vp, vp, vp, i32, i32, i32, f32, vp, u64,
+                                u32, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.spec_verify.restype = i32
+    _lib = lib
+    return lib
+
+
+def spec_version():
+    return load_library().spec_version()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t, name):
+    if t.dtype == torch.float32:
+        return SPEC_F32
+    if t.dtype == torch.bfloat16:
+        return SPEC_BF16
+    raise SpecError(f"{name} must be float32 or bfloat16, got {t.dtype}")
+
+
+def _dev(t, name):
+    if not (t.is_cuda and t.is_contiguous()):
+        raise SpecError(f"{name} must be a contiguous device tensor")
+    return t
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(st, what):
+    if st != 0:
+        msg = load_library().spec_last_error().decode()
+        raise SpecError(f"{what} failed with status {st}: {msg}")
+
+
+def workspace_bytes(kind, **dims):
+    lib = load_library()
+    if kind == "markov":
+        return lib.spec_draft_markov_workspace_size(dims["B"], dims["gamma"], dims["V"], dims["r"])
+    if kind == "rnn":
+        return lib.spec_draft_rnn_workspace_size(dims["B"], dims["gamma"], dims["V"], dims["r"],
+                                                 dims["d"])
+    if kind == "verify":
+        return lib.spec_verify_workspace_size(dims["B"], dims["gamma_max"], dims["V"])
+    raise ValueError(kind)
+
+
+def _workspace(nbytes, device, ws):
+    if nbytes == 0:
+        return None, 0
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if ws.numel() < nbytes:
+        raise SpecError(f"workspace too small: {ws.numel()} < {nbytes}")
+    return ws, ws.numel()
+
+
+def spec_philox_uniforms(seed, offset, stream_id, B, K, device="cuda", out=None, stream=None):
+    """[B, K] float32 uniforms u(seed, offset, b, k, stream_id)."""
+    lib = load_library()
+    out = torch.empty((B, K), dtype=torch.float32, device=device) if out is None else out
+    _check(lib.spec_philox_uniforms(seed, offset, stream_id, B, K, _ptr(out), _stream(stream)),
+           "spec_philox_uniforms")
+    return out
+
+
+def _draft_outputs(B, gamma, V, device, out):
+    if out is not None:
+        return out
+    return dict(tokens=torch.empty((B, gamma), dtype=torch.int32, device=device),
+                q_logits=torch.empty((B, gamma, V), dtype=torch.float32, device=device),
+                q_logZ=torch.empty((B, gamma), dtype=torch.float32, device=device),
+                q_tok_prob=torch.empty((B, gamma), dtype=torch.float32, device=device))
+
+
+def spec_draft_sample_markov(U, x0, W1, W2, T=1.0, *, uniforms=None, seed=0, offset=0,
+                             out=None, workspace=None, stream=None):
+    """Markov-head draft.  U [B, gamma, V], x0 [B] int32, W1 [V, r], W2 [r, V]."""
+    lib = load_library()
+    for t, n in ((U, "U"), (x0, "x0"), (W1, "W1"), (W2, "W2")):
+        _dev(t, n)
+    B, gamma, V = U.shape
+    r = W1.shape[1]
+    if x0.dtype != torch.int32 or x0.shape != (B,):
+        raise SpecError("x0 must be int32 [B]")
+    if W1.shape != (V, r) or W2.shape != (r, V) or W1.dtype != W2.dtype:
+        raise SpecError("W1 must be [V, r] and W2 [r, V] of one dtype")
+    if uniforms is not None and (uniforms.dtype != torch.float32 or uniforms.shape != (B, gamma)):
+        raise SpecError("uniforms must be float32 [B, gamma]")
+    o = _draft_outputs(B, gamma, V, U.device, out)
+    ws, nws = _workspace(lib.spec_draft_markov_workspace_size(B, gamma, V, r), U.device, workspace)
+    st = lib.spec_draft_sample_markov(
+        _ptr(U), _dtype_code(U, "U"), _ptr(x0), _ptr(W1), _ptr(W2), _dtype_code(W1, "W1"), r,
+        B, gamma, V, float(T), _ptr(uniforms), seed, offset, _ptr(o["tokens"]), _ptr(o["q_logits"]),
+        _ptr(o.get("q_logZ")), _ptr(o.get("q_tok_prob")), _ptr(ws), nws, _stream(stream))
+    _check(st, "spec_draft_sample_markov")
+    return o
+
+
+def spec_draft_sample_rnn(U, x0, h, W1, W2, Wg, Wc, Wo, T=1.0, *, uniforms=None, seed=0,
+                          offset=0, out=None, workspace=None, stream=None):
+    """RNN-head draft.  h [B, gamma, d]; Wg, Wc, Wo [r, 2r + d]."""
+    lib = load_library()
+    for t, n in ((U, "U"), (x0, "x0"), (h, "h"), (W1, "W1"), (W2, "W2"), (Wg, "Wg"), (Wc, "Wc"),
+                 (Wo, "Wo")):
+        _dev(t, n)
+    B, gamma, V = U.shape
+    r = W1.shape[1]
+    d = h.shape[2]
+    if h.shape[:2] != (B, gamma):
+        raise SpecError("h must be [B, gamma, d]")
+    for t, n in ((Wg, "Wg"), (Wc, "Wc"), (Wo, "Wo")):
+        if t.shape != (r, 2 * r + d):
+            raise SpecError(f"{n} must be [r, 2r + d]")
+    o = _draft_outputs(B, gamma, V, U.device, out)
+    ws, nws = _workspace(lib.spec_draft_rnn_workspace_size(B, gamma, V, r, d), U.device, workspace)
+    st = lib.spec_draft_sample_rnn(
+        _ptr(U), _dtype_code(U, "U"), _ptr(x0), _ptr(h), _dtype_code(h, "h"), d, _ptr(W1),
+        _ptr(W2), _ptr(Wg), _ptr(Wc), _ptr(Wo), _dtype_code(W1, "W1"), r, B, gamma, V, float(T),
+        _ptr(uniforms), seed, offset, _ptr(o["tokens"]), _ptr(o["q_logits"]), _ptr(o.get("q_logZ")),
+        _ptr(o.get("q_tok_prob")), _ptr(ws), nws, _stream(stream))
+    _check(st, "spec_draft_sample_rnn")
+    return o
+
+
+def spec_verify(P, Q, draft, T=1.0, *, gamma_max=None, lens=None, p_row_off=None, q_row_off=None,
+                uniforms=None, seed=0, offset=0, diagnostics=True, out=None, workspace=None,
+                stream=None):
+    """Lossless verification.  Dense: P [B, gamma+1, V], Q [B, gamma, V],
+    draft [B, gamma].  Packed: P [rows, V] with p_row_off, Q [rows, V] with
+    q_row_off, lens [B] int32, gamma_max given."""
+    lib = load_library()
+    _dev(P, "P")
+    _dev(draft, "draft")
+    B = draft.shape[0]
+    if gamma_max is None:
+        gamma_max = draft.shape[1]
+    V = P.shape[-1]
+    if draft.dtype != torch.int32 or draft.shape != (B, gamma_max):
+        raise SpecError("draft must be int32 [B, gamma_max]")
+    if p_row_off is None and P.dim() == 3 and P.shape != (B, gamma_max + 1, V):
+        raise SpecError("dense P must be [B, gamma_max + 1, V]")
+    if Q is not None:
+        _dev(Q, "Q")
+        if Q.shape[-1] != V:
+            raise SpecError("Q and P must share V")
+        if q_row_off is None and Q.dim() == 3 and Q.shape != (B, gamma_max, V):
+            raise SpecError("dense Q must be [B, gamma_max, V]")
+    for t, n, dt in ((lens, "lens", torch.int32), (p_row_off, "p_row_off", torch.int64),
+                     (q_row_off, "q_row_off", torch.int64)):
+        if t is not None:
+            _dev(t, n)
+            if t.dtype != dt or t.shape != (B,):
+                raise SpecError(f"{n} must be {dt} [B]")
+    if uniforms is not None and (uniforms.dtype != torch.float32
+                                 or uniforms.shape != (B, gamma_max + 1)):
+        raise SpecError("uniforms must be float32 [B, gamma_max + 1]")
+    dev = P.device
+    if out is None:
+        out = dict(accepted=torch.empty(B, dtype=torch.int32, device=dev),
+                   out_tokens=torch.empty((B, gamma_max + 1), dtype=torch.int32, device=dev))
+        if diagnostics:
+            out["p_logZ"] = torch.empty((B, gamma_max + 1), dtype=torch.float32, device=dev)
+            out["q_logZ"] = torch.empty((B, gamma_max), dtype=torch.float32, device=dev)
+            out["accept_prob"] = torch.empty((B, gamma_max), dtype=torch.float32, device=dev)
+    ws, nws = _workspace(lib.spec_verify_workspace_size(B, gamma_max, V), dev, workspace)
+    st = lib.spec_verify(
+        _ptr(P), _dtype_code(P, "P"), _ptr(Q), _dtype_code(Q, "Q") if Q is not None else SPEC_F32,
+        _ptr(draft), _ptr(lens), _ptr(p_row_off), _ptr(q_row_off), B, gamma_max, V, float(T),
+        _ptr(uniforms), seed, offset, _ptr(out["accepted"]), _ptr(out["out_tokens"]),
+        _ptr(out.get("p_logZ")), _ptr(out.get("q_logZ")), _ptr(out.get("accept_prob")), _ptr(ws),
+        nws, _stream(stream))
+    _check(st, "spec_verify")
+    return out

@@ -1,0 +1,120 @@
+// Device helpers shared by the draft and verify kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace specdec {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// Per-(row, segment) summary written by the streaming passes: max logit m,
+// sum of exp((l - m) / T) over the segment, and the argmax (lowest id on ties).
+struct alignas(16) SegStat {
+    float m;
+    float s;
+    int idx;
+    int pad;
+};
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bits (finite inputs).
+__device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// Philox4x32 with ten rounds (Salmon, Moraes, Dror, Shaw, SC'11): the two
+// multipliers act on counter words 0 and 2; the key advances by the Weyl
+// increments after every round.  Only output word 0 is needed per draw.
+__device__ __forceinline__ uint32_t philox10_word0(uint32_t x0, uint32_t x1, uint32_t x2,
+                                                   uint32_t x3, uint32_t key0, uint32_t key1) {
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {
+        const uint32_t a = 0xD2511F53u * x0;
+        const uint32_t ah = __umulhi(0xD2511F53u, x0);
+        const uint32_t b = 0xCD9E8D57u * x2;
+        const uint32_t bh = __umulhi(0xCD9E8D57u, x2);
+        x0 = bh ^ x1 ^ key0;
+        x1 = b;
+        x2 = ah ^ x3 ^ key1;
+        x3 = a;
+        key0 += 0x9E3779B9u;
+        key1 += 0xBB67AE85u;
+    }
+    return x0;
+}
+
+// Uniform of request b, position k, stream (0 draft, 1 ratio test, 2 final):
+// the top 24 bits of word 0 scaled by 2^-24, exact in fp32.
+__device__ __forceinline__ float counter_uniform(uint64_t seed, uint32_t offset, uint32_t b,
+                                                 uint32_t k, uint32_t stream) {
+    const uint32_t w = philox10_word0(b, k, stream, offset, (uint32_t)seed,
+                                      (uint32_t)(seed >> 32));
+    return (float)(w >> 8) * 5.9604644775390625e-08f;
+}
+
+// (max, sum) pair merge for online softmax; sums are relative to their max.
+__device__ __forceinline__ void merge_ms(float& m, float& s, float m2, float s2, float invT) {
+    if (m2 > m) {
+        s = s * __expf((m - m2) * invT) + s2;
+        m = m2;
+    } else if (m2 != -INFINITY) {
+        s = s + s2 * __expf((m2 - m) * invT);
+    }
+}
+
+// argmax merge with the lowest index on ties.
+__device__ __forceinline__ void merge_arg(float& v, int& i, float v2, int i2) {
+    if (v2 > v || (v2 == v && i2 < i)) {
+        v = v2;
+        i = i2;
+    }
+}
+
+// Full-wave reductions (wave64).
+__device__ __forceinline__ void wave_reduce_stat(float& m, float& s, int& idx, float invT) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        float m2 = __shfl_xor(m, off);
+        float s2 = __shfl_xor(s, off);
+        int i2 = __shfl_xor(idx, off);
+        float mv = m;
+        int iv = idx;
+        merge_arg(mv, iv, m2, i2);
+        merge_ms(m, s, m2, s2, invT);
+        idx = iv;
+    }
+}
+
+__device__ __forceinline__ double wave_sum_f64(double x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+    return x;
+}
+
+__device__ __forceinline__ float wave_max_f32(float x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+    return x;
+}
+
+// Inclusive prefix sum across the wave (lane order).
+__device__ __forceinline__ double wave_inclusive_scan_f64(double x) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        double y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+}  // namespace specdec

@@ -1,0 +1,100 @@
+// Internal interface between the C ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace specdec {
+
+struct SegStat;
+
+enum { kHeadMarkov = 0, kHeadRnn = 1 };
+
+// Everything one draft call needs, resolved and validated by the C ABI layer.
+struct DraftArgs {
+    int head;            // kHeadMarkov or kHeadRnn
+    const void* U;       // [B, gamma, V]
+    int u_bf16;
+    const int32_t* x0;   // [B]
+    const void* W1;      // [V, r]
+    const void* W2;      // [r, V]
+    int w_bf16;
+    const void* h;       // RNN: [B, gamma, d] bf16
+    const void* Wg;      // RNN: [r, 2r + d] bf16
+    const void* Wc;
+    const void* Wo;
+    int B, gamma, V, r, d;
+    float invT;          // 1 / T (1 when greedy)
+    int greedy;
+    const float* uniforms;
+    uint64_t seed;
+    uint32_t offset;
+    int32_t* tokens;     // [B, gamma]
+    float* q_logits;     // [B, gamma, V]
+    float* q_logZ;       // [B, gamma] or null
+    float* q_tok;        // [B, gamma] or null
+    // workspace carve-outs
+    SegStat* stats;      // [B, nseg]
+    float* hproj;        // RNN: [B * gamma, 3r]
+    float* state;        // RNN: [2, B, r]
+    uint16_t* Erows;     // RNN: [B, 3, r]
+};
+
+int draft_num_segments(int B, int V, int w_bf16);
+int draft_segment_len(int B, int w_bf16);
+hipError_t draft_tile_launch(const DraftArgs& a, int k, hipStream_t s);
+hipError_t draft_finalize_launch(const DraftArgs& a, int k, hipStream_t s);
+hipError_t rnn_hidden_proj_launch(const DraftArgs& a, hipStream_t s);
+hipError_t rnn_gates_launch(const DraftArgs& a, int k, hipStream_t s);
+
+// Per (request, row slot) summary written by the verify streaming pass.
+struct alignas(16) RowStat {
+    float m;        // max logit of the row
+    float s;        // sum exp((l - m) / T)
+    int idx;        // argmax, lowest id on ties
+    float gathered; // logit at the draft token of that position (or 0)
+};
+
+// Per-request decision carried from the decide pass to the final draw.
+struct alignas(16) FinalInfo {
+    double logZp;   // normaliser of the target row used by the final draw
+    double logZq;   // normaliser of the draft row (residual mode)
+    int n;          // accepted count, or -1 for an invalid request
+    int mode;       // 0 none (greedy or invalid), 1 residual, 2 bonus
+    int pad0, pad1;
+};
+
+struct VerifyArgs {
+    const void* P;
+    int p_bf16;
+    const void* Q;
+    int q_bf16;
+    const int32_t* draft;       // [B, gamma_max]
+    const int32_t* lens;        // [B] or null
+    const int64_t* p_row_off;   // [B] or null
+    const int64_t* q_row_off;   // [B] or null
+    int B, gamma_max, V;
+    float invT;
+    int greedy;
+    const float* uniforms;      // [B, gamma_max + 1] or null
+    uint64_t seed;
+    uint32_t offset;
+    int32_t* accepted;
+    int32_t* out_tokens;
+    float* p_logZ;
+    float* q_logZ;
+    float* accept_prob;
+    // workspace carve-outs
+    RowStat* rows;              // [B, 2 * gamma_max + 1]
+    FinalInfo* fin;             // [B]
+    double* chunk_sums;         // [B, nchunk]
+};
+
+int verify_num_chunks(int V);
+hipError_t verify_launch(const VerifyArgs& a, hipStream_t s);
+
+hipError_t philox_uniforms_launch(uint64_t seed, uint32_t offset, uint32_t stream, int B, int K,
+                                  float* out, hipStream_t s);
+
+}  // namespace specdec

@@ -1,0 +1,304 @@
+// C ABI of the library (declared in include/specdec.h): argument
+// validation, workspace carving and kernel dispatch on the caller's stream.
+#include <cmath>
+#include <cstdint>
+#include <string>
+
+#include "device_common.hpp"
+#include "launch.hpp"
+#include "specdec.h"
+
+using namespace specdec;
+
+namespace {
+
+thread_local std::string g_err;
+
+spec_status_t fail(spec_status_t st, const std::string& msg) {
+    g_err = msg;
+    return st;
+}
+
+spec_status_t hip_fail(hipError_t e, const char* where) {
+    g_err = std::string(where) + ": " + hipGetErrorString(e);
+    return SPEC_ERR_HIP;
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool dtype_ok(int dt) { return dt == SPEC_F32 || dt == SPEC_BF16; }
+
+constexpr int kMaxV = 1 << 28;
+
+struct DraftLayout {
+    size_t stats, hproj, state, erows, total;
+};
+
+DraftLayout draft_layout(bool rnn, int B, int gamma, int V, int r) {
+    DraftLayout L{};
+    size_t off = 0;
+    L.stats = off;
+    off += align_up((size_t)B * draft_num_segments(B, V, 1) * sizeof(SegStat));
+    if (rnn) {
+        L.hproj = off;
+        off += align_up((size_t)B * gamma * 3 * r * sizeof(float));
+        L.state = off;
+        off += align_up((size_t)2 * B * r * sizeof(float));
+        L.erows = off;
+        off += align_up((size_t)B * 3 * r * sizeof(uint16_t));
+    }
+    L.total = off;
+    return L;
+}
+
+struct VerifyLayout {
+    size_t rows, fin, chunks, total;
+};
+
+VerifyLayout verify_layout(int B, int gamma_max, int V) {
+    VerifyLayout L{};
+    size_t off = 0;
+    L.rows = off;
+    off += align_up((size_t)B * (2 * gamma_max + 1) * sizeof(RowStat));
+    L.fin = off;
+    off += align_up((size_t)B * sizeof(FinalInfo));
+    L.chunks = off;
+    off += align_up((size_t)B * verify_num_chunks(V) * sizeof(double));
+    L.total = off;
+    return L;
+}
+
+spec_status_t check_ws(void* ws, size_t ws_bytes, size_t need) {
+    if (need == 0) return SPEC_OK;
+    if (!ws) return fail(SPEC_ERR_WORKSPACE, "workspace pointer is null");
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+        return fail(SPEC_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (ws_bytes < need)
+        return fail(SPEC_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need) +
+                                            " bytes, got " + std::to_string(ws_bytes));
+    return SPEC_OK;
+}
+
+spec_status_t check_T(float T) {
+    if (!(T >= 0.0f) || std::isinf(T)) return fail(SPEC_ERR_INVALID, "temperature must be finite and >= 0");
+    return SPEC_OK;
+}
+
+// Shared validation of the draft entry points (both heads).
+spec_status_t check_draft_common(const void* U, int U_dtype, const int32_t* x0, const void* W1,
+                                 const void* W2, int w_dtype, int r, int B, int gamma, int V,
+                                 float T, int32_t* tokens, float* q_logits) {
+    if (B < 0 || gamma < 0) return fail(SPEC_ERR_INVALID, "B and gamma must be >= 0");
+    if (V <= 0 || V > kMaxV) return fail(SPEC_ERR_INVALID, "V must be in [1, 2^28]");
+    if (r <= 0) return fail(SPEC_ERR_INVALID, "rank r must be > 0");
+    if (spec_status_t st = check_T(T)) return st;
+    if (!dtype_ok(U_dtype) || !dtype_ok(w_dtype)) return fail(SPEC_ERR_UNSUPPORTED, "dtype must be SPEC_F32 or SPEC_BF16");
+    if ((int64_t)B * gamma > INT32_MAX) return fail(SPEC_ERR_UNSUPPORTED, "B * gamma too large");
+    if (B == 0 || gamma == 0) return SPEC_OK;
+    if (!U || !x0 || !W1 || !W2 || !tokens || !q_logits)
+        return fail(SPEC_ERR_INVALID, "null required pointer (U, x0, W1, W2, tokens, q_logits)");
+    if (!aligned16(U) || !aligned16(W1) || !aligned16(W2) || !aligned16(q_logits))
+        return fail(SPEC_ERR_UNSUPPORTED, "U, W1, W2 and q_logits must be 16-byte aligned");
+    if (w_dtype == SPEC_BF16 && (r % 16 != 0 || r > 256))
+        return fail(SPEC_ERR_UNSUPPORTED, "bf16 weights need r % 16 == 0 and r <= 256");
+    return SPEC_OK;
+}
+
+spec_status_t run_draft(DraftArgs& a, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (a.head == kHeadRnn) {
+        if ((e = rnn_hidden_proj_launch(a, s)) != hipSuccess) return hip_fail(e, "rnn_hidden_proj");
+    }
+    for (int k = 0; k < a.gamma; ++k) {
+        if (a.head == kHeadRnn) {
+            if ((e = rnn_gates_launch(a, k, s)) != hipSuccess) return hip_fail(e, "rnn_gates");
+        }
+        if ((e = draft_tile_launch(a, k, s)) != hipSuccess) return hip_fail(e, "draft_tile");
+        if ((e = draft_finalize_launch(a, k, s)) != hipSuccess) return hip_fail(e, "draft_finalize");
+    }
+    return SPEC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int spec_version(void) { return 100; }
+
+const char* spec_last_error(void) { return g_err.c_str(); }
+
+spec_status_t spec_philox_uniforms(uint64_t seed, uint32_t offset, uint32_t stream, int B, int K,
+                                   float* out, void* stream_handle) {
+    g_err.clear();
+    if (B < 0 || K < 0) return fail(SPEC_ERR_INVALID, "B and K must be >= 0");
+    if ((int64_t)B * K == 0) return SPEC_OK;
+    if (!out) return fail(SPEC_ERR_INVALID, "out is null");
+    hipError_t e = philox_uniforms_launch(seed, offset, stream, B, K, out,
+                                          static_cast<hipStream_t>(stream_handle));
+    return e == hipSuccess ? SPEC_OK : hip_fail(e, "philox_uniforms");
+}
+
+size_t spec_draft_markov_workspace_size(int B, int gamma, int V, int r) {
+    if (B <= 0 || gamma <= 0 || V <= 0 || r <= 0) return 0;
+    return draft_layout(false, B, gamma, V, r).total;
+}
+
+spec_status_t spec_draft_sample_markov(const void* U, int U_dtype, const int32_t* x0,
+                                       const void* W1, const void* W2, int w_dtype, int r, int B,
+                                       int gamma, int V, float T, const float* uniforms,
+                                       uint64_t seed, uint32_t offset, int32_t* tokens,
+                                       float* q_logits, float* q_logZ, float* q_tok_prob,
+                                       void* ws, size_t ws_bytes, void* stream) {
+    g_err.clear();
+    if (spec_status_t st = check_draft_common(U, U_dtype, x0, W1, W2, w_dtype, r, B, gamma, V, T,
+                                              tokens, q_logits))
+        return st;
+    if (B == 0 || gamma == 0) return SPEC_OK;
+    const DraftLayout L = draft_layout(false, B, gamma, V, r);
+    if (spec_status_t st = check_ws(ws, ws_bytes, L.total)) return st;
+    char* w = static_cast<char*>(ws);
+    DraftArgs a{};
+    a.head = kHeadMarkov;
+    a.U = U;
+    a.u_bf16 = U_dtype == SPEC_BF16;
+    a.x0 = x0;
+    a.W1 = W1;
+    a.W2 = W2;
+    a.w_bf16 = w_dtype == SPEC_BF16;
+    a.B = B;
+    a.gamma = gamma;
+    a.V = V;
+    a.r = r;
+    a.greedy = T == 0.0f;
+    a.invT = a.greedy ? 1.0f : 1.0f / T;
+    a.uniforms = uniforms;
+    a.seed = seed;
+    a.offset = offset;
+    a.tokens = tokens;
+    a.q_logits = q_logits;
+    a.q_logZ = q_logZ;
+    a.q_tok = q_tok_prob;
+    a.stats = reinterpret_cast<SegStat*>(w + L.stats);
+    return run_draft(a, stream);
+}
+
+size_t spec_draft_rnn_workspace_size(int B, int gamma, int V, int r, int d) {
+    if (B <= 0 || gamma <= 0 || V <= 0 || r <= 0 || d < 0) return 0;
+    return draft_layout(true, B, gamma, V, r).total;
+}
+
+spec_status_t spec_draft_sample_rnn(const void* U, int U_dtype, const int32_t* x0, const void* h,
+                                    int h_dtype, int d, const void* W1, const void* W2,
+                                    const void* Wg, const void* Wc, const void* Wo, int w_dtype,
+                                    int r, int B, int gamma, int V, float T,
+                                    const float* uniforms, uint64_t seed, uint32_t offset,
+                                    int32_t* tokens, float* q_logits, float* q_logZ,
+                                    float* q_tok_prob, void* ws, size_t ws_bytes, void* stream) {
+    g_err.clear();
+    if (spec_status_t st = check_draft_common(U, U_dtype, x0, W1, W2, w_dtype, r, B, gamma, V, T,
+                                              tokens, q_logits))
+        return st;
+    if (d < 0) return fail(SPEC_ERR_INVALID, "hidden size d must be >= 0");
+    if (!dtype_ok(h_dtype)) return fail(SPEC_ERR_UNSUPPORTED, "dtype must be SPEC_F32 or SPEC_BF16");
+    if (B == 0 || gamma == 0) return SPEC_OK;
+    if (!h || !Wg || !Wc || !Wo) return fail(SPEC_ERR_INVALID, "null required pointer (h, Wg, Wc, Wo)");
+    if (w_dtype != SPEC_BF16 || h_dtype != SPEC_BF16)
+        return fail(SPEC_ERR_UNSUPPORTED, "the RNN head needs bf16 weights and bf16 hidden states");
+    if (d % 8 != 0) return fail(SPEC_ERR_UNSUPPORTED, "the RNN head needs d % 8 == 0");
+    if (!aligned16(h) || !aligned16(Wg) || !aligned16(Wc) || !aligned16(Wo))
+        return fail(SPEC_ERR_UNSUPPORTED, "h, Wg, Wc and Wo must be 16-byte aligned");
+    const DraftLayout L = draft_layout(true, B, gamma, V, r);
+    if (spec_status_t st = check_ws(ws, ws_bytes, L.total)) return st;
+    char* w = static_cast<char*>(ws);
+    DraftArgs a{};
+    a.head = kHeadRnn;
+    a.U = U;
+    a.u_bf16 = U_dtype == SPEC_BF16;
+    a.x0 = x0;
+    a.W1 = W1;
+    a.W2 = W2;
+    a.w_bf16 = 1;
+    a.h = h;
+    a.Wg = Wg;
+    a.Wc = Wc;
+    a.Wo = Wo;
+    a.B = B;
+    a.gamma = gamma;
+    a.V = V;
+    a.r = r;
+    a.d = d;
+    a.greedy = T == 0.0f;
+    a.invT = a.greedy ? 1.0f : 1.0f / T;
+    a.uniforms = uniforms;
+    a.seed = seed;
+    a.offset = offset;
+    a.tokens = tokens;
+    a.q_logits = q_logits;
+    a.q_logZ = q_logZ;
+    a.q_tok = q_tok_prob;
+    a.stats = reinterpret_cast<SegStat*>(w + L.stats);
+    a.hproj = reinterpret_cast<float*>(w + L.hproj);
+    a.state = reinterpret_cast<float*>(w + L.state);
+    a.Erows = reinterpret_cast<uint16_t*>(w + L.erows);
+    return run_draft(a, stream);
+}
+
+size_t spec_verify_workspace_size(int B, int gamma_max, int V) {
+    if (B <= 0 || gamma_max < 0 || V <= 0) return 0;
+    return verify_layout(B, gamma_max, V).total;
+}
+
+spec_status_t spec_verify(const void* P, int p_dtype, const void* Q, int q_dtype,
+                          const int32_t* draft, const int32_t* lens, const int64_t* p_row_off,
+                          const int64_t* q_row_off, int B, int gamma_max, int V, float T,
+                          const float* uniforms, uint64_t seed, uint32_t offset,
+                          int32_t* accepted, int32_t* out_tokens, float* p_logZ, float* q_logZ,
+                          float* accept_prob, void* ws, size_t ws_bytes, void* stream) {
+    g_err.clear();
+    if (B < 0 || gamma_max < 0) return fail(SPEC_ERR_INVALID, "B and gamma_max must be >= 0");
+    if (V <= 0 || V > kMaxV) return fail(SPEC_ERR_INVALID, "V must be in [1, 2^28]");
+    if (spec_status_t st = check_T(T)) return st;
+    if (!dtype_ok(p_dtype) || !dtype_ok(q_dtype)) return fail(SPEC_ERR_UNSUPPORTED, "dtype must be SPEC_F32 or SPEC_BF16");
+    if (B == 0) return SPEC_OK;
+    if (!P || !accepted || !out_tokens)
+        return fail(SPEC_ERR_INVALID, "null required pointer (P, accepted, out_tokens)");
+    if (gamma_max > 0 && (!Q || !draft))
+        return fail(SPEC_ERR_INVALID, "null required pointer (Q, draft)");
+    if (!aligned16(P) || (Q && !aligned16(Q)))
+        return fail(SPEC_ERR_UNSUPPORTED, "P and Q must be 16-byte aligned");
+    const VerifyLayout L = verify_layout(B, gamma_max, V);
+    if (spec_status_t st = check_ws(ws, ws_bytes, L.total)) return st;
+    char* w = static_cast<char*>(ws);
+    VerifyArgs a{};
+    a.P = P;
+    a.p_bf16 = p_dtype == SPEC_BF16;
+    a.Q = Q;
+    a.q_bf16 = q_dtype == SPEC_BF16;
+    a.draft = draft;
+    a.lens = lens;
+    a.p_row_off = p_row_off;
+    a.q_row_off = q_row_off;
+    a.B = B;
+    a.gamma_max = gamma_max;
+    a.V = V;
+    a.greedy = T == 0.0f;
+    a.invT = a.greedy ? 1.0f : 1.0f / T;
+    a.uniforms = uniforms;
+    a.seed = seed;
+    a.offset = offset;
+    a.accepted = accepted;
+    a.out_tokens = out_tokens;
+    a.p_logZ = p_logZ;
+    a.q_logZ = q_logZ;
+    a.accept_prob = accept_prob;
+    a.rows = reinterpret_cast<RowStat*>(w + L.rows);
+    a.fin = reinterpret_cast<FinalInfo*>(w + L.fin);
+    a.chunk_sums = reinterpret_cast<double*>(w + L.chunks);
+    hipError_t e = verify_launch(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SPEC_OK : hip_fail(e, "verify");
+}
+
+}  // extern "C"

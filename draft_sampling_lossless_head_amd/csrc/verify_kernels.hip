@@ -1,0 +1,540 @@
+// Lossless verification kernels (VESSL "Speculative Decoding Part 1",
+// sections "알고리즘" and "수락 규칙").  Four launches on the caller's stream:
+//
+//   verify_rows (x2)      one workgroup per target row p_k (k <= L) and per
+//                         draft row q_k (k < L): one pass over the row with
+//                         16-byte loads -> max, sum exp((l - max)/T), argmax,
+//                         and the logit at the draft token.
+//   verify_decide         one thread per request: normalisers, the ratio test
+//                         u * q(x) < p(x) at every position, first rejection
+//                         n, emitted draft tokens, diagnostics.
+//   verify_final_partials one workgroup per (request, 4096-token chunk) of the
+//                         row that feeds the final draw: sum of max(0, p_n - q_n)
+//                         (correction) or of p_L (bonus).
+//   verify_final_draw     one workgroup per request: inverse CDF over the chunk
+//                         sums, then over the chosen chunk -> final token.
+// The final-draw pair is skipped for T == 0 (argmax of p_n, set by decide).
+#include <climits>
+
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace specdec {
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kChunk = 4096;          // tokens per chunk of the final draw
+constexpr int kPerThread = kChunk / 256;
+
+int verify_num_chunks(int V) { return (V + kChunk - 1) / kChunk; }
+
+__device__ __forceinline__ int64_t p_row(const VerifyArgs& a, int b, int k) {
+    return (a.p_row_off ? a.p_row_off[b] : (int64_t)b * (a.gamma_max + 1)) + k;
+}
+
+__device__ __forceinline__ int64_t q_row(const VerifyArgs& a, int b, int k) {
+    return (a.q_row_off ? a.q_row_off[b] : (int64_t)b * a.gamma_max) + k;
+}
+
+__device__ __forceinline__ int request_len(const VerifyArgs& a, int b) {
+    return a.lens ? a.lens[b] : a.gamma_max;
+}
+
+// Online update of (m, s, argmax) with n consecutive values starting at v0.
+template <int N, bool GREEDY>
+__device__ __forceinline__ void absorb(const float (&x)[N], int v0, float& m, float& s, int& idx,
+                                       float invT) {
+    float lm = x[0];
+    int li = 0;
+#pragma unroll
+    for (int t = 1; t < N; ++t)
+        if (x[t] > lm) {
+            lm = x[t];
+            li = t;
+        }
+    if (lm > m) {
+        if (!GREEDY) s *= __expf((m - lm) * invT);
+        m = lm;
+        idx = v0 + li;
+    }
+    if (!GREEDY && m != -INFINITY) {
+#pragma unroll
+        for (int t = 0; t < N; ++t) s += __expf((x[t] - m) * invT);
+    }
+}
+
+template <bool BF16, bool GREEDY>
+__global__ __launch_bounds__(256)
+void verify_rows(VerifyArgs a, int is_q) {
+    __shared__ float red_m[4], red_s[4];
+    __shared__ int red_i[4];
+    const int k = blockIdx.x;
+    const int b = blockIdx.y;
+    const int L = request_len(a, b);
+    if (L < 0 || L > a.gamma_max) return;
+    if (is_q ? (k >= L) : (k > L)) return;
+    const int V = a.V;
+    const int64_t row = is_q ? q_row(a, b, k) : p_row(a, b, k);
+    const void* base = is_q ? a.Q : a.P;
+    const int tid = threadIdx.x;
+    float m = -INFINITY, s = 0.0f;
+    int idx = INT_MAX;
+    const float invT = a.invT;
+
+    if constexpr (BF16) {
+        const uint16_t* r = static_cast<const uint16_t*>(base) + row * (int64_t)V;
+        const int nvec = (V % 8 == 0) ? V / 8 : 0;
+        const u32x4_t* rv = reinterpret_cast<const u32x4_t*>(r);
+        int i = tid;
+        for (; i + 3 * 256 < nvec; i += 4 * 256) {
+            u32x4_t t[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) t[u] = __builtin_nontemporal_load(rv + i + u * 256);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t w[4] = {t[u][0], t[u][1], t[u][2], t[u][3]};
+                float x[8];
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    x[2 * h] = bf16_bits_to_float(w[h] & 0xFFFFu);
+                    x[2 * h + 1] = bf16_bits_to_float(w[h] >> 16);
+                }
+                absorb<8, GREEDY>(x, (i + u * 256) * 8, m, s, idx, invT);
+            }
+        }
+        for (; i < nvec; i += 256) {
+            const u32x4_t t = __builtin_nontemporal_load(rv + i);
+            const uint32_t w[4] = {t[0], t[1], t[2], t[3]};
+            float x[8];
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                x[2 * h] = bf16_bits_to_float(w[h] & 0xFFFFu);
+                x[2 * h + 1] = bf16_bits_to_float(w[h] >> 16);
+            }
+            absorb<8, GREEDY>(x, i * 8, m, s, idx, invT);
+        }
+        for (int v = nvec * 8 + tid; v < V; v += 256) {
+            const float x[1] = {bf16_bits_to_float(r[v])};
+            absorb<1, GREEDY>(x, v, m, s, idx, invT);
+        }
+    } else {
+        const float* r = static_cast<const float*>(base) + row * (int64_t)V;
+        const int nvec = (V % 4 == 0) ? V / 4 : 0;
+        const f32x4_t* rv = reinterpret_cast<const f32x4_t*>(r);
+        int i = tid;
+        for (; i + 3 * 256 < nvec; i += 4 * 256) {
+            f32x4_t t[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) t[u] = __builtin_nontemporal_load(rv + i + u * 256);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float x[4] = {t[u][0], t[u][1], t[u][2], t[u][3]};
+                absorb<4, GREEDY>(x, (i + u * 256) * 4, m, s, idx, invT);
+            }
+        }
+        for (; i < nvec; i += 256) {
+            const f32x4_t t = __builtin_nontemporal_load(rv + i);
+            const float x[4] = {t[0], t[1], t[2], t[3]};
+            absorb<4, GREEDY>(x, i * 4, m, s, idx, invT);
+        }
+        for (int v = nvec * 4 + tid; v < V; v += 256) {
+            const float x[1] = {r[v]};
+            absorb<1, GREEDY>(x, v, m, s, idx, invT);
+        }
+    }
+
+    wave_reduce_stat(m, s, idx, invT);
+    const int lane = tid & 63, wave = tid >> 6;
+    if (lane == 0) {
+        red_m[wave] = m;
+        red_s[wave] = s;
+        red_i[wave] = idx;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        float M = red_m[0], S = red_s[0];
+        int I = red_i[0];
+        for (int w = 1; w < 4; ++w) {
+            float mv = M;
+            int iv = I;
+            merge_arg(mv, iv, red_m[w], red_i[w]);
+            merge_ms(M, S, red_m[w], red_s[w], invT);
+            I = iv;
+        }
+        float gathered = 0.0f;
+        if (k < L) {
+            const int x = a.draft[(size_t)b * a.gamma_max + k];
+            if (x >= 0 && x < V) {
+                gathered = BF16 ? bf16_bits_to_float(static_cast<const uint16_t*>(base)[row * (int64_t)V + x])
+                                : static_cast<const float*>(base)[row * (int64_t)V + x];
+            }
+        }
+        RowStat rs;
+        rs.m = M;
+        rs.s = S;
+        rs.idx = I;
+        rs.gathered = gathered;
+        a.rows[(size_t)b * (2 * a.gamma_max + 1) + (is_q ? a.gamma_max + 1 + k : k)] = rs;
+    }
+}
+
+__global__ __launch_bounds__(256)
+void verify_decide(VerifyArgs a) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= a.B) return;
+    const int G = a.gamma_max;
+    const int L = request_len(a, b);
+    int32_t* out = a.out_tokens + (size_t)b * (G + 1);
+    const int32_t* dr = a.draft + (size_t)b * G;
+    const RowStat* rs = a.rows + (size_t)b * (2 * G + 1);
+    bool bad = L < 0 || L > G;
+    if (!bad) {
+        for (int k = 0; k < L; ++k)
+            if (dr[k] < 0 || dr[k] >= a.V) bad = true;
+        for (int k = 0; k <= L && !bad; ++k)
+            if (rs[k].m == -INFINITY) bad = true;
+        for (int k = 0; k < L && !bad; ++k)
+            if (rs[G + 1 + k].m == -INFINITY) bad = true;
+    }
+    if (bad) {
+        a.accepted[b] = -1;
+        for (int j = 0; j <= G; ++j) out[j] = -1;
+        for (int j = 0; j <= G; ++j) {
+            if (a.p_logZ) a.p_logZ[(size_t)b * (G + 1) + j] = 0.0f;
+            if (j < G && a.q_logZ) a.q_logZ[(size_t)b * G + j] = 0.0f;
+            if (j < G && a.accept_prob) a.accept_prob[(size_t)b * G + j] = 0.0f;
+        }
+        FinalInfo f;
+        f.logZp = 0.0;
+        f.logZq = 0.0;
+        f.n = -1;
+        f.mode = 0;
+        f.pad0 = f.pad1 = 0;
+        a.fin[b] = f;
+        return;
+    }
+    const double invT = (double)a.invT;
+    int n = L;
+    double lzp_n = 0.0, lzq_n = 0.0;
+    for (int k = 0; k <= G; ++k) {
+        double lzp = 0.0, lzq = 0.0, ap = 0.0;
+        if (k <= L) {
+            const RowStat p = rs[k];
+            lzp = a.greedy ? (double)p.m : (double)p.m * invT + log((double)p.s);
+        }
+        if (k < L) {
+            const RowStat p = rs[k];
+            const RowStat q = rs[G + 1 + k];
+            bool acc;
+            if (a.greedy) {
+                lzq = (double)q.m;
+                acc = p.idx == dr[k];
+                ap = acc ? 1.0 : 0.0;
+            } else {
+                lzq = (double)q.m * invT + log((double)q.s);
+                const double px = exp((double)p.gathered * invT - lzp);
+                const double qx = exp((double)q.gathered * invT - lzq);
+                ap = qx > 0.0 ? fmin(1.0, px / qx) : (px > 0.0 ? 1.0 : 0.0);
+                const float u = a.uniforms ? a.uniforms[(size_t)b * (G + 1) + k]
+                                           : counter_uniform(a.seed, a.offset, b, k, 1);
+                acc = (double)u * qx < px;
+            }
+            if (!acc && n == L) {
+                n = k;
+                lzp_n = lzp;
+                lzq_n = lzq;
+            }
+        }
+        if (k == L && n == L) lzp_n = lzp;
+        if (a.p_logZ) a.p_logZ[(size_t)b * (G + 1) + k] = (float)lzp;
+        if (k < G && a.q_logZ) a.q_logZ[(size_t)b * G + k] = (float)lzq;
+        if (k < G && a.accept_prob) a.accept_prob[(size_t)b * G + k] = (float)ap;
+    }
+    a.accepted[b] = n;
+    for (int j = 0; j <= G; ++j) out[j] = j < n ? dr[j] : -1;
+    if (a.greedy) out[n] = rs[n].idx;
+    FinalInfo f;
+    f.logZp = lzp_n;
+    f.logZq = lzq_n;
+    f.n = n;
+    f.mode = a.greedy ? 0 : (n < L ? 1 : 2);
+    f.pad0 = f.pad1 = 0;
+    a.fin[b] = f;
+}
+
+// Weight of token v for the final draw: max(0, p - q) or p.  The exponent
+// subtracts the fp64 normaliser as an exact (hi, lo) float pair.
+template <bool PB, bool QB>
+struct FinalRow {
+    const void* pr;
+    const void* qr;
+    float invT, lzp_hi, lzp_lo, lzq_hi, lzq_lo;
+    int residual;
+
+    __device__ __forceinline__ float logit(const void* base, bool bf, int64_t v) const {
+        return bf ? bf16_bits_to_float(static_cast<const uint16_t*>(base)[v])
+                  : static_cast<const float*>(base)[v];
+    }
+    __device__ __forceinline__ float weight(int64_t v) const {
+        const float lp = logit(pr, PB, v);
+        const float p = expf(fmaf(lp, invT, -lzp_hi) - lzp_lo);
+        if (!residual) return p;
+        const float lq = logit(qr, QB, v);
+        const float q = expf(fmaf(lq, invT, -lzq_hi) - lzq_lo);
+        return fmaxf(p - q, 0.0f);
+    }
+};
+
+template <bool PB, bool QB>
+__device__ __forceinline__ FinalRow<PB, QB> make_final_row(const VerifyArgs& a, int b,
+                                                           const FinalInfo& f, int residual) {
+    FinalRow<PB, QB> fr;
+    const int64_t V = a.V;
+    fr.pr = PB ? (const void*)(static_cast<const uint16_t*>(a.P) + p_row(a, b, f.n) * V)
+               : (const void*)(static_cast<const float*>(a.P) + p_row(a, b, f.n) * V);
+    fr.qr = nullptr;
+    if (residual)
+        fr.qr = QB ? (const void*)(static_cast<const uint16_t*>(a.Q) + q_row(a, b, f.n) * V)
+                   : (const void*)(static_cast<const float*>(a.Q) + q_row(a, b, f.n) * V);
+    fr.invT = a.invT;
+    fr.lzp_hi = (float)f.logZp;
+    fr.lzp_lo = (float)(f.logZp - (double)fr.lzp_hi);
+    fr.lzq_hi = (float)f.logZq;
+    fr.lzq_lo = (float)(f.logZq - (double)fr.lzq_hi);
+    fr.residual = residual;
+    return fr;
+}
+
+// fp64 sum of this thread's kPerThread consecutive tokens of chunk c.
+template <bool PB, bool QB>
+__device__ __forceinline__ double thread_chunk_sum(const FinalRow<PB, QB>& fr, int c, int V,
+                                                   int tid) {
+    const int v0 = c * kChunk + tid * kPerThread;
+    double acc = 0.0;
+#pragma unroll 4
+    for (int t = 0; t < kPerThread; ++t) {
+        const int v = v0 + t;
+        if (v < V) acc += (double)fr.weight(v);
+    }
+    return acc;
+}
+
+__device__ __forceinline__ double block_sum_f64(double x, double* sh) {
+    x = wave_sum_f64(x);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __syncthreads();
+    if (lane == 0) sh[wave] = x;
+    __syncthreads();
+    return sh[0] + sh[1] + sh[2] + sh[3];
+}
+
+template <bool PB, bool QB>
+__global__ __launch_bounds__(256)
+void verify_final_partials(VerifyArgs a) {
+    __shared__ double sh[4];
+    const int c = blockIdx.x;
+    const int b = blockIdx.y;
+    const FinalInfo f = a.fin[b];
+    if (f.mode == 0) return;
+    const FinalRow<PB, QB> fr = make_final_row<PB, QB>(a, b, f, f.mode == 1);
+    const double tot = block_sum_f64(thread_chunk_sum(fr, c, a.V, threadIdx.x), sh);
+    if (threadIdx.x == 0) a.chunk_sums[(size_t)b * gridDim.x + c] = tot;
+}
+
+// Block-wide exclusive scan of one fp64 value per thread (256 threads).
+__device__ __forceinline__ void block_scan_f64(double x, double* scan, double& excl,
+                                               double& incl, double& total) {
+    const int tid = threadIdx.x;
+    __syncthreads();
+    scan[tid] = x;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+        const double add = tid >= off ? scan[tid - off] : 0.0;
+        __syncthreads();
+        scan[tid] += add;
+        __syncthreads();
+    }
+    incl = scan[tid];
+    excl = tid > 0 ? scan[tid - 1] : 0.0;
+    total = scan[255];
+}
+
+template <bool PB, bool QB>
+__global__ __launch_bounds__(256)
+void verify_final_draw(VerifyArgs a, int nchunk) {
+    __shared__ double scan[256];
+    __shared__ int sh_pick, sh_last[4];
+    __shared__ double sh_rem;
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    FinalInfo f = a.fin[b];
+    if (f.mode == 0) return;
+    const int G = a.gamma_max;
+    const int V = a.V;
+    double* sums = a.chunk_sums + (size_t)b * nchunk;
+
+    const float u = a.uniforms ? a.uniforms[(size_t)b * (G + 1) + G]
+                               : counter_uniform(a.seed, a.offset, b, 0, 2);
+    const int per = (nchunk + 255) / 256;
+    const int c0 = min(nchunk, tid * per);
+    const int c1 = min(nchunk, c0 + per);
+    double tsum = 0.0;
+    for (int c = c0; c < c1; ++c) tsum += sums[c];
+    double excl, incl, R;
+    block_scan_f64(tsum, scan, excl, incl, R);
+
+    int residual = f.mode == 1;
+    if (!(R > 0.0)) {
+        // Residual without mass after rounding: draw from p_n instead.
+        residual = 0;
+        const FinalRow<PB, QB> fp = make_final_row<PB, QB>(a, b, f, 0);
+        for (int c = 0; c < nchunk; ++c) {
+            const double t = block_sum_f64(thread_chunk_sum(fp, c, V, tid), scan);
+            if (tid == 0) sums[c] = t;
+        }
+        __syncthreads();
+        tsum = 0.0;
+        for (int c = c0; c < c1; ++c) tsum += sums[c];
+        block_scan_f64(tsum, scan, excl, incl, R);
+    }
+    const FinalRow<PB, QB> fr = make_final_row<PB, QB>(a, b, f, residual);
+    const double thr = (double)u * R;
+
+    // chunk holding thr (clamped to the last chunk with mass)
+    if (tid == 0) sh_pick = -1;
+    __syncthreads();
+    if (tsum > 0.0 && thr >= excl && thr < incl) {
+        double run = excl;
+        int found = -1, last = -1;
+        double last_run = 0.0;
+        for (int c = c0; c < c1; ++c) {
+            const double w = sums[c];
+            if (w > 0.0) {
+                last = c;
+                last_run = run;
+                if (thr < run + w) {
+                    found = c;
+                    break;
+                }
+            }
+            run += w;
+        }
+        sh_pick = found >= 0 ? found : last;
+        sh_rem = found >= 0 ? thr - run : thr - last_run;
+    }
+    __syncthreads();
+    if (sh_pick < 0) {
+        int lastc = -1;
+        for (int c = c0; c < c1; ++c)
+            if (sums[c] > 0.0) lastc = c;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) lastc = max(lastc, __shfl_xor(lastc, off));
+        if (lane == 0) sh_last[wave] = lastc;
+        __syncthreads();
+        if (tid == 0) {
+            sh_pick = max(max(sh_last[0], sh_last[1]), max(sh_last[2], sh_last[3]));
+            sh_rem = INFINITY;
+        }
+        __syncthreads();
+    }
+    const int cstar = sh_pick;
+    const double rem = sh_rem;
+    if (cstar < 0) {   // no mass anywhere (cannot happen for a finite target row)
+        if (tid == 0) a.out_tokens[(size_t)b * (G + 1) + f.n] = -1;
+        return;
+    }
+
+    // rescan the chunk: per-thread runs of kPerThread tokens, same sums as
+    // verify_final_partials, then the owning thread walks its run.
+    const double mine = thread_chunk_sum(fr, cstar, V, tid);
+    double e2, i2, tot2;
+    block_scan_f64(mine, scan, e2, i2, tot2);
+    if (tid == 0) sh_pick = -1;
+    __syncthreads();
+    if (mine > 0.0 && rem >= e2 && rem < i2) {
+        double run = e2;
+        int pick = -1, last = -1;
+        const int v0 = cstar * kChunk + tid * kPerThread;
+        for (int t = 0; t < kPerThread && v0 + t < V; ++t) {
+            const double w = (double)fr.weight(v0 + t);
+            if (w > 0.0) {
+                last = v0 + t;
+                if (rem < run + w) {
+                    pick = v0 + t;
+                    break;
+                }
+            }
+            run += w;
+        }
+        sh_pick = pick >= 0 ? pick : last;
+    }
+    __syncthreads();
+    if (sh_pick < 0) {
+        // rem beyond the rescanned total: last token of the chunk with weight
+        int lastv = -1;
+        const int v0 = cstar * kChunk + tid * kPerThread;
+        for (int t = 0; t < kPerThread && v0 + t < V; ++t)
+            if (fr.weight(v0 + t) > 0.0f) lastv = v0 + t;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) lastv = max(lastv, __shfl_xor(lastv, off));
+        if (lane == 0) sh_last[wave] = lastv;
+        __syncthreads();
+        if (tid == 0) sh_pick = max(max(sh_last[0], sh_last[1]), max(sh_last[2], sh_last[3]));
+        __syncthreads();
+    }
+    if (tid == 0) a.out_tokens[(size_t)b * (G + 1) + f.n] = sh_pick;
+}
+
+__global__ void philox_uniforms_kernel(uint64_t seed, uint32_t offset, uint32_t stream, int B,
+                                       int K, float* out) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (int64_t)B * K) return;
+    const int b = (int)(i / K), k = (int)(i % K);
+    out[i] = counter_uniform(seed, offset, b, k, stream);
+}
+
+template <bool PB, bool QB>
+static void launch_final(const VerifyArgs& a, hipStream_t s) {
+    const int nc = verify_num_chunks(a.V);
+    hipLaunchKernelGGL((verify_final_partials<PB, QB>), dim3(nc, a.B), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((verify_final_draw<PB, QB>), dim3(a.B), dim3(256), 0, s, a, nc);
+}
+
+template <bool BF16>
+static void launch_rows(const VerifyArgs& a, int is_q, hipStream_t s) {
+    const int nrow = is_q ? a.gamma_max : a.gamma_max + 1;
+    if (nrow == 0) return;
+    dim3 grid(nrow, a.B);
+    if (a.greedy)
+        hipLaunchKernelGGL((verify_rows<BF16, true>), grid, dim3(256), 0, s, a, is_q);
+    else
+        hipLaunchKernelGGL((verify_rows<BF16, false>), grid, dim3(256), 0, s, a, is_q);
+}
+
+hipError_t verify_launch(const VerifyArgs& a, hipStream_t s) {
+    if (a.p_bf16) launch_rows<true>(a, 0, s);
+    else launch_rows<false>(a, 0, s);
+    if (a.q_bf16) launch_rows<true>(a, 1, s);
+    else launch_rows<false>(a, 1, s);
+    hipLaunchKernelGGL(verify_decide, dim3((a.B + 127) / 128), dim3(128), 0, s, a);
+    if (!a.greedy) {
+        if (a.p_bf16 && a.q_bf16) launch_final<true, true>(a, s);
+        else if (a.p_bf16) launch_final<true, false>(a, s);
+        else if (a.q_bf16) launch_final<false, true>(a, s);
+        else launch_final<false, false>(a, s);
+    }
+    return hipGetLastError();
+}
+
+hipError_t philox_uniforms_launch(uint64_t seed, uint32_t offset, uint32_t stream, int B, int K,
+                                  float* out, hipStream_t s) {
+    const int64_t n = (int64_t)B * K;
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(philox_uniforms_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       seed, offset, stream, B, K, out);
+    return hipGetLastError();
+}
+
+}  // namespace specdec

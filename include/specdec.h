@@ -1,0 +1,203 @@
+/*
+ * specdec.h -- C ABI of the MI355X (gfx950) speculative-decoding sampling
+ * library: DSpark's sequential draft stage (Markov or RNN head) and lossless
+ * rejection-sampling verification.
+ *
+ * Sources of the operations (page title, then section / equation):
+ *   [DSpark]  "[논문리뷰] DSpark: Confidence-Scheduled Speculative Decoding
+ *             with Semi-Autoregressive Generation" (kimjy99.github.io),
+ *             §1.2 Sequential stage: block factorisation, per-position softmax,
+ *             Markov-head equation, RNN-head equation; §2.2 scheduled
+ *             acceptance lengths l_r in {0..gamma}.
+ *   [VESSL]   "Speculative Decoding Part 1" (vessl.ai blog), section
+ *             "알고리즘" (one speculative cycle) and section "수락 규칙"
+ *             (acceptance rule, residual distribution, lossless theorem).
+ *   [H-Spec]  "H-Spec: Parallel Speculative Decoding Without a Drafter-Side KV
+ *             Cache" (jaehun.me), Appx. B.1 settings: Markov rank 256,
+ *             vocabulary pruned to 32000, fixed-length verification.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor arguments are DEVICE pointers to caller-owned, contiguous,
+ *   row-major buffers on the current HIP device.  The library never
+ *   allocates or frees caller memory and keeps no state between calls; the
+ *   only scratch is the caller's workspace (size from the *_workspace_size
+ *   query, alignment 256 bytes).  Concurrent calls need distinct workspaces.
+ * - `stream` is a hipStream_t passed as void* (NULL = default stream).
+ *   All work is enqueued asynchronously on it; outputs are valid once the
+ *   stream has been synchronised.
+ * - Argument validation is synchronous and happens before any launch; a
+ *   non-SPEC_OK status means nothing was enqueued.  Checks that need device
+ *   data (token ids, lengths) are done by the kernels: an offending request
+ *   gets token -1 / accepted -1 in its outputs and the others are unaffected.
+ *   Device faults surface at the caller's next synchronisation.
+ * - spec_last_error() returns a thread-local description of the last failure.
+ * - Logit dtypes: SPEC_F32 or SPEC_BF16.  Temperature T > 0 samples from
+ *   softmax(logits / T); T == 0 is greedy (argmax, lowest token id on ties)
+ *   and consumes no uniforms.  The library multiplies logits by the fp32
+ *   value 1/T.
+ * - Uniforms: if `uniforms` is non-NULL it is a device float array in
+ *   [0, 1) laid out as documented per call; otherwise uniforms come from the
+ *   counter-based Philox4x32-10 generator (Salmon et al., SC'11) with key
+ *   (seed low 32 bits, seed high 32 bits) and counter
+ *   (request b, position k, stream, offset); u = (word0 >> 8) * 2^-24.
+ *   Streams: 0 = draft sample at position k, 1 = ratio test at position k,
+ *   2 = the final (corrected or bonus) draw, position 0.  A draft call and a
+ *   verify call of one cycle may therefore share (seed, offset).
+ * - Sampling is by inverse CDF over ascending token id: the token is the
+ *   smallest v with u * Z < S_v, S_v the running sum of the unnormalised
+ *   weights and Z their total.
+ */
+#ifndef SPECDEC_H
+#define SPECDEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SPEC_OK = 0,
+    SPEC_ERR_INVALID = 1,      /* bad argument (null pointer, size, T < 0) */
+    SPEC_ERR_UNSUPPORTED = 2,  /* dtype combination or size not supported */
+    SPEC_ERR_WORKSPACE = 3,    /* workspace missing, too small or misaligned */
+    SPEC_ERR_HIP = 4           /* a HIP call or kernel launch failed */
+} spec_status_t;
+
+typedef enum {
+    SPEC_F32 = 0,
+    SPEC_BF16 = 1
+} spec_dtype_t;
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int spec_version(void);
+
+/* Thread-local text of the last error ("" if none). */
+const char *spec_last_error(void);
+
+/*
+ * Counter-based uniforms, as used by every entry point: out[b * K + k] =
+ * u(seed, offset, request b, position k, stream) for b < B, k < K.
+ * out: device float [B, K].  Exposed so callers can reproduce or log the
+ * draws of a cycle.
+ */
+spec_status_t spec_philox_uniforms(uint64_t seed, uint32_t offset, uint32_t stream,
+                                   int B, int K, float *out, void *stream_handle);
+
+/*
+ * ---------------------------------------------------------------------------
+ * Draft, Markov head  [DSpark §1.2, block factorisation and Markov-head eq.]
+ * ---------------------------------------------------------------------------
+ * For every request b and position k = 0..gamma-1, left to right:
+ *     prev    = (k == 0) ? x0[b] : tokens[b, k-1]
+ *     l[v]    = U[b, k, v] + sum_j W1[prev, j] * W2[j, v]
+ *     tokens[b, k] ~ softmax(l / T)      (greedy if T == 0)
+ *
+ * U        [B, gamma, V]  base logits, dtype U_dtype (F32 or BF16)
+ * x0       [B]            int32 anchor tokens (the previous cycle's last)
+ * W1       [V, r]         embedding table,  dtype w_dtype
+ * W2       [r, V]         logit projection, dtype w_dtype
+ *                         (BF16 runs on MFMA with fp32 accumulation; F32 runs
+ *                         on the vector ALUs)
+ * uniforms [B, gamma]     optional caller uniforms (stream 0 otherwise)
+ * tokens   [B, gamma]     out: int32 draft tokens
+ * q_logits [B, gamma, V]  out: fp32 draft logits l BEFORE temperature; pass
+ *                         them unchanged (with the same T) to spec_verify
+ * q_logZ   [B, gamma]     optional out: ln sum_v exp(l[v] / T) (T == 0: max l)
+ * q_tok_prob [B, gamma]   optional out: q(tokens[b, k]) (T == 0: 1)
+ * Errors: SPEC_ERR_INVALID for null required pointers, B < 0, gamma < 0,
+ * V <= 0, r <= 0, T < 0 or NaN; SPEC_ERR_UNSUPPORTED for other dtypes;
+ * SPEC_ERR_WORKSPACE if ws_bytes < spec_draft_markov_workspace_size(...).
+ * A request whose anchor is outside [0, V) gets tokens -1 from there on.
+ */
+size_t spec_draft_markov_workspace_size(int B, int gamma, int V, int r);
+
+spec_status_t spec_draft_sample_markov(
+    const void *U, int U_dtype, const int32_t *x0,
+    const void *W1, const void *W2, int w_dtype, int r,
+    int B, int gamma, int V, float T,
+    const float *uniforms, uint64_t seed, uint32_t offset,
+    int32_t *tokens, float *q_logits, float *q_logZ, float *q_tok_prob,
+    void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * ---------------------------------------------------------------------------
+ * Draft, RNN head  [DSpark §1.2, RNN-head equation]
+ * ---------------------------------------------------------------------------
+ * As the Markov head, with the bias of position k given by
+ *     z_k  = [s_{k-1}; W1[prev]; h[b, k]]            (length 2r + d)
+ *     g    = sigmoid(Wg z_k),  c = tanh(Wc z_k),  o = tanh(Wo z_k)
+ *     s_k  = g * s_{k-1} + (1 - g) * c,    s_0 = 0
+ *     l[v] = U[b, k, v] + sum_j W2[j, v] * o[j]
+ * h  [B, gamma, d]  backbone hidden states, dtype h_dtype (BF16)
+ * Wg, Wc, Wo [r, 2r + d]  gate matrices, dtype w_dtype (BF16), no bias terms
+ * The state s and o are kept in fp32; o enters the W2 contraction as an
+ * exact three-term bf16 split so the bf16 MFMA path keeps fp32 accuracy.
+ * Other arguments, outputs and errors as spec_draft_sample_markov.
+ */
+size_t spec_draft_rnn_workspace_size(int B, int gamma, int V, int r, int d);
+
+spec_status_t spec_draft_sample_rnn(
+    const void *U, int U_dtype, const int32_t *x0,
+    const void *h, int h_dtype, int d,
+    const void *W1, const void *W2, const void *Wg, const void *Wc, const void *Wo,
+    int w_dtype, int r,
+    int B, int gamma, int V, float T,
+    const float *uniforms, uint64_t seed, uint32_t offset,
+    int32_t *tokens, float *q_logits, float *q_logZ, float *q_tok_prob,
+    void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * ---------------------------------------------------------------------------
+ * Lossless verification  [VESSL "알고리즘" and "수락 규칙"]
+ * ---------------------------------------------------------------------------
+ * For every request b with L = lens ? lens[b] : gamma_max drafted positions:
+ *     p_k = softmax(P_k / T) for k = 0..L,  q_k = softmax(Q_k / T) for k < L
+ *     accept position k iff u_k * q_k(x_k) < p_k(x_k)   (x_k = draft[b, k])
+ *     n = first rejected position, or L
+ *     n < L: final ~ max(0, p_n - q_n) / sum(max(0, p_n - q_n))
+ *     n = L: final ~ p_L (bonus token)
+ *     out[b] = x_0..x_{n-1}, final, then -1;   accepted[b] = n  (tau = n + 1)
+ * T == 0: accept iff argmax p_k == x_k; final = argmax p_n.
+ * If the residual has zero mass after rounding, p_n is sampled instead.
+ *
+ * P         target logits, dtype p_dtype.  Dense: [B, gamma_max + 1, V].
+ *           Packed (p_row_off != NULL): request b owns rows
+ *           p_row_off[b] .. p_row_off[b] + L (L + 1 rows of V).
+ * Q         draft logits before temperature, dtype q_dtype.  Dense:
+ *           [B, gamma_max, V]; packed (q_row_off != NULL): rows
+ *           q_row_off[b] .. q_row_off[b] + L - 1.
+ * draft     [B, gamma_max] int32 draft tokens (first L used)
+ * lens      [B] int32 in [0, gamma_max], or NULL for fixed length gamma_max
+ * p_row_off, q_row_off  [B] int64 row offsets, or NULL for dense
+ * uniforms  [B, gamma_max + 1] optional caller uniforms: column k < gamma_max
+ *           is the ratio test of position k, column gamma_max the final draw
+ * accepted  [B] out int32 n (-1 for a request with invalid tokens/length)
+ * out_tokens [B, gamma_max + 1] out int32
+ * p_logZ    [B, gamma_max + 1] optional out: ln sum exp(P_k / T) (T == 0:
+ *           max logit); q_logZ [B, gamma_max] likewise for Q;
+ * accept_prob [B, gamma_max] optional out: min(1, p_k(x_k) / q_k(x_k))
+ *           (T == 0: 1 or 0).  Entries for k beyond L are 0.
+ * Errors: SPEC_ERR_INVALID for null required pointers, B < 0,
+ * gamma_max < 0, V <= 0, T < 0 or NaN; SPEC_ERR_UNSUPPORTED for other
+ * dtypes; SPEC_ERR_WORKSPACE for a short workspace.
+ */
+size_t spec_verify_workspace_size(int B, int gamma_max, int V);
+
+spec_status_t spec_verify(
+    const void *P, int p_dtype, const void *Q, int q_dtype,
+    const int32_t *draft, const int32_t *lens,
+    const int64_t *p_row_off, const int64_t *q_row_off,
+    int B, int gamma_max, int V, float T,
+    const float *uniforms, uint64_t seed, uint32_t offset,
+    int32_t *accepted, int32_t *out_tokens,
+    float *p_logZ, float *q_logZ, float *accept_prob,
+    void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECDEC_H */

@@ -1,0 +1,154 @@
+"""Element-by-element comparison of a GPU result with the oracle's.
+
+TEST INFRASTRUCTURE ONLY.  The oracle runs on the same seeded inputs as the
+GPU and never receives anything the GPU produced.  The bar:
+
+* token ids and accepted counts match exactly, except a draw whose uniform
+  lies within BAND (1e-6) of the oracle's CDF boundary between the oracle's
+  choice and the GPU's (or, at T = 0, whose top-2 logit gap is within the
+  fp32 accumulation tolerance).  Such draws are counted and reported.  After
+  a boundary draw in a draft chain the rest of that request conditions on a
+  different prefix and is not compared.
+* normalisers (log Z): |delta| <= 1e-5; probabilities q(x), min(1, p/q):
+  relative 1e-5; draft logits: |delta| <= 1e-5 * max(1, |l|).
+"""
+import numpy as np
+
+from . import binding as orc
+
+BAND = 1e-6
+TOL_LOGZ = 1e-5
+TOL_REL = 1e-5
+
+
+class Tally:
+    def __init__(self):
+        self.draws = 0
+        self.boundary = 0
+        self.compared_positions = 0
+        self.requests = 0
+        self.skipped_after_boundary = 0
+        self.fallbacks = 0
+
+    def as_dict(self):
+        return dict(draws=self.draws, boundary=self.boundary,
+                    compared_positions=self.compared_positions, requests=self.requests,
+                    skipped_after_boundary=self.skipped_after_boundary, fallbacks=self.fallbacks)
+
+
+def _interval_distance(w, y, u):
+    lo, hi = orc.cdf_interval(w, y)
+    if not np.isfinite(lo):
+        return np.inf
+    if lo <= u < hi:
+        return 0.0
+    return max(lo - u, u - hi)
+
+
+def _check_draw(w, orc_tok, gpu_tok, u, what):
+    """Token equality or a draw inside the boundary band.  Returns True when
+    it was a boundary draw."""
+    if gpu_tok == orc_tok:
+        return False
+    if gpu_tok < 0 or gpu_tok >= len(w):
+        raise AssertionError(f"{what}: GPU token {gpu_tok} out of range (oracle {orc_tok})")
+    dist = _interval_distance(w, gpu_tok, u)
+    if dist > BAND:
+        raise AssertionError(f"{what}: GPU token {gpu_tok} != oracle {orc_tok}, uniform {u} is "
+                             f"{dist:.3e} from the GPU token's CDF interval (band {BAND})")
+    return True
+
+
+def _check_greedy(l, orc_tok, gpu_tok, what):
+    if gpu_tok == orc_tok:
+        return False
+    gap = l[orc_tok] - l[gpu_tok]
+    tol = TOL_REL * max(1.0, abs(l[orc_tok]))
+    if not (0 <= gap <= tol):
+        raise AssertionError(f"{what}: greedy GPU token {gpu_tok} != oracle {orc_tok}, "
+                             f"logit gap {gap:.3e} > {tol:.1e}")
+    return True
+
+
+def _close(a, b, atol, rtol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    bad = ~(np.abs(a - b) <= atol + rtol * np.abs(b))
+    if np.any(bad):
+        i = int(np.flatnonzero(bad.ravel())[0])
+        raise AssertionError(f"{what}: GPU {a.ravel()[i]!r} vs oracle {b.ravel()[i]!r} at flat "
+                             f"index {i} ({int(bad.sum())} mismatches)")
+
+
+def compare_draft_request(orc_out, U, gpu, T, u, what, tally, check_logits=True):
+    """Compare one request's draft.  orc_out: oracle draft dict; U: base
+    logits [gamma, V] (float64); gpu: dict of numpy arrays for this request
+    (tokens [gamma], q_logits [gamma, V], q_logZ, q_tok_prob); u: uniforms."""
+    gamma = len(orc_out["tokens"])
+    tally.requests += 1
+    for k in range(gamma):
+        l = orc_out["q_logits"][k]
+        gt, ot = int(gpu["tokens"][k]), int(orc_out["tokens"][k])
+        if check_logits:
+            _close(gpu["q_logits"][k], l, TOL_REL * np.maximum(1.0, np.abs(l)), 0.0,
+                   f"{what} q_logits[k={k}]")
+        if T > 0:
+            _close(gpu["q_logZ"][k], orc_out["logZ"][k], TOL_LOGZ, 0.0, f"{what} q_logZ[k={k}]")
+        tally.draws += 1
+        tally.compared_positions += 1
+        if T == 0:
+            boundary = _check_greedy(l, ot, gt, f"{what} k={k}")
+        else:
+            w, Z, _ = orc.softmax_weights(l, T)
+            boundary = _check_draw(w, ot, gt, u[k], f"{what} k={k}")
+            if not boundary:
+                _close(gpu["q_tok_prob"][k], orc_out["q_tok"][k], 1e-30, TOL_REL,
+                       f"{what} q_tok_prob[k={k}]")
+        if boundary:
+            tally.boundary += 1
+            tally.skipped_after_boundary += gamma - k - 1
+            return False
+    return True
+
+
+def compare_verify_request(P, Q, draft, T, u_test, u_final, gpu, what, tally):
+    """Compare one request's verification.  P [L+1, V], Q [L, V] float64
+    (the exact values both sides received); gpu: dict with accepted (int),
+    out_tokens [gamma_max+1], optional p_logZ, q_logZ, accept_prob rows."""
+    L = len(draft)
+    o = orc.verify(P, Q, draft, T, u_test, u_final)
+    tally.requests += 1
+    tally.fallbacks += o["fallback"]
+    n_g, n_o = int(gpu["accepted"]), o["n"]
+    if "p_logZ" in gpu:
+        _close(gpu["p_logZ"][:L + 1], o["logZp"], TOL_LOGZ, 0.0, f"{what} p_logZ")
+        if L:
+            _close(gpu["q_logZ"][:L], o["logZq"], TOL_LOGZ, 0.0, f"{what} q_logZ")
+            _close(gpu["accept_prob"][:L], o["accept_prob"], 1e-7, TOL_REL, f"{what} accept_prob")
+    out_g = np.asarray(gpu["out_tokens"])
+    if n_g != n_o:
+        k = min(n_g, n_o)
+        tally.draws += 1
+        if T == 0 or not (o["test_margin"][k] <= BAND):
+            raise AssertionError(f"{what}: accepted {n_g} != oracle {n_o}; ratio-test margin at "
+                                 f"position {k} is {o['test_margin'][k]:.3e}")
+        tally.boundary += 1
+        return False
+    if not np.array_equal(out_g[:n_o], np.asarray(draft[:n_o])):
+        raise AssertionError(f"{what}: emitted draft tokens differ")
+    if np.any(out_g[n_o + 1:] != -1):
+        raise AssertionError(f"{what}: slots after the final token must be -1")
+    tally.draws += 1
+    final_g, final_o = int(out_g[n_o]), int(o["out"][n_o])
+    if final_g == final_o:
+        return True
+    if T == 0:
+        raise AssertionError(f"{what}: greedy final token {final_g} != oracle {final_o}")
+    logZp = o["logZp"][n_o]
+    if n_o < L and not o["fallback"]:
+        w, _ = orc.residual_weights(P[n_o], Q[n_o], T, logZp, o["logZq"][n_o])
+    else:
+        w, _, _ = orc.softmax_weights(P[n_o], T)
+    _check_draw(w, final_o, final_g, u_final, f"{what} final draw (n={n_o})")
+    tally.boundary += 1
+    return False

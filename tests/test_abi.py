@@ -1,0 +1,128 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function
+include/specdec.h declares, and rejects invalid arguments before any launch
+(these calls return during validation and never touch a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import draft_sampling_lossless_head_amd as sd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specdec.h")
+
+SPEC_OK, SPEC_ERR_INVALID, SPEC_ERR_UNSUPPORTED, SPEC_ERR_WORKSPACE = 0, 1, 2, 3
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spec_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sd.library_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    return sd.load_library()
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("spec_draft_sample_markov", "spec_draft_sample_rnn", "spec_verify",
+              "spec_draft_markov_workspace_size", "spec_draft_rnn_workspace_size",
+              "spec_verify_workspace_size", "spec_philox_uniforms", "spec_last_error",
+              "spec_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in _declared():
+        assert hasattr(lib, n), n
+    assert lib.spec_version() == 100
+
+
+def test_workspace_sizes(lib):
+    assert lib.spec_verify_workspace_size(0, 4, 100) == 0
+    a = lib.spec_draft_markov_workspace_size(128, 16, 151936, 256)
+    assert a > 0 and a % 256 == 0
+    assert lib.spec_draft_rnn_workspace_size(64, 8, 32000, 256, 4096) > \
+        lib.spec_draft_markov_workspace_size(64, 8, 32000, 256)
+
+
+def _markov(lib, **kw):
+    fake = ctypes.c_void_p(4096)   # never dereferenced: validation fails first
+    a = dict(U=fake, U_dtype=0, x0=fake, W1=fake, W2=fake, w_dtype=1, r=256, B=2, gamma=3,
+             V=1000, T=1.0, uniforms=None, seed=0, offset=0, tokens=fake, q_logits=fake,
+             q_logZ=None, q_tok=None, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return lib.spec_draft_sample_markov(*a.values())
+
+
+def test_markov_validation(lib):
+    assert _markov(lib, U=None) == SPEC_ERR_INVALID
+    assert _markov(lib, B=-1) == SPEC_ERR_INVALID
+    assert _markov(lib, V=0) == SPEC_ERR_INVALID
+    assert _markov(lib, r=0) == SPEC_ERR_INVALID
+    assert _markov(lib, T=-1.0) == SPEC_ERR_INVALID
+    assert _markov(lib, T=float("nan")) == SPEC_ERR_INVALID
+    assert _markov(lib, U_dtype=7) == SPEC_ERR_UNSUPPORTED
+    assert _markov(lib, r=40) == SPEC_ERR_UNSUPPORTED         # bf16 MFMA needs r % 16 == 0
+    assert _markov(lib, r=512) == SPEC_ERR_UNSUPPORTED
+    assert _markov(lib, W1=ctypes.c_void_p(4098)) == SPEC_ERR_UNSUPPORTED   # misaligned
+    assert _markov(lib) == SPEC_ERR_WORKSPACE                 # no workspace given
+    assert _markov(lib, ws=ctypes.c_void_p(4096 + 64), ws_bytes=1 << 30) == SPEC_ERR_WORKSPACE
+    assert _markov(lib, ws=ctypes.c_void_p(4096), ws_bytes=16) == SPEC_ERR_WORKSPACE
+    assert "workspace" in lib.spec_last_error().decode()
+    assert _markov(lib, B=0) == SPEC_OK                        # empty batch: nothing to do
+    assert _markov(lib, gamma=0) == SPEC_OK
+
+
+def _verify(lib, **kw):
+    fake = ctypes.c_void_p(4096)
+    a = dict(P=fake, p_dtype=1, Q=fake, q_dtype=0, draft=fake, lens=None, p_off=None, q_off=None,
+             B=2, G=3, V=1000, T=1.0, uniforms=None, seed=0, offset=0, accepted=fake, out=fake,
+             p_logZ=None, q_logZ=None, ap=None, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return lib.spec_verify(*a.values())
+
+
+def test_verify_validation(lib):
+    assert _verify(lib, P=None) == SPEC_ERR_INVALID
+    assert _verify(lib, Q=None) == SPEC_ERR_INVALID
+    assert _verify(lib, G=0, Q=None, draft=None) == SPEC_ERR_WORKSPACE   # bonus-only is valid
+    assert _verify(lib, G=-1) == SPEC_ERR_INVALID
+    assert _verify(lib, T=-0.5) == SPEC_ERR_INVALID
+    assert _verify(lib, q_dtype=3) == SPEC_ERR_UNSUPPORTED
+    assert _verify(lib, P=ctypes.c_void_p(4100)) == SPEC_ERR_UNSUPPORTED
+    assert _verify(lib) == SPEC_ERR_WORKSPACE
+    assert _verify(lib, B=0) == SPEC_OK
+
+
+def test_rnn_validation(lib):
+    fake = ctypes.c_void_p(4096)
+    base = dict(U=fake, U_dtype=0, x0=fake, h=fake, h_dtype=1, d=64, W1=fake, W2=fake, Wg=fake,
+                Wc=fake, Wo=fake, w_dtype=1, r=32, B=2, gamma=2, V=500, T=1.0, uniforms=None,
+                seed=0, offset=0, tokens=fake, q_logits=fake, q_logZ=None, q_tok=None, ws=None,
+                ws_bytes=0, stream=None)
+
+    def call(**kw):
+        a = dict(base)
+        a.update(kw)
+        return lib.spec_draft_sample_rnn(*a.values())
+
+    assert call(h=None) == SPEC_ERR_INVALID
+    assert call(d=-1) == SPEC_ERR_INVALID
+    assert call(d=12) == SPEC_ERR_UNSUPPORTED
+    assert call(w_dtype=0) == SPEC_ERR_UNSUPPORTED
+    assert call() == SPEC_ERR_WORKSPACE
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    import draft_sampling_lossless_head_amd.api as api
+    monkeypatch.setattr(api, "_lib", None)
+    monkeypatch.setattr(api, "_LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(api.SpecError):
+        api.load_library()
