@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Benchmark of one speculative cycle on one MI355X: DSpark Markov-head draft
+(gamma sequential positions for a batch of requests) followed by lossless
+verification of the drafted block.
+
+A step = spec_draft_sample_markov + spec_verify on one batch of seeded
+synthetic inputs already resident in HBM.  value = B * gamma * steps / time
+("verified+drafted tokens/s": every drafted token is also verified in the
+same step).  Prints ONE JSON line on stdout; progress goes to stderr.
+
+Roofline: every kernel of a step is timed in a second timed region with
+hipEvents that the library records on the launch stream; the dominant
+kernel's algorithmic bytes per launch divided by its average duration give
+`achieved`.  `traffic` comes from committed rocprofv3 counter summaries of
+that kernel when they were taken on the current kernel source.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified+drafted tokens/s at B=128,gamma=16,V=152k; % of HBM roofline"
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_bytes(wl):
+    """Algorithmic bytes per launch of each streaming kernel (every input read
+    once, every output written once; W2 counted once per draft call)."""
+    B, g, V, r = wl["B"], wl["gamma"], wl["V"], wl["r"]
+    lb = 2 if wl["logit_dtype"] == "bf16" else 4
+    wb = 2 if wl["w_dtype"] == "bf16" else 4
+    return {
+        # U_k read, q_k written, W2 / gamma, the B gathered W1 rows
+        "draft_tile": B * V * (lb + 4) + r * V * wb / g + B * r * wb,
+        "verify_rows_p": B * (g + 1) * V * lb,
+        "verify_rows_q": B * g * V * 4,
+    }
+
+
+def source_sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "draft_tile": ["draft_sampling_lossless_head_amd/csrc/draft_kernels.hip",
+                   "draft_sampling_lossless_head_amd/csrc/device_common.hpp"],
+    "verify_rows_p": ["draft_sampling_lossless_head_amd/csrc/verify_kernels.hip",
+                      "draft_sampling_lossless_head_amd/csrc/device_common.hpp"],
+    "verify_rows_q": ["draft_sampling_lossless_head_amd/csrc/verify_kernels.hip",
+                      "draft_sampling_lossless_head_amd/csrc/device_common.hpp"],
+}
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from profiles/<kernel>__<workload>.traffic.json,
+    or None when missing or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}__{workload}.traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_sha") != source_sha(KERNEL_SOURCES[kernel]):
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(wl, seed, nsample, threads):
+    """The fp64 oracle (as it stands) on the first nsample requests: draft then
+    verify of each request, requests spread over `threads` host threads."""
+    import concurrent.futures
+
+    import numpy as np
+
+    import oracle
+    import workloads
+
+    B, g = wl["B"], wl["gamma"]
+    lb, wbt = wl["logit_dtype"], wl["w_dtype"]
+    W1 = workloads.as_f64(wl["W1"], wbt)
+    W2 = workloads.as_f64(wl["W2"], wbt)
+    ud = oracle.draft_uniforms(seed, 0, nsample, g)
+    uv = oracle.verify_uniforms(seed, 0, nsample, g)
+    U = [workloads.as_f64(wl["U"][b], lb) for b in range(nsample)]
+    P = [workloads.as_f64(wl["P"][b], lb) for b in range(nsample)]
+    T = wl["T"]
+
+    def one(b):
+        d = oracle.draft_markov(U[b], W1, W2, int(wl["x0"][b]), T, ud[b])
+        v = oracle.verify(P[b], d["q_logits"], d["tokens"], T, uv[b, :g], uv[b, g])
+        return v["n"]
+
+    t0 = time.perf_counter()
+    with concurrent.futures.ThreadPoolExecutor(max_workers=threads) as ex:
+        ns = list(ex.map(one, range(nsample)))
+    dt = time.perf_counter() - t0
+    return dict(value=nsample * g / dt, unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"first {nsample} of {B} requests of the same workload (draft + verify, "
+                       f"fp64, {threads} threads), {dt:.2f} s wall",
+                mean_tau=float(np.mean(ns)) + 1.0)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="markov-152k-b128")
+    ap.add_argument("--sigma", type=float, default=None, help="override target/draft noise")
+    ap.add_argument("--cpu-sample", type=int, default=16, help="requests timed on the oracle")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one device copy of this size (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): the method's requests are "
+              "independent, so several GPUs would each run this same step on their own share of "
+              "the batch with no exchange; multi-GPU runs are not part of this build.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import draft_sampling_lossless_head_amd as sd
+    import workloads
+
+    cfg = dict(workloads.CONFIGS[args.workload])
+    if args.sigma is not None:
+        cfg["sigma"] = args.sigma
+    t0 = time.time()
+    wl = workloads.make_markov(cfg)
+    log(f"generated {args.workload} in {time.time() - t0:.1f}s")
+    B, g, V, r, T = wl["B"], wl["gamma"], wl["V"], wl["r"], wl["T"]
+    lb, wbt = wl["logit_dtype"], wl["w_dtype"]
+    dev = torch.device("cuda:0")
+
+    def to_dev(x, dt=None):
+        t = torch.from_numpy(np.ascontiguousarray(x))
+        if dt == "bf16":
+            t = t.view(torch.bfloat16)
+        return t.to(dev)
+
+    U, P = to_dev(wl["U"], lb), to_dev(wl["P"], lb)
+    W1, W2, x0 = to_dev(wl["W1"], wbt), to_dev(wl["W2"], wbt), to_dev(wl["x0"])
+    d_out = dict(tokens=torch.empty((B, g), dtype=torch.int32, device=dev),
+                 q_logits=torch.empty((B, g, V), dtype=torch.float32, device=dev),
+                 q_logZ=torch.empty((B, g), dtype=torch.float32, device=dev),
+                 q_tok_prob=torch.empty((B, g), dtype=torch.float32, device=dev))
+    v_out = dict(accepted=torch.empty(B, dtype=torch.int32, device=dev),
+                 out_tokens=torch.empty((B, g + 1), dtype=torch.int32, device=dev))
+    ws_d = torch.empty(sd.workspace_bytes("markov", B=B, gamma=g, V=V, r=r), dtype=torch.uint8,
+                       device=dev)
+    ws_v = torch.empty(sd.workspace_bytes("verify", B=B, gamma_max=g, V=V), dtype=torch.uint8,
+                       device=dev)
+    seed = 0
+
+    def step(i):
+        sd.spec_draft_sample_markov(U, x0, W1, W2, T, seed=seed, offset=i, out=d_out,
+                                    workspace=ws_d)
+        sd.spec_verify(P, d_out["q_logits"], d_out["tokens"], T, seed=seed, offset=i,
+                       out=v_out, workspace=ws_v)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = B * g * args.steps / elapsed
+    tau = float(v_out["accepted"].float().mean().item()) + 1.0
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step, {value / 1e6:.3f} M tok/s, "
+        f"mean tau {tau:.3f}")
+
+    # Second timed region: the same steps with every kernel bracketed by events.
+    sd.spec_profile_enable("*")
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    prof_ms_per_step = (time.perf_counter() - t1) * 1e3 / args.steps
+    sd.spec_profile_enable(None)
+    kernels = {}
+    names = ["w2_transpose", "draft_tile", "draft_finalize", "verify_rows_p", "verify_rows_q", "verify_decide",
+             "verify_final_partials", "verify_final_draw"]
+    for name in names:
+        sd.spec_profile_enable(name)
+        for i in range(args.steps):
+            step(args.warmup + i)
+        n, ms = sd.spec_profile_read()
+        sd.spec_profile_enable(None)
+        if n:
+            kernels[name] = dict(launches_per_step=n / args.steps, avg_us=ms * 1e3 / n,
+                                 us_per_step=ms * 1e3 / args.steps)
+    nbytes = kernel_bytes(wl)
+    for name, kb in nbytes.items():
+        if name in kernels:
+            kernels[name]["alg_bytes_per_launch"] = kb
+            kernels[name]["achieved_GBs"] = kb / (kernels[name]["avg_us"] * 1e-6) / 1e9
+    dom = max((k for k in kernels if k in nbytes), key=lambda k: kernels[k]["us_per_step"])
+    ach = kernels[dom]["achieved_GBs"]
+    roofline = dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(ach / HBM_PEAK_GBS, 4),
+                    traffic=measured_traffic(dom, args.workload), kernel=dom,
+                    alg_bytes_per_launch=nbytes[dom],
+                    avg_launch_us=round(kernels[dom]["avg_us"], 2))
+    log("kernels: " + json.dumps({k: {a: round(b, 2) for a, b in v.items()}
+                                  for k, v in kernels.items()}))
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded Zipf+Gaussian logits, random-init weights)",
+        "config": {"workload": args.workload, "B": B, "gamma": g, "V": V, "r": r,
+                   "logits": lb, "weights": wbt, "accumulate": "fp32", "T": T,
+                   "sigma": float(wl["sigma"][0]), "head": "markov",
+                   "verify": "fixed-length"},
+        "roofline": roofline,
+        "breakdown": {
+            "drafted_per_s": None, "verified_per_s": None,
+            "mean_tau": round(tau, 4),
+            "emitted_per_s": round(tau * B * args.steps / elapsed, 1),
+            "profiled_ms_per_step": round(prof_ms_per_step, 4),
+            "kernels": {k: {a: round(b, 3) for a, b in v.items()} for k, v in kernels.items()},
+        },
+    }
+    tdraft = sum(kernels[k]["us_per_step"] for k in ("w2_transpose", "draft_tile", "draft_finalize")
+                 if k in kernels)
+    tver = sum(kernels[k]["us_per_step"] for k in kernels if k.startswith("verify"))
+    if tdraft > 0:
+        result["breakdown"]["drafted_per_s"] = round(B * g / (tdraft * 1e-6), 1)
+    if tver > 0:
+        result["breakdown"]["verified_per_s"] = round(B * g / (tver * 1e-6), 1)
+
+    if not args.no_cpu_baseline:
+        threads = min(args.cpu_sample, len(os.sched_getaffinity(0)), 16)
+        log(f"oracle baseline on {args.cpu_sample} requests, {threads} threads ...")
+        result["cpu_baseline"] = cpu_baseline(wl, seed, min(args.cpu_sample, B), threads)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

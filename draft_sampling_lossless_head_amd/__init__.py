@@ -14,6 +14,8 @@ from .api import (  # noqa: F401
     spec_draft_sample_markov,
     spec_draft_sample_rnn,
     spec_philox_uniforms,
+    spec_profile_enable,
+    spec_profile_read,
     spec_verify,
     spec_version,
     workspace_bytes,

@@ -57,6 +57,10 @@ def load_library():
     lib.spec_verify.argtypes = [vp, i32, vp, i32, vp, vp, vp, vp, i32, i32, i32, f32, vp, u64,
                                 u32, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.spec_verify.restype = i32
+    lib.spec_profile_enable.argtypes = [ctypes.c_char_p]
+    lib.spec_profile_enable.restype = i32
+    lib.spec_profile_read.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_double)]
+    lib.spec_profile_read.restype = i32
     _lib = lib
     return lib
 
@@ -233,3 +237,18 @@ def spec_verify(P, Q, draft, T=1.0, *, gamma_max=None, lens=None, p_row_off=None
         nws, _stream(stream))
     _check(st, "spec_verify")
     return out
+
+
+def spec_profile_enable(kernel):
+    """Start timing every launch of `kernel` ("*" = all, None = stop)."""
+    lib = load_library()
+    _check(lib.spec_profile_enable(None if kernel is None else kernel.encode()),
+           "spec_profile_enable")
+
+
+def spec_profile_read():
+    """(launches, total milliseconds) of the kernel being timed."""
+    lib = load_library()
+    n, ms = ctypes.c_int(), ctypes.c_double()
+    _check(lib.spec_profile_read(ctypes.byref(n), ctypes.byref(ms)), "spec_profile_read")
+    return n.value, ms.value

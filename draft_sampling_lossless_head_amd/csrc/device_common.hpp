@@ -117,4 +117,43 @@ __device__ __forceinline__ double wave_inclusive_scan_f64(double x) {
     return x;
 }
 
+// Reductions across the 16 lanes of a DPP row (lanes 16i .. 16i+15): xor-1 and
+// xor-2 quad permutes, then the half-row and row mirrors; every lane of the
+// row ends with the result.
+template <int CTRL>
+__device__ __forceinline__ int dpp_mov(int x) {
+    return __builtin_amdgcn_mov_dpp(x, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- 7 - i within each 8 lanes
+constexpr int kDppMirror = 0x140;     // lane i <- 15 - i within each 16 lanes
+
+__device__ __forceinline__ float row16_max(float x) {
+    x = fmaxf(x, dpp_mov<kDppXor1>(x));
+    x = fmaxf(x, dpp_mov<kDppXor2>(x));
+    x = fmaxf(x, dpp_mov<kDppHalfMirror>(x));
+    return fmaxf(x, dpp_mov<kDppMirror>(x));
+}
+
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp_mov<kDppXor1>(x);
+    x += dpp_mov<kDppXor2>(x);
+    x += dpp_mov<kDppHalfMirror>(x);
+    return x + dpp_mov<kDppMirror>(x);
+}
+
+__device__ __forceinline__ int row16_min(int x) {
+    x = min(x, dpp_mov<kDppXor1>(x));
+    x = min(x, dpp_mov<kDppXor2>(x));
+    x = min(x, dpp_mov<kDppHalfMirror>(x));
+    return min(x, dpp_mov<kDppMirror>(x));
+}
+
 }  // namespace specdec

@@ -16,6 +16,7 @@
 // The RNN head adds rnn_hidden_proj (the h_k part of W_g, W_c, W_o for all
 // positions at once, bf16 MFMA) and rnn_gates (per position: the s_{k-1} and
 // W1[x_{k-1}] parts, the gated state update and o = tanh(W_o z_k)).
+#include <algorithm>
 #include <climits>
 
 #include "device_common.hpp"
@@ -52,87 +53,122 @@ __device__ __forceinline__ float load1(const void* base, size_t i) {
 // ---------------------------------------------------------------------------
 // bf16 MFMA bias tile.
 //
-// Workgroup = 4 waves.  WB waves split the request rows (32 rows each), the
-// other 4/WB split the 128 columns, so each wave owns MB = WB blocks of 32
-// columns.  The MFMA computes C[v][b] = sum_j W2[j][v] * E[b][j]:
-//   A operand (32 v x 16 j) from the transposed W2 tile in LDS,
-//   B operand (16 j x 32 b) straight from the E rows held in registers.
-// Lane l then owns request row b = l % 32 and, per 32-column block, the 16
-// columns 8*(i/4) + 4*(l/32) + i%4 (i = 0..15), i.e. four runs of four
-// consecutive tokens: the epilogue adds U and stores q with 16-byte accesses,
-// and the per-row reduction over v is lane-local plus one exchange.
+// Workgroup = 4 waves on one 128-token tile and Rt = 32*WB request rows.  WB
+// waves split the rows (32 each), the other 4/WB split the columns, so each
+// wave owns MB = WB blocks of 32 columns.  The MFMA computes
+// C[v][b] = sum_j W2[j][v] * E[b][j]:
+//   A operand (32 v x 16 j) from the W2 tile transposed into LDS,
+//   B operand (16 j x 32 b) from the E rows held in registers.
+// The accumulators are then written back into the same LDS as an [Rt][128]
+// fp32 tile, and the epilogue walks it row-contiguously: 16 lanes per request
+// row, 8 tokens per lane, U prefetched at kernel start, q stored with
+// nontemporal 16-byte stores, and the row summary reduced over the 16 lanes.
+// Row-contiguous access matters: with the MFMA lane layout each store
+// instruction would touch 32 request rows 16 bytes at a time.
 // ---------------------------------------------------------------------------
+constexpr int kOutLd = kTileV + 4;   // fp32 row stride of the staged output tile
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// W2 [r, V] -> W2T [V, r] (bf16), once per draft call: each bias tile then
+// stages one contiguous block of W2T.  64 x 64 tiles through LDS.
+__global__ __launch_bounds__(256)
+void w2_transpose(const uint16_t* __restrict__ W2, uint16_t* __restrict__ W2T, int r, int V) {
+    __shared__ uint16_t t[64][64 + 2];
+    const int v0 = blockIdx.x * 64;
+    const int j0 = blockIdx.y * 64;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int e = tid + i * 256;
+        const int jj = e / 64, vv = e % 64;
+        const int j = j0 + jj, v = v0 + vv;
+        t[jj][vv] = (j < r && v < V) ? W2[(size_t)j * V + v] : (uint16_t)0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int e = tid + i * 256;
+        const int vv = e / 64, jj = e % 64;
+        const int j = j0 + jj, v = v0 + vv;
+        if (j < r && v < V) W2T[(size_t)v * r + j] = t[jj][vv];
+    }
+}
+
+// Workgroup = 4 waves on one 128-token tile and RT = 32*WB request rows.
 template <int WB, int MODE, bool U_BF16>
 __global__ __launch_bounds__(256, 2)
 void draft_tile_mfma(const void* __restrict__ U, const uint16_t* __restrict__ W1,
-                     const uint16_t* __restrict__ W2, const uint16_t* __restrict__ Erows,
+                     const uint16_t* __restrict__ W2T, const uint16_t* __restrict__ Erows,
                      const int32_t* __restrict__ x0, const int32_t* __restrict__ tokens,
                      float* __restrict__ q_logits, SegStat* __restrict__ stats,
                      int B, int gamma, int V, int r, int k, float invT, int greedy) {
     constexpr int MB = WB;
-    constexpr int WV = 4 / WB;
     constexpr int NS = (MODE == kHeadRnn) ? 3 : 1;
-    extern __shared__ __align__(16) uint16_t w2t[];   // [kTileV][r + kLdsPad]
+    constexpr int RT = 32 * WB;            // request rows of the tile
+    constexpr int ITEMS = RT * 16 / 256;   // (row, 8-token group) items per thread
+    constexpr int UV = U_BF16 ? 1 : 2;     // 16-byte vectors per 8 tokens of U
+    extern __shared__ __align__(16) uint16_t smem[];
     const int ldr = r + kLdsPad;
+    uint16_t* w2t = smem;                                   // [kTileV][ldr] bf16
+    float* otile = reinterpret_cast<float*>(smem);          // [RT][kOutLd] fp32 (reused)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wb = wave % WB;
     const int wv = wave / WB;
     const int v_tile = blockIdx.x * kTileV;
-    const int b = blockIdx.y * (32 * WB) + wb * 32 + (lane & 31);
+    const int row0 = blockIdx.y * RT;
+    const int b = row0 + wb * 32 + (lane & 31);
     const bool brow = b < B;
     const int kgrp = lane >> 5;
+    const int nks = r / 16;
+    const bool vec_u = U_BF16 ? (V % 8) == 0 : (V % 4) == 0;
 
-    // 1) W2[:, tile] -> LDS, transposed to [v][j] in 8x8 register blocks.
-    {
-        const int nblk = (r / 8) * (kTileV / 8);
-        const bool vec_ok = (V % 8) == 0;
-        for (int blk = tid; blk < nblk; blk += 256) {
-            const int vb = blk % (kTileV / 8);
-            const int jb = blk / (kTileV / 8);
-            const int v0 = v_tile + vb * 8;
-            const int j0 = jb * 8;
-            uint32_t w[8][4];
-            if (vec_ok && v0 + 8 <= V) {
+    // 1) the W2T tile: kTileV rows of r contiguous bf16, 16 bytes per chunk.
+    const int cpr = r / 8;                       // chunks per W2T row
+    const int nchunk = kTileV * cpr;             // <= 4096
+    uint4 wch[16];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const uint4 t = *reinterpret_cast<const uint4*>(W2 + (size_t)(j0 + i) * V + v0);
-                    w[i][0] = t.x; w[i][1] = t.y; w[i][2] = t.z; w[i][3] = t.w;
-                }
-            } else {
+    for (int i = 0; i < 16; ++i) {
+        const int c = tid + i * 256;
+        const int vr = c / cpr;
+        wch[i] = make_uint4(0u, 0u, 0u, 0u);
+        if (c < nchunk && v_tile + vr < V)
+            wch[i] = *reinterpret_cast<const uint4*>(W2T + (size_t)(v_tile + vr) * r + (c % cpr) * 8);
+    }
+
+    // 2) prefetch this thread's U items (row-contiguous epilogue mapping).
+    u32x4_t ureg[ITEMS][UV];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
+    for (int it = 0; it < ITEMS; ++it) {
+        const int item = tid + it * 256;
+        const int br = row0 + item / 16;
+        const int v0 = v_tile + (item % 16) * 8;
 #pragma unroll
-                    for (int h = 0; h < 4; ++h) {
-                        const int va = v0 + 2 * h;
-                        const uint32_t lo = va < V ? W2[(size_t)(j0 + i) * V + va] : 0u;
-                        const uint32_t hi = va + 1 < V ? W2[(size_t)(j0 + i) * V + va + 1] : 0u;
-                        w[i][h] = lo | (hi << 16);
-                    }
-                }
-            }
+        for (int h = 0; h < UV; ++h) ureg[it][h] = u32x4_t{0u, 0u, 0u, 0u};
+        if (br < B && vec_u && v0 + 8 <= V) {
+            const size_t off = ((size_t)br * gamma + k) * (size_t)V + v0;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                uint32_t o[4];
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const uint32_t a = w[2 * p][e >> 1];
-                    const uint32_t c = w[2 * p + 1][e >> 1];
-                    o[p] = (e & 1) ? ((a >> 16) | (c & 0xFFFF0000u)) : ((a & 0xFFFFu) | (c << 16));
-                }
-                *reinterpret_cast<uint4*>(w2t + (vb * 8 + e) * ldr + j0) =
-                    make_uint4(o[0], o[1], o[2], o[3]);
-            }
+            for (int h = 0; h < UV; ++h)
+                ureg[it][h] = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4_t*>(static_cast<const char*>(U) +
+                                                     off * (U_BF16 ? 2 : 4)) + h);
         }
     }
 
-    // 2) conditioning rows and the contraction.
+    // 3) conditioning rows (Markov: W1[x_{k-1}]; RNN: split o rows).
     int prev = 0;
     bool erow_ok = brow;
     if (MODE == kHeadMarkov && brow) {
         prev = (k == 0) ? x0[b] : tokens[(size_t)b * gamma + k - 1];
         erow_ok = prev >= 0 && prev < V;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int c = tid + i * 256;
+        if (c < nchunk) *reinterpret_cast<uint4*>(w2t + (c / cpr) * ldr + (c % cpr) * 8) = wch[i];
     }
     f32x16_t acc[MB];
 #pragma unroll
@@ -141,12 +177,12 @@ void draft_tile_mfma(const void* __restrict__ U, const uint16_t* __restrict__ W1
         for (int i = 0; i < 16; ++i) acc[mb][i] = 0.0f;
     __syncthreads();
 
-    const int nks = r / 16;
+    // 4) the contraction (RNN: three bf16 terms of o against the same tile).
 #pragma unroll
     for (int split = 0; split < NS; ++split) {
         const uint16_t* erow = (MODE == kHeadMarkov)
                                    ? W1 + (size_t)prev * r
-                                   : Erows + ((size_t)b * 3 + split) * r;
+                                   : Erows + ((size_t)(brow ? b : 0) * 3 + split) * r;
         bf16x8_t e[16];
 #pragma unroll
         for (int ks = 0; ks < 16; ++ks) {
@@ -173,64 +209,88 @@ void draft_tile_mfma(const void* __restrict__ U, const uint16_t* __restrict__ W1
         }
     }
 
-    // 3) l = U + bias, store q, per-lane max / argmax.
-    const size_t rowoff = ((size_t)(brow ? b : 0) * gamma + k) * (size_t)V;
-    const bool vec_io = (V % 4) == 0;
-    float m = -INFINITY;
-    int amax = INT_MAX;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int v4 = v_tile + wv * (32 * MB) + mb * 32 + g * 8 + kgrp * 4;
-            float u4[4];
-            if (brow && vec_io && v4 + 3 < V) {
-                load4<U_BF16>(U, rowoff + v4, u4);
-#pragma unroll
-                for (int t = 0; t < 4; ++t) acc[mb][4 * g + t] += u4[t];
-                *reinterpret_cast<float4*>(q_logits + rowoff + v4) =
-                    make_float4(acc[mb][4 * g], acc[mb][4 * g + 1], acc[mb][4 * g + 2],
-                                acc[mb][4 * g + 3]);
-            } else {
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    if (brow && v4 + t < V) {
-                        acc[mb][4 * g + t] += load1<U_BF16>(U, rowoff + v4 + t);
-                        q_logits[rowoff + v4 + t] = acc[mb][4 * g + t];
-                    } else {
-                        acc[mb][4 * g + t] = -INFINITY;
-                    }
-                }
-            }
-#pragma unroll
-            for (int t = 0; t < 4; ++t) merge_arg(m, amax, acc[mb][4 * g + t], v4 + t);
-        }
-    }
-    float s = 0.0f;
-    if (!greedy && m != -INFINITY) {
+    // 5) accumulators -> LDS as an [RT][128] fp32 tile (row = request).
+    __syncthreads();
+    {
+        const int rl = wb * 32 + (lane & 31);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) s += __expf((acc[mb][i] - m) * invT);
+            for (int g = 0; g < 4; ++g) {
+                const int c = wv * (32 * MB) + mb * 32 + g * 8 + kgrp * 4;
+                *reinterpret_cast<float4*>(otile + rl * kOutLd + c) =
+                    make_float4(acc[mb][4 * g], acc[mb][4 * g + 1], acc[mb][4 * g + 2],
+                                acc[mb][4 * g + 3]);
+            }
     }
-    {
-        const float m2 = __shfl_xor(m, 32);
-        const float s2 = __shfl_xor(s, 32);
-        const int i2 = __shfl_xor(amax, 32);
-        float mv = m;
-        int iv = amax;
-        merge_arg(mv, iv, m2, i2);
-        merge_ms(m, s, m2, s2, invT);
-        amax = iv;
-    }
-    if (brow && lane < 32) {
-        const int nseg = gridDim.x * WV;
-        SegStat st;
-        st.m = m;
-        st.s = s;
-        st.idx = amax;
-        st.pad = 0;
-        stats[(size_t)b * nseg + blockIdx.x * WV + wv] = st;
+    __syncthreads();
+
+    // 6) row-contiguous epilogue: l = U + bias, store q, and the row summary
+    //    of the tile (max, sum exp((l - max)/T), lowest argmax) reduced over
+    //    the row's 16 lanes with DPP moves.
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+        const int item = tid + it * 256;
+        const int rl = item / 16;
+        const int br = row0 + rl;
+        const int v0 = v_tile + (item % 16) * 8;
+        const float4 b0 = *reinterpret_cast<const float4*>(otile + rl * kOutLd + (item % 16) * 8);
+        const float4 b1 = *reinterpret_cast<const float4*>(otile + rl * kOutLd + (item % 16) * 8 + 4);
+        float x[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+        const bool rowok = br < B;
+        const size_t off = ((size_t)(rowok ? br : 0) * gamma + k) * (size_t)V + v0;
+        if (rowok && vec_u && v0 + 8 <= V) {
+            if constexpr (U_BF16) {
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    x[2 * h] += bf16_bits_to_float(ureg[it][0][h] & 0xFFFFu);
+                    x[2 * h + 1] += bf16_bits_to_float(ureg[it][0][h] >> 16);
+                }
+            } else {
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    x[h] += __uint_as_float(ureg[it][0][h]);
+                    x[4 + h] += __uint_as_float(ureg[it][UV - 1][h]);
+                }
+            }
+            f32x4_t o0 = {x[0], x[1], x[2], x[3]};
+            f32x4_t o1 = {x[4], x[5], x[6], x[7]};
+            __builtin_nontemporal_store(o0, reinterpret_cast<f32x4_t*>(q_logits + off));
+            __builtin_nontemporal_store(o1, reinterpret_cast<f32x4_t*>(q_logits + off) + 1);
+        } else {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                if (rowok && v0 + t < V) {
+                    x[t] += load1<U_BF16>(U, off + t);
+                    q_logits[off + t] = x[t];
+                } else {
+                    x[t] = -INFINITY;
+                }
+            }
+        }
+        float m = x[0];
+#pragma unroll
+        for (int t = 1; t < 8; ++t) m = fmaxf(m, x[t]);
+        m = row16_max(m);
+        float sum = 0.0f;
+        if (!greedy && m != -INFINITY) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) sum += __expf((x[t] - m) * invT);
+        }
+        sum = row16_sum(sum);
+        int amax = INT_MAX;
+#pragma unroll
+        for (int t = 7; t >= 0; --t)
+            if (x[t] == m) amax = v0 + t;
+        amax = row16_min(amax);
+        if (rowok && (item % 16) == 0) {
+            SegStat st;
+            st.m = m;
+            st.s = sum;
+            st.idx = amax;
+            st.pad = 0;
+            stats[(size_t)br * gridDim.x + blockIdx.x] = st;
+        }
     }
 }
 
@@ -295,24 +355,31 @@ void draft_tile_valu_f32w(const void* __restrict__ U, const float* __restrict__ 
 
 // ---------------------------------------------------------------------------
 // Per-row finalize: normaliser, inverse-CDF draw, outputs of position k.
+// One workgroup (4 waves) per request row.  Thread t owns a contiguous run of
+// about nseg/256 segment summaries; the fp64 run weights are scanned in token
+// order (wave scans, then the four wave totals), the thread whose run holds
+// u * Z walks it to the segment, and wave 0 rescans that segment's logits.
 // ---------------------------------------------------------------------------
+constexpr int kFinRun = 8;   // max summaries per thread (nseg <= 2048)
+
 __global__ __launch_bounds__(256)
 void draft_finalize(const SegStat* __restrict__ stats, int nseg, int seg_len,
                     const float* __restrict__ q_logits, const int32_t* __restrict__ x0,
                     int32_t* __restrict__ tokens, float* __restrict__ q_logZ,
                     float* __restrict__ q_tok, const float* __restrict__ uniforms,
-                    uint64_t seed, uint32_t offset, int gamma, int V, int k, float invT,
+                    uint64_t seed, uint32_t offset, int B, int gamma, int V, int k, float invT,
                     int greedy) {
-    __shared__ double scan[256];
-    __shared__ float red_m[4];
-    __shared__ int red_i[4];
-    __shared__ int sh_seg;
+    __shared__ float sh_m[4];
+    __shared__ int sh_i[4];
+    __shared__ double sh_tot[4];
+    __shared__ int sh_seg, sh_owner_last;
     __shared__ double sh_rem;
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const size_t outi = (size_t)b * gamma + k;
+    (void)B;
 
     const int prev = (k == 0) ? x0[b] : tokens[outi - 1];
     if (prev < 0 || prev >= V) {
@@ -324,14 +391,30 @@ void draft_finalize(const SegStat* __restrict__ stats, int nseg, int seg_len,
         return;
     }
     const SegStat* st = stats + (size_t)b * nseg;
+    const int per = (nseg + 255) / 256;
+    const int j0 = min(nseg, tid * per);
+    const int n = min(nseg, j0 + per) - j0;
+    float sm[kFinRun], ss[kFinRun];
+    int si[kFinRun];
+#pragma unroll
+    for (int t = 0; t < kFinRun; ++t) {
+        if (t < n) {
+            const SegStat x = st[j0 + t];
+            sm[t] = x.m;
+            ss[t] = x.s;
+            si[t] = x.idx;
+        } else {
+            sm[t] = -INFINITY;
+            ss[t] = 0.0f;
+            si[t] = INT_MAX;
+        }
+    }
 
-    // 1) row max and argmax over the segment summaries.
+    // 1) row max and argmax.
     float M = -INFINITY;
     int AM = INT_MAX;
-    for (int j = tid; j < nseg; j += 256) {
-        const SegStat t = st[j];
-        merge_arg(M, AM, t.m, t.idx);
-    }
+#pragma unroll
+    for (int t = 0; t < kFinRun; ++t) merge_arg(M, AM, sm[t], si[t]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
         const float m2 = __shfl_xor(M, off);
@@ -339,14 +422,14 @@ void draft_finalize(const SegStat* __restrict__ stats, int nseg, int seg_len,
         merge_arg(M, AM, m2, i2);
     }
     if (lane == 0) {
-        red_m[wave] = M;
-        red_i[wave] = AM;
+        sh_m[wave] = M;
+        sh_i[wave] = AM;
     }
     __syncthreads();
-    M = red_m[0];
-    AM = red_i[0];
-    for (int w = 1; w < 4; ++w) merge_arg(M, AM, red_m[w], red_i[w]);
-
+    M = sh_m[0];
+    AM = sh_i[0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) merge_arg(M, AM, sh_m[w], sh_i[w]);
     if (greedy || M == -INFINITY) {
         if (tid == 0) {
             tokens[outi] = (M == -INFINITY) ? -1 : AM;
@@ -356,114 +439,104 @@ void draft_finalize(const SegStat* __restrict__ stats, int nseg, int seg_len,
         return;
     }
 
-    // 2) fp64 sums of the segment summaries, contiguous chunk per thread,
-    //    then an exclusive scan across threads (segment order = token order).
-    const int per = (nseg + 255) / 256;
-    const int j0 = min(nseg, tid * per);
-    const int j1 = min(nseg, j0 + per);
-    const double Md = (double)M;
+    // 2) run weights (fp64) and their scan in token order.
+    double wr[kFinRun];
     double tsum = 0.0;
-    for (int j = j0; j < j1; ++j) {
-        const SegStat t = st[j];
-        if (t.m != -INFINITY) tsum += (double)t.s * exp(((double)t.m - Md) * (double)invT);
+#pragma unroll
+    for (int t = 0; t < kFinRun; ++t) {
+        wr[t] = sm[t] != -INFINITY ? (double)ss[t] * (double)expf((sm[t] - M) * invT) : 0.0;
+        tsum += wr[t];
     }
-    scan[tid] = tsum;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-        const double add = tid >= off ? scan[tid - off] : 0.0;
-        __syncthreads();
-        scan[tid] += add;
-        __syncthreads();
+    // Neighbouring intervals share exact end points (the previous lane's
+    // inclusive value), so [excl, incl) tile [0, Z) without gaps.
+    const double incl_w = wave_inclusive_scan_f64(tsum);
+    double excl_w = __shfl_up(incl_w, 1);
+    if (lane == 0) excl_w = 0.0;
+    if (lane == kWave - 1) sh_tot[wave] = incl_w;
+    if (tid == 0) {
+        sh_seg = -1;
+        sh_owner_last = -1;
     }
-    const double incl = scan[tid];
-    const double excl = tid > 0 ? scan[tid - 1] : 0.0;
-    const double Z = scan[255];
-    if (tid == 0) sh_seg = -1;
     __syncthreads();
-
+    double base = 0.0;
+    for (int w = 0; w < wave; ++w) base += sh_tot[w];
+    double Z = 0.0;
+    for (int w = 0; w < 4; ++w) Z += sh_tot[w];
+    const double incl = base + incl_w;
+    const double excl = base + excl_w;
     const float u = uniforms ? uniforms[outi] : counter_uniform(seed, offset, b, k, 0);
     const double thr = (double)u * Z;
 
-    // 3) locate the segment holding thr.
+    // 3) the owning thread walks its run.
     if (tsum > 0.0 && thr >= excl && thr < incl) {
         double run = excl;
-        int found = -1, last = -1;
-        double last_run = 0.0, last_w = 0.0;
-        for (int j = j0; j < j1; ++j) {
-            const SegStat t = st[j];
-            const double w = t.m != -INFINITY ? (double)t.s * exp(((double)t.m - Md) * (double)invT) : 0.0;
-            if (w > 0.0) {
-                last = j;
+        int seg = -1, last = -1;
+        double rem = 0.0, last_run = 0.0;
+#pragma unroll
+        for (int t = 0; t < kFinRun; ++t) {
+            if (seg < 0 && wr[t] > 0.0) {
+                last = j0 + t;
                 last_run = run;
-                last_w = w;
-                if (thr < run + w) {
-                    found = j;
-                    break;
+                if (thr < run + wr[t]) {
+                    seg = j0 + t;
+                    rem = thr - run;
                 }
             }
-            run += w;
+            run += wr[t];
         }
-        if (found >= 0) {
-            sh_seg = found;
-            sh_rem = thr - run;
-        } else {
-            // rounding left thr past this chunk's own running sum: clamp
-            // to the end of its last segment with weight.
-            sh_seg = last;
-            sh_rem = thr - last_run;
-            (void)last_w;
+        if (seg < 0) {   // rounding: end of the last segment with weight
+            seg = last;
+            rem = thr - last_run;
         }
+        sh_seg = seg;
+        sh_rem = rem;
+    }
+    if (tsum > 0.0) atomicMax(&sh_owner_last, tid);
+    __syncthreads();
+    if (sh_seg < 0 && tid == sh_owner_last) {
+        // thr >= Z after rounding: clamp to the last segment with weight
+        int last = -1;
+#pragma unroll
+        for (int t = 0; t < kFinRun; ++t)
+            if (wr[t] > 0.0) last = j0 + t;
+        sh_seg = last;
+        sh_rem = INFINITY;
     }
     __syncthreads();
-    if (sh_seg < 0) {
-        // thr >= Z after rounding: clamp to the last segment with weight.
-        int lastj = -1;
-        for (int j = j0; j < j1; ++j)
-            if (st[j].m != -INFINITY && st[j].s > 0.0f) lastj = j;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) lastj = max(lastj, __shfl_xor(lastj, off));
-        if (lane == 0) red_i[wave] = lastj;
-        __syncthreads();
-        if (tid == 0) {
-            sh_seg = max(max(red_i[0], red_i[1]), max(red_i[2], red_i[3]));
-            sh_rem = INFINITY;
-        }
-        __syncthreads();
-    }
+    if (wave != 0) return;
 
-    // 4) rescan the chosen segment with one wave (2 tokens per lane).
-    if (wave == 0) {
-        const int seg = sh_seg;
-        const double rem = sh_rem;
-        const int v0 = seg * seg_len;
-        const int v1 = min(V, v0 + seg_len);
-        const float* row = q_logits + outi * (size_t)V;
-        const int va = v0 + 2 * lane;
-        const int vb = va + 1;
-        const double w0 = va < v1 ? exp(((double)row[va] - Md) * (double)invT) : 0.0;
-        const double w1 = vb < v1 ? exp(((double)row[vb] - Md) * (double)invT) : 0.0;
-        const double lsum = w0 + w1;
-        const double inc = wave_inclusive_scan_f64(lsum);
-        double exc = __shfl_up(inc, 1);
-        if (lane == 0) exc = 0.0;
-        const unsigned long long hit = __ballot(lsum > 0.0 && inc > rem);
-        int pick;
-        if (hit) {
-            const int L0 = __ffsll((long long)hit) - 1;
-            const int mine = (w0 > 0.0 && rem < exc + w0) ? va : vb;
-            pick = __shfl(mine, L0);
-        } else {
-            const unsigned long long pos = __ballot(lsum > 0.0);
-            const int L1 = 63 - __clzll((long long)pos);
-            const int mine = w1 > 0.0 ? vb : va;
-            pick = __shfl(mine, L1);
-        }
-        pick = max(v0, min(pick, v1 - 1));   // stays inside the rescanned segment
-        if (lane == 0) {
-            tokens[outi] = pick;
-            if (q_logZ) q_logZ[outi] = (float)(Md * (double)invT + log(Z));
-            if (q_tok) q_tok[outi] = (float)(exp(((double)row[pick] - Md) * (double)invT) / Z);
-        }
+    // 4) wave 0 rescans the segment (2 tokens per lane).
+    const int seg = sh_seg;
+    const double rem = sh_rem;
+    const double Md = (double)M;
+    const int v0 = seg * seg_len;
+    const int v1 = min(V, v0 + seg_len);
+    const float* row = q_logits + outi * (size_t)V;
+    const int va = v0 + 2 * lane;
+    const int vb = va + 1;
+    const double w0 = va < v1 ? exp(((double)row[va] - Md) * (double)invT) : 0.0;
+    const double w1 = vb < v1 ? exp(((double)row[vb] - Md) * (double)invT) : 0.0;
+    const double lsum = w0 + w1;
+    const double inc = wave_inclusive_scan_f64(lsum);
+    double exc = __shfl_up(inc, 1);
+    if (lane == 0) exc = 0.0;
+    const unsigned long long found = __ballot(lsum > 0.0 && inc > rem);
+    int pick;
+    if (found) {
+        const int L0 = __ffsll((long long)found) - 1;
+        const int mine = (w0 > 0.0 && rem < exc + w0) ? va : vb;
+        pick = __shfl(mine, L0);
+    } else {
+        const unsigned long long pos = __ballot(lsum > 0.0);
+        const int L1 = pos ? 63 - __clzll((long long)pos) : 0;
+        const int mine = w1 > 0.0 ? vb : va;
+        pick = __shfl(mine, L1);
+    }
+    pick = max(v0, min(pick, v1 - 1));   // stays inside the rescanned segment
+    if (lane == 0) {
+        tokens[outi] = pick;
+        if (q_logZ) q_logZ[outi] = (float)(Md * (double)invT + log(Z));
+        if (q_tok) q_tok[outi] = (float)(exp(((double)row[pick] - Md) * (double)invT) / Z);
     }
 }
 
@@ -586,39 +659,47 @@ void rnn_gates(const float* __restrict__ hproj, const uint16_t* __restrict__ Wg,
 static int pick_wb(int B) { return B <= 32 ? 1 : (B <= 64 ? 2 : 4); }
 
 int draft_num_segments(int B, int V, int w_bf16) {
-    const int nt = (V + kTileV - 1) / kTileV;
-    if (!w_bf16) return nt;
-    return nt * (4 / pick_wb(B));
+    (void)B;
+    (void)w_bf16;
+    return (V + kTileV - 1) / kTileV;
 }
 
 int draft_segment_len(int B, int w_bf16) {
-    if (!w_bf16) return kTileV;
-    return kTileV / (4 / pick_wb(B));
+    (void)B;
+    (void)w_bf16;
+    return kTileV;
 }
 
 template <int WB, int MODE>
 static hipError_t launch_tile_wb(const DraftArgs& a, int k, hipStream_t s) {
     const int nt = (a.V + kTileV - 1) / kTileV;
     dim3 grid(nt, (a.B + 32 * WB - 1) / (32 * WB));
-    const size_t lds = (size_t)kTileV * (a.r + kLdsPad) * sizeof(uint16_t);
+    const size_t lds = std::max((size_t)kTileV * (a.r + kLdsPad) * sizeof(uint16_t),
+                                (size_t)32 * WB * kOutLd * sizeof(float));
     // r = 256 needs 66 KB of LDS per workgroup (gfx950 has 160 KB per CU)
     static bool attr_set = false;
     if (!attr_set) {
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&draft_tile_mfma<WB, MODE, true>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&draft_tile_mfma<WB, MODE, true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&draft_tile_mfma<WB, MODE, false>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&draft_tile_mfma<WB, MODE, false>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         (void)hipGetLastError();
         attr_set = true;
     }
     if (a.u_bf16)
         hipLaunchKernelGGL((draft_tile_mfma<WB, MODE, true>), grid, dim3(256), lds, s, a.U,
-                           (const uint16_t*)a.W1, (const uint16_t*)a.W2, a.Erows, a.x0, a.tokens,
+                           (const uint16_t*)a.W1, a.W2T, a.Erows, a.x0, a.tokens,
                            a.q_logits, a.stats, a.B, a.gamma, a.V, a.r, k, a.invT, a.greedy);
     else
         hipLaunchKernelGGL((draft_tile_mfma<WB, MODE, false>), grid, dim3(256), lds, s, a.U,
-                           (const uint16_t*)a.W1, (const uint16_t*)a.W2, a.Erows, a.x0, a.tokens,
+                           (const uint16_t*)a.W1, a.W2T, a.Erows, a.x0, a.tokens,
                            a.q_logits, a.stats, a.B, a.gamma, a.V, a.r, k, a.invT, a.greedy);
+    return hipGetLastError();
+}
+
+hipError_t w2_transpose_launch(const DraftArgs& a, hipStream_t s) {
+    dim3 grid((a.V + 63) / 64, (a.r + 63) / 64);
+    hipLaunchKernelGGL(w2_transpose, grid, dim3(256), 0, s, (const uint16_t*)a.W2, a.W2T, a.r, a.V);
     return hipGetLastError();
 }
 
@@ -649,9 +730,9 @@ hipError_t draft_tile_launch(const DraftArgs& a, int k, hipStream_t s) {
 hipError_t draft_finalize_launch(const DraftArgs& a, int k, hipStream_t s) {
     const int nseg = draft_num_segments(a.B, a.V, a.w_bf16);
     const int seg = draft_segment_len(a.B, a.w_bf16);
-    hipLaunchKernelGGL(draft_finalize, dim3(a.B), dim3(256), 0, s, a.stats, nseg, seg, a.q_logits,
-                       a.x0, a.tokens, a.q_logZ, a.q_tok, a.uniforms, a.seed, a.offset, a.gamma,
-                       a.V, k, a.invT, a.greedy);
+    hipLaunchKernelGGL(draft_finalize, dim3(a.B), dim3(256), 0, s, a.stats, nseg, seg,
+                       a.q_logits, a.x0, a.tokens, a.q_logZ, a.q_tok, a.uniforms, a.seed, a.offset,
+                       a.B, a.gamma, a.V, k, a.invT, a.greedy);
     return hipGetLastError();
 }
 

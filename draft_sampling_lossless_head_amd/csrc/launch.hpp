@@ -39,12 +39,14 @@ struct DraftArgs {
     float* hproj;        // RNN: [B * gamma, 3r]
     float* state;        // RNN: [2, B, r]
     uint16_t* Erows;     // RNN: [B, 3, r]
+    uint16_t* W2T;       // bf16 weights: [V, r] transposed copy of W2
 };
 
 int draft_num_segments(int B, int V, int w_bf16);
 int draft_segment_len(int B, int w_bf16);
 hipError_t draft_tile_launch(const DraftArgs& a, int k, hipStream_t s);
 hipError_t draft_finalize_launch(const DraftArgs& a, int k, hipStream_t s);
+hipError_t w2_transpose_launch(const DraftArgs& a, hipStream_t s);
 hipError_t rnn_hidden_proj_launch(const DraftArgs& a, hipStream_t s);
 hipError_t rnn_gates_launch(const DraftArgs& a, int k, hipStream_t s);
 

@@ -6,6 +6,7 @@
 
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "profile.hpp"
 #include "specdec.h"
 
 using namespace specdec;
@@ -31,9 +32,10 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool dtype_ok(int dt) { return dt == SPEC_F32 || dt == SPEC_BF16; }
 
 constexpr int kMaxV = 1 << 28;
+constexpr int kMaxDraftV = 2048 * 128;   // the finalize holds <= 8 tile summaries per thread
 
 struct DraftLayout {
-    size_t stats, hproj, state, erows, total;
+    size_t stats, w2t, hproj, state, erows, total;
 };
 
 DraftLayout draft_layout(bool rnn, int B, int gamma, int V, int r) {
@@ -41,6 +43,8 @@ DraftLayout draft_layout(bool rnn, int B, int gamma, int V, int r) {
     size_t off = 0;
     L.stats = off;
     off += align_up((size_t)B * draft_num_segments(B, V, 1) * sizeof(SegStat));
+    L.w2t = off;   // transposed bf16 W2 (also reserved for fp32 weights)
+    off += align_up((size_t)V * r * sizeof(uint16_t));
     if (rnn) {
         L.hproj = off;
         off += align_up((size_t)B * gamma * 3 * r * sizeof(float));
@@ -93,6 +97,8 @@ spec_status_t check_draft_common(const void* U, int U_dtype, const int32_t* x0, 
     if (B < 0 || gamma < 0) return fail(SPEC_ERR_INVALID, "B and gamma must be >= 0");
     if (V <= 0 || V > kMaxV) return fail(SPEC_ERR_INVALID, "V must be in [1, 2^28]");
     if (r <= 0) return fail(SPEC_ERR_INVALID, "rank r must be > 0");
+    if (V > kMaxDraftV)
+        return fail(SPEC_ERR_UNSUPPORTED, "draft sampling supports V <= 262144 (2048 tiles of 128)");
     if (spec_status_t st = check_T(T)) return st;
     if (!dtype_ok(U_dtype) || !dtype_ok(w_dtype)) return fail(SPEC_ERR_UNSUPPORTED, "dtype must be SPEC_F32 or SPEC_BF16");
     if ((int64_t)B * gamma > INT32_MAX) return fail(SPEC_ERR_UNSUPPORTED, "B * gamma too large");
@@ -109,15 +115,34 @@ spec_status_t check_draft_common(const void* U, int U_dtype, const int32_t* x0, 
 spec_status_t run_draft(DraftArgs& a, void* stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
+    void* t;
+    if (a.w_bf16) {
+        t = prof_begin("w2_transpose", s);
+        e = w2_transpose_launch(a, s);
+        prof_end(t, s);
+        if (e != hipSuccess) return hip_fail(e, "w2_transpose");
+    }
     if (a.head == kHeadRnn) {
-        if ((e = rnn_hidden_proj_launch(a, s)) != hipSuccess) return hip_fail(e, "rnn_hidden_proj");
+        t = prof_begin("rnn_hidden_proj", s);
+        e = rnn_hidden_proj_launch(a, s);
+        prof_end(t, s);
+        if (e != hipSuccess) return hip_fail(e, "rnn_hidden_proj");
     }
     for (int k = 0; k < a.gamma; ++k) {
         if (a.head == kHeadRnn) {
-            if ((e = rnn_gates_launch(a, k, s)) != hipSuccess) return hip_fail(e, "rnn_gates");
+            t = prof_begin("rnn_gates", s);
+            e = rnn_gates_launch(a, k, s);
+            prof_end(t, s);
+            if (e != hipSuccess) return hip_fail(e, "rnn_gates");
         }
-        if ((e = draft_tile_launch(a, k, s)) != hipSuccess) return hip_fail(e, "draft_tile");
-        if ((e = draft_finalize_launch(a, k, s)) != hipSuccess) return hip_fail(e, "draft_finalize");
+        t = prof_begin("draft_tile", s);
+        e = draft_tile_launch(a, k, s);
+        prof_end(t, s);
+        if (e != hipSuccess) return hip_fail(e, "draft_tile");
+        t = prof_begin("draft_finalize", s);
+        e = draft_finalize_launch(a, k, s);
+        prof_end(t, s);
+        if (e != hipSuccess) return hip_fail(e, "draft_finalize");
     }
     return SPEC_OK;
 }
@@ -182,6 +207,7 @@ spec_status_t spec_draft_sample_markov(const void* U, int U_dtype, const int32_t
     a.q_logZ = q_logZ;
     a.q_tok = q_tok_prob;
     a.stats = reinterpret_cast<SegStat*>(w + L.stats);
+    a.W2T = reinterpret_cast<uint16_t*>(w + L.w2t);
     return run_draft(a, stream);
 }
 
@@ -243,6 +269,7 @@ spec_status_t spec_draft_sample_rnn(const void* U, int U_dtype, const int32_t* x
     a.hproj = reinterpret_cast<float*>(w + L.hproj);
     a.state = reinterpret_cast<float*>(w + L.state);
     a.Erows = reinterpret_cast<uint16_t*>(w + L.erows);
+    a.W2T = reinterpret_cast<uint16_t*>(w + L.w2t);
     return run_draft(a, stream);
 }
 

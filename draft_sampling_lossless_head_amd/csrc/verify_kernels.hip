@@ -18,6 +18,7 @@
 
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "profile.hpp"
 
 namespace specdec {
 
@@ -26,6 +27,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kChunk = 4096;          // tokens per chunk of the final draw
 constexpr int kPerThread = kChunk / 256;
+static_assert(kPerThread == 16, "the final draw works on runs of 16 tokens per thread");
 
 int verify_num_chunks(int V) { return (V + kChunk - 1) / kChunk; }
 
@@ -179,46 +181,54 @@ void verify_rows(VerifyArgs a, int is_q) {
     }
 }
 
+// One wave per request; lane k handles position k (in chunks of 64).  The
+// first rejection is the lowest set bit of a ballot.
 __global__ __launch_bounds__(256)
 void verify_decide(VerifyArgs a) {
-    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (b >= a.B) return;
     const int G = a.gamma_max;
     const int L = request_len(a, b);
     int32_t* out = a.out_tokens + (size_t)b * (G + 1);
     const int32_t* dr = a.draft + (size_t)b * G;
     const RowStat* rs = a.rows + (size_t)b * (2 * G + 1);
-    bool bad = L < 0 || L > G;
-    if (!bad) {
-        for (int k = 0; k < L; ++k)
-            if (dr[k] < 0 || dr[k] >= a.V) bad = true;
-        for (int k = 0; k <= L && !bad; ++k)
-            if (rs[k].m == -INFINITY) bad = true;
-        for (int k = 0; k < L && !bad; ++k)
-            if (rs[G + 1 + k].m == -INFINITY) bad = true;
+
+    bool bad_l = L < 0 || L > G;
+    if (!bad_l) {
+        for (int k = lane; k <= L; k += kWave) {
+            if (k < L && (dr[k] < 0 || dr[k] >= a.V)) bad_l = true;
+            if (rs[k].m == -INFINITY) bad_l = true;
+            if (k < L && rs[G + 1 + k].m == -INFINITY) bad_l = true;
+        }
     }
-    if (bad) {
-        a.accepted[b] = -1;
-        for (int j = 0; j <= G; ++j) out[j] = -1;
-        for (int j = 0; j <= G; ++j) {
+    if (__ballot(bad_l)) {
+        for (int j = lane; j <= G; j += kWave) {
+            out[j] = -1;
             if (a.p_logZ) a.p_logZ[(size_t)b * (G + 1) + j] = 0.0f;
             if (j < G && a.q_logZ) a.q_logZ[(size_t)b * G + j] = 0.0f;
             if (j < G && a.accept_prob) a.accept_prob[(size_t)b * G + j] = 0.0f;
         }
-        FinalInfo f;
-        f.logZp = 0.0;
-        f.logZq = 0.0;
-        f.n = -1;
-        f.mode = 0;
-        f.pad0 = f.pad1 = 0;
-        a.fin[b] = f;
+        if (lane == 0) {
+            a.accepted[b] = -1;
+            FinalInfo f;
+            f.logZp = 0.0;
+            f.logZq = 0.0;
+            f.n = -1;
+            f.mode = 0;
+            f.pad0 = f.pad1 = 0;
+            a.fin[b] = f;
+        }
         return;
     }
+
     const double invT = (double)a.invT;
     int n = L;
-    double lzp_n = 0.0, lzq_n = 0.0;
-    for (int k = 0; k <= G; ++k) {
+    double lzp_n = 0.0, lzq_n = 0.0, lzp_L = 0.0;
+    for (int c0 = 0; c0 <= G; c0 += kWave) {
+        const int k = c0 + lane;
         double lzp = 0.0, lzq = 0.0, ap = 0.0;
+        bool reject = false;
         if (k <= L) {
             const RowStat p = rs[k];
             lzp = a.greedy ? (double)p.m : (double)p.m * invT + log((double)p.s);
@@ -226,11 +236,10 @@ void verify_decide(VerifyArgs a) {
         if (k < L) {
             const RowStat p = rs[k];
             const RowStat q = rs[G + 1 + k];
-            bool acc;
             if (a.greedy) {
                 lzq = (double)q.m;
-                acc = p.idx == dr[k];
-                ap = acc ? 1.0 : 0.0;
+                reject = p.idx != dr[k];
+                ap = reject ? 0.0 : 1.0;
             } else {
                 lzq = (double)q.m * invT + log((double)q.s);
                 const double px = exp((double)p.gathered * invT - lzp);
@@ -238,33 +247,40 @@ void verify_decide(VerifyArgs a) {
                 ap = qx > 0.0 ? fmin(1.0, px / qx) : (px > 0.0 ? 1.0 : 0.0);
                 const float u = a.uniforms ? a.uniforms[(size_t)b * (G + 1) + k]
                                            : counter_uniform(a.seed, a.offset, b, k, 1);
-                acc = (double)u * qx < px;
-            }
-            if (!acc && n == L) {
-                n = k;
-                lzp_n = lzp;
-                lzq_n = lzq;
+                reject = !((double)u * qx < px);
             }
         }
-        if (k == L && n == L) lzp_n = lzp;
-        if (a.p_logZ) a.p_logZ[(size_t)b * (G + 1) + k] = (float)lzp;
-        if (k < G && a.q_logZ) a.q_logZ[(size_t)b * G + k] = (float)lzq;
-        if (k < G && a.accept_prob) a.accept_prob[(size_t)b * G + k] = (float)ap;
+        if (k <= G) {
+            if (a.p_logZ) a.p_logZ[(size_t)b * (G + 1) + k] = (float)lzp;
+            if (k < G && a.q_logZ) a.q_logZ[(size_t)b * G + k] = (float)lzq;
+            if (k < G && a.accept_prob) a.accept_prob[(size_t)b * G + k] = (float)ap;
+        }
+        const unsigned long long rej = __ballot(reject);
+        if (n == L && rej) {
+            n = c0 + __ffsll((long long)rej) - 1;
+            lzp_n = __shfl(lzp, n - c0);
+            lzq_n = __shfl(lzq, n - c0);
+        }
+        if (L >= c0 && L < c0 + kWave) lzp_L = __shfl(lzp, L - c0);
     }
-    a.accepted[b] = n;
-    for (int j = 0; j <= G; ++j) out[j] = j < n ? dr[j] : -1;
-    if (a.greedy) out[n] = rs[n].idx;
-    FinalInfo f;
-    f.logZp = lzp_n;
-    f.logZq = lzq_n;
-    f.n = n;
-    f.mode = a.greedy ? 0 : (n < L ? 1 : 2);
-    f.pad0 = f.pad1 = 0;
-    a.fin[b] = f;
+    if (n == L) lzp_n = lzp_L;
+    for (int j = lane; j <= G; j += kWave) out[j] = j < n ? dr[j] : -1;
+    if (lane == 0) {
+        if (a.greedy) out[n] = rs[n].idx;
+        a.accepted[b] = n;
+        FinalInfo f;
+        f.logZp = lzp_n;
+        f.logZq = lzq_n;
+        f.n = n;
+        f.mode = a.greedy ? 0 : (n < L ? 1 : 2);
+        f.pad0 = f.pad1 = 0;
+        a.fin[b] = f;
+    }
 }
 
-// Weight of token v for the final draw: max(0, p - q) or p.  The exponent
-// subtracts the fp64 normaliser as an exact (hi, lo) float pair.
+// Weights of the final draw: max(0, p - q) (correction) or p (bonus), with
+// p = exp(P/T - logZp) and q = exp(Q/T - logZq); the exponent subtracts the
+// fp64 normaliser as a (hi, lo) float pair.
 template <bool PB, bool QB>
 struct FinalRow {
     const void* pr;
@@ -272,17 +288,54 @@ struct FinalRow {
     float invT, lzp_hi, lzp_lo, lzq_hi, lzq_lo;
     int residual;
 
-    __device__ __forceinline__ float logit(const void* base, bool bf, int64_t v) const {
-        return bf ? bf16_bits_to_float(static_cast<const uint16_t*>(base)[v])
-                  : static_cast<const float*>(base)[v];
+    template <bool BF>
+    __device__ __forceinline__ static void load16(const void* base, int v0, int V, float x[16]) {
+        if (BF) {
+            const uint16_t* r = static_cast<const uint16_t*>(base);
+            if ((V % 8) == 0 && v0 + 16 <= V) {
+                const uint4 t0 = *reinterpret_cast<const uint4*>(r + v0);
+                const uint4 t1 = *reinterpret_cast<const uint4*>(r + v0 + 8);
+                const uint32_t w[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+#pragma unroll
+                for (int h = 0; h < 8; ++h) {
+                    x[2 * h] = bf16_bits_to_float(w[h] & 0xFFFFu);
+                    x[2 * h + 1] = bf16_bits_to_float(w[h] >> 16);
+                }
+                return;
+            }
+#pragma unroll
+            for (int t = 0; t < 16; ++t) x[t] = v0 + t < V ? bf16_bits_to_float(r[v0 + t]) : 0.0f;
+        } else {
+            const float* r = static_cast<const float*>(base);
+            if ((V % 4) == 0 && v0 + 16 <= V) {
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    const float4 t = *reinterpret_cast<const float4*>(r + v0 + 4 * h);
+                    x[4 * h] = t.x; x[4 * h + 1] = t.y; x[4 * h + 2] = t.z; x[4 * h + 3] = t.w;
+                }
+                return;
+            }
+#pragma unroll
+            for (int t = 0; t < 16; ++t) x[t] = v0 + t < V ? r[v0 + t] : 0.0f;
+        }
     }
-    __device__ __forceinline__ float weight(int64_t v) const {
-        const float lp = logit(pr, PB, v);
-        const float p = expf(fmaf(lp, invT, -lzp_hi) - lzp_lo);
-        if (!residual) return p;
-        const float lq = logit(qr, QB, v);
-        const float q = expf(fmaf(lq, invT, -lzq_hi) - lzq_lo);
-        return fmaxf(p - q, 0.0f);
+
+    // the 16 weights of tokens v0 .. v0 + 15 (0 beyond V)
+    __device__ __forceinline__ void weights16(int v0, int V, float w[16]) const {
+        float lp[16];
+        load16<PB>(pr, v0, V, lp);
+#pragma unroll
+        for (int t = 0; t < 16; ++t) w[t] = __expf(fmaf(lp[t], invT, -lzp_hi) - lzp_lo);
+        if (residual) {
+            float lq[16];
+            load16<QB>(qr, v0, V, lq);
+#pragma unroll
+            for (int t = 0; t < 16; ++t)
+                w[t] = fmaxf(w[t] - __expf(fmaf(lq[t], invT, -lzq_hi) - lzq_lo), 0.0f);
+        }
+#pragma unroll
+        for (int t = 0; t < 16; ++t)
+            if (v0 + t >= V) w[t] = 0.0f;
     }
 };
 
@@ -306,17 +359,15 @@ __device__ __forceinline__ FinalRow<PB, QB> make_final_row(const VerifyArgs& a, 
     return fr;
 }
 
-// fp64 sum of this thread's kPerThread consecutive tokens of chunk c.
+// fp64 sum of this thread's run of kPerThread consecutive tokens of chunk c.
 template <bool PB, bool QB>
 __device__ __forceinline__ double thread_chunk_sum(const FinalRow<PB, QB>& fr, int c, int V,
                                                    int tid) {
-    const int v0 = c * kChunk + tid * kPerThread;
+    float w[kPerThread];
+    fr.weights16(c * kChunk + tid * kPerThread, V, w);
     double acc = 0.0;
-#pragma unroll 4
-    for (int t = 0; t < kPerThread; ++t) {
-        const int v = v0 + t;
-        if (v < V) acc += (double)fr.weight(v);
-    }
+#pragma unroll
+    for (int t = 0; t < kPerThread; ++t) acc += (double)w[t];
     return acc;
 }
 
@@ -457,8 +508,10 @@ void verify_final_draw(VerifyArgs a, int nchunk) {
         double run = e2;
         int pick = -1, last = -1;
         const int v0 = cstar * kChunk + tid * kPerThread;
+        float wr[kPerThread];
+        fr.weights16(v0, V, wr);
         for (int t = 0; t < kPerThread && v0 + t < V; ++t) {
-            const double w = (double)fr.weight(v0 + t);
+            const double w = (double)wr[t];
             if (w > 0.0) {
                 last = v0 + t;
                 if (rem < run + w) {
@@ -475,8 +528,10 @@ void verify_final_draw(VerifyArgs a, int nchunk) {
         // rem beyond the rescanned total: last token of the chunk with weight
         int lastv = -1;
         const int v0 = cstar * kChunk + tid * kPerThread;
+        float wr[kPerThread];
+        fr.weights16(v0, V, wr);
         for (int t = 0; t < kPerThread && v0 + t < V; ++t)
-            if (fr.weight(v0 + t) > 0.0f) lastv = v0 + t;
+            if (wr[t] > 0.0f) lastv = v0 + t;
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) lastv = max(lastv, __shfl_xor(lastv, off));
         if (lane == 0) sh_last[wave] = lastv;
@@ -498,8 +553,12 @@ __global__ void philox_uniforms_kernel(uint64_t seed, uint32_t offset, uint32_t 
 template <bool PB, bool QB>
 static void launch_final(const VerifyArgs& a, hipStream_t s) {
     const int nc = verify_num_chunks(a.V);
+    void* t = prof_begin("verify_final_partials", s);
     hipLaunchKernelGGL((verify_final_partials<PB, QB>), dim3(nc, a.B), dim3(256), 0, s, a);
+    prof_end(t, s);
+    t = prof_begin("verify_final_draw", s);
     hipLaunchKernelGGL((verify_final_draw<PB, QB>), dim3(a.B), dim3(256), 0, s, a, nc);
+    prof_end(t, s);
 }
 
 template <bool BF16>
@@ -507,10 +566,12 @@ static void launch_rows(const VerifyArgs& a, int is_q, hipStream_t s) {
     const int nrow = is_q ? a.gamma_max : a.gamma_max + 1;
     if (nrow == 0) return;
     dim3 grid(nrow, a.B);
+    void* t = prof_begin(is_q ? "verify_rows_q" : "verify_rows_p", s);
     if (a.greedy)
         hipLaunchKernelGGL((verify_rows<BF16, true>), grid, dim3(256), 0, s, a, is_q);
     else
         hipLaunchKernelGGL((verify_rows<BF16, false>), grid, dim3(256), 0, s, a, is_q);
+    prof_end(t, s);
 }
 
 hipError_t verify_launch(const VerifyArgs& a, hipStream_t s) {
@@ -518,7 +579,9 @@ hipError_t verify_launch(const VerifyArgs& a, hipStream_t s) {
     else launch_rows<false>(a, 0, s);
     if (a.q_bf16) launch_rows<true>(a, 1, s);
     else launch_rows<false>(a, 1, s);
-    hipLaunchKernelGGL(verify_decide, dim3((a.B + 127) / 128), dim3(128), 0, s, a);
+    void* t = prof_begin("verify_decide", s);
+    hipLaunchKernelGGL(verify_decide, dim3((a.B + 3) / 4), dim3(256), 0, s, a);
+    prof_end(t, s);
     if (!a.greedy) {
         if (a.p_bf16 && a.q_bf16) launch_final<true, true>(a, s);
         else if (a.p_bf16) launch_final<true, false>(a, s);

@@ -111,6 +111,7 @@ spec_status_t spec_philox_uniforms(uint64_t seed, uint32_t offset, uint32_t stre
  * V <= 0, r <= 0, T < 0 or NaN; SPEC_ERR_UNSUPPORTED for other dtypes;
  * SPEC_ERR_WORKSPACE if ws_bytes < spec_draft_markov_workspace_size(...).
  * A request whose anchor is outside [0, V) gets tokens -1 from there on.
+ * The draft entry points support V <= 262144 (SPEC_ERR_UNSUPPORTED above).
  */
 size_t spec_draft_markov_workspace_size(int B, int gamma, int V, int r);
 
@@ -195,6 +196,22 @@ spec_status_t spec_verify(
     int32_t *accepted, int32_t *out_tokens,
     float *p_logZ, float *q_logZ, float *accept_prob,
     void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * ---------------------------------------------------------------------------
+ * Kernel timing (benchmarking aid; not needed for correct use)
+ * ---------------------------------------------------------------------------
+ * spec_profile_enable(name) starts a fresh record: from then on every launch
+ * of the kernel `name` ("draft_tile", "draft_finalize", "rnn_hidden_proj",
+ * "rnn_gates", "verify_rows_p", "verify_rows_q", "verify_decide",
+ * "verify_final_partials", "verify_final_draw", or "*" for all) is bracketed
+ * by two hipEvents recorded on its launch stream.  NULL or "" stops timing.
+ * spec_profile_read waits for the recorded events and returns the number of
+ * timed launches and their summed duration in milliseconds.  Process-wide
+ * state, guarded by a mutex; events are created on first use and reused.
+ */
+spec_status_t spec_profile_enable(const char *kernel);
+spec_status_t spec_profile_read(int *launches, double *total_ms);
 
 #ifdef __cplusplus
 }
