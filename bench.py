@@ -121,6 +121,8 @@ def main():
     ap.add_argument("--sigma", type=float, default=None, help="override target/draft noise")
     ap.add_argument("--cpu-sample", type=int, default=16, help="requests timed on the oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--quick", action="store_true",
+                    help="only the timed region (no per-kernel timing passes, no CPU baseline)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -188,6 +190,19 @@ def main():
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step, {value / 1e6:.3f} M tok/s, "
         f"mean tau {tau:.3f}")
 
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    if args.quick:
+        print(json.dumps({"metric": METRIC, "value": round(value, 1), "unit": "tokens/s",
+                          "ms_per_step": round(ms_per_step, 4), "steps": args.steps,
+                          "quick": True}), flush=True)
+        return
+
     # Second timed region: the same steps with every kernel bracketed by events.
     sd.spec_profile_enable("*")
     torch.cuda.synchronize()
@@ -223,14 +238,6 @@ def main():
                     avg_launch_us=round(kernels[dom]["avg_us"], 2))
     log("kernels: " + json.dumps({k: {a: round(b, 2) for a, b in v.items()}
                                   for k, v in kernels.items()}))
-
-    if args.copy_probe_mib:
-        n = args.copy_probe_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,

@@ -69,30 +69,54 @@ __device__ __forceinline__ float load1(const void* base, size_t i) {
 constexpr int kOutLd = kTileV + 4;   // fp32 row stride of the staged output tile
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // W2 [r, V] -> W2T [V, r] (bf16), once per draft call: each bias tile then
-// stages one contiguous block of W2T.  64 x 64 tiles through LDS.
+// stages one contiguous block of W2T.  64 x 64 tiles through LDS with 16-byte
+// global accesses on both sides.
 __global__ __launch_bounds__(256)
 void w2_transpose(const uint16_t* __restrict__ W2, uint16_t* __restrict__ W2T, int r, int V) {
-    __shared__ uint16_t t[64][64 + 2];
+    __shared__ __align__(16) uint16_t t[64][72];   // [j][v]
     const int v0 = blockIdx.x * 64;
     const int j0 = blockIdx.y * 64;
     const int tid = threadIdx.x;
+    const bool vec = (V % 8) == 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int e = tid + i * 256;
-        const int jj = e / 64, vv = e % 64;
-        const int j = j0 + jj, v = v0 + vv;
-        t[jj][vv] = (j < r && v < V) ? W2[(size_t)j * V + v] : (uint16_t)0;
+    for (int i = 0; i < 2; ++i) {
+        const int c = tid + i * 256;
+        const int jj = c / 8, vc = (c % 8) * 8;
+        const int j = j0 + jj, v = v0 + vc;
+        uint4 val = make_uint4(0u, 0u, 0u, 0u);
+        if (j < r) {
+            if (vec && v + 8 <= V) {
+                val = *reinterpret_cast<const uint4*>(W2 + (size_t)j * V + v);
+            } else {
+                uint32_t w[4];
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    const uint32_t lo = v + 2 * h < V ? W2[(size_t)j * V + v + 2 * h] : 0u;
+                    const uint32_t hi = v + 2 * h + 1 < V ? W2[(size_t)j * V + v + 2 * h + 1] : 0u;
+                    w[h] = lo | (hi << 16);
+                }
+                val = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
+        *reinterpret_cast<uint4*>(&t[jj][vc]) = val;
     }
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int e = tid + i * 256;
-        const int vv = e / 64, jj = e % 64;
-        const int j = j0 + jj, v = v0 + vv;
-        if (j < r && v < V) W2T[(size_t)v * r + j] = t[jj][vv];
+    for (int i = 0; i < 2; ++i) {
+        const int c = tid + i * 256;
+        const int vv = c / 8, jc = (c % 8) * 8;
+        const int v = v0 + vv, j = j0 + jc;
+        if (v < V && j < r) {
+            uint32_t w[4];
+#pragma unroll
+            for (int h = 0; h < 4; ++h)
+                w[h] = (uint32_t)t[jc + 2 * h][vv] | ((uint32_t)t[jc + 2 * h + 1][vv] << 16);
+            *reinterpret_cast<uint4*>(W2T + (size_t)v * r + j) = make_uint4(w[0], w[1], w[2], w[3]);
+        }
     }
 }
 
@@ -139,22 +163,31 @@ void draft_tile_mfma(const void* __restrict__ U, const uint16_t* __restrict__ W1
             wch[i] = *reinterpret_cast<const uint4*>(W2T + (size_t)(v_tile + vr) * r + (c % cpr) * 8);
     }
 
-    // 2) prefetch this thread's U items (row-contiguous epilogue mapping).
-    u32x4_t ureg[ITEMS][UV];
+    // 2) prefetch this thread's U items.  Item (row, j) covers the two runs of
+    //    four tokens 4j .. 4j+3 and 64 + 4j .. 64 + 4j + 3 of the tile row, so
+    //    the 16 lanes of a row read and write 256 contiguous bytes per access.
+    u32x4_t ureg[ITEMS][2];
 #pragma unroll
     for (int it = 0; it < ITEMS; ++it) {
         const int item = tid + it * 256;
         const int br = row0 + item / 16;
-        const int v0 = v_tile + (item % 16) * 8;
-#pragma unroll
-        for (int h = 0; h < UV; ++h) ureg[it][h] = u32x4_t{0u, 0u, 0u, 0u};
-        if (br < B && vec_u && v0 + 8 <= V) {
-            const size_t off = ((size_t)br * gamma + k) * (size_t)V + v0;
-#pragma unroll
-            for (int h = 0; h < UV; ++h)
-                ureg[it][h] = __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x4_t*>(static_cast<const char*>(U) +
-                                                     off * (U_BF16 ? 2 : 4)) + h);
+        const int va = v_tile + (item % 16) * 4;
+        ureg[it][0] = u32x4_t{0u, 0u, 0u, 0u};
+        ureg[it][1] = u32x4_t{0u, 0u, 0u, 0u};
+        if (br < B && vec_u && va + 68 <= V) {
+            const size_t off = ((size_t)br * gamma + k) * (size_t)V + va;
+            if constexpr (U_BF16) {
+                const u32x2_t a0 = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x2_t*>(static_cast<const uint16_t*>(U) + off));
+                const u32x2_t a1 = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x2_t*>(static_cast<const uint16_t*>(U) + off + 64));
+                ureg[it][0] = u32x4_t{a0[0], a0[1], a1[0], a1[1]};
+            } else {
+                ureg[it][0] = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4_t*>(static_cast<const float*>(U) + off));
+                ureg[it][1] = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4_t*>(static_cast<const float*>(U) + off + 64));
+            }
         }
     }
 
@@ -233,13 +266,17 @@ void draft_tile_mfma(const void* __restrict__ U, const uint16_t* __restrict__ W1
         const int item = tid + it * 256;
         const int rl = item / 16;
         const int br = row0 + rl;
-        const int v0 = v_tile + (item % 16) * 8;
-        const float4 b0 = *reinterpret_cast<const float4*>(otile + rl * kOutLd + (item % 16) * 8);
-        const float4 b1 = *reinterpret_cast<const float4*>(otile + rl * kOutLd + (item % 16) * 8 + 4);
+        const int ca = (item % 16) * 4;            // first run: tile columns ca .. ca+3
+        const int va = v_tile + ca;                // second run: va + 64 ..
+        const float4 b0 = *reinterpret_cast<const float4*>(otile + rl * kOutLd + ca);
+        const float4 b1 = *reinterpret_cast<const float4*>(otile + rl * kOutLd + ca + 64);
         float x[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+        int vi[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) vi[t] = va + (t & 3) + (t >> 2) * 64;
         const bool rowok = br < B;
-        const size_t off = ((size_t)(rowok ? br : 0) * gamma + k) * (size_t)V + v0;
-        if (rowok && vec_u && v0 + 8 <= V) {
+        const size_t off = ((size_t)(rowok ? br : 0) * gamma + k) * (size_t)V + va;
+        if (rowok && vec_u && va + 68 <= V) {
             if constexpr (U_BF16) {
 #pragma unroll
                 for (int h = 0; h < 4; ++h) {
@@ -250,19 +287,20 @@ void draft_tile_mfma(const void* __restrict__ U, const uint16_t* __restrict__ W1
 #pragma unroll
                 for (int h = 0; h < 4; ++h) {
                     x[h] += __uint_as_float(ureg[it][0][h]);
-                    x[4 + h] += __uint_as_float(ureg[it][UV - 1][h]);
+                    x[4 + h] += __uint_as_float(ureg[it][1][h]);
                 }
             }
             f32x4_t o0 = {x[0], x[1], x[2], x[3]};
             f32x4_t o1 = {x[4], x[5], x[6], x[7]};
             __builtin_nontemporal_store(o0, reinterpret_cast<f32x4_t*>(q_logits + off));
-            __builtin_nontemporal_store(o1, reinterpret_cast<f32x4_t*>(q_logits + off) + 1);
+            __builtin_nontemporal_store(o1, reinterpret_cast<f32x4_t*>(q_logits + off + 64));
         } else {
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                if (rowok && v0 + t < V) {
-                    x[t] += load1<U_BF16>(U, off + t);
-                    q_logits[off + t] = x[t];
+                const size_t o = off + (t & 3) + (t >> 2) * 64;
+                if (rowok && vi[t] < V) {
+                    x[t] += load1<U_BF16>(U, o);
+                    q_logits[o] = x[t];
                 } else {
                     x[t] = -INFINITY;
                 }
@@ -281,7 +319,7 @@ void draft_tile_mfma(const void* __restrict__ U, const uint16_t* __restrict__ W1
         int amax = INT_MAX;
 #pragma unroll
         for (int t = 7; t >= 0; --t)
-            if (x[t] == m) amax = v0 + t;
+            if (x[t] == m) amax = min(amax, vi[t]);
         amax = row16_min(amax);
         if (rowok && (item % 16) == 0) {
             SegStat st;
