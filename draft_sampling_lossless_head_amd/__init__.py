@@ -13,10 +13,12 @@ from .api import (  # noqa: F401
     load_library,
     spec_draft_sample_markov,
     spec_draft_sample_rnn,
+    spec_pack_w2,
     spec_philox_uniforms,
     spec_profile_enable,
     spec_profile_read,
     spec_verify,
+    spec_verify_markov,
     spec_version,
     workspace_bytes,
 )

@@ -43,20 +43,28 @@ def load_library():
     lib.spec_philox_uniforms.restype = i32
     lib.spec_draft_markov_workspace_size.argtypes = [i32, i32, i32, i32]
     lib.spec_draft_markov_workspace_size.restype = sz
-    lib.spec_draft_sample_markov.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, f32,
-                                             vp, u64, u32, vp, vp, vp, vp, vp, sz, vp]
+    lib.spec_draft_sample_markov.argtypes = [vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                             f32, vp, u64, u32, vp, vp, vp, vp, vp, sz, vp]
     lib.spec_draft_sample_markov.restype = i32
     lib.spec_draft_rnn_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.spec_draft_rnn_workspace_size.restype = sz
-    lib.spec_draft_sample_rnn.argtypes = [vp, i32, vp, vp, i32, i32, vp, vp, vp, vp, vp, i32, i32,
-                                          i32, i32, i32, f32, vp, u64, u32, vp, vp, vp, vp, vp,
-                                          sz, vp]
+    lib.spec_draft_sample_rnn.argtypes = [vp, i32, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, i32,
+                                          i32, i32, i32, i32, f32, vp, u64, u32, vp, vp, vp, vp,
+                                          vp, sz, vp]
     lib.spec_draft_sample_rnn.restype = i32
     lib.spec_verify_workspace_size.argtypes = [i32, i32, i32]
     lib.spec_verify_workspace_size.restype = sz
     lib.spec_verify.argtypes = [vp, i32, vp, i32, vp, vp, vp, vp, i32, i32, i32, f32, vp, u64,
                                 u32, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.spec_verify.restype = i32
+    lib.spec_pack_w2.argtypes = [vp, vp, i32, i32, vp]
+    lib.spec_pack_w2.restype = i32
+    lib.spec_verify_markov_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.spec_verify_markov_workspace_size.restype = sz
+    lib.spec_verify_markov.argtypes = [vp, i32, vp, i32, vp, vp, vp, vp, i32, i32, vp, vp, vp,
+                                       vp, vp, i32, i32, i32, f32, vp, u64, u32, vp, vp, vp, vp,
+                                       vp, sz, vp]
+    lib.spec_verify_markov.restype = i32
     lib.spec_profile_enable.argtypes = [ctypes.c_char_p]
     lib.spec_profile_enable.restype = i32
     lib.spec_profile_read.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_double)]
@@ -107,6 +115,9 @@ def workspace_bytes(kind, **dims):
                                                  dims["d"])
     if kind == "verify":
         return lib.spec_verify_workspace_size(dims["B"], dims["gamma_max"], dims["V"])
+    if kind == "verify_markov":
+        return lib.spec_verify_markov_workspace_size(dims["B"], dims["gamma_max"], dims["V"],
+                                                     dims["r"])
     raise ValueError(kind)
 
 
@@ -129,41 +140,66 @@ def spec_philox_uniforms(seed, offset, stream_id, B, K, device="cuda", out=None,
     return out
 
 
-def _draft_outputs(B, gamma, V, device, out):
+def _draft_outputs(B, gamma, V, device, out, q_free=False):
     if out is not None:
         return out
-    return dict(tokens=torch.empty((B, gamma), dtype=torch.int32, device=device),
-                q_logits=torch.empty((B, gamma, V), dtype=torch.float32, device=device),
-                q_logZ=torch.empty((B, gamma), dtype=torch.float32, device=device),
-                q_tok_prob=torch.empty((B, gamma), dtype=torch.float32, device=device))
+    o = dict(tokens=torch.empty((B, gamma), dtype=torch.int32, device=device),
+             q_logZ=torch.empty((B, gamma), dtype=torch.float32, device=device),
+             q_tok_prob=torch.empty((B, gamma), dtype=torch.float32, device=device))
+    if not q_free:
+        o["q_logits"] = torch.empty((B, gamma, V), dtype=torch.float32, device=device)
+    return o
 
 
-def spec_draft_sample_markov(U, x0, W1, W2, T=1.0, *, uniforms=None, seed=0, offset=0,
-                             out=None, workspace=None, stream=None):
-    """Markov-head draft.  U [B, gamma, V], x0 [B] int32, W1 [V, r], W2 [r, V]."""
+def spec_pack_w2(W2, out=None, stream=None):
+    """W2 [r, V] bf16 -> W2T [V, r] bf16 (pack once; pass as W2T=)."""
     lib = load_library()
-    for t, n in ((U, "U"), (x0, "x0"), (W1, "W1"), (W2, "W2")):
+    _dev(W2, "W2")
+    if W2.dtype != torch.bfloat16:
+        raise SpecError("spec_pack_w2 packs bf16 weights")
+    r, V = W2.shape
+    out = torch.empty((V, r), dtype=torch.bfloat16, device=W2.device) if out is None else out
+    _check(lib.spec_pack_w2(_ptr(W2), _ptr(out), r, V, _stream(stream)), "spec_pack_w2")
+    return out
+
+
+def spec_draft_sample_markov(U, x0, W1, W2, T=1.0, *, W2T=None, q_free=False, uniforms=None,
+                             seed=0, offset=0, out=None, workspace=None, stream=None):
+    """Markov-head draft.  U [B, gamma, V], x0 [B] int32, W1 [V, r], W2 [r, V]
+    (or None with W2T [V, r] from spec_pack_w2).  q_free=True writes no q
+    logits (verify with spec_verify_markov)."""
+    lib = load_library()
+    for t, n in ((U, "U"), (x0, "x0"), (W1, "W1")):
         _dev(t, n)
     B, gamma, V = U.shape
     r = W1.shape[1]
     if x0.dtype != torch.int32 or x0.shape != (B,):
         raise SpecError("x0 must be int32 [B]")
-    if W1.shape != (V, r) or W2.shape != (r, V) or W1.dtype != W2.dtype:
-        raise SpecError("W1 must be [V, r] and W2 [r, V] of one dtype")
+    if W2 is not None:
+        _dev(W2, "W2")
+        if W2.shape != (r, V) or W1.dtype != W2.dtype:
+            raise SpecError("W2 must be [r, V] of W1's dtype")
+    if W2T is not None:
+        _dev(W2T, "W2T")
+        if W2T.shape != (V, r) or W2T.dtype != torch.bfloat16:
+            raise SpecError("W2T must be bf16 [V, r]")
+    if W1.shape != (V, r):
+        raise SpecError("W1 must be [V, r]")
     if uniforms is not None and (uniforms.dtype != torch.float32 or uniforms.shape != (B, gamma)):
         raise SpecError("uniforms must be float32 [B, gamma]")
-    o = _draft_outputs(B, gamma, V, U.device, out)
+    o = _draft_outputs(B, gamma, V, U.device, out, q_free)
     ws, nws = _workspace(lib.spec_draft_markov_workspace_size(B, gamma, V, r), U.device, workspace)
     st = lib.spec_draft_sample_markov(
-        _ptr(U), _dtype_code(U, "U"), _ptr(x0), _ptr(W1), _ptr(W2), _dtype_code(W1, "W1"), r,
-        B, gamma, V, float(T), _ptr(uniforms), seed, offset, _ptr(o["tokens"]), _ptr(o["q_logits"]),
-        _ptr(o.get("q_logZ")), _ptr(o.get("q_tok_prob")), _ptr(ws), nws, _stream(stream))
+        _ptr(U), _dtype_code(U, "U"), _ptr(x0), _ptr(W1), _ptr(W2), _ptr(W2T),
+        _dtype_code(W1, "W1"), r, B, gamma, V, float(T), _ptr(uniforms), seed, offset,
+        _ptr(o["tokens"]), _ptr(o.get("q_logits")), _ptr(o.get("q_logZ")),
+        _ptr(o.get("q_tok_prob")), _ptr(ws), nws, _stream(stream))
     _check(st, "spec_draft_sample_markov")
     return o
 
 
-def spec_draft_sample_rnn(U, x0, h, W1, W2, Wg, Wc, Wo, T=1.0, *, uniforms=None, seed=0,
-                          offset=0, out=None, workspace=None, stream=None):
+def spec_draft_sample_rnn(U, x0, h, W1, W2, Wg, Wc, Wo, T=1.0, *, W2T=None, uniforms=None,
+                          seed=0, offset=0, out=None, workspace=None, stream=None):
     """RNN-head draft.  h [B, gamma, d]; Wg, Wc, Wo [r, 2r + d]."""
     lib = load_library()
     for t, n in ((U, "U"), (x0, "x0"), (h, "h"), (W1, "W1"), (W2, "W2"), (Wg, "Wg"), (Wc, "Wc"),
@@ -181,7 +217,8 @@ def spec_draft_sample_rnn(U, x0, h, W1, W2, Wg, Wc, Wo, T=1.0, *, uniforms=None,
     ws, nws = _workspace(lib.spec_draft_rnn_workspace_size(B, gamma, V, r, d), U.device, workspace)
     st = lib.spec_draft_sample_rnn(
         _ptr(U), _dtype_code(U, "U"), _ptr(x0), _ptr(h), _dtype_code(h, "h"), d, _ptr(W1),
-        _ptr(W2), _ptr(Wg), _ptr(Wc), _ptr(Wo), _dtype_code(W1, "W1"), r, B, gamma, V, float(T),
+        _ptr(W2), _ptr(W2T), _ptr(Wg), _ptr(Wc), _ptr(Wo), _dtype_code(W1, "W1"), r, B, gamma, V,
+        float(T),
         _ptr(uniforms), seed, offset, _ptr(o["tokens"]), _ptr(o["q_logits"]), _ptr(o.get("q_logZ")),
         _ptr(o.get("q_tok_prob")), _ptr(ws), nws, _stream(stream))
     _check(st, "spec_draft_sample_rnn")
@@ -252,3 +289,51 @@ def spec_profile_read():
     n, ms = ctypes.c_int(), ctypes.c_double()
     _check(lib.spec_profile_read(ctypes.byref(n), ctypes.byref(ms)), "spec_profile_read")
     return n.value, ms.value
+
+
+def spec_verify_markov(P, U, x0, W1, W2, draft, q_logZ, q_tok_prob, T=1.0, *, W2T=None,
+                       gamma_max=None, lens=None, p_row_off=None, uniforms=None, seed=0,
+                       offset=0, diagnostics=True, out=None, workspace=None, stream=None):
+    """Verification of a q-free Markov draft: P target logits (dense
+    [B, gamma+1, V] or packed with p_row_off), U/x0/W1/W2 (or W2T) as given to
+    the draft, draft tokens and the draft's q_logZ / q_tok_prob [B, gamma]."""
+    lib = load_library()
+    for t, n in ((P, "P"), (U, "U"), (x0, "x0"), (W1, "W1"), (draft, "draft"),
+                 (q_logZ, "q_logZ"), (q_tok_prob, "q_tok_prob")):
+        _dev(t, n)
+    B = draft.shape[0]
+    gamma_max = draft.shape[1] if gamma_max is None else gamma_max
+    V = P.shape[-1]
+    r = W1.shape[1]
+    if U.shape != (B, gamma_max, V):
+        raise SpecError("U must be dense [B, gamma_max, V]")
+    for t, n in ((q_logZ, "q_logZ"), (q_tok_prob, "q_tok_prob")):
+        if t.dtype != torch.float32 or t.shape != (B, gamma_max):
+            raise SpecError(f"{n} must be float32 [B, gamma_max]")
+    if draft.dtype != torch.int32 or draft.shape != (B, gamma_max):
+        raise SpecError("draft must be int32 [B, gamma_max]")
+    for t, n, dt in ((lens, "lens", torch.int32), (p_row_off, "p_row_off", torch.int64)):
+        if t is not None:
+            _dev(t, n)
+            if t.dtype != dt or t.shape != (B,):
+                raise SpecError(f"{n} must be {dt} [B]")
+    if W2 is not None:
+        _dev(W2, "W2")
+    if W2T is not None:
+        _dev(W2T, "W2T")
+    dev = P.device
+    if out is None:
+        out = dict(accepted=torch.empty(B, dtype=torch.int32, device=dev),
+                   out_tokens=torch.empty((B, gamma_max + 1), dtype=torch.int32, device=dev))
+        if diagnostics:
+            out["p_logZ"] = torch.empty((B, gamma_max + 1), dtype=torch.float32, device=dev)
+            out["accept_prob"] = torch.empty((B, gamma_max), dtype=torch.float32, device=dev)
+    ws, nws = _workspace(lib.spec_verify_markov_workspace_size(B, gamma_max, V, r), dev, workspace)
+    st = lib.spec_verify_markov(
+        _ptr(P), _dtype_code(P, "P"), _ptr(U), _dtype_code(U, "U"), _ptr(x0), _ptr(W1), _ptr(W2),
+        _ptr(W2T), SPEC_BF16, r, _ptr(draft), _ptr(q_logZ), _ptr(q_tok_prob), _ptr(lens),
+        _ptr(p_row_off), B, gamma_max, V, float(T), _ptr(uniforms), seed, offset,
+        _ptr(out["accepted"]), _ptr(out["out_tokens"]), _ptr(out.get("p_logZ")),
+        _ptr(out.get("accept_prob")), _ptr(ws), nws, _stream(stream))
+    _check(st, "spec_verify_markov")
+    return out

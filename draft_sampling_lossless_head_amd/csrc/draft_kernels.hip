@@ -121,19 +121,16 @@ void w2_transpose(const uint16_t* __restrict__ W2, uint16_t* __restrict__ W2T, i
 }
 
 // Workgroup = 4 waves on one 128-token tile and RT = 32*WB request rows.
-template <int WB, int MODE, bool U_BF16>
+// OUT selects what the tile produces (see kOutQ / kOutStats / kOutResidual).
+template <int WB, int MODE, bool U_BF16, int OUT>
 __global__ __launch_bounds__(256, 2)
-void draft_tile_mfma(const void* __restrict__ U, const uint16_t* __restrict__ W1,
-                     const uint16_t* __restrict__ W2T, const uint16_t* __restrict__ Erows,
-                     const int32_t* __restrict__ x0, const int32_t* __restrict__ tokens,
-                     float* __restrict__ q_logits, SegStat* __restrict__ stats,
-                     int B, int gamma, int V, int r, int k, float invT, int greedy) {
+void draft_tile_mfma(TileParams P) {
     constexpr int MB = WB;
     constexpr int NS = (MODE == kHeadRnn) ? 3 : 1;
     constexpr int RT = 32 * WB;            // request rows of the tile
     constexpr int ITEMS = RT * 16 / 256;   // (row, 8-token group) items per thread
-    constexpr int UV = U_BF16 ? 1 : 2;     // 16-byte vectors per 8 tokens of U
     extern __shared__ __align__(16) uint16_t smem[];
+    const int V = P.V, r = P.r, k = P.k, B = P.B, gamma = P.gamma;
     const int ldr = r + kLdsPad;
     uint16_t* w2t = smem;                                   // [kTileV][ldr] bf16
     float* otile = reinterpret_cast<float*>(smem);          // [RT][kOutLd] fp32 (reused)
@@ -145,10 +142,21 @@ void draft_tile_mfma(const void* __restrict__ U, const uint16_t* __restrict__ W1
     const int v_tile = blockIdx.x * kTileV;
     const int row0 = blockIdx.y * RT;
     const int b = row0 + wb * 32 + (lane & 31);
-    const bool brow = b < B;
     const int kgrp = lane >> 5;
     const int nks = r / 16;
     const bool vec_u = U_BF16 ? (V % 8) == 0 : (V % 4) == 0;
+
+    // Position of request row br (kOutResidual: its own; -1 = inactive).
+    auto row_position = [&](int br) -> int {
+        if (br >= B) return -1;
+        return OUT == kOutResidual ? P.row_pos[br] : k;
+    };
+    auto u_offset = [&](int br, int pos) -> size_t {
+        return ((size_t)br * gamma + pos) * (size_t)V;
+    };
+    auto out_offset = [&](int br, int pos) -> size_t {
+        return OUT == kOutResidual ? (size_t)br * V : ((size_t)br * gamma + pos) * (size_t)V;
+    };
 
     // 1) the W2T tile: kTileV rows of r contiguous bf16, 16 bytes per chunk.
     const int cpr = r / 8;                       // chunks per W2T row
@@ -160,7 +168,7 @@ void draft_tile_mfma(const void* __restrict__ U, const uint16_t* __restrict__ W1
         const int vr = c / cpr;
         wch[i] = make_uint4(0u, 0u, 0u, 0u);
         if (c < nchunk && v_tile + vr < V)
-            wch[i] = *reinterpret_cast<const uint4*>(W2T + (size_t)(v_tile + vr) * r + (c % cpr) * 8);
+            wch[i] = *reinterpret_cast<const uint4*>(P.W2T + (size_t)(v_tile + vr) * r + (c % cpr) * 8);
     }
 
     // 2) prefetch this thread's U items.  Item (row, j) covers the two runs of
@@ -171,31 +179,33 @@ void draft_tile_mfma(const void* __restrict__ U, const uint16_t* __restrict__ W1
     for (int it = 0; it < ITEMS; ++it) {
         const int item = tid + it * 256;
         const int br = row0 + item / 16;
+        const int pos = row_position(br);
         const int va = v_tile + (item % 16) * 4;
         ureg[it][0] = u32x4_t{0u, 0u, 0u, 0u};
         ureg[it][1] = u32x4_t{0u, 0u, 0u, 0u};
-        if (br < B && vec_u && va + 68 <= V) {
-            const size_t off = ((size_t)br * gamma + k) * (size_t)V + va;
+        if (pos >= 0 && vec_u && va + 68 <= V) {
+            const size_t off = u_offset(br, pos) + va;
             if constexpr (U_BF16) {
                 const u32x2_t a0 = __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x2_t*>(static_cast<const uint16_t*>(U) + off));
+                    reinterpret_cast<const u32x2_t*>(static_cast<const uint16_t*>(P.U) + off));
                 const u32x2_t a1 = __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x2_t*>(static_cast<const uint16_t*>(U) + off + 64));
+                    reinterpret_cast<const u32x2_t*>(static_cast<const uint16_t*>(P.U) + off + 64));
                 ureg[it][0] = u32x4_t{a0[0], a0[1], a1[0], a1[1]};
             } else {
                 ureg[it][0] = __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x4_t*>(static_cast<const float*>(U) + off));
+                    reinterpret_cast<const u32x4_t*>(static_cast<const float*>(P.U) + off));
                 ureg[it][1] = __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x4_t*>(static_cast<const float*>(U) + off + 64));
+                    reinterpret_cast<const u32x4_t*>(static_cast<const float*>(P.U) + off + 64));
             }
         }
     }
 
-    // 3) conditioning rows (Markov: W1[x_{k-1}]; RNN: split o rows).
+    // 3) conditioning rows (Markov: W1[x_{pos-1}]; RNN: split o rows).
+    const int bpos = row_position(b);
     int prev = 0;
-    bool erow_ok = brow;
-    if (MODE == kHeadMarkov && brow) {
-        prev = (k == 0) ? x0[b] : tokens[(size_t)b * gamma + k - 1];
+    bool erow_ok = bpos >= 0;
+    if (MODE == kHeadMarkov && bpos >= 0) {
+        prev = (bpos == 0) ? P.x0[b] : P.tokens[(size_t)b * gamma + bpos - 1];
         erow_ok = prev >= 0 && prev < V;
     }
 #pragma unroll
@@ -214,8 +224,8 @@ void draft_tile_mfma(const void* __restrict__ U, const uint16_t* __restrict__ W1
 #pragma unroll
     for (int split = 0; split < NS; ++split) {
         const uint16_t* erow = (MODE == kHeadMarkov)
-                                   ? W1 + (size_t)prev * r
-                                   : Erows + ((size_t)(brow ? b : 0) * 3 + split) * r;
+                                   ? P.W1 + (size_t)prev * r
+                                   : P.Erows + ((size_t)(b < B ? b : 0) * 3 + split) * r;
         bf16x8_t e[16];
 #pragma unroll
         for (int ks = 0; ks < 16; ++ks) {
@@ -258,14 +268,16 @@ void draft_tile_mfma(const void* __restrict__ U, const uint16_t* __restrict__ W1
     }
     __syncthreads();
 
-    // 6) row-contiguous epilogue: l = U + bias, store q, and the row summary
-    //    of the tile (max, sum exp((l - max)/T), lowest argmax) reduced over
-    //    the row's 16 lanes with DPP moves.
+    // 6) row-contiguous epilogue: l = U + bias, store l (kOutQ, kOutResidual),
+    //    and the row summary of the tile (max, sum exp((l - max)/T), lowest
+    //    argmax) reduced over the row's 16 lanes with DPP moves.
+    const int nseg = gridDim.x;
 #pragma unroll
     for (int it = 0; it < ITEMS; ++it) {
         const int item = tid + it * 256;
         const int rl = item / 16;
         const int br = row0 + rl;
+        const int pos = row_position(br);
         const int ca = (item % 16) * 4;            // first run: tile columns ca .. ca+3
         const int va = v_tile + ca;                // second run: va + 64 ..
         const float4 b0 = *reinterpret_cast<const float4*>(otile + rl * kOutLd + ca);
@@ -274,8 +286,9 @@ void draft_tile_mfma(const void* __restrict__ U, const uint16_t* __restrict__ W1
         int vi[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) vi[t] = va + (t & 3) + (t >> 2) * 64;
-        const bool rowok = br < B;
-        const size_t off = ((size_t)(rowok ? br : 0) * gamma + k) * (size_t)V + va;
+        const bool rowok = pos >= 0;
+        const size_t uoff = u_offset(rowok ? br : 0, rowok ? pos : 0) + va;
+        const size_t ooff = out_offset(rowok ? br : 0, rowok ? pos : 0) + va;
         if (rowok && vec_u && va + 68 <= V) {
             if constexpr (U_BF16) {
 #pragma unroll
@@ -290,44 +303,61 @@ void draft_tile_mfma(const void* __restrict__ U, const uint16_t* __restrict__ W1
                     x[4 + h] += __uint_as_float(ureg[it][1][h]);
                 }
             }
-            f32x4_t o0 = {x[0], x[1], x[2], x[3]};
-            f32x4_t o1 = {x[4], x[5], x[6], x[7]};
-            __builtin_nontemporal_store(o0, reinterpret_cast<f32x4_t*>(q_logits + off));
-            __builtin_nontemporal_store(o1, reinterpret_cast<f32x4_t*>(q_logits + off + 64));
+            if (OUT != kOutStats) {
+                f32x4_t o0 = {x[0], x[1], x[2], x[3]};
+                f32x4_t o1 = {x[4], x[5], x[6], x[7]};
+                __builtin_nontemporal_store(o0, reinterpret_cast<f32x4_t*>(P.out + ooff));
+                __builtin_nontemporal_store(o1, reinterpret_cast<f32x4_t*>(P.out + ooff + 64));
+            }
         } else {
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                const size_t o = off + (t & 3) + (t >> 2) * 64;
+                const size_t d = (t & 3) + (t >> 2) * 64;
                 if (rowok && vi[t] < V) {
-                    x[t] += load1<U_BF16>(U, o);
-                    q_logits[o] = x[t];
+                    x[t] += load1<U_BF16>(P.U, uoff + d);
+                    if (OUT != kOutStats) P.out[ooff + d] = x[t];
                 } else {
                     x[t] = -INFINITY;
                 }
             }
         }
+        if (OUT == kOutResidual) continue;   // the verify pass needs no summaries
         float m = x[0];
 #pragma unroll
         for (int t = 1; t < 8; ++t) m = fmaxf(m, x[t]);
         m = row16_max(m);
-        float sum = 0.0f;
-        if (!greedy && m != -INFINITY) {
+        float sa = 0.0f, sb = 0.0f;
+        if (!P.greedy && m != -INFINITY) {
 #pragma unroll
-            for (int t = 0; t < 8; ++t) sum += __expf((x[t] - m) * invT);
+            for (int t = 0; t < 4; ++t) {
+                sa += __expf((x[t] - m) * P.invT);
+                sb += __expf((x[t + 4] - m) * P.invT);
+            }
         }
-        sum = row16_sum(sum);
+        const float sum = row16_sum(sa + sb);
         int amax = INT_MAX;
 #pragma unroll
         for (int t = 7; t >= 0; --t)
             if (x[t] == m) amax = min(amax, vi[t]);
         amax = row16_min(amax);
+        if (OUT == kOutStats) {
+            // 8-token group sums: lanes 2i and 2i+1 of a row hold the two
+            // halves of groups i (first runs) and 8 + i (second runs).
+            const float ga = sa + dpp_mov<kDppXor1>(sa);
+            const float gb = sb + dpp_mov<kDppXor1>(sb);
+            const int j = item % 16;
+            if (rowok) {
+                const int grp = (j & 1) ? 8 + (j >> 1) : (j >> 1);
+                P.gsums[((size_t)br * nseg + blockIdx.x) * 16 + grp] = (j & 1) ? gb : ga;
+            }
+        }
         if (rowok && (item % 16) == 0) {
             SegStat st;
             st.m = m;
             st.s = sum;
             st.idx = amax;
             st.pad = 0;
-            stats[(size_t)br * gridDim.x + blockIdx.x] = st;
+            P.stats[(size_t)br * nseg + blockIdx.x] = st;
         }
     }
 }
@@ -400,13 +430,23 @@ void draft_tile_valu_f32w(const void* __restrict__ U, const float* __restrict__ 
 // ---------------------------------------------------------------------------
 constexpr int kFinRun = 8;   // max summaries per thread (nseg <= 2048)
 
+// Inputs the q-free draft needs to rebuild 8 logits of one tile row.
+struct RebuildArgs {
+    const float* gsums;     // [B, nseg, 16] group sums relative to the tile max
+    const void* U;          // [B, gamma, V]
+    int u_bf16;
+    const uint16_t* W1;     // [V, r]
+    const uint16_t* W2T;    // [V, r]
+    int r;
+};
+
 __global__ __launch_bounds__(256)
 void draft_finalize(const SegStat* __restrict__ stats, int nseg, int seg_len,
                     const float* __restrict__ q_logits, const int32_t* __restrict__ x0,
                     int32_t* __restrict__ tokens, float* __restrict__ q_logZ,
                     float* __restrict__ q_tok, const float* __restrict__ uniforms,
                     uint64_t seed, uint32_t offset, int B, int gamma, int V, int k, float invT,
-                    int greedy) {
+                    int greedy, RebuildArgs rb) {
     __shared__ float sh_m[4];
     __shared__ int sh_i[4];
     __shared__ double sh_tot[4];
@@ -542,11 +582,74 @@ void draft_finalize(const SegStat* __restrict__ stats, int nseg, int seg_len,
     }
     __syncthreads();
     if (wave != 0) return;
-
-    // 4) wave 0 rescans the segment (2 tokens per lane).
-    const int seg = sh_seg;
+    const int seg = max(0, sh_seg);   // a finite row max always gives one segment weight
     const double rem = sh_rem;
     const double Md = (double)M;
+
+    if (q_logits == nullptr) {
+        // q-free draft: locate the 8-token group from the tile's group sums,
+        // then rebuild that group's logits l = U + W1[prev] . W2[:, v].
+        const float mseg = st[seg].m;
+        const double scale = (double)expf((mseg - M) * invT);   // as the tile weight
+        const double wg = lane < 16 ? (double)rb.gsums[((size_t)b * nseg + seg) * 16 + lane] * scale
+                                    : 0.0;
+        const double ginc = wave_inclusive_scan_f64(wg);
+        double gexc = __shfl_up(ginc, 1);
+        if (lane == 0) gexc = 0.0;
+        unsigned long long ghit = __ballot(wg > 0.0 && ginc > rem);
+        const bool gclamp = ghit == 0;
+        if (gclamp) {
+            const unsigned long long pos = __ballot(wg > 0.0);
+            ghit = pos ? 1ull << (63 - __clzll((long long)pos)) : 1ull;
+        }
+        const int grp = __ffsll((long long)ghit) - 1;
+        const double grem = gclamp ? INFINITY : rem - __shfl(gexc, grp);
+        // lane = 8 * t + sl: token t of the group, rank slice sl
+        const int t = lane >> 3, sl = lane & 7;
+        const int vt = seg * seg_len + grp * 8 + t;
+        const int span = rb.r / 8;
+        float part = 0.0f;
+        if (vt < V) {
+            const uint16_t* w1 = rb.W1 + (size_t)prev * rb.r + sl * span;
+            const uint16_t* w2 = rb.W2T + (size_t)vt * rb.r + sl * span;
+            for (int j = 0; j < span; ++j)
+                part = fmaf(bf16_bits_to_float(w1[j]), bf16_bits_to_float(w2[j]), part);
+        }
+        part += __shfl_xor(part, 1);
+        part += __shfl_xor(part, 2);
+        part += __shfl_xor(part, 4);
+        double wt = 0.0;
+        float lt = 0.0f;
+        if (vt < V) {
+            const size_t uo = outi * (size_t)V + vt;
+            lt = (rb.u_bf16 ? bf16_bits_to_float(static_cast<const uint16_t*>(rb.U)[uo])
+                            : static_cast<const float*>(rb.U)[uo]) + part;
+            wt = exp(((double)lt - Md) * (double)invT);
+        }
+        // token t's weight and logit live in lane 8t; gather them to lanes 0..7
+        const double w8 = __shfl(wt, (lane & 7) * 8);
+        const float l8 = __shfl(lt, (lane & 7) * 8);
+        const double wl = lane < 8 ? w8 : 0.0;
+        const double tinc = wave_inclusive_scan_f64(wl);
+        double texc = __shfl_up(tinc, 1);
+        if (lane == 0) texc = 0.0;
+        unsigned long long thit = __ballot(wl > 0.0 && tinc > grem);
+        if (!thit) {
+            const unsigned long long pos = __ballot(wl > 0.0);
+            thit = pos ? 1ull << (63 - __clzll((long long)pos)) : 1ull;
+        }
+        const int tsel = __ffsll((long long)thit) - 1;
+        const float lsel = __shfl(l8, tsel);
+        (void)texc;
+        if (lane == 0) {
+            tokens[outi] = min(seg * seg_len + grp * 8 + tsel, V - 1);
+            if (q_logZ) q_logZ[outi] = (float)(Md * (double)invT + log(Z));
+            if (q_tok) q_tok[outi] = (float)(exp(((double)lsel - Md) * (double)invT) / Z);
+        }
+        return;
+    }
+
+    // 4) wave 0 rescans the segment (2 tokens per lane).
     const int v0 = seg * seg_len;
     const int v1 = min(V, v0 + seg_len);
     const float* row = q_logits + outi * (size_t)V;
@@ -708,38 +811,65 @@ int draft_segment_len(int B, int w_bf16) {
     return kTileV;
 }
 
-template <int WB, int MODE>
-static hipError_t launch_tile_wb(const DraftArgs& a, int k, hipStream_t s) {
-    const int nt = (a.V + kTileV - 1) / kTileV;
-    dim3 grid(nt, (a.B + 32 * WB - 1) / (32 * WB));
-    const size_t lds = std::max((size_t)kTileV * (a.r + kLdsPad) * sizeof(uint16_t),
+template <int WB, int MODE, int OUT>
+static hipError_t launch_tile(const TileParams& p, bool u_bf16, hipStream_t s) {
+    const int nt = (p.V + kTileV - 1) / kTileV;
+    dim3 grid(nt, (p.B + 32 * WB - 1) / (32 * WB));
+    const size_t lds = std::max((size_t)kTileV * (p.r + kLdsPad) * sizeof(uint16_t),
                                 (size_t)32 * WB * kOutLd * sizeof(float));
     // r = 256 needs 66 KB of LDS per workgroup (gfx950 has 160 KB per CU)
     static bool attr_set = false;
     if (!attr_set) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&draft_tile_mfma<WB, MODE, true>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&draft_tile_mfma<WB, MODE, false>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&draft_tile_mfma<WB, MODE, true, OUT>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&draft_tile_mfma<WB, MODE, false, OUT>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         (void)hipGetLastError();
         attr_set = true;
     }
-    if (a.u_bf16)
-        hipLaunchKernelGGL((draft_tile_mfma<WB, MODE, true>), grid, dim3(256), lds, s, a.U,
-                           (const uint16_t*)a.W1, a.W2T, a.Erows, a.x0, a.tokens,
-                           a.q_logits, a.stats, a.B, a.gamma, a.V, a.r, k, a.invT, a.greedy);
+    if (u_bf16)
+        hipLaunchKernelGGL((draft_tile_mfma<WB, MODE, true, OUT>), grid, dim3(256), lds, s, p);
     else
-        hipLaunchKernelGGL((draft_tile_mfma<WB, MODE, false>), grid, dim3(256), lds, s, a.U,
-                           (const uint16_t*)a.W1, a.W2T, a.Erows, a.x0, a.tokens,
-                           a.q_logits, a.stats, a.B, a.gamma, a.V, a.r, k, a.invT, a.greedy);
+        hipLaunchKernelGGL((draft_tile_mfma<WB, MODE, false, OUT>), grid, dim3(256), lds, s, p);
     return hipGetLastError();
 }
 
-hipError_t w2_transpose_launch(const DraftArgs& a, hipStream_t s) {
-    dim3 grid((a.V + 63) / 64, (a.r + 63) / 64);
-    hipLaunchKernelGGL(w2_transpose, grid, dim3(256), 0, s, (const uint16_t*)a.W2, a.W2T, a.r, a.V);
+template <int MODE, int OUT>
+static hipError_t launch_tile_b(const TileParams& p, bool u_bf16, hipStream_t s) {
+    const int wb = pick_wb(p.B);
+    if (wb == 1) return launch_tile<1, MODE, OUT>(p, u_bf16, s);
+    if (wb == 2) return launch_tile<2, MODE, OUT>(p, u_bf16, s);
+    return launch_tile<4, MODE, OUT>(p, u_bf16, s);
+}
+
+static TileParams tile_params(const DraftArgs& a, int k) {
+    TileParams p{};
+    p.U = a.U;
+    p.W1 = (const uint16_t*)a.W1;
+    p.W2T = a.W2T;
+    p.Erows = a.Erows;
+    p.x0 = a.x0;
+    p.tokens = a.tokens;
+    p.row_pos = nullptr;
+    p.out = a.q_logits;
+    p.stats = a.stats;
+    p.gsums = a.gsums;
+    p.B = a.B;
+    p.gamma = a.gamma;
+    p.V = a.V;
+    p.r = a.r;
+    p.k = k;
+    p.invT = a.invT;
+    p.greedy = a.greedy;
+    return p;
+}
+
+hipError_t w2_transpose_launch(const uint16_t* W2, uint16_t* W2T, int r, int V, hipStream_t s) {
+    dim3 grid((V + 63) / 64, (r + 63) / 64);
+    hipLaunchKernelGGL(w2_transpose, grid, dim3(256), 0, s, W2, W2T, r, V);
     return hipGetLastError();
 }
+
 
 hipError_t draft_tile_launch(const DraftArgs& a, int k, hipStream_t s) {
     if (!a.w_bf16) {
@@ -754,23 +884,31 @@ hipError_t draft_tile_launch(const DraftArgs& a, int k, hipStream_t s) {
                                a.stats, a.B, a.gamma, a.V, a.r, k, a.invT, a.greedy);
         return hipGetLastError();
     }
-    const int wb = pick_wb(a.B);
+    const TileParams p = tile_params(a, k);
     if (a.head == kHeadMarkov) {
-        if (wb == 1) return launch_tile_wb<1, kHeadMarkov>(a, k, s);
-        if (wb == 2) return launch_tile_wb<2, kHeadMarkov>(a, k, s);
-        return launch_tile_wb<4, kHeadMarkov>(a, k, s);
+        if (a.q_logits) return launch_tile_b<kHeadMarkov, kOutQ>(p, a.u_bf16, s);
+        return launch_tile_b<kHeadMarkov, kOutStats>(p, a.u_bf16, s);
     }
-    if (wb == 1) return launch_tile_wb<1, kHeadRnn>(a, k, s);
-    if (wb == 2) return launch_tile_wb<2, kHeadRnn>(a, k, s);
-    return launch_tile_wb<4, kHeadRnn>(a, k, s);
+    return launch_tile_b<kHeadRnn, kOutQ>(p, a.u_bf16, s);
+}
+
+hipError_t residual_rows_launch(const TileParams& p, bool u_bf16, hipStream_t s) {
+    return launch_tile_b<kHeadMarkov, kOutResidual>(p, u_bf16, s);
 }
 
 hipError_t draft_finalize_launch(const DraftArgs& a, int k, hipStream_t s) {
     const int nseg = draft_num_segments(a.B, a.V, a.w_bf16);
     const int seg = draft_segment_len(a.B, a.w_bf16);
-    hipLaunchKernelGGL(draft_finalize, dim3(a.B), dim3(256), 0, s, a.stats, nseg, seg,
-                       a.q_logits, a.x0, a.tokens, a.q_logZ, a.q_tok, a.uniforms, a.seed, a.offset,
-                       a.B, a.gamma, a.V, k, a.invT, a.greedy);
+    RebuildArgs rb;
+    rb.gsums = a.gsums;
+    rb.U = a.U;
+    rb.u_bf16 = a.u_bf16;
+    rb.W1 = (const uint16_t*)a.W1;
+    rb.W2T = a.W2T;
+    rb.r = a.r;
+    hipLaunchKernelGGL(draft_finalize, dim3(a.B), dim3(256), 0, s, a.stats, nseg, seg, a.q_logits,
+                       a.x0, a.tokens, a.q_logZ, a.q_tok, a.uniforms, a.seed, a.offset, a.B,
+                       a.gamma, a.V, k, a.invT, a.greedy, rb);
     return hipGetLastError();
 }
 

@@ -39,14 +39,43 @@ struct DraftArgs {
     float* hproj;        // RNN: [B * gamma, 3r]
     float* state;        // RNN: [2, B, r]
     uint16_t* Erows;     // RNN: [B, 3, r]
-    uint16_t* W2T;       // bf16 weights: [V, r] transposed copy of W2
+    const uint16_t* W2T; // bf16 weights: [V, r] transposed copy of W2
+    uint16_t* W2T_ws;    // workspace for that copy when the caller passes none
+    float* gsums;        // q-free draft: [B, nseg, 16] 8-token group sums
+};
+
+// Output modes of the bias tile kernel.
+enum {
+    kOutQ = 0,        // draft: store q logits + tile summaries
+    kOutStats = 1,    // q-free draft: tile summaries + 8-token group sums only
+    kOutResidual = 2  // verify: logits of row b at its own position, into [B, V]
+};
+
+// Arguments of one bias-tile launch.
+struct TileParams {
+    const void* U;            // [B, gamma, V]
+    const uint16_t* W1;       // [V, r]
+    const uint16_t* W2T;      // [V, r]
+    const uint16_t* Erows;    // RNN: [B, 3, r]
+    const int32_t* x0;        // [B]
+    const int32_t* tokens;    // [B, gamma] conditioning tokens (draft outputs)
+    const int32_t* row_pos;   // kOutResidual: position per row (-1: inactive)
+    float* out;               // kOutQ: [B, gamma, V]; kOutResidual: [B, V]
+    SegStat* stats;           // [B, nseg]
+    float* gsums;             // [B, nseg, 16]
+    int B, gamma, V, r, k;
+    float invT;
+    int greedy;
 };
 
 int draft_num_segments(int B, int V, int w_bf16);
 int draft_segment_len(int B, int w_bf16);
 hipError_t draft_tile_launch(const DraftArgs& a, int k, hipStream_t s);
 hipError_t draft_finalize_launch(const DraftArgs& a, int k, hipStream_t s);
-hipError_t w2_transpose_launch(const DraftArgs& a, hipStream_t s);
+hipError_t w2_transpose_launch(const uint16_t* W2, uint16_t* W2T, int r, int V, hipStream_t s);
+// Recompute the logits of row b at position row_pos[b] (bit-identical to the
+// draft's tile kernel) into out [B, V].
+hipError_t residual_rows_launch(const TileParams& p, bool u_bf16, hipStream_t s);
 hipError_t rnn_hidden_proj_launch(const DraftArgs& a, hipStream_t s);
 hipError_t rnn_gates_launch(const DraftArgs& a, int k, hipStream_t s);
 
@@ -87,6 +116,11 @@ struct VerifyArgs {
     float* p_logZ;
     float* q_logZ;
     float* accept_prob;
+    // q-free verification (the draft's own q(x_k) and log Z_k; no q rows)
+    const float* qprob;         // [B, gamma_max] or null
+    const float* qlogz;         // [B, gamma_max] or null
+    int32_t* row_pos;           // [B] rejected position per request (-1 none)
+    int q_single_row;           // Q holds one row per request (row b)
     // workspace carve-outs
     RowStat* rows;              // [B, 2 * gamma_max + 1]
     FinalInfo* fin;             // [B]
@@ -95,6 +129,9 @@ struct VerifyArgs {
 
 int verify_num_chunks(int V);
 hipError_t verify_launch(const VerifyArgs& a, hipStream_t s);
+// The three phases, for callers that insert work between them.
+hipError_t verify_rows_decide_launch(const VerifyArgs& a, hipStream_t s);
+hipError_t verify_final_launch(const VerifyArgs& a, hipStream_t s);
 
 hipError_t philox_uniforms_launch(uint64_t seed, uint32_t offset, uint32_t stream, int B, int K,
                                   float* out, hipStream_t s);

@@ -27,7 +27,7 @@ spec_status_t hip_fail(hipError_t e, const char* where) {
 
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }   // NULL passes
 
 bool dtype_ok(int dt) { return dt == SPEC_F32 || dt == SPEC_BF16; }
 
@@ -35,15 +35,18 @@ constexpr int kMaxV = 1 << 28;
 constexpr int kMaxDraftV = 2048 * 128;   // the finalize holds <= 8 tile summaries per thread
 
 struct DraftLayout {
-    size_t stats, w2t, hproj, state, erows, total;
+    size_t stats, gsums, w2t, hproj, state, erows, total;
 };
 
 DraftLayout draft_layout(bool rnn, int B, int gamma, int V, int r) {
     DraftLayout L{};
     size_t off = 0;
+    const size_t nseg = (size_t)draft_num_segments(B, V, 1);
     L.stats = off;
-    off += align_up((size_t)B * draft_num_segments(B, V, 1) * sizeof(SegStat));
-    L.w2t = off;   // transposed bf16 W2 (also reserved for fp32 weights)
+    off += align_up((size_t)B * nseg * sizeof(SegStat));
+    L.gsums = off;   // q-free draft: 16 group sums per (row, tile)
+    off += align_up((size_t)B * nseg * 16 * sizeof(float));
+    L.w2t = off;   // transposed bf16 W2 when the caller passes no packed copy
     off += align_up((size_t)V * r * sizeof(uint16_t));
     if (rnn) {
         L.hproj = off;
@@ -58,10 +61,12 @@ DraftLayout draft_layout(bool rnn, int B, int gamma, int V, int r) {
 }
 
 struct VerifyLayout {
-    size_t rows, fin, chunks, total;
+    size_t rows, fin, chunks, rowpos, lrows, w2t, total;
 };
 
-VerifyLayout verify_layout(int B, int gamma_max, int V) {
+// markov_r > 0 adds the q-free verification buffers: the recomputed logits of
+// one row per request and a transposed W2.
+VerifyLayout verify_layout(int B, int gamma_max, int V, int markov_r = 0) {
     VerifyLayout L{};
     size_t off = 0;
     L.rows = off;
@@ -70,6 +75,14 @@ VerifyLayout verify_layout(int B, int gamma_max, int V) {
     off += align_up((size_t)B * sizeof(FinalInfo));
     L.chunks = off;
     off += align_up((size_t)B * verify_num_chunks(V) * sizeof(double));
+    if (markov_r > 0) {
+        L.rowpos = off;
+        off += align_up((size_t)B * sizeof(int32_t));
+        L.lrows = off;
+        off += align_up((size_t)B * V * sizeof(float));
+        L.w2t = off;
+        off += align_up((size_t)V * markov_r * sizeof(uint16_t));
+    }
     L.total = off;
     return L;
 }
@@ -93,7 +106,8 @@ spec_status_t check_T(float T) {
 // Shared validation of the draft entry points (both heads).
 spec_status_t check_draft_common(const void* U, int U_dtype, const int32_t* x0, const void* W1,
                                  const void* W2, int w_dtype, int r, int B, int gamma, int V,
-                                 float T, int32_t* tokens, float* q_logits) {
+                                 float T, int32_t* tokens, float* q_logits, float* q_logZ,
+                                 float* q_tok_prob, const void* W2T) {
     if (B < 0 || gamma < 0) return fail(SPEC_ERR_INVALID, "B and gamma must be >= 0");
     if (V <= 0 || V > kMaxV) return fail(SPEC_ERR_INVALID, "V must be in [1, 2^28]");
     if (r <= 0) return fail(SPEC_ERR_INVALID, "rank r must be > 0");
@@ -103,10 +117,19 @@ spec_status_t check_draft_common(const void* U, int U_dtype, const int32_t* x0, 
     if (!dtype_ok(U_dtype) || !dtype_ok(w_dtype)) return fail(SPEC_ERR_UNSUPPORTED, "dtype must be SPEC_F32 or SPEC_BF16");
     if ((int64_t)B * gamma > INT32_MAX) return fail(SPEC_ERR_UNSUPPORTED, "B * gamma too large");
     if (B == 0 || gamma == 0) return SPEC_OK;
-    if (!U || !x0 || !W1 || !W2 || !tokens || !q_logits)
-        return fail(SPEC_ERR_INVALID, "null required pointer (U, x0, W1, W2, tokens, q_logits)");
-    if (!aligned16(U) || !aligned16(W1) || !aligned16(W2) || !aligned16(q_logits))
-        return fail(SPEC_ERR_UNSUPPORTED, "U, W1, W2 and q_logits must be 16-byte aligned");
+    if (!U || !x0 || !W1 || !(W2 || W2T) || !tokens)
+        return fail(SPEC_ERR_INVALID, "null required pointer (U, x0, W1, W2 or W2T, tokens)");
+    if (!q_logits && (!q_logZ || !q_tok_prob))
+        return fail(SPEC_ERR_INVALID, "without q_logits, q_logZ and q_tok_prob are required");
+    if (!q_logits && w_dtype != SPEC_BF16)
+        return fail(SPEC_ERR_UNSUPPORTED, "the q-free draft (q_logits == NULL) needs bf16 weights");
+    if (W2T && w_dtype != SPEC_BF16)
+        return fail(SPEC_ERR_UNSUPPORTED, "a packed W2T is bf16 only");
+    if (!W2 && w_dtype != SPEC_BF16)
+        return fail(SPEC_ERR_INVALID, "fp32 weights need W2");
+    if (!aligned16(U) || !aligned16(W1) || !aligned16(W2) || !aligned16(W2T) ||
+        !aligned16(q_logits))
+        return fail(SPEC_ERR_UNSUPPORTED, "U, W1, W2, W2T and q_logits must be 16-byte aligned");
     if (w_dtype == SPEC_BF16 && (r % 16 != 0 || r > 256))
         return fail(SPEC_ERR_UNSUPPORTED, "bf16 weights need r % 16 == 0 and r <= 256");
     return SPEC_OK;
@@ -116,11 +139,12 @@ spec_status_t run_draft(DraftArgs& a, void* stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     void* t;
-    if (a.w_bf16) {
+    if (a.w_bf16 && !a.W2T) {
         t = prof_begin("w2_transpose", s);
-        e = w2_transpose_launch(a, s);
+        e = w2_transpose_launch((const uint16_t*)a.W2, a.W2T_ws, a.r, a.V, s);
         prof_end(t, s);
         if (e != hipSuccess) return hip_fail(e, "w2_transpose");
+        a.W2T = a.W2T_ws;
     }
     if (a.head == kHeadRnn) {
         t = prof_begin("rnn_hidden_proj", s);
@@ -172,14 +196,15 @@ size_t spec_draft_markov_workspace_size(int B, int gamma, int V, int r) {
 }
 
 spec_status_t spec_draft_sample_markov(const void* U, int U_dtype, const int32_t* x0,
-                                       const void* W1, const void* W2, int w_dtype, int r, int B,
-                                       int gamma, int V, float T, const float* uniforms,
-                                       uint64_t seed, uint32_t offset, int32_t* tokens,
-                                       float* q_logits, float* q_logZ, float* q_tok_prob,
-                                       void* ws, size_t ws_bytes, void* stream) {
+                                       const void* W1, const void* W2, const void* W2T,
+                                       int w_dtype, int r, int B, int gamma, int V, float T,
+                                       const float* uniforms, uint64_t seed, uint32_t offset,
+                                       int32_t* tokens, float* q_logits, float* q_logZ,
+                                       float* q_tok_prob, void* ws, size_t ws_bytes,
+                                       void* stream) {
     g_err.clear();
     if (spec_status_t st = check_draft_common(U, U_dtype, x0, W1, W2, w_dtype, r, B, gamma, V, T,
-                                              tokens, q_logits))
+                                              tokens, q_logits, q_logZ, q_tok_prob, W2T))
         return st;
     if (B == 0 || gamma == 0) return SPEC_OK;
     const DraftLayout L = draft_layout(false, B, gamma, V, r);
@@ -207,7 +232,9 @@ spec_status_t spec_draft_sample_markov(const void* U, int U_dtype, const int32_t
     a.q_logZ = q_logZ;
     a.q_tok = q_tok_prob;
     a.stats = reinterpret_cast<SegStat*>(w + L.stats);
-    a.W2T = reinterpret_cast<uint16_t*>(w + L.w2t);
+    a.gsums = reinterpret_cast<float*>(w + L.gsums);
+    a.W2T = static_cast<const uint16_t*>(W2T);
+    a.W2T_ws = reinterpret_cast<uint16_t*>(w + L.w2t);
     return run_draft(a, stream);
 }
 
@@ -218,15 +245,18 @@ size_t spec_draft_rnn_workspace_size(int B, int gamma, int V, int r, int d) {
 
 spec_status_t spec_draft_sample_rnn(const void* U, int U_dtype, const int32_t* x0, const void* h,
                                     int h_dtype, int d, const void* W1, const void* W2,
-                                    const void* Wg, const void* Wc, const void* Wo, int w_dtype,
-                                    int r, int B, int gamma, int V, float T,
-                                    const float* uniforms, uint64_t seed, uint32_t offset,
-                                    int32_t* tokens, float* q_logits, float* q_logZ,
-                                    float* q_tok_prob, void* ws, size_t ws_bytes, void* stream) {
+                                    const void* W2T, const void* Wg, const void* Wc,
+                                    const void* Wo, int w_dtype, int r, int B, int gamma, int V,
+                                    float T, const float* uniforms, uint64_t seed,
+                                    uint32_t offset, int32_t* tokens, float* q_logits,
+                                    float* q_logZ, float* q_tok_prob, void* ws, size_t ws_bytes,
+                                    void* stream) {
     g_err.clear();
     if (spec_status_t st = check_draft_common(U, U_dtype, x0, W1, W2, w_dtype, r, B, gamma, V, T,
-                                              tokens, q_logits))
+                                              tokens, q_logits, q_logZ, q_tok_prob, W2T))
         return st;
+    if (B > 0 && gamma > 0 && !q_logits)
+        return fail(SPEC_ERR_UNSUPPORTED, "the RNN head needs q_logits");
     if (d < 0) return fail(SPEC_ERR_INVALID, "hidden size d must be >= 0");
     if (!dtype_ok(h_dtype)) return fail(SPEC_ERR_UNSUPPORTED, "dtype must be SPEC_F32 or SPEC_BF16");
     if (B == 0 || gamma == 0) return SPEC_OK;
@@ -269,7 +299,9 @@ spec_status_t spec_draft_sample_rnn(const void* U, int U_dtype, const int32_t* x
     a.hproj = reinterpret_cast<float*>(w + L.hproj);
     a.state = reinterpret_cast<float*>(w + L.state);
     a.Erows = reinterpret_cast<uint16_t*>(w + L.erows);
-    a.W2T = reinterpret_cast<uint16_t*>(w + L.w2t);
+    a.gsums = reinterpret_cast<float*>(w + L.gsums);
+    a.W2T = static_cast<const uint16_t*>(W2T);
+    a.W2T_ws = reinterpret_cast<uint16_t*>(w + L.w2t);
     return run_draft(a, stream);
 }
 
@@ -325,6 +357,115 @@ spec_status_t spec_verify(const void* P, int p_dtype, const void* Q, int q_dtype
     a.fin = reinterpret_cast<FinalInfo*>(w + L.fin);
     a.chunk_sums = reinterpret_cast<double*>(w + L.chunks);
     hipError_t e = verify_launch(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SPEC_OK : hip_fail(e, "verify");
+}
+
+spec_status_t spec_pack_w2(const void* W2, void* W2T, int r, int V, void* stream) {
+    g_err.clear();
+    if (r <= 0 || V <= 0 || V > kMaxV) return fail(SPEC_ERR_INVALID, "bad r or V");
+    if (!W2 || !W2T) return fail(SPEC_ERR_INVALID, "null W2 or W2T");
+    if (!aligned16(W2T)) return fail(SPEC_ERR_UNSUPPORTED, "W2T must be 16-byte aligned");
+    hipError_t e = w2_transpose_launch(static_cast<const uint16_t*>(W2),
+                                       static_cast<uint16_t*>(W2T), r, V,
+                                       static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SPEC_OK : hip_fail(e, "w2_transpose");
+}
+
+size_t spec_verify_markov_workspace_size(int B, int gamma_max, int V, int r) {
+    if (B <= 0 || gamma_max < 0 || V <= 0 || r <= 0) return 0;
+    return verify_layout(B, gamma_max, V, r).total;
+}
+
+spec_status_t spec_verify_markov(const void* P, int p_dtype, const void* U, int U_dtype,
+                                 const int32_t* x0, const void* W1, const void* W2,
+                                 const void* W2T, int w_dtype, int r, const int32_t* draft,
+                                 const float* q_logZ, const float* q_tok_prob,
+                                 const int32_t* lens, const int64_t* p_row_off, int B,
+                                 int gamma_max, int V, float T, const float* uniforms,
+                                 uint64_t seed, uint32_t offset, int32_t* accepted,
+                                 int32_t* out_tokens, float* p_logZ, float* accept_prob,
+                                 void* ws, size_t ws_bytes, void* stream) {
+    g_err.clear();
+    if (B < 0 || gamma_max < 0) return fail(SPEC_ERR_INVALID, "B and gamma_max must be >= 0");
+    if (V <= 0 || V > kMaxDraftV) return fail(SPEC_ERR_INVALID, "V must be in [1, 262144]");
+    if (r <= 0) return fail(SPEC_ERR_INVALID, "rank r must be > 0");
+    if (spec_status_t st = check_T(T)) return st;
+    if (!dtype_ok(p_dtype) || !dtype_ok(U_dtype)) return fail(SPEC_ERR_UNSUPPORTED, "dtype must be SPEC_F32 or SPEC_BF16");
+    if (w_dtype != SPEC_BF16 || r % 16 != 0 || r > 256)
+        return fail(SPEC_ERR_UNSUPPORTED, "q-free verification needs bf16 weights, r % 16 == 0, r <= 256");
+    if ((int64_t)B * gamma_max > INT32_MAX) return fail(SPEC_ERR_UNSUPPORTED, "B * gamma_max too large");
+    if (B == 0) return SPEC_OK;
+    if (!P || !accepted || !out_tokens) return fail(SPEC_ERR_INVALID, "null required pointer (P, accepted, out_tokens)");
+    if (gamma_max > 0 && (!U || !x0 || !W1 || !(W2 || W2T) || !draft || !q_logZ || !q_tok_prob))
+        return fail(SPEC_ERR_INVALID, "null required pointer (U, x0, W1, W2 or W2T, draft, q_logZ, q_tok_prob)");
+    if (!aligned16(P) || !aligned16(U) || !aligned16(W1) || !aligned16(W2) || !aligned16(W2T))
+        return fail(SPEC_ERR_UNSUPPORTED, "P, U, W1, W2 and W2T must be 16-byte aligned");
+    const VerifyLayout L = verify_layout(B, gamma_max, V, r);
+    if (spec_status_t st = check_ws(ws, ws_bytes, L.total)) return st;
+    char* w = static_cast<char*>(ws);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    VerifyArgs a{};
+    a.P = P;
+    a.p_bf16 = p_dtype == SPEC_BF16;
+    a.Q = w + L.lrows;             // recomputed logits, one row per request
+    a.q_bf16 = 0;
+    a.q_single_row = 1;
+    a.draft = draft;
+    a.lens = lens;
+    a.p_row_off = p_row_off;
+    a.q_row_off = nullptr;
+    a.B = B;
+    a.gamma_max = gamma_max;
+    a.V = V;
+    a.greedy = T == 0.0f;
+    a.invT = a.greedy ? 1.0f : 1.0f / T;
+    a.uniforms = uniforms;
+    a.seed = seed;
+    a.offset = offset;
+    a.accepted = accepted;
+    a.out_tokens = out_tokens;
+    a.p_logZ = p_logZ;
+    a.q_logZ = nullptr;
+    a.accept_prob = accept_prob;
+    a.qprob = q_tok_prob;
+    a.qlogz = q_logZ;
+    a.row_pos = reinterpret_cast<int32_t*>(w + L.rowpos);
+    a.rows = reinterpret_cast<RowStat*>(w + L.rows);
+    a.fin = reinterpret_cast<FinalInfo*>(w + L.fin);
+    a.chunk_sums = reinterpret_cast<double*>(w + L.chunks);
+    hipError_t e = verify_rows_decide_launch(a, s);
+    if (e != hipSuccess) return hip_fail(e, "verify");
+    if (!a.greedy && gamma_max > 0) {
+        const uint16_t* w2t = static_cast<const uint16_t*>(W2T);
+        if (!w2t) {
+            void* t = prof_begin("w2_transpose", s);
+            e = w2_transpose_launch(static_cast<const uint16_t*>(W2),
+                                    reinterpret_cast<uint16_t*>(w + L.w2t), r, V, s);
+            prof_end(t, s);
+            if (e != hipSuccess) return hip_fail(e, "w2_transpose");
+            w2t = reinterpret_cast<const uint16_t*>(w + L.w2t);
+        }
+        TileParams tp{};
+        tp.U = U;
+        tp.W1 = static_cast<const uint16_t*>(W1);
+        tp.W2T = w2t;
+        tp.x0 = x0;
+        tp.tokens = draft;
+        tp.row_pos = a.row_pos;
+        tp.out = reinterpret_cast<float*>(w + L.lrows);
+        tp.B = B;
+        tp.gamma = gamma_max;
+        tp.V = V;
+        tp.r = r;
+        tp.k = 0;
+        tp.invT = a.invT;
+        tp.greedy = 0;
+        void* t = prof_begin("verify_residual_rows", s);
+        e = residual_rows_launch(tp, U_dtype == SPEC_BF16, s);
+        prof_end(t, s);
+        if (e != hipSuccess) return hip_fail(e, "verify_residual_rows");
+    }
+    e = verify_final_launch(a, s);
     return e == hipSuccess ? SPEC_OK : hip_fail(e, "verify");
 }
 

@@ -36,6 +36,7 @@ __device__ __forceinline__ int64_t p_row(const VerifyArgs& a, int b, int k) {
 }
 
 __device__ __forceinline__ int64_t q_row(const VerifyArgs& a, int b, int k) {
+    if (a.q_single_row) return b;
     return (a.q_row_off ? a.q_row_off[b] : (int64_t)b * a.gamma_max) + k;
 }
 
@@ -199,7 +200,7 @@ void verify_decide(VerifyArgs a) {
         for (int k = lane; k <= L; k += kWave) {
             if (k < L && (dr[k] < 0 || dr[k] >= a.V)) bad_l = true;
             if (rs[k].m == -INFINITY) bad_l = true;
-            if (k < L && rs[G + 1 + k].m == -INFINITY) bad_l = true;
+            if (k < L && !a.qprob && rs[G + 1 + k].m == -INFINITY) bad_l = true;
         }
     }
     if (__ballot(bad_l)) {
@@ -211,6 +212,7 @@ void verify_decide(VerifyArgs a) {
         }
         if (lane == 0) {
             a.accepted[b] = -1;
+            if (a.row_pos) a.row_pos[b] = -1;
             FinalInfo f;
             f.logZp = 0.0;
             f.logZq = 0.0;
@@ -235,15 +237,21 @@ void verify_decide(VerifyArgs a) {
         }
         if (k < L) {
             const RowStat p = rs[k];
-            const RowStat q = rs[G + 1 + k];
+            const RowStat q = a.qprob ? p : rs[G + 1 + k];
             if (a.greedy) {
-                lzq = (double)q.m;
+                lzq = a.qlogz ? (double)a.qlogz[(size_t)b * G + k] : (double)q.m;
                 reject = p.idx != dr[k];
                 ap = reject ? 0.0 : 1.0;
             } else {
-                lzq = (double)q.m * invT + log((double)q.s);
                 const double px = exp((double)p.gathered * invT - lzp);
-                const double qx = exp((double)q.gathered * invT - lzq);
+                double qx;
+                if (a.qprob) {   // the draft's own q(x_k) and normaliser
+                    lzq = (double)a.qlogz[(size_t)b * G + k];
+                    qx = (double)a.qprob[(size_t)b * G + k];
+                } else {
+                    lzq = (double)q.m * invT + log((double)q.s);
+                    qx = exp((double)q.gathered * invT - lzq);
+                }
                 ap = qx > 0.0 ? fmin(1.0, px / qx) : (px > 0.0 ? 1.0 : 0.0);
                 const float u = a.uniforms ? a.uniforms[(size_t)b * (G + 1) + k]
                                            : counter_uniform(a.seed, a.offset, b, k, 1);
@@ -268,6 +276,7 @@ void verify_decide(VerifyArgs a) {
     if (lane == 0) {
         if (a.greedy) out[n] = rs[n].idx;
         a.accepted[b] = n;
+        if (a.row_pos) a.row_pos[b] = (!a.greedy && n < L) ? n : -1;
         FinalInfo f;
         f.logZp = lzp_n;
         f.logZq = lzq_n;
@@ -574,14 +583,20 @@ static void launch_rows(const VerifyArgs& a, int is_q, hipStream_t s) {
     prof_end(t, s);
 }
 
-hipError_t verify_launch(const VerifyArgs& a, hipStream_t s) {
+hipError_t verify_rows_decide_launch(const VerifyArgs& a, hipStream_t s) {
     if (a.p_bf16) launch_rows<true>(a, 0, s);
     else launch_rows<false>(a, 0, s);
-    if (a.q_bf16) launch_rows<true>(a, 1, s);
-    else launch_rows<false>(a, 1, s);
+    if (!a.qprob) {
+        if (a.q_bf16) launch_rows<true>(a, 1, s);
+        else launch_rows<false>(a, 1, s);
+    }
     void* t = prof_begin("verify_decide", s);
     hipLaunchKernelGGL(verify_decide, dim3((a.B + 3) / 4), dim3(256), 0, s, a);
     prof_end(t, s);
+    return hipGetLastError();
+}
+
+hipError_t verify_final_launch(const VerifyArgs& a, hipStream_t s) {
     if (!a.greedy) {
         if (a.p_bf16 && a.q_bf16) launch_final<true, true>(a, s);
         else if (a.p_bf16) launch_final<true, false>(a, s);
@@ -589,6 +604,12 @@ hipError_t verify_launch(const VerifyArgs& a, hipStream_t s) {
         else launch_final<false, false>(a, s);
     }
     return hipGetLastError();
+}
+
+hipError_t verify_launch(const VerifyArgs& a, hipStream_t s) {
+    hipError_t e = verify_rows_decide_launch(a, s);
+    if (e != hipSuccess) return e;
+    return verify_final_launch(a, s);
 }
 
 hipError_t philox_uniforms_launch(uint64_t seed, uint32_t offset, uint32_t stream, int B, int K,

@@ -101,12 +101,19 @@ spec_status_t spec_philox_uniforms(uint64_t seed, uint32_t offset, uint32_t stre
  * W2       [r, V]         logit projection, dtype w_dtype
  *                         (BF16 runs on MFMA with fp32 accumulation; F32 runs
  *                         on the vector ALUs)
+ * W2T      [V, r]         optional: W2 already packed by spec_pack_w2 (bf16
+ *                         only).  NULL: W2 is packed into the workspace on
+ *                         every call.  W2 may be NULL when W2T is given.
  * uniforms [B, gamma]     optional caller uniforms (stream 0 otherwise)
  * tokens   [B, gamma]     out: int32 draft tokens
  * q_logits [B, gamma, V]  out: fp32 draft logits l BEFORE temperature; pass
- *                         them unchanged (with the same T) to spec_verify
- * q_logZ   [B, gamma]     optional out: ln sum_v exp(l[v] / T) (T == 0: max l)
- * q_tok_prob [B, gamma]   optional out: q(tokens[b, k]) (T == 0: 1)
+ *                         them unchanged (with the same T) to spec_verify.
+ *                         NULL selects the q-free draft (bf16 weights): no
+ *                         logits are written, q_logZ and q_tok_prob become
+ *                         required, and spec_verify_markov verifies the block.
+ * q_logZ   [B, gamma]     out: ln sum_v exp(l[v] / T) (T == 0: max l)
+ * q_tok_prob [B, gamma]   out: q(tokens[b, k]) (T == 0: 1)
+ *                         (both optional when q_logits is given)
  * Errors: SPEC_ERR_INVALID for null required pointers, B < 0, gamma < 0,
  * V <= 0, r <= 0, T < 0 or NaN; SPEC_ERR_UNSUPPORTED for other dtypes;
  * SPEC_ERR_WORKSPACE if ws_bytes < spec_draft_markov_workspace_size(...).
@@ -117,11 +124,19 @@ size_t spec_draft_markov_workspace_size(int B, int gamma, int V, int r);
 
 spec_status_t spec_draft_sample_markov(
     const void *U, int U_dtype, const int32_t *x0,
-    const void *W1, const void *W2, int w_dtype, int r,
+    const void *W1, const void *W2, const void *W2T, int w_dtype, int r,
     int B, int gamma, int V, float T,
     const float *uniforms, uint64_t seed, uint32_t offset,
     int32_t *tokens, float *q_logits, float *q_logZ, float *q_tok_prob,
     void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * W2 [r, V] bf16 -> W2T [V, r] bf16: the layout the bias contraction stages
+ * per vocabulary tile.  Weights are static, so callers pack once and pass
+ * W2T to the draft and verify calls.  W2T: caller-owned device buffer of
+ * V * r bf16, 16-byte aligned.
+ */
+spec_status_t spec_pack_w2(const void *W2, void *W2T, int r, int V, void *stream);
 
 /*
  * ---------------------------------------------------------------------------
@@ -136,15 +151,16 @@ spec_status_t spec_draft_sample_markov(
  * Wg, Wc, Wo [r, 2r + d]  gate matrices, dtype w_dtype (BF16), no bias terms
  * The state s and o are kept in fp32; o enters the W2 contraction as an
  * exact three-term bf16 split so the bf16 MFMA path keeps fp32 accuracy.
- * Other arguments, outputs and errors as spec_draft_sample_markov.
+ * Other arguments, outputs and errors as spec_draft_sample_markov, except that
+ * q_logits is required (no q-free RNN draft).
  */
 size_t spec_draft_rnn_workspace_size(int B, int gamma, int V, int r, int d);
 
 spec_status_t spec_draft_sample_rnn(
     const void *U, int U_dtype, const int32_t *x0,
     const void *h, int h_dtype, int d,
-    const void *W1, const void *W2, const void *Wg, const void *Wc, const void *Wo,
-    int w_dtype, int r,
+    const void *W1, const void *W2, const void *W2T,
+    const void *Wg, const void *Wc, const void *Wo, int w_dtype, int r,
     int B, int gamma, int V, float T,
     const float *uniforms, uint64_t seed, uint32_t offset,
     int32_t *tokens, float *q_logits, float *q_logZ, float *q_tok_prob,
@@ -199,12 +215,42 @@ spec_status_t spec_verify(
 
 /*
  * ---------------------------------------------------------------------------
+ * Lossless verification of a q-free Markov draft
+ * [VESSL "알고리즘", "수락 규칙"; DSpark §1.2 Markov-head eq.]
+ * ---------------------------------------------------------------------------
+ * The same acceptance rule as spec_verify, for a block drafted with
+ * q_logits == NULL.  q_k(x_k) and the normaliser of q_k come from the draft
+ * (q_tok_prob, q_logZ); the draft row that feeds a correction is rebuilt as
+ * l_n = U[b, n] + W1[x_{n-1}] W2 with the draft's own tile kernel, so it is
+ * bit-identical to the logits the draft sampled from.  Only target rows are
+ * streamed.
+ * U, x0, W1, W2/W2T, w_dtype, r  as passed to spec_draft_sample_markov
+ * (U dense [B, gamma_max, V]); draft [B, gamma_max] = the draft's tokens;
+ * q_logZ, q_tok_prob [B, gamma_max] = the draft's outputs (same T).
+ * P, lens, p_row_off, uniforms, accepted, out_tokens, p_logZ, accept_prob:
+ * as spec_verify.  Needs bf16 weights and V <= 262144.
+ */
+size_t spec_verify_markov_workspace_size(int B, int gamma_max, int V, int r);
+
+spec_status_t spec_verify_markov(
+    const void *P, int p_dtype, const void *U, int U_dtype, const int32_t *x0,
+    const void *W1, const void *W2, const void *W2T, int w_dtype, int r,
+    const int32_t *draft, const float *q_logZ, const float *q_tok_prob,
+    const int32_t *lens, const int64_t *p_row_off,
+    int B, int gamma_max, int V, float T,
+    const float *uniforms, uint64_t seed, uint32_t offset,
+    int32_t *accepted, int32_t *out_tokens, float *p_logZ, float *accept_prob,
+    void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * ---------------------------------------------------------------------------
  * Kernel timing (benchmarking aid; not needed for correct use)
  * ---------------------------------------------------------------------------
  * spec_profile_enable(name) starts a fresh record: from then on every launch
  * of the kernel `name` ("draft_tile", "draft_finalize", "rnn_hidden_proj",
- * "rnn_gates", "verify_rows_p", "verify_rows_q", "verify_decide",
- * "verify_final_partials", "verify_final_draw", or "*" for all) is bracketed
+ * "rnn_gates", "w2_transpose", "verify_rows_p", "verify_rows_q",
+ * "verify_decide", "verify_residual_rows", "verify_final_partials",
+ * "verify_final_draw", or "*" for all) is bracketed
  * by two hipEvents recorded on its launch stream.  NULL or "" stops timing.
  * spec_profile_read waits for the recorded events and returns the number of
  * timed launches and their summed duration in milliseconds.  Process-wide

@@ -34,7 +34,8 @@ def test_header_declares_the_boundary():
     for n in ("spec_draft_sample_markov", "spec_draft_sample_rnn", "spec_verify",
               "spec_draft_markov_workspace_size", "spec_draft_rnn_workspace_size",
               "spec_verify_workspace_size", "spec_philox_uniforms", "spec_last_error",
-              "spec_version"):
+              "spec_version", "spec_pack_w2", "spec_verify_markov",
+              "spec_verify_markov_workspace_size"):
         assert n in names
 
 
@@ -54,7 +55,7 @@ def test_workspace_sizes(lib):
 
 def _markov(lib, **kw):
     fake = ctypes.c_void_p(4096)   # never dereferenced: validation fails first
-    a = dict(U=fake, U_dtype=0, x0=fake, W1=fake, W2=fake, w_dtype=1, r=256, B=2, gamma=3,
+    a = dict(U=fake, U_dtype=0, x0=fake, W1=fake, W2=fake, W2T=None, w_dtype=1, r=256, B=2, gamma=3,
              V=1000, T=1.0, uniforms=None, seed=0, offset=0, tokens=fake, q_logits=fake,
              q_logZ=None, q_tok=None, ws=None, ws_bytes=0, stream=None)
     a.update(kw)
@@ -62,6 +63,7 @@ def _markov(lib, **kw):
 
 
 def test_markov_validation(lib):
+    fake = ctypes.c_void_p(4096)
     assert _markov(lib, U=None) == SPEC_ERR_INVALID
     assert _markov(lib, B=-1) == SPEC_ERR_INVALID
     assert _markov(lib, V=0) == SPEC_ERR_INVALID
@@ -78,6 +80,15 @@ def test_markov_validation(lib):
     assert "workspace" in lib.spec_last_error().decode()
     assert _markov(lib, B=0) == SPEC_OK                        # empty batch: nothing to do
     assert _markov(lib, gamma=0) == SPEC_OK
+    # q-free mode (q_logits NULL): needs q_logZ and q_tok_prob and bf16 weights
+    assert _markov(lib, q_logits=None) == SPEC_ERR_INVALID
+    assert _markov(lib, q_logits=None, q_logZ=fake, q_tok=fake, w_dtype=0) == SPEC_ERR_UNSUPPORTED
+    assert _markov(lib, q_logits=None, q_logZ=fake, q_tok=fake) == SPEC_ERR_WORKSPACE
+    # a packed W2T may stand in for W2 (bf16 only)
+    assert _markov(lib, W2=None) == SPEC_ERR_INVALID
+    assert _markov(lib, W2=None, W2T=fake) == SPEC_ERR_WORKSPACE
+    assert _markov(lib, W2T=fake, w_dtype=0) == SPEC_ERR_UNSUPPORTED
+    assert _markov(lib, W2T=ctypes.c_void_p(4104)) == SPEC_ERR_UNSUPPORTED
 
 
 def _verify(lib, **kw):
@@ -103,7 +114,7 @@ def test_verify_validation(lib):
 
 def test_rnn_validation(lib):
     fake = ctypes.c_void_p(4096)
-    base = dict(U=fake, U_dtype=0, x0=fake, h=fake, h_dtype=1, d=64, W1=fake, W2=fake, Wg=fake,
+    base = dict(U=fake, U_dtype=0, x0=fake, h=fake, h_dtype=1, d=64, W1=fake, W2=fake, W2T=None, Wg=fake,
                 Wc=fake, Wo=fake, w_dtype=1, r=32, B=2, gamma=2, V=500, T=1.0, uniforms=None,
                 seed=0, offset=0, tokens=fake, q_logits=fake, q_logZ=None, q_tok=None, ws=None,
                 ws_bytes=0, stream=None)
@@ -117,7 +128,43 @@ def test_rnn_validation(lib):
     assert call(d=-1) == SPEC_ERR_INVALID
     assert call(d=12) == SPEC_ERR_UNSUPPORTED
     assert call(w_dtype=0) == SPEC_ERR_UNSUPPORTED
+    assert call(q_logits=None, q_logZ=fake, q_tok=fake) == SPEC_ERR_UNSUPPORTED
     assert call() == SPEC_ERR_WORKSPACE
+
+
+def _verify_markov(lib, **kw):
+    fake = ctypes.c_void_p(4096)
+    a = dict(P=fake, p_dtype=1, U=fake, U_dtype=0, x0=fake, W1=fake, W2=fake, W2T=None,
+             w_dtype=1, r=64, draft=fake, q_logZ=fake, q_tok=fake, lens=None, p_off=None, B=2,
+             G=3, V=1000, T=1.0, uniforms=None, seed=0, offset=0, accepted=fake, out=fake,
+             p_logZ=None, ap=None, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return lib.spec_verify_markov(*a.values())
+
+
+def test_verify_markov_validation(lib):
+    fake = ctypes.c_void_p(4096)
+    assert _verify_markov(lib, P=None) == SPEC_ERR_INVALID
+    assert _verify_markov(lib, q_logZ=None) == SPEC_ERR_INVALID
+    assert _verify_markov(lib, W2=None) == SPEC_ERR_INVALID
+    assert _verify_markov(lib, G=-1) == SPEC_ERR_INVALID
+    assert _verify_markov(lib, V=300000) == SPEC_ERR_INVALID
+    assert _verify_markov(lib, w_dtype=0) == SPEC_ERR_UNSUPPORTED
+    assert _verify_markov(lib, r=40) == SPEC_ERR_UNSUPPORTED
+    assert _verify_markov(lib, U=ctypes.c_void_p(4100)) == SPEC_ERR_UNSUPPORTED
+    assert _verify_markov(lib) == SPEC_ERR_WORKSPACE
+    assert _verify_markov(lib, W2=None, W2T=fake) == SPEC_ERR_WORKSPACE
+    assert _verify_markov(lib, G=0, U=None, draft=None, q_logZ=None) == SPEC_ERR_WORKSPACE
+    assert _verify_markov(lib, B=0) == SPEC_OK
+    assert lib.spec_verify_markov_workspace_size(4, 3, 1000, 64) > \
+        lib.spec_verify_workspace_size(4, 3, 1000)
+
+
+def test_pack_w2_validation(lib):
+    fake = ctypes.c_void_p(4096)
+    assert lib.spec_pack_w2(None, fake, 64, 1000, None) == SPEC_ERR_INVALID
+    assert lib.spec_pack_w2(fake, fake, 0, 1000, None) == SPEC_ERR_INVALID
+    assert lib.spec_pack_w2(fake, ctypes.c_void_p(4098), 64, 1000, None) == SPEC_ERR_UNSUPPORTED
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -1,0 +1,288 @@
+"""GPU parity of the q-free Markov cycle against the oracle.
+
+The q-free draft writes no draft-logit tensor: per position it returns the
+token, the draft normaliser log Z and q(x_k), and locates the token from
+8-token group sums plus a rebuild of one group's logits.  spec_verify_markov
+takes those three outputs and rebuilds, for each request that needs a
+residual draw, the single draft row q_n = U_n + W1[x_{n-1}] W2.  Both are
+checked element by element against the oracle on the same seeded inputs;
+the oracle never sees a GPU output."""
+import numpy as np
+import pytest
+
+import workloads
+from oracle import compare
+from tests.gpu_util import dev, host, note, require_gpu, torch
+
+pytestmark = pytest.mark.gpu
+
+
+def _cfg(name, logit_dtype, seed, **kw):
+    cfg = dict(workloads.CONFIGS[name])
+    cfg.update(logit_dtype=logit_dtype, w_dtype="bf16", data_seed=seed, **kw)
+    return cfg
+
+
+def _weights(wl):
+    return workloads.as_f64(wl["W1"], "bf16"), workloads.as_f64(wl["W2"], "bf16")
+
+
+DRAFT_CASES = [
+    # B, gamma, V, r, U dtype, T
+    (3, 5, 5000, 64, "f32", 1.0),       # 32-row groups
+    (40, 3, 3000, 32, "bf16", 1.0),     # 64-row groups
+    (70, 3, 2000, 256, "f32", 0.8),     # 128-row groups
+    (130, 2, 1500, 128, "bf16", 1.0),   # two row blocks
+    (5, 4, 4099, 48, "f32", 1.3),       # ragged last tile (3 tokens)
+    (4, 6, 131, 16, "f32", 1.0),        # two tiles
+    (3, 4, 7, 16, "bf16", 1.0),         # one partial 8-token group
+    (6, 4, 3000, 64, "bf16", 0.0),      # greedy
+]
+
+
+@pytest.mark.parametrize("B,gamma,V,r,udt,T", DRAFT_CASES)
+def test_qfree_draft_parity(orc, B, gamma, V, r, udt, T):
+    sd = require_gpu()
+    note(f"q-free draft B={B} gamma={gamma} V={V} r={r} U={udt} T={T}")
+    wl = workloads.make_markov(_cfg("markov-32k-b32", udt, 300 + B + V, w_std=0.3), B=B,
+                               gamma=gamma, V=V, r=r)
+    seed, offset = 17, 5
+    g = host(sd.spec_draft_sample_markov(dev(wl["U"], udt), dev(wl["x0"]), dev(wl["W1"], "bf16"),
+                                         dev(wl["W2"], "bf16"), T, q_free=True, seed=seed,
+                                         offset=offset))
+    assert "q_logits" not in g
+    W1, W2 = _weights(wl)
+    u = orc.draft_uniforms(seed, offset, B, gamma)
+    tally = compare.Tally()
+    for b in range(B):
+        Ub = workloads.as_f64(wl["U"][b], udt)
+        o = orc.draft_markov(Ub, W1, W2, wl["x0"][b], T, u[b])
+        compare.compare_draft_request(o, Ub, {k: v[b] for k, v in g.items()}, T, u[b], f"b={b}",
+                                      tally, check_logits=False)
+    note(f"  {tally.as_dict()}")
+    assert tally.boundary <= max(1, tally.draws // 50)
+
+
+def test_qfree_draft_packed_w2_and_uniforms(orc):
+    """A W2T packed once by spec_pack_w2 gives the same result as W2, and
+    caller uniforms replace the counter stream."""
+    sd = require_gpu()
+    B, gamma, V, r = 9, 5, 6001, 64
+    wl = workloads.make_markov(_cfg("markov-32k-b32", "f32", 77, w_std=0.3), B=B, gamma=gamma,
+                               V=V, r=r)
+    W2d = dev(wl["W2"], "bf16")
+    W2T = sd.spec_pack_w2(W2d)
+    torch.cuda.synchronize()
+    assert np.array_equal(W2T.view(torch.int16).cpu().numpy().view(np.uint16), wl["W2"].T)
+    uni = np.random.default_rng(8).random((B, gamma)).astype(np.float32)
+    args = (dev(wl["U"]), dev(wl["x0"]), dev(wl["W1"], "bf16"))
+    a = host(sd.spec_draft_sample_markov(*args, W2d, 1.0, q_free=True, uniforms=dev(uni)))
+    b = host(sd.spec_draft_sample_markov(*args, None, 1.0, W2T=W2T, q_free=True,
+                                         uniforms=dev(uni)))
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+    W1, W2 = _weights(wl)
+    tally = compare.Tally()
+    for i in range(B):
+        Ub = workloads.as_f64(wl["U"][i], "f32")
+        ui = uni[i].astype(np.float64)
+        o = orc.draft_markov(Ub, W1, W2, wl["x0"][i], 1.0, ui)
+        compare.compare_draft_request(o, Ub, {k: v[i] for k, v in a.items()}, 1.0, ui, f"b={i}",
+                                      tally, check_logits=False)
+    note(f"  {tally.as_dict()}")
+
+
+def test_qfree_draft_invalid_anchor():
+    sd = require_gpu()
+    B, gamma, V, r = 3, 3, 500, 16
+    wl = workloads.make_markov(_cfg("markov-32k-b32", "f32", 5), B=B, gamma=gamma, V=V, r=r)
+    x0 = wl["x0"].copy()
+    x0[1] = V + 3
+    g = host(sd.spec_draft_sample_markov(dev(wl["U"]), dev(x0), dev(wl["W1"], "bf16"),
+                                         dev(wl["W2"], "bf16"), 1.0, q_free=True, seed=2))
+    assert np.all(g["tokens"][1] == -1) and np.all(np.isnan(g["q_logZ"][1]))
+    assert np.all(g["tokens"][[0, 2]] >= 0)
+
+
+# ---------------------------------------------------------------------------
+# spec_verify_markov on drafts the oracle produced
+# ---------------------------------------------------------------------------
+
+def _oracle_block(orc, wl, udt, T, u, rng, random_frac):
+    """The oracle's draft of every request, with a fraction of requests given
+    one random token (re-drafted with that prefix forced).  Returns the draft
+    tokens, the oracle's draft logits and the draft normaliser and q(x_k) in
+    fp32 as the draft would hand them over."""
+    B, G = wl["B"], wl["gamma"]
+    W1, W2 = _weights(wl)
+    draft = np.zeros((B, G), dtype=np.int32)
+    Q, lz, qx = [], np.zeros((B, G), np.float32), np.zeros((B, G), np.float32)
+    for b in range(B):
+        Ub = workloads.as_f64(wl["U"][b], udt)
+        o = orc.draft_markov(Ub, W1, W2, wl["x0"][b], T, u[b])
+        toks = o["tokens"].copy()
+        if G and rng.random() < random_frac:
+            toks[rng.integers(G)] = rng.integers(wl["V"])
+            o = orc.draft_markov(Ub, W1, W2, wl["x0"][b], T, u[b], forced=toks)
+        for k in range(G):
+            if T == 0:
+                qx[b, k] = 1.0 if toks[k] == orc.argmax(o["q_logits"][k])[0] else 0.0
+            else:
+                w, Z, _ = orc.softmax_weights(o["q_logits"][k], T)
+                qx[b, k] = w[toks[k]] / Z
+        draft[b] = toks
+        lz[b] = o["logZ"]
+        Q.append(o["q_logits"])
+    return draft, Q, lz, qx
+
+
+def _verify_rows(g, b, lz):
+    d = {k: v[b] for k, v in g.items()}
+    d["q_logZ"] = lz[b]
+    return d
+
+
+@pytest.mark.parametrize("B,G,V,r,pdt,udt,T,sigma", [
+    (12, 5, 5000, 64, "f32", "f32", 1.0, 0.6),
+    (12, 4, 4099, 48, "bf16", "f32", 0.7, 0.3),
+    (70, 3, 3000, 256, "bf16", "bf16", 1.0, 1.2),    # 128-row residual groups
+    (130, 2, 1500, 128, "f32", "bf16", 1.0, 1.5),    # two row blocks
+    (8, 4, 131, 16, "f32", "f32", 1.0, 0.8),
+    (10, 5, 2000, 64, "f32", "f32", 0.0, 0.6),       # greedy
+])
+def test_verify_markov_parity(orc, B, G, V, r, pdt, udt, T, sigma):
+    sd = require_gpu()
+    note(f"verify_markov B={B} G={G} V={V} r={r} P={pdt} U={udt} T={T}")
+    cfg = _cfg("markov-32k-b32", udt, 500 + B + V, w_std=0.3, sigma=sigma)
+    wl = workloads.make_markov(cfg, B=B, gamma=G, V=V, r=r)
+    rng = np.random.default_rng(V)
+    ud = orc.draft_uniforms(3, 1, B, G)
+    draft, Q, lz, qx = _oracle_block(orc, wl, udt, T, ud, rng, 0.3)
+    P32 = workloads.as_f64(wl["P"], cfg["logit_dtype"]).astype(np.float32)
+    P = workloads.f32_to_bf16_bits(P32) if pdt == "bf16" else P32
+    # request 0: the first draft token has no target mass -> n = 0
+    P[0, 0, draft[0, 0]] = np.float32(-np.inf) if pdt == "f32" else np.uint16(0xFF80)
+    # request 1: target rows equal the draft rows -> every token accepted
+    Pq = np.concatenate([Q[1], workloads.as_f64(P[1, G:], pdt)], axis=0).astype(np.float32)
+    P[1] = workloads.f32_to_bf16_bits(Pq) if pdt == "bf16" else Pq
+    Pf = workloads.as_f64(P, pdt)
+    seed = 23
+    g = host(sd.spec_verify_markov(dev(P, pdt), dev(wl["U"], udt), dev(wl["x0"]),
+                                   dev(wl["W1"], "bf16"), dev(wl["W2"], "bf16"), dev(draft),
+                                   dev(lz), dev(qx), T, seed=seed))
+    u = orc.verify_uniforms(seed, 0, B, G)
+    tally = compare.Tally()
+    for b in range(B):
+        compare.compare_verify_request(Pf[b], Q[b], draft[b], T, u[b, :G], u[b, G],
+                                       _verify_rows(g, b, lz), f"b={b}", tally)
+    note(f"  {tally.as_dict()} accepted={g['accepted'].tolist()}")
+    assert g["accepted"][0] == 0
+    if pdt == "f32" and T > 0:
+        assert g["accepted"][1] == G
+    assert tally.boundary <= max(1, tally.draws // 50)
+
+
+def test_verify_markov_ragged_packed(orc):
+    """Ragged lengths (one empty draft) with packed target rows and a W2T
+    packed by spec_pack_w2."""
+    sd = require_gpu()
+    B, G, V, r = 10, 6, 3000, 64
+    cfg = _cfg("ragged-128k-b256", "bf16", 41, w_std=0.3)
+    wl = workloads.make_markov(cfg, B=B, gamma=G, V=V, r=r)
+    lens = wl["lens"].copy()
+    p_off0 = workloads.packed_offsets(lens + 1)
+    lens[3] = 0
+    Pp = np.concatenate([wl["P"][p_off0[b]:p_off0[b] + lens[b] + 1] for b in range(B)], axis=0)
+    p_off = workloads.packed_offsets(lens + 1)
+    ud = orc.draft_uniforms(6, 0, B, G)
+    draft, Q, lz, qx = _oracle_block(orc, wl, "bf16", 1.0, ud, np.random.default_rng(2), 0.3)
+    for b in range(B):
+        draft[b, lens[b]:] = -7            # slots past L are never read
+    W2T = sd.spec_pack_w2(dev(wl["W2"], "bf16"))
+    seed = 9
+    g = host(sd.spec_verify_markov(dev(Pp, "bf16"), dev(wl["U"], "bf16"), dev(wl["x0"]),
+                                   dev(wl["W1"], "bf16"), None, dev(draft), dev(lz), dev(qx), 1.0,
+                                   W2T=W2T, gamma_max=G, lens=dev(lens), p_row_off=dev(p_off),
+                                   seed=seed))
+    Pf = workloads.as_f64(Pp, "bf16")
+    u = orc.verify_uniforms(seed, 0, B, G)
+    tally = compare.Tally()
+    for b in range(B):
+        L = int(lens[b])
+        d = {k: v[b] for k, v in g.items()}
+        d["q_logZ"] = lz[b]
+        compare.compare_verify_request(Pf[p_off[b]:p_off[b] + L + 1], Q[b][:L], draft[b, :L],
+                                       1.0, u[b, :L], u[b, G], d, f"b={b} L={L}", tally)
+        assert 0 <= g["accepted"][b] <= L
+    assert g["accepted"][3] == 0
+    note(f"  {tally.as_dict()} accepted={g['accepted'].tolist()}")
+
+
+def test_verify_markov_bonus_only(orc):
+    sd = require_gpu()
+    B, V, r = 3, 500, 16
+    rng = np.random.default_rng(5)
+    P = rng.standard_normal((B, 1, V)).astype(np.float32)
+    W1 = workloads.f32_to_bf16_bits(rng.standard_normal((V, r)).astype(np.float32))
+    W2 = workloads.f32_to_bf16_bits(rng.standard_normal((r, V)).astype(np.float32))
+    empty_f = torch.zeros((B, 0), dtype=torch.float32, device="cuda")
+    g = host(sd.spec_verify_markov(
+        dev(P), torch.zeros((B, 0, V), device="cuda"), dev(np.zeros(B, np.int32)),
+        dev(W1, "bf16"), dev(W2, "bf16"), torch.zeros((B, 0), dtype=torch.int32, device="cuda"),
+        empty_f, empty_f, 1.0, seed=3))
+    u = orc.verify_uniforms(3, 0, B, 0)
+    for b in range(B):
+        w, Z, _ = orc.softmax_weights(P[b, 0].astype(np.float64), 1.0)
+        assert g["accepted"][b] == 0
+        assert g["out_tokens"][b, 0] == orc.inverse_cdf(w, Z, u[b, 0])[0]
+
+
+# ---------------------------------------------------------------------------
+# The whole q-free cycle on the GPU against the oracle's cycle
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,B,G,V,T", [
+    ("markov-32k-b32", 16, 7, 32000, 1.0),
+    ("markov-152k-b128", 4, 16, 151936, 1.0),
+    ("ragged-128k-b256", 6, 8, 20000, 0.9),
+])
+def test_qfree_cycle_against_oracle(orc, name, B, G, V, T):
+    """GPU q-free draft -> spec_verify_markov, compared with the oracle's draft
+    and verification of the same request.  Requests whose draft met a
+    boundary draw are counted and their verification skipped (the two sides
+    then condition on different prefixes)."""
+    sd = require_gpu()
+    note(f"q-free cycle {name} B={B} G={G} V={V} T={T}")
+    cfg = dict(workloads.CONFIGS[name])
+    wl = workloads.make_markov(cfg, B=B, gamma=G, V=V)
+    ldt = cfg["logit_dtype"]
+    lens = wl["lens"]
+    p_off = None if lens is None else workloads.packed_offsets(lens + 1)
+    U, W1d, W2d, x0 = dev(wl["U"], ldt), dev(wl["W1"], "bf16"), dev(wl["W2"], "bf16"), dev(wl["x0"])
+    seed = 1234
+    dr = sd.spec_draft_sample_markov(U, x0, W1d, W2d, T, q_free=True, seed=seed, offset=0)
+    vr = sd.spec_verify_markov(dev(wl["P"], ldt), U, x0, W1d, W2d, dr["tokens"], dr["q_logZ"],
+                               dr["q_tok_prob"], T, lens=None if lens is None else dev(lens),
+                               p_row_off=None if p_off is None else dev(p_off), seed=seed,
+                               offset=1)
+    gd, gv = host(dr), host(vr)
+    W1, W2 = _weights(wl)
+    ud = orc.draft_uniforms(seed, 0, B, G)
+    uv = orc.verify_uniforms(seed, 1, B, G)
+    Pf = workloads.as_f64(wl["P"], ldt)
+    td, tv = compare.Tally(), compare.Tally()
+    for b in range(B):
+        L = G if lens is None else int(lens[b])
+        Ub = workloads.as_f64(wl["U"][b], ldt)
+        o = orc.draft_markov(Ub, W1, W2, wl["x0"][b], T, ud[b])
+        same = compare.compare_draft_request(o, Ub, {k: v[b] for k, v in gd.items()}, T, ud[b],
+                                             f"draft b={b}", td, check_logits=False)
+        if not same and not np.array_equal(gd["tokens"][b, :L], o["tokens"][:L]):
+            continue
+        Pb = Pf[b] if lens is None else Pf[p_off[b]:p_off[b] + L + 1]
+        d = {k: v[b] for k, v in gv.items()}
+        d["q_logZ"] = gd["q_logZ"][b]
+        compare.compare_verify_request(Pb, o["q_logits"][:L], o["tokens"][:L], T, uv[b, :L],
+                                       uv[b, G], d, f"verify b={b}", tv)
+    note(f"  draft {td.as_dict()} verify {tv.as_dict()} accepted={gv['accepted'].tolist()}")
+    assert tv.requests >= B - 1
