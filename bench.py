@@ -3,10 +3,18 @@
 (gamma sequential positions for a batch of requests) followed by lossless
 verification of the drafted block.
 
-A step = spec_draft_sample_markov + spec_verify on one batch of seeded
-synthetic inputs already resident in HBM.  value = B * gamma * steps / time
-("verified+drafted tokens/s": every drafted token is also verified in the
-same step).  Prints ONE JSON line on stdout; progress goes to stderr.
+A step is one whole cycle on one batch of seeded synthetic inputs already
+resident in HBM:
+
+* --path qfree (default): spec_draft_sample_markov without draft logits, then
+  spec_verify_markov, which rebuilds only the draft row a residual draw needs;
+* --path materialized: the draft writes its fp32 logits [B, gamma, V] and
+  spec_verify reads them back.
+
+W2 is packed once (spec_pack_w2) before timing, as at weight load.  value =
+B * gamma * steps / time ("verified+drafted tokens/s": every drafted token is
+also verified in the same step).  Prints ONE JSON line on stdout; progress
+goes to stderr.
 
 Roofline: every kernel of a step is timed in a second timed region with
 hipEvents that the library records on the launch stream; the dominant
@@ -38,9 +46,12 @@ def kernel_bytes(wl):
     B, g, V, r = wl["B"], wl["gamma"], wl["V"], wl["r"]
     lb = 2 if wl["logit_dtype"] == "bf16" else 4
     wb = 2 if wl["w_dtype"] == "bf16" else 4
+    nseg = (V + 127) // 128
     return {
         # U_k read, q_k written, W2 / gamma, the B gathered W1 rows
         "draft_tile": B * V * (lb + 4) + r * V * wb / g + B * r * wb,
+        # U_k read, 16 group sums + one 16-byte summary per (row, tile) written
+        "draft_tile_qfree": B * V * lb + B * nseg * (16 * 4 + 16) + r * V * wb / g + B * r * wb,
         "verify_rows_p": B * (g + 1) * V * lb,
         "verify_rows_q": B * g * V * 4,
     }
@@ -55,6 +66,8 @@ def source_sha(paths):
 
 
 KERNEL_SOURCES = {
+    "draft_tile_qfree": ["draft_sampling_lossless_head_amd/csrc/draft_kernels.hip",
+                         "draft_sampling_lossless_head_amd/csrc/device_common.hpp"],
     "draft_tile": ["draft_sampling_lossless_head_amd/csrc/draft_kernels.hip",
                    "draft_sampling_lossless_head_amd/csrc/device_common.hpp"],
     "verify_rows_p": ["draft_sampling_lossless_head_amd/csrc/verify_kernels.hip",
@@ -118,6 +131,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="markov-152k-b128")
+    ap.add_argument("--path", choices=("qfree", "materialized"), default="qfree",
+                    help="q-free cycle (no draft-logit tensor) or materialized draft logits")
     ap.add_argument("--sigma", type=float, default=None, help="override target/draft noise")
     ap.add_argument("--cpu-sample", type=int, default=16, help="requests timed on the oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -158,23 +173,34 @@ def main():
 
     U, P = to_dev(wl["U"], lb), to_dev(wl["P"], lb)
     W1, W2, x0 = to_dev(wl["W1"], wbt), to_dev(wl["W2"], wbt), to_dev(wl["x0"])
+    qfree = args.path == "qfree"
+    W2T = sd.spec_pack_w2(W2)          # once per model load
     d_out = dict(tokens=torch.empty((B, g), dtype=torch.int32, device=dev),
-                 q_logits=torch.empty((B, g, V), dtype=torch.float32, device=dev),
                  q_logZ=torch.empty((B, g), dtype=torch.float32, device=dev),
                  q_tok_prob=torch.empty((B, g), dtype=torch.float32, device=dev))
+    if not qfree:
+        d_out["q_logits"] = torch.empty((B, g, V), dtype=torch.float32, device=dev)
     v_out = dict(accepted=torch.empty(B, dtype=torch.int32, device=dev),
                  out_tokens=torch.empty((B, g + 1), dtype=torch.int32, device=dev))
     ws_d = torch.empty(sd.workspace_bytes("markov", B=B, gamma=g, V=V, r=r), dtype=torch.uint8,
                        device=dev)
-    ws_v = torch.empty(sd.workspace_bytes("verify", B=B, gamma_max=g, V=V), dtype=torch.uint8,
-                       device=dev)
+    if qfree:
+        nws_v = sd.workspace_bytes("verify_markov", B=B, gamma_max=g, V=V, r=r)
+    else:
+        nws_v = sd.workspace_bytes("verify", B=B, gamma_max=g, V=V)
+    ws_v = torch.empty(nws_v, dtype=torch.uint8, device=dev)
     seed = 0
 
     def step(i):
-        sd.spec_draft_sample_markov(U, x0, W1, W2, T, seed=seed, offset=i, out=d_out,
-                                    workspace=ws_d)
-        sd.spec_verify(P, d_out["q_logits"], d_out["tokens"], T, seed=seed, offset=i,
-                       out=v_out, workspace=ws_v)
+        sd.spec_draft_sample_markov(U, x0, W1, None, T, W2T=W2T, seed=seed, offset=i,
+                                    out=d_out, workspace=ws_d)
+        if qfree:
+            sd.spec_verify_markov(P, U, x0, W1, None, d_out["tokens"], d_out["q_logZ"],
+                                  d_out["q_tok_prob"], T, W2T=W2T, seed=seed, offset=i,
+                                  out=v_out, workspace=ws_v)
+        else:
+            sd.spec_verify(P, d_out["q_logits"], d_out["tokens"], T, seed=seed, offset=i,
+                           out=v_out, workspace=ws_v)
 
     for i in range(args.warmup):
         step(i)
@@ -213,8 +239,9 @@ def main():
     prof_ms_per_step = (time.perf_counter() - t1) * 1e3 / args.steps
     sd.spec_profile_enable(None)
     kernels = {}
-    names = ["w2_transpose", "draft_tile", "draft_finalize", "verify_rows_p", "verify_rows_q", "verify_decide",
-             "verify_final_partials", "verify_final_draw"]
+    names = ["w2_pack", "draft_tile", "draft_tile_qfree", "draft_finalize", "verify_rows_p",
+             "verify_rows_q", "verify_decide", "verify_residual_rows", "verify_final_partials",
+             "verify_final_draw"]
     for name in names:
         sd.spec_profile_enable(name)
         for i in range(args.steps):
@@ -247,7 +274,7 @@ def main():
         "config": {"workload": args.workload, "B": B, "gamma": g, "V": V, "r": r,
                    "logits": lb, "weights": wbt, "accumulate": "fp32", "T": T,
                    "sigma": float(wl["sigma"][0]), "head": "markov",
-                   "verify": "fixed-length"},
+                   "verify": "fixed-length", "path": args.path},
         "roofline": roofline,
         "breakdown": {
             "drafted_per_s": None, "verified_per_s": None,
@@ -257,8 +284,8 @@ def main():
             "kernels": {k: {a: round(b, 3) for a, b in v.items()} for k, v in kernels.items()},
         },
     }
-    tdraft = sum(kernels[k]["us_per_step"] for k in ("w2_transpose", "draft_tile", "draft_finalize")
-                 if k in kernels)
+    tdraft = sum(kernels[k]["us_per_step"] for k in kernels if k.startswith("draft")
+                 or k == "w2_pack")
     tver = sum(kernels[k]["us_per_step"] for k in kernels if k.startswith("verify"))
     if tdraft > 0:
         result["breakdown"]["drafted_per_s"] = round(B * g / (tdraft * 1e-6), 1)

@@ -14,6 +14,7 @@ from .api import (  # noqa: F401
     spec_draft_sample_markov,
     spec_draft_sample_rnn,
     spec_pack_w2,
+    spec_pack_w2_bytes,
     spec_philox_uniforms,
     spec_profile_enable,
     spec_profile_read,

@@ -57,6 +57,8 @@ def load_library():
     lib.spec_verify.argtypes = [vp, i32, vp, i32, vp, vp, vp, vp, i32, i32, i32, f32, vp, u64,
                                 u32, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.spec_verify.restype = i32
+    lib.spec_pack_w2_bytes.argtypes = [i32, i32]
+    lib.spec_pack_w2_bytes.restype = sz
     lib.spec_pack_w2.argtypes = [vp, vp, i32, i32, vp]
     lib.spec_pack_w2.restype = i32
     lib.spec_verify_markov_workspace_size.argtypes = [i32, i32, i32, i32]
@@ -151,22 +153,37 @@ def _draft_outputs(B, gamma, V, device, out, q_free=False):
     return o
 
 
+def spec_pack_w2_bytes(r, V):
+    return load_library().spec_pack_w2_bytes(r, V)
+
+
 def spec_pack_w2(W2, out=None, stream=None):
-    """W2 [r, V] bf16 -> W2T [V, r] bf16 (pack once; pass as W2T=)."""
+    """W2 [r, V] bf16 -> packed image (uint8 [spec_pack_w2_bytes(r, V)]);
+    pack once per model load and pass as W2T=."""
     lib = load_library()
     _dev(W2, "W2")
     if W2.dtype != torch.bfloat16:
         raise SpecError("spec_pack_w2 packs bf16 weights")
     r, V = W2.shape
-    out = torch.empty((V, r), dtype=torch.bfloat16, device=W2.device) if out is None else out
+    nbytes = lib.spec_pack_w2_bytes(r, V)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=W2.device)
+    elif out.numel() * out.element_size() < nbytes:
+        raise SpecError(f"W2T buffer needs {nbytes} bytes")
     _check(lib.spec_pack_w2(_ptr(W2), _ptr(out), r, V, _stream(stream)), "spec_pack_w2")
     return out
+
+
+def _check_w2t(W2T, r, V):
+    _dev(W2T, "W2T")
+    if W2T.numel() * W2T.element_size() < load_library().spec_pack_w2_bytes(r, V):
+        raise SpecError("W2T must be a packed image from spec_pack_w2 (too small)")
 
 
 def spec_draft_sample_markov(U, x0, W1, W2, T=1.0, *, W2T=None, q_free=False, uniforms=None,
                              seed=0, offset=0, out=None, workspace=None, stream=None):
     """Markov-head draft.  U [B, gamma, V], x0 [B] int32, W1 [V, r], W2 [r, V]
-    (or None with W2T [V, r] from spec_pack_w2).  q_free=True writes no q
+    (or None with W2T, the packed image from spec_pack_w2).  q_free=True writes no q
     logits (verify with spec_verify_markov)."""
     lib = load_library()
     for t, n in ((U, "U"), (x0, "x0"), (W1, "W1")):
@@ -180,9 +197,7 @@ def spec_draft_sample_markov(U, x0, W1, W2, T=1.0, *, W2T=None, q_free=False, un
         if W2.shape != (r, V) or W1.dtype != W2.dtype:
             raise SpecError("W2 must be [r, V] of W1's dtype")
     if W2T is not None:
-        _dev(W2T, "W2T")
-        if W2T.shape != (V, r) or W2T.dtype != torch.bfloat16:
-            raise SpecError("W2T must be bf16 [V, r]")
+        _check_w2t(W2T, r, V)
     if W1.shape != (V, r):
         raise SpecError("W1 must be [V, r]")
     if uniforms is not None and (uniforms.dtype != torch.float32 or uniforms.shape != (B, gamma)):
@@ -320,7 +335,7 @@ def spec_verify_markov(P, U, x0, W1, W2, draft, q_logZ, q_tok_prob, T=1.0, *, W2
     if W2 is not None:
         _dev(W2, "W2")
     if W2T is not None:
-        _dev(W2T, "W2T")
+        _check_w2t(W2T, r, V)
     dev = P.device
     if out is None:
         out = dict(accepted=torch.empty(B, dtype=torch.int32, device=dev),

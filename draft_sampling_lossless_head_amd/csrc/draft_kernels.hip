@@ -25,6 +25,7 @@
 namespace specdec {
 
 constexpr int kTileV = 128;   // vocabulary columns per tile workgroup
+static_assert(kTileV == kPackTile, "a bias tile is one tile of the packed W2 image");
 constexpr int kLdsPad = 8;    // bf16 elements of padding per transposed W2 row
 
 // ---------------------------------------------------------------------------
@@ -72,11 +73,11 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-// W2 [r, V] -> W2T [V, r] (bf16), once per draft call: each bias tile then
-// stages one contiguous block of W2T.  64 x 64 tiles through LDS with 16-byte
-// global accesses on both sides.
+// W2 [r, V] -> packed image (bf16; layout at w2p_index): 64 x 64 blocks of
+// (rank, token) through LDS with 16-byte global accesses on both sides; tokens
+// from V up to the end of the last 128-token tile are written as zeros.
 __global__ __launch_bounds__(256)
-void w2_transpose(const uint16_t* __restrict__ W2, uint16_t* __restrict__ W2T, int r, int V) {
+void w2_pack(const uint16_t* __restrict__ W2, uint16_t* __restrict__ W2P, int r, int V) {
     __shared__ __align__(16) uint16_t t[64][72];   // [j][v]
     const int v0 = blockIdx.x * 64;
     const int j0 = blockIdx.y * 64;
@@ -105,17 +106,18 @@ void w2_transpose(const uint16_t* __restrict__ W2, uint16_t* __restrict__ W2T, i
         *reinterpret_cast<uint4*>(&t[jj][vc]) = val;
     }
     __syncthreads();
+    const int vpad = (V + kPackTile - 1) / kPackTile * kPackTile;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int c = tid + i * 256;
         const int vv = c / 8, jc = (c % 8) * 8;
         const int v = v0 + vv, j = j0 + jc;
-        if (v < V && j < r) {
+        if (v < vpad && j < r) {
             uint32_t w[4];
 #pragma unroll
             for (int h = 0; h < 4; ++h)
                 w[h] = (uint32_t)t[jc + 2 * h][vv] | ((uint32_t)t[jc + 2 * h + 1][vv] << 16);
-            *reinterpret_cast<uint4*>(W2T + (size_t)v * r + j) = make_uint4(w[0], w[1], w[2], w[3]);
+            *reinterpret_cast<uint4*>(W2P + w2p_index(v, j, r)) = make_uint4(w[0], w[1], w[2], w[3]);
         }
     }
 }
@@ -158,17 +160,17 @@ void draft_tile_mfma(TileParams P) {
         return OUT == kOutResidual ? (size_t)br * V : ((size_t)br * gamma + pos) * (size_t)V;
     };
 
-    // 1) the W2T tile: kTileV rows of r contiguous bf16, 16 bytes per chunk.
-    const int cpr = r / 8;                       // chunks per W2T row
+    // 1) the packed W2 tile: one contiguous block of kTileV rows of r bf16
+    //    (zero past V), read in 16-byte chunks and un-swizzled into LDS.
+    const int cpr = r / 8;                       // chunks per token row
     const int nchunk = kTileV * cpr;             // <= 4096
+    const uint16_t* wtile = P.W2T + (size_t)v_tile * r;
     uint4 wch[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int c = tid + i * 256;
-        const int vr = c / cpr;
         wch[i] = make_uint4(0u, 0u, 0u, 0u);
-        if (c < nchunk && v_tile + vr < V)
-            wch[i] = *reinterpret_cast<const uint4*>(P.W2T + (size_t)(v_tile + vr) * r + (c % cpr) * 8);
+        if (c < nchunk) wch[i] = *reinterpret_cast<const uint4*>(wtile + (size_t)c * 8);
     }
 
     // 2) prefetch this thread's U items.  Item (row, j) covers the two runs of
@@ -211,7 +213,11 @@ void draft_tile_mfma(TileParams P) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int c = tid + i * 256;
-        if (c < nchunk) *reinterpret_cast<uint4*>(w2t + (c / cpr) * ldr + (c % cpr) * 8) = wch[i];
+        if (c < nchunk) {
+            const int vr = c / cpr;
+            const int kc = (c % cpr) ^ w2p_swizzle(vr, cpr);
+            *reinterpret_cast<uint4*>(w2t + vr * ldr + kc * 8) = wch[i];
+        }
     }
     f32x16_t acc[MB];
 #pragma unroll
@@ -363,6 +369,468 @@ void draft_tile_mfma(TileParams P) {
 }
 
 // ---------------------------------------------------------------------------
+// q-free bias tile: summaries only, straight from the MFMA accumulators.
+//
+// Same work split as draft_tile_mfma (WB waves along the request rows, 4/WB
+// along the tile's tokens, MB = WB blocks of 32 tokens per wave), but:
+//   * the packed W2 tile is copied into LDS by direct global->LDS loads (16
+//     bytes per lane, no register round trip) and read back swizzled;
+//   * the A operand's rows are assigned to tokens so that every lane ends with
+//     one contiguous run of RUN = 16 * MB tokens of its request row: MFMA row
+//     i = 8g + 4h + c of block mb is token  wv*32*MB + 16*MB*h + 16*mb + 4g + c,
+//     and the accumulator element idx of lane (b, h) is token
+//     wv*32*MB + 16*MB*h + 16*mb + idx;
+//   * U is read as that run (16-byte loads), and the epilogue reduces each
+//     lane's run in registers: no output staging, no q store.
+// Outputs per (row, tile): the SegStat (max, sum exp((l - max)/T), argmax) and
+// the 16 sums over 8-token groups relative to the same max.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+template <int WB, bool U_BF16>
+__global__ __launch_bounds__(256, 2)
+void draft_tile_stats(TileParams P) {
+    constexpr int MB = WB;
+    constexpr int NWV = 4 / WB;           // waves along the tile's tokens
+    constexpr int RT = 32 * WB;           // request rows of the tile
+    constexpr int RUN = 16 * MB;          // contiguous tokens per lane
+    constexpr int NG = RUN / 8;           // 8-token groups per lane
+    constexpr int UV = U_BF16 ? RUN / 8 : RUN / 4;   // 16-byte U loads per lane
+    extern __shared__ __align__(16) uint16_t smem[];   // packed W2 tile [128][r]
+    __shared__ float x_m[NWV][RT];
+    __shared__ float x_s[NWV][RT];
+    __shared__ int x_i[NWV][RT];
+    const int V = P.V, r = P.r, k = P.k, B = P.B, gamma = P.gamma;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wb = wave % WB;
+    const int wv = wave / WB;
+    const int tile = blockIdx.x;
+    const int v_tile = tile * kTileV;
+    const int rl = wb * 32 + (lane & 31);  // request row within the tile
+    const int b = blockIdx.y * RT + rl;
+    const int h = lane >> 5;
+    const int kgrp = lane >> 5;
+    const int nks = r / 16;
+    const int nchunk = r / 8;
+    const bool active = b < B;
+
+    // 1) the packed W2 tile (256 * r bytes) into LDS: wave w copies the 1 KB
+    //    pieces w, w + 4, ... with one direct load per piece.
+    {
+        const char* src = reinterpret_cast<const char*>(P.W2T) + (size_t)tile * 256 * r;
+        char* dst = reinterpret_cast<char*>(smem);
+        const int npiece = r / 4;
+        for (int pc = wave; pc < npiece; pc += 4)
+            __builtin_amdgcn_global_load_lds(src + pc * 1024 + lane * 16,
+                                             (lds_ptr_t)(dst + pc * 1024), 16, 0, 0);
+    }
+
+    // 2) the conditioning row E = W1[x_{k-1}] (MFMA B operand) and the U run.
+    int prev = 0;
+    bool erow_ok = false;
+    if (active) {
+        prev = (k == 0) ? P.x0[b] : P.tokens[(size_t)b * gamma + k - 1];
+        erow_ok = prev >= 0 && prev < V;
+    }
+    const uint16_t* erow = P.W1 + (size_t)prev * r;
+    bf16x8_t e[16];
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) {
+        if (ks < nks) {
+            if (erow_ok) {
+                e[ks] = *reinterpret_cast<const bf16x8_t*>(erow + ks * 16 + kgrp * 8);
+            } else {
+#pragma unroll
+                for (int t = 0; t < 8; ++t) e[ks][t] = (__bf16)0.0f;
+            }
+        }
+    }
+    f32x16_t acc[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[mb][i] = 0.0f;
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's direct loads have landed
+    __syncthreads();                 // ... and every other wave's
+
+    // The U run, issued now so that it arrives during the contraction.  Each
+    // lane reads whole lines over its consecutive loads, so these are plain
+    // (cached) loads: a streaming hint would drop a line between them.
+    const int run0 = wv * 32 * MB + 16 * MB * h;     // first token of the lane's run (tile-local)
+    const int v0 = v_tile + run0;
+    const size_t urow = ((size_t)(active ? b : 0) * gamma + k) * (size_t)V;
+    const bool vec_u = (U_BF16 ? (V % 8) == 0 : (V % 4) == 0) && v0 + RUN <= V && erow_ok;
+    u32x4_t ureg[UV];
+#pragma unroll
+    for (int q = 0; q < UV; ++q) {
+        ureg[q] = u32x4_t{0u, 0u, 0u, 0u};
+        if (vec_u) {
+            if constexpr (U_BF16)
+                ureg[q] = *reinterpret_cast<const u32x4_t*>(
+                    static_cast<const uint16_t*>(P.U) + urow + v0 + q * 8);
+            else
+                ureg[q] = *reinterpret_cast<const u32x4_t*>(
+                    static_cast<const float*>(P.U) + urow + v0 + q * 4);
+        }
+    }
+
+    // 3) the contraction.  Lane l supplies A row i = l % 32 of each block.
+    int arow[MB];
+    int aswz[MB];
+    {
+        const int i = lane & 31;
+        const int hi = (i >> 2) & 1, g = i >> 3, c = i & 3;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int vl = wv * 32 * MB + 16 * MB * hi + 16 * mb + 4 * g + c;
+            arow[mb] = vl * r;
+            aswz[mb] = w2p_swizzle(vl, nchunk);
+        }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) {
+        if (ks < nks) {
+            const int kc = 2 * ks + kgrp;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
+                    smem + arow[mb] + ((kc ^ aswz[mb]) << 3));
+                acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, e[ks], acc[mb], 0, 0, 0);
+            }
+        }
+    }
+
+    // 4) logits of the run: l = bias + U (-inf past V or for an inactive row).
+    float x[RUN];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[16 * mb + i] = acc[mb][i];
+    if (vec_u) {
+#pragma unroll
+        for (int q = 0; q < UV; ++q) {
+            if constexpr (U_BF16) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    x[8 * q + 2 * t] += bf16_bits_to_float(ureg[q][t] & 0xFFFFu);
+                    x[8 * q + 2 * t + 1] += bf16_bits_to_float(ureg[q][t] >> 16);
+                }
+            } else {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) x[4 * q + t] += __uint_as_float(ureg[q][t]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < RUN; ++t) {
+            const int v = v0 + t;
+            if (erow_ok && v < V) x[t] += load1<U_BF16>(P.U, urow + v);
+            else x[t] = -INFINITY;
+        }
+    }
+
+    // 5) tile-row max and lowest argmax: the lane's run, its partner lane
+    //    (l ^ 32 holds the row's other half), then the other token waves.
+    float m = x[0];
+#pragma unroll
+    for (int t = 1; t < RUN; ++t) m = fmaxf(m, x[t]);
+    int am = INT_MAX;
+#pragma unroll
+    for (int t = RUN - 1; t >= 0; --t)
+        if (x[t] == m) am = v0 + t;
+    {
+        const float m2 = __shfl_xor(m, 32);
+        const int a2 = __shfl_xor(am, 32);
+        merge_arg(m, am, m2, a2);
+    }
+    if constexpr (NWV > 1) {
+        if (h == 0) {
+            x_m[wv][rl] = m;
+            x_i[wv][rl] = am;
+        }
+        __syncthreads();
+        m = x_m[0][rl];
+        am = x_i[0][rl];
+#pragma unroll
+        for (int w = 1; w < NWV; ++w) merge_arg(m, am, x_m[w][rl], x_i[w][rl]);
+    }
+    if (am == INT_MAX) am = v_tile;   // all -inf: any in-tile id (weight 0)
+
+    // 6) group sums and the tile sum, relative to the tile-row max.
+    float gs[NG];
+    float tot = 0.0f;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        float sg = 0.0f;
+        if (!P.greedy && m != -INFINITY) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) sg += __expf((x[8 * g + t] - m) * P.invT);
+        }
+        gs[g] = sg;
+        tot += sg;
+    }
+    tot += __shfl_xor(tot, 32);
+    const int nseg = gridDim.x;
+    if (active && !P.greedy) {
+        float* gdst = P.gsums + ((size_t)b * nseg + tile) * 16 + run0 / 8;
+        if constexpr (NG % 4 == 0) {
+#pragma unroll
+            for (int q = 0; q < NG / 4; ++q)
+                *reinterpret_cast<float4*>(gdst + 4 * q) =
+                    make_float4(gs[4 * q], gs[4 * q + 1], gs[4 * q + 2], gs[4 * q + 3]);
+        } else {
+            *reinterpret_cast<float2*>(gdst) = make_float2(gs[0], gs[1]);
+        }
+    }
+    if constexpr (NWV > 1) {
+        if (h == 0) x_s[wv][rl] = tot;
+        __syncthreads();
+        tot = x_s[0][rl];
+#pragma unroll
+        for (int w = 1; w < NWV; ++w) tot += x_s[w][rl];
+    }
+    if (active && h == 0 && wv == 0) {
+        SegStat st;
+        st.m = m;
+        st.s = tot;
+        st.idx = am;
+        st.pad = 0;
+        P.stats[(size_t)b * nseg + tile] = st;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Streaming q-free bias tile: one persistent workgroup per CU.
+//
+// Work item = (64-token slice, block of 128 request rows); the workgroup takes
+// items blockIdx.x, blockIdx.x + gridDim.x, ...  Every item's two inputs are
+// copied into an LDS stage by direct global->LDS loads: the packed W2 slice
+// (64 rows of r bf16, contiguous in the packed image) and the U slice (128 rows
+// x 64 bf16, 16-byte chunk c of row bl stored in slot bl*8 + (c ^ ((bl>>1)&7))).
+// Three stages: item i+2 streams in while item i is contracted and reduced,
+// so the memory pipe never waits for the ALUs.  The conditioning rows E stay
+// in registers for all items of a row block.
+//
+// Each wave owns 32 rows and all 64 tokens of an item (MB = 2 blocks), with
+// the token assignment of draft_tile_stats: lane (b, h) ends with tokens
+// 32h .. 32h + 31 of the slice.  A 64-token slice is one segment: per (row,
+// segment) the SegStat and 8 group sums, reduced over the lane and its partner
+// lane l ^ 32 only.
+//
+// Only the bf16-U, V % 8 == 0 shape is streamed this way (chunks never straddle
+// V); waits on the direct loads use explicit vmcnt counts and a bare s_barrier,
+// since a fenced barrier would drain the prefetches as well.
+// ---------------------------------------------------------------------------
+constexpr int kStreamItem = 64;     // tokens per item / segment
+constexpr int kStreamRows = 128;    // request rows per item
+constexpr int kStreamStages = 3;
+
+__device__ __forceinline__ void wait_vmcnt_le(int n) {
+    // s_waitcnt with expcnt and lgkmcnt at their "no wait" maxima; n <= 63
+    switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+    case 12: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;   // waiting for all is always safe
+    }
+}
+
+template <int NKS>
+__global__ __launch_bounds__(256, 1)
+void draft_tile_stream(TileParams P, int nitem_v, int nrb) {
+    constexpr int R = NKS * 16;
+    constexpr int W2B = kStreamItem * R * 2;             // packed W2 slice bytes
+    constexpr int UB = kStreamRows * kStreamItem * 2;    // U slice bytes
+    constexpr int STAGE = W2B + UB;
+    constexpr int W2P = W2B / 1024 / 4;                  // 1 KB pieces per wave
+    constexpr int UP = UB / 1024 / 4;
+    constexpr int LOADS = W2P + UP;                      // direct loads per wave per item
+    constexpr int NCH = R / 8;
+    static_assert(W2P >= 1 && UP == 4, "piece split");
+    extern __shared__ __align__(16) char smem_s[];
+    const int V = P.V, k = P.k, B = P.B, gamma = P.gamma;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int h = lane >> 5;
+    const int kgrp = lane >> 5;
+    const int G = gridDim.x;
+    const int nitems = nitem_v * nrb;
+    if ((int)blockIdx.x >= nitems) return;
+    const int my_n = (nitems - 1 - (int)blockIdx.x) / G + 1;
+    const uint16_t* Ub = static_cast<const uint16_t*>(P.U);
+
+    auto issue = [&](int i) {
+        const int w = blockIdx.x + i * G;
+        const int rb = w / nitem_v, iv = w % nitem_v;
+        char* st = smem_s + (i % kStreamStages) * STAGE;
+        const char* wsrc = reinterpret_cast<const char*>(P.W2T) + (size_t)iv * W2B;
+#pragma unroll
+        for (int q = 0; q < W2P; ++q) {
+            const int pc = q * 4 + wave;
+            __builtin_amdgcn_global_load_lds(wsrc + pc * 1024 + lane * 16,
+                                             (lds_ptr_t)(st + pc * 1024), 16, 0, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < UP; ++q) {
+            const int pc = q * 4 + wave;
+            const int sl = pc * 64 + lane;                 // 16-byte slot of the U slice
+            const int bl = sl >> 3;
+            const int c = (sl & 7) ^ ((bl >> 1) & 7);
+            const int bg = rb * kStreamRows + bl;
+            const int v = iv * kStreamItem + c * 8;
+            const size_t off = (bg < B && v < V) ? ((size_t)bg * gamma + k) * (size_t)V + v
+                                                 : (size_t)k * (size_t)V;   // any valid chunk
+            __builtin_amdgcn_global_load_lds(Ub + off, (lds_ptr_t)(st + W2B + pc * 1024), 16, 0, 0);
+        }
+    };
+
+    // Conditioning rows E = W1[x_{k-1}] of a row block.
+    int cur_rb = -1;
+    bf16x8_t e[NKS];
+    bool erow_ok = false;
+    int b = 0;
+    auto load_e = [&](int rb) {
+        cur_rb = rb;
+        b = rb * kStreamRows + wave * 32 + (lane & 31);
+        int prev = 0;
+        erow_ok = false;
+        if (b < B) {
+            prev = (k == 0) ? P.x0[b] : P.tokens[(size_t)b * gamma + k - 1];
+            erow_ok = prev >= 0 && prev < V;
+        }
+        const uint16_t* erow = P.W1 + (size_t)(erow_ok ? prev : 0) * R;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            if (erow_ok) {
+                e[ks] = *reinterpret_cast<const bf16x8_t*>(erow + ks * 16 + kgrp * 8);
+            } else {
+#pragma unroll
+                for (int t = 0; t < 8; ++t) e[ks][t] = (__bf16)0.0f;
+            }
+        }
+    };
+    // E must be complete before any direct load is in flight: the compiler
+    // treats plain and direct loads pending together as unordered and would
+    // otherwise drain every prefetch before each contraction.
+    load_e((int)blockIdx.x / nitem_v);
+    wait_vmcnt_le(0);
+    issue(0);
+    if (my_n > 1) issue(1);
+
+    // A-operand rows of this lane (token of MFMA row i = lane % 32, block mb)
+    int arow[2], aswz_lo[2];
+    {
+        const int i = lane & 31;
+        const int hi = (i >> 2) & 1, g = i >> 3, c = i & 3;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            const int t = 32 * hi + 16 * mb + 4 * g + c;
+            arow[mb] = t * R;
+            aswz_lo[mb] = t;   // swizzle needs the token's position in its 128-token tile
+        }
+    }
+
+    for (int i = 0; i < my_n; ++i) {
+        const int w = blockIdx.x + i * G;
+        const int rb = w / nitem_v, iv = w % nitem_v;
+        if (rb != cur_rb) {   // a new row block (B > 128): reload E and drain
+            load_e(rb);
+            wait_vmcnt_le(0);
+        }
+        wait_vmcnt_le(i + 1 < my_n ? LOADS : 0);   // item i's direct loads (this wave)
+        asm volatile("s_barrier" ::: "memory");    // ... and every wave's; stage (i-1)%3 is free
+        if (i + 2 < my_n) issue(i + 2);
+
+        const char* st = smem_s + (i % kStreamStages) * STAGE;
+        const uint16_t* w2s = reinterpret_cast<const uint16_t*>(st);
+        const int half = (iv & 1) * 64;
+        f32x16_t acc[2];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int t = 0; t < 16; ++t) acc[mb][t] = 0.0f;
+        int sw[2];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) sw[mb] = w2p_swizzle(half + aswz_lo[mb], NCH);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const int kc = 2 * ks + kgrp;
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+                const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
+                    w2s + arow[mb] + ((kc ^ sw[mb]) << 3));
+                acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, e[ks], acc[mb], 0, 0, 0);
+            }
+        }
+
+        // logits of the lane's 32 tokens: bias + U (from the stage), -inf past V
+        const int bl = wave * 32 + (lane & 31);
+        const uint32_t* us = reinterpret_cast<const uint32_t*>(st + W2B);
+        const int v0 = iv * kStreamItem + 32 * h;
+        float x[32];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int c = 4 * h + q;
+            const u32x4_t u4 = *reinterpret_cast<const u32x4_t*>(
+                us + (bl * 8 + (c ^ ((bl >> 1) & 7))) * 4);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int j = 8 * q + 2 * t;   // run position of the pair
+                x[j] = acc[j >> 4][j & 15] + bf16_bits_to_float(u4[t] & 0xFFFFu);
+                x[j + 1] = acc[(j + 1) >> 4][(j + 1) & 15] + bf16_bits_to_float(u4[t] >> 16);
+            }
+        }
+        if (v0 + 32 > V) {
+#pragma unroll
+            for (int t = 0; t < 32; ++t)
+                if (v0 + t >= V) x[t] = -INFINITY;
+        }
+        float m = x[0];
+#pragma unroll
+        for (int t = 1; t < 32; ++t) m = fmaxf(m, x[t]);
+        int am = INT_MAX;
+#pragma unroll
+        for (int t = 31; t >= 0; --t)
+            if (x[t] == m) am = v0 + t;
+        {
+            const float m2 = __shfl_xor(m, 32);
+            const int a2 = __shfl_xor(am, 32);
+            merge_arg(m, am, m2, a2);
+        }
+        float gs[4];
+        float tot = 0.0f;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            float sg = 0.0f;
+            if (!P.greedy && m != -INFINITY) {
+#pragma unroll
+                for (int t = 0; t < 8; ++t) sg += __expf((x[8 * g + t] - m) * P.invT);
+            }
+            gs[g] = sg;
+            tot += sg;
+        }
+        tot += __shfl_xor(tot, 32);
+        if (b < B && erow_ok) {
+            if (!P.greedy)
+                *reinterpret_cast<float4*>(P.gsums + ((size_t)b * nitem_v + iv) * 8 + 4 * h) =
+                    make_float4(gs[0], gs[1], gs[2], gs[3]);
+            if (h == 0) {
+                SegStat sst;
+                sst.m = m;
+                sst.s = tot;
+                sst.idx = am;
+                sst.pad = 0;
+                P.stats[(size_t)b * nitem_v + iv] = sst;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // fp32-weight variant on the vector ALUs (small ranks such as r = 16).
 // Workgroup = one 128-column tile; each thread owns one column and loops over
 // the request rows; the per-row summary is a block reduction.
@@ -428,11 +896,12 @@ void draft_tile_valu_f32w(const void* __restrict__ U, const float* __restrict__ 
 // order (wave scans, then the four wave totals), the thread whose run holds
 // u * Z walks it to the segment, and wave 0 rescans that segment's logits.
 // ---------------------------------------------------------------------------
-constexpr int kFinRun = 8;   // max summaries per thread (nseg <= 2048)
+constexpr int kFinRun = 16;  // max summaries per thread (nseg <= 4096)
 
 // Inputs the q-free draft needs to rebuild 8 logits of one tile row.
 struct RebuildArgs {
-    const float* gsums;     // [B, nseg, 16] group sums relative to the tile max
+    const float* gsums;     // [B, nseg, gps] group sums relative to the segment max
+    int gps;                // 8-token groups per segment
     const void* U;          // [B, gamma, V]
     int u_bf16;
     const uint16_t* W1;     // [V, r]
@@ -591,8 +1060,9 @@ void draft_finalize(const SegStat* __restrict__ stats, int nseg, int seg_len,
         // then rebuild that group's logits l = U + W1[prev] . W2[:, v].
         const float mseg = st[seg].m;
         const double scale = (double)expf((mseg - M) * invT);   // as the tile weight
-        const double wg = lane < 16 ? (double)rb.gsums[((size_t)b * nseg + seg) * 16 + lane] * scale
-                                    : 0.0;
+        const double wg = lane < rb.gps
+                              ? (double)rb.gsums[((size_t)b * nseg + seg) * rb.gps + lane] * scale
+                              : 0.0;
         const double ginc = wave_inclusive_scan_f64(wg);
         double gexc = __shfl_up(ginc, 1);
         if (lane == 0) gexc = 0.0;
@@ -610,10 +1080,32 @@ void draft_finalize(const SegStat* __restrict__ stats, int nseg, int seg_len,
         const int span = rb.r / 8;
         float part = 0.0f;
         if (vt < V) {
-            const uint16_t* w1 = rb.W1 + (size_t)prev * rb.r + sl * span;
-            const uint16_t* w2 = rb.W2T + (size_t)vt * rb.r + sl * span;
-            for (int j = 0; j < span; ++j)
-                part = fmaf(bf16_bits_to_float(w1[j]), bf16_bits_to_float(w2[j]), part);
+            const uint16_t* w1 = rb.W1 + (size_t)prev * rb.r;
+            if ((span & 7) == 0) {   // whole 16-byte chunks: span / 8 <= 4 of them
+                const int nswz = w2p_swizzle(vt & (kPackTile - 1), rb.r >> 3);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if (q < (span >> 3)) {
+                        const int kc = sl * (span >> 3) + q;
+                        const uint4 a = *reinterpret_cast<const uint4*>(w1 + kc * 8);
+                        const uint4 c = *reinterpret_cast<const uint4*>(
+                            rb.W2T + (size_t)vt * rb.r + ((kc ^ nswz) << 3));
+                        const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
+                        const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            part = fmaf(bf16_bits_to_float(aw[t] & 0xFFFFu),
+                                        bf16_bits_to_float(cw[t] & 0xFFFFu), part);
+                            part = fmaf(bf16_bits_to_float(aw[t] >> 16),
+                                        bf16_bits_to_float(cw[t] >> 16), part);
+                        }
+                    }
+                }
+            } else {
+                for (int j = sl * span; j < (sl + 1) * span; ++j)
+                    part = fmaf(bf16_bits_to_float(w1[j]),
+                                bf16_bits_to_float(rb.W2T[w2p_index(vt, j, rb.r)]), part);
+            }
         }
         part += __shfl_xor(part, 1);
         part += __shfl_xor(part, 2);
@@ -799,16 +1291,53 @@ void rnn_gates(const float* __restrict__ hproj, const uint16_t* __restrict__ Wg,
 // ---------------------------------------------------------------------------
 static int pick_wb(int B) { return B <= 32 ? 1 : (B <= 64 ? 2 : 4); }
 
-int draft_num_segments(int B, int V, int w_bf16) {
-    (void)B;
-    (void)w_bf16;
-    return (V + kTileV - 1) / kTileV;
+// The streaming tile serves the q-free Markov draft for bf16 U, V % 8 == 0,
+// more than 64 rows and r in {64, 128, 256}; its segments are 64 tokens.
+bool draft_streams(const DraftArgs& a) {
+    return a.head == kHeadMarkov && a.w_bf16 && !a.q_logits && a.u_bf16 && (a.V % 8) == 0 &&
+           pick_wb(a.B) == 4 && (a.r == 64 || a.r == 128 || a.r == 256);
 }
 
-int draft_segment_len(int B, int w_bf16) {
-    (void)B;
-    (void)w_bf16;
-    return kTileV;
+int draft_segment_len(const DraftArgs& a) { return draft_streams(a) ? kStreamItem : kTileV; }
+
+int draft_num_segments(const DraftArgs& a) {
+    const int len = draft_segment_len(a);
+    return (a.V + len - 1) / len;
+}
+
+int draft_max_segments(int V) { return (V + kStreamItem - 1) / kStreamItem; }
+
+static int cu_count() {
+    static int n[64] = {0};
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    if (dev < 0 || dev >= 64) dev = 0;
+    if (!n[dev]) {
+        int c = 0;
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            c <= 0)
+            c = 256;
+        n[dev] = c;
+    }
+    return n[dev];
+}
+
+template <int NKS>
+static hipError_t launch_stream(const TileParams& p, hipStream_t s) {
+    constexpr int STAGE = kStreamItem * NKS * 16 * 2 + kStreamRows * kStreamItem * 2;
+    const size_t lds = (size_t)kStreamStages * STAGE;
+    static bool attr_set = false;
+    if (!attr_set) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&draft_tile_stream<NKS>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        (void)hipGetLastError();
+        attr_set = true;
+    }
+    const int nitem_v = (p.V + kStreamItem - 1) / kStreamItem;
+    const int nrb = (p.B + kStreamRows - 1) / kStreamRows;
+    const int grid = std::min(nitem_v * nrb, cu_count());
+    hipLaunchKernelGGL((draft_tile_stream<NKS>), dim3(grid), dim3(256), lds, s, p, nitem_v, nrb);
+    return hipGetLastError();
 }
 
 template <int WB, int MODE, int OUT>
@@ -831,6 +1360,27 @@ static hipError_t launch_tile(const TileParams& p, bool u_bf16, hipStream_t s) {
         hipLaunchKernelGGL((draft_tile_mfma<WB, MODE, true, OUT>), grid, dim3(256), lds, s, p);
     else
         hipLaunchKernelGGL((draft_tile_mfma<WB, MODE, false, OUT>), grid, dim3(256), lds, s, p);
+    return hipGetLastError();
+}
+
+template <int WB>
+static hipError_t launch_stats(const TileParams& p, bool u_bf16, hipStream_t s) {
+    constexpr int RT = 32 * WB;
+    dim3 grid((p.V + kTileV - 1) / kTileV, (p.B + RT - 1) / RT);
+    const size_t lds = (size_t)256 * p.r;   // the packed W2 tile
+    static bool attr_set = false;
+    if (!attr_set) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&draft_tile_stats<WB, true>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&draft_tile_stats<WB, false>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
+        (void)hipGetLastError();
+        attr_set = true;
+    }
+    if (u_bf16)
+        hipLaunchKernelGGL((draft_tile_stats<WB, true>), grid, dim3(256), lds, s, p);
+    else
+        hipLaunchKernelGGL((draft_tile_stats<WB, false>), grid, dim3(256), lds, s, p);
     return hipGetLastError();
 }
 
@@ -864,9 +1414,10 @@ static TileParams tile_params(const DraftArgs& a, int k) {
     return p;
 }
 
-hipError_t w2_transpose_launch(const uint16_t* W2, uint16_t* W2T, int r, int V, hipStream_t s) {
-    dim3 grid((V + 63) / 64, (r + 63) / 64);
-    hipLaunchKernelGGL(w2_transpose, grid, dim3(256), 0, s, W2, W2T, r, V);
+hipError_t w2_pack_launch(const uint16_t* W2, uint16_t* W2P, int r, int V, hipStream_t s) {
+    const int vpad = (V + kPackTile - 1) / kPackTile * kPackTile;
+    dim3 grid(vpad / 64, (r + 63) / 64);
+    hipLaunchKernelGGL(w2_pack, grid, dim3(256), 0, s, W2, W2P, r, V);
     return hipGetLastError();
 }
 
@@ -887,7 +1438,15 @@ hipError_t draft_tile_launch(const DraftArgs& a, int k, hipStream_t s) {
     const TileParams p = tile_params(a, k);
     if (a.head == kHeadMarkov) {
         if (a.q_logits) return launch_tile_b<kHeadMarkov, kOutQ>(p, a.u_bf16, s);
-        return launch_tile_b<kHeadMarkov, kOutStats>(p, a.u_bf16, s);
+        if (draft_streams(a)) {
+            if (a.r == 256) return launch_stream<16>(p, s);
+            if (a.r == 128) return launch_stream<8>(p, s);
+            return launch_stream<4>(p, s);
+        }
+        const int wb = pick_wb(a.B);
+        if (wb == 1) return launch_stats<1>(p, a.u_bf16, s);
+        if (wb == 2) return launch_stats<2>(p, a.u_bf16, s);
+        return launch_stats<4>(p, a.u_bf16, s);
     }
     return launch_tile_b<kHeadRnn, kOutQ>(p, a.u_bf16, s);
 }
@@ -897,10 +1456,11 @@ hipError_t residual_rows_launch(const TileParams& p, bool u_bf16, hipStream_t s)
 }
 
 hipError_t draft_finalize_launch(const DraftArgs& a, int k, hipStream_t s) {
-    const int nseg = draft_num_segments(a.B, a.V, a.w_bf16);
-    const int seg = draft_segment_len(a.B, a.w_bf16);
+    const int nseg = draft_num_segments(a);
+    const int seg = draft_segment_len(a);
     RebuildArgs rb;
     rb.gsums = a.gsums;
+    rb.gps = seg / 8;
     rb.U = a.U;
     rb.u_bf16 = a.u_bf16;
     rb.W1 = (const uint16_t*)a.W1;

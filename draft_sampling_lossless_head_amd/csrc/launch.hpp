@@ -11,6 +11,32 @@ struct SegStat;
 
 enum { kHeadMarkov = 0, kHeadRnn = 1 };
 
+// Packed W2 image (bf16).  W2 [r, V] is stored token-major in tiles of 128
+// tokens: tile t holds tokens 128t .. 128t + 127 (zeros past V), token v as r
+// contiguous bf16 split into r / 8 chunks of 16 bytes, and chunk kc of token
+// v sits in slot kc ^ w2p_swizzle(v % 128, r / 8) of its row.  A tile is one
+// contiguous block of 256 * r bytes that a workgroup copies into LDS as is;
+// the XOR swizzle spreads the 16-byte reads of an MFMA operand over all LDS
+// banks.
+constexpr int kPackTile = 128;
+
+__host__ __device__ inline int w2p_swizzle(int vl, int nchunk) {
+    int f = (vl & 7) | ((((vl >> 4) ^ (vl >> 5) ^ (vl >> 6)) & 1) << 3);
+    int F = nchunk & -nchunk;           // largest power of two dividing nchunk
+    if (F > 16) F = 16;
+    return f & (F - 1);
+}
+
+// bf16 element offset of W2[j][v] in the packed image.
+__host__ __device__ inline size_t w2p_index(int v, int j, int r) {
+    const int slot = (j >> 3) ^ w2p_swizzle(v & (kPackTile - 1), r >> 3);
+    return (size_t)v * r + (size_t)slot * 8 + (j & 7);
+}
+
+inline size_t w2p_bytes(int r, int V) {
+    return (size_t)((V + kPackTile - 1) / kPackTile) * kPackTile * (size_t)r * 2;
+}
+
 // Everything one draft call needs, resolved and validated by the C ABI layer.
 struct DraftArgs {
     int head;            // kHeadMarkov or kHeadRnn
@@ -39,8 +65,8 @@ struct DraftArgs {
     float* hproj;        // RNN: [B * gamma, 3r]
     float* state;        // RNN: [2, B, r]
     uint16_t* Erows;     // RNN: [B, 3, r]
-    const uint16_t* W2T; // bf16 weights: [V, r] transposed copy of W2
-    uint16_t* W2T_ws;    // workspace for that copy when the caller passes none
+    const uint16_t* W2T; // bf16 weights: packed W2 image
+    uint16_t* W2T_ws;    // workspace for that image when the caller passes none
     float* gsums;        // q-free draft: [B, nseg, 16] 8-token group sums
 };
 
@@ -55,7 +81,7 @@ enum {
 struct TileParams {
     const void* U;            // [B, gamma, V]
     const uint16_t* W1;       // [V, r]
-    const uint16_t* W2T;      // [V, r]
+    const uint16_t* W2T;      // packed W2 image
     const uint16_t* Erows;    // RNN: [B, 3, r]
     const int32_t* x0;        // [B]
     const int32_t* tokens;    // [B, gamma] conditioning tokens (draft outputs)
@@ -68,11 +94,15 @@ struct TileParams {
     int greedy;
 };
 
-int draft_num_segments(int B, int V, int w_bf16);
-int draft_segment_len(int B, int w_bf16);
+// Segment = the token range one (row, tile) summary covers: 128 tokens, or 64
+// for the streaming q-free tile.  Workspace is sized for the larger count.
+int draft_num_segments(const DraftArgs& a);
+int draft_segment_len(const DraftArgs& a);
+int draft_max_segments(int V);
 hipError_t draft_tile_launch(const DraftArgs& a, int k, hipStream_t s);
 hipError_t draft_finalize_launch(const DraftArgs& a, int k, hipStream_t s);
-hipError_t w2_transpose_launch(const uint16_t* W2, uint16_t* W2T, int r, int V, hipStream_t s);
+// W2 [r, V] bf16 -> packed image of w2p_bytes(r, V) bytes.
+hipError_t w2_pack_launch(const uint16_t* W2, uint16_t* W2P, int r, int V, hipStream_t s);
 // Recompute the logits of row b at position row_pos[b] (bit-identical to the
 // draft's tile kernel) into out [B, V].
 hipError_t residual_rows_launch(const TileParams& p, bool u_bf16, hipStream_t s);

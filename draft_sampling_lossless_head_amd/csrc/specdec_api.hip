@@ -2,6 +2,7 @@
 // validation, workspace carving and kernel dispatch on the caller's stream.
 #include <cmath>
 #include <cstdint>
+#include <algorithm>
 #include <string>
 
 #include "device_common.hpp"
@@ -32,7 +33,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool dtype_ok(int dt) { return dt == SPEC_F32 || dt == SPEC_BF16; }
 
 constexpr int kMaxV = 1 << 28;
-constexpr int kMaxDraftV = 2048 * 128;   // the finalize holds <= 8 tile summaries per thread
+constexpr int kMaxDraftV = 4096 * 64;    // the finalize holds <= 16 segment summaries per thread
 
 struct DraftLayout {
     size_t stats, gsums, w2t, hproj, state, erows, total;
@@ -41,13 +42,16 @@ struct DraftLayout {
 DraftLayout draft_layout(bool rnn, int B, int gamma, int V, int r) {
     DraftLayout L{};
     size_t off = 0;
-    const size_t nseg = (size_t)draft_num_segments(B, V, 1);
+    const size_t nseg = (size_t)draft_max_segments(V);   // 64-token segments at most
     L.stats = off;
     off += align_up((size_t)B * nseg * sizeof(SegStat));
-    L.gsums = off;   // q-free draft: 16 group sums per (row, tile)
-    off += align_up((size_t)B * nseg * 16 * sizeof(float));
-    L.w2t = off;   // transposed bf16 W2 when the caller passes no packed copy
-    off += align_up((size_t)V * r * sizeof(uint16_t));
+    // q-free draft: one sum per 8 tokens, per segment (16 per 128-token
+    // segment, 8 per 64-token segment; the 128-token layout can be larger)
+    const size_t ngs = std::max((size_t)((V + 127) / 128) * 16, nseg * 8);
+    L.gsums = off;
+    off += align_up((size_t)B * ngs * sizeof(float));
+    L.w2t = off;   // packed bf16 W2 when the caller passes none
+    off += align_up(w2p_bytes(r, V));
     if (rnn) {
         L.hproj = off;
         off += align_up((size_t)B * gamma * 3 * r * sizeof(float));
@@ -81,7 +85,7 @@ VerifyLayout verify_layout(int B, int gamma_max, int V, int markov_r = 0) {
         L.lrows = off;
         off += align_up((size_t)B * V * sizeof(float));
         L.w2t = off;
-        off += align_up((size_t)V * markov_r * sizeof(uint16_t));
+        off += align_up(w2p_bytes(markov_r, V));
     }
     L.total = off;
     return L;
@@ -140,10 +144,10 @@ spec_status_t run_draft(DraftArgs& a, void* stream) {
     hipError_t e;
     void* t;
     if (a.w_bf16 && !a.W2T) {
-        t = prof_begin("w2_transpose", s);
-        e = w2_transpose_launch((const uint16_t*)a.W2, a.W2T_ws, a.r, a.V, s);
+        t = prof_begin("w2_pack", s);
+        e = w2_pack_launch((const uint16_t*)a.W2, a.W2T_ws, a.r, a.V, s);
         prof_end(t, s);
-        if (e != hipSuccess) return hip_fail(e, "w2_transpose");
+        if (e != hipSuccess) return hip_fail(e, "w2_pack");
         a.W2T = a.W2T_ws;
     }
     if (a.head == kHeadRnn) {
@@ -159,7 +163,7 @@ spec_status_t run_draft(DraftArgs& a, void* stream) {
             prof_end(t, s);
             if (e != hipSuccess) return hip_fail(e, "rnn_gates");
         }
-        t = prof_begin("draft_tile", s);
+        t = prof_begin(a.q_logits ? "draft_tile" : "draft_tile_qfree", s);
         e = draft_tile_launch(a, k, s);
         prof_end(t, s);
         if (e != hipSuccess) return hip_fail(e, "draft_tile");
@@ -360,15 +364,20 @@ spec_status_t spec_verify(const void* P, int p_dtype, const void* Q, int q_dtype
     return e == hipSuccess ? SPEC_OK : hip_fail(e, "verify");
 }
 
+size_t spec_pack_w2_bytes(int r, int V) {
+    if (r <= 0 || V <= 0 || V > kMaxV) return 0;
+    return w2p_bytes(r, V);
+}
+
 spec_status_t spec_pack_w2(const void* W2, void* W2T, int r, int V, void* stream) {
     g_err.clear();
     if (r <= 0 || V <= 0 || V > kMaxV) return fail(SPEC_ERR_INVALID, "bad r or V");
     if (!W2 || !W2T) return fail(SPEC_ERR_INVALID, "null W2 or W2T");
+    if (r % 16 != 0 || r > 256) return fail(SPEC_ERR_UNSUPPORTED, "packing needs r % 16 == 0 and r <= 256");
     if (!aligned16(W2T)) return fail(SPEC_ERR_UNSUPPORTED, "W2T must be 16-byte aligned");
-    hipError_t e = w2_transpose_launch(static_cast<const uint16_t*>(W2),
-                                       static_cast<uint16_t*>(W2T), r, V,
-                                       static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? SPEC_OK : hip_fail(e, "w2_transpose");
+    hipError_t e = w2_pack_launch(static_cast<const uint16_t*>(W2), static_cast<uint16_t*>(W2T),
+                                  r, V, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SPEC_OK : hip_fail(e, "w2_pack");
 }
 
 size_t spec_verify_markov_workspace_size(int B, int gamma_max, int V, int r) {
@@ -438,11 +447,11 @@ spec_status_t spec_verify_markov(const void* P, int p_dtype, const void* U, int 
     if (!a.greedy && gamma_max > 0) {
         const uint16_t* w2t = static_cast<const uint16_t*>(W2T);
         if (!w2t) {
-            void* t = prof_begin("w2_transpose", s);
-            e = w2_transpose_launch(static_cast<const uint16_t*>(W2),
+            void* t = prof_begin("w2_pack", s);
+            e = w2_pack_launch(static_cast<const uint16_t*>(W2),
                                     reinterpret_cast<uint16_t*>(w + L.w2t), r, V, s);
             prof_end(t, s);
-            if (e != hipSuccess) return hip_fail(e, "w2_transpose");
+            if (e != hipSuccess) return hip_fail(e, "w2_pack");
             w2t = reinterpret_cast<const uint16_t*>(w + L.w2t);
         }
         TileParams tp{};

@@ -101,7 +101,7 @@ spec_status_t spec_philox_uniforms(uint64_t seed, uint32_t offset, uint32_t stre
  * W2       [r, V]         logit projection, dtype w_dtype
  *                         (BF16 runs on MFMA with fp32 accumulation; F32 runs
  *                         on the vector ALUs)
- * W2T      [V, r]         optional: W2 already packed by spec_pack_w2 (bf16
+ * W2T                     optional: W2 already packed by spec_pack_w2 (bf16
  *                         only).  NULL: W2 is packed into the workspace on
  *                         every call.  W2 may be NULL when W2T is given.
  * uniforms [B, gamma]     optional caller uniforms (stream 0 otherwise)
@@ -131,11 +131,20 @@ spec_status_t spec_draft_sample_markov(
     void *ws, size_t ws_bytes, void *stream);
 
 /*
- * W2 [r, V] bf16 -> W2T [V, r] bf16: the layout the bias contraction stages
- * per vocabulary tile.  Weights are static, so callers pack once and pass
- * W2T to the draft and verify calls.  W2T: caller-owned device buffer of
- * V * r bf16, 16-byte aligned.
+ * W2 [r, V] bf16 -> W2T, the packed image the bias contraction copies into
+ * LDS one 128-token tile at a time.  Weights are static, so callers pack once
+ * and pass W2T to the draft and verify calls.
+ * Layout (bf16 elements; a stable part of this interface): tile t holds tokens
+ * 128t .. 128t + 127 as 128 rows of r elements (rows past V are zero); row v's
+ * 16-byte chunk kc (elements 8kc .. 8kc + 7) is stored in chunk slot
+ * kc ^ s(v mod 128), where s(u) = (u & 7) | (((u >> 4) ^ (u >> 5) ^ (u >> 6)) & 1) << 3
+ * masked to F - 1, F = the largest power of two <= 16 that divides r / 8.
+ * So W2[j][v] sits at element v * r + 8 * ((j / 8) ^ s) + j % 8.
+ * W2T: caller-owned device buffer of spec_pack_w2_bytes(r, V) bytes,
+ * 16-byte aligned.  Needs r % 16 == 0 and r <= 256 (SPEC_ERR_UNSUPPORTED).
  */
+size_t spec_pack_w2_bytes(int r, int V);
+
 spec_status_t spec_pack_w2(const void *W2, void *W2T, int r, int V, void *stream);
 
 /*

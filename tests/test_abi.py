@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
     for n in ("spec_draft_sample_markov", "spec_draft_sample_rnn", "spec_verify",
               "spec_draft_markov_workspace_size", "spec_draft_rnn_workspace_size",
               "spec_verify_workspace_size", "spec_philox_uniforms", "spec_last_error",
-              "spec_version", "spec_pack_w2", "spec_verify_markov",
+              "spec_version", "spec_pack_w2", "spec_pack_w2_bytes", "spec_verify_markov",
               "spec_verify_markov_workspace_size"):
         assert n in names
 
@@ -51,6 +51,11 @@ def test_workspace_sizes(lib):
     assert a > 0 and a % 256 == 0
     assert lib.spec_draft_rnn_workspace_size(64, 8, 32000, 256, 4096) > \
         lib.spec_draft_markov_workspace_size(64, 8, 32000, 256)
+    # room for the summaries of 64-token segments, the 16 group sums of every
+    # 128-token segment and a packed W2 copy (V = 3000: 47 and 24 segments)
+    B, V, r = 40, 3000, 32
+    need = B * 47 * 16 + B * 24 * 16 * 4 + lib.spec_pack_w2_bytes(r, V)
+    assert lib.spec_draft_markov_workspace_size(B, 3, V, r) >= need
 
 
 def _markov(lib, **kw):
@@ -165,6 +170,12 @@ def test_pack_w2_validation(lib):
     assert lib.spec_pack_w2(None, fake, 64, 1000, None) == SPEC_ERR_INVALID
     assert lib.spec_pack_w2(fake, fake, 0, 1000, None) == SPEC_ERR_INVALID
     assert lib.spec_pack_w2(fake, ctypes.c_void_p(4098), 64, 1000, None) == SPEC_ERR_UNSUPPORTED
+    assert lib.spec_pack_w2(fake, fake, 40, 1000, None) == SPEC_ERR_UNSUPPORTED
+    assert lib.spec_pack_w2(fake, fake, 512, 1000, None) == SPEC_ERR_UNSUPPORTED
+    # whole 128-token tiles of r bf16
+    assert lib.spec_pack_w2_bytes(256, 151936) == 1187 * 128 * 256 * 2
+    assert lib.spec_pack_w2_bytes(16, 129) == 2 * 128 * 16 * 2
+    assert lib.spec_pack_w2_bytes(0, 100) == 0
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

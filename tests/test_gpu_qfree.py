@@ -37,6 +37,11 @@ DRAFT_CASES = [
     (4, 6, 131, 16, "f32", 1.0),        # two tiles
     (3, 4, 7, 16, "bf16", 1.0),         # one partial 8-token group
     (6, 4, 3000, 64, "bf16", 0.0),      # greedy
+    # streaming tile (bf16 U, V % 8 == 0, B > 64, r in {64, 128, 256}):
+    (130, 3, 3000, 256, "bf16", 1.0),   # two row blocks, one item per workgroup
+    (100, 3, 40000, 128, "bf16", 1.0),  # three items per workgroup: full pipeline
+    (200, 2, 20008, 64, "bf16", 0.9),   # row block changes inside a workgroup; 40-token tail
+    (80, 3, 16384, 256, "bf16", 0.0),   # greedy
 ]
 
 
@@ -63,6 +68,60 @@ def test_qfree_draft_parity(orc, B, gamma, V, r, udt, T):
     assert tally.boundary <= max(1, tally.draws // 50)
 
 
+def packed_image(W2, r, V):
+    """The packed W2 layout as the header documents it, built element by
+    element from W2 [r, V] (uint16 bf16 bits)."""
+    ntile = (V + 127) // 128
+    img = np.zeros(ntile * 128 * r, dtype=np.uint16)
+    nchunk = r // 8
+    F = min(16, nchunk & -nchunk)
+    for v in range(V):
+        u = v % 128
+        s = ((u & 7) | ((((u >> 4) ^ (u >> 5) ^ (u >> 6)) & 1) << 3)) & (F - 1)
+        for kc in range(nchunk):
+            dst = v * r + 8 * (kc ^ s)
+            img[dst:dst + 8] = W2[8 * kc:8 * kc + 8, v]
+    return img
+
+
+@pytest.mark.parametrize("r,V", [(64, 6001), (48, 300), (256, 1000), (16, 129)])
+def test_pack_w2_layout(r, V):
+    sd = require_gpu()
+    W2 = workloads.f32_to_bf16_bits(
+        np.random.default_rng(r + V).standard_normal((r, V)).astype(np.float32))
+    img = sd.spec_pack_w2(dev(W2, "bf16"))
+    torch.cuda.synchronize()
+    got = img.cpu().numpy().view(np.uint16)
+    assert got.nbytes == sd.spec_pack_w2_bytes(r, V)
+    assert np.array_equal(got, packed_image(W2, r, V))
+
+
+def test_qfree_draft_full_size_sampled(orc):
+    """B = 128, gamma = 16, V = 151936, r = 256, bf16: the streaming tile at the
+    size it is timed at; four requests are checked against the oracle."""
+    sd = require_gpu()
+    B, gamma, V, r = 128, 16, 151936, 256
+    sample = [0, 45, 96, 127]
+    cfg = dict(workloads.CONFIGS["markov-152k-b128"])
+    wl = workloads.make_markov(cfg, B=B, gamma=gamma, V=V, r=r)
+    seed = 77
+    W2T = sd.spec_pack_w2(dev(wl["W2"], "bf16"))
+    g = host(sd.spec_draft_sample_markov(dev(wl["U"], "bf16"), dev(wl["x0"]),
+                                         dev(wl["W1"], "bf16"), None, 1.0, W2T=W2T, q_free=True,
+                                         seed=seed))
+    W1, W2 = _weights(wl)
+    u = orc.draft_uniforms(seed, 0, B, gamma)
+    tally = compare.Tally()
+    for b in sample:
+        Ub = workloads.as_f64(wl["U"][b], "bf16")
+        o = orc.draft_markov(Ub, W1, W2, wl["x0"][b], 1.0, u[b])
+        compare.compare_draft_request(o, Ub, {k: v[b] for k, v in g.items()}, 1.0, u[b],
+                                      f"b={b}", tally, check_logits=False)
+    note(f"  {tally.as_dict()}")
+    assert np.all((g["tokens"] >= 0) & (g["tokens"] < V))
+    assert np.all(np.isfinite(g["q_logZ"])) and np.all(g["q_tok_prob"] > 0)
+
+
 def test_qfree_draft_packed_w2_and_uniforms(orc):
     """A W2T packed once by spec_pack_w2 gives the same result as W2, and
     caller uniforms replace the counter stream."""
@@ -72,8 +131,6 @@ def test_qfree_draft_packed_w2_and_uniforms(orc):
                                V=V, r=r)
     W2d = dev(wl["W2"], "bf16")
     W2T = sd.spec_pack_w2(W2d)
-    torch.cuda.synchronize()
-    assert np.array_equal(W2T.view(torch.int16).cpu().numpy().view(np.uint16), wl["W2"].T)
     uni = np.random.default_rng(8).random((B, gamma)).astype(np.float32)
     args = (dev(wl["U"]), dev(wl["x0"]), dev(wl["W1"], "bf16"))
     a = host(sd.spec_draft_sample_markov(*args, W2d, 1.0, q_free=True, uniforms=dev(uni)))
