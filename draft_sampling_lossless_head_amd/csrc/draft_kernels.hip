@@ -609,15 +609,16 @@ void draft_tile_stats(TileParams P) {
 // copied into an LDS stage by direct global->LDS loads: the packed W2 slice
 // (64 rows of r bf16, contiguous in the packed image) and the U slice (128 rows
 // x 64 bf16, 16-byte chunk c of row bl stored in slot bl*8 + (c ^ ((bl>>1)&7))).
-// Three stages: item i+2 streams in while item i is contracted and reduced,
-// so the memory pipe never waits for the ALUs.  The conditioning rows E stay
-// in registers for all items of a row block.
+// Three stages: item i+2 streams in while item i is contracted and reduced.
 //
-// Each wave owns 32 rows and all 64 tokens of an item (MB = 2 blocks), with
-// the token assignment of draft_tile_stats: lane (b, h) ends with tokens
-// 32h .. 32h + 31 of the slice.  A 64-token slice is one segment: per (row,
-// segment) the SegStat and 8 group sums, reduced over the lane and its partner
-// lane l ^ 32 only.
+// Eight waves, two per SIMD, so that one wave's MFMAs overlap the other's
+// vector work and load issue.  Wave w owns rows 16w .. 16w + 15 and all 64
+// tokens of an item, on 16x16x32 MFMAs: A = W2 slice (tokens x rank), B = E =
+// W1[x_{k-1}] rows (kept in registers for all items of a row block).  Block
+// m's MFMA row i = 4a + c is token 16a + 4m + c, so lane (row, a = lane/16)
+// ends with tokens 16a .. 16a + 15 of its row.  A 64-token slice is one
+// segment: per (row, segment) the SegStat and 8 group sums, reduced over the
+// four lanes of the row.
 //
 // Only the bf16-U, V % 8 == 0 shape is streamed this way (chunks never straddle
 // V); waits on the direct loads use explicit vmcnt counts and a bare s_barrier,
@@ -626,42 +627,60 @@ void draft_tile_stats(TileParams P) {
 constexpr int kStreamItem = 64;     // tokens per item / segment
 constexpr int kStreamRows = 128;    // request rows per item
 constexpr int kStreamStages = 3;
+constexpr int kStreamWaves = 8;
+constexpr int kCpolNT = 2;          // cache-policy bit "nt": streamed once, do not keep
+
+typedef float f32x4v_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ void wait_vmcnt_le(int n) {
     // s_waitcnt with expcnt and lgkmcnt at their "no wait" maxima; n <= 63
     switch (n) {
     case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
     case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
-    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
-    case 12: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
     default: __builtin_amdgcn_s_waitcnt(0x0F70); break;   // waiting for all is always safe
     }
 }
 
-template <int NKS>
-__global__ __launch_bounds__(256, 1)
+template <int NK, bool GREEDY>   // NK = r / 32 rank steps of the 16x16x32 MFMA
+__global__ __launch_bounds__(kStreamWaves * 64, 1)
 void draft_tile_stream(TileParams P, int nitem_v, int nrb) {
-    constexpr int R = NKS * 16;
+    constexpr int R = NK * 32;
     constexpr int W2B = kStreamItem * R * 2;             // packed W2 slice bytes
     constexpr int UB = kStreamRows * kStreamItem * 2;    // U slice bytes
     constexpr int STAGE = W2B + UB;
-    constexpr int W2P = W2B / 1024 / 4;                  // 1 KB pieces per wave
-    constexpr int UP = UB / 1024 / 4;
+    constexpr int W2P = W2B / 1024 / kStreamWaves;       // 1 KB pieces per wave
+    constexpr int UP = UB / 1024 / kStreamWaves;
     constexpr int LOADS = W2P + UP;                      // direct loads per wave per item
     constexpr int NCH = R / 8;
-    static_assert(W2P >= 1 && UP == 4, "piece split");
+    static_assert(W2P >= 1 && UP == 2, "piece split");
     extern __shared__ __align__(16) char smem_s[];
     const int V = P.V, k = P.k, B = P.B, gamma = P.gamma;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int h = lane >> 5;
-    const int kgrp = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar LDS addresses
+    const int a4 = lane >> 4;        // MFMA lane group: K chunk of the operands, token run of C
     const int G = gridDim.x;
     const int nitems = nitem_v * nrb;
     if ((int)blockIdx.x >= nitems) return;
     const int my_n = (nitems - 1 - (int)blockIdx.x) / G + 1;
     const uint16_t* Ub = static_cast<const uint16_t*>(P.U);
+
+    // This lane's U pieces: row bl and 16-byte chunk c of every item's slice,
+    // as offsets from the row block's first row.
+    size_t ubase[UP];
+    int ubl[UP], uc8[UP];
+#pragma unroll
+    for (int q = 0; q < UP; ++q) {
+        const int sl = (q * kStreamWaves + wave) * 64 + lane;
+        const int bl = sl >> 3;
+        const int c = (sl & 7) ^ ((bl >> 1) & 7);
+        ubl[q] = bl;
+        uc8[q] = c * 8;
+        ubase[q] = ((size_t)bl * gamma + k) * (size_t)V + c * 8;
+    }
+    const size_t rb_stride = (size_t)kStreamRows * gamma * (size_t)V;
 
     auto issue = [&](int i) {
         const int w = blockIdx.x + i * G;
@@ -670,32 +689,29 @@ void draft_tile_stream(TileParams P, int nitem_v, int nrb) {
         const char* wsrc = reinterpret_cast<const char*>(P.W2T) + (size_t)iv * W2B;
 #pragma unroll
         for (int q = 0; q < W2P; ++q) {
-            const int pc = q * 4 + wave;
+            const int pc = q * kStreamWaves + wave;
             __builtin_amdgcn_global_load_lds(wsrc + pc * 1024 + lane * 16,
                                              (lds_ptr_t)(st + pc * 1024), 16, 0, 0);
         }
+        const size_t item_off = (size_t)rb * rb_stride + (size_t)iv * kStreamItem;
 #pragma unroll
         for (int q = 0; q < UP; ++q) {
-            const int pc = q * 4 + wave;
-            const int sl = pc * 64 + lane;                 // 16-byte slot of the U slice
-            const int bl = sl >> 3;
-            const int c = (sl & 7) ^ ((bl >> 1) & 7);
-            const int bg = rb * kStreamRows + bl;
-            const int v = iv * kStreamItem + c * 8;
-            const size_t off = (bg < B && v < V) ? ((size_t)bg * gamma + k) * (size_t)V + v
-                                                 : (size_t)k * (size_t)V;   // any valid chunk
-            __builtin_amdgcn_global_load_lds(Ub + off, (lds_ptr_t)(st + W2B + pc * 1024), 16, 0, 0);
+            const int pc = q * kStreamWaves + wave;
+            const bool ok = rb * kStreamRows + ubl[q] < B && iv * kStreamItem + uc8[q] < V;
+            const size_t off = ok ? ubase[q] + item_off : (size_t)k * (size_t)V;   // any valid chunk
+            __builtin_amdgcn_global_load_lds(Ub + off, (lds_ptr_t)(st + W2B + pc * 1024), 16, 0,
+                                             kCpolNT);
         }
     };
 
-    // Conditioning rows E = W1[x_{k-1}] of a row block.
+    // Conditioning rows E = W1[x_{k-1}] of a row block (MFMA B operand).
     int cur_rb = -1;
-    bf16x8_t e[NKS];
+    bf16x8_t e[NK];
     bool erow_ok = false;
     int b = 0;
     auto load_e = [&](int rb) {
         cur_rb = rb;
-        b = rb * kStreamRows + wave * 32 + (lane & 31);
+        b = rb * kStreamRows + wave * 16 + (lane & 15);
         int prev = 0;
         erow_ok = false;
         if (b < B) {
@@ -704,9 +720,9 @@ void draft_tile_stream(TileParams P, int nitem_v, int nrb) {
         }
         const uint16_t* erow = P.W1 + (size_t)(erow_ok ? prev : 0) * R;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
+        for (int ks = 0; ks < NK; ++ks) {
             if (erow_ok) {
-                e[ks] = *reinterpret_cast<const bf16x8_t*>(erow + ks * 16 + kgrp * 8);
+                e[ks] = *reinterpret_cast<const bf16x8_t*>(erow + ks * 32 + a4 * 8);
             } else {
 #pragma unroll
                 for (int t = 0; t < 8; ++t) e[ks][t] = (__bf16)0.0f;
@@ -721,19 +737,99 @@ void draft_tile_stream(TileParams P, int nitem_v, int nrb) {
     issue(0);
     if (my_n > 1) issue(1);
 
-    // A-operand rows of this lane (token of MFMA row i = lane % 32, block mb)
-    int arow[2], aswz_lo[2];
-    {
-        const int i = lane & 31;
-        const int hi = (i >> 2) & 1, g = i >> 3, c = i & 3;
+    // A-operand row of this lane in block m: token 16 * (i / 4) + 4m + i % 4, i = lane % 16
+    int arow[4], atok[4];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-            const int t = 32 * hi + 16 * mb + 4 * g + c;
-            arow[mb] = t * R;
-            aswz_lo[mb] = t;   // swizzle needs the token's position in its 128-token tile
-        }
+    for (int mb = 0; mb < 4; ++mb) {
+        const int i = lane & 15;
+        atok[mb] = 16 * (i >> 2) + 4 * mb + (i & 3);
+        arow[mb] = atok[mb] * R;
     }
+    const int bl = wave * 16 + (lane & 15);
+    const int uslot0 = bl * 8;
+    const int uswz = (bl >> 1) & 7;
+    const float sc = P.invT * 1.4426950408889634f;   // exp(y / T) = 2^(y * sc)
 
+    // Reduction of one finished item (its accumulators and U chunks) to the
+    // summaries of (row, segment iv).  Branch-free, and run one iteration
+    // behind the contraction so that the scheduler can interleave the vector
+    // work of item i-1 with the MFMAs of item i.
+    struct Red {
+        float m, tot, gs0, gs1;
+        int am;
+    };
+    auto reduce = [&](const f32x4v_t (&ac)[4], const u32x4_t (&uf)[2], int iv) -> Red {
+        const int v0 = iv * kStreamItem + 16 * a4;
+        float x[16];
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int j = 8 * q + 2 * t;   // run position of the pair
+                x[j] = ac[j >> 2][j & 3] + __uint_as_float(uf[q][t] << 16);
+                x[j + 1] = ac[(j + 1) >> 2][(j + 1) & 3] + __uint_as_float(uf[q][t] & 0xFFFF0000u);
+            }
+#pragma unroll
+        for (int t = 0; t < 16; ++t) x[t] = v0 + t < V ? x[t] : -INFINITY;
+        Red o;
+        float m = x[0];
+#pragma unroll
+        for (int t = 1; t < 16; ++t) m = fmaxf(m, x[t]);
+        o.am = 0;   // the argmax is only read by greedy decoding
+        if constexpr (GREEDY) {
+            int am = INT_MAX;
+#pragma unroll
+            for (int t = 15; t >= 0; --t) am = x[t] == m ? v0 + t : am;
+#pragma unroll
+            for (int off = 16; off <= 32; off <<= 1) {
+                const float m2 = __shfl_xor(m, off);
+                const int a2 = __shfl_xor(am, off);
+                am = (m2 > m || (m2 == m && a2 < am)) ? a2 : am;
+                m = fmaxf(m, m2);
+            }
+            o.am = am;
+            o.gs0 = o.gs1 = o.tot = 0.0f;
+        } else {
+            m = fmaxf(m, __shfl_xor(m, 16));
+            m = fmaxf(m, __shfl_xor(m, 32));
+            const float ms = m == -INFINITY ? 0.0f : m * sc;   // all -inf: every weight 0
+            float g0 = 0.0f, g1 = 0.0f;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                g0 += __builtin_amdgcn_exp2f(fmaf(x[t], sc, -ms));
+                g1 += __builtin_amdgcn_exp2f(fmaf(x[8 + t], sc, -ms));
+            }
+            float tot = g0 + g1;
+            tot += __shfl_xor(tot, 16);
+            tot += __shfl_xor(tot, 32);
+            o.gs0 = g0;
+            o.gs1 = g1;
+            o.tot = tot;
+        }
+        o.m = m;
+        return o;
+    };
+    auto store = [&](const Red& o, int iv, int bw) {
+        if constexpr (!GREEDY)
+            *reinterpret_cast<float2*>(P.gsums + ((size_t)bw * nitem_v + iv) * 8 + 2 * a4) =
+                make_float2(o.gs0, o.gs1);
+        if (a4 == 0) {
+            SegStat sst;
+            sst.m = o.m;
+            sst.s = o.tot;
+            sst.idx = o.am;
+            sst.pad = 0;
+            P.stats[(size_t)bw * nitem_v + iv] = sst;
+        }
+    };
+
+    f32x4v_t accp[4];
+    u32x4_t ufrp[2];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) accp[mb] = f32x4v_t{0.0f, 0.0f, 0.0f, 0.0f};
+    ufrp[0] = ufrp[1] = u32x4_t{0u, 0u, 0u, 0u};
+    int ivp = 0, bp = 0;
+    bool okp = false;   // nothing to store before the first item
     for (int i = 0; i < my_n; ++i) {
         const int w = blockIdx.x + i * G;
         const int rb = w / nitem_v, iv = w % nitem_v;
@@ -748,86 +844,54 @@ void draft_tile_stream(TileParams P, int nitem_v, int nrb) {
         const char* st = smem_s + (i % kStreamStages) * STAGE;
         const uint16_t* w2s = reinterpret_cast<const uint16_t*>(st);
         const int half = (iv & 1) * 64;
-        f32x16_t acc[2];
+        int sw[4];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < 4; ++mb) sw[mb] = w2p_swizzle(half + atok[mb], NCH);
+        bf16x8_t afr[NK][4];
 #pragma unroll
-            for (int t = 0; t < 16; ++t) acc[mb][t] = 0.0f;
-        int sw[2];
+        for (int ks = 0; ks < NK; ++ks) {
+            const int kc = 4 * ks + a4;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) sw[mb] = w2p_swizzle(half + aswz_lo[mb], NCH);
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            const int kc = 2 * ks + kgrp;
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-                const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-                    w2s + arow[mb] + ((kc ^ sw[mb]) << 3));
-                acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, e[ks], acc[mb], 0, 0, 0);
-            }
+            for (int mb = 0; mb < 4; ++mb)
+                afr[ks][mb] = *reinterpret_cast<const bf16x8_t*>(w2s + arow[mb] + ((kc ^ sw[mb]) << 3));
         }
-
-        // logits of the lane's 32 tokens: bias + U (from the stage), -inf past V
-        const int bl = wave * 32 + (lane & 31);
         const uint32_t* us = reinterpret_cast<const uint32_t*>(st + W2B);
-        const int v0 = iv * kStreamItem + 32 * h;
-        float x[32];
+        u32x4_t ufr[2];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int c = 4 * h + q;
-            const u32x4_t u4 = *reinterpret_cast<const u32x4_t*>(
-                us + (bl * 8 + (c ^ ((bl >> 1) & 7))) * 4);
+        for (int q = 0; q < 2; ++q)
+            ufr[q] = *reinterpret_cast<const u32x4_t*>(us + (uslot0 + ((2 * a4 + q) ^ uswz)) * 4);
+        f32x4v_t acc[4];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int j = 8 * q + 2 * t;   // run position of the pair
-                x[j] = acc[j >> 4][j & 15] + bf16_bits_to_float(u4[t] & 0xFFFFu);
-                x[j + 1] = acc[(j + 1) >> 4][(j + 1) & 15] + bf16_bits_to_float(u4[t] >> 16);
+        for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x4v_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < NK; ++ks)
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+                acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[ks][mb], e[ks], acc[mb], 0, 0, 0);
+        const Red red = reduce(accp, ufrp, ivp);
+        {   // schedule: LDS reads ahead, then MFMAs interleaved with the reads
+            // and with the previous item's vector work
+            constexpr int NR = 4 * NK + 2;
+            constexpr int kAhead = NR < 10 ? NR : 10;
+            __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+            for (int j = 0; j < 4 * NK; ++j) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (j < NR - kAhead) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
             }
         }
-        if (v0 + 32 > V) {
+        if (okp) store(red, ivp, bp);
 #pragma unroll
-            for (int t = 0; t < 32; ++t)
-                if (v0 + t >= V) x[t] = -INFINITY;
-        }
-        float m = x[0];
-#pragma unroll
-        for (int t = 1; t < 32; ++t) m = fmaxf(m, x[t]);
-        int am = INT_MAX;
-#pragma unroll
-        for (int t = 31; t >= 0; --t)
-            if (x[t] == m) am = v0 + t;
-        {
-            const float m2 = __shfl_xor(m, 32);
-            const int a2 = __shfl_xor(am, 32);
-            merge_arg(m, am, m2, a2);
-        }
-        float gs[4];
-        float tot = 0.0f;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            float sg = 0.0f;
-            if (!P.greedy && m != -INFINITY) {
-#pragma unroll
-                for (int t = 0; t < 8; ++t) sg += __expf((x[8 * g + t] - m) * P.invT);
-            }
-            gs[g] = sg;
-            tot += sg;
-        }
-        tot += __shfl_xor(tot, 32);
-        if (b < B && erow_ok) {
-            if (!P.greedy)
-                *reinterpret_cast<float4*>(P.gsums + ((size_t)b * nitem_v + iv) * 8 + 4 * h) =
-                    make_float4(gs[0], gs[1], gs[2], gs[3]);
-            if (h == 0) {
-                SegStat sst;
-                sst.m = m;
-                sst.s = tot;
-                sst.idx = am;
-                sst.pad = 0;
-                P.stats[(size_t)b * nitem_v + iv] = sst;
-            }
-        }
+        for (int mb = 0; mb < 4; ++mb) accp[mb] = acc[mb];
+        ufrp[0] = ufr[0];
+        ufrp[1] = ufr[1];
+        ivp = iv;
+        bp = b;
+        okp = b < B && erow_ok;
     }
+    const Red red = reduce(accp, ufrp, ivp);
+    if (okp) store(red, ivp, bp);
 }
 
 // ---------------------------------------------------------------------------
@@ -1322,13 +1386,15 @@ static int cu_count() {
     return n[dev];
 }
 
-template <int NKS>
+template <int NK>
 static hipError_t launch_stream(const TileParams& p, hipStream_t s) {
-    constexpr int STAGE = kStreamItem * NKS * 16 * 2 + kStreamRows * kStreamItem * 2;
+    constexpr int STAGE = kStreamItem * NK * 32 * 2 + kStreamRows * kStreamItem * 2;
     const size_t lds = (size_t)kStreamStages * STAGE;
     static bool attr_set = false;
     if (!attr_set) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&draft_tile_stream<NKS>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&draft_tile_stream<NK, false>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&draft_tile_stream<NK, true>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         (void)hipGetLastError();
         attr_set = true;
@@ -1336,7 +1402,12 @@ static hipError_t launch_stream(const TileParams& p, hipStream_t s) {
     const int nitem_v = (p.V + kStreamItem - 1) / kStreamItem;
     const int nrb = (p.B + kStreamRows - 1) / kStreamRows;
     const int grid = std::min(nitem_v * nrb, cu_count());
-    hipLaunchKernelGGL((draft_tile_stream<NKS>), dim3(grid), dim3(256), lds, s, p, nitem_v, nrb);
+    if (p.greedy)
+        hipLaunchKernelGGL((draft_tile_stream<NK, true>), dim3(grid), dim3(kStreamWaves * 64), lds,
+                           s, p, nitem_v, nrb);
+    else
+        hipLaunchKernelGGL((draft_tile_stream<NK, false>), dim3(grid), dim3(kStreamWaves * 64), lds,
+                           s, p, nitem_v, nrb);
     return hipGetLastError();
 }
 
@@ -1439,9 +1510,9 @@ hipError_t draft_tile_launch(const DraftArgs& a, int k, hipStream_t s) {
     if (a.head == kHeadMarkov) {
         if (a.q_logits) return launch_tile_b<kHeadMarkov, kOutQ>(p, a.u_bf16, s);
         if (draft_streams(a)) {
-            if (a.r == 256) return launch_stream<16>(p, s);
-            if (a.r == 128) return launch_stream<8>(p, s);
-            return launch_stream<4>(p, s);
+            if (a.r == 256) return launch_stream<8>(p, s);
+            if (a.r == 128) return launch_stream<4>(p, s);
+            return launch_stream<2>(p, s);
         }
         const int wb = pick_wb(a.B);
         if (wb == 1) return launch_stats<1>(p, a.u_bf16, s);

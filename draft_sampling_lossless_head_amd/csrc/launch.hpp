@@ -15,13 +15,14 @@ enum { kHeadMarkov = 0, kHeadRnn = 1 };
 // tokens: tile t holds tokens 128t .. 128t + 127 (zeros past V), token v as r
 // contiguous bf16 split into r / 8 chunks of 16 bytes, and chunk kc of token
 // v sits in slot kc ^ w2p_swizzle(v % 128, r / 8) of its row.  A tile is one
-// contiguous block of 256 * r bytes that a workgroup copies into LDS as is;
-// the XOR swizzle spreads the 16-byte reads of an MFMA operand over all LDS
-// banks.
+// contiguous block of 256 * r bytes that a workgroup copies into LDS as is.
+// The XOR swizzle makes the 16-byte operand reads of a 16x16x32 MFMA block
+// conflict-free: 16 lanes read tokens 16a + 4m + c (a, c = 0..3, block m
+// fixed) at one chunk, and s = c | ((a ^ m) << 2) gives 16 distinct slots.
 constexpr int kPackTile = 128;
 
 __host__ __device__ inline int w2p_swizzle(int vl, int nchunk) {
-    int f = (vl & 7) | ((((vl >> 4) ^ (vl >> 5) ^ (vl >> 6)) & 1) << 3);
+    const int f = (vl & 3) | ((((vl >> 4) ^ (vl >> 2)) & 3) << 2);
     int F = nchunk & -nchunk;           // largest power of two dividing nchunk
     if (F > 16) F = 16;
     return f & (F - 1);

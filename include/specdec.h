@@ -137,7 +137,7 @@ spec_status_t spec_draft_sample_markov(
  * Layout (bf16 elements; a stable part of this interface): tile t holds tokens
  * 128t .. 128t + 127 as 128 rows of r elements (rows past V are zero); row v's
  * 16-byte chunk kc (elements 8kc .. 8kc + 7) is stored in chunk slot
- * kc ^ s(v mod 128), where s(u) = (u & 7) | (((u >> 4) ^ (u >> 5) ^ (u >> 6)) & 1) << 3
+ * kc ^ s(v mod 128), where s(u) = (u & 3) | ((((u >> 4) ^ (u >> 2)) & 3) << 2)
  * masked to F - 1, F = the largest power of two <= 16 that divides r / 8.
  * So W2[j][v] sits at element v * r + 8 * ((j / 8) ^ s) + j % 8.
  * W2T: caller-owned device buffer of spec_pack_w2_bytes(r, V) bytes,

@@ -77,7 +77,7 @@ def packed_image(W2, r, V):
     F = min(16, nchunk & -nchunk)
     for v in range(V):
         u = v % 128
-        s = ((u & 7) | ((((u >> 4) ^ (u >> 5) ^ (u >> 6)) & 1) << 3)) & (F - 1)
+        s = ((u & 3) | ((((u >> 4) ^ (u >> 2)) & 3) << 2)) & (F - 1)
         for kc in range(nchunk):
             dst = v * r + 8 * (kc ^ s)
             img[dst:dst + 8] = W2[8 * kc:8 * kc + 8, v]
