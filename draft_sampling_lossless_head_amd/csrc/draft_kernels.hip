@@ -628,6 +628,7 @@ constexpr int kStreamItem = 64;     // tokens per item / segment
 constexpr int kStreamRows = 128;    // request rows per item
 constexpr int kStreamStages = 3;
 constexpr int kStreamWaves = 8;
+constexpr int kMaxShares = 256;    // share summaries per row (one per finalize thread)
 constexpr int kCpolNT = 2;          // cache-policy bit "nt": streamed once, do not keep
 
 typedef float f32x4v_t __attribute__((ext_vector_type(4)));
@@ -645,7 +646,7 @@ __device__ __forceinline__ void wait_vmcnt_le(int n) {
 
 template <int NK, bool GREEDY>   // NK = r / 32 rank steps of the 16x16x32 MFMA
 __global__ __launch_bounds__(kStreamWaves * 64, 1)
-void draft_tile_stream(TileParams P, int nitem_v, int nrb) {
+void draft_tile_stream(TileParams P, int nitem_v, int nrb, int ws) {
     constexpr int R = NK * 32;
     constexpr int W2B = kStreamItem * R * 2;             // packed W2 slice bytes
     constexpr int UB = kStreamRows * kStreamItem * 2;    // U slice bytes
@@ -661,10 +662,15 @@ void draft_tile_stream(TileParams P, int nitem_v, int nrb) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar LDS addresses
     const int a4 = lane >> 4;        // MFMA lane group: K chunk of the operands, token run of C
-    const int G = gridDim.x;
-    const int nitems = nitem_v * nrb;
-    if ((int)blockIdx.x >= nitems) return;
-    const int my_n = (nitems - 1 - (int)blockIdx.x) / G + 1;
+    // Workgroup g takes row block g / ws and the j-th contiguous share [lo, hi)
+    // of that block's slices (j = g % ws; ws <= nitem_v, so every share is
+    // non-empty).  Contiguous shares let the workgroup also summarise its
+    // whole token range per row.
+    const int rb0 = (int)blockIdx.x / ws;
+    const int jw = (int)blockIdx.x % ws;
+    const int lo = (int)((long long)jw * nitem_v / ws);
+    const int hi = (int)((long long)(jw + 1) * nitem_v / ws);
+    const int my_n = hi - lo;
     const uint16_t* Ub = static_cast<const uint16_t*>(P.U);
 
     // This lane's U pieces: row bl and 16-byte chunk c of every item's slice,
@@ -683,8 +689,7 @@ void draft_tile_stream(TileParams P, int nitem_v, int nrb) {
     const size_t rb_stride = (size_t)kStreamRows * gamma * (size_t)V;
 
     auto issue = [&](int i) {
-        const int w = blockIdx.x + i * G;
-        const int rb = w / nitem_v, iv = w % nitem_v;
+        const int rb = rb0, iv = lo + i;
         char* st = smem_s + (i % kStreamStages) * STAGE;
         const char* wsrc = reinterpret_cast<const char*>(P.W2T) + (size_t)iv * W2B;
 #pragma unroll
@@ -704,13 +709,11 @@ void draft_tile_stream(TileParams P, int nitem_v, int nrb) {
         }
     };
 
-    // Conditioning rows E = W1[x_{k-1}] of a row block (MFMA B operand).
-    int cur_rb = -1;
+    // Conditioning rows E = W1[x_{k-1}] of the row block (MFMA B operand).
     bf16x8_t e[NK];
     bool erow_ok = false;
     int b = 0;
     auto load_e = [&](int rb) {
-        cur_rb = rb;
         b = rb * kStreamRows + wave * 16 + (lane & 15);
         int prev = 0;
         erow_ok = false;
@@ -732,7 +735,7 @@ void draft_tile_stream(TileParams P, int nitem_v, int nrb) {
     // E must be complete before any direct load is in flight: the compiler
     // treats plain and direct loads pending together as unordered and would
     // otherwise drain every prefetch before each contraction.
-    load_e((int)blockIdx.x / nitem_v);
+    load_e(rb0);
     wait_vmcnt_le(0);
     issue(0);
     if (my_n > 1) issue(1);
@@ -809,17 +812,20 @@ void draft_tile_stream(TileParams P, int nitem_v, int nrb) {
         o.m = m;
         return o;
     };
+    // Summaries are segment-major, [segment][row] with rows padded to whole
+    // row blocks, so one wave's stores for an item are one contiguous run.
+    const size_t bpad = (size_t)nrb * kStreamRows;
     auto store = [&](const Red& o, int iv, int bw) {
+        const size_t si = (size_t)iv * bpad + bw;
         if constexpr (!GREEDY)
-            *reinterpret_cast<float2*>(P.gsums + ((size_t)bw * nitem_v + iv) * 8 + 2 * a4) =
-                make_float2(o.gs0, o.gs1);
+            *reinterpret_cast<float2*>(P.gsums + si * 8 + 2 * a4) = make_float2(o.gs0, o.gs1);
         if (a4 == 0) {
             SegStat sst;
             sst.m = o.m;
             sst.s = o.tot;
             sst.idx = o.am;
             sst.pad = 0;
-            P.stats[(size_t)bw * nitem_v + iv] = sst;
+            P.stats[si] = sst;
         }
     };
 
@@ -829,17 +835,41 @@ void draft_tile_stream(TileParams P, int nitem_v, int nrb) {
     for (int mb = 0; mb < 4; ++mb) accp[mb] = f32x4v_t{0.0f, 0.0f, 0.0f, 0.0f};
     ufrp[0] = ufrp[1] = u32x4_t{0u, 0u, 0u, 0u};
     int ivp = 0, bp = 0;
-    bool okp = false;   // nothing to store before the first item
-    for (int i = 0; i < my_n; ++i) {
-        const int w = blockIdx.x + i * G;
-        const int rb = w / nitem_v, iv = w % nitem_v;
-        if (rb != cur_rb) {   // a new row block (B > 128): reload E and drain
-            load_e(rb);
-            wait_vmcnt_le(0);
+    bool okp = false;   // nothing to reduce before the first item
+    // Item i-2's summaries are stored at the top of iteration i, before the
+    // prefetch: stores count in vmcnt too, and only loads may be newer than
+    // the item a wait is for (stores and loads may retire out of order).
+    Red redh{};
+    int ivh = 0, bh = 0;
+    bool okh = false;
+    // Running summary of the workgroup's whole range for this lane's row.
+    float run_m = -INFINITY, run_s = 0.0f;
+    int run_a = INT_MAX;
+    auto absorb_run = [&](const Red& o) {
+        if constexpr (GREEDY) {
+            run_a = (o.m > run_m || (o.m == run_m && o.am < run_a)) ? o.am : run_a;
+            run_m = fmaxf(run_m, o.m);
+        } else {
+            const float nm = fmaxf(run_m, o.m);
+            const float a = run_m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((run_m - nm) * sc);
+            const float c = o.m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((o.m - nm) * sc);
+            run_s = run_s * a + o.tot * c;
+            run_m = nm;
         }
+    };
+    for (int i = 0; i < my_n; ++i) {
+        const int iv = lo + i;
         wait_vmcnt_le(i + 1 < my_n ? LOADS : 0);   // item i's direct loads (this wave)
         asm volatile("s_barrier" ::: "memory");    // ... and every wave's; stage (i-1)%3 is free
+        if (okh) store(redh, ivh, bh);
         if (i + 2 < my_n) issue(i + 2);
+
+        // The two waves of a SIMD (w and w + 4) take the phases in opposite
+        // order: one contracts item i while the other reduces item i-1, so the
+        // matrix core and the vector ALU are busy at the same time.
+        const bool reduce_first = (wave & 4) != 0;
+        Red red;
+        if (reduce_first) red = reduce(accp, ufrp, ivp);
 
         const char* st = smem_s + (i % kStreamStages) * STAGE;
         const uint16_t* w2s = reinterpret_cast<const uint16_t*>(st);
@@ -868,20 +898,23 @@ void draft_tile_stream(TileParams P, int nitem_v, int nrb) {
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb)
                 acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[ks][mb], e[ks], acc[mb], 0, 0, 0);
-        const Red red = reduce(accp, ufrp, ivp);
-        {   // schedule: LDS reads ahead, then MFMAs interleaved with the reads
-            // and with the previous item's vector work
+        {   // schedule: LDS reads ahead, then one MFMA per further read
             constexpr int NR = 4 * NK + 2;
             constexpr int kAhead = NR < 10 ? NR : 10;
             __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
 #pragma unroll
-            for (int j = 0; j < 4 * NK; ++j) {
+            for (int j = 0; j < NR - kAhead; ++j) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (j < NR - kAhead) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4 * NK - (NR - kAhead), 0);
         }
-        if (okp) store(red, ivp, bp);
+        if (!reduce_first) red = reduce(accp, ufrp, ivp);
+        if (okp) absorb_run(red);
+        redh = red;
+        ivh = ivp;
+        bh = bp;
+        okh = okp;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) accp[mb] = acc[mb];
         ufrp[0] = ufr[0];
@@ -890,8 +923,20 @@ void draft_tile_stream(TileParams P, int nitem_v, int nrb) {
         bp = b;
         okp = b < B && erow_ok;
     }
+    if (okh) store(redh, ivh, bh);
     const Red red = reduce(accp, ufrp, ivp);
-    if (okp) store(red, ivp, bp);
+    if (okp) {
+        store(red, ivp, bp);
+        absorb_run(red);
+        if (a4 == 0) {   // the workgroup's summary of row b over segments [lo, hi)
+            SegStat sst;
+            sst.m = run_m;
+            sst.s = GREEDY ? 0.0f : run_s;
+            sst.idx = GREEDY ? run_a : 0;
+            sst.pad = 0;
+            P.sup[(size_t)jw * bpad + bp] = sst;
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -964,8 +1009,10 @@ constexpr int kFinRun = 16;  // max summaries per thread (nseg <= 4096)
 
 // Inputs the q-free draft needs to rebuild 8 logits of one tile row.
 struct RebuildArgs {
-    const float* gsums;     // [B, nseg, gps] group sums relative to the segment max
+    const float* gsums;     // group sums relative to the segment max, gps per summary
     int gps;                // 8-token groups per segment
+    int row_stride;         // summaries between rows b and b + 1 (stats and gsums)
+    int seg_stride;         // summaries between segments j and j + 1 of one row
     const void* U;          // [B, gamma, V]
     int u_bf16;
     const uint16_t* W1;     // [V, r]
@@ -1001,7 +1048,8 @@ void draft_finalize(const SegStat* __restrict__ stats, int nseg, int seg_len,
         }
         return;
     }
-    const SegStat* st = stats + (size_t)b * nseg;
+    const SegStat* st = stats + (size_t)b * rb.row_stride;   // segment j at st[j * seg_stride]
+    const size_t sj = (size_t)rb.seg_stride;
     const int per = (nseg + 255) / 256;
     const int j0 = min(nseg, tid * per);
     const int n = min(nseg, j0 + per) - j0;
@@ -1010,7 +1058,7 @@ void draft_finalize(const SegStat* __restrict__ stats, int nseg, int seg_len,
 #pragma unroll
     for (int t = 0; t < kFinRun; ++t) {
         if (t < n) {
-            const SegStat x = st[j0 + t];
+            const SegStat x = st[(size_t)(j0 + t) * sj];
             sm[t] = x.m;
             ss[t] = x.s;
             si[t] = x.idx;
@@ -1122,10 +1170,11 @@ void draft_finalize(const SegStat* __restrict__ stats, int nseg, int seg_len,
     if (q_logits == nullptr) {
         // q-free draft: locate the 8-token group from the tile's group sums,
         // then rebuild that group's logits l = U + W1[prev] . W2[:, v].
-        const float mseg = st[seg].m;
+        const float mseg = st[(size_t)seg * sj].m;
         const double scale = (double)expf((mseg - M) * invT);   // as the tile weight
         const double wg = lane < rb.gps
-                              ? (double)rb.gsums[((size_t)b * nseg + seg) * rb.gps + lane] * scale
+                              ? (double)rb.gsums[((size_t)b * rb.row_stride + (size_t)seg * sj) *
+                                                         rb.gps + lane] * scale
                               : 0.0;
         const double ginc = wave_inclusive_scan_f64(wg);
         double gexc = __shfl_up(ginc, 1);
@@ -1234,6 +1283,243 @@ void draft_finalize(const SegStat* __restrict__ stats, int nseg, int seg_len,
         tokens[outi] = pick;
         if (q_logZ) q_logZ[outi] = (float)(Md * (double)invT + log(Z));
         if (q_tok) q_tok[outi] = (float)(exp(((double)row[pick] - Md) * (double)invT) / Z);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Finalize of the streaming q-free draft.  One wave per request row (no
+// workgroup barriers); the inverse-CDF descent takes three dependent reads:
+//   1. the row's ws <= 256 share summaries, four per lane: max, normaliser and
+//      the share holding u * Z (fp64 weights and scan);
+//   2. the share's segment summaries and their 8 group sums, read together:
+//      the segment, then the 8-token group;
+//   3. the group's 8 logits rebuilt as U + W1[prev] . W2 (the W1 row slice is
+//      fetched at entry), then the token.
+// Scaling factors use fp32 exponentials (relative error ~1e-7); sums, scans
+// and the threshold are fp64.
+// ---------------------------------------------------------------------------
+struct FinStreamArgs {
+    const SegStat* sup;     // [ws][bpad]
+    const SegStat* stats;   // [nseg][bpad]
+    const float* gsums;     // [nseg][bpad][8]
+    int ws, nseg, bpad;
+    const int32_t* x0;
+    int32_t* tokens;
+    float* q_logZ;
+    float* q_tok;
+    const float* uniforms;
+    uint64_t seed;
+    uint32_t offset;
+    int gamma, V, k;
+    float invT;
+    int greedy;
+    const uint16_t* U;      // bf16 [B, gamma, V]
+    const uint16_t* W1;     // [V, r]
+    const uint16_t* W2P;    // packed W2 image
+    int r;
+};
+
+// Inverse CDF over one weight per lane (lanes in token order): the lane whose
+// interval [excl, incl) holds thr and thr - excl; past the end (rounding) the
+// last lane with weight and +inf.  Neighbouring intervals share end points.
+__device__ __forceinline__ int wave_pick(double w, double thr, double& rem) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const double incl = wave_inclusive_scan_f64(w);
+    double excl = __shfl_up(incl, 1);
+    if (lane == 0) excl = 0.0;
+    unsigned long long hit = __ballot(w > 0.0 && thr >= excl && thr < incl);
+    if (hit) {
+        const int l = __ffsll((long long)hit) - 1;
+        rem = thr - __shfl(excl, l);
+        return l;
+    }
+    const unsigned long long pos = __ballot(w > 0.0);
+    rem = INFINITY;
+    return pos ? 63 - __clzll((long long)pos) : 0;
+}
+
+__global__ __launch_bounds__(64)
+void draft_finalize_stream(FinStreamArgs A) {
+    const int b = blockIdx.x;
+    const int lane = threadIdx.x;
+    const size_t outi = (size_t)b * A.gamma + A.k;
+    const int V = A.V;
+    const float invT = A.invT;
+
+    const int prev = (A.k == 0) ? A.x0[b] : A.tokens[outi - 1];
+    if (prev < 0 || prev >= V) {
+        if (lane == 0) {
+            A.tokens[outi] = -1;
+            if (A.q_logZ) A.q_logZ[outi] = NAN;
+            if (A.q_tok) A.q_tok[outi] = NAN;
+        }
+        return;
+    }
+    const float u = A.uniforms ? A.uniforms[outi] : counter_uniform(A.seed, A.offset, b, A.k, 0);
+    // this lane's W1 slice for the rebuild (lane = 8t + sl: rank slice sl)
+    const int span = A.r / 8;   // <= 32 bf16: at most 4 chunks of 16 bytes
+    uint4 w1c[4];
+    {
+        const uint16_t* w1 = A.W1 + (size_t)prev * A.r + (lane & 7) * span;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            w1c[q] = (q * 8 < span) ? *reinterpret_cast<const uint4*>(w1 + q * 8)
+                                    : make_uint4(0u, 0u, 0u, 0u);
+    }
+
+    // 1) share summaries, four per lane (shares 4 * lane + q).
+    float sm[4], ss[4];
+    int si[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int j = 4 * lane + q;
+        if (j < A.ws) {
+            const SegStat x = A.sup[(size_t)j * A.bpad + b];
+            sm[q] = x.m;
+            ss[q] = x.s;
+            si[q] = x.idx;
+        } else {
+            sm[q] = -INFINITY;
+            ss[q] = 0.0f;
+            si[q] = INT_MAX;
+        }
+    }
+    float M = sm[0];
+    int AM = si[0];
+#pragma unroll
+    for (int q = 1; q < 4; ++q) merge_arg(M, AM, sm[q], si[q]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const float m2 = __shfl_xor(M, off);
+        const int i2 = __shfl_xor(AM, off);
+        merge_arg(M, AM, m2, i2);
+    }
+    if (A.greedy || M == -INFINITY) {
+        if (lane == 0) {
+            A.tokens[outi] = (M == -INFINITY) ? -1 : AM;
+            if (A.q_logZ) A.q_logZ[outi] = M == -INFINITY ? NAN : M;
+            if (A.q_tok) A.q_tok[outi] = M == -INFINITY ? NAN : 1.0f;
+        }
+        return;
+    }
+    double w[4];
+    double lsum = 0.0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        w[q] = sm[q] != -INFINITY ? (double)ss[q] * (double)__expf((sm[q] - M) * invT) : 0.0;
+        lsum += w[q];
+    }
+    const double Z = __shfl(wave_inclusive_scan_f64(lsum), kWave - 1);
+    const double thr = (double)u * Z;
+    double rem;
+    const int ol = wave_pick(lsum, thr, rem);
+    // the owning lane walks its four shares
+    int qsel = 3;
+    double qrem = INFINITY;
+    {
+        double run = 0.0;
+        int last = -1;
+        double last_run = 0.0;
+        int found = -1;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (found < 0 && w[q] > 0.0) {
+                last = q;
+                last_run = run;
+                if (rem < run + w[q]) {
+                    found = q;
+                    qrem = rem - run;
+                }
+            }
+            run += w[q];
+        }
+        if (found < 0) {
+            found = last < 0 ? 0 : last;
+            qrem = rem == INFINITY ? INFINITY : rem - last_run;
+        }
+        qsel = found;
+    }
+    const int sh = 4 * ol + __shfl(qsel, ol);
+    const double rem1 = __shfl(qrem, ol);
+
+    // 2) the share's segments and their group sums, one read.
+    const int s0 = (int)((long long)sh * A.nseg / A.ws);
+    const int s1 = (int)((long long)(sh + 1) * A.nseg / A.ws);
+    const int sg = s0 + lane;
+    const bool have = sg < s1;   // at most 64 segments per share (launcher guarantee)
+    float ym = -INFINITY, ys = 0.0f;
+    float4 g0 = make_float4(0.f, 0.f, 0.f, 0.f), g1 = g0;
+    if (have) {
+        const size_t sx = (size_t)sg * A.bpad + b;
+        const SegStat y = A.stats[sx];
+        ym = y.m;
+        ys = y.s;
+        g0 = *reinterpret_cast<const float4*>(A.gsums + sx * 8);
+        g1 = *reinterpret_cast<const float4*>(A.gsums + sx * 8 + 4);
+    }
+    const double ysc = ym != -INFINITY ? (double)__expf((ym - M) * invT) : 0.0;
+    double rem2;
+    const int sl_seg = wave_pick((double)ys * ysc, rem1, rem2);
+    const int seg = s0 + sl_seg;
+    // the chosen segment's 8 group weights to lanes 0..7
+    const double gscale = __shfl(ysc, sl_seg);
+    const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    float mine = 0.0f;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+        const float v = __shfl(gv[g], sl_seg);
+        if (lane == g) mine = v;
+    }
+    double grem;
+    const int grp = wave_pick(lane < 8 ? (double)mine * gscale : 0.0, rem2, grem);
+
+    // 3) rebuild the group's 8 logits: lane = 8t + sl.
+    const int t = lane >> 3, sl = lane & 7;
+    const int vt = seg * kStreamItem + grp * 8 + t;
+    float part = 0.0f;
+    float ut = 0.0f;
+    if (vt < V) {
+        const int nswz = w2p_swizzle(vt & (kPackTile - 1), A.r >> 3);
+        if ((span & 7) == 0) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (q * 8 < span) {
+                    const int kc = sl * (span >> 3) + q;
+                    const uint4 c = *reinterpret_cast<const uint4*>(
+                        A.W2P + (size_t)vt * A.r + ((kc ^ nswz) << 3));
+                    const uint32_t aw[4] = {w1c[q].x, w1c[q].y, w1c[q].z, w1c[q].w};
+                    const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) {
+                        part = fmaf(bf16_bits_to_float(aw[h] & 0xFFFFu),
+                                    bf16_bits_to_float(cw[h] & 0xFFFFu), part);
+                        part = fmaf(bf16_bits_to_float(aw[h] >> 16),
+                                    bf16_bits_to_float(cw[h] >> 16), part);
+                    }
+                }
+            }
+        } else {   // span < 8 (r < 64)
+            const uint16_t* w1 = A.W1 + (size_t)prev * A.r;
+            for (int j = sl * span; j < (sl + 1) * span; ++j)
+                part = fmaf(bf16_bits_to_float(w1[j]),
+                            bf16_bits_to_float(A.W2P[w2p_index(vt, j, A.r)]), part);
+        }
+        ut = bf16_bits_to_float(A.U[outi * (size_t)V + vt]);
+    }
+    part += __shfl_xor(part, 1);
+    part += __shfl_xor(part, 2);
+    part += __shfl_xor(part, 4);
+    const float lt = ut + part;
+    const float wtk = vt < V ? __expf((lt - M) * invT) : 0.0f;
+    const float w8 = __shfl(wtk, (lane & 7) * 8);
+    const float l8 = __shfl(lt, (lane & 7) * 8);
+    double trem;
+    const int tsel = wave_pick(lane < 8 ? (double)w8 : 0.0, grem, trem);
+    const float lsel = __shfl(l8, tsel);
+    if (lane == 0) {
+        A.tokens[outi] = min(seg * kStreamItem + grp * 8 + tsel, V - 1);
+        if (A.q_logZ) A.q_logZ[outi] = (float)((double)M * (double)invT + (double)__logf((float)Z));
+        if (A.q_tok) A.q_tok[outi] = (float)((double)__expf((lsel - M) * invT) / Z);
     }
 }
 
@@ -1355,11 +1641,28 @@ void rnn_gates(const float* __restrict__ hproj, const uint16_t* __restrict__ Wg,
 // ---------------------------------------------------------------------------
 static int pick_wb(int B) { return B <= 32 ? 1 : (B <= 64 ? 2 : 4); }
 
+static int cu_count();
+
+// Contiguous shares per row block of the streaming tile: one workgroup per CU
+// in all, at most 256 shares, none empty.
+int stream_shares(int B, int V) {
+    const int nitem_v = (V + kStreamItem - 1) / kStreamItem;
+    const int nrb = (B + kStreamRows - 1) / kStreamRows;
+    int ws = std::max(1, cu_count() / nrb);
+    ws = std::min(ws, kMaxShares);
+    return std::min(ws, nitem_v);
+}
+
 // The streaming tile serves the q-free Markov draft for bf16 U, V % 8 == 0,
-// more than 64 rows and r in {64, 128, 256}; its segments are 64 tokens.
+// more than 64 rows and r in {64, 128, 256}; its segments are 64 tokens, and
+// its finalize reads at most 64 segments per share.
 bool draft_streams(const DraftArgs& a) {
-    return a.head == kHeadMarkov && a.w_bf16 && !a.q_logits && a.u_bf16 && (a.V % 8) == 0 &&
-           pick_wb(a.B) == 4 && (a.r == 64 || a.r == 128 || a.r == 256);
+    if (!(a.head == kHeadMarkov && a.w_bf16 && !a.q_logits && a.u_bf16 && (a.V % 8) == 0 &&
+          pick_wb(a.B) == 4 && (a.r == 64 || a.r == 128 || a.r == 256)))
+        return false;
+    const int nitem_v = (a.V + kStreamItem - 1) / kStreamItem;
+    const int ws = stream_shares(a.B, a.V);
+    return (nitem_v + ws - 1) / ws <= 64;
 }
 
 int draft_segment_len(const DraftArgs& a) { return draft_streams(a) ? kStreamItem : kTileV; }
@@ -1401,13 +1704,14 @@ static hipError_t launch_stream(const TileParams& p, hipStream_t s) {
     }
     const int nitem_v = (p.V + kStreamItem - 1) / kStreamItem;
     const int nrb = (p.B + kStreamRows - 1) / kStreamRows;
-    const int grid = std::min(nitem_v * nrb, cu_count());
+    const int ws = stream_shares(p.B, p.V);
+    const int grid = nrb * ws;
     if (p.greedy)
         hipLaunchKernelGGL((draft_tile_stream<NK, true>), dim3(grid), dim3(kStreamWaves * 64), lds,
-                           s, p, nitem_v, nrb);
+                           s, p, nitem_v, nrb, ws);
     else
         hipLaunchKernelGGL((draft_tile_stream<NK, false>), dim3(grid), dim3(kStreamWaves * 64), lds,
-                           s, p, nitem_v, nrb);
+                           s, p, nitem_v, nrb, ws);
     return hipGetLastError();
 }
 
@@ -1475,6 +1779,7 @@ static TileParams tile_params(const DraftArgs& a, int k) {
     p.out = a.q_logits;
     p.stats = a.stats;
     p.gsums = a.gsums;
+    p.sup = a.sup;
     p.B = a.B;
     p.gamma = a.gamma;
     p.V = a.V;
@@ -1527,11 +1832,45 @@ hipError_t residual_rows_launch(const TileParams& p, bool u_bf16, hipStream_t s)
 }
 
 hipError_t draft_finalize_launch(const DraftArgs& a, int k, hipStream_t s) {
+    if (draft_streams(a)) {
+        FinStreamArgs f;
+        f.sup = a.sup;
+        f.stats = a.stats;
+        f.gsums = a.gsums;
+        f.ws = stream_shares(a.B, a.V);
+        f.nseg = (a.V + kStreamItem - 1) / kStreamItem;
+        f.bpad = (a.B + kStreamRows - 1) / kStreamRows * kStreamRows;
+        f.x0 = a.x0;
+        f.tokens = a.tokens;
+        f.q_logZ = a.q_logZ;
+        f.q_tok = a.q_tok;
+        f.uniforms = a.uniforms;
+        f.seed = a.seed;
+        f.offset = a.offset;
+        f.gamma = a.gamma;
+        f.V = a.V;
+        f.k = k;
+        f.invT = a.invT;
+        f.greedy = a.greedy;
+        f.U = static_cast<const uint16_t*>(a.U);
+        f.W1 = static_cast<const uint16_t*>(a.W1);
+        f.W2P = a.W2T;
+        f.r = a.r;
+        hipLaunchKernelGGL(draft_finalize_stream, dim3(a.B), dim3(64), 0, s, f);
+        return hipGetLastError();
+    }
     const int nseg = draft_num_segments(a);
     const int seg = draft_segment_len(a);
     RebuildArgs rb;
     rb.gsums = a.gsums;
     rb.gps = seg / 8;
+    if (draft_streams(a)) {   // segment-major summaries [nseg][rows padded to 128]
+        rb.row_stride = 1;
+        rb.seg_stride = (a.B + kStreamRows - 1) / kStreamRows * kStreamRows;
+    } else {                  // row-major [B][nseg]
+        rb.row_stride = nseg;
+        rb.seg_stride = 1;
+    }
     rb.U = a.U;
     rb.u_bf16 = a.u_bf16;
     rb.W1 = (const uint16_t*)a.W1;

@@ -69,6 +69,7 @@ struct DraftArgs {
     const uint16_t* W2T; // bf16 weights: packed W2 image
     uint16_t* W2T_ws;    // workspace for that image when the caller passes none
     float* gsums;        // q-free draft: [B, nseg, 16] 8-token group sums
+    SegStat* sup;        // streaming q-free draft: [shares][rows] range summaries
 };
 
 // Output modes of the bias tile kernel.
@@ -90,6 +91,7 @@ struct TileParams {
     float* out;               // kOutQ: [B, gamma, V]; kOutResidual: [B, V]
     SegStat* stats;           // [B, nseg]
     float* gsums;             // [B, nseg, 16]
+    SegStat* sup;             // streaming tile: per (workgroup share, row) summaries
     int B, gamma, V, r, k;
     float invT;
     int greedy;

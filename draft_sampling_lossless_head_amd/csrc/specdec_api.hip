@@ -36,20 +36,23 @@ constexpr int kMaxV = 1 << 28;
 constexpr int kMaxDraftV = 4096 * 64;    // the finalize holds <= 16 segment summaries per thread
 
 struct DraftLayout {
-    size_t stats, gsums, w2t, hproj, state, erows, total;
+    size_t stats, gsums, sup, w2t, hproj, state, erows, total;
 };
 
 DraftLayout draft_layout(bool rnn, int B, int gamma, int V, int r) {
     DraftLayout L{};
     size_t off = 0;
     const size_t nseg = (size_t)draft_max_segments(V);   // 64-token segments at most
+    const size_t bpad = ((size_t)B + 127) / 128 * 128;     // streamed rows come in blocks of 128
     L.stats = off;
-    off += align_up((size_t)B * nseg * sizeof(SegStat));
+    off += align_up(bpad * nseg * sizeof(SegStat));
     // q-free draft: one sum per 8 tokens, per segment (16 per 128-token
     // segment, 8 per 64-token segment; the 128-token layout can be larger)
     const size_t ngs = std::max((size_t)((V + 127) / 128) * 16, nseg * 8);
     L.gsums = off;
-    off += align_up((size_t)B * ngs * sizeof(float));
+    off += align_up(bpad * ngs * sizeof(float));
+    L.sup = off;   // streaming q-free draft: share summaries [256][bpad]
+    off += align_up((size_t)256 * bpad * sizeof(SegStat));
     L.w2t = off;   // packed bf16 W2 when the caller passes none
     off += align_up(w2p_bytes(r, V));
     if (rnn) {
@@ -237,6 +240,7 @@ spec_status_t spec_draft_sample_markov(const void* U, int U_dtype, const int32_t
     a.q_tok = q_tok_prob;
     a.stats = reinterpret_cast<SegStat*>(w + L.stats);
     a.gsums = reinterpret_cast<float*>(w + L.gsums);
+    a.sup = reinterpret_cast<SegStat*>(w + L.sup);
     a.W2T = static_cast<const uint16_t*>(W2T);
     a.W2T_ws = reinterpret_cast<uint16_t*>(w + L.w2t);
     return run_draft(a, stream);
@@ -304,6 +308,7 @@ spec_status_t spec_draft_sample_rnn(const void* U, int U_dtype, const int32_t* x
     a.state = reinterpret_cast<float*>(w + L.state);
     a.Erows = reinterpret_cast<uint16_t*>(w + L.erows);
     a.gsums = reinterpret_cast<float*>(w + L.gsums);
+    a.sup = reinterpret_cast<SegStat*>(w + L.sup);
     a.W2T = static_cast<const uint16_t*>(W2T);
     a.W2T_ws = reinterpret_cast<uint16_t*>(w + L.w2t);
     return run_draft(a, stream);
