@@ -50,8 +50,10 @@ def kernel_bytes(wl):
     return {
         # U_k read, q_k written, W2 / gamma, the B gathered W1 rows
         "draft_tile": B * V * (lb + 4) + r * V * wb / g + B * r * wb,
-        # U_k read, 16 group sums + one 16-byte summary per (row, tile) written
-        "draft_tile_qfree": B * V * lb + B * nseg * (16 * 4 + 16) + r * V * wb / g + B * r * wb,
+        # U_k read; per (row, 64-token segment) a 16-byte summary and 8 group
+        # sums, per (row, share) one summary (256 shares) written
+        "draft_tile_qfree": B * V * lb + B * ((V + 63) // 64) * (16 + 8 * 4) + B * 256 * 16
+                            + r * V * wb / g + B * r * wb,
         "verify_rows_p": B * (g + 1) * V * lb,
         "verify_rows_q": B * g * V * 4,
     }
@@ -67,7 +69,8 @@ def source_sha(paths):
 
 KERNEL_SOURCES = {
     "draft_tile_qfree": ["draft_sampling_lossless_head_amd/csrc/draft_kernels.hip",
-                         "draft_sampling_lossless_head_amd/csrc/device_common.hpp"],
+                         "draft_sampling_lossless_head_amd/csrc/device_common.hpp",
+                         "draft_sampling_lossless_head_amd/csrc/launch.hpp"],
     "draft_tile": ["draft_sampling_lossless_head_amd/csrc/draft_kernels.hip",
                    "draft_sampling_lossless_head_amd/csrc/device_common.hpp"],
     "verify_rows_p": ["draft_sampling_lossless_head_amd/csrc/verify_kernels.hip",
@@ -88,6 +91,42 @@ def measured_traffic(kernel, workload):
     if t.get("source_sha") != source_sha(KERNEL_SOURCES[kernel]):
         return None
     return t.get("traffic_bytes_per_launch")
+
+
+def traffic_from_pmc(fetch_csv, write_csv, kernel_substr, label, workload, probe_bytes):
+    """HBM bytes per launch of one kernel from two rocprofv3 --pmc runs
+    (FETCH_SIZE, WRITE_SIZE in KiB per dispatch), each scaled so that the
+    largest device copy in the same run (the --copy-probe-mib copy) reads and
+    writes exactly probe_bytes.  Writes profiles/<label>__<workload>.traffic.json
+    tagged with the hash of the kernel's sources."""
+    import csv
+
+    def rows(path, counter):
+        with open(path) as f:
+            return [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
+
+    out = {}
+    for path, counter in ((fetch_csv, "FETCH_SIZE"), (write_csv, "WRITE_SIZE")):
+        rr = rows(path, counter)
+        probe = max(float(r["Counter_Value"]) for r in rr if "copyBuffer" in r["Kernel_Name"])
+        scale = probe_bytes / (probe * 1024.0)
+        vals = [float(r["Counter_Value"]) for r in rr if kernel_substr in r["Kernel_Name"]]
+        if not vals:
+            raise SystemExit(f"no dispatch of {kernel_substr!r} in {path}")
+        out[counter] = dict(kib_per_dispatch=sum(vals) / len(vals), dispatches=len(vals),
+                            probe_kib=probe, scale=scale,
+                            bytes_per_launch=sum(vals) / len(vals) * 1024.0 * scale)
+    rec = dict(kernel=label, kernel_match=kernel_substr, workload=workload,
+               read_bytes_per_launch=out["FETCH_SIZE"]["bytes_per_launch"],
+               write_bytes_per_launch=out["WRITE_SIZE"]["bytes_per_launch"],
+               traffic_bytes_per_launch=out["FETCH_SIZE"]["bytes_per_launch"]
+               + out["WRITE_SIZE"]["bytes_per_launch"],
+               counters=out, probe_bytes=probe_bytes,
+               source_sha=source_sha(KERNEL_SOURCES[label]))
+    path = os.path.join(ROOT, "profiles", f"{label}__{workload}.traffic.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
 
 
 def cpu_baseline(wl, seed, nsample, threads):
@@ -134,13 +173,22 @@ def main():
     ap.add_argument("--path", choices=("qfree", "materialized"), default="qfree",
                     help="q-free cycle (no draft-logit tensor) or materialized draft logits")
     ap.add_argument("--sigma", type=float, default=None, help="override target/draft noise")
-    ap.add_argument("--cpu-sample", type=int, default=16, help="requests timed on the oracle")
+    ap.add_argument("--cpu-sample", type=int, default=64, help="requests timed on the oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true",
                     help="only the timed region (no per-kernel timing passes, no CPU baseline)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device copy of this size (counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU run: turn two rocprofv3 --pmc counter CSVs into the traffic "
+                         "record of --traffic-kernel")
+    ap.add_argument("--traffic-kernel", default="draft_tile_stream<8, false>")
+    ap.add_argument("--traffic-label", default="draft_tile_qfree")
     args = ap.parse_args()
+    if args.traffic_from:
+        traffic_from_pmc(args.traffic_from[0], args.traffic_from[1], args.traffic_kernel,
+                         args.traffic_label, args.workload, (args.copy_probe_mib or 1024) << 20)
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): the method's requests are "
