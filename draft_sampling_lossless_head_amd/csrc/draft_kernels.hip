@@ -604,34 +604,34 @@ void draft_tile_stats(TileParams P) {
 // ---------------------------------------------------------------------------
 // Streaming q-free bias tile: one persistent workgroup per CU.
 //
-// Work item = (64-token slice, block of 128 request rows); the workgroup takes
-// items blockIdx.x, blockIdx.x + gridDim.x, ...  Every item's two inputs are
-// copied into an LDS stage by direct global->LDS loads: the packed W2 slice
-// (64 rows of r bf16, contiguous in the packed image) and the U slice (128 rows
-// x 64 bf16, 16-byte chunk c of row bl stored in slot bl*8 + (c ^ ((bl>>1)&7))).
-// Three stages: item i+2 streams in while item i is contracted and reduced.
+// Work item = (64-token slice, block of 128 request rows).  Workgroup g takes
+// row block g / ws and the j-th contiguous share of that block's slices
+// (j = g % ws).  Every item's two inputs are copied into an LDS stage by direct
+// global->LDS loads: the packed W2 slice (64 rows of r bf16, contiguous in the
+// packed image) and the U slice (128 rows x 64 bf16, 16-byte chunk c of row bl
+// stored in slot bl*8 + (c ^ ((bl>>1)&7))).  Three stages: item i+2 streams in
+// while item i is contracted and item i-1 reduced.
 //
-// Eight waves, two per SIMD, so that one wave's MFMAs overlap the other's
-// vector work and load issue.  Wave w owns rows 16w .. 16w + 15 and all 64
-// tokens of an item, on 16x16x32 MFMAs: A = W2 slice (tokens x rank), B = E =
-// W1[x_{k-1}] rows (kept in registers for all items of a row block).  Block
-// m's MFMA row i = 4a + c is token 16a + 4m + c, so lane (row, a = lane/16)
-// ends with tokens 16a .. 16a + 15 of its row.  A 64-token slice is one
-// segment: per (row, segment) the SegStat and 8 group sums, reduced over the
-// four lanes of the row.
+// Eight waves, two per SIMD.  Wave w owns rows 32 (w & 3) .. + 31 and tokens
+// 32 (w >> 2) .. + 31 of each item, on 32x32x16 MFMAs: A = W2 slice (tokens x
+// rank) from LDS, B = E = W1[x_{k-1}] rows in registers.  MFMA row i = 8g + 4h
+// + c is token 16h + p(g, c) of the wave's 32, p(g, c) = 8 (g & 1) + 4 (g >> 1)
+// + c, so lane (row, h = lane / 32) ends with tokens 16h .. 16h + 15 of its row
+// and the 16-byte operand reads stay conflict-free under the packed swizzle.
+// A segment is the wave's 32 tokens of one row: its max and four 8-token group
+// sums relative to it; a running merge gives one summary per (row, share).
 //
 // Only the bf16-U, V % 8 == 0 shape is streamed this way (chunks never straddle
 // V); waits on the direct loads use explicit vmcnt counts and a bare s_barrier,
 // since a fenced barrier would drain the prefetches as well.
 // ---------------------------------------------------------------------------
-constexpr int kStreamItem = 64;     // tokens per item / segment
+constexpr int kStreamItem = 64;     // tokens per item
+constexpr int kStreamSeg = 32;      // tokens per segment (one wave's half of an item)
 constexpr int kStreamRows = 128;    // request rows per item
 constexpr int kStreamStages = 3;
 constexpr int kStreamWaves = 8;
-constexpr int kMaxShares = 256;    // share summaries per row (one per finalize thread)
+constexpr int kMaxShares = 256;     // share summaries per row (four per finalize lane)
 constexpr int kCpolNT = 2;          // cache-policy bit "nt": streamed once, do not keep
-
-typedef float f32x4v_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ void wait_vmcnt_le(int n) {
     // s_waitcnt with expcnt and lgkmcnt at their "no wait" maxima; n <= 63
@@ -644,10 +644,10 @@ __device__ __forceinline__ void wait_vmcnt_le(int n) {
     }
 }
 
-template <int NK, bool GREEDY>   // NK = r / 32 rank steps of the 16x16x32 MFMA
+template <int NKS, bool GREEDY>   // NKS = r / 16 rank steps of the 32x32x16 MFMA
 __global__ __launch_bounds__(kStreamWaves * 64, 1)
 void draft_tile_stream(TileParams P, int nitem_v, int nrb, int ws) {
-    constexpr int R = NK * 32;
+    constexpr int R = NKS * 16;
     constexpr int W2B = kStreamItem * R * 2;             // packed W2 slice bytes
     constexpr int UB = kStreamRows * kStreamItem * 2;    // U slice bytes
     constexpr int STAGE = W2B + UB;
@@ -661,17 +661,16 @@ void draft_tile_stream(TileParams P, int nitem_v, int nrb, int ws) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar LDS addresses
-    const int a4 = lane >> 4;        // MFMA lane group: K chunk of the operands, token run of C
-    // Workgroup g takes row block g / ws and the j-th contiguous share [lo, hi)
-    // of that block's slices (j = g % ws; ws <= nitem_v, so every share is
-    // non-empty).  Contiguous shares let the workgroup also summarise its
-    // whole token range per row.
+    const int h = lane >> 5;
+    const int rg = wave & 3;         // row group: rows 32 rg .. + 31 of the row block
+    const int th = wave >> 2;        // token half: tokens 32 th .. + 31 of an item
     const int rb0 = (int)blockIdx.x / ws;
     const int jw = (int)blockIdx.x % ws;
     const int lo = (int)((long long)jw * nitem_v / ws);
     const int hi = (int)((long long)(jw + 1) * nitem_v / ws);
-    const int my_n = hi - lo;
+    const int my_n = hi - lo;        // >= 1: ws <= nitem_v
     const uint16_t* Ub = static_cast<const uint16_t*>(P.U);
+    const size_t bpad = (size_t)nrb * kStreamRows;
 
     // This lane's U pieces: row bl and 16-byte chunk c of every item's slice,
     // as offsets from the row block's first row.
@@ -689,7 +688,7 @@ void draft_tile_stream(TileParams P, int nitem_v, int nrb, int ws) {
     const size_t rb_stride = (size_t)kStreamRows * gamma * (size_t)V;
 
     auto issue = [&](int i) {
-        const int rb = rb0, iv = lo + i;
+        const int iv = lo + i;
         char* st = smem_s + (i % kStreamStages) * STAGE;
         const char* wsrc = reinterpret_cast<const char*>(P.W2T) + (size_t)iv * W2B;
 #pragma unroll
@@ -698,82 +697,84 @@ void draft_tile_stream(TileParams P, int nitem_v, int nrb, int ws) {
             __builtin_amdgcn_global_load_lds(wsrc + pc * 1024 + lane * 16,
                                              (lds_ptr_t)(st + pc * 1024), 16, 0, 0);
         }
-        const size_t item_off = (size_t)rb * rb_stride + (size_t)iv * kStreamItem;
+        const size_t item_off = (size_t)rb0 * rb_stride + (size_t)iv * kStreamItem;
 #pragma unroll
         for (int q = 0; q < UP; ++q) {
             const int pc = q * kStreamWaves + wave;
-            const bool ok = rb * kStreamRows + ubl[q] < B && iv * kStreamItem + uc8[q] < V;
+            const bool ok = rb0 * kStreamRows + ubl[q] < B && iv * kStreamItem + uc8[q] < V;
             const size_t off = ok ? ubase[q] + item_off : (size_t)k * (size_t)V;   // any valid chunk
             __builtin_amdgcn_global_load_lds(Ub + off, (lds_ptr_t)(st + W2B + pc * 1024), 16, 0,
                                              kCpolNT);
         }
     };
 
-    // Conditioning rows E = W1[x_{k-1}] of the row block (MFMA B operand).
-    bf16x8_t e[NK];
+    // Conditioning rows E = W1[x_{k-1}] of this lane's row (MFMA B operand).
+    const int bl = 32 * rg + (lane & 31);
+    const int b = rb0 * kStreamRows + bl;
     bool erow_ok = false;
-    int b = 0;
-    auto load_e = [&](int rb) {
-        b = rb * kStreamRows + wave * 16 + (lane & 15);
+    bf16x8_t e[NKS];
+    {
         int prev = 0;
-        erow_ok = false;
         if (b < B) {
             prev = (k == 0) ? P.x0[b] : P.tokens[(size_t)b * gamma + k - 1];
             erow_ok = prev >= 0 && prev < V;
         }
         const uint16_t* erow = P.W1 + (size_t)(erow_ok ? prev : 0) * R;
 #pragma unroll
-        for (int ks = 0; ks < NK; ++ks) {
+        for (int ks = 0; ks < NKS; ++ks) {
             if (erow_ok) {
-                e[ks] = *reinterpret_cast<const bf16x8_t*>(erow + ks * 32 + a4 * 8);
+                e[ks] = *reinterpret_cast<const bf16x8_t*>(erow + ks * 16 + h * 8);
             } else {
 #pragma unroll
                 for (int t = 0; t < 8; ++t) e[ks][t] = (__bf16)0.0f;
             }
         }
-    };
+    }
     // E must be complete before any direct load is in flight: the compiler
     // treats plain and direct loads pending together as unordered and would
     // otherwise drain every prefetch before each contraction.
-    load_e(rb0);
     wait_vmcnt_le(0);
     issue(0);
     if (my_n > 1) issue(1);
 
-    // A-operand row of this lane in block m: token 16 * (i / 4) + 4m + i % 4, i = lane % 16
-    int arow[4], atok[4];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-        const int i = lane & 15;
-        atok[mb] = 16 * (i >> 2) + 4 * mb + (i & 3);
-        arow[mb] = atok[mb] * R;
+    // A-operand row of this lane: MFMA row i = lane % 32 = 8g + 4h' + c.
+    int atok, arow;
+    {
+        const int i = lane & 31;
+        const int g = i >> 3, hh = (i >> 2) & 1, c = i & 3;
+        atok = 32 * th + 16 * hh + 8 * (g & 1) + 4 * (g >> 1) + c;
+        arow = atok * R;
     }
-    const int bl = wave * 16 + (lane & 15);
-    const int uslot0 = bl * 8;
-    const int uswz = (bl >> 1) & 7;
+    // U chunks of the lane's 16 tokens (chunks 4 th + 2 h and + 1 of row bl)
+    int uslot[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) uslot[q] = bl * 8 + ((4 * th + 2 * h + q) ^ ((bl >> 1) & 7));
     const float sc = P.invT * 1.4426950408889634f;   // exp(y / T) = 2^(y * sc)
 
-    // Reduction of one finished item (its accumulators and U chunks) to the
-    // summaries of (row, segment iv).  Branch-free, and run one iteration
-    // behind the contraction so that the scheduler can interleave the vector
-    // work of item i-1 with the MFMAs of item i.
+    // Reduction of one finished item for this lane's row: the segment max and
+    // the sums of this lane's two 8-token groups relative to it.
     struct Red {
-        float m, tot, gs0, gs1;
+        float m, g0, g1;
         int am;
     };
-    auto reduce = [&](const f32x4v_t (&ac)[4], const u32x4_t (&uf)[2], int iv) -> Red {
-        const int v0 = iv * kStreamItem + 16 * a4;
+    auto reduce = [&](const f32x16_t& ac, const u32x4_t (&uf)[2], int iv) -> Red {
+        // accumulator idx = 4g + c holds run position 8 (g & 1) + 4 (g >> 1) + c
         float x[16];
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
+        for (int g = 0; g < 4; ++g)
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int j = 8 * q + 2 * t;   // run position of the pair
-                x[j] = ac[j >> 2][j & 3] + __uint_as_float(uf[q][t] << 16);
-                x[j + 1] = ac[(j + 1) >> 2][(j + 1) & 3] + __uint_as_float(uf[q][t] & 0xFFFF0000u);
+            for (int c = 0; c < 4; ++c) {
+                const int pos = 8 * (g & 1) + 4 * (g >> 1) + c;
+                const uint32_t w = uf[pos >> 3][(pos & 7) >> 1];
+                const float uv = (pos & 1) ? __uint_as_float(w & 0xFFFF0000u)
+                                           : __uint_as_float(w << 16);
+                x[pos] = ac[4 * g + c] + uv;
             }
+        const int v0 = iv * kStreamItem + 32 * th + 16 * h;
+        if (iv * kStreamItem + kStreamItem > V) {   // the last slice: tokens past V
 #pragma unroll
-        for (int t = 0; t < 16; ++t) x[t] = v0 + t < V ? x[t] : -INFINITY;
+            for (int t = 0; t < 16; ++t) x[t] = v0 + t < V ? x[t] : -INFINITY;
+        }
         Red o;
         float m = x[0];
 #pragma unroll
@@ -783,17 +784,13 @@ void draft_tile_stream(TileParams P, int nitem_v, int nrb, int ws) {
             int am = INT_MAX;
 #pragma unroll
             for (int t = 15; t >= 0; --t) am = x[t] == m ? v0 + t : am;
-#pragma unroll
-            for (int off = 16; off <= 32; off <<= 1) {
-                const float m2 = __shfl_xor(m, off);
-                const int a2 = __shfl_xor(am, off);
-                am = (m2 > m || (m2 == m && a2 < am)) ? a2 : am;
-                m = fmaxf(m, m2);
-            }
+            const float m2 = __shfl_xor(m, 32);
+            const int a2 = __shfl_xor(am, 32);
+            am = (m2 > m || (m2 == m && a2 < am)) ? a2 : am;
+            m = fmaxf(m, m2);
             o.am = am;
-            o.gs0 = o.gs1 = o.tot = 0.0f;
+            o.g0 = o.g1 = 0.0f;
         } else {
-            m = fmaxf(m, __shfl_xor(m, 16));
             m = fmaxf(m, __shfl_xor(m, 32));
             const float ms = m == -INFINITY ? 0.0f : m * sc;   // all -inf: every weight 0
             float g0 = 0.0f, g1 = 0.0f;
@@ -802,47 +799,22 @@ void draft_tile_stream(TileParams P, int nitem_v, int nrb, int ws) {
                 g0 += __builtin_amdgcn_exp2f(fmaf(x[t], sc, -ms));
                 g1 += __builtin_amdgcn_exp2f(fmaf(x[8 + t], sc, -ms));
             }
-            float tot = g0 + g1;
-            tot += __shfl_xor(tot, 16);
-            tot += __shfl_xor(tot, 32);
-            o.gs0 = g0;
-            o.gs1 = g1;
-            o.tot = tot;
+            o.g0 = g0;
+            o.g1 = g1;
         }
         o.m = m;
         return o;
     };
-    // Summaries are segment-major, [segment][row] with rows padded to whole
-    // row blocks, so one wave's stores for an item are one contiguous run.
-    const size_t bpad = (size_t)nrb * kStreamRows;
-    auto store = [&](const Red& o, int iv, int bw) {
-        const size_t si = (size_t)iv * bpad + bw;
+    // Segment-major outputs: the max [seg][bpad] and the four group sums
+    // [seg][bpad][4]; one wave's stores for an item are contiguous runs.
+    auto store = [&](const Red& o, int iv) {
+        const size_t si = (2 * (size_t)iv + th) * bpad + b;
         if constexpr (!GREEDY)
-            *reinterpret_cast<float2*>(P.gsums + si * 8 + 2 * a4) = make_float2(o.gs0, o.gs1);
-        if (a4 == 0) {
-            SegStat sst;
-            sst.m = o.m;
-            sst.s = o.tot;
-            sst.idx = o.am;
-            sst.pad = 0;
-            P.stats[si] = sst;
-        }
+            *reinterpret_cast<float2*>(P.gsums + si * 4 + 2 * h) = make_float2(o.g0, o.g1);
+        if (h == 0) P.segm[si] = o.m;
     };
 
-    f32x4v_t accp[4];
-    u32x4_t ufrp[2];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) accp[mb] = f32x4v_t{0.0f, 0.0f, 0.0f, 0.0f};
-    ufrp[0] = ufrp[1] = u32x4_t{0u, 0u, 0u, 0u};
-    int ivp = 0, bp = 0;
-    bool okp = false;   // nothing to reduce before the first item
-    // Item i-2's summaries are stored at the top of iteration i, before the
-    // prefetch: stores count in vmcnt too, and only loads may be newer than
-    // the item a wait is for (stores and loads may retire out of order).
-    Red redh{};
-    int ivh = 0, bh = 0;
-    bool okh = false;
-    // Running summary of the workgroup's whole range for this lane's row.
+    // Running summary of this wave's half of the share for the lane's row.
     float run_m = -INFINITY, run_s = 0.0f;
     int run_a = INT_MAX;
     auto absorb_run = [&](const Red& o) {
@@ -850,92 +822,117 @@ void draft_tile_stream(TileParams P, int nitem_v, int nrb, int ws) {
             run_a = (o.m > run_m || (o.m == run_m && o.am < run_a)) ? o.am : run_a;
             run_m = fmaxf(run_m, o.m);
         } else {
+            float tot = o.g0 + o.g1;
+            tot += __shfl_xor(tot, 32);
             const float nm = fmaxf(run_m, o.m);
             const float a = run_m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((run_m - nm) * sc);
             const float c = o.m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((o.m - nm) * sc);
-            run_s = run_s * a + o.tot * c;
+            run_s = run_s * a + tot * c;
             run_m = nm;
         }
     };
+
+    f32x16_t accp;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) accp[t] = 0.0f;
+    u32x4_t ufrp[2] = {u32x4_t{0u, 0u, 0u, 0u}, u32x4_t{0u, 0u, 0u, 0u}};
+    int ivp = 0;
+    bool have_p = false;   // an item waiting to be reduced
+    // Item i-2's outputs are stored at the top of iteration i, before the
+    // prefetch: stores count in vmcnt too, and only loads may be newer than
+    // the item a wait is for (stores and loads may retire out of order).
+    Red redh{};
+    int ivh = 0;
+    bool have_h = false;
+    const bool reduce_first = th != 0;   // the two waves of a SIMD alternate phases
     for (int i = 0; i < my_n; ++i) {
         const int iv = lo + i;
         wait_vmcnt_le(i + 1 < my_n ? LOADS : 0);   // item i's direct loads (this wave)
         asm volatile("s_barrier" ::: "memory");    // ... and every wave's; stage (i-1)%3 is free
-        if (okh) store(redh, ivh, bh);
+        if (have_h && erow_ok) store(redh, ivh);
         if (i + 2 < my_n) issue(i + 2);
 
-        // The two waves of a SIMD (w and w + 4) take the phases in opposite
-        // order: one contracts item i while the other reduces item i-1, so the
-        // matrix core and the vector ALU are busy at the same time.
-        const bool reduce_first = (wave & 4) != 0;
         Red red;
         if (reduce_first) red = reduce(accp, ufrp, ivp);
 
         const char* st = smem_s + (i % kStreamStages) * STAGE;
         const uint16_t* w2s = reinterpret_cast<const uint16_t*>(st);
-        const int half = (iv & 1) * 64;
-        int sw[4];
+        const int sw = w2p_swizzle((iv & 1) * 64 + atok, NCH);
+        bf16x8_t afr[NKS];
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) sw[mb] = w2p_swizzle(half + atok[mb], NCH);
-        bf16x8_t afr[NK][4];
-#pragma unroll
-        for (int ks = 0; ks < NK; ++ks) {
-            const int kc = 4 * ks + a4;
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
-                afr[ks][mb] = *reinterpret_cast<const bf16x8_t*>(w2s + arow[mb] + ((kc ^ sw[mb]) << 3));
-        }
-        const uint32_t* us = reinterpret_cast<const uint32_t*>(st + W2B);
+        for (int ks = 0; ks < NKS; ++ks)
+            afr[ks] = *reinterpret_cast<const bf16x8_t*>(w2s + arow + (((2 * ks + h) ^ sw) << 3));
+        const u32x4_t* us = reinterpret_cast<const u32x4_t*>(st + W2B);
         u32x4_t ufr[2];
+        ufr[0] = us[uslot[0]];
+        ufr[1] = us[uslot[1]];
+        f32x16_t acc;
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
-            ufr[q] = *reinterpret_cast<const u32x4_t*>(us + (uslot0 + ((2 * a4 + q) ^ uswz)) * 4);
-        f32x4v_t acc[4];
+        for (int t = 0; t < 16; ++t) acc[t] = 0.0f;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x4v_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int ks = 0; ks < NK; ++ks)
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
-                acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[ks][mb], e[ks], acc[mb], 0, 0, 0);
+        for (int ks = 0; ks < NKS; ++ks)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[ks], e[ks], acc, 0, 0, 0);
         {   // schedule: LDS reads ahead, then one MFMA per further read
-            constexpr int NR = 4 * NK + 2;
-            constexpr int kAhead = NR < 10 ? NR : 10;
+            constexpr int NR = NKS + 2;
+            constexpr int kAhead = NR < 8 ? NR : 8;
             __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
 #pragma unroll
             for (int j = 0; j < NR - kAhead; ++j) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, 4 * NK - (NR - kAhead), 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, NKS - (NR - kAhead), 0);
         }
         if (!reduce_first) red = reduce(accp, ufrp, ivp);
-        if (okp) absorb_run(red);
+
+        if (have_p) absorb_run(red);
         redh = red;
         ivh = ivp;
-        bh = bp;
-        okh = okp;
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) accp[mb] = acc[mb];
+        have_h = have_p;
+        accp = acc;
         ufrp[0] = ufr[0];
         ufrp[1] = ufr[1];
         ivp = iv;
-        bp = b;
-        okp = b < B && erow_ok;
+        have_p = true;
     }
-    if (okh) store(redh, ivh, bh);
+    if (have_h && erow_ok) store(redh, ivh);
     const Red red = reduce(accp, ufrp, ivp);
-    if (okp) {
-        store(red, ivp, bp);
-        absorb_run(red);
-        if (a4 == 0) {   // the workgroup's summary of row b over segments [lo, hi)
-            SegStat sst;
-            sst.m = run_m;
-            sst.s = GREEDY ? 0.0f : run_s;
-            sst.idx = GREEDY ? run_a : 0;
-            sst.pad = 0;
-            P.sup[(size_t)jw * bpad + bp] = sst;
+    if (erow_ok) store(red, ivp);
+    absorb_run(red);
+
+    // Share summaries: the token-half-1 waves hand their running summary to
+    // the half-0 waves of the same rows, which merge and store them.
+    float* xm = reinterpret_cast<float*>(smem_s);   // the stages are idle now
+    float* xs = xm + kStreamRows;
+    int* xa = reinterpret_cast<int*>(xs + kStreamRows);
+    __syncthreads();
+    if (th == 1 && h == 0) {
+        xm[bl] = run_m;
+        xs[bl] = run_s;
+        xa[bl] = run_a;
+    }
+    __syncthreads();
+    if (th == 0 && h == 0 && erow_ok) {
+        const float m2 = xm[bl], s2 = xs[bl];
+        const int a2 = xa[bl];
+        SegStat sst;
+        if constexpr (GREEDY) {
+            float m = run_m;
+            int am = run_a;
+            merge_arg(m, am, m2, a2);
+            sst.m = m;
+            sst.s = 0.0f;
+            sst.idx = am;
+        } else {
+            const float nm = fmaxf(run_m, m2);
+            const float a = run_m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((run_m - nm) * sc);
+            const float c = m2 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((m2 - nm) * sc);
+            sst.m = nm;
+            sst.s = run_s * a + s2 * c;
+            sst.idx = 0;
         }
+        sst.pad = 0;
+        P.sup[(size_t)jw * bpad + b] = sst;
     }
 }
 
@@ -1291,7 +1288,7 @@ void draft_finalize(const SegStat* __restrict__ stats, int nseg, int seg_len,
 // workgroup barriers); the inverse-CDF descent takes three dependent reads:
 //   1. the row's ws <= 256 share summaries, four per lane: max, normaliser and
 //      the share holding u * Z (fp64 weights and scan);
-//   2. the share's segment summaries and their 8 group sums, read together:
+//   2. the share's 32-token segments (max and 4 group sums), read together:
 //      the segment, then the 8-token group;
 //   3. the group's 8 logits rebuilt as U + W1[prev] . W2 (the W1 row slice is
 //      fetched at entry), then the token.
@@ -1299,10 +1296,10 @@ void draft_finalize(const SegStat* __restrict__ stats, int nseg, int seg_len,
 // and the threshold are fp64.
 // ---------------------------------------------------------------------------
 struct FinStreamArgs {
-    const SegStat* sup;     // [ws][bpad]
-    const SegStat* stats;   // [nseg][bpad]
-    const float* gsums;     // [nseg][bpad][8]
-    int ws, nseg, bpad;
+    const SegStat* sup;     // [ws][bpad] share summaries
+    const float* segm;      // [2 nitem][bpad] max of each 32-token segment
+    const float* gsums;     // [2 nitem][bpad][4] 8-token group sums relative to it
+    int ws, nitem, bpad;
     const int32_t* x0;
     int32_t* tokens;
     float* q_logZ;
@@ -1442,40 +1439,38 @@ void draft_finalize_stream(FinStreamArgs A) {
     const int sh = 4 * ol + __shfl(qsel, ol);
     const double rem1 = __shfl(qrem, ol);
 
-    // 2) the share's segments and their group sums, one read.
-    const int s0 = (int)((long long)sh * A.nseg / A.ws);
-    const int s1 = (int)((long long)(sh + 1) * A.nseg / A.ws);
+    // 2) the share's 32-token segments and their group sums, one read.
+    const int s0 = 2 * (int)((long long)sh * A.nitem / A.ws);
+    const int s1 = 2 * (int)((long long)(sh + 1) * A.nitem / A.ws);
     const int sg = s0 + lane;
     const bool have = sg < s1;   // at most 64 segments per share (launcher guarantee)
-    float ym = -INFINITY, ys = 0.0f;
-    float4 g0 = make_float4(0.f, 0.f, 0.f, 0.f), g1 = g0;
+    float ym = -INFINITY;
+    float4 g4 = make_float4(0.f, 0.f, 0.f, 0.f);
     if (have) {
         const size_t sx = (size_t)sg * A.bpad + b;
-        const SegStat y = A.stats[sx];
-        ym = y.m;
-        ys = y.s;
-        g0 = *reinterpret_cast<const float4*>(A.gsums + sx * 8);
-        g1 = *reinterpret_cast<const float4*>(A.gsums + sx * 8 + 4);
+        ym = A.segm[sx];
+        g4 = *reinterpret_cast<const float4*>(A.gsums + sx * 4);
     }
     const double ysc = ym != -INFINITY ? (double)__expf((ym - M) * invT) : 0.0;
+    const double ys = ((double)g4.x + (double)g4.y) + ((double)g4.z + (double)g4.w);
     double rem2;
-    const int sl_seg = wave_pick((double)ys * ysc, rem1, rem2);
+    const int sl_seg = wave_pick(ys * ysc, rem1, rem2);
     const int seg = s0 + sl_seg;
-    // the chosen segment's 8 group weights to lanes 0..7
+    // the chosen segment's 4 group weights to lanes 0..3
     const double gscale = __shfl(ysc, sl_seg);
-    const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    const float gv[4] = {g4.x, g4.y, g4.z, g4.w};
     float mine = 0.0f;
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
+    for (int g = 0; g < 4; ++g) {
         const float v = __shfl(gv[g], sl_seg);
         if (lane == g) mine = v;
     }
     double grem;
-    const int grp = wave_pick(lane < 8 ? (double)mine * gscale : 0.0, rem2, grem);
+    const int grp = wave_pick(lane < 4 ? (double)mine * gscale : 0.0, rem2, grem);
 
     // 3) rebuild the group's 8 logits: lane = 8t + sl.
     const int t = lane >> 3, sl = lane & 7;
-    const int vt = seg * kStreamItem + grp * 8 + t;
+    const int vt = seg * kStreamSeg + grp * 8 + t;
     float part = 0.0f;
     float ut = 0.0f;
     if (vt < V) {
@@ -1517,7 +1512,7 @@ void draft_finalize_stream(FinStreamArgs A) {
     const int tsel = wave_pick(lane < 8 ? (double)w8 : 0.0, grem, trem);
     const float lsel = __shfl(l8, tsel);
     if (lane == 0) {
-        A.tokens[outi] = min(seg * kStreamItem + grp * 8 + tsel, V - 1);
+        A.tokens[outi] = min(seg * kStreamSeg + grp * 8 + tsel, V - 1);
         if (A.q_logZ) A.q_logZ[outi] = (float)((double)M * (double)invT + (double)__logf((float)Z));
         if (A.q_tok) A.q_tok[outi] = (float)((double)__expf((lsel - M) * invT) / Z);
     }
@@ -1662,7 +1657,7 @@ bool draft_streams(const DraftArgs& a) {
         return false;
     const int nitem_v = (a.V + kStreamItem - 1) / kStreamItem;
     const int ws = stream_shares(a.B, a.V);
-    return (nitem_v + ws - 1) / ws <= 64;
+    return 2 * ((nitem_v + ws - 1) / ws) <= 64;   // 32-token segments per share
 }
 
 int draft_segment_len(const DraftArgs& a) { return draft_streams(a) ? kStreamItem : kTileV; }
@@ -1689,15 +1684,15 @@ static int cu_count() {
     return n[dev];
 }
 
-template <int NK>
+template <int NKS>
 static hipError_t launch_stream(const TileParams& p, hipStream_t s) {
-    constexpr int STAGE = kStreamItem * NK * 32 * 2 + kStreamRows * kStreamItem * 2;
+    constexpr int STAGE = kStreamItem * NKS * 16 * 2 + kStreamRows * kStreamItem * 2;
     const size_t lds = (size_t)kStreamStages * STAGE;
     static bool attr_set = false;
     if (!attr_set) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&draft_tile_stream<NK, false>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&draft_tile_stream<NKS, false>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&draft_tile_stream<NK, true>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&draft_tile_stream<NKS, true>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         (void)hipGetLastError();
         attr_set = true;
@@ -1707,10 +1702,10 @@ static hipError_t launch_stream(const TileParams& p, hipStream_t s) {
     const int ws = stream_shares(p.B, p.V);
     const int grid = nrb * ws;
     if (p.greedy)
-        hipLaunchKernelGGL((draft_tile_stream<NK, true>), dim3(grid), dim3(kStreamWaves * 64), lds,
+        hipLaunchKernelGGL((draft_tile_stream<NKS, true>), dim3(grid), dim3(kStreamWaves * 64), lds,
                            s, p, nitem_v, nrb, ws);
     else
-        hipLaunchKernelGGL((draft_tile_stream<NK, false>), dim3(grid), dim3(kStreamWaves * 64), lds,
+        hipLaunchKernelGGL((draft_tile_stream<NKS, false>), dim3(grid), dim3(kStreamWaves * 64), lds,
                            s, p, nitem_v, nrb, ws);
     return hipGetLastError();
 }
@@ -1780,6 +1775,7 @@ static TileParams tile_params(const DraftArgs& a, int k) {
     p.stats = a.stats;
     p.gsums = a.gsums;
     p.sup = a.sup;
+    p.segm = reinterpret_cast<float*>(a.stats);   // the streaming tile's per-segment maxima
     p.B = a.B;
     p.gamma = a.gamma;
     p.V = a.V;
@@ -1815,9 +1811,9 @@ hipError_t draft_tile_launch(const DraftArgs& a, int k, hipStream_t s) {
     if (a.head == kHeadMarkov) {
         if (a.q_logits) return launch_tile_b<kHeadMarkov, kOutQ>(p, a.u_bf16, s);
         if (draft_streams(a)) {
-            if (a.r == 256) return launch_stream<8>(p, s);
-            if (a.r == 128) return launch_stream<4>(p, s);
-            return launch_stream<2>(p, s);
+            if (a.r == 256) return launch_stream<16>(p, s);
+            if (a.r == 128) return launch_stream<8>(p, s);
+            return launch_stream<4>(p, s);
         }
         const int wb = pick_wb(a.B);
         if (wb == 1) return launch_stats<1>(p, a.u_bf16, s);
@@ -1835,10 +1831,10 @@ hipError_t draft_finalize_launch(const DraftArgs& a, int k, hipStream_t s) {
     if (draft_streams(a)) {
         FinStreamArgs f;
         f.sup = a.sup;
-        f.stats = a.stats;
+        f.segm = reinterpret_cast<const float*>(a.stats);
         f.gsums = a.gsums;
         f.ws = stream_shares(a.B, a.V);
-        f.nseg = (a.V + kStreamItem - 1) / kStreamItem;
+        f.nitem = (a.V + kStreamItem - 1) / kStreamItem;
         f.bpad = (a.B + kStreamRows - 1) / kStreamRows * kStreamRows;
         f.x0 = a.x0;
         f.tokens = a.tokens;

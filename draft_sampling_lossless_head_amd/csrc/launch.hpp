@@ -92,6 +92,7 @@ struct TileParams {
     SegStat* stats;           // [B, nseg]
     float* gsums;             // [B, nseg, 16]
     SegStat* sup;             // streaming tile: per (workgroup share, row) summaries
+    float* segm;              // streaming tile: per (32-token segment, row) max
     int B, gamma, V, r, k;
     float invT;
     int greedy;
