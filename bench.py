@@ -288,7 +288,7 @@ def main():
     sd.spec_profile_enable(None)
     kernels = {}
     names = ["w2_pack", "draft_tile", "draft_tile_qfree", "draft_finalize", "verify_rows_p",
-             "verify_rows_q", "verify_decide", "verify_residual_rows", "verify_final_partials",
+             "verify_rows_q", "verify_decide", "verify_residual_rows", "verify_resid", "verify_final_partials",
              "verify_final_draw"]
     for name in names:
         sd.spec_profile_enable(name)

@@ -10,6 +10,7 @@ constexpr int kWave = 64;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // Per-(row, segment) summary written by the streaming passes: max logit m,
 // sum of exp((l - m) / T) over the segment, and the argmax (lowest id on ties).
@@ -154,6 +155,41 @@ __device__ __forceinline__ int row16_min(int x) {
     x = min(x, dpp_mov<kDppXor2>(x));
     x = min(x, dpp_mov<kDppHalfMirror>(x));
     return min(x, dpp_mov<kDppMirror>(x));
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Wait until at most n vector-memory operations of this wave are outstanding
+// (expcnt and lgkmcnt left at their "no wait" maxima).  Direct global->LDS
+// loads count here too; loads complete in issue order.
+__device__ __forceinline__ void wait_vmcnt_le(int n) {
+    // s_waitcnt with expcnt and lgkmcnt at their "no wait" maxima; n <= 63
+    switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;   // waiting for all is always safe
+    }
+}
+
+// Inverse CDF over one weight per lane (lanes in token order): the lane whose
+// interval [excl, incl) holds thr and thr - excl; past the end (rounding) the
+// last lane with weight and +inf.  Neighbouring intervals share end points.
+__device__ __forceinline__ int wave_pick(double w, double thr, double& rem) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const double incl = wave_inclusive_scan_f64(w);
+    double excl = __shfl_up(incl, 1);
+    if (lane == 0) excl = 0.0;
+    unsigned long long hit = __ballot(w > 0.0 && thr >= excl && thr < incl);
+    if (hit) {
+        const int l = __ffsll((long long)hit) - 1;
+        rem = thr - __shfl(excl, l);
+        return l;
+    }
+    const unsigned long long pos = __ballot(w > 0.0);
+    rem = INFINITY;
+    return pos ? 63 - __clzll((long long)pos) : 0;
 }
 
 }  // namespace specdec

@@ -385,7 +385,6 @@ void draft_tile_mfma(TileParams P) {
 // Outputs per (row, tile): the SegStat (max, sum exp((l - max)/T), argmax) and
 // the 16 sums over 8-token groups relative to the same max.
 // ---------------------------------------------------------------------------
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 template <int WB, bool U_BF16>
 __global__ __launch_bounds__(256, 2)
@@ -625,24 +624,8 @@ void draft_tile_stats(TileParams P) {
 // V); waits on the direct loads use explicit vmcnt counts and a bare s_barrier,
 // since a fenced barrier would drain the prefetches as well.
 // ---------------------------------------------------------------------------
-constexpr int kStreamItem = 64;     // tokens per item
-constexpr int kStreamSeg = 32;      // tokens per segment (one wave's half of an item)
-constexpr int kStreamRows = 128;    // request rows per item
 constexpr int kStreamStages = 3;
-constexpr int kStreamWaves = 8;
-constexpr int kMaxShares = 256;     // share summaries per row (four per finalize lane)
-constexpr int kCpolNT = 2;          // cache-policy bit "nt": streamed once, do not keep
 
-__device__ __forceinline__ void wait_vmcnt_le(int n) {
-    // s_waitcnt with expcnt and lgkmcnt at their "no wait" maxima; n <= 63
-    switch (n) {
-    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
-    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
-    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
-    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;   // waiting for all is always safe
-    }
-}
 
 template <int NKS, bool GREEDY>   // NKS = r / 16 rank steps of the 32x32x16 MFMA
 __global__ __launch_bounds__(kStreamWaves * 64, 1)
@@ -1316,24 +1299,6 @@ struct FinStreamArgs {
     int r;
 };
 
-// Inverse CDF over one weight per lane (lanes in token order): the lane whose
-// interval [excl, incl) holds thr and thr - excl; past the end (rounding) the
-// last lane with weight and +inf.  Neighbouring intervals share end points.
-__device__ __forceinline__ int wave_pick(double w, double thr, double& rem) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const double incl = wave_inclusive_scan_f64(w);
-    double excl = __shfl_up(incl, 1);
-    if (lane == 0) excl = 0.0;
-    unsigned long long hit = __ballot(w > 0.0 && thr >= excl && thr < incl);
-    if (hit) {
-        const int l = __ffsll((long long)hit) - 1;
-        rem = thr - __shfl(excl, l);
-        return l;
-    }
-    const unsigned long long pos = __ballot(w > 0.0);
-    rem = INFINITY;
-    return pos ? 63 - __clzll((long long)pos) : 0;
-}
 
 __global__ __launch_bounds__(64)
 void draft_finalize_stream(FinStreamArgs A) {

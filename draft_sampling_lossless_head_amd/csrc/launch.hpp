@@ -34,6 +34,18 @@ __host__ __device__ inline size_t w2p_index(int v, int j, int r) {
     return (size_t)v * r + (size_t)slot * 8 + (j & 7);
 }
 
+// Streaming bias tiles (q-free draft and residual): a work item is a 64-token
+// slice x 128 request rows; one wave covers 32 tokens x 32 rows of it, and a
+// segment is those 32 tokens of one row.  Workgroups take contiguous shares of
+// a row block's slices, at most kMaxShares per row.
+constexpr int kStreamItem = 64;
+constexpr int kStreamSeg = 32;
+constexpr int kStreamRows = 128;
+constexpr int kStreamWaves = 8;
+constexpr int kMaxShares = 256;
+constexpr int kCpolNT = 2;          // cache-policy bit "nt": streamed once, do not keep
+int stream_shares(int B, int V);
+
 inline size_t w2p_bytes(int r, int V) {
     return (size_t)((V + kPackTile - 1) / kPackTile) * kPackTile * (size_t)r * 2;
 }
@@ -160,6 +172,30 @@ struct VerifyArgs {
     FinalInfo* fin;             // [B]
     double* chunk_sums;         // [B, nchunk]
 };
+
+// Final draw of q-free verification, streamed (residual_kernels.hip).
+struct ResidArgs {
+    const uint16_t* P;          // bf16 target rows: dense [B, G + 1, V] or packed
+    const int64_t* p_row_off;   // [B] first target row of each request, or null
+    const uint16_t* U;          // bf16 [B, G, V] draft base logits (G > 0)
+    const uint16_t* W1;         // [V, r]
+    const uint16_t* W2P;        // packed W2 image
+    const int32_t* x0;          // [B]
+    const int32_t* draft;       // [B, G]
+    const FinalInfo* fin;       // [B] decisions of verify_decide
+    float* gsums;               // [2 nitem][bpad][4] weight sums per 8-token group
+    float* sup;                 // [ws][bpad] weight sums per (share, row)
+    int32_t* out_tokens;        // [B, G + 1]
+    const float* uniforms;      // [B, G + 1] or null
+    uint64_t seed;
+    uint32_t offset;
+    int B, G, V, r;
+    float invT;
+};
+
+// bf16 P and U, V % 8 == 0, r in {64, 128, 256}, at most 64 segments per share.
+bool resid_streams(int B, int V, int r);
+hipError_t verify_resid_launch(const ResidArgs& A, hipStream_t s);
 
 int verify_num_chunks(int V);
 hipError_t verify_launch(const VerifyArgs& a, hipStream_t s);

@@ -68,7 +68,7 @@ DraftLayout draft_layout(bool rnn, int B, int gamma, int V, int r) {
 }
 
 struct VerifyLayout {
-    size_t rows, fin, chunks, rowpos, lrows, w2t, total;
+    size_t rows, fin, chunks, rowpos, lrows, w2t, rgs, rsup, total;
 };
 
 // markov_r > 0 adds the q-free verification buffers: the recomputed logits of
@@ -89,6 +89,14 @@ VerifyLayout verify_layout(int B, int gamma_max, int V, int markov_r = 0) {
         off += align_up((size_t)B * V * sizeof(float));
         L.w2t = off;
         off += align_up(w2p_bytes(markov_r, V));
+        // streamed final draw: group sums [2 nitem][rows padded to 128][4] and
+        // share sums [256][rows padded]
+        const size_t bpad = ((size_t)B + 127) / 128 * 128;
+        const size_t nitem = ((size_t)V + 63) / 64;
+        L.rgs = off;
+        off += align_up(2 * nitem * bpad * 4 * sizeof(float));
+        L.rsup = off;
+        off += align_up((size_t)kMaxShares * bpad * sizeof(float));
     }
     L.total = off;
     return L;
@@ -449,6 +457,44 @@ spec_status_t spec_verify_markov(const void* P, int p_dtype, const void* U, int 
     a.chunk_sums = reinterpret_cast<double*>(w + L.chunks);
     hipError_t e = verify_rows_decide_launch(a, s);
     if (e != hipSuccess) return hip_fail(e, "verify");
+    if (!a.greedy && gamma_max > 0 && p_dtype == SPEC_BF16 && U_dtype == SPEC_BF16 &&
+        resid_streams(B, V, r)) {
+        // streamed final draw: residual rows rebuilt in registers, never stored
+        // (gamma_max == 0 has no residual: the bonus draw below serves it)
+        const uint16_t* w2t = static_cast<const uint16_t*>(W2T);
+        if (!w2t) {
+            void* t = prof_begin("w2_pack", s);
+            e = w2_pack_launch(static_cast<const uint16_t*>(W2),
+                               reinterpret_cast<uint16_t*>(w + L.w2t), r, V, s);
+            prof_end(t, s);
+            if (e != hipSuccess) return hip_fail(e, "w2_pack");
+            w2t = reinterpret_cast<const uint16_t*>(w + L.w2t);
+        }
+        ResidArgs ra{};
+        ra.P = static_cast<const uint16_t*>(P);
+        ra.p_row_off = p_row_off;
+        ra.U = static_cast<const uint16_t*>(U);
+        ra.W1 = static_cast<const uint16_t*>(W1);
+        ra.W2P = w2t;
+        ra.x0 = x0;
+        ra.draft = draft;
+        ra.fin = a.fin;
+        ra.gsums = reinterpret_cast<float*>(w + L.rgs);
+        ra.sup = reinterpret_cast<float*>(w + L.rsup);
+        ra.out_tokens = out_tokens;
+        ra.uniforms = uniforms;
+        ra.seed = seed;
+        ra.offset = offset;
+        ra.B = B;
+        ra.G = gamma_max;
+        ra.V = V;
+        ra.r = r;
+        ra.invT = a.invT;
+        void* t = prof_begin("verify_resid", s);
+        e = verify_resid_launch(ra, s);
+        prof_end(t, s);
+        return e == hipSuccess ? SPEC_OK : hip_fail(e, "verify_resid");
+    }
     if (!a.greedy && gamma_max > 0) {
         const uint16_t* w2t = static_cast<const uint16_t*>(W2T);
         if (!w2t) {

@@ -206,6 +206,9 @@ def _verify_rows(g, b, lz):
     (130, 2, 1500, 128, "f32", "bf16", 1.0, 1.5),    # two row blocks
     (8, 4, 131, 16, "f32", "f32", 1.0, 0.8),
     (10, 5, 2000, 64, "f32", "f32", 0.0, 0.6),       # greedy
+    # streamed final draw (bf16 P and U, V % 8 == 0, r in {64, 128, 256}):
+    (140, 3, 4104, 128, "bf16", "bf16", 0.8, 1.0),   # two row blocks, 8-token tail slice
+    (20, 4, 3000, 256, "bf16", "bf16", 1.3, 0.4),
 ])
 def test_verify_markov_parity(orc, B, G, V, r, pdt, udt, T, sigma):
     sd = require_gpu()
@@ -273,6 +276,35 @@ def test_verify_markov_ragged_packed(orc):
         assert 0 <= g["accepted"][b] <= L
     assert g["accepted"][3] == 0
     note(f"  {tally.as_dict()} accepted={g['accepted'].tolist()}")
+
+
+def test_verify_markov_bonus_only_bf16(orc):
+    """gamma_max = 0 with bf16 rows: every request draws its bonus token from
+    its single target row (no residual, so the streamed draw is not used; the
+    library must not touch a packed W2 it never built)."""
+    sd = require_gpu()
+    B, V, r = 5, 4000, 64
+    rng = np.random.default_rng(12)
+    P32 = (rng.standard_normal((B, 1, V)) * 3).astype(np.float32)
+    P = workloads.f32_to_bf16_bits(P32)
+    W1 = workloads.f32_to_bf16_bits(rng.standard_normal((V, r)).astype(np.float32))
+    W2 = workloads.f32_to_bf16_bits(rng.standard_normal((r, V)).astype(np.float32))
+    empty_f = torch.zeros((B, 0), dtype=torch.float32, device="cuda")
+    g = host(sd.spec_verify_markov(
+        dev(P, "bf16"), torch.zeros((B, 0, V), dtype=torch.bfloat16, device="cuda"),
+        dev(np.zeros(B, np.int32)), dev(W1, "bf16"), dev(W2, "bf16"),
+        torch.zeros((B, 0), dtype=torch.int32, device="cuda"), empty_f, empty_f, 1.0, seed=6))
+    u = orc.verify_uniforms(6, 0, B, 0)
+    Pf = workloads.as_f64(P, "bf16")
+    tally = compare.Tally()
+    for b in range(B):
+        w, Z, _ = orc.softmax_weights(Pf[b, 0], 1.0)
+        want = orc.inverse_cdf(w, Z, u[b, 0])[0]
+        assert g["accepted"][b] == 0
+        if g["out_tokens"][b, 0] != want:
+            compare._check_draw(w, want, int(g["out_tokens"][b, 0]), u[b, 0], f"b={b}")
+            tally.boundary += 1
+    assert tally.boundary <= 1
 
 
 def test_verify_markov_bonus_only(orc):
