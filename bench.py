@@ -46,13 +46,12 @@ def kernel_bytes(wl):
     B, g, V, r = wl["B"], wl["gamma"], wl["V"], wl["r"]
     lb = 2 if wl["logit_dtype"] == "bf16" else 4
     wb = 2 if wl["w_dtype"] == "bf16" else 4
-    nseg = (V + 127) // 128
     return {
         # U_k read, q_k written, W2 / gamma, the B gathered W1 rows
         "draft_tile": B * V * (lb + 4) + r * V * wb / g + B * r * wb,
-        # U_k read; per (row, 64-token segment) a 16-byte summary and 8 group
-        # sums, per (row, share) one summary (256 shares) written
-        "draft_tile_qfree": B * V * lb + B * ((V + 63) // 64) * (16 + 8 * 4) + B * 256 * 16
+        # U_k read; per (row, 32-token segment) its max and 4 group sums, per
+        # (row, share) one 16-byte summary (256 shares) written
+        "draft_tile_qfree": B * V * lb + B * ((V + 31) // 32) * (4 + 4 * 4) + B * 256 * 16
                             + r * V * wb / g + B * r * wb,
         "verify_rows_p": B * (g + 1) * V * lb,
         "verify_rows_q": B * g * V * 4,
@@ -182,7 +181,7 @@ def main():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU run: turn two rocprofv3 --pmc counter CSVs into the traffic "
                          "record of --traffic-kernel")
-    ap.add_argument("--traffic-kernel", default="draft_tile_stream<8, false>")
+    ap.add_argument("--traffic-kernel", default="draft_tile_stream<16, false>")
     ap.add_argument("--traffic-label", default="draft_tile_qfree")
     args = ap.parse_args()
     if args.traffic_from:
