@@ -53,6 +53,10 @@ def kernel_bytes(wl):
         # (row, share) one 16-byte summary (256 shares) written
         "draft_tile_qfree": B * V * lb + B * ((V + 31) // 32) * (4 + 4 * 4) + B * 256 * 16
                             + r * V * wb / g + B * r * wb,
+        # the whole draft in one launch: per position U_k, the W1 rows and the
+        # same summaries; W2 once
+        "draft_persist": g * (B * V * lb + B * ((V + 31) // 32) * (4 + 4 * 4) + B * 256 * 16
+                              + B * r * wb) + r * V * wb,
         "verify_rows_p": B * (g + 1) * V * lb,
         "verify_rows_q": B * g * V * 4,
     }
@@ -67,6 +71,10 @@ def source_sha(paths):
 
 
 KERNEL_SOURCES = {
+    "draft_persist": ["draft_sampling_lossless_head_amd/csrc/draft_persist.hip",
+                      "draft_sampling_lossless_head_amd/csrc/stream_finalize.hpp",
+                      "draft_sampling_lossless_head_amd/csrc/device_common.hpp",
+                      "draft_sampling_lossless_head_amd/csrc/launch.hpp"],
     "draft_tile_qfree": ["draft_sampling_lossless_head_amd/csrc/draft_kernels.hip",
                          "draft_sampling_lossless_head_amd/csrc/device_common.hpp",
                          "draft_sampling_lossless_head_amd/csrc/launch.hpp"],
@@ -171,6 +179,8 @@ def main():
     ap.add_argument("--workload", default="markov-152k-b128")
     ap.add_argument("--path", choices=("qfree", "materialized"), default="qfree",
                     help="q-free cycle (no draft-logit tensor) or materialized draft logits")
+    ap.add_argument("--engine", choices=("persistent", "per_position"), default="persistent",
+                    help="q-free draft: one persistent launch, or two launches per position")
     ap.add_argument("--sigma", type=float, default=None, help="override target/draft noise")
     ap.add_argument("--cpu-sample", type=int, default=64, help="requests timed on the oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -221,6 +231,7 @@ def main():
     U, P = to_dev(wl["U"], lb), to_dev(wl["P"], lb)
     W1, W2, x0 = to_dev(wl["W1"], wbt), to_dev(wl["W2"], wbt), to_dev(wl["x0"])
     qfree = args.path == "qfree"
+    sd.spec_draft_set_persistent(args.engine == "persistent")
     W2T = sd.spec_pack_w2(W2)          # once per model load
     d_out = dict(tokens=torch.empty((B, g), dtype=torch.int32, device=dev),
                  q_logZ=torch.empty((B, g), dtype=torch.float32, device=dev),
@@ -286,7 +297,7 @@ def main():
     prof_ms_per_step = (time.perf_counter() - t1) * 1e3 / args.steps
     sd.spec_profile_enable(None)
     kernels = {}
-    names = ["w2_pack", "draft_tile", "draft_tile_qfree", "draft_finalize", "verify_rows_p",
+    names = ["w2_pack", "draft_persist", "draft_tile", "draft_tile_qfree", "draft_finalize", "verify_rows_p",
              "verify_rows_q", "verify_decide", "verify_residual_rows", "verify_resid", "verify_final_partials",
              "verify_final_draw"]
     for name in names:
@@ -321,7 +332,8 @@ def main():
         "config": {"workload": args.workload, "B": B, "gamma": g, "V": V, "r": r,
                    "logits": lb, "weights": wbt, "accumulate": "fp32", "T": T,
                    "sigma": float(wl["sigma"][0]), "head": "markov",
-                   "verify": "fixed-length", "path": args.path},
+                   "verify": "fixed-length", "path": args.path,
+                   "engine": args.engine if qfree else "per_position"},
         "roofline": roofline,
         "breakdown": {
             "drafted_per_s": None, "verified_per_s": None,

@@ -13,6 +13,7 @@ from .api import (  # noqa: F401
     load_library,
     spec_draft_sample_markov,
     spec_draft_sample_rnn,
+    spec_draft_set_persistent,
     spec_pack_w2,
     spec_pack_w2_bytes,
     spec_philox_uniforms,

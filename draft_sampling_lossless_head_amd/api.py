@@ -67,6 +67,8 @@ def load_library():
                                        vp, vp, i32, i32, i32, f32, vp, u64, u32, vp, vp, vp, vp,
                                        vp, sz, vp]
     lib.spec_verify_markov.restype = i32
+    lib.spec_draft_set_persistent.argtypes = [i32]
+    lib.spec_draft_set_persistent.restype = i32
     lib.spec_profile_enable.argtypes = [ctypes.c_char_p]
     lib.spec_profile_enable.restype = i32
     lib.spec_profile_read.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_double)]
@@ -289,6 +291,13 @@ def spec_verify(P, Q, draft, T=1.0, *, gamma_max=None, lens=None, p_row_off=None
         nws, _stream(stream))
     _check(st, "spec_verify")
     return out
+
+
+def spec_draft_set_persistent(enable):
+    """Engine of the q-free Markov draft: True runs all positions in one
+    persistent launch where the shape allows it, False two launches per
+    position.  Returns the previous setting."""
+    return bool(load_library().spec_draft_set_persistent(1 if enable else 0))
 
 
 def spec_profile_enable(kernel):

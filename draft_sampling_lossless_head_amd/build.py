@@ -14,7 +14,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libspecdec.so")
 OBJDIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["draft_kernels.hip", "verify_kernels.hip", "residual_kernels.hip", "specdec_api.hip",
+SOURCES = ["draft_kernels.hip", "draft_persist.hip", "verify_kernels.hip", "residual_kernels.hip",
+           "specdec_api.hip",
            "profile.hip"]
 
 HIPCC_FLAGS = [

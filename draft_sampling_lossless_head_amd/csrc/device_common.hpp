@@ -161,15 +161,99 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // Wait until at most n vector-memory operations of this wave are outstanding
 // (expcnt and lgkmcnt left at their "no wait" maxima).  Direct global->LDS
-// loads count here too; loads complete in issue order.
+// loads count here too; loads complete in issue order.  The s_waitcnt
+// immediate holds vmcnt bits 3:0 at 3:0 and bits 5:4 at 15:14.
+#define SPECDEC_VMCNT_IMM(n) (0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
+#define SPECDEC_VMCNT_CASE(n) \
+    case n: __builtin_amdgcn_s_waitcnt(SPECDEC_VMCNT_IMM(n)); break;
 __device__ __forceinline__ void wait_vmcnt_le(int n) {
-    // s_waitcnt with expcnt and lgkmcnt at their "no wait" maxima; n <= 63
     switch (n) {
-    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
-    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
-    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
-    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;   // waiting for all is always safe
+        SPECDEC_VMCNT_CASE(1) SPECDEC_VMCNT_CASE(2) SPECDEC_VMCNT_CASE(3)
+        SPECDEC_VMCNT_CASE(4) SPECDEC_VMCNT_CASE(5) SPECDEC_VMCNT_CASE(6)
+        SPECDEC_VMCNT_CASE(7) SPECDEC_VMCNT_CASE(8) SPECDEC_VMCNT_CASE(9)
+        SPECDEC_VMCNT_CASE(10) SPECDEC_VMCNT_CASE(11) SPECDEC_VMCNT_CASE(12)
+        SPECDEC_VMCNT_CASE(13) SPECDEC_VMCNT_CASE(14) SPECDEC_VMCNT_CASE(15)
+        SPECDEC_VMCNT_CASE(16) SPECDEC_VMCNT_CASE(17) SPECDEC_VMCNT_CASE(18)
+        SPECDEC_VMCNT_CASE(19) SPECDEC_VMCNT_CASE(20) SPECDEC_VMCNT_CASE(21)
+        SPECDEC_VMCNT_CASE(22) SPECDEC_VMCNT_CASE(23) SPECDEC_VMCNT_CASE(24)
+        SPECDEC_VMCNT_CASE(25) SPECDEC_VMCNT_CASE(26) SPECDEC_VMCNT_CASE(27)
+        SPECDEC_VMCNT_CASE(28) SPECDEC_VMCNT_CASE(29) SPECDEC_VMCNT_CASE(30)
+        SPECDEC_VMCNT_CASE(31) SPECDEC_VMCNT_CASE(32)
+    default: __builtin_amdgcn_s_waitcnt(SPECDEC_VMCNT_IMM(0)); break;   // waiting for all is always safe
+    }
+}
+#undef SPECDEC_VMCNT_CASE
+
+// The same wait with a compile-time count (no branch).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt(SPECDEC_VMCNT_IMM(N));
+}
+
+// Accesses to data that workgroups on other XCDs read or wrote in the same
+// launch.  With COH they are agent-scope relaxed atomics, which bypass the
+// per-XCD caches (write-through stores, coherent loads), so no cache
+// write-back or invalidate is needed around a grid barrier; without it they
+// are plain accesses.  Wider values move as 64-bit halves.
+template <bool COH, typename T>
+__device__ __forceinline__ T coh_load(const T* p) {
+    if constexpr (COH) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else return *p;
+}
+template <bool COH, typename T>
+__device__ __forceinline__ void coh_store(T* p, T v) {
+    if constexpr (COH) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else *p = v;
+}
+template <bool COH>
+__device__ __forceinline__ float4 coh_load_f32x4(const float* p) {
+    if constexpr (COH) {
+        const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
+        const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return make_float4(__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)(a >> 32)),
+                           __uint_as_float((uint32_t)b), __uint_as_float((uint32_t)(b >> 32)));
+    } else {
+        return *reinterpret_cast<const float4*>(p);
+    }
+}
+template <bool COH>
+__device__ __forceinline__ void coh_store_f32x2(float* p, float a, float b) {
+    if constexpr (COH) {
+        const uint64_t v = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+        __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+        *reinterpret_cast<float2*>(p) = make_float2(a, b);
+    }
+}
+template <bool COH>
+__device__ __forceinline__ SegStat coh_load_seg(const SegStat* p) {
+    if constexpr (COH) {
+        const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
+        const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        SegStat x;
+        x.m = __uint_as_float((uint32_t)a);
+        x.s = __uint_as_float((uint32_t)(a >> 32));
+        x.idx = (int)(uint32_t)b;
+        x.pad = (int)(uint32_t)(b >> 32);
+        return x;
+    } else {
+        return *p;
+    }
+}
+template <bool COH>
+__device__ __forceinline__ void coh_store_seg(SegStat* p, const SegStat& x) {
+    if constexpr (COH) {
+        uint64_t* q = reinterpret_cast<uint64_t*>(p);
+        __hip_atomic_store(q, (uint64_t)__float_as_uint(x.m) | ((uint64_t)__float_as_uint(x.s) << 32),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(q + 1, (uint64_t)(uint32_t)x.idx | ((uint64_t)(uint32_t)x.pad << 32),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+        *p = x;
     }
 }
 

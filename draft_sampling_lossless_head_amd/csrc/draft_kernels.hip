@@ -21,6 +21,7 @@
 
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "stream_finalize.hpp"
 
 namespace specdec {
 
@@ -1266,222 +1267,8 @@ void draft_finalize(const SegStat* __restrict__ stats, int nseg, int seg_len,
     }
 }
 
-// ---------------------------------------------------------------------------
-// Finalize of the streaming q-free draft.  One wave per request row (no
-// workgroup barriers); the inverse-CDF descent takes three dependent reads:
-//   1. the row's ws <= 256 share summaries, four per lane: max, normaliser and
-//      the share holding u * Z (fp64 weights and scan);
-//   2. the share's 32-token segments (max and 4 group sums), read together:
-//      the segment, then the 8-token group;
-//   3. the group's 8 logits rebuilt as U + W1[prev] . W2 (the W1 row slice is
-//      fetched at entry), then the token.
-// Scaling factors use fp32 exponentials (relative error ~1e-7); sums, scans
-// and the threshold are fp64.
-// ---------------------------------------------------------------------------
-struct FinStreamArgs {
-    const SegStat* sup;     // [ws][bpad] share summaries
-    const float* segm;      // [2 nitem][bpad] max of each 32-token segment
-    const float* gsums;     // [2 nitem][bpad][4] 8-token group sums relative to it
-    int ws, nitem, bpad;
-    const int32_t* x0;
-    int32_t* tokens;
-    float* q_logZ;
-    float* q_tok;
-    const float* uniforms;
-    uint64_t seed;
-    uint32_t offset;
-    int gamma, V, k;
-    float invT;
-    int greedy;
-    const uint16_t* U;      // bf16 [B, gamma, V]
-    const uint16_t* W1;     // [V, r]
-    const uint16_t* W2P;    // packed W2 image
-    int r;
-};
-
-
 __global__ __launch_bounds__(64)
-void draft_finalize_stream(FinStreamArgs A) {
-    const int b = blockIdx.x;
-    const int lane = threadIdx.x;
-    const size_t outi = (size_t)b * A.gamma + A.k;
-    const int V = A.V;
-    const float invT = A.invT;
-
-    const int prev = (A.k == 0) ? A.x0[b] : A.tokens[outi - 1];
-    if (prev < 0 || prev >= V) {
-        if (lane == 0) {
-            A.tokens[outi] = -1;
-            if (A.q_logZ) A.q_logZ[outi] = NAN;
-            if (A.q_tok) A.q_tok[outi] = NAN;
-        }
-        return;
-    }
-    const float u = A.uniforms ? A.uniforms[outi] : counter_uniform(A.seed, A.offset, b, A.k, 0);
-    // this lane's W1 slice for the rebuild (lane = 8t + sl: rank slice sl)
-    const int span = A.r / 8;   // <= 32 bf16: at most 4 chunks of 16 bytes
-    uint4 w1c[4];
-    {
-        const uint16_t* w1 = A.W1 + (size_t)prev * A.r + (lane & 7) * span;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            w1c[q] = (q * 8 < span) ? *reinterpret_cast<const uint4*>(w1 + q * 8)
-                                    : make_uint4(0u, 0u, 0u, 0u);
-    }
-
-    // 1) share summaries, four per lane (shares 4 * lane + q).
-    float sm[4], ss[4];
-    int si[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int j = 4 * lane + q;
-        if (j < A.ws) {
-            const SegStat x = A.sup[(size_t)j * A.bpad + b];
-            sm[q] = x.m;
-            ss[q] = x.s;
-            si[q] = x.idx;
-        } else {
-            sm[q] = -INFINITY;
-            ss[q] = 0.0f;
-            si[q] = INT_MAX;
-        }
-    }
-    float M = sm[0];
-    int AM = si[0];
-#pragma unroll
-    for (int q = 1; q < 4; ++q) merge_arg(M, AM, sm[q], si[q]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const float m2 = __shfl_xor(M, off);
-        const int i2 = __shfl_xor(AM, off);
-        merge_arg(M, AM, m2, i2);
-    }
-    if (A.greedy || M == -INFINITY) {
-        if (lane == 0) {
-            A.tokens[outi] = (M == -INFINITY) ? -1 : AM;
-            if (A.q_logZ) A.q_logZ[outi] = M == -INFINITY ? NAN : M;
-            if (A.q_tok) A.q_tok[outi] = M == -INFINITY ? NAN : 1.0f;
-        }
-        return;
-    }
-    double w[4];
-    double lsum = 0.0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        w[q] = sm[q] != -INFINITY ? (double)ss[q] * (double)__expf((sm[q] - M) * invT) : 0.0;
-        lsum += w[q];
-    }
-    const double Z = __shfl(wave_inclusive_scan_f64(lsum), kWave - 1);
-    const double thr = (double)u * Z;
-    double rem;
-    const int ol = wave_pick(lsum, thr, rem);
-    // the owning lane walks its four shares
-    int qsel = 3;
-    double qrem = INFINITY;
-    {
-        double run = 0.0;
-        int last = -1;
-        double last_run = 0.0;
-        int found = -1;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            if (found < 0 && w[q] > 0.0) {
-                last = q;
-                last_run = run;
-                if (rem < run + w[q]) {
-                    found = q;
-                    qrem = rem - run;
-                }
-            }
-            run += w[q];
-        }
-        if (found < 0) {
-            found = last < 0 ? 0 : last;
-            qrem = rem == INFINITY ? INFINITY : rem - last_run;
-        }
-        qsel = found;
-    }
-    const int sh = 4 * ol + __shfl(qsel, ol);
-    const double rem1 = __shfl(qrem, ol);
-
-    // 2) the share's 32-token segments and their group sums, one read.
-    const int s0 = 2 * (int)((long long)sh * A.nitem / A.ws);
-    const int s1 = 2 * (int)((long long)(sh + 1) * A.nitem / A.ws);
-    const int sg = s0 + lane;
-    const bool have = sg < s1;   // at most 64 segments per share (launcher guarantee)
-    float ym = -INFINITY;
-    float4 g4 = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (have) {
-        const size_t sx = (size_t)sg * A.bpad + b;
-        ym = A.segm[sx];
-        g4 = *reinterpret_cast<const float4*>(A.gsums + sx * 4);
-    }
-    const double ysc = ym != -INFINITY ? (double)__expf((ym - M) * invT) : 0.0;
-    const double ys = ((double)g4.x + (double)g4.y) + ((double)g4.z + (double)g4.w);
-    double rem2;
-    const int sl_seg = wave_pick(ys * ysc, rem1, rem2);
-    const int seg = s0 + sl_seg;
-    // the chosen segment's 4 group weights to lanes 0..3
-    const double gscale = __shfl(ysc, sl_seg);
-    const float gv[4] = {g4.x, g4.y, g4.z, g4.w};
-    float mine = 0.0f;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        const float v = __shfl(gv[g], sl_seg);
-        if (lane == g) mine = v;
-    }
-    double grem;
-    const int grp = wave_pick(lane < 4 ? (double)mine * gscale : 0.0, rem2, grem);
-
-    // 3) rebuild the group's 8 logits: lane = 8t + sl.
-    const int t = lane >> 3, sl = lane & 7;
-    const int vt = seg * kStreamSeg + grp * 8 + t;
-    float part = 0.0f;
-    float ut = 0.0f;
-    if (vt < V) {
-        const int nswz = w2p_swizzle(vt & (kPackTile - 1), A.r >> 3);
-        if ((span & 7) == 0) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if (q * 8 < span) {
-                    const int kc = sl * (span >> 3) + q;
-                    const uint4 c = *reinterpret_cast<const uint4*>(
-                        A.W2P + (size_t)vt * A.r + ((kc ^ nswz) << 3));
-                    const uint32_t aw[4] = {w1c[q].x, w1c[q].y, w1c[q].z, w1c[q].w};
-                    const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-                    for (int h = 0; h < 4; ++h) {
-                        part = fmaf(bf16_bits_to_float(aw[h] & 0xFFFFu),
-                                    bf16_bits_to_float(cw[h] & 0xFFFFu), part);
-                        part = fmaf(bf16_bits_to_float(aw[h] >> 16),
-                                    bf16_bits_to_float(cw[h] >> 16), part);
-                    }
-                }
-            }
-        } else {   // span < 8 (r < 64)
-            const uint16_t* w1 = A.W1 + (size_t)prev * A.r;
-            for (int j = sl * span; j < (sl + 1) * span; ++j)
-                part = fmaf(bf16_bits_to_float(w1[j]),
-                            bf16_bits_to_float(A.W2P[w2p_index(vt, j, A.r)]), part);
-        }
-        ut = bf16_bits_to_float(A.U[outi * (size_t)V + vt]);
-    }
-    part += __shfl_xor(part, 1);
-    part += __shfl_xor(part, 2);
-    part += __shfl_xor(part, 4);
-    const float lt = ut + part;
-    const float wtk = vt < V ? __expf((lt - M) * invT) : 0.0f;
-    const float w8 = __shfl(wtk, (lane & 7) * 8);
-    const float l8 = __shfl(lt, (lane & 7) * 8);
-    double trem;
-    const int tsel = wave_pick(lane < 8 ? (double)w8 : 0.0, grem, trem);
-    const float lsel = __shfl(l8, tsel);
-    if (lane == 0) {
-        A.tokens[outi] = min(seg * kStreamSeg + grp * 8 + tsel, V - 1);
-        if (A.q_logZ) A.q_logZ[outi] = (float)((double)M * (double)invT + (double)__logf((float)Z));
-        if (A.q_tok) A.q_tok[outi] = (float)((double)__expf((lsel - M) * invT) / Z);
-    }
-}
+void draft_finalize_stream(FinStreamArgs A, int k) { finalize_row_stream<false>(A, blockIdx.x, k, threadIdx.x & (kWave - 1)); }
 
 // ---------------------------------------------------------------------------
 // RNN head.
@@ -1799,7 +1586,8 @@ hipError_t draft_finalize_launch(const DraftArgs& a, int k, hipStream_t s) {
         f.segm = reinterpret_cast<const float*>(a.stats);
         f.gsums = a.gsums;
         f.ws = stream_shares(a.B, a.V);
-        f.nitem = (a.V + kStreamItem - 1) / kStreamItem;
+        f.nunit = (a.V + kStreamItem - 1) / kStreamItem;
+        f.seg_mult = kStreamItem / kStreamSeg;
         f.bpad = (a.B + kStreamRows - 1) / kStreamRows * kStreamRows;
         f.x0 = a.x0;
         f.tokens = a.tokens;
@@ -1810,14 +1598,16 @@ hipError_t draft_finalize_launch(const DraftArgs& a, int k, hipStream_t s) {
         f.offset = a.offset;
         f.gamma = a.gamma;
         f.V = a.V;
-        f.k = k;
         f.invT = a.invT;
         f.greedy = a.greedy;
         f.U = static_cast<const uint16_t*>(a.U);
         f.W1 = static_cast<const uint16_t*>(a.W1);
         f.W2P = a.W2T;
         f.r = a.r;
-        hipLaunchKernelGGL(draft_finalize_stream, dim3(a.B), dim3(64), 0, s, f);
+        f.tflag = nullptr;
+        f.abort_word = nullptr;
+        f.poll_limit = 0;
+        hipLaunchKernelGGL(draft_finalize_stream, dim3(a.B), dim3(64), 0, s, f, k);
         return hipGetLastError();
     }
     const int nseg = draft_num_segments(a);

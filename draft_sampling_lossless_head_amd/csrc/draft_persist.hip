@@ -1,0 +1,637 @@
+// Persistent, weight-stationary q-free Markov draft ("[논문리뷰] DSpark ...",
+// §1.2 Sequential stage, Markov-head equation): every position of every
+// request in one cooperative launch of one workgroup per CU.
+//
+// The per-position kernels read all of the packed W2 image once per position.
+// Here each workgroup owns a fixed contiguous range of 32-token blocks (its
+// share of the vocabulary) for the whole call, and each of its four waves
+// (one per SIMD, so 512 registers each) keeps the MFMA A operands of up to NB
+// of those blocks in registers: W2 crosses HBM once per call, and only U_k
+// streams per position.  Position k then runs as
+//
+//   1. E = W1[x_{k-1}] of 128 request rows gathered into LDS (direct loads,
+//      chunk c of row n stored in slot c ^ (n & 7): conflict-free B reads);
+//   2. per wave, units (32 rows x one of its 32-token blocks): U_k of the unit
+//      streams through a wave-private LDS ring (direct loads, D units ahead),
+//      16 (r = 256) 32x32x16 MFMAs against the resident W2 operands, then the
+//      reduction of the previous unit: the block's max and four 8-token group
+//      sums relative to it (the same segment summaries as the per-position
+//      streaming tile), and a running (max, sum) of the wave's blocks per row;
+//   3. the four waves' running summaries merged into one summary per (row,
+//      workgroup share);
+//   4. grid barrier; one wave per row runs the shared finalize (shares ->
+//      segment -> group -> token, rebuilding 8 logits) -> x_k, log Z, q(x_k);
+//   5. grid barrier (every workgroup needs every row's x_k), next position.
+//
+// MFMA row i = 8g + 4h + c of a block holds token 16h + 8 (g & 1) + 4 (g >> 1)
+// + c, so a lane's 16 accumulators are 16 contiguous tokens of one row and its
+// U values are two 16-byte chunks.  The grid barriers are counter based with a
+// bounded wait: the launch is cooperative (all workgroups resident), and if a
+// barrier still does not complete within the poll limit every workgroup
+// leaves, setting an abort word the host can read.
+#include <algorithm>
+#include <climits>
+
+#include "device_common.hpp"
+#include "launch.hpp"
+#include "stream_finalize.hpp"
+
+namespace specdec {
+
+constexpr int kPersistWaves = 4;             // one wave per SIMD
+constexpr int kPersistUnit = 2048;           // U bytes of one unit: 32 rows x 32 tokens
+constexpr unsigned kBarrierPolls = 1u << 20; // polls (with s_sleep) before a barrier gives up
+
+// Both values of a lane pair (l, l ^ 32), one in each result: swapping the
+// upper half of one copy with the lower half of the other leaves lane l with
+// {x[l % 32], x[32 + l % 32]}.  Max and sum of the two are pair-symmetric.
+__device__ __forceinline__ float pair_max32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void pair_argmax32(float& m, int& a) {
+    const auto rm = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    const auto ra = __builtin_amdgcn_permlane32_swap((unsigned)a, (unsigned)a, false, false);
+    float m0 = __uint_as_float(rm[0]);
+    int a0 = (int)ra[0];
+    merge_arg(m0, a0, __uint_as_float(rm[1]), (int)ra[1]);
+    m = m0;
+    a = a0;
+}
+
+// Chunk swizzle of a U ring slot (32 rows x 64 bytes): conflict-free reads of
+// chunks 2h and 2h + 1 of row m by lane (m, h), in groups of 8 or 16 lanes.
+__device__ __forceinline__ int uswz(int m) { return ((m >> 1) ^ (m >> 2)) & 3; }
+
+struct PersistArgs {
+    FinStreamArgs fin;   // finalize inputs and outputs (tokens, q_logZ, q_tok, ...)
+    float* segm;         // [nblk][bpad] max of each 32-token block
+    float* gsums;        // [nblk][bpad][4] 8-token group sums relative to it
+    SegStat* sup;        // [shares][bpad] per-(share, row) summaries
+    unsigned* bar;       // barrier words (kBarWords, zero at launch except the -inf
+                         // values that stand in for the U chunks of absent tokens)
+    int B, gamma, V, nblk, bpad;
+};
+
+// Layout of the synchronisation words (unsigned, in the workspace): the abort
+// word and eight bf16 -inf values.
+constexpr int kBarAbort = 0;
+constexpr int kBarNegInf = 4;     // [4, 8)
+constexpr int kBarWords = 8;
+static_assert(kBarWords * sizeof(unsigned) <= kPersistBarBytes, "barrier words");
+
+// Launch preamble: clears the abort word, the token words [B] and the tagged
+// share summaries [ns] (two 64-bit words each), and sets the -inf chunk.
+__global__ void persist_bar_reset(unsigned* bar, uint64_t* tflag, int B, uint64_t* sup64,
+                                  size_t ns) {
+    const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t < (size_t)kBarWords) bar[t] = (t >= (size_t)kBarNegInf) ? 0xFF80FF80u : 0u;
+    if (t < (size_t)B) tflag[t] = 0u;
+    for (size_t i = t; i < 2 * ns; i += (size_t)gridDim.x * blockDim.x) sup64[i] = 0u;
+}
+
+// Wait until every request row has its token of position k: the word of row
+// b reads ((k + 1) << 32) | token once its finalize is done (so the summaries
+// it read may be overwritten).  Wave 0 polls with coherent loads; with
+// xprev_out the tokens of rows 0 .. B - 1 (B <= 128) are written there
+// (-1 for an invalid row).  Same bounded wait and abort word as grid_sync.
+__device__ __forceinline__ bool token_sync(unsigned* bar, const uint64_t* tflag, int B,
+                                           unsigned k1, int* xprev_out, int* ok_s) {
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        int lane = threadIdx.x;
+        asm volatile("" : "+v"(lane));   // recomputed here, not kept live across the kernel
+        int ok = 1;
+        for (unsigned polls = 0;; ++polls) {
+            bool up = true;
+            for (int i = lane; i < B; i += 64) {
+                const uint64_t w = coh_load<true>(tflag + i);
+                up = up && (uint32_t)(w >> 32) >= k1;
+                if (xprev_out) xprev_out[i] = (int)(uint32_t)w;
+            }
+            if (__all(up)) break;
+            if (coh_load<true>(bar + kBarAbort) != 0u || polls > kBarrierPolls) {
+                if (lane == 0) coh_store<true>(bar + kBarAbort, 1u);
+                ok = 0;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        if (lane == 0) *ok_s = ok;
+    }
+    __syncthreads();
+    return *ok_s != 0;
+}
+
+template <int NKS, int NB, int NR, bool GREEDY>
+__global__ __launch_bounds__(kPersistWaves * 64, 1)
+void draft_persist(PersistArgs P) {
+    constexpr int R = NKS * 16;
+    constexpr int NCH = R / 8;                  // 16-byte chunks per rank row
+    constexpr int D = NR - 2;                   // units in flight per wave
+    constexpr int EB = kStreamRows * R * 2;     // E rows of one row block
+    static_assert(NCH >= 8 && NCH % 2 == 0, "rank");
+    static_assert(2 * D <= 32, "vmcnt waits");
+    static_assert(NKS >= 4, "the U read follows the stages that use the previous unit's U");
+    extern __shared__ __align__(16) char smem_p[];
+    __shared__ int ok_s;
+    char* e_lds = smem_p;
+    char* ring = smem_p + EB;
+    int* xprev = reinterpret_cast<int*>(ring + kPersistWaves * NR * kPersistUnit);
+    float* xsum = reinterpret_cast<float*>(xprev + kStreamRows);   // [wave][row][3]
+
+    const FinStreamArgs& F = P.fin;
+    const int V = P.V, B = P.B, G = P.gamma;
+    const int tid = threadIdx.x;
+    const int lane0 = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int NG = gridDim.x, g = blockIdx.x;
+    const int blo = (int)((long long)g * P.nblk / NG);
+    const int bhi = (int)((long long)(g + 1) * P.nblk / NG);
+    auto wave_blocks = [&](int w) { return min(NB, max(0, (bhi - blo - w + 3) / 4)); };
+    const int nj = wave_blocks(wave);   // this wave's blocks: blo + wave + 4 j, j < nj
+    const size_t bpad = (size_t)P.bpad;
+    const float sc = F.invT * 1.4426950408889634f;   // exp(y / T) = 2^(y * sc)
+
+    // Resident MFMA A operands: block j, rank step ks, MFMA row lane % 32.
+    const int i32 = lane0 & 31;
+    const int h0 = lane0 >> 5;
+    const int ptok = 16 * ((i32 >> 2) & 1) + 8 * ((i32 >> 3) & 1) + 4 * (i32 >> 4) + (i32 & 3);
+    bf16x8_t wf[NB][NKS];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+        const bool ok = j < nj;
+        const int v = (ok ? blo + wave + 4 * j : 0) * kStreamSeg + ptok;
+        const int swz = w2p_swizzle(v & (kPackTile - 1), NCH);
+        const uint16_t* row = F.W2P + (size_t)v * R;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            if (ok) {
+                wf[j][ks] = *reinterpret_cast<const bf16x8_t*>(row + (((2 * ks + h0) ^ swz) << 3));
+            } else {
+#pragma unroll
+                for (int t = 0; t < 8; ++t) wf[j][ks][t] = (__bf16)0.0f;
+            }
+        }
+    }
+
+    struct Red {
+        float m, g0, g1;
+        int am;
+    };
+    // Reduction of one finished unit (block t, this lane's row) in 16 stages,
+    // so that the next unit's MFMAs can be interleaved with it: logits
+    // x = accumulators + U (tokens past V carry U = -inf and W2 = 0), the
+    // block max, then this lane's two 8-token group sums relative to it
+    // (greedy: max and argmax).  Accumulator 4g + c holds run position
+    // 8 (g & 1) + 4 (g >> 1) + c.
+    struct Reducer {
+        float x[16];
+        float ma, mb, m, ms, g0, g1;
+        int am;
+    };
+    // vb: the first of this lane's 16 tokens (greedy only).
+    auto stage = [&](Reducer& R, const f32x16_t& ac, const u32x4_t (&uf)[2], int vb, int st) {
+        if (st < 4) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int pos = 8 * (st & 1) + 4 * (st >> 1) + c;
+                const uint32_t w = uf[pos >> 3][(pos & 7) >> 1];
+                const float uv = (pos & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
+                R.x[pos] = ac[4 * st + c] + uv;
+            }
+        } else if (st == 4) {
+            R.ma = fmaxf(fmaxf(fmaxf(R.x[0], R.x[1]), fmaxf(R.x[2], R.x[3])),
+                         fmaxf(fmaxf(R.x[4], R.x[5]), fmaxf(R.x[6], R.x[7])));
+        } else if (st == 5) {
+            R.mb = fmaxf(fmaxf(fmaxf(R.x[8], R.x[9]), fmaxf(R.x[10], R.x[11])),
+                         fmaxf(fmaxf(R.x[12], R.x[13]), fmaxf(R.x[14], R.x[15])));
+        } else if (st == 6) {
+            R.m = fmaxf(R.ma, R.mb);
+            if constexpr (GREEDY) {
+                R.am = INT_MAX;
+            } else {
+                R.m = pair_max32(R.m);
+                R.ms = R.m == -INFINITY ? 0.0f : R.m * sc;   // all -inf: every weight 0
+                R.g0 = 0.0f;
+                R.g1 = 0.0f;
+            }
+        } else if (st < 15) {
+            const int q = st - 7;
+            if constexpr (GREEDY) {
+                R.am = (R.x[15 - 2 * q] == R.m) ? vb + 15 - 2 * q : R.am;
+                R.am = (R.x[14 - 2 * q] == R.m) ? vb + 14 - 2 * q : R.am;
+                if (q == 7) pair_argmax32(R.m, R.am);
+            } else {
+                R.g0 += __builtin_amdgcn_exp2f(fmaf(R.x[q], sc, -R.ms));
+                R.g1 += __builtin_amdgcn_exp2f(fmaf(R.x[8 + q], sc, -R.ms));
+            }
+        }
+    };
+    auto finish = [&](const Reducer& R) -> Red {
+        Red o;
+        o.m = R.m;
+        o.g0 = GREEDY ? 0.0f : R.g0;
+        o.g1 = GREEDY ? 0.0f : R.g1;
+        o.am = GREEDY ? R.am : 0;
+        return o;
+    };
+    auto reduce = [&](const f32x16_t& ac, const u32x4_t (&uf)[2], int vb) -> Red {
+        Reducer R;
+#pragma unroll
+        for (int st = 0; st < 15; ++st) stage(R, ac, uf, vb, st);
+        return finish(R);
+    };
+
+    const int nrb = (B + kStreamRows - 1) / kStreamRows;
+    const uint16_t* ninf = reinterpret_cast<const uint16_t*>(P.bar + kBarNegInf);
+    for (int k = 0; k < G; ++k) {
+        for (int rb = 0; rb < nrb; ++rb) {
+            // Per-lane values below are recomputed for every row block from an
+            // opaque copy of the lane id: hoisted out of the position loop they
+            // would stay live next to the resident W2 operands and be spilled.
+            int lane = lane0;
+            asm volatile("" : "+v"(lane));
+            const int h = lane >> 5, n = lane & 31;
+            const int rows = min(kStreamRows, B - rb * kStreamRows);
+            const int nrg = (rows + 31) / 32;
+            // 1. conditioning tokens of the row block (-1: invalid or absent);
+            // with one row block they come with the token words after k = 0
+            if ((k == 0 || nrb > 1) && tid < kStreamRows) {
+                const int b = rb * kStreamRows + tid;
+                int prev = -1;
+                if (b < B) prev = k == 0 ? F.x0[b] : coh_load<true>(F.tokens + (size_t)b * G + k - 1);
+                xprev[tid] = (prev >= 0 && prev < V) ? prev : -1;
+            }
+            __syncthreads();
+            // 2. E rows into LDS, then the first D units of U.
+#pragma unroll
+            for (int q = 0; q < NCH / 2; ++q) {
+                const int pc = q * kPersistWaves + wave;
+                const int o = pc * 64 + lane;
+                const int row = o / NCH, slot = o % NCH;
+                const int p = max(xprev[row], 0);
+                __builtin_amdgcn_global_load_lds(F.W1 + (size_t)p * R + ((slot ^ (row & 7)) << 3),
+                                                 (lds_ptr_t)(e_lds + pc * 1024), 16, 0, 0);
+            }
+            // U of unit (rgi, j): rows 32 rgi .. + 31 of the row block, the 64
+            // bytes of block blo + wave + 4 j in each, into a ring slot of 32
+            // rows x 64 bytes with 16-byte chunk c of row m in slot
+            // c ^ uswz(m): direct load q (of 2) covers rows 16 q .. + 15, four
+            // lanes per row, so each load reads whole 64-byte row pieces.
+            // Absent rows and tokens read the -inf chunk.  A cursor issues
+            // units in order; past the last unit it issues the same two loads
+            // of the -inf chunk into the slot just freed, so every wait allows
+            // the same count.
+            const uint16_t* usrc[2];
+            int utok[2], urow[2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int m = 16 * q + (lane >> 2);
+                const int c = (lane & 3) ^ uswz(m);
+                urow[q] = m;
+                utok[q] = kStreamSeg * (blo + wave) + 8 * c;
+                usrc[q] = F.U + ((size_t)(rb * kStreamRows + m) * G + k) * (size_t)V + utok[q];
+            }
+            const int rows_b = rows;
+            const size_t rg_step = (size_t)32 * G * (size_t)V;
+            int ci = 0, cj = 0, cs = 0;   // issue cursor: row group, block, ring slot
+            auto issue_next = [&]() {
+                char* dst = ring + (wave * NR + cs) * kPersistUnit;
+                const bool real = ci < nrg;
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const bool ok = real && 32 * ci + urow[q] < rows_b && utok[q] + 128 * cj < V;
+                    const uint16_t* src = usrc[q] + (size_t)ci * rg_step + 128 * cj;
+                    __builtin_amdgcn_global_load_lds(ok ? src : ninf, (lds_ptr_t)(dst + q * 1024), 16,
+                                                     0, 0);
+                }
+                if (++cj == nj) {
+                    cj = 0;
+                    ++ci;
+                }
+                if (++cs == NR) cs = 0;
+            };
+            if (nj > 0) {
+#pragma unroll
+                for (int u = 0; u < D; ++u) issue_next();
+                wait_vm<2 * D>();                      // this wave's E loads have landed
+            } else {
+                wait_vm<0>();
+            }
+            asm volatile("s_barrier" ::: "memory");    // ... and every wave's
+
+            // 3. units of this wave, row group major.
+            auto flush_run = [&](int rgi, float m, float s, int a) {
+                if (h == 0) {
+                    float* xs = xsum + ((size_t)wave * kStreamRows + 32 * rgi + n) * 3;
+                    xs[0] = m;
+                    xs[1] = s;
+                    xs[2] = __int_as_float(a);
+                }
+            };
+            // lane row of row group q present and conditioned: bit q
+            unsigned vrow = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int bl = 32 * q + n;
+                if (bl < rows && xprev[bl] >= 0) vrow |= 1u << q;
+            }
+            // summaries of unit (rgi, j) at offset 4 j bpad + 32 rgi from the lane's base
+            float* segm_l = P.segm + (size_t)(blo + wave) * bpad + rb * kStreamRows + n;
+            float* gs_l = P.gsums + ((size_t)(blo + wave) * bpad + rb * kStreamRows + n) * 4 + 2 * h;
+            auto store = [&](const Red& o, int off, int rgi) {
+                if (!((vrow >> rgi) & 1u)) return;
+                if constexpr (!GREEDY) coh_store_f32x2<true>(gs_l + (size_t)off * 4, o.g0, o.g1);
+                if (h == 0) coh_store<true>(segm_l + off, o.m);
+            };
+            float run_m = -INFINITY, run_s = 0.0f;
+            int run_a = INT_MAX;
+            auto absorb = [&](const Red& o) {
+                if constexpr (GREEDY) {
+                    run_a = (o.m > run_m || (o.m == run_m && o.am < run_a)) ? o.am : run_a;
+                    run_m = fmaxf(run_m, o.m);
+                } else {
+                    const float tot = pair_sum32(o.g0 + o.g1);
+                    const float nm = fmaxf(run_m, o.m);
+                    const float a = run_m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((run_m - nm) * sc);
+                    const float c = o.m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((o.m - nm) * sc);
+                    run_s = run_s * a + tot * c;
+                    run_m = nm;
+                }
+            };
+            auto flush_reset = [&](int rgi) {
+                flush_run(rgi, run_m, run_s, run_a);
+                run_m = -INFINITY;
+                run_s = 0.0f;
+                run_a = INT_MAX;
+            };
+
+            f32x16_t accp;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) accp[q] = 0.0f;
+            u32x4_t ufp[2] = {u32x4_t{0u, 0u, 0u, 0u}, u32x4_t{0u, 0u, 0u, 0u}};
+            Red redh{};
+            int tp = 0, offp = 0, rgp = 0, offh = 0, rgh = 0;
+            int done = 0;   // units consumed
+            int cu = 0;     // ring slot of the next unit
+            bf16x8_t e[NKS];
+            for (int rgi = 0; rgi < nrg; ++rgi) {
+                {   // B operand of row group rgi: row 32 rgi + n, chunk 2 ks + h
+                    const uint16_t* er = reinterpret_cast<const uint16_t*>(e_lds) + (32 * rgi + n) * R;
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks)
+                        e[ks] = *reinterpret_cast<const bf16x8_t*>(er + (((2 * ks + h) ^ (n & 7)) << 3));
+                }
+#pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    if (j < nj) {
+                        // This unit's MFMAs, each followed by a stage of the previous
+                        // unit's reduction; the stores and the running-summary update
+                        // of the unit before that, the next direct load and the read of
+                        // this unit's U go between them.  The order is fixed by
+                        // scheduling barriers.
+                        f32x16_t acc;
+#pragma unroll
+                        for (int q = 0; q < 16; ++q) acc[q] = 0.0f;
+                        Reducer Rd;
+                        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                        for (int ks = 0; ks < NKS; ++ks) {
+                            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j][ks], e[ks], acc, 0, 0, 0);
+#pragma unroll
+                            for (int st = ks * 15 / NKS; st < (ks + 1) * 15 / NKS; ++st)
+                                stage(Rd, accp, ufp, tp * kStreamSeg + 16 * h, st);
+                            if (ks == 0 && done >= 2) store(redh, offh, rgh);
+                            if (ks == 1) issue_next();
+                            if (ks == 2 && done >= 2) {
+                                absorb(redh);
+                                if (rgp != rgh) flush_reset(rgh);   // that unit closed its row group
+                            }
+                            if (ks == 3 * NKS / 4) {
+                                // U of this unit for the next reduction (the stages that
+                                // read the previous unit's U are done): D newer units are
+                                // in flight.
+                                wait_vm<2 * D>();
+                                const u32x4_t* us = reinterpret_cast<const u32x4_t*>(
+                                    ring + (wave * NR + cu) * kPersistUnit);
+                                ufp[0] = us[4 * n + ((2 * h) ^ uswz(n))];
+                                ufp[1] = us[4 * n + ((2 * h + 1) ^ uswz(n))];
+                            }
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                        if (++cu == NR) cu = 0;
+                        redh = finish(Rd);
+                        offh = offp;
+                        rgh = rgp;
+                        accp = acc;
+                        tp = blo + wave + 4 * j;
+                        offp = 4 * j * (int)bpad + 32 * rgi;
+                        rgp = rgi;
+                        ++done;
+                    }
+                }
+            }
+            if (done >= 2) {
+                store(redh, offh, rgh);
+                absorb(redh);
+                if (rgp != rgh) flush_reset(rgh);
+            }
+            if (done >= 1) {
+                const Red red = reduce(accp, ufp, tp * kStreamSeg + 16 * h);
+                absorb(red);
+                store(red, offp, rgp);
+                flush_reset(rgp);
+            }
+            wait_vm<0>();      // this wave's segment summaries are out (written through)
+            __syncthreads();
+            // 4. one summary per (share, row): merge the waves' runs, tagged with
+            // k + 1 in both words (read by the finalize without a grid barrier).
+            if (tid < rows && xprev[tid] >= 0) {
+                float m = -INFINITY, s = 0.0f;
+                int a = INT_MAX;
+                for (int w = 0; w < kPersistWaves; ++w) {
+                    if (wave_blocks(w) == 0) continue;
+                    const float* xs = xsum + ((size_t)w * kStreamRows + tid) * 3;
+                    const float m2 = xs[0], s2 = xs[1];
+                    const int a2 = __float_as_int(xs[2]);
+                    if constexpr (GREEDY) {
+                        merge_arg(m, a, m2, a2);
+                    } else {
+                        const float nm = fmaxf(m, m2);
+                        const float ca = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((m - nm) * sc);
+                        const float cb = m2 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((m2 - nm) * sc);
+                        s = s * ca + s2 * cb;
+                        m = nm;
+                    }
+                }
+                const uint64_t tag = (uint64_t)(k + 1) << 32;
+                uint64_t* e64 = reinterpret_cast<uint64_t*>(P.sup) +
+                                2 * ((size_t)g * bpad + rb * kStreamRows + tid);
+                coh_store<true>(e64, tag | __float_as_uint(m));
+                coh_store<true>(e64 + 1, tag | (GREEDY ? (uint32_t)a : __float_as_uint(s)));
+            }
+            __syncthreads();   // LDS (E, ring, xsum) is reused by the next row block
+        }
+        // 5. draw the tokens (each finalize waits for its row's shares).
+        for (int b = g + NG * wave; b < B; b += NG * kPersistWaves) {
+            int lane = lane0;
+            asm volatile("" : "+v"(lane));
+            const bool one = nrb == 1;   // E and the tokens of every row are in LDS
+            finalize_row_stream<true, true>(F, b, k, lane, one ? xprev : nullptr,
+                                      one ? reinterpret_cast<const uint16_t*>(e_lds) : nullptr);
+        }
+        if (k + 1 < G && !token_sync(P.bar, F.tflag, B, k + 1, nrb == 1 ? xprev : nullptr, &ok_s))
+            return;
+    }
+}
+
+// Blocks per wave held in registers (320 VGPRs of W2 operands) and U ring
+// slots per wave (LDS: E rows + rings + tokens + run summaries <= 160 KB).
+template <int NKS> struct PersistShape;
+template <> struct PersistShape<16> { static constexpr int NB = 5, NR = 11; };
+template <> struct PersistShape<8> { static constexpr int NB = 10, NR = 15; };
+template <> struct PersistShape<4> { static constexpr int NB = 20, NR = 16; };
+
+template <int NKS>
+static size_t persist_lds() {
+    return (size_t)kStreamRows * NKS * 16 * 2 + (size_t)kPersistWaves * PersistShape<NKS>::NR * kPersistUnit +
+           kStreamRows * sizeof(int) + (size_t)kPersistWaves * kStreamRows * 3 * sizeof(float);
+}
+
+static int persist_nks(int r) { return r == 256 ? 16 : (r == 128 ? 8 : (r == 64 ? 4 : 0)); }
+
+static int persist_nb(int r) {
+    switch (persist_nks(r)) {
+    case 16: return PersistShape<16>::NB;
+    case 8: return PersistShape<8>::NB;
+    case 4: return PersistShape<4>::NB;
+    default: return 0;
+    }
+}
+
+static bool g_persist_enabled = true;
+
+int persist_set_enabled(int enable) {
+    const int was = g_persist_enabled ? 1 : 0;
+    g_persist_enabled = enable != 0;
+    return was;
+}
+
+static int persist_device_ok() {
+    static int ok[64] = {0};   // 0 unknown, 1 yes, -1 no
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    if (dev < 0 || dev >= 64) return 0;
+    if (!ok[dev]) {
+        int coop = 0, cus = 0;
+        if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess)
+            coop = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            cus = 0;
+        ok[dev] = coop && cus > 0 ? cus : -1;
+    }
+    return ok[dev] > 0 ? ok[dev] : 0;
+}
+
+// Workgroups of the persistent draft: one per CU, at most one per 32-token
+// block and at most kMaxShares (the finalize reads four shares per lane).
+static int persist_grid(int V) {
+    const int cus = persist_device_ok();
+    const int nblk = (V + kStreamSeg - 1) / kStreamSeg;
+    return std::min(std::min(cus, nblk), kMaxShares);
+}
+
+bool draft_persists(const DraftArgs& a) {
+    if (!g_persist_enabled) return false;
+    if (!(a.head == kHeadMarkov && a.w_bf16 && a.u_bf16 && !a.q_logits && (a.V % 8) == 0 &&
+          persist_nks(a.r) != 0 && a.B > 0 && a.gamma > 0))
+        return false;
+    const int ng = persist_grid(a.V);
+    if (ng <= 0) return false;
+    const int nblk = (a.V + kStreamSeg - 1) / kStreamSeg;
+    return (nblk + ng - 1) / ng <= kPersistWaves * persist_nb(a.r);   // <= 20 blocks per share
+}
+
+template <int NKS>
+static hipError_t launch_persist(const PersistArgs& p, int ng, bool greedy, hipStream_t s) {
+    constexpr int NB = PersistShape<NKS>::NB, NR = PersistShape<NKS>::NR;
+    const void* fn = greedy ? reinterpret_cast<const void*>(&draft_persist<NKS, NB, NR, true>)
+                            : reinterpret_cast<const void*>(&draft_persist<NKS, NB, NR, false>);
+    const size_t lds = persist_lds<NKS>();
+    static bool attr_set = false;
+    if (!attr_set) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&draft_persist<NKS, NB, NR, true>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&draft_persist<NKS, NB, NR, false>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        (void)hipGetLastError();
+        attr_set = true;
+    }
+    PersistArgs arg = p;
+    void* args[] = {&arg};
+    return hipLaunchCooperativeKernel(fn, dim3(ng), dim3(kPersistWaves * 64), args,
+                                      (unsigned)lds, s);
+}
+
+hipError_t draft_persist_launch(const DraftArgs& a, unsigned* bar, hipStream_t s) {
+    const int ng = persist_grid(a.V);
+    if (ng <= 0 || !bar || !a.tflag || !a.W2T) return hipErrorInvalidValue;
+    PersistArgs p{};
+    FinStreamArgs& f = p.fin;
+    const int nblk = (a.V + kStreamSeg - 1) / kStreamSeg;
+    const int bpad = (a.B + kStreamRows - 1) / kStreamRows * kStreamRows;
+    f.sup = a.sup;
+    f.segm = reinterpret_cast<const float*>(a.stats);
+    f.gsums = a.gsums;
+    f.ws = ng;
+    f.nunit = nblk;
+    f.seg_mult = 1;
+    f.bpad = bpad;
+    f.x0 = a.x0;
+    f.tokens = a.tokens;
+    f.q_logZ = a.q_logZ;
+    f.q_tok = a.q_tok;
+    f.uniforms = a.uniforms;
+    f.seed = a.seed;
+    f.offset = a.offset;
+    f.gamma = a.gamma;
+    f.V = a.V;
+    f.invT = a.invT;
+    f.greedy = a.greedy;
+    f.U = static_cast<const uint16_t*>(a.U);
+    f.W1 = static_cast<const uint16_t*>(a.W1);
+    f.W2P = a.W2T;
+    f.r = a.r;
+    f.tflag = a.tflag;
+    f.abort_word = bar + kBarAbort;
+    f.poll_limit = kBarrierPolls;
+    p.segm = reinterpret_cast<float*>(a.stats);
+    p.gsums = a.gsums;
+    p.sup = a.sup;
+    p.bar = bar;
+    p.B = a.B;
+    p.gamma = a.gamma;
+    p.V = a.V;
+    p.nblk = nblk;
+    p.bpad = bpad;
+    const size_t ns = (size_t)ng * bpad;
+    const size_t nreset = std::max<size_t>(std::max(kBarWords, a.B), 2 * ns);
+    const unsigned nblk_reset = (unsigned)std::min<size_t>((nreset + 255) / 256, 1024);
+    hipLaunchKernelGGL(persist_bar_reset, dim3(nblk_reset), dim3(256), 0, s, bar, a.tflag, a.B,
+                       reinterpret_cast<uint64_t*>(a.sup), ns);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    switch (persist_nks(a.r)) {
+    case 16: return launch_persist<16>(p, ng, a.greedy != 0, s);
+    case 8: return launch_persist<8>(p, ng, a.greedy != 0, s);
+    case 4: return launch_persist<4>(p, ng, a.greedy != 0, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace specdec

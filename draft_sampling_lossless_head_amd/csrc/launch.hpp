@@ -82,6 +82,8 @@ struct DraftArgs {
     uint16_t* W2T_ws;    // workspace for that image when the caller passes none
     float* gsums;        // q-free draft: [B, nseg, 16] 8-token group sums
     SegStat* sup;        // streaming q-free draft: [shares][rows] range summaries
+    unsigned* bar;       // persistent draft: grid-barrier words (kPersistBarBytes)
+    uint64_t* tflag;     // persistent draft: per-row token words [B]
 };
 
 // Output modes of the bias tile kernel.
@@ -117,6 +119,11 @@ int draft_segment_len(const DraftArgs& a);
 int draft_max_segments(int V);
 hipError_t draft_tile_launch(const DraftArgs& a, int k, hipStream_t s);
 hipError_t draft_finalize_launch(const DraftArgs& a, int k, hipStream_t s);
+// Persistent q-free Markov draft: all positions in one cooperative launch.
+constexpr size_t kPersistBarBytes = 2048;   // abort word, -inf chunk, 256 arrival flags
+bool draft_persists(const DraftArgs& a);
+hipError_t draft_persist_launch(const DraftArgs& a, unsigned* bar, hipStream_t s);
+int persist_set_enabled(int enable);
 // W2 [r, V] bf16 -> packed image of w2p_bytes(r, V) bytes.
 hipError_t w2_pack_launch(const uint16_t* W2, uint16_t* W2P, int r, int V, hipStream_t s);
 // Recompute the logits of row b at position row_pos[b] (bit-identical to the

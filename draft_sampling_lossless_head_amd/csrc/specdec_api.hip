@@ -36,7 +36,7 @@ constexpr int kMaxV = 1 << 28;
 constexpr int kMaxDraftV = 4096 * 64;    // the finalize holds <= 16 segment summaries per thread
 
 struct DraftLayout {
-    size_t stats, gsums, sup, w2t, hproj, state, erows, total;
+    size_t stats, gsums, sup, bar, tflag, w2t, hproj, state, erows, total;
 };
 
 DraftLayout draft_layout(bool rnn, int B, int gamma, int V, int r) {
@@ -53,6 +53,10 @@ DraftLayout draft_layout(bool rnn, int B, int gamma, int V, int r) {
     off += align_up(bpad * ngs * sizeof(float));
     L.sup = off;   // streaming q-free draft: share summaries [256][bpad]
     off += align_up((size_t)256 * bpad * sizeof(SegStat));
+    L.bar = off;   // persistent draft: barrier words
+    off += align_up(kPersistBarBytes);
+    L.tflag = off;   // persistent draft: per-row token words
+    off += align_up(bpad * sizeof(uint64_t));
     L.w2t = off;   // packed bf16 W2 when the caller passes none
     off += align_up(w2p_bytes(r, V));
     if (rnn) {
@@ -167,6 +171,13 @@ spec_status_t run_draft(DraftArgs& a, void* stream) {
         prof_end(t, s);
         if (e != hipSuccess) return hip_fail(e, "rnn_hidden_proj");
     }
+    if (draft_persists(a)) {
+        t = prof_begin("draft_persist", s);
+        e = draft_persist_launch(a, a.bar, s);
+        prof_end(t, s);
+        if (e != hipSuccess) return hip_fail(e, "draft_persist");
+        return SPEC_OK;
+    }
     for (int k = 0; k < a.gamma; ++k) {
         if (a.head == kHeadRnn) {
             t = prof_begin("rnn_gates", s);
@@ -193,6 +204,8 @@ extern "C" {
 int spec_version(void) { return 100; }
 
 const char* spec_last_error(void) { return g_err.c_str(); }
+
+int spec_draft_set_persistent(int enable) { return persist_set_enabled(enable); }
 
 spec_status_t spec_philox_uniforms(uint64_t seed, uint32_t offset, uint32_t stream, int B, int K,
                                    float* out, void* stream_handle) {
@@ -249,6 +262,8 @@ spec_status_t spec_draft_sample_markov(const void* U, int U_dtype, const int32_t
     a.stats = reinterpret_cast<SegStat*>(w + L.stats);
     a.gsums = reinterpret_cast<float*>(w + L.gsums);
     a.sup = reinterpret_cast<SegStat*>(w + L.sup);
+    a.bar = reinterpret_cast<unsigned*>(w + L.bar);
+    a.tflag = reinterpret_cast<uint64_t*>(w + L.tflag);
     a.W2T = static_cast<const uint16_t*>(W2T);
     a.W2T_ws = reinterpret_cast<uint16_t*>(w + L.w2t);
     return run_draft(a, stream);
@@ -317,6 +332,8 @@ spec_status_t spec_draft_sample_rnn(const void* U, int U_dtype, const int32_t* x
     a.Erows = reinterpret_cast<uint16_t*>(w + L.erows);
     a.gsums = reinterpret_cast<float*>(w + L.gsums);
     a.sup = reinterpret_cast<SegStat*>(w + L.sup);
+    a.bar = reinterpret_cast<unsigned*>(w + L.bar);
+    a.tflag = reinterpret_cast<uint64_t*>(w + L.tflag);
     a.W2T = static_cast<const uint16_t*>(W2T);
     a.W2T_ws = reinterpret_cast<uint16_t*>(w + L.w2t);
     return run_draft(a, stream);

@@ -148,6 +148,18 @@ size_t spec_pack_w2_bytes(int r, int V);
 spec_status_t spec_pack_w2(const void *W2, void *W2T, int r, int V, void *stream);
 
 /*
+ * Engine of the q-free Markov draft (bf16 U and weights, q_logits == NULL).
+ * 1 (the default): where the shape allows it (V % 8 == 0, r in {64, 128,
+ * 256}, the device's share of packed W2 fitting in registers: V <= 163840
+ * at r = 256 on 256 CUs, twice that per halving of r), every position runs in
+ * one cooperative launch that keeps W2 on chip and synchronises the
+ * workgroups between positions with grid barriers.  0: two launches per
+ * position (streaming tile + finalize).  Both give the same draws up to the
+ * rounding of the sums.  Process-wide; returns the previous setting.
+ */
+int spec_draft_set_persistent(int enable);
+
+/*
  * ---------------------------------------------------------------------------
  * Draft, RNN head  [DSpark §1.2, RNN-head equation]
  * ---------------------------------------------------------------------------
@@ -256,7 +268,8 @@ spec_status_t spec_verify_markov(
  * Kernel timing (benchmarking aid; not needed for correct use)
  * ---------------------------------------------------------------------------
  * spec_profile_enable(name) starts a fresh record: from then on every launch
- * of the kernel `name` ("draft_tile", "draft_finalize", "rnn_hidden_proj",
+ * of the kernel `name` ("draft_tile", "draft_tile_qfree", "draft_finalize",
+ * "draft_persist", "rnn_hidden_proj",
  * "rnn_gates", "w2_transpose", "verify_rows_p", "verify_rows_q",
  * "verify_decide", "verify_residual_rows", "verify_final_partials",
  * "verify_final_draw", or "*" for all) is bracketed

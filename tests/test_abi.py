@@ -35,7 +35,7 @@ def test_header_declares_the_boundary():
               "spec_draft_markov_workspace_size", "spec_draft_rnn_workspace_size",
               "spec_verify_workspace_size", "spec_philox_uniforms", "spec_last_error",
               "spec_version", "spec_pack_w2", "spec_pack_w2_bytes", "spec_verify_markov",
-              "spec_verify_markov_workspace_size"):
+              "spec_verify_markov_workspace_size", "spec_draft_set_persistent"):
         assert n in names
 
 
@@ -184,3 +184,11 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(api, "_LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(api.SpecError):
         api.load_library()
+
+
+def test_draft_engine_switch(lib):
+    """The draft engine setting is process-wide and returns the previous value."""
+    was = lib.spec_draft_set_persistent(0)
+    assert was in (0, 1)
+    assert lib.spec_draft_set_persistent(1) == 0
+    assert lib.spec_draft_set_persistent(was) == 1

@@ -42,19 +42,50 @@ DRAFT_CASES = [
     (100, 3, 40000, 128, "bf16", 1.0),  # three items per workgroup: full pipeline
     (200, 2, 20008, 64, "bf16", 0.9),   # row block changes inside a workgroup; 40-token tail
     (80, 3, 16384, 256, "bf16", 0.0),   # greedy
+    # persistent draft (bf16 U, V % 8 == 0, r in {64, 128, 256}, W2 share fits):
+    (1, 3, 5000, 64, "bf16", 1.0),      # one row: 31 absent rows in its group
+    (33, 2, 8, 64, "bf16", 1.0),        # V = 8: one block, one workgroup
+    (5, 2, 1000, 128, "bf16", 0.7),     # 32 blocks: one per workgroup, three idle waves
+    (4, 2, 163840, 256, "bf16", 1.0),   # 20 blocks per workgroup: all register blocks in use
+    (3, 1, 163848, 256, "bf16", 1.0),   # one block more than fits: per-position kernels
 ]
 
 
-@pytest.mark.parametrize("B,gamma,V,r,udt,T", DRAFT_CASES)
-def test_qfree_draft_parity(orc, B, gamma, V, r, udt, T):
+def persist_eligible(B, gamma, V, r, udt):
+    """Shapes the library runs as one persistent launch (256 CUs: at most
+    20 / 40 / 80 blocks of 32 tokens per workgroup for r = 256 / 128 / 64)."""
+    if udt != "bf16" or V % 8 or r not in (64, 128, 256) or B < 1 or gamma < 1:
+        return False
+    nblk = (V + 31) // 32
+    ng = min(256, nblk)
+    return -(-nblk // ng) <= 4 * {256: 5, 128: 10, 64: 20}[r]
+
+
+@pytest.fixture(params=["persistent", "per_position"])
+def engine(request):
     sd = require_gpu()
-    note(f"q-free draft B={B} gamma={gamma} V={V} r={r} U={udt} T={T}")
+    was = sd.spec_draft_set_persistent(request.param == "persistent")
+    yield request.param
+    sd.spec_draft_set_persistent(was)
+
+
+@pytest.mark.parametrize("B,gamma,V,r,udt,T", DRAFT_CASES)
+def test_qfree_draft_parity(orc, engine, B, gamma, V, r, udt, T):
+    sd = require_gpu()
+    eligible = persist_eligible(B, gamma, V, r, udt)
+    if engine == "per_position" and not eligible:
+        pytest.skip("same kernels as the persistent engine for this shape")
+    note(f"q-free draft B={B} gamma={gamma} V={V} r={r} U={udt} T={T} engine={engine}")
     wl = workloads.make_markov(_cfg("markov-32k-b32", udt, 300 + B + V, w_std=0.3), B=B,
                                gamma=gamma, V=V, r=r)
     seed, offset = 17, 5
+    sd.spec_profile_enable("draft_persist")
     g = host(sd.spec_draft_sample_markov(dev(wl["U"], udt), dev(wl["x0"]), dev(wl["W1"], "bf16"),
                                          dev(wl["W2"], "bf16"), T, q_free=True, seed=seed,
                                          offset=offset))
+    launches, _ = sd.spec_profile_read()
+    sd.spec_profile_enable(None)
+    assert launches == (1 if engine == "persistent" and eligible else 0)
     assert "q_logits" not in g
     W1, W2 = _weights(wl)
     u = orc.draft_uniforms(seed, offset, B, gamma)
@@ -96,10 +127,11 @@ def test_pack_w2_layout(r, V):
     assert np.array_equal(got, packed_image(W2, r, V))
 
 
-def test_qfree_draft_full_size_sampled(orc):
-    """B = 128, gamma = 16, V = 151936, r = 256, bf16: the streaming tile at the
-    size it is timed at; four requests are checked against the oracle."""
+def test_qfree_draft_full_size_sampled(orc, engine):
+    """B = 128, gamma = 16, V = 151936, r = 256, bf16: both draft engines at the
+    size they are timed at; four requests are checked against the oracle."""
     sd = require_gpu()
+    note(f"full-size q-free draft engine={engine}")
     B, gamma, V, r = 128, 16, 151936, 256
     sample = [0, 45, 96, 127]
     cfg = dict(workloads.CONFIGS["markov-152k-b128"])
@@ -146,6 +178,33 @@ def test_qfree_draft_packed_w2_and_uniforms(orc):
         o = orc.draft_markov(Ub, W1, W2, wl["x0"][i], 1.0, ui)
         compare.compare_draft_request(o, Ub, {k: v[i] for k, v in a.items()}, 1.0, ui, f"b={i}",
                                       tally, check_logits=False)
+    note(f"  {tally.as_dict()}")
+
+
+def test_qfree_draft_invalid_anchor_persistent(orc):
+    """An anchor outside [0, V) in the persistent engine: that request gets -1
+    tokens and NaN normalisers; the other requests still match the oracle."""
+    sd = require_gpu()
+    B, gamma, V, r = 40, 3, 2000, 64
+    wl = workloads.make_markov(_cfg("markov-32k-b32", "bf16", 6, w_std=0.3), B=B, gamma=gamma,
+                               V=V, r=r)
+    x0 = wl["x0"].copy()
+    x0[7] = V
+    x0[33] = -2
+    g = host(sd.spec_draft_sample_markov(dev(wl["U"], "bf16"), dev(x0), dev(wl["W1"], "bf16"),
+                                         dev(wl["W2"], "bf16"), 1.0, q_free=True, seed=4))
+    for b in (7, 33):
+        assert np.all(g["tokens"][b] == -1) and np.all(np.isnan(g["q_logZ"][b]))
+    W1, W2 = _weights(wl)
+    u = orc.draft_uniforms(4, 0, B, gamma)
+    tally = compare.Tally()
+    for b in range(B):
+        if b in (7, 33):
+            continue
+        Ub = workloads.as_f64(wl["U"][b], "bf16")
+        o = orc.draft_markov(Ub, W1, W2, x0[b], 1.0, u[b])
+        compare.compare_draft_request(o, Ub, {k: v[b] for k, v in g.items()}, 1.0, u[b],
+                                      f"b={b}", tally, check_logits=False)
     note(f"  {tally.as_dict()}")
 
 
