@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <climits>
+
 namespace specdec {
 
 constexpr int kWave = 64;
@@ -107,14 +109,36 @@ __device__ __forceinline__ float wave_max_f32(float x) {
     return x;
 }
 
-// Inclusive prefix sum across the wave (lane order).
+// A 64-bit value moved through a DPP lane pattern, both halves with the same
+// control; lanes whose source is outside the pattern (or whose row is masked
+// off) read 0.
+template <int CTRL, int ROWM = 0xF, int BANKM = 0xF, bool BC = true>
+__device__ __forceinline__ double dpp_f64(double x) {
+    const uint64_t u = (uint64_t)__double_as_longlong(x);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, ROWM, BANKM, BC);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, ROWM, BANKM, BC);
+    return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143, kDppWaveShr1 = 0x138;
+
+__device__ __forceinline__ double readlane_f64(double x, int l) {
+    const uint64_t u = (uint64_t)__double_as_longlong(x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Inclusive prefix sum across the wave (lane order), Hillis-Steele on DPP:
+// shifts by 1, 2, 4 and 8 inside each row of 16 lanes, then the total of row
+// 0 into rows 1 and 3 and the total of rows 0-1 into rows 2 and 3.
 __device__ __forceinline__ double wave_inclusive_scan_f64(double x) {
-    const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        double y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
+    x += dpp_f64<kDppRowShr1>(x);
+    x += dpp_f64<kDppRowShr2>(x);
+    x += dpp_f64<kDppRowShr4>(x);
+    x += dpp_f64<kDppRowShr8>(x);
+    x += dpp_f64<kDppRowBcast15, 0xA, 0xF, false>(x);
+    x += dpp_f64<kDppRowBcast31, 0xC, 0xF, false>(x);
     return x;
 }
 
@@ -155,6 +179,33 @@ __device__ __forceinline__ int row16_min(int x) {
     x = min(x, dpp_mov<kDppXor2>(x));
     x = min(x, dpp_mov<kDppHalfMirror>(x));
     return min(x, dpp_mov<kDppMirror>(x));
+}
+
+// Sum over each group of 8 lanes (8i .. 8i + 7); every lane of the group ends
+// with it.
+__device__ __forceinline__ float row8_sum(float x) {
+    x += dpp_mov<kDppXor1>(x);
+    x += dpp_mov<kDppXor2>(x);
+    return x + dpp_mov<kDppHalfMirror>(x);
+}
+
+// Wave-wide max and (max, lowest index among the lanes holding it), uniform.
+__device__ __forceinline__ float readlane_f32(float x, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+__device__ __forceinline__ float wave_max_f32_dpp(float x) {
+    x = row16_max(x);
+    return fmaxf(fmaxf(readlane_f32(x, 0), readlane_f32(x, 16)),
+                 fmaxf(readlane_f32(x, 32), readlane_f32(x, 48)));
+}
+__device__ __forceinline__ void wave_argmax_dpp(float& m, int& idx) {
+    const float M = wave_max_f32_dpp(m);
+    int cand = m == M ? idx : INT_MAX;
+    cand = row16_min(cand);
+    const int c = min(min(__builtin_amdgcn_readlane(cand, 0), __builtin_amdgcn_readlane(cand, 16)),
+                      min(__builtin_amdgcn_readlane(cand, 32), __builtin_amdgcn_readlane(cand, 48)));
+    m = M;
+    idx = c;
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -261,14 +312,12 @@ __device__ __forceinline__ void coh_store_seg(SegStat* p, const SegStat& x) {
 // interval [excl, incl) holds thr and thr - excl; past the end (rounding) the
 // last lane with weight and +inf.  Neighbouring intervals share end points.
 __device__ __forceinline__ int wave_pick(double w, double thr, double& rem) {
-    const int lane = threadIdx.x & (kWave - 1);
     const double incl = wave_inclusive_scan_f64(w);
-    double excl = __shfl_up(incl, 1);
-    if (lane == 0) excl = 0.0;
+    const double excl = dpp_f64<kDppWaveShr1>(incl);   // lane 0 reads 0
     unsigned long long hit = __ballot(w > 0.0 && thr >= excl && thr < incl);
     if (hit) {
         const int l = __ffsll((long long)hit) - 1;
-        rem = thr - __shfl(excl, l);
+        rem = thr - readlane_f64(excl, l);
         return l;
     }
     const unsigned long long pos = __ballot(w > 0.0);

@@ -156,12 +156,8 @@ __device__ __forceinline__ void finalize_row_stream(const FinStreamArgs& A, int 
     int AM = si[0];
 #pragma unroll
     for (int q = 1; q < 4; ++q) merge_arg(M, AM, sm[q], si[q]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const float m2 = __shfl_xor(M, off);
-        const int i2 = __shfl_xor(AM, off);
-        merge_arg(M, AM, m2, i2);
-    }
+    if (A.greedy) wave_argmax_dpp(M, AM);   // uniform from here on
+    else M = wave_max_f32_dpp(M);
     if (A.greedy || M == -INFINITY) {
         if (lane == 0) {
             if (A.q_logZ) A.q_logZ[outi] = M == -INFINITY ? NAN : M;
@@ -177,7 +173,7 @@ __device__ __forceinline__ void finalize_row_stream(const FinStreamArgs& A, int 
         w[q] = sm[q] != -INFINITY ? (double)ss[q] * (double)__expf((sm[q] - M) * invT) : 0.0;
         lsum += w[q];
     }
-    const double Z = __shfl(wave_inclusive_scan_f64(lsum), kWave - 1);
+    const double Z = readlane_f64(wave_inclusive_scan_f64(lsum), kWave - 1);
     const double thr = (double)u * Z;
     double rem;
     const int ol = wave_pick(lsum, thr, rem);
@@ -207,8 +203,8 @@ __device__ __forceinline__ void finalize_row_stream(const FinStreamArgs& A, int 
         }
         qsel = found;
     }
-    const int sh = 4 * ol + __shfl(qsel, ol);
-    const double rem1 = __shfl(qrem, ol);
+    const int sh = 4 * ol + __builtin_amdgcn_readlane(qsel, ol);
+    const double rem1 = readlane_f64(qrem, ol);
 
     // 2) the share's 32-token segments and their group sums, one read.
     const int s0 = A.seg_mult * (int)((long long)sh * A.nunit / A.ws);
@@ -228,12 +224,12 @@ __device__ __forceinline__ void finalize_row_stream(const FinStreamArgs& A, int 
     const int sl_seg = wave_pick(ys * ysc, rem1, rem2);
     const int seg = s0 + sl_seg;
     // the chosen segment's 4 group weights to lanes 0..3
-    const double gscale = __shfl(ysc, sl_seg);
+    const double gscale = readlane_f64(ysc, sl_seg);
     const float gv[4] = {g4.x, g4.y, g4.z, g4.w};
     float mine = 0.0f;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-        const float v = __shfl(gv[g], sl_seg);
+        const float v = readlane_f32(gv[g], sl_seg);
         if (lane == g) mine = v;
     }
     double grem;
@@ -272,16 +268,23 @@ __device__ __forceinline__ void finalize_row_stream(const FinStreamArgs& A, int 
         }
         ut = bf16_bits_to_float(A.U[outi * (size_t)V + vt]);
     }
-    part += __shfl_xor(part, 1);
-    part += __shfl_xor(part, 2);
-    part += __shfl_xor(part, 4);
+    part = row8_sum(part);
     const float lt = ut + part;
     const float wtk = vt < V ? __expf((lt - M) * invT) : 0.0f;
-    const float w8 = __shfl(wtk, (lane & 7) * 8);
-    const float l8 = __shfl(lt, (lane & 7) * 8);
+    // token t's weight and logit to lane t
+    float w8 = 0.0f, l8 = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const float wq = readlane_f32(wtk, 8 * q);
+        const float lq = readlane_f32(lt, 8 * q);
+        if (lane == q) {
+            w8 = wq;
+            l8 = lq;
+        }
+    }
     double trem;
     const int tsel = wave_pick(lane < 8 ? (double)w8 : 0.0, grem, trem);
-    const float lsel = __shfl(l8, tsel);
+    const float lsel = readlane_f32(l8, tsel);
     if (lane == 0) {
         if (A.q_logZ) A.q_logZ[outi] = (float)((double)M * (double)invT + (double)__logf((float)Z));
         if (A.q_tok) A.q_tok[outi] = (float)((double)__expf((lsel - M) * invT) / Z);
