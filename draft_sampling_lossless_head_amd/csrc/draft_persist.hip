@@ -299,20 +299,25 @@ void draft_persist(PersistArgs P) {
             }
             const int rows_b = rows;
             const size_t rg_step = (size_t)32 * G * (size_t)V;
-            int ci = 0, cj = 0, cs = 0;   // issue cursor: row group, block, ring slot
+            // issue cursor: row group, block, ring slot, and the U offset of
+            // (ci, cj) from the lane's unit-0 address (ci * rg_step + 128 cj)
+            int ci = 0, cj = 0, cs = 0;
+            size_t coff = 0;
             auto issue_next = [&]() {
                 char* dst = ring + (wave * NR + cs) * kPersistUnit;
-                const bool real = ci < nrg;
+                const int rlim = rows_b - 32 * ci;   // rows of the group present (<= 0 past the last)
+                const int vlim = V - 128 * cj;
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
-                    const bool ok = real && 32 * ci + urow[q] < rows_b && utok[q] + 128 * cj < V;
-                    const uint16_t* src = usrc[q] + (size_t)ci * rg_step + 128 * cj;
-                    __builtin_amdgcn_global_load_lds(ok ? src : ninf, (lds_ptr_t)(dst + q * 1024), 16,
-                                                     0, 0);
+                    const bool ok = urow[q] < rlim && utok[q] < vlim;
+                    __builtin_amdgcn_global_load_lds(ok ? usrc[q] + coff : ninf,
+                                                     (lds_ptr_t)(dst + q * 1024), 16, 0, 0);
                 }
+                coff += 128;
                 if (++cj == nj) {
                     cj = 0;
                     ++ci;
+                    coff += rg_step - (size_t)128 * nj;
                 }
                 if (++cs == NR) cs = 0;
             };
@@ -334,20 +339,15 @@ void draft_persist(PersistArgs P) {
                     xs[2] = __int_as_float(a);
                 }
             };
-            // lane row of row group q present and conditioned: bit q
-            unsigned vrow = 0;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int bl = 32 * q + n;
-                if (bl < rows && xprev[bl] >= 0) vrow |= 1u << q;
-            }
             // summaries of unit (rgi, j) at offset 4 j bpad + 32 rgi from the lane's base
             float* segm_l = P.segm + (size_t)(blo + wave) * bpad + rb * kStreamRows + n;
             float* gs_l = P.gsums + ((size_t)(blo + wave) * bpad + rb * kStreamRows + n) * 4 + 2 * h;
-            auto store = [&](const Red& o, int off, int rgi) {
-                if (!((vrow >> rgi) & 1u)) return;
+            // Every lane stores: rows without a valid conditioning token or past
+            // B hold values nothing reads, and both halves of a row hold the
+            // same block max.
+            auto store = [&](const Red& o, int off) {
                 if constexpr (!GREEDY) coh_store_f32x2<true>(gs_l + (size_t)off * 4, o.g0, o.g1);
-                if (h == 0) coh_store<true>(segm_l + off, o.m);
+                coh_store<true>(segm_l + off, o.m);
             };
             float run_m = -INFINITY, run_s = 0.0f;
             int run_a = INT_MAX;
@@ -371,11 +371,19 @@ void draft_persist(PersistArgs P) {
                 run_a = INT_MAX;
             };
 
+            // The pipeline starts from a previous unit whose logits are all -inf
+            // (U = -inf, zero accumulators): it reduces to an empty record (max
+            // -inf, sums 0) that stores into the first unit's slots, overwritten
+            // later, and leaves the running summary unchanged.
             f32x16_t accp;
 #pragma unroll
             for (int q = 0; q < 16; ++q) accp[q] = 0.0f;
-            u32x4_t ufp[2] = {u32x4_t{0u, 0u, 0u, 0u}, u32x4_t{0u, 0u, 0u, 0u}};
-            Red redh{};
+            const u32x4_t ninf4 = u32x4_t{0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u};
+            u32x4_t ufp[2] = {ninf4, ninf4};
+            Red redh;
+            redh.m = -INFINITY;
+            redh.g0 = redh.g1 = 0.0f;
+            redh.am = INT_MAX;
             int tp = 0, offp = 0, rgp = 0, offh = 0, rgh = 0;
             int done = 0;   // units consumed
             int cu = 0;     // ring slot of the next unit
@@ -406,11 +414,12 @@ void draft_persist(PersistArgs P) {
 #pragma unroll
                             for (int st = ks * 15 / NKS; st < (ks + 1) * 15 / NKS; ++st)
                                 stage(Rd, accp, ufp, tp * kStreamSeg + 16 * h, st);
-                            if (ks == 0 && done >= 2) store(redh, offh, rgh);
+                            if (ks == 0) store(redh, offh);
                             if (ks == 1) issue_next();
-                            if (ks == 2 && done >= 2) {
+                            if (ks == 2) {
                                 absorb(redh);
-                                if (rgp != rgh) flush_reset(rgh);   // that unit closed its row group
+                                // the unit after it opened a row group (j - 1 == 0): flush
+                                if (j == 1 || nj == 1) flush_reset(rgh);
                             }
                             if (ks == 3 * NKS / 4) {
                                 // U of this unit for the next reduction (the stages that
@@ -436,15 +445,13 @@ void draft_persist(PersistArgs P) {
                     }
                 }
             }
-            if (done >= 2) {
-                store(redh, offh, rgh);
-                absorb(redh);
-                if (rgp != rgh) flush_reset(rgh);
-            }
             if (done >= 1) {
+                store(redh, offh);
+                absorb(redh);
+                if (nj == 1 || done == 1) flush_reset(rgh);
                 const Red red = reduce(accp, ufp, tp * kStreamSeg + 16 * h);
                 absorb(red);
-                store(red, offp, rgp);
+                store(red, offp);
                 flush_reset(rgp);
             }
             wait_vm<0>();      // this wave's segment summaries are out (written through)
