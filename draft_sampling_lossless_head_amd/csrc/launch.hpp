@@ -132,7 +132,8 @@ hipError_t residual_rows_launch(const TileParams& p, bool u_bf16, hipStream_t s)
 hipError_t rnn_hidden_proj_launch(const DraftArgs& a, hipStream_t s);
 hipError_t rnn_gates_launch(const DraftArgs& a, int k, hipStream_t s);
 
-// Per (request, row slot) summary written by the verify streaming pass.
+// Per (request, row slot, segment) summary written by the verify streaming
+// pass; s is 0 for greedy rows.
 struct alignas(16) RowStat {
     float m;        // max logit of the row
     float s;        // sum exp((l - m) / T)
@@ -175,7 +176,8 @@ struct VerifyArgs {
     int32_t* row_pos;           // [B] rejected position per request (-1 none)
     int q_single_row;           // Q holds one row per request (row b)
     // workspace carve-outs
-    RowStat* rows;              // [B, 2 * gamma_max + 1]
+    RowStat* rows;              // [B, 2 * gamma_max + 1, row_segs]
+    int row_segs;               // segments per row (verify_row_segs)
     FinalInfo* fin;             // [B]
     double* chunk_sums;         // [B, nchunk]
 };
@@ -205,6 +207,7 @@ bool resid_streams(int B, int V, int r);
 hipError_t verify_resid_launch(const ResidArgs& A, hipStream_t s);
 
 int verify_num_chunks(int V);
+int verify_row_segs(int B, int gamma_max, int V);
 hipError_t verify_launch(const VerifyArgs& a, hipStream_t s);
 // The three phases, for callers that insert work between them.
 hipError_t verify_rows_decide_launch(const VerifyArgs& a, hipStream_t s);

@@ -81,7 +81,7 @@ VerifyLayout verify_layout(int B, int gamma_max, int V, int markov_r = 0) {
     VerifyLayout L{};
     size_t off = 0;
     L.rows = off;
-    off += align_up((size_t)B * (2 * gamma_max + 1) * sizeof(RowStat));
+    off += align_up((size_t)B * (2 * gamma_max + 1) * verify_row_segs(B, gamma_max, V) * sizeof(RowStat));
     L.fin = off;
     off += align_up((size_t)B * sizeof(FinalInfo));
     L.chunks = off;
@@ -388,6 +388,7 @@ spec_status_t spec_verify(const void* P, int p_dtype, const void* Q, int q_dtype
     a.q_logZ = q_logZ;
     a.accept_prob = accept_prob;
     a.rows = reinterpret_cast<RowStat*>(w + L.rows);
+    a.row_segs = verify_row_segs(B, gamma_max, V);
     a.fin = reinterpret_cast<FinalInfo*>(w + L.fin);
     a.chunk_sums = reinterpret_cast<double*>(w + L.chunks);
     hipError_t e = verify_launch(a, static_cast<hipStream_t>(stream));
@@ -470,6 +471,7 @@ spec_status_t spec_verify_markov(const void* P, int p_dtype, const void* U, int 
     a.qlogz = q_logZ;
     a.row_pos = reinterpret_cast<int32_t*>(w + L.rowpos);
     a.rows = reinterpret_cast<RowStat*>(w + L.rows);
+    a.row_segs = verify_row_segs(B, gamma_max, V);
     a.fin = reinterpret_cast<FinalInfo*>(w + L.fin);
     a.chunk_sums = reinterpret_cast<double*>(w + L.chunks);
     hipError_t e = verify_rows_decide_launch(a, s);

@@ -1,11 +1,13 @@
 // Lossless verification kernels (VESSL "Speculative Decoding Part 1",
 // sections "알고리즘" and "수락 규칙").  Four launches on the caller's stream:
 //
-//   verify_rows (x2)      one workgroup per target row p_k (k <= L) and per
-//                         draft row q_k (k < L): one pass over the row with
-//                         16-byte loads -> max, sum exp((l - max)/T), argmax,
-//                         and the logit at the draft token.
-//   verify_decide         one thread per request: normalisers, the ratio test
+//   verify_rows (x2)      one workgroup per segment of each target row p_k
+//                         (k <= L) and draft row q_k (k < L): one pass with
+//                         16-byte loads -> max and sum exp((l - max)/T)
+//                         (sampling) or max and argmax (greedy), plus the
+//                         logit at the draft token.
+//   verify_decide         one thread per request: merges the segments,
+//                         normalisers, the ratio test
 //                         u * q(x) < p(x) at every position, first rejection
 //                         n, emitted draft tokens, diagnostics.
 //   verify_final_partials one workgroup per (request, 4096-token chunk) of the
@@ -14,7 +16,10 @@
 //   verify_final_draw     one workgroup per request: inverse CDF over the chunk
 //                         sums, then over the chosen chunk -> final token.
 // The final-draw pair is skipped for T == 0 (argmax of p_n, set by decide).
+#include <algorithm>
+#include <cfloat>
 #include <climits>
+#include <type_traits>
 
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -29,7 +34,20 @@ constexpr int kChunk = 4096;          // tokens per chunk of the final draw
 constexpr int kPerThread = kChunk / 256;
 static_assert(kPerThread == 16, "the final draw works on runs of 16 tokens per thread");
 
+// Cache policy of a streaming buffer load: non-temporal.
+constexpr int kBufNontemporal = 2;
+
 int verify_num_chunks(int V) { return (V + kChunk - 1) / kChunk; }
+
+// Segments per verified row: enough workgroups to fill the chip several
+// times over (2176 whole rows against 2048 resident workgroups would leave a
+// second, nearly empty wave of rows), each segment at least 4096 tokens.
+int verify_row_segs(int B, int gamma_max, int V) {
+    const int64_t rows = std::max<int64_t>(1, (int64_t)B * (gamma_max + 1));
+    const int64_t want = (8192 + rows - 1) / rows;
+    const int64_t cap = std::max(1, std::min(16, V / 4096));
+    return (int)std::max<int64_t>(1, std::min(want, cap));
+}
 
 __device__ __forceinline__ int64_t p_row(const VerifyArgs& a, int b, int k) {
     return (a.p_row_off ? a.p_row_off[b] : (int64_t)b * (a.gamma_max + 1)) + k;
@@ -44,10 +62,9 @@ __device__ __forceinline__ int request_len(const VerifyArgs& a, int b) {
     return a.lens ? a.lens[b] : a.gamma_max;
 }
 
-// Online update of (m, s, argmax) with n consecutive values starting at v0.
-template <int N, bool GREEDY>
-__device__ __forceinline__ void absorb(const float (&x)[N], int v0, float& m, float& s, int& idx,
-                                       float invT) {
+// Greedy rows: online (max, argmax) over n consecutive values from v0.
+template <int N>
+__device__ __forceinline__ void absorb_arg(const float (&x)[N], int v0, float& m, int& idx) {
     float lm = x[0];
     int li = 0;
 #pragma unroll
@@ -57,94 +74,246 @@ __device__ __forceinline__ void absorb(const float (&x)[N], int v0, float& m, fl
             li = t;
         }
     if (lm > m) {
-        if (!GREEDY) s *= __expf((m - lm) * invT);
         m = lm;
         idx = v0 + li;
     }
-    if (!GREEDY && m != -INFINITY) {
+}
+
+// Sampling rows: running max m, its scaled copy mc = max(m c, -FLT_MAX) with
+// c = log2(e) / T, and two partial sums of 2^(x c - mc).  A run of N values
+// costs one max tree (v_max3), one rescale, and per value one fma, one exp2
+// and one add; no argmax is kept (sampling never reads it).  The clamp keeps
+// an all -inf prefix NaN-free: its terms are 2^(-inf) = 0.
+struct SampStat {
+    float m, mc, s0, s1;
+};
+
+template <int N>
+__device__ __forceinline__ void absorb_samp(const float (&x)[N], SampStat& st, float c) {
+    float lm = st.m;
 #pragma unroll
-        for (int t = 0; t < N; ++t) s += __expf((x[t] - m) * invT);
+    for (int t = 0; t < N; ++t) lm = fmaxf(lm, x[t]);
+    const float mc = fmaxf(lm * c, -FLT_MAX);
+    const float r = __builtin_amdgcn_exp2f(st.mc - mc);
+    st.s0 *= r;
+    st.s1 *= r;
+    st.m = lm;
+    st.mc = mc;
+#pragma unroll
+    for (int t = 0; t < N; ++t) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(x[t], c, -mc));
+        if (t & 1) st.s1 += e;
+        else st.s0 += e;
     }
 }
 
+// sum exp((x - m) / T) against the exact m: the terms were taken against the
+// rounded mc, off by the factor 2^(m c - mc), whose exponent fma gives exactly.
+__device__ __forceinline__ float samp_sum(const SampStat& st, float c) {
+    const float s = st.s0 + st.s1;
+    return st.m == -INFINITY ? s : s * __builtin_amdgcn_exp2f(fmaf(-st.m, c, st.mc));
+}
+
+__device__ __forceinline__ void bf16x8_to_f32(const u32x4_t& w, float* x) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        x[2 * h] = __uint_as_float(w[h] << 16);
+        x[2 * h + 1] = __uint_as_float(w[h] & 0xFFFF0000u);
+    }
+}
+
+// Range-checked view of nbytes at base (raw buffer, no stride): a 16-byte
+// load at an offset at or past nbytes returns zeros and touches no memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* base, int64_t nbytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
+                                             (int)(nbytes > 0 ? nbytes : 0), 0x00020000);
+}
+
+template <typename Vec>
+__device__ __forceinline__ Vec load16_nt(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(Vec, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kBufNontemporal));
+}
+
+// Words that decode to -inf in every lane of a vector.
+template <bool BF16>
+__device__ __forceinline__ uint32_t neg_inf_word() {
+    return BF16 ? 0xFF80FF80u : 0xFF800000u;
+}
+
+// Runs of four vectors at j, j + 256, j + 512, j + 768 of the segment's n
+// vectors at rv, in two ping-pong buffers so one run's loads are in flight
+// while the other is absorbed.  Vector u of a run goes through its own view
+// starting 256 u vectors in, so one 32-bit offset serves the four loads and
+// a load past the end reads zeros instead of memory; the last run, partial
+// or not, has such vectors replaced by -inf (no weight, never the max).
+// Every load of the loop is unconditional: a load under a branch, or one
+// whose only use lies past a loop exit, would be waited for together with
+// the current run.
+template <bool BF16, typename Vec, typename F>
+__device__ __forceinline__ void scan_runs(const Vec* rv, int n, int j, int vid0, F& f) {
+    if (j >= n) return;
+    __amdgpu_buffer_rsrc_t r[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) r[u] = range_rsrc(rv + u * 256, (int64_t)(n - u * 256) * 16);
+    const int nr = (n - j + 1023) / 1024;   // runs, the last possibly partial
+    Vec A[4], Bv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) A[u] = load16_nt<Vec>(r[u], j * 16);
+    int q = 0;
+    for (; q + 2 < nr; q += 2) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) Bv[u] = load16_nt<Vec>(r[u], (j + 1024) * 16);
+        __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the run
+        f.template run<4>(A, vid0 + j);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) A[u] = load16_nt<Vec>(r[u], (j + 2048) * 16);
+        __builtin_amdgcn_sched_barrier(0);
+        f.template run<4>(Bv, vid0 + j + 1024);
+        j += 2048;
+    }
+    auto last = [&](Vec (&w)[4], int jj) {
+        using W = uint32_t __attribute__((ext_vector_type(4)));
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (jj + u * 256 >= n) {
+                const uint32_t ni = neg_inf_word<BF16>();
+                w[u] = __builtin_bit_cast(Vec, W{ni, ni, ni, ni});
+            }
+        }
+        f.template run<4>(w, vid0 + jj);
+    };
+    if (nr - q == 2) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) Bv[u] = load16_nt<Vec>(r[u], (j + 1024) * 16);
+        __builtin_amdgcn_sched_barrier(0);
+        f.template run<4>(A, vid0 + j);
+        last(Bv, j + 1024);
+    } else {
+        last(A, j);
+    }
+}
+
+// One segment of one row: 16-byte vectors [vlo, vhi), or, when the row
+// length is no multiple of the vector width, single values [slo, shi).
+// Thread tid takes vectors vlo + tid, + 256, ...; f.run<U>(w, i) absorbs U
+// vectors at ids i, i + 256, ..., f.one(x, v) a single value.
+template <bool BF16, typename F>
+__device__ __forceinline__ void scan_segment(const void* row, int vlo, int vhi, int slo, int shi,
+                                             int tid, F& f) {
+    using Vec = typename std::conditional<BF16, u32x4_t, f32x4_t>::type;
+    scan_runs<BF16>(reinterpret_cast<const Vec*>(row) + vlo, vhi - vlo, tid, vlo, f);
+    if constexpr (BF16) {
+        const uint16_t* r = static_cast<const uint16_t*>(row);
+        for (int v = slo + tid; v < shi; v += 256) f.one(__uint_as_float((uint32_t)r[v] << 16), v);
+    } else {
+        const float* r = static_cast<const float*>(row);
+        for (int v = slo + tid; v < shi; v += 256) f.one(r[v], v);
+    }
+}
+
+// Absorbers over runs of U vectors at vector ids i, i + 256, ...
+template <bool BF16>
+struct SampAbsorb {
+    SampStat st;
+    float c;
+    template <int U, typename Vec>
+    __device__ __forceinline__ void run(const Vec (&w)[U], int) {
+        constexpr int VW = BF16 ? 8 : 4;
+        float x[U * VW];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if constexpr (BF16) {
+                bf16x8_to_f32(w[u], x + u * 8);
+            } else {
+#pragma unroll
+                for (int h = 0; h < 4; ++h) x[u * 4 + h] = w[u][h];
+            }
+        }
+        absorb_samp<U * VW>(x, st, c);
+    }
+    __device__ __forceinline__ void one(float v, int) {
+        const float x[1] = {v};
+        absorb_samp<1>(x, st, c);
+    }
+};
+
+template <bool BF16>
+struct ArgAbsorb {
+    float m;
+    int idx;
+    template <int U, typename Vec>
+    __device__ __forceinline__ void run(const Vec (&w)[U], int i) {
+        constexpr int VW = BF16 ? 8 : 4;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float x[VW];
+            if constexpr (BF16) {
+                bf16x8_to_f32(w[u], x);
+            } else {
+#pragma unroll
+                for (int h = 0; h < 4; ++h) x[h] = w[u][h];
+            }
+            absorb_arg<VW>(x, (i + u * 256) * VW, m, idx);
+        }
+    }
+    __device__ __forceinline__ void one(float v, int id) {
+        const float x[1] = {v};
+        absorb_arg<1>(x, id, m, idx);
+    }
+};
+
+// One workgroup per (segment, row): the row's statistics over that segment,
+// as one RowStat part; verify_decide merges the parts of a row.
 template <bool BF16, bool GREEDY>
 __global__ __launch_bounds__(256)
 void verify_rows(VerifyArgs a, int is_q) {
     __shared__ float red_m[4], red_s[4];
     __shared__ int red_i[4];
-    const int k = blockIdx.x;
-    const int b = blockIdx.y;
+    const int seg = blockIdx.x;
+    const int k = blockIdx.y;
+    const int b = blockIdx.z;
+    const int S = a.row_segs;
     const int L = request_len(a, b);
     if (L < 0 || L > a.gamma_max) return;
     if (is_q ? (k >= L) : (k > L)) return;
     const int V = a.V;
     const int64_t row = is_q ? q_row(a, b, k) : p_row(a, b, k);
     const void* base = is_q ? a.Q : a.P;
+    const void* rp = BF16 ? static_cast<const void*>(static_cast<const uint16_t*>(base) + row * (int64_t)V)
+                          : static_cast<const void*>(static_cast<const float*>(base) + row * (int64_t)V);
     const int tid = threadIdx.x;
-    float m = -INFINITY, s = 0.0f;
-    int idx = INT_MAX;
+    constexpr int VW = BF16 ? 8 : 4;
+    const int nvec = (V % VW == 0) ? V / VW : 0;
+    const int vlo = (int)((int64_t)nvec * seg / S), vhi = (int)((int64_t)nvec * (seg + 1) / S);
+    const int slo = nvec ? 0 : (int)((int64_t)V * seg / S);
+    const int shi = nvec ? 0 : (int)((int64_t)V * (seg + 1) / S);
     const float invT = a.invT;
+    // The logit at the draft token (segment 0 of a drafted position), loaded
+    // ahead of the scan through a view that is empty when there is none, so
+    // the load is unconditional and nothing waits for it before the end.
+    int xg = -1;
+    if (seg == 0 && k < L) xg = a.draft[(size_t)b * a.gamma_max + k];
+    const bool gv = xg >= 0 && xg < V;
+    const __amdgpu_buffer_rsrc_t grs = range_rsrc(rp, gv ? (int64_t)V * (BF16 ? 2 : 4) : 0);
+    uint32_t gbits;
+    if constexpr (BF16) gbits = __builtin_amdgcn_raw_buffer_load_b16(grs, gv ? xg * 2 : 0, 0, 0);
+    else gbits = __builtin_amdgcn_raw_buffer_load_b32(grs, gv ? xg * 4 : 0, 0, 0);
 
-    if constexpr (BF16) {
-        const uint16_t* r = static_cast<const uint16_t*>(base) + row * (int64_t)V;
-        const int nvec = (V % 8 == 0) ? V / 8 : 0;
-        const u32x4_t* rv = reinterpret_cast<const u32x4_t*>(r);
-        int i = tid;
-        for (; i + 3 * 256 < nvec; i += 4 * 256) {
-            u32x4_t t[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) t[u] = __builtin_nontemporal_load(rv + i + u * 256);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const uint32_t w[4] = {t[u][0], t[u][1], t[u][2], t[u][3]};
-                float x[8];
-#pragma unroll
-                for (int h = 0; h < 4; ++h) {
-                    x[2 * h] = bf16_bits_to_float(w[h] & 0xFFFFu);
-                    x[2 * h + 1] = bf16_bits_to_float(w[h] >> 16);
-                }
-                absorb<8, GREEDY>(x, (i + u * 256) * 8, m, s, idx, invT);
-            }
-        }
-        for (; i < nvec; i += 256) {
-            const u32x4_t t = __builtin_nontemporal_load(rv + i);
-            const uint32_t w[4] = {t[0], t[1], t[2], t[3]};
-            float x[8];
-#pragma unroll
-            for (int h = 0; h < 4; ++h) {
-                x[2 * h] = bf16_bits_to_float(w[h] & 0xFFFFu);
-                x[2 * h + 1] = bf16_bits_to_float(w[h] >> 16);
-            }
-            absorb<8, GREEDY>(x, i * 8, m, s, idx, invT);
-        }
-        for (int v = nvec * 8 + tid; v < V; v += 256) {
-            const float x[1] = {bf16_bits_to_float(r[v])};
-            absorb<1, GREEDY>(x, v, m, s, idx, invT);
-        }
+    float m, s;
+    int idx;
+    if constexpr (GREEDY) {
+        ArgAbsorb<BF16> f{-INFINITY, INT_MAX};
+        scan_segment<BF16>(rp, vlo, vhi, slo, shi, tid, f);
+        m = f.m;
+        s = 0.0f;
+        idx = f.idx;
     } else {
-        const float* r = static_cast<const float*>(base) + row * (int64_t)V;
-        const int nvec = (V % 4 == 0) ? V / 4 : 0;
-        const f32x4_t* rv = reinterpret_cast<const f32x4_t*>(r);
-        int i = tid;
-        for (; i + 3 * 256 < nvec; i += 4 * 256) {
-            f32x4_t t[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) t[u] = __builtin_nontemporal_load(rv + i + u * 256);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float x[4] = {t[u][0], t[u][1], t[u][2], t[u][3]};
-                absorb<4, GREEDY>(x, (i + u * 256) * 4, m, s, idx, invT);
-            }
-        }
-        for (; i < nvec; i += 256) {
-            const f32x4_t t = __builtin_nontemporal_load(rv + i);
-            const float x[4] = {t[0], t[1], t[2], t[3]};
-            absorb<4, GREEDY>(x, i * 4, m, s, idx, invT);
-        }
-        for (int v = nvec * 4 + tid; v < V; v += 256) {
-            const float x[1] = {r[v]};
-            absorb<1, GREEDY>(x, v, m, s, idx, invT);
-        }
+        const float c = invT * 1.44269504088896340736f;
+        SampAbsorb<BF16> f{{-INFINITY, -FLT_MAX, 0.0f, 0.0f}, c};
+        scan_segment<BF16>(rp, vlo, vhi, slo, shi, tid, f);
+        m = f.st.m;
+        s = samp_sum(f.st, c);
+        idx = INT_MAX;
     }
 
     wave_reduce_stat(m, s, idx, invT);
@@ -156,30 +325,39 @@ void verify_rows(VerifyArgs a, int is_q) {
     }
     __syncthreads();
     if (tid == 0) {
-        float M = red_m[0], S = red_s[0];
+        float M = red_m[0], Sm = red_s[0];
         int I = red_i[0];
         for (int w = 1; w < 4; ++w) {
             float mv = M;
             int iv = I;
             merge_arg(mv, iv, red_m[w], red_i[w]);
-            merge_ms(M, S, red_m[w], red_s[w], invT);
+            merge_ms(M, Sm, red_m[w], red_s[w], invT);
             I = iv;
         }
-        float gathered = 0.0f;
-        if (k < L) {
-            const int x = a.draft[(size_t)b * a.gamma_max + k];
-            if (x >= 0 && x < V) {
-                gathered = BF16 ? bf16_bits_to_float(static_cast<const uint16_t*>(base)[row * (int64_t)V + x])
-                                : static_cast<const float*>(base)[row * (int64_t)V + x];
-            }
-        }
+        const float gathered = BF16 ? __uint_as_float(gbits << 16) : __uint_as_float(gbits);
         RowStat rs;
         rs.m = M;
-        rs.s = S;
+        rs.s = Sm;
         rs.idx = I;
         rs.gathered = gathered;
-        a.rows[(size_t)b * (2 * a.gamma_max + 1) + (is_q ? a.gamma_max + 1 + k : k)] = rs;
+        const size_t slot = (size_t)b * (2 * a.gamma_max + 1) + (is_q ? a.gamma_max + 1 + k : k);
+        a.rows[slot * S + seg] = rs;
     }
+}
+
+// The statistics of a whole row from its per-segment parts: max and sum
+// merged online, argmax by lowest id on ties, the gathered logit from part 0.
+__device__ __forceinline__ RowStat merged_row(const RowStat* parts, int S, float invT) {
+    RowStat r = parts[0];
+    for (int g = 1; g < S; ++g) {
+        const RowStat o = parts[g];
+        float mv = r.m;
+        int iv = r.idx;
+        merge_arg(mv, iv, o.m, o.idx);
+        merge_ms(r.m, r.s, o.m, o.s, invT);
+        r.idx = iv;
+    }
+    return r;
 }
 
 // One wave per request; lane k handles position k (in chunks of 64).  The
@@ -193,14 +371,17 @@ void verify_decide(VerifyArgs a) {
     const int L = request_len(a, b);
     int32_t* out = a.out_tokens + (size_t)b * (G + 1);
     const int32_t* dr = a.draft + (size_t)b * G;
-    const RowStat* rs = a.rows + (size_t)b * (2 * G + 1);
+    const int S = a.row_segs;
+    const RowStat* rs = a.rows + (size_t)b * (2 * G + 1) * S;
+    const float invTf = a.invT;
 
     bool bad_l = L < 0 || L > G;
     if (!bad_l) {
         for (int k = lane; k <= L; k += kWave) {
             if (k < L && (dr[k] < 0 || dr[k] >= a.V)) bad_l = true;
-            if (rs[k].m == -INFINITY) bad_l = true;
-            if (k < L && !a.qprob && rs[G + 1 + k].m == -INFINITY) bad_l = true;
+            if (merged_row(rs + (size_t)k * S, S, invTf).m == -INFINITY) bad_l = true;
+            if (k < L && !a.qprob && merged_row(rs + (size_t)(G + 1 + k) * S, S, invTf).m == -INFINITY)
+                bad_l = true;
         }
     }
     if (__ballot(bad_l)) {
@@ -231,13 +412,13 @@ void verify_decide(VerifyArgs a) {
         const int k = c0 + lane;
         double lzp = 0.0, lzq = 0.0, ap = 0.0;
         bool reject = false;
+        RowStat p{};
         if (k <= L) {
-            const RowStat p = rs[k];
+            p = merged_row(rs + (size_t)k * S, S, invTf);
             lzp = a.greedy ? (double)p.m : (double)p.m * invT + log((double)p.s);
         }
         if (k < L) {
-            const RowStat p = rs[k];
-            const RowStat q = a.qprob ? p : rs[G + 1 + k];
+            const RowStat q = a.qprob ? p : merged_row(rs + (size_t)(G + 1 + k) * S, S, invTf);
             if (a.greedy) {
                 lzq = a.qlogz ? (double)a.qlogz[(size_t)b * G + k] : (double)q.m;
                 reject = p.idx != dr[k];
@@ -274,7 +455,7 @@ void verify_decide(VerifyArgs a) {
     if (n == L) lzp_n = lzp_L;
     for (int j = lane; j <= G; j += kWave) out[j] = j < n ? dr[j] : -1;
     if (lane == 0) {
-        if (a.greedy) out[n] = rs[n].idx;
+        if (a.greedy) out[n] = merged_row(rs + (size_t)n * S, S, invTf).idx;
         a.accepted[b] = n;
         if (a.row_pos) a.row_pos[b] = (!a.greedy && n < L) ? n : -1;
         FinalInfo f;
@@ -574,7 +755,7 @@ template <bool BF16>
 static void launch_rows(const VerifyArgs& a, int is_q, hipStream_t s) {
     const int nrow = is_q ? a.gamma_max : a.gamma_max + 1;
     if (nrow == 0) return;
-    dim3 grid(nrow, a.B);
+    dim3 grid(a.row_segs, nrow, a.B);
     void* t = prof_begin(is_q ? "verify_rows_q" : "verify_rows_p", s);
     if (a.greedy)
         hipLaunchKernelGGL((verify_rows<BF16, true>), grid, dim3(256), 0, s, a, is_q);
