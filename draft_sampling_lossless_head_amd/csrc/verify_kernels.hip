@@ -34,6 +34,9 @@ constexpr int kChunk = 4096;          // tokens per chunk of the final draw
 constexpr int kPerThread = kChunk / 256;
 static_assert(kPerThread == 16, "the final draw works on runs of 16 tokens per thread");
 
+// Most segments a verified row is split into.
+constexpr int kMaxRowSegs = 16;
+
 // Cache policy of a streaming buffer load: non-temporal.
 constexpr int kBufNontemporal = 2;
 
@@ -45,7 +48,7 @@ int verify_num_chunks(int V) { return (V + kChunk - 1) / kChunk; }
 int verify_row_segs(int B, int gamma_max, int V) {
     const int64_t rows = std::max<int64_t>(1, (int64_t)B * (gamma_max + 1));
     const int64_t want = (8192 + rows - 1) / rows;
-    const int64_t cap = std::max(1, std::min(16, V / 4096));
+    const int64_t cap = std::max(1, std::min(kMaxRowSegs, V / 4096));
     return (int)std::max<int64_t>(1, std::min(want, cap));
 }
 
@@ -347,21 +350,36 @@ void verify_rows(VerifyArgs a, int is_q) {
 
 // The statistics of a whole row from its per-segment parts: max and sum
 // merged online, argmax by lowest id on ties, the gathered logit from part 0.
+// Parts are loaded four at a time, all four issued at once (ids clamped to
+// the last part); the copies past S act as the neutral part (-inf, 0,
+// INT_MAX).
 __device__ __forceinline__ RowStat merged_row(const RowStat* parts, int S, float invT) {
-    RowStat r = parts[0];
-    for (int g = 1; g < S; ++g) {
-        const RowStat o = parts[g];
-        float mv = r.m;
-        int iv = r.idx;
-        merge_arg(mv, iv, o.m, o.idx);
-        merge_ms(r.m, r.s, o.m, o.s, invT);
-        r.idx = iv;
+    RowStat r{-INFINITY, 0.0f, INT_MAX, parts[0].gathered};
+    for (int g0 = 0; g0 < S; g0 += 4) {
+        RowStat p[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) p[g] = parts[min(g0 + g, S - 1)];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const bool in = g0 + g < S;
+            const float om = in ? p[g].m : -INFINITY;
+            const float os = in ? p[g].s : 0.0f;
+            const int oi = in ? p[g].idx : INT_MAX;
+            float mv = r.m;
+            int iv = r.idx;
+            merge_arg(mv, iv, om, oi);
+            merge_ms(r.m, r.s, om, os, invT);
+            r.idx = iv;
+        }
     }
     return r;
 }
 
 // One wave per request; lane k handles position k (in chunks of 64).  The
-// first rejection is the lowest set bit of a ballot.
+// first rejection is the lowest set bit of a ballot.  One pass merges each
+// row once and writes the per-position outputs; a request found invalid on
+// the way (a draft token out of range, a row with no finite logit) has them
+// overwritten afterwards.
 __global__ __launch_bounds__(256)
 void verify_decide(VerifyArgs a) {
     const int lane = threadIdx.x & 63;
@@ -374,54 +392,29 @@ void verify_decide(VerifyArgs a) {
     const int S = a.row_segs;
     const RowStat* rs = a.rows + (size_t)b * (2 * G + 1) * S;
     const float invTf = a.invT;
-
-    bool bad_l = L < 0 || L > G;
-    if (!bad_l) {
-        for (int k = lane; k <= L; k += kWave) {
-            if (k < L && (dr[k] < 0 || dr[k] >= a.V)) bad_l = true;
-            if (merged_row(rs + (size_t)k * S, S, invTf).m == -INFINITY) bad_l = true;
-            if (k < L && !a.qprob && merged_row(rs + (size_t)(G + 1 + k) * S, S, invTf).m == -INFINITY)
-                bad_l = true;
-        }
-    }
-    if (__ballot(bad_l)) {
-        for (int j = lane; j <= G; j += kWave) {
-            out[j] = -1;
-            if (a.p_logZ) a.p_logZ[(size_t)b * (G + 1) + j] = 0.0f;
-            if (j < G && a.q_logZ) a.q_logZ[(size_t)b * G + j] = 0.0f;
-            if (j < G && a.accept_prob) a.accept_prob[(size_t)b * G + j] = 0.0f;
-        }
-        if (lane == 0) {
-            a.accepted[b] = -1;
-            if (a.row_pos) a.row_pos[b] = -1;
-            FinalInfo f;
-            f.logZp = 0.0;
-            f.logZq = 0.0;
-            f.n = -1;
-            f.mode = 0;
-            f.pad0 = f.pad1 = 0;
-            a.fin[b] = f;
-        }
-        return;
-    }
-
     const double invT = (double)a.invT;
-    int n = L;
+
+    bool bad = L < 0 || L > G;
+    int n = L, idx_n = -1, idx_L = -1;
     double lzp_n = 0.0, lzq_n = 0.0, lzp_L = 0.0;
-    for (int c0 = 0; c0 <= G; c0 += kWave) {
+    for (int c0 = 0; !bad && c0 <= G; c0 += kWave) {
         const int k = c0 + lane;
         double lzp = 0.0, lzq = 0.0, ap = 0.0;
-        bool reject = false;
+        bool reject = false, bad_l = false;
         RowStat p{};
         if (k <= L) {
             p = merged_row(rs + (size_t)k * S, S, invTf);
+            bad_l = p.m == -INFINITY;
             lzp = a.greedy ? (double)p.m : (double)p.m * invT + log((double)p.s);
         }
         if (k < L) {
+            const int x = dr[k];
+            bad_l = bad_l || x < 0 || x >= a.V;
             const RowStat q = a.qprob ? p : merged_row(rs + (size_t)(G + 1 + k) * S, S, invTf);
+            if (!a.qprob) bad_l = bad_l || q.m == -INFINITY;
             if (a.greedy) {
                 lzq = a.qlogz ? (double)a.qlogz[(size_t)b * G + k] : (double)q.m;
-                reject = p.idx != dr[k];
+                reject = p.idx != x;
                 ap = reject ? 0.0 : 1.0;
             } else {
                 const double px = exp((double)p.gathered * invT - lzp);
@@ -444,18 +437,46 @@ void verify_decide(VerifyArgs a) {
             if (k < G && a.q_logZ) a.q_logZ[(size_t)b * G + k] = (float)lzq;
             if (k < G && a.accept_prob) a.accept_prob[(size_t)b * G + k] = (float)ap;
         }
+        bad = __ballot(bad_l) != 0;
         const unsigned long long rej = __ballot(reject);
         if (n == L && rej) {
             n = c0 + __ffsll((long long)rej) - 1;
             lzp_n = __shfl(lzp, n - c0);
             lzq_n = __shfl(lzq, n - c0);
+            idx_n = __shfl(p.idx, n - c0);
         }
-        if (L >= c0 && L < c0 + kWave) lzp_L = __shfl(lzp, L - c0);
+        if (L >= c0 && L < c0 + kWave) {
+            lzp_L = __shfl(lzp, L - c0);
+            idx_L = __shfl(p.idx, L - c0);
+        }
     }
-    if (n == L) lzp_n = lzp_L;
+    if (bad) {
+        for (int j = lane; j <= G; j += kWave) {
+            out[j] = -1;
+            if (a.p_logZ) a.p_logZ[(size_t)b * (G + 1) + j] = 0.0f;
+            if (j < G && a.q_logZ) a.q_logZ[(size_t)b * G + j] = 0.0f;
+            if (j < G && a.accept_prob) a.accept_prob[(size_t)b * G + j] = 0.0f;
+        }
+        if (lane == 0) {
+            a.accepted[b] = -1;
+            if (a.row_pos) a.row_pos[b] = -1;
+            FinalInfo f;
+            f.logZp = 0.0;
+            f.logZq = 0.0;
+            f.n = -1;
+            f.mode = 0;
+            f.pad0 = f.pad1 = 0;
+            a.fin[b] = f;
+        }
+        return;
+    }
+    if (n == L) {
+        lzp_n = lzp_L;
+        idx_n = idx_L;
+    }
     for (int j = lane; j <= G; j += kWave) out[j] = j < n ? dr[j] : -1;
     if (lane == 0) {
-        if (a.greedy) out[n] = merged_row(rs + (size_t)n * S, S, invTf).idx;
+        if (a.greedy) out[n] = idx_n;
         a.accepted[b] = n;
         if (a.row_pos) a.row_pos[b] = (!a.greedy && n < L) ? n : -1;
         FinalInfo f;

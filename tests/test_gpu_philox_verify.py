@@ -130,6 +130,38 @@ def test_verify_invalid_requests_are_flagged(orc):
     assert g["accepted"][0] >= 0 and g["out_tokens"][0][g["accepted"][0]] >= 0
 
 
+@pytest.mark.parametrize("dtype,V,T", [
+    ("f32", 24584, 1.0), ("bf16", 24584, 0.0), ("bf16", 16387, 1.0), ("f32", 16387, 0.0)])
+def test_verify_segmented_rows(orc, dtype, V, T):
+    """Rows split into several segments: a ragged split of the 16-byte
+    vectors (V = 8 * 3073) or of single values (V odd), rows whose finite
+    logits all sit in one segment, and more than 64 positions per request so
+    the decision runs over several chunks; request 2 has an out-of-range
+    draft token at position 66 (second chunk) and must come back invalid."""
+    sd = require_gpu()
+    B, G = 3, 70
+    note(f"verify segmented dtype={dtype} V={V} T={T}")
+    vw = workloads.make_verify_only(B, G, V, seed=31 + V, dtype=dtype, sigma=0.5)
+    P, Q = vw["P"], vw["Q"]
+    ninf = np.uint16(0xFF80) if dtype == "bf16" else np.float32(-np.inf)
+    P[1, 3, :V - 100] = ninf        # mass only in the last segment
+    Q[0, 2, 50:] = ninf             # mass only in the first segment
+    P[0, 40, V // 3:] = ninf        # mass only in the first segments
+    Pf, Qf = workloads.as_f64(P, dtype), workloads.as_f64(Q, dtype)
+    draft = _oracle_drafts(orc, Qf, T, np.random.default_rng(V), random_frac=0.05)
+    draft[2, 66] = V
+    seed = 19
+    g = host(sd.spec_verify(dev(P, dtype), dev(Q, dtype), dev(draft), T, seed=seed))
+    u = orc.verify_uniforms(seed, 0, B, G)
+    tally = compare.Tally()
+    for b in range(2):
+        compare.compare_verify_request(Pf[b], Qf[b], draft[b], T, u[b, :G], u[b, G],
+                                       _gpu_rows(g, b), f"b={b}", tally)
+    note(f"  {tally.as_dict()} accepted={g['accepted'].tolist()}")
+    assert g["accepted"][2] == -1 and np.all(g["out_tokens"][2] == -1)
+    assert np.all(g["p_logZ"][2] == 0.0) and np.all(g["accept_prob"][2] == 0.0)
+
+
 def test_verify_zero_sizes(orc):
     sd = require_gpu()
     V = 100
