@@ -3,32 +3,39 @@
 // request in one cooperative launch of one workgroup per CU.
 //
 // The per-position kernels read all of the packed W2 image once per position.
-// Here each workgroup owns a fixed contiguous range of 32-token blocks (its
-// share of the vocabulary) for the whole call, and each of its four waves
-// (one per SIMD, so 512 registers each) keeps the MFMA A operands of up to NB
-// of those blocks in registers: W2 crosses HBM once per call, and only U_k
-// streams per position.  Position k then runs as
+// Here each unit workgroup owns a fixed contiguous range of 32-token blocks
+// (its share of the vocabulary) for the whole call, and each of its four
+// waves (one per SIMD, so 512 registers each) keeps the MFMA A operands of up
+// to NB of those blocks in registers: W2 crosses HBM once per call, and only
+// U_k streams per position.  The requests are taken in blocks of 64 rows;
+// for position k and row block rb a unit workgroup runs
 //
-//   1. E = W1[x_{k-1}] of 128 request rows gathered into LDS (direct loads,
-//      chunk c of row n stored in slot c ^ (n & 7): conflict-free B reads);
-//   2. per wave, units (32 rows x one of its 32-token blocks): U_k of the unit
+//   1. wait for the tokens x_{k-1} of the block's rows (token words written by
+//      the finalize workgroups; the anchors x_0 at k = 0);
+//   2. E = W1[x_{k-1}] of the 64 rows gathered into LDS (direct loads, chunk c
+//      of row n stored in slot c ^ (n & 7): conflict-free B reads);
+//   3. per wave, units (32 rows x one of its 32-token blocks): U_k of the unit
 //      streams through a wave-private LDS ring (direct loads, D units ahead),
 //      16 (r = 256) 32x32x16 MFMAs against the resident W2 operands, then the
 //      reduction of the previous unit: the block's max and four 8-token group
 //      sums relative to it (the same segment summaries as the per-position
 //      streaming tile), and a running (max, sum) of the wave's blocks per row;
-//   3. the four waves' running summaries merged into one summary per (row,
-//      workgroup share);
-//   4. grid barrier; one wave per row runs the shared finalize (shares ->
-//      segment -> group -> token, rebuilding 8 logits) -> x_k, log Z, q(x_k);
-//   5. grid barrier (every workgroup needs every row's x_k), next position.
+//   4. the four waves' running summaries merged into one summary per (row,
+//      workgroup share), written with the tag k + 1.
+//
+// The last few workgroups only finalize: one wave per row polls the row's
+// tagged share summaries, runs the shared finalize (shares -> segment ->
+// group -> token, rebuilding 8 logits) -> x_k, log Z, q(x_k), and publishes
+// the token word.  While they draw the tokens of one row block, the unit
+// workgroups already compute the next block, so the draw is off the critical
+// path whenever there are two or more row blocks (B > 64).
 //
 // MFMA row i = 8g + 4h + c of a block holds token 16h + 8 (g & 1) + 4 (g >> 1)
 // + c, so a lane's 16 accumulators are 16 contiguous tokens of one row and its
-// U values are two 16-byte chunks.  The grid barriers are counter based with a
-// bounded wait: the launch is cooperative (all workgroups resident), and if a
-// barrier still does not complete within the poll limit every workgroup
-// leaves, setting an abort word the host can read.
+// U values are two 16-byte chunks.  Every wait is a bounded poll: the launch
+// is cooperative (all workgroups resident), and if a wait still does not
+// complete within the poll limit the workgroup sets an abort word the host
+// can read and every other workgroup leaves at its next poll.
 #include <algorithm>
 #include <climits>
 
@@ -39,8 +46,10 @@
 namespace specdec {
 
 constexpr int kPersistWaves = 4;             // one wave per SIMD
+constexpr int kPersistRows = 64;             // request rows of one row block
+constexpr int kPersistFinWgs = 16;           // workgroups that only finalize
 constexpr int kPersistUnit = 2048;           // U bytes of one unit: 32 rows x 32 tokens
-constexpr unsigned kBarrierPolls = 1u << 20; // polls (with s_sleep) before a barrier gives up
+constexpr unsigned kBarrierPolls = 1u << 20; // polls (with s_sleep) before a wait gives up
 
 // Both values of a lane pair (l, l ^ 32), one in each result: swapping the
 // upper half of one copy with the lower half of the other leaves lane l with
@@ -75,6 +84,7 @@ struct PersistArgs {
     unsigned* bar;       // barrier words (kBarWords, zero at launch except the -inf
                          // values that stand in for the U chunks of absent tokens)
     int B, gamma, V, nblk, bpad;
+    int nu;              // unit workgroups 0 .. nu - 1; the others finalize
 };
 
 // Layout of the synchronisation words (unsigned, in the workspace): the abort
@@ -94,26 +104,30 @@ __global__ void persist_bar_reset(unsigned* bar, uint64_t* tflag, int B, uint64_
     for (size_t i = t; i < 2 * ns; i += (size_t)gridDim.x * blockDim.x) sup64[i] = 0u;
 }
 
-// Wait until every request row has its token of position k: the word of row
-// b reads ((k + 1) << 32) | token once its finalize is done (so the summaries
-// it read may be overwritten).  Wave 0 polls with coherent loads; with
-// xprev_out the tokens of rows 0 .. B - 1 (B <= 128) are written there
-// (-1 for an invalid row).  Same bounded wait and abort word as grid_sync.
-__device__ __forceinline__ bool token_sync(unsigned* bar, const uint64_t* tflag, int B,
-                                           unsigned k1, int* xprev_out, int* ok_s) {
-    __syncthreads();
+// Wait until the token words of rows r0 .. r0 + rows - 1 (rows <= 64) carry
+// position k - 1: the word of row b reads (k << 32) | token once the
+// finalize of (b, k - 1) is done.  Wave 0 polls with coherent loads and
+// leaves the tokens in xprev[0 .. 63] (-1 for an invalid or absent row).
+// Bounded: past the poll limit, or when another wave set the abort word,
+// the abort word is set and false returned.
+__device__ __forceinline__ bool rows_tokens(unsigned* bar, const uint64_t* tflag, int r0, int rows,
+                                            unsigned k, int V, int* xprev, int* ok_s) {
     if (threadIdx.x < 64) {
         int lane = threadIdx.x;
         asm volatile("" : "+v"(lane));   // recomputed here, not kept live across the kernel
         int ok = 1;
         for (unsigned polls = 0;; ++polls) {
             bool up = true;
-            for (int i = lane; i < B; i += 64) {
-                const uint64_t w = coh_load<true>(tflag + i);
-                up = up && (uint32_t)(w >> 32) >= k1;
-                if (xprev_out) xprev_out[i] = (int)(uint32_t)w;
+            int tok = -1;
+            if (lane < rows) {
+                const uint64_t w = coh_load<true>(tflag + r0 + lane);
+                up = (uint32_t)(w >> 32) >= k;
+                tok = (int)(uint32_t)w;
             }
-            if (__all(up)) break;
+            if (__all(up)) {
+                xprev[lane] = (tok >= 0 && tok < V) ? tok : -1;
+                break;
+            }
             if (coh_load<true>(bar + kBarAbort) != 0u || polls > kBarrierPolls) {
                 if (lane == 0) coh_store<true>(bar + kBarAbort, 1u);
                 ok = 0;
@@ -133,7 +147,7 @@ void draft_persist(PersistArgs P) {
     constexpr int R = NKS * 16;
     constexpr int NCH = R / 8;                  // 16-byte chunks per rank row
     constexpr int D = NR - 2;                   // units in flight per wave
-    constexpr int EB = kStreamRows * R * 2;     // E rows of one row block
+    constexpr int EB = kPersistRows * R * 2;    // E rows of one row block
     static_assert(NCH >= 8 && NCH % 2 == 0, "rank");
     static_assert(2 * D <= 32, "vmcnt waits");
     static_assert(NKS >= 4, "the U read follows the stages that use the previous unit's U");
@@ -142,16 +156,36 @@ void draft_persist(PersistArgs P) {
     char* e_lds = smem_p;
     char* ring = smem_p + EB;
     int* xprev = reinterpret_cast<int*>(ring + kPersistWaves * NR * kPersistUnit);
-    float* xsum = reinterpret_cast<float*>(xprev + kStreamRows);   // [wave][row][3]
+    float* xsum = reinterpret_cast<float*>(xprev + kPersistRows);  // [wave][row][3]
 
     const FinStreamArgs& F = P.fin;
     const int V = P.V, B = P.B, G = P.gamma;
     const int tid = threadIdx.x;
     const int lane0 = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int NG = gridDim.x, g = blockIdx.x;
-    const int blo = (int)((long long)g * P.nblk / NG);
-    const int bhi = (int)((long long)(g + 1) * P.nblk / NG);
+    const int NU = P.nu, g = blockIdx.x;
+    const int nrb = (B + kPersistRows - 1) / kPersistRows;
+
+    if (g >= NU) {
+        // Finalize workgroups: wave fw draws rows fw, fw + nfw, ... of each row
+        // block, positions in order; each draw waits for its row's shares.
+        const int fw = (g - NU) * kPersistWaves + wave;
+        const int nfw = ((int)gridDim.x - NU) * kPersistWaves;
+        for (int k = 0; k < G; ++k) {
+            for (int rb = 0; rb < nrb; ++rb) {
+                const int r1 = min(B, (rb + 1) * kPersistRows);
+                for (int b = rb * kPersistRows + fw; b < r1; b += nfw) {
+                    int lane = lane0;
+                    asm volatile("" : "+v"(lane));
+                    if (!finalize_row_stream<true, true>(F, b, k, lane)) return;
+                }
+            }
+        }
+        return;
+    }
+
+    const int blo = (int)((long long)g * P.nblk / NU);
+    const int bhi = (int)((long long)(g + 1) * P.nblk / NU);
     auto wave_blocks = [&](int w) { return min(NB, max(0, (bhi - blo - w + 3) / 4)); };
     const int nj = wave_blocks(wave);   // this wave's blocks: blo + wave + 4 j, j < nj
     const size_t bpad = (size_t)P.bpad;
@@ -247,7 +281,6 @@ void draft_persist(PersistArgs P) {
         return finish(R);
     };
 
-    const int nrb = (B + kStreamRows - 1) / kStreamRows;
     const uint16_t* ninf = reinterpret_cast<const uint16_t*>(P.bar + kBarNegInf);
     for (int k = 0; k < G; ++k) {
         for (int rb = 0; rb < nrb; ++rb) {
@@ -257,20 +290,23 @@ void draft_persist(PersistArgs P) {
             int lane = lane0;
             asm volatile("" : "+v"(lane));
             const int h = lane >> 5, n = lane & 31;
-            const int rows = min(kStreamRows, B - rb * kStreamRows);
+            const int r0 = rb * kPersistRows;
+            const int rows = min(kPersistRows, B - r0);
             const int nrg = (rows + 31) / 32;
-            // 1. conditioning tokens of the row block (-1: invalid or absent);
-            // with one row block they come with the token words after k = 0
-            if ((k == 0 || nrb > 1) && tid < kStreamRows) {
-                const int b = rb * kStreamRows + tid;
-                int prev = -1;
-                if (b < B) prev = k == 0 ? F.x0[b] : coh_load<true>(F.tokens + (size_t)b * G + k - 1);
-                xprev[tid] = (prev >= 0 && prev < V) ? prev : -1;
+            // 1. conditioning tokens of the row block (-1: invalid or absent):
+            // the anchors, then the tokens the finalize workgroups publish.
+            if (k == 0) {
+                if (tid < kPersistRows) {
+                    const int prev = tid < rows ? F.x0[r0 + tid] : -1;
+                    xprev[tid] = (prev >= 0 && prev < V) ? prev : -1;
+                }
+                __syncthreads();
+            } else if (!rows_tokens(P.bar, F.tflag, r0, rows, (unsigned)k, V, xprev, &ok_s)) {
+                return;
             }
-            __syncthreads();
             // 2. E rows into LDS, then the first D units of U.
 #pragma unroll
-            for (int q = 0; q < NCH / 2; ++q) {
+            for (int q = 0; q < NCH / 4; ++q) {
                 const int pc = q * kPersistWaves + wave;
                 const int o = pc * 64 + lane;
                 const int row = o / NCH, slot = o % NCH;
@@ -295,7 +331,7 @@ void draft_persist(PersistArgs P) {
                 const int c = (lane & 3) ^ uswz(m);
                 urow[q] = m;
                 utok[q] = kStreamSeg * (blo + wave) + 8 * c;
-                usrc[q] = F.U + ((size_t)(rb * kStreamRows + m) * G + k) * (size_t)V + utok[q];
+                usrc[q] = F.U + ((size_t)(r0 + m) * G + k) * (size_t)V + utok[q];
             }
             const int rows_b = rows;
             const size_t rg_step = (size_t)32 * G * (size_t)V;
@@ -333,15 +369,15 @@ void draft_persist(PersistArgs P) {
             // 3. units of this wave, row group major.
             auto flush_run = [&](int rgi, float m, float s, int a) {
                 if (h == 0) {
-                    float* xs = xsum + ((size_t)wave * kStreamRows + 32 * rgi + n) * 3;
+                    float* xs = xsum + ((size_t)wave * kPersistRows + 32 * rgi + n) * 3;
                     xs[0] = m;
                     xs[1] = s;
                     xs[2] = __int_as_float(a);
                 }
             };
             // summaries of unit (rgi, j) at offset 4 j bpad + 32 rgi from the lane's base
-            float* segm_l = P.segm + (size_t)(blo + wave) * bpad + rb * kStreamRows + n;
-            float* gs_l = P.gsums + ((size_t)(blo + wave) * bpad + rb * kStreamRows + n) * 4 + 2 * h;
+            float* segm_l = P.segm + (size_t)(blo + wave) * bpad + r0 + n;
+            float* gs_l = P.gsums + ((size_t)(blo + wave) * bpad + r0 + n) * 4 + 2 * h;
             // Every lane stores: rows without a valid conditioning token or past
             // B hold values nothing reads, and both halves of a row hold the
             // same block max.
@@ -463,7 +499,7 @@ void draft_persist(PersistArgs P) {
                 int a = INT_MAX;
                 for (int w = 0; w < kPersistWaves; ++w) {
                     if (wave_blocks(w) == 0) continue;
-                    const float* xs = xsum + ((size_t)w * kStreamRows + tid) * 3;
+                    const float* xs = xsum + ((size_t)w * kPersistRows + tid) * 3;
                     const float m2 = xs[0], s2 = xs[1];
                     const int a2 = __float_as_int(xs[2]);
                     if constexpr (GREEDY) {
@@ -478,22 +514,12 @@ void draft_persist(PersistArgs P) {
                 }
                 const uint64_t tag = (uint64_t)(k + 1) << 32;
                 uint64_t* e64 = reinterpret_cast<uint64_t*>(P.sup) +
-                                2 * ((size_t)g * bpad + rb * kStreamRows + tid);
+                                2 * ((size_t)g * bpad + r0 + tid);
                 coh_store<true>(e64, tag | __float_as_uint(m));
                 coh_store<true>(e64 + 1, tag | (GREEDY ? (uint32_t)a : __float_as_uint(s)));
             }
             __syncthreads();   // LDS (E, ring, xsum) is reused by the next row block
         }
-        // 5. draw the tokens (each finalize waits for its row's shares).
-        for (int b = g + NG * wave; b < B; b += NG * kPersistWaves) {
-            int lane = lane0;
-            asm volatile("" : "+v"(lane));
-            const bool one = nrb == 1;   // E and the tokens of every row are in LDS
-            finalize_row_stream<true, true>(F, b, k, lane, one ? xprev : nullptr,
-                                      one ? reinterpret_cast<const uint16_t*>(e_lds) : nullptr);
-        }
-        if (k + 1 < G && !token_sync(P.bar, F.tflag, B, k + 1, nrb == 1 ? xprev : nullptr, &ok_s))
-            return;
     }
 }
 
@@ -506,8 +532,8 @@ template <> struct PersistShape<4> { static constexpr int NB = 20, NR = 16; };
 
 template <int NKS>
 static size_t persist_lds() {
-    return (size_t)kStreamRows * NKS * 16 * 2 + (size_t)kPersistWaves * PersistShape<NKS>::NR * kPersistUnit +
-           kStreamRows * sizeof(int) + (size_t)kPersistWaves * kStreamRows * 3 * sizeof(float);
+    return (size_t)kPersistRows * NKS * 16 * 2 + (size_t)kPersistWaves * PersistShape<NKS>::NR * kPersistUnit +
+           kPersistRows * sizeof(int) + (size_t)kPersistWaves * kPersistRows * 3 * sizeof(float);
 }
 
 static int persist_nks(int r) { return r == 256 ? 16 : (r == 128 ? 8 : (r == 64 ? 4 : 0)); }
@@ -545,12 +571,18 @@ static int persist_device_ok() {
     return ok[dev] > 0 ? ok[dev] : 0;
 }
 
-// Workgroups of the persistent draft: one per CU, at most one per 32-token
-// block and at most kMaxShares (the finalize reads four shares per lane).
-static int persist_grid(int V) {
+// Workgroups of the persistent draft, one per CU: kPersistFinWgs finalize
+// workgroups (fewer on a small device) and nu unit workgroups, at most one per
+// 32-token block and at most kMaxShares (the finalize reads four shares per
+// lane).  Returns nu + nf, or 0 when the device cannot run it.
+static int persist_grid(int V, int* nu_out) {
     const int cus = persist_device_ok();
     const int nblk = (V + kStreamSeg - 1) / kStreamSeg;
-    return std::min(std::min(cus, nblk), kMaxShares);
+    const int nf = std::max(1, std::min(kPersistFinWgs, cus / 16));
+    const int nu = std::min(std::min(cus - nf, nblk), kMaxShares);
+    if (nu <= 0) return 0;
+    if (nu_out) *nu_out = nu;
+    return nu + nf;
 }
 
 bool draft_persists(const DraftArgs& a) {
@@ -558,10 +590,10 @@ bool draft_persists(const DraftArgs& a) {
     if (!(a.head == kHeadMarkov && a.w_bf16 && a.u_bf16 && !a.q_logits && (a.V % 8) == 0 &&
           persist_nks(a.r) != 0 && a.B > 0 && a.gamma > 0))
         return false;
-    const int ng = persist_grid(a.V);
-    if (ng <= 0) return false;
+    int nu = 0;
+    if (persist_grid(a.V, &nu) <= 0) return false;
     const int nblk = (a.V + kStreamSeg - 1) / kStreamSeg;
-    return (nblk + ng - 1) / ng <= kPersistWaves * persist_nb(a.r);   // <= 20 blocks per share
+    return (nblk + nu - 1) / nu <= kPersistWaves * persist_nb(a.r);   // <= 20 blocks per share
 }
 
 template <int NKS>
@@ -586,7 +618,8 @@ static hipError_t launch_persist(const PersistArgs& p, int ng, bool greedy, hipS
 }
 
 hipError_t draft_persist_launch(const DraftArgs& a, unsigned* bar, hipStream_t s) {
-    const int ng = persist_grid(a.V);
+    int nu = 0;
+    const int ng = persist_grid(a.V, &nu);
     if (ng <= 0 || !bar || !a.tflag || !a.W2T) return hipErrorInvalidValue;
     PersistArgs p{};
     FinStreamArgs& f = p.fin;
@@ -595,7 +628,7 @@ hipError_t draft_persist_launch(const DraftArgs& a, unsigned* bar, hipStream_t s
     f.sup = a.sup;
     f.segm = reinterpret_cast<const float*>(a.stats);
     f.gsums = a.gsums;
-    f.ws = ng;
+    f.ws = nu;
     f.nunit = nblk;
     f.seg_mult = 1;
     f.bpad = bpad;
@@ -626,7 +659,8 @@ hipError_t draft_persist_launch(const DraftArgs& a, unsigned* bar, hipStream_t s
     p.V = a.V;
     p.nblk = nblk;
     p.bpad = bpad;
-    const size_t ns = (size_t)ng * bpad;
+    p.nu = nu;
+    const size_t ns = (size_t)nu * bpad;
     const size_t nreset = std::max<size_t>(std::max(kBarWords, a.B), 2 * ns);
     const unsigned nblk_reset = (unsigned)std::min<size_t>((nreset + 255) / 256, 1024);
     hipLaunchKernelGGL(persist_bar_reset, dim3(nblk_reset), dim3(256), 0, s, bar, a.tflag, a.B,

@@ -61,8 +61,9 @@ struct FinStreamArgs {
 // xprev_lds / e_lds (optional, row b < 128): the conditioning token of row b
 // (-1 if invalid) and the rows W1[prev] of the 128-row block already in LDS,
 // 16-byte chunk c of row m in slot c ^ (m & 7).
+// Returns false only when a tagged wait gave up (abort word set).
 template <bool COH, bool TAGGED = false>
-__device__ __forceinline__ void finalize_row_stream(const FinStreamArgs& A, int b, int k,
+__device__ __forceinline__ bool finalize_row_stream(const FinStreamArgs& A, int b, int k,
                                                     int lane, const int* xprev_lds = nullptr,
                                                     const uint16_t* e_lds = nullptr) {
     const size_t outi = (size_t)b * A.gamma + k;
@@ -82,7 +83,7 @@ __device__ __forceinline__ void finalize_row_stream(const FinStreamArgs& A, int 
             if (A.q_tok) A.q_tok[outi] = NAN;
             put_token(-1);
         }
-        return;
+        return true;
     }
     const float u = A.uniforms ? A.uniforms[outi] : counter_uniform(A.seed, A.offset, b, k, 0);
     // this lane's W1 slice for the rebuild (lane = 8t + sl: rank slice sl)
@@ -132,7 +133,7 @@ __device__ __forceinline__ void finalize_row_stream(const FinStreamArgs& A, int 
             if (__all(up)) break;
             if (coh_load<true>(A.abort_word) != 0u || polls > A.poll_limit) {
                 if (lane == 0) coh_store<true>(A.abort_word, 1u);
-                return;
+                return false;
             }
             __builtin_amdgcn_s_sleep(1);
         }
@@ -164,7 +165,7 @@ __device__ __forceinline__ void finalize_row_stream(const FinStreamArgs& A, int 
             if (A.q_tok) A.q_tok[outi] = M == -INFINITY ? NAN : 1.0f;
             put_token((M == -INFINITY) ? -1 : AM);
         }
-        return;
+        return true;
     }
     double w[4];
     double lsum = 0.0;
@@ -290,6 +291,7 @@ __device__ __forceinline__ void finalize_row_stream(const FinStreamArgs& A, int 
         if (A.q_tok) A.q_tok[outi] = (float)((double)__expf((lsel - M) * invT) / Z);
         put_token(min(seg * kStreamSeg + grp * 8 + tsel, V - 1));
     }
+    return true;
 }
 
 }  // namespace specdec

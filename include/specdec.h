@@ -150,10 +150,11 @@ spec_status_t spec_pack_w2(const void *W2, void *W2T, int r, int V, void *stream
 /*
  * Engine of the q-free Markov draft (bf16 U and weights, q_logits == NULL).
  * 1 (the default): where the shape allows it (V % 8 == 0, r in {64, 128,
- * 256}, the device's share of packed W2 fitting in registers: V <= 163840
+ * 256}, the device's share of packed W2 fitting in registers: V <= 153600
  * at r = 256 on 256 CUs, twice that per halving of r), every position runs in
- * one cooperative launch that keeps W2 on chip and synchronises the
- * workgroups between positions with grid barriers.  0: two launches per
+ * one cooperative launch that keeps W2 on chip: most workgroups compute the
+ * bias and softmax summaries of 64-row blocks, a few draw the tokens, and
+ * they synchronise through tagged summary and token words.  0: two launches per
  * position (streaming tile + finalize).  Both give the same draws up to the
  * rounding of the sums.  Process-wide; returns the previous setting.
  */

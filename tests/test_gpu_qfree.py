@@ -46,18 +46,20 @@ DRAFT_CASES = [
     (1, 3, 5000, 64, "bf16", 1.0),      # one row: 31 absent rows in its group
     (33, 2, 8, 64, "bf16", 1.0),        # V = 8: one block, one workgroup
     (5, 2, 1000, 128, "bf16", 0.7),     # 32 blocks: one per workgroup, three idle waves
-    (4, 2, 163840, 256, "bf16", 1.0),   # 20 blocks per workgroup: all register blocks in use
-    (3, 1, 163848, 256, "bf16", 1.0),   # one block more than fits: per-position kernels
+    (4, 2, 153600, 256, "bf16", 1.0),   # 20 blocks per workgroup: all register blocks in use
+    (3, 1, 153608, 256, "bf16", 1.0),   # one block more than fits: per-position kernels
+    (130, 3, 8192, 128, "bf16", 1.0),   # three 64-row blocks, the last one of 2 rows
 ]
 
 
 def persist_eligible(B, gamma, V, r, udt):
-    """Shapes the library runs as one persistent launch (256 CUs: at most
-    20 / 40 / 80 blocks of 32 tokens per workgroup for r = 256 / 128 / 64)."""
+    """Shapes the library runs as one persistent launch (256 CUs, 16 of them
+    finalizing: at most 20 / 40 / 80 blocks of 32 tokens per unit workgroup
+    for r = 256 / 128 / 64)."""
     if udt != "bf16" or V % 8 or r not in (64, 128, 256) or B < 1 or gamma < 1:
         return False
     nblk = (V + 31) // 32
-    ng = min(256, nblk)
+    ng = min(240, nblk)
     return -(-nblk // ng) <= 4 * {256: 5, 128: 10, 64: 20}[r]
 
 
