@@ -525,8 +525,11 @@ void draft_persist(PersistArgs P) {
 
 // Blocks per wave held in registers (320 VGPRs of W2 operands) and U ring
 // slots per wave (LDS: E rows + rings + tokens + run summaries <= 160 KB).
+// At r = 256 a shallow ring (four units ahead) is faster than a deep one: a
+// row block's first prefetch is issued by every CU at once and queues behind
+// the whole chip's, and fewer loads in flight also shorten the unit loop.
 template <int NKS> struct PersistShape;
-template <> struct PersistShape<16> { static constexpr int NB = 5, NR = 11; };
+template <> struct PersistShape<16> { static constexpr int NB = 5, NR = 6; };
 template <> struct PersistShape<8> { static constexpr int NB = 10, NR = 15; };
 template <> struct PersistShape<4> { static constexpr int NB = 20, NR = 16; };
 
