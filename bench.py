@@ -179,8 +179,10 @@ def main():
     ap.add_argument("--workload", default="markov-152k-b128")
     ap.add_argument("--path", choices=("qfree", "materialized"), default="qfree",
                     help="q-free cycle (no draft-logit tensor) or materialized draft logits")
-    ap.add_argument("--engine", choices=("persistent", "per_position"), default="persistent",
-                    help="q-free draft: one persistent launch, or two launches per position")
+    ap.add_argument("--engine", choices=("persistent", "persistent_coop", "per_position"),
+                    default="persistent",
+                    help="q-free draft: one persistent launch (plain, or cooperative), or two "
+                         "launches per position")
     ap.add_argument("--sigma", type=float, default=None, help="override target/draft noise")
     ap.add_argument("--cpu-sample", type=int, default=64, help="requests timed on the oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -231,7 +233,7 @@ def main():
     U, P = to_dev(wl["U"], lb), to_dev(wl["P"], lb)
     W1, W2, x0 = to_dev(wl["W1"], wbt), to_dev(wl["W2"], wbt), to_dev(wl["x0"])
     qfree = args.path == "qfree"
-    sd.spec_draft_set_persistent(args.engine == "persistent")
+    sd.spec_draft_set_persistent({"per_position": 0, "persistent": 1, "persistent_coop": 2}[args.engine])
     W2T = sd.spec_pack_w2(W2)          # once per model load
     d_out = dict(tokens=torch.empty((B, g), dtype=torch.int32, device=dev),
                  q_logZ=torch.empty((B, g), dtype=torch.float32, device=dev),

@@ -293,11 +293,16 @@ def spec_verify(P, Q, draft, T=1.0, *, gamma_max=None, lens=None, p_row_off=None
     return out
 
 
-def spec_draft_set_persistent(enable):
-    """Engine of the q-free Markov draft: True runs all positions in one
-    persistent launch where the shape allows it, False two launches per
-    position.  Returns the previous setting."""
-    return bool(load_library().spec_draft_set_persistent(1 if enable else 0))
+def spec_draft_set_persistent(mode):
+    """Engine of the q-free Markov draft: 1 (or True) one persistent plain
+    launch for all positions where the shape allows it, 2 the same kernel
+    under a cooperative launch, 0 (or False) two launches per position.
+    Returns the previous mode."""
+    mode = int(mode)
+    was = load_library().spec_draft_set_persistent(mode)
+    if was < 0:
+        raise SpecError(f"spec_draft_set_persistent: no mode {mode}")
+    return was
 
 
 def spec_profile_enable(kernel):

@@ -95,13 +95,17 @@ constexpr int kBarWords = 8;
 static_assert(kBarWords * sizeof(unsigned) <= kPersistBarBytes, "barrier words");
 
 // Launch preamble: clears the abort word, the token words [B] and the tagged
-// share summaries [ns] (two 64-bit words each), and sets the -inf chunk.
+// share summaries [ns] (two 64-bit words each), sets the -inf chunk, and
+// fills the output tokens [ntok] with -1, which is what a draw that never
+// happens (a wait that gave up) leaves behind.
 __global__ void persist_bar_reset(unsigned* bar, uint64_t* tflag, int B, uint64_t* sup64,
-                                  size_t ns) {
+                                  size_t ns, int32_t* tokens, size_t ntok) {
     const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
     if (t < (size_t)kBarWords) bar[t] = (t >= (size_t)kBarNegInf) ? 0xFF80FF80u : 0u;
     if (t < (size_t)B) tflag[t] = 0u;
-    for (size_t i = t; i < 2 * ns; i += (size_t)gridDim.x * blockDim.x) sup64[i] = 0u;
+    for (size_t i = t; i < 2 * ns; i += stride) sup64[i] = 0u;
+    for (size_t i = t; i < ntok; i += stride) tokens[i] = -1;
 }
 
 // Wait until the token words of rows r0 .. r0 + rows - 1 (rows <= 64) carry
@@ -550,11 +554,14 @@ static int persist_nb(int r) {
     }
 }
 
-static bool g_persist_enabled = true;
+// 0: per-position kernels; 1: persistent, plain launch; 2: persistent,
+// cooperative launch.
+static int g_persist_mode = 1;
 
-int persist_set_enabled(int enable) {
-    const int was = g_persist_enabled ? 1 : 0;
-    g_persist_enabled = enable != 0;
+int persist_set_mode(int mode) {
+    if (mode < 0 || mode > 2) return -1;
+    const int was = g_persist_mode;
+    g_persist_mode = mode;
     return was;
 }
 
@@ -589,7 +596,7 @@ static int persist_grid(int V, int* nu_out) {
 }
 
 bool draft_persists(const DraftArgs& a) {
-    if (!g_persist_enabled) return false;
+    if (g_persist_mode == 0) return false;
     if (!(a.head == kHeadMarkov && a.w_bf16 && a.u_bf16 && !a.q_logits && (a.V % 8) == 0 &&
           persist_nks(a.r) != 0 && a.B > 0 && a.gamma > 0))
         return false;
@@ -616,8 +623,15 @@ static hipError_t launch_persist(const PersistArgs& p, int ng, bool greedy, hipS
     }
     PersistArgs arg = p;
     void* args[] = {&arg};
-    return hipLaunchCooperativeKernel(fn, dim3(ng), dim3(kPersistWaves * 64), args,
-                                      (unsigned)lds, s);
+    // Every workgroup must be resident at once (one per CU, grid <= CUs).  A
+    // cooperative launch guarantees it by running alone on the device, which
+    // costs ~10 us of idle device on each side of the launch; a plain launch
+    // gets it whenever no other kernel holds CUs meanwhile, and otherwise the
+    // bounded waits give up (abort word set, tokens left at -1).
+    if (g_persist_mode == 2)
+        return hipLaunchCooperativeKernel(fn, dim3(ng), dim3(kPersistWaves * 64), args,
+                                          (unsigned)lds, s);
+    return hipLaunchKernel(fn, dim3(ng), dim3(kPersistWaves * 64), args, (unsigned)lds, s);
 }
 
 hipError_t draft_persist_launch(const DraftArgs& a, unsigned* bar, hipStream_t s) {
@@ -664,10 +678,11 @@ hipError_t draft_persist_launch(const DraftArgs& a, unsigned* bar, hipStream_t s
     p.bpad = bpad;
     p.nu = nu;
     const size_t ns = (size_t)nu * bpad;
-    const size_t nreset = std::max<size_t>(std::max(kBarWords, a.B), 2 * ns);
+    const size_t ntok = (size_t)a.B * a.gamma;
+    const size_t nreset = std::max<size_t>(std::max<size_t>(kBarWords, a.B), std::max(2 * ns, ntok));
     const unsigned nblk_reset = (unsigned)std::min<size_t>((nreset + 255) / 256, 1024);
     hipLaunchKernelGGL(persist_bar_reset, dim3(nblk_reset), dim3(256), 0, s, bar, a.tflag, a.B,
-                       reinterpret_cast<uint64_t*>(a.sup), ns);
+                       reinterpret_cast<uint64_t*>(a.sup), ns, a.tokens, ntok);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     switch (persist_nks(a.r)) {

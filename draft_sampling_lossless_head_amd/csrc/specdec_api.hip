@@ -205,7 +205,7 @@ int spec_version(void) { return 100; }
 
 const char* spec_last_error(void) { return g_err.c_str(); }
 
-int spec_draft_set_persistent(int enable) { return persist_set_enabled(enable); }
+int spec_draft_set_persistent(int mode) { return persist_set_mode(mode); }
 
 spec_status_t spec_philox_uniforms(uint64_t seed, uint32_t offset, uint32_t stream, int B, int K,
                                    float* out, void* stream_handle) {

@@ -149,16 +149,29 @@ spec_status_t spec_pack_w2(const void *W2, void *W2T, int r, int V, void *stream
 
 /*
  * Engine of the q-free Markov draft (bf16 U and weights, q_logits == NULL).
- * 1 (the default): where the shape allows it (V % 8 == 0, r in {64, 128,
- * 256}, the device's share of packed W2 fitting in registers: V <= 153600
+ *
+ * 1 (the default) and 2: where the shape allows it (V % 8 == 0, r in {64,
+ * 128, 256}, the device's share of packed W2 fitting in registers: V <= 153600
  * at r = 256 on 256 CUs, twice that per halving of r), every position runs in
- * one cooperative launch that keeps W2 on chip: most workgroups compute the
- * bias and softmax summaries of 64-row blocks, a few draw the tokens, and
- * they synchronise through tagged summary and token words.  0: two launches per
- * position (streaming tile + finalize).  Both give the same draws up to the
- * rounding of the sums.  Process-wide; returns the previous setting.
+ * one launch of one workgroup per CU that keeps W2 on chip: most workgroups
+ * compute the bias and softmax summaries of 64-row blocks, a few draw the
+ * tokens, and they synchronise through tagged summary and token words, so
+ * every workgroup must be resident at once.
+ *   1: plain launch.  Residency holds when no other kernel keeps CUs busy
+ *      during the draft (e.g. the draft and the target model on one
+ *      stream).  If it does not hold, the draft's bounded waits give up
+ *      after about a second and the rows not drawn keep token -1 (the
+ *      verification then marks those requests invalid).
+ *   2: cooperative launch: the runtime guarantees residency by running the
+ *      launch alone on the device, at the cost of ~20 us of idle device per
+ *      call.  For callers that run other kernels concurrently.
+ * 0: two launches per position (streaming tile + finalize).
+ *
+ * All modes give the same draws up to the rounding of the sums (1 and 2 are
+ * the same kernel and give identical results).  Process-wide; returns the
+ * previous mode, or -1 (nothing changed) for a mode outside 0..2.
  */
-int spec_draft_set_persistent(int enable);
+int spec_draft_set_persistent(int mode);
 
 /*
  * ---------------------------------------------------------------------------

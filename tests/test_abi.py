@@ -187,8 +187,12 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
 
 
 def test_draft_engine_switch(lib):
-    """The draft engine setting is process-wide and returns the previous value."""
+    """The draft engine setting is process-wide and returns the previous value;
+    a mode outside 0..2 is refused and changes nothing."""
     was = lib.spec_draft_set_persistent(0)
-    assert was in (0, 1)
+    assert was in (0, 1, 2)
     assert lib.spec_draft_set_persistent(1) == 0
-    assert lib.spec_draft_set_persistent(was) == 1
+    assert lib.spec_draft_set_persistent(2) == 1
+    assert lib.spec_draft_set_persistent(7) == -1
+    assert lib.spec_draft_set_persistent(-1) == -1
+    assert lib.spec_draft_set_persistent(was) == 2

@@ -156,6 +156,33 @@ def test_qfree_draft_full_size_sampled(orc, engine):
     assert np.all(np.isfinite(g["q_logZ"])) and np.all(g["q_tok_prob"] > 0)
 
 
+@pytest.mark.parametrize("B,gamma,V,r", [(128, 16, 151936, 256), (130, 3, 8192, 128)])
+def test_qfree_draft_launch_modes(B, gamma, V, r):
+    """The persistent draft under a plain launch (mode 1) and a cooperative
+    launch (mode 2) is the same kernel: identical tokens, log Z and q(x_k)."""
+    sd = require_gpu()
+    assert persist_eligible(B, gamma, V, r, "bf16")
+    note(f"persistent draft launch modes B={B} gamma={gamma} V={V} r={r}")
+    cfg = dict(workloads.CONFIGS["markov-152k-b128"])
+    wl = workloads.make_markov(cfg, B=B, gamma=gamma, V=V, r=r)
+    args = (dev(wl["U"], "bf16"), dev(wl["x0"]), dev(wl["W1"], "bf16"), dev(wl["W2"], "bf16"), 1.0)
+    res = {}
+    was = sd.spec_draft_set_persistent(1)
+    try:
+        for mode in (1, 2):
+            sd.spec_draft_set_persistent(mode)
+            sd.spec_profile_enable("draft_persist")
+            res[mode] = host(sd.spec_draft_sample_markov(*args, q_free=True, seed=5, offset=2))
+            launches, _ = sd.spec_profile_read()
+            sd.spec_profile_enable(None)
+            assert launches == 1
+    finally:
+        sd.spec_draft_set_persistent(was)
+    for k in ("tokens", "q_logZ", "q_tok_prob"):
+        np.testing.assert_array_equal(res[1][k], res[2][k], err_msg=k)
+    assert np.all((res[1]["tokens"] >= 0) & (res[1]["tokens"] < V))
+
+
 def test_qfree_draft_packed_w2_and_uniforms(orc):
     """A W2T packed once by spec_pack_w2 gives the same result as W2, and
     caller uniforms replace the counter stream."""
