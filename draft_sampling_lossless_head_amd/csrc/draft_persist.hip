@@ -1,6 +1,6 @@
 // Persistent, weight-stationary q-free Markov draft ("[논문리뷰] DSpark ...",
 // §1.2 Sequential stage, Markov-head equation): every position of every
-// request in one cooperative launch of one workgroup per CU.
+// request in one launch of one workgroup per CU, all resident at once.
 //
 // The per-position kernels read all of the packed W2 image once per position.
 // Here each unit workgroup owns a fixed contiguous range of 32-token blocks
@@ -32,10 +32,11 @@
 //
 // MFMA row i = 8g + 4h + c of a block holds token 16h + 8 (g & 1) + 4 (g >> 1)
 // + c, so a lane's 16 accumulators are 16 contiguous tokens of one row and its
-// U values are two 16-byte chunks.  Every wait is a bounded poll: the launch
-// is cooperative (all workgroups resident), and if a wait still does not
-// complete within the poll limit the workgroup sets an abort word the host
-// can read and every other workgroup leaves at its next poll.
+// U values are two 16-byte chunks.  Every workgroup must be resident at once
+// (one per CU: a cooperative launch guarantees it, a plain launch gets it on an
+// otherwise idle device).  Every wait is a bounded poll: if a wait does not
+// complete within the poll limit the workgroup sets an abort word and every
+// other workgroup leaves at its next poll, so the launch always ends.
 #include <algorithm>
 #include <climits>
 
