@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "verified+drafted tokens/s at B=128,gamma=16,V=152k; % of HBM roofline"
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
+MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 
 
 def log(*a):
@@ -98,6 +99,54 @@ def measured_traffic(kernel, workload):
     if t.get("source_sha") != source_sha(KERNEL_SOURCES[kernel]):
         return None
     return t.get("traffic_bytes_per_launch")
+
+
+def bias_flops(wl):
+    """Algorithmic flops of the Markov bias contraction E . W2 per launch of
+    each kernel that performs it (2 B r V per draft position)."""
+    B, g, V, r = wl["B"], wl["gamma"], wl["V"], wl["r"]
+    return {"draft_persist": 2.0 * B * r * V * g, "draft_tile_qfree": 2.0 * B * r * V,
+            "draft_tile": 2.0 * B * r * V}
+
+
+def measured_mfma(kernel, workload):
+    """Matrix-core busy fraction from profiles/<kernel>__<workload>.mfma.json,
+    or None when missing or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}__{workload}.mfma.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_sha") != source_sha(KERNEL_SOURCES[kernel]):
+        return None
+    return t.get("mfma_busy_frac")
+
+
+def mfma_from_sq(sq_csv, kernel_substr, label, workload):
+    """Matrix-core busy fraction of one kernel from a rocprofv3 --pmc run with
+    SQ_VALU_MFMA_BUSY_CYCLES (cycles, summed over SIMDs) and SQ_WAVE_CYCLES
+    (quad-cycles, summed over waves): busy / (4 x wave cycles), i.e. the share
+    of the kernel's wave-occupied SIMD cycles in which the matrix core works
+    (one wave per SIMD in the persistent draft).  Writes
+    profiles/<label>__<workload>.mfma.json tagged with the kernel's source hash."""
+    import csv
+
+    vals = {}
+    with open(sq_csv) as f:
+        for r in csv.DictReader(f):
+            if kernel_substr in r["Kernel_Name"]:
+                vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    if "SQ_VALU_MFMA_BUSY_CYCLES" not in vals or "SQ_WAVE_CYCLES" not in vals:
+        raise SystemExit(f"no SQ_VALU_MFMA_BUSY_CYCLES / SQ_WAVE_CYCLES for {kernel_substr!r}")
+    avg = {k: sum(v) / len(v) for k, v in vals.items()}
+    rec = dict(kernel=label, kernel_match=kernel_substr, workload=workload,
+               counters_per_dispatch=avg, dispatches=len(vals["SQ_WAVE_CYCLES"]),
+               mfma_busy_frac=avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (4.0 * avg["SQ_WAVE_CYCLES"]),
+               source_sha=source_sha(KERNEL_SOURCES[label]))
+    path = os.path.join(ROOT, "profiles", f"{label}__{workload}.mfma.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
 
 
 def traffic_from_pmc(fetch_csv, write_csv, kernel_substr, label, workload, probe_bytes):
@@ -193,9 +242,15 @@ def main():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU run: turn two rocprofv3 --pmc counter CSVs into the traffic "
                          "record of --traffic-kernel")
+    ap.add_argument("--mfma-from", metavar="SQ_CSV",
+                    help="no GPU run: turn a rocprofv3 --pmc run with SQ_VALU_MFMA_BUSY_CYCLES and "
+                         "SQ_WAVE_CYCLES into the matrix-core record of --traffic-kernel")
     ap.add_argument("--traffic-kernel", default="draft_tile_stream<16, false>")
     ap.add_argument("--traffic-label", default="draft_tile_qfree")
     args = ap.parse_args()
+    if args.mfma_from:
+        mfma_from_sq(args.mfma_from, args.traffic_kernel, args.traffic_label, args.workload)
+        return
     if args.traffic_from:
         traffic_from_pmc(args.traffic_from[0], args.traffic_from[1], args.traffic_kernel,
                          args.traffic_label, args.workload, (args.copy_probe_mib or 1024) << 20)
@@ -323,6 +378,14 @@ def main():
                     traffic=measured_traffic(dom, args.workload), kernel=dom,
                     alg_bytes_per_launch=nbytes[dom],
                     avg_launch_us=round(kernels[dom]["avg_us"], 2))
+    fl = bias_flops(wl)
+    mk = max((k for k in kernels if k in fl), key=lambda k: kernels[k]["us_per_step"], default=None)
+    mfma = None
+    if mk is not None:
+        tf = fl[mk] / (kernels[mk]["avg_us"] * 1e-6) / 1e12
+        mfma = dict(kernel=mk, dtype="bf16", flops_per_launch=fl[mk], achieved=round(tf, 1),
+                    peak=MFMA_PEAK_TFLOPS, unit="TFLOP/s", frac=round(tf / MFMA_PEAK_TFLOPS, 4),
+                    busy_frac_counter=measured_mfma(mk, args.workload))
     log("kernels: " + json.dumps({k: {a: round(b, 2) for a, b in v.items()}
                                   for k, v in kernels.items()}))
 
@@ -337,6 +400,7 @@ def main():
                    "verify": "fixed-length", "path": args.path,
                    "engine": args.engine if qfree else "per_position"},
         "roofline": roofline,
+        "mfma": mfma,
         "breakdown": {
             "drafted_per_s": None, "verified_per_s": None,
             "mean_tau": round(tau, 4),
