@@ -69,6 +69,8 @@ def load_library():
     lib.spec_verify_markov.restype = i32
     lib.spec_draft_set_persistent.argtypes = [i32]
     lib.spec_draft_set_persistent.restype = i32
+    lib.spec_draft_set_poll_limit.argtypes = [u32]
+    lib.spec_draft_set_poll_limit.restype = u32
     lib.spec_profile_enable.argtypes = [ctypes.c_char_p]
     lib.spec_profile_enable.restype = i32
     lib.spec_profile_read.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_double)]
@@ -291,6 +293,12 @@ def spec_verify(P, Q, draft, T=1.0, *, gamma_max=None, lens=None, p_row_off=None
         nws, _stream(stream))
     _check(st, "spec_verify")
     return out
+
+
+def spec_draft_set_poll_limit(polls):
+    """Wait limit of the persistent draft in polls (0: the default); a
+    testing aid.  Returns the previous limit."""
+    return int(load_library().spec_draft_set_poll_limit(int(polls)))
 
 
 def spec_draft_set_persistent(mode):

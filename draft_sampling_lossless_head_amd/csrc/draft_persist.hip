@@ -116,7 +116,8 @@ __global__ void persist_bar_reset(unsigned* bar, uint64_t* tflag, int B, uint64_
 // Bounded: past the poll limit, or when another wave set the abort word,
 // the abort word is set and false returned.
 __device__ __forceinline__ bool rows_tokens(unsigned* bar, const uint64_t* tflag, int r0, int rows,
-                                            unsigned k, int V, int* xprev, int* ok_s) {
+                                            unsigned k, int V, unsigned limit, int* xprev,
+                                            int* ok_s) {
     if (threadIdx.x < 64) {
         int lane = threadIdx.x;
         asm volatile("" : "+v"(lane));   // recomputed here, not kept live across the kernel
@@ -133,7 +134,7 @@ __device__ __forceinline__ bool rows_tokens(unsigned* bar, const uint64_t* tflag
                 xprev[lane] = (tok >= 0 && tok < V) ? tok : -1;
                 break;
             }
-            if (coh_load<true>(bar + kBarAbort) != 0u || polls > kBarrierPolls) {
+            if (coh_load<true>(bar + kBarAbort) != 0u || polls > limit) {
                 if (lane == 0) coh_store<true>(bar + kBarAbort, 1u);
                 ok = 0;
                 break;
@@ -306,7 +307,8 @@ void draft_persist(PersistArgs P) {
                     xprev[tid] = (prev >= 0 && prev < V) ? prev : -1;
                 }
                 __syncthreads();
-            } else if (!rows_tokens(P.bar, F.tflag, r0, rows, (unsigned)k, V, xprev, &ok_s)) {
+            } else if (!rows_tokens(P.bar, F.tflag, r0, rows, (unsigned)k, V, F.poll_limit, xprev,
+                                    &ok_s)) {
                 return;
             }
             // 2. E rows into LDS, then the first D units of U.
@@ -559,6 +561,14 @@ static int persist_nb(int r) {
 // cooperative launch.
 static int g_persist_mode = 1;
 
+static unsigned g_poll_limit = kBarrierPolls;
+
+unsigned persist_set_poll_limit(unsigned polls) {
+    const unsigned was = g_poll_limit;
+    g_poll_limit = polls == 0 ? kBarrierPolls : polls;
+    return was;
+}
+
 int persist_set_mode(int mode) {
     if (mode < 0 || mode > 2) return -1;
     const int was = g_persist_mode;
@@ -667,7 +677,7 @@ hipError_t draft_persist_launch(const DraftArgs& a, unsigned* bar, hipStream_t s
     f.r = a.r;
     f.tflag = a.tflag;
     f.abort_word = bar + kBarAbort;
-    f.poll_limit = kBarrierPolls;
+    f.poll_limit = g_poll_limit;
     p.segm = reinterpret_cast<float*>(a.stats);
     p.gsums = a.gsums;
     p.sup = a.sup;

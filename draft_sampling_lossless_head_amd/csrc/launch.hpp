@@ -123,7 +123,8 @@ hipError_t draft_finalize_launch(const DraftArgs& a, int k, hipStream_t s);
 constexpr size_t kPersistBarBytes = 2048;   // abort word, -inf chunk, 256 arrival flags
 bool draft_persists(const DraftArgs& a);
 hipError_t draft_persist_launch(const DraftArgs& a, unsigned* bar, hipStream_t s);
-int persist_set_mode(int mode);   // 0 per-position, 1 persistent, 2 persistent (cooperative launch)
+int persist_set_mode(int mode);
+unsigned persist_set_poll_limit(unsigned polls);   // 0: the default   // 0 per-position, 1 persistent, 2 persistent (cooperative launch)
 // W2 [r, V] bf16 -> packed image of w2p_bytes(r, V) bytes.
 hipError_t w2_pack_launch(const uint16_t* W2, uint16_t* W2P, int r, int V, hipStream_t s);
 // Recompute the logits of row b at position row_pos[b] (bit-identical to the

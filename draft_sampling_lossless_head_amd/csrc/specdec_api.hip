@@ -207,6 +207,8 @@ const char* spec_last_error(void) { return g_err.c_str(); }
 
 int spec_draft_set_persistent(int mode) { return persist_set_mode(mode); }
 
+unsigned spec_draft_set_poll_limit(unsigned polls) { return persist_set_poll_limit(polls); }
+
 spec_status_t spec_philox_uniforms(uint64_t seed, uint32_t offset, uint32_t stream, int B, int K,
                                    float* out, void* stream_handle) {
     g_err.clear();

@@ -295,6 +295,18 @@ spec_status_t spec_verify_markov(
 spec_status_t spec_profile_enable(const char *kernel);
 spec_status_t spec_profile_read(int *launches, double *total_ms);
 
+/*
+ * Wait limit of the persistent draft (testing aid; not needed for correct
+ * use).  Every wait of the persistent draft (a unit workgroup for the token
+ * words of its rows, a finalize wave for the share summaries of its row) is a
+ * poll that gives up after `polls` polls (about 1 us each on an idle device):
+ * it sets the launch's abort word, every workgroup leaves at its next poll,
+ * and the rows not drawn keep token -1.  0 restores the default (2^20 polls).
+ * Lets a test force that path from the host.  Process-wide; applies to later
+ * launches; returns the previous limit.
+ */
+unsigned spec_draft_set_poll_limit(unsigned polls);
+
 #ifdef __cplusplus
 }
 #endif

@@ -35,7 +35,8 @@ def test_header_declares_the_boundary():
               "spec_draft_markov_workspace_size", "spec_draft_rnn_workspace_size",
               "spec_verify_workspace_size", "spec_philox_uniforms", "spec_last_error",
               "spec_version", "spec_pack_w2", "spec_pack_w2_bytes", "spec_verify_markov",
-              "spec_verify_markov_workspace_size", "spec_draft_set_persistent"):
+              "spec_verify_markov_workspace_size", "spec_draft_set_persistent",
+              "spec_draft_set_poll_limit"):
         assert n in names
 
 
@@ -184,6 +185,19 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(api, "_LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(api.SpecError):
         api.load_library()
+
+
+def test_draft_poll_limit(lib):
+    """The wait limit is process-wide, returns the previous value, and 0
+    restores the default."""
+    import ctypes
+    lib.spec_draft_set_poll_limit.argtypes = [ctypes.c_uint32]
+    lib.spec_draft_set_poll_limit.restype = ctypes.c_uint32
+    default = lib.spec_draft_set_poll_limit(0)
+    assert default == 1 << 20
+    assert lib.spec_draft_set_poll_limit(3) == 1 << 20
+    assert lib.spec_draft_set_poll_limit(0) == 3
+    assert lib.spec_draft_set_poll_limit(0) == 1 << 20
 
 
 def test_draft_engine_switch(lib):

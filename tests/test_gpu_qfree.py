@@ -183,6 +183,45 @@ def test_qfree_draft_launch_modes(B, gamma, V, r):
     assert np.all((res[1]["tokens"] >= 0) & (res[1]["tokens"] < V))
 
 
+def test_persistent_draft_gives_up_cleanly():
+    """With a wait limit of two polls (set from the host) the persistent draft
+    gives up on its waits: the launch still ends, every token is -1 or a valid
+    id and some rows stay -1, verification marks the requests holding a -1
+    invalid (accepted -1), and the next call with the default limit matches a
+    call made before."""
+    sd = require_gpu()
+    B, gamma, V, r = 128, 4, 32000, 256
+    assert persist_eligible(B, gamma, V, r, "bf16")
+    note(f"persistent draft wait limit B={B} gamma={gamma} V={V} r={r}")
+    cfg = dict(workloads.CONFIGS["markov-152k-b128"])
+    wl = workloads.make_markov(cfg, B=B, gamma=gamma, V=V, r=r)
+    U, x0 = dev(wl["U"], "bf16"), dev(wl["x0"])
+    W1, W2 = dev(wl["W1"], "bf16"), dev(wl["W2"], "bf16")
+    was_mode = sd.spec_draft_set_persistent(1)
+    try:
+        ref = host(sd.spec_draft_sample_markov(U, x0, W1, W2, 1.0, q_free=True, seed=3))
+        sd.spec_draft_set_poll_limit(2)
+        d = sd.spec_draft_sample_markov(U, x0, W1, W2, 1.0, q_free=True, seed=3)
+        torch.cuda.synchronize()
+        sd.spec_draft_set_poll_limit(0)
+        bad = host(d)
+        again = host(sd.spec_draft_sample_markov(U, x0, W1, W2, 1.0, q_free=True, seed=3))
+        v = host(sd.spec_verify_markov(dev(wl["P"], "bf16"), U, x0, W1, W2, d["tokens"],
+                                       d["q_logZ"], d["q_tok_prob"], 1.0, seed=3))
+    finally:
+        sd.spec_draft_set_poll_limit(0)
+        sd.spec_draft_set_persistent(was_mode)
+    tok = bad["tokens"]
+    assert np.all((tok == -1) | ((tok >= 0) & (tok < V)))
+    assert (tok == -1).any()
+    undrawn = (tok == -1).any(axis=1)
+    note(f"  requests with an undrawn token: {int(undrawn.sum())} of {B}")
+    assert np.all(v["accepted"][undrawn] == -1)
+    assert np.all(v["accepted"][~undrawn] >= 0)
+    for k in ("tokens", "q_logZ", "q_tok_prob"):
+        np.testing.assert_array_equal(ref[k], again[k], err_msg=k)
+
+
 def test_qfree_draft_packed_w2_and_uniforms(orc):
     """A W2T packed once by spec_pack_w2 gives the same result as W2, and
     caller uniforms replace the counter stream."""
