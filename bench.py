@@ -378,6 +378,7 @@ def main():
                     traffic=measured_traffic(dom, args.workload), kernel=dom,
                     alg_bytes_per_launch=nbytes[dom],
                     avg_launch_us=round(kernels[dom]["avg_us"], 2))
+    result_extra = {}
     fl = bias_flops(wl)
     mk = max((k for k in kernels if k in fl), key=lambda k: kernels[k]["us_per_step"], default=None)
     mfma = None
@@ -409,9 +410,29 @@ def main():
             "kernels": {k: {a: round(b, 3) for a, b in v.items()} for k, v in kernels.items()},
         },
     }
+    # The per-position acceptance rate alpha_k = sum min(p_k, q_k) (not part of
+    # the cycle): target rows against the draft's base rows U_k, the same
+    # number of timed launches.  Algorithmic bytes: every used P and U row read
+    # once; the kernel reads them twice (normalisers, then the sums).
+    if wl["logit_dtype"] == "bf16":
+        sd.spec_profile_enable("acceptance_rate")
+        aout = dict(alpha=torch.empty((B, g), dtype=torch.float32, device=dev),
+                    tv=torch.empty((B, g), dtype=torch.float32, device=dev))
+        for i in range(args.steps):
+            sd.spec_acceptance_rate(P, U, T, out=aout)
+        n, ms = sd.spec_profile_read()
+        sd.spec_profile_enable(None)
+        if n:
+            ab = B * g * V * 4
+            us = ms * 1e3 / n
+            result_extra["acceptance_rate"] = dict(
+                avg_us=round(us, 2), alg_bytes_per_launch=ab, achieved_GBs=round(ab / us / 1e3, 1),
+                read_bytes_per_launch=2 * ab, read_GBs=round(2 * ab / us / 1e3, 1),
+                mean_alpha=round(float(aout["alpha"].mean().item()), 4))
     tdraft = sum(kernels[k]["us_per_step"] for k in kernels if k.startswith("draft")
                  or k == "w2_pack")
     tver = sum(kernels[k]["us_per_step"] for k in kernels if k.startswith("verify"))
+    result["breakdown"].update(result_extra)
     if tdraft > 0:
         result["breakdown"]["drafted_per_s"] = round(B * g / (tdraft * 1e-6), 1)
     if tver > 0:

@@ -11,6 +11,7 @@ from .api import (  # noqa: F401
     SpecError,
     library_path,
     load_library,
+    spec_acceptance_rate,
     spec_draft_sample_markov,
     spec_draft_sample_rnn,
     spec_draft_set_persistent,

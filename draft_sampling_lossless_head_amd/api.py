@@ -69,6 +69,9 @@ def load_library():
     lib.spec_verify_markov.restype = i32
     lib.spec_draft_set_persistent.argtypes = [i32]
     lib.spec_draft_set_persistent.restype = i32
+    lib.spec_acceptance_rate.argtypes = [vp, i32, vp, i32, vp, vp, vp, i32, i32, i32, f32, vp,
+                                         vp, vp]
+    lib.spec_acceptance_rate.restype = i32
     lib.spec_draft_set_poll_limit.argtypes = [u32]
     lib.spec_draft_set_poll_limit.restype = u32
     lib.spec_profile_enable.argtypes = [ctypes.c_char_p]
@@ -292,6 +295,51 @@ def spec_verify(P, Q, draft, T=1.0, *, gamma_max=None, lens=None, p_row_off=None
         _ptr(out.get("p_logZ")), _ptr(out.get("q_logZ")), _ptr(out.get("accept_prob")), _ptr(ws),
         nws, _stream(stream))
     _check(st, "spec_verify")
+    return out
+
+
+def spec_acceptance_rate(P, Q, T=1.0, *, gamma_max=None, lens=None, p_row_off=None,
+                         q_row_off=None, want_tv=True, out=None, stream=None):
+    """Acceptance rate alpha[b, k] = sum min(p_k, q_k) (and the total variation
+    1/2 sum |p_k - q_k|) of every drafted position.  Dense: P [B, gamma+1, V],
+    Q [B, gamma, V].  Packed: P and Q [rows, V] with p_row_off / q_row_off
+    int64 [B], lens int32 [B] and gamma_max given.  NaN where a request has no
+    such position."""
+    lib = load_library()
+    _dev(P, "P")
+    _dev(Q, "Q")
+    V = P.shape[-1]
+    if Q.shape[-1] != V:
+        raise SpecError("Q and P must share V")
+    if p_row_off is None:
+        if P.dim() != 3:
+            raise SpecError("dense P must be [B, gamma + 1, V]")
+        B = P.shape[0]
+        if gamma_max is None:
+            gamma_max = P.shape[1] - 1
+        if P.shape != (B, gamma_max + 1, V):
+            raise SpecError("dense P must be [B, gamma_max + 1, V]")
+    else:
+        B = p_row_off.shape[0]
+        if gamma_max is None:
+            raise SpecError("packed rows need gamma_max")
+    if q_row_off is None and Q.shape != (B, gamma_max, V):
+        raise SpecError("dense Q must be [B, gamma_max, V]")
+    for t, n, dt in ((lens, "lens", torch.int32), (p_row_off, "p_row_off", torch.int64),
+                     (q_row_off, "q_row_off", torch.int64)):
+        if t is not None:
+            _dev(t, n)
+            if t.dtype != dt or t.shape != (B,):
+                raise SpecError(f"{n} must be {dt} [B]")
+    if out is None:
+        out = dict(alpha=torch.empty((B, gamma_max), dtype=torch.float32, device=P.device))
+        if want_tv:
+            out["tv"] = torch.empty((B, gamma_max), dtype=torch.float32, device=P.device)
+    st = lib.spec_acceptance_rate(_ptr(P), _dtype_code(P, "P"), _ptr(Q), _dtype_code(Q, "Q"),
+                                  _ptr(lens), _ptr(p_row_off), _ptr(q_row_off), B, gamma_max, V,
+                                  float(T), _ptr(out["alpha"]), _ptr(out.get("tv")),
+                                  _stream(stream))
+    _check(st, "spec_acceptance_rate")
     return out
 
 

@@ -214,6 +214,23 @@ hipError_t verify_launch(const VerifyArgs& a, hipStream_t s);
 hipError_t verify_rows_decide_launch(const VerifyArgs& a, hipStream_t s);
 hipError_t verify_final_launch(const VerifyArgs& a, hipStream_t s);
 
+// Acceptance rate and total variation per drafted position (alpha_kernels.hip).
+struct AlphaArgs {
+    const void* P;              // target rows: dense [B, G + 1, V] or packed
+    int p_bf16;
+    const void* Q;              // draft rows: dense [B, G, V] or packed
+    int q_bf16;
+    const int32_t* lens;        // [B] or null (every request has G positions)
+    const int64_t* p_row_off;   // [B] or null
+    const int64_t* q_row_off;   // [B] or null
+    int B, gamma_max, V;
+    float invT;                 // 1 / T (1 when greedy)
+    int greedy;
+    float* alpha;               // [B, G]
+    float* tv;                  // [B, G] or null
+};
+hipError_t acceptance_rate_launch(const AlphaArgs& a, hipStream_t s);
+
 hipError_t philox_uniforms_launch(uint64_t seed, uint32_t offset, uint32_t stream, int B, int K,
                                   float* out, hipStream_t s);
 

@@ -397,6 +397,40 @@ spec_status_t spec_verify(const void* P, int p_dtype, const void* Q, int q_dtype
     return e == hipSuccess ? SPEC_OK : hip_fail(e, "verify");
 }
 
+spec_status_t spec_acceptance_rate(const void* P, int p_dtype, const void* Q, int q_dtype,
+                                   const int32_t* lens, const int64_t* p_row_off,
+                                   const int64_t* q_row_off, int B, int gamma_max, int V, float T,
+                                   float* alpha, float* tv, void* stream) {
+    g_err.clear();
+    if (B < 0 || gamma_max < 0) return fail(SPEC_ERR_INVALID, "B and gamma_max must be >= 0");
+    if (V <= 0 || V > kMaxV) return fail(SPEC_ERR_INVALID, "V must be in [1, 2^28]");
+    if (spec_status_t st = check_T(T)) return st;
+    if (!dtype_ok(p_dtype) || !dtype_ok(q_dtype)) return fail(SPEC_ERR_UNSUPPORTED, "dtype must be SPEC_F32 or SPEC_BF16");
+    if ((int64_t)B * gamma_max > INT32_MAX) return fail(SPEC_ERR_UNSUPPORTED, "B * gamma_max too large");
+    if (B == 0 || gamma_max == 0) return SPEC_OK;
+    if (!P || !Q || !alpha) return fail(SPEC_ERR_INVALID, "null required pointer (P, Q, alpha)");
+    AlphaArgs a{};
+    a.P = P;
+    a.p_bf16 = p_dtype == SPEC_BF16;
+    a.Q = Q;
+    a.q_bf16 = q_dtype == SPEC_BF16;
+    a.lens = lens;
+    a.p_row_off = p_row_off;
+    a.q_row_off = q_row_off;
+    a.B = B;
+    a.gamma_max = gamma_max;
+    a.V = V;
+    a.greedy = T == 0.0f;
+    a.invT = a.greedy ? 1.0f : 1.0f / T;
+    a.alpha = alpha;
+    a.tv = tv;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* t = prof_begin("acceptance_rate", s);
+    hipError_t e = acceptance_rate_launch(a, s);
+    prof_end(t, s);
+    return e == hipSuccess ? SPEC_OK : hip_fail(e, "acceptance_rate");
+}
+
 size_t spec_pack_w2_bytes(int r, int V) {
     if (r <= 0 || V <= 0 || V > kMaxV) return 0;
     return w2p_bytes(r, V);

@@ -279,6 +279,34 @@ spec_status_t spec_verify_markov(
 
 /*
  * ---------------------------------------------------------------------------
+ * Acceptance rate per drafted position  [VESSL "Speculative Decoding Part 1",
+ * section "수락 규칙": a token drawn from q passes the ratio test with
+ * probability alpha = sum_v min(p(v), q(v)) = 1 - D_TV(p, q)]
+ * ---------------------------------------------------------------------------
+ * For every request b and position k < L_b (L_b = lens[b], or gamma_max when
+ * lens is NULL): p_k = softmax(P row / T), q_k = softmax(Q row / T),
+ *   alpha[b, k] = sum_v min(p_k(v), q_k(v)),
+ *   tv[b, k]    = 1/2 sum_v |p_k(v) - q_k(v)|   (optional; equals 1 - alpha).
+ * T = 0: both are one-hot at their argmax (lowest id on ties), so alpha is 1
+ * when the argmaxes agree and 0 otherwise.  The row layout is spec_verify's:
+ * P dense [B, gamma_max + 1, V] or packed rows from p_row_off[b] on (position
+ * k at row p_row_off[b] + k); Q dense [B, gamma_max, V] or packed from
+ * q_row_off[b] on.  The bonus row of P is not read.  Positions k >= L_b, a
+ * length outside [0, gamma_max] and rows without a finite logit give NaN.
+ *
+ * P, Q, alpha, tv: caller-owned device buffers (f32 or bf16 logits; alpha and
+ * tv fp32 [B, gamma_max]).  No workspace.  Errors: SPEC_ERR_INVALID (null P,
+ * Q or alpha, B or gamma_max < 0, V out of range, T < 0 or not finite),
+ * SPEC_ERR_UNSUPPORTED (dtype), SPEC_ERR_HIP (launch).  One pass for the
+ * normalisers and one for the sums: reads every used P and Q row twice.
+ */
+spec_status_t spec_acceptance_rate(const void *P, int p_dtype, const void *Q, int q_dtype,
+                                   const int32_t *lens, const int64_t *p_row_off,
+                                   const int64_t *q_row_off, int B, int gamma_max, int V,
+                                   float T, float *alpha, float *tv, void *stream);
+
+/*
+ * ---------------------------------------------------------------------------
  * Kernel timing (benchmarking aid; not needed for correct use)
  * ---------------------------------------------------------------------------
  * spec_profile_enable(name) starts a fresh record: from then on every launch
@@ -286,7 +314,7 @@ spec_status_t spec_verify_markov(
  * "draft_persist", "rnn_hidden_proj",
  * "rnn_gates", "w2_transpose", "verify_rows_p", "verify_rows_q",
  * "verify_decide", "verify_residual_rows", "verify_final_partials",
- * "verify_final_draw", or "*" for all) is bracketed
+ * "verify_final_draw", "verify_resid", "acceptance_rate", or "*" for all) is bracketed
  * by two hipEvents recorded on its launch stream.  NULL or "" stops timing.
  * spec_profile_read waits for the recorded events and returns the number of
  * timed launches and their summed duration in milliseconds.  Process-wide

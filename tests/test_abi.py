@@ -36,7 +36,7 @@ def test_header_declares_the_boundary():
               "spec_verify_workspace_size", "spec_philox_uniforms", "spec_last_error",
               "spec_version", "spec_pack_w2", "spec_pack_w2_bytes", "spec_verify_markov",
               "spec_verify_markov_workspace_size", "spec_draft_set_persistent",
-              "spec_draft_set_poll_limit"):
+              "spec_draft_set_poll_limit", "spec_acceptance_rate"):
         assert n in names
 
 
@@ -185,6 +185,29 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(api, "_LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(api.SpecError):
         api.load_library()
+
+
+def test_acceptance_rate_validation(lib):
+    """Argument checks of spec_acceptance_rate happen before any launch."""
+    fake = ctypes.c_void_p(4096)
+    f = lib.spec_acceptance_rate
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+
+    def call(P=fake, pd=0, Q=fake, qd=0, B=2, G=3, V=100, T=1.0, alpha=fake):
+        return f(P, pd, Q, qd, None, None, None, B, G, V, T, alpha, None, None)
+    assert call(P=None) == SPEC_ERR_INVALID
+    assert call(Q=None) == SPEC_ERR_INVALID
+    assert call(alpha=None) == SPEC_ERR_INVALID
+    assert call(B=-1) == SPEC_ERR_INVALID
+    assert call(V=0) == SPEC_ERR_INVALID
+    assert call(T=-0.5) == SPEC_ERR_INVALID
+    assert call(T=float("inf")) == SPEC_ERR_INVALID
+    assert call(pd=7) == SPEC_ERR_UNSUPPORTED
+    assert call(B=0, P=None) == SPEC_OK        # nothing to do
+    assert call(G=0, P=None) == SPEC_OK
 
 
 def test_draft_poll_limit(lib):
