@@ -22,4 +22,6 @@ from .binding import (  # noqa: F401
     draft_markov,
     draft_rnn,
     verify,
+    confidence,
+    prefix_schedule,
 )

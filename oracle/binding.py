@@ -27,6 +27,12 @@ PINS = {
     "verify": "exact output law by brute-force enumeration equals p (lossless theorem); "
               "acceptance frequency equals sum min(p,q); E[tau] closed form; T=0 top-1 match",
     "alpha_tv": "sum min(p,q) == 1 - D_TV identity; MC acceptance frequency",
+    "confidence": "w=0 gives 1/2; one-hot weights on either block give scipy expit of that "
+                  "input; c(-w) = 1 - c(w); logits add over disjoint weight supports",
+    "prefix_schedule": "brute force over every length assignment on tiny cases with unimodal "
+                       "throughput; admitted set is the global top-t; constant SPS admits all; "
+                       "SPS that vanishes past R admits none; hand-worked example; early stop at "
+                       "the first fall even when a later size would be higher",
 }
 
 
@@ -82,6 +88,12 @@ def _L():
                                    d, d, i, d, ctypes.c_double,
                                    i, i, d, d, d, d, d, d, i]
         lib.orc_verify.restype = ctypes.c_int
+        lib.orc_confidence.argtypes = [d, ctypes.c_int, d, ctypes.c_int, d]
+        lib.orc_confidence.restype = ctypes.c_double
+        f = ctypes.POINTER(ctypes.c_float)
+        lib.orc_prefix_schedule.argtypes = [f, ctypes.c_int, ctypes.c_int, d, ctypes.c_int, i,
+                                            d, d]
+        lib.orc_prefix_schedule.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -270,3 +282,32 @@ def verify(P, Q, draft, T, u_test, u_final):
     return dict(n=n.value, out=out, logZp=logZp, logZq=logZq[:L], accept_prob=ap[:L],
                 test_margin=tm[:L], final_thr=fthr.value, final_margin=fmar.value,
                 fallback=fb.value)
+
+
+# --------------------------------------------------------------------------
+# Confidence head and hardware-aware prefix scheduler (DSpark §2.1-2.2)
+# --------------------------------------------------------------------------
+
+def confidence(h, e, w):
+    """c = sigmoid(w . [h; e]) for one drafted position (fp64)."""
+    h, e, w = _f64(h), _f64(e), _f64(w)
+    if w.size != h.size + e.size:
+        raise ValueError("w must have len(h) + len(e) weights")
+    return _L().orc_confidence(_dp(h), h.size, _dp(e), e.size, _dp(w))
+
+
+def prefix_schedule(c, sps):
+    """Acceptance lengths l [R] (int32), the chosen batch size B and expected
+    accepted count tau from confidences c [R, gamma] (float32) and the
+    steps-per-second table sps[B]."""
+    c = np.ascontiguousarray(c, dtype=np.float32)
+    R, gamma = c.shape
+    sps = _f64(sps)
+    lens = np.zeros(R, dtype=np.int32)
+    B, tau = ctypes.c_double(), ctypes.c_double()
+    st = _L().orc_prefix_schedule(c.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), R, gamma,
+                                  _dp(sps), sps.size, _ip(lens), ctypes.byref(B),
+                                  ctypes.byref(tau))
+    if st != 0:
+        raise MemoryError("orc_prefix_schedule")
+    return lens, int(B.value), tau.value

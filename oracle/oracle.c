@@ -19,6 +19,9 @@
  *        (one speculative cycle: draft loop, ratio tests, first rejection,
  *        corrected or bonus token); section "수락 규칙" (acceptance rule,
  *        residual distribution, lossless theorem, closed form of alpha).
+ *   [P1] also §2.1 "Confidence Head" (c_k = sigma(w^T [h_k; W1[x_{k-1}]]))
+ *        and §2.2 "Hardware-Aware Prefix Scheduler" (survival products,
+ *        B and tau, Theta = tau * SPS(B), global greedy order, early stop).
  *   [PX] Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as
  *        1, 2, 3", SC'11 -- Philox4x32 with 10 rounds.
  *
@@ -34,6 +37,12 @@
  *   - uniforms: Philox4x32-10, key = (seed lo, seed hi), counter =
  *     (request b, position k, stream, call offset); u = (word0 >> 8) * 2^-24.
  *     stream 0 = draft sample, 1 = ratio test, 2 = final (corrected/bonus).
+ *   - scheduler: survival a_{r,j} is the float32 product of c_{r,0..j} taken
+ *     left to right; candidates are ordered by a descending, then request,
+ *     then position; tau sums each a cut to a multiple of 2^-48 in exact
+ *     integers; B = R + admitted; SPS(B) = 0 past the end of its table; the
+ *     search stops at the first admission that lowers tau * SPS(B) (ties
+ *     continue), and that admission is not made.
  */
 #include <math.h>
 #include <stdint.h>
@@ -468,4 +477,86 @@ void orc_alpha_tv(const double *lp, const double *lq, int V, double T, double *a
     *tv = 0.5 * t;
     free(wp);
     free(wq);
+}
+
+/* ------------------------------------------------------------------------ */
+/* [P1] §2.1 Confidence head and §2.2 hardware-aware prefix scheduler.        */
+/* ------------------------------------------------------------------------ */
+
+/* c = sigma(w^T [h; e]) with h the backbone hidden state (d values) and e the
+ * Markov embedding W1[x_{k-1}] (r values); w has d + r weights. */
+double orc_confidence(const double *h, int d, const double *e, int r, const double *w)
+{
+    double z = 0.0;
+    int i;
+    for (i = 0; i < d; i++) z += w[i] * h[i];
+    for (i = 0; i < r; i++) z += w[d + i] * e[i];
+    return 1.0 / (1.0 + exp(-z));
+}
+
+/* One candidate prefix extension: request r, position j (0-based), survival
+ * probability a_{r,j}. */
+typedef struct { float a; int r, j; } orc_cand;
+
+static int orc_cand_cmp(const void *x, const void *y)
+{
+    const orc_cand *p = (const orc_cand *)x, *q = (const orc_cand *)y;
+    if (p->a != q->a) return p->a > q->a ? -1 : 1;   /* higher survival first */
+    if (p->r != q->r) return p->r < q->r ? -1 : 1;
+    return p->j < q->j ? -1 : (p->j > q->j);
+}
+
+/* Acceptance lengths l_r in {0..gamma} for R requests from their per-position
+ * confidences c [R][gamma] (each in [0, 1]) and the engine's steps-per-second
+ * table sps[B], B = 0 .. nsps - 1 (0 beyond it):
+ *   a_{r,j} = prod_{i <= j} c_{r,i}                (fp32, left to right)
+ *   candidates sorted by a descending (then request, then position), admitted
+ *   one by one; after t admissions B_t = R + t and
+ *   tau_t = R + sum of the admitted a (each a cut to a multiple of 2^-48 and
+ *   summed exactly in integers), Theta_t = tau_t * SPS(B_t) in double;
+ *   the search stops at the first t with Theta_t < Theta_{t-1} (that
+ *   candidate is not admitted).
+ * Fixing the precision of a (fp32 products) and of tau (exact integer sums)
+ * makes the decisions independent of summation order.  Outputs l [R], the
+ * chosen B and tau.  Returns 0, or -1 when memory runs out. */
+int orc_prefix_schedule(const float *c, int R, int gamma, const double *sps, int nsps,
+                        int *lens, double *B_out, double *tau_out)
+{
+    const int N = R * gamma;
+    orc_cand *cand = (orc_cand *)malloc(sizeof(orc_cand) * (size_t)(N > 0 ? N : 1));
+    const double scale = 281474976710656.0;   /* 2^48 */
+    int64_t sum_q = 0;
+    int r, j, t, admitted = 0;
+    double theta_prev, tau;
+    if (!cand) return -1;
+    for (r = 0; r < R; r++) {
+        float a = 1.0f;
+        for (j = 0; j < gamma; j++) {
+            a = a * c[(size_t)r * gamma + j];
+            cand[r * gamma + j].a = a;
+            cand[r * gamma + j].r = r;
+            cand[r * gamma + j].j = j;
+        }
+    }
+    qsort(cand, (size_t)N, sizeof(orc_cand), orc_cand_cmp);
+    tau = (double)((int64_t)R * (int64_t)scale) / scale;
+    theta_prev = tau * (R < nsps ? sps[R] : 0.0);
+    for (t = 1; t <= N; t++) {
+        const int64_t q = (int64_t)((double)cand[t - 1].a * scale);   /* exact, truncated */
+        const int Bt = R + t;
+        double tau_t, theta;
+        sum_q += q;
+        tau_t = (double)((int64_t)R * (int64_t)scale + sum_q) / scale;
+        theta = tau_t * (Bt < nsps ? sps[Bt] : 0.0);
+        if (theta < theta_prev) break;   /* throughput fell: stop before it */
+        theta_prev = theta;
+        tau = tau_t;
+        admitted = t;
+    }
+    for (r = 0; r < R; r++) lens[r] = 0;
+    for (t = 0; t < admitted; t++) lens[cand[t].r]++;
+    *B_out = (double)(R + admitted);
+    *tau_out = tau;
+    free(cand);
+    return 0;
 }
