@@ -429,6 +429,40 @@ def main():
                 avg_us=round(us, 2), alg_bytes_per_launch=ab, achieved_GBs=round(ab / us / 1e3, 1),
                 read_bytes_per_launch=2 * ab, read_GBs=round(2 * ab / us / 1e3, 1),
                 mean_alpha=round(float(aout["alpha"].mean().item()), 4))
+    # DSpark's confidence head over the drafted tokens (hidden states h_k of a
+    # 4096-wide backbone, bf16) and the prefix scheduler on its output (an
+    # engine whose step time is flat up to 4 B tokens, then grows linearly).
+    # Not part of the timed cycle.  Algorithmic bytes of the head: every h row,
+    # the embedding row of each previous token, c and the token read, w once.
+    if wbt == "bf16" and lb == "bf16":
+        dh = 4096
+        cw = workloads.make_confidence(B, g, 8, r, dh, 1234)
+        h_d, w_d = to_dev(cw["h"], "bf16"), to_dev(cw["w"])
+        sps_d = to_dev(workloads.make_schedule(B, g, 1234)["sps"])
+        c_d = torch.empty((B, g), dtype=torch.float32, device=dev)
+        s_out = dict(lens=torch.empty(B, dtype=torch.int32, device=dev),
+                     B=torch.empty(1, dtype=torch.int32, device=dev),
+                     tau=torch.empty(1, dtype=torch.float64, device=dev))
+        for name in ("confidence_head", "prefix_schedule"):
+            sd.spec_profile_enable(name)
+            for i in range(args.steps):
+                sd.spec_confidence_head(h_d, x0, d_out["tokens"], W1, w_d, out=c_d)
+                sd.spec_prefix_schedule(c_d, sps_d, out=s_out)
+            n, ms = sd.spec_profile_read()
+            sd.spec_profile_enable(None)
+            if not n:
+                continue
+            us = ms * 1e3 / n
+            if name == "confidence_head":
+                cb = B * g * (dh * 2 + r * 2 + 4 + 4) + (dh + r) * 4
+                result_extra[name] = dict(avg_us=round(us, 2), alg_bytes_per_launch=cb,
+                                          achieved_GBs=round(cb / us / 1e3, 1),
+                                          mean_c=round(float(c_d.mean().item()), 4), d=dh)
+            else:
+                result_extra[name] = dict(avg_us=round(us, 2), candidates=B * g,
+                                          chosen_batch=int(s_out["B"].item()),
+                                          tau=round(float(s_out["tau"].item()), 3),
+                                          mean_len=round(float(s_out["lens"].float().mean().item()), 3))
     tdraft = sum(kernels[k]["us_per_step"] for k in kernels if k.startswith("draft")
                  or k == "w2_pack")
     tver = sum(kernels[k]["us_per_step"] for k in kernels if k.startswith("verify"))

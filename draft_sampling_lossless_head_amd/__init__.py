@@ -12,6 +12,7 @@ from .api import (  # noqa: F401
     library_path,
     load_library,
     spec_acceptance_rate,
+    spec_confidence_head,
     spec_draft_sample_markov,
     spec_draft_sample_rnn,
     spec_draft_set_persistent,
@@ -19,6 +20,7 @@ from .api import (  # noqa: F401
     spec_pack_w2,
     spec_pack_w2_bytes,
     spec_philox_uniforms,
+    spec_prefix_schedule,
     spec_profile_enable,
     spec_profile_read,
     spec_verify,

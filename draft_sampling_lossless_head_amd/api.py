@@ -72,6 +72,11 @@ def load_library():
     lib.spec_acceptance_rate.argtypes = [vp, i32, vp, i32, vp, vp, vp, i32, i32, i32, f32, vp,
                                          vp, vp]
     lib.spec_acceptance_rate.restype = i32
+    lib.spec_confidence_head.argtypes = [vp, i32, i32, vp, vp, vp, i32, i32, vp, i32, i32, i32,
+                                         vp, vp]
+    lib.spec_confidence_head.restype = i32
+    lib.spec_prefix_schedule.argtypes = [vp, i32, i32, vp, i32, vp, vp, vp, vp]
+    lib.spec_prefix_schedule.restype = i32
     lib.spec_draft_set_poll_limit.argtypes = [u32]
     lib.spec_draft_set_poll_limit.restype = u32
     lib.spec_profile_enable.argtypes = [ctypes.c_char_p]
@@ -340,6 +345,55 @@ def spec_acceptance_rate(P, Q, T=1.0, *, gamma_max=None, lens=None, p_row_off=No
                                   float(T), _ptr(out["alpha"]), _ptr(out.get("tv")),
                                   _stream(stream))
     _check(st, "spec_acceptance_rate")
+    return out
+
+
+def spec_confidence_head(h, x0, draft, W1, w, *, out=None, stream=None):
+    """Confidence c[b, k] = sigmoid(w[:d] . h[b, k] + w[d:] . W1[prev]) of every
+    drafted position (prev = x0[b] at k = 0, else draft[b, k-1]).  h [R, gamma,
+    d], x0 int32 [R], draft int32 [R, gamma], W1 [V, r], w float32 [d + r]."""
+    lib = load_library()
+    for t, n in ((h, "h"), (x0, "x0"), (draft, "draft"), (W1, "W1"), (w, "w")):
+        _dev(t, n)
+    if h.dim() != 3 or W1.dim() != 2:
+        raise SpecError("h must be [R, gamma, d] and W1 [V, r]")
+    R, gamma, d = h.shape
+    V, r = W1.shape
+    if x0.dtype != torch.int32 or x0.shape != (R,):
+        raise SpecError("x0 must be int32 [R]")
+    if draft.dtype != torch.int32 or draft.shape != (R, gamma):
+        raise SpecError("draft must be int32 [R, gamma]")
+    if w.dtype != torch.float32 or w.shape != (d + r,):
+        raise SpecError("w must be float32 [d + r]")
+    if out is None:
+        out = torch.empty((R, gamma), dtype=torch.float32, device=h.device)
+    st = lib.spec_confidence_head(_ptr(h), _dtype_code(h, "h"), d, _ptr(x0), _ptr(draft),
+                                  _ptr(W1), _dtype_code(W1, "W1"), r, _ptr(w), R, gamma, V,
+                                  _ptr(out), _stream(stream))
+    _check(st, "spec_confidence_head")
+    return out
+
+
+def spec_prefix_schedule(c, sps, *, out=None, stream=None):
+    """Acceptance lengths l [R] (int32) from confidences c float32 [R, gamma]
+    and the steps-per-second table sps float64 [nsps] (index = batch size).
+    Returns dict(lens, B, tau) of device tensors (B int32 [1], tau float64
+    [1])."""
+    lib = load_library()
+    _dev(c, "c")
+    _dev(sps, "sps")
+    if c.dtype != torch.float32 or c.dim() != 2:
+        raise SpecError("c must be float32 [R, gamma]")
+    if sps.dtype != torch.float64 or sps.dim() != 1:
+        raise SpecError("sps must be float64 [nsps]")
+    R, gamma = c.shape
+    if out is None:
+        out = dict(lens=torch.empty(R, dtype=torch.int32, device=c.device),
+                   B=torch.empty(1, dtype=torch.int32, device=c.device),
+                   tau=torch.empty(1, dtype=torch.float64, device=c.device))
+    st = lib.spec_prefix_schedule(_ptr(c), R, gamma, _ptr(sps), sps.numel(), _ptr(out["lens"]),
+                                  _ptr(out.get("B")), _ptr(out.get("tau")), _stream(stream))
+    _check(st, "spec_prefix_schedule")
     return out
 
 

@@ -231,6 +231,35 @@ struct AlphaArgs {
 };
 hipError_t acceptance_rate_launch(const AlphaArgs& a, hipStream_t s);
 
+// Confidence head: c[b, k] = sigmoid(w[:d] . h[b, k] + w[d:] . W1[prev]).
+struct ConfArgs {
+    const void* h;              // [R, gamma, d] hidden states
+    int h_bf16;
+    int d;
+    const int32_t* x0;          // [R] anchors
+    const int32_t* draft;       // [R, gamma] drafted tokens
+    const void* W1;             // [V, r] Markov embedding
+    int w_bf16;
+    int r;
+    const float* w;             // [d + r] head weights
+    int R, gamma, V;
+    float* c;                   // [R, gamma] out
+};
+hipError_t confidence_launch(const ConfArgs& a, hipStream_t s);
+
+// Prefix scheduler over R * gamma <= kSchedMax candidates.
+constexpr int kSchedMax = 8192;
+struct SchedArgs {
+    const float* c;             // [R, gamma] confidences in [0, 1]
+    int R, gamma;
+    const double* sps;          // [nsps] steps per second by batch size
+    int nsps;
+    int32_t* lens;              // [R] out
+    int32_t* B_out;             // [1] out or null
+    double* tau_out;            // [1] out or null
+};
+hipError_t prefix_schedule_launch(const SchedArgs& a, hipStream_t s);
+
 hipError_t philox_uniforms_launch(uint64_t seed, uint32_t offset, uint32_t stream, int B, int K,
                                   float* out, hipStream_t s);
 

@@ -1,0 +1,276 @@
+// DSpark confidence head and hardware-aware prefix scheduler (DSpark review,
+// §2.1 "Confidence Head" and §2.2 "Hardware-Aware Prefix Scheduler").
+//
+// confidence_rows: one wave per drafted position (request b, position k).
+//   The head reads the backbone hidden state h_k and the Markov embedding of
+//   the token before position k, W1[x_{k-1}], and returns
+//   c = sigmoid(w_h . h_k + w_e . W1[x_{k-1}]).  HBM-bound on h (d values per
+//   position); w is a few KB and stays in L2.
+//
+// prefix_schedule: one workgroup of 1024 threads for the whole batch.
+//   1. survival a_{r,j} = c_{r,0} * ... * c_{r,j}: one thread per request,
+//      float32 products left to right;
+//   2. one 64-bit key per candidate, (~bits(a) << 32) | (r * gamma + j):
+//      for a in [0, 1] ascending keys mean descending a, ties broken by the
+//      lower request, then the lower position; bitonic sort in LDS;
+//   3. q_t = a_t cut to a multiple of 2^-48 as an integer; inclusive integer
+//      prefix sums S_t give tau_t = R + S_t 2^-48 exactly (no dependence on
+//      the order of the sums); Theta_t = tau_t * SPS(R + t) in double for every
+//      t at once; the admitted count is the last t before the first fall of
+//      Theta (ties do not stop the search);
+//   4. l_r = number of admitted candidates of request r.
+#include <climits>
+
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace specdec {
+
+// ---------------------------------------------------------------------------
+// Confidence head
+// ---------------------------------------------------------------------------
+
+constexpr int kConfThreads = 256;
+
+template <bool BF16>
+__device__ __forceinline__ float elem_at(const void* base, size_t i) {
+    if constexpr (BF16) return bf16_bits_to_float(static_cast<const uint16_t*>(base)[i]);
+    else return static_cast<const float*>(base)[i];
+}
+
+// Partial dot product of one lane: sum over i = lane*8 + 512 n (+ 0..7) of
+// x[i] w[i], with 16-byte loads of x (i % 8 == 0 rows, 16-byte aligned).
+template <bool BF16>
+__device__ __forceinline__ float lane_dot_vec(const void* x, size_t x0, const float* w, int n,
+                                              int lane) {
+    float acc = 0.0f;
+    for (int i = lane * 8; i < n; i += kWave * 8) {
+        float v[8];
+        if constexpr (BF16) {
+            const u32x4_t q = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(x) + x0 + i));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[2 * j] = __uint_as_float(q[j] << 16);
+                v[2 * j + 1] = __uint_as_float(q[j] & 0xFFFF0000u);
+            }
+        } else {
+            typedef float f32x4v __attribute__((ext_vector_type(4)));
+            const f32x4v* p = reinterpret_cast<const f32x4v*>(static_cast<const float*>(x) + x0 + i);
+            const f32x4v a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[j] = a[j];
+                v[4 + j] = b[j];
+            }
+        }
+        const float4 wa = *reinterpret_cast<const float4*>(w + i);
+        const float4 wb = *reinterpret_cast<const float4*>(w + i + 4);
+        acc += v[0] * wa.x + v[1] * wa.y + v[2] * wa.z + v[3] * wa.w;
+        acc += v[4] * wb.x + v[5] * wb.y + v[6] * wb.z + v[7] * wb.w;
+    }
+    return acc;
+}
+
+template <bool BF16>
+__device__ __forceinline__ float lane_dot_any(const void* x, size_t x0, const float* w, int n,
+                                              int lane) {
+    float acc = 0.0f;
+    for (int i = lane; i < n; i += kWave) acc += elem_at<BF16>(x, x0 + i) * w[i];
+    return acc;
+}
+
+template <bool HB, bool WB, bool VEC>
+__global__ __launch_bounds__(kConfThreads)
+void confidence_rows(ConfArgs A) {
+    const int lane = threadIdx.x & 63;
+    const size_t row = (size_t)blockIdx.x * (kConfThreads / kWave) + (threadIdx.x >> 6);
+    const size_t nrows = (size_t)A.R * A.gamma;
+    if (row >= nrows) return;
+    const int b = (int)(row / (unsigned)A.gamma), k = (int)(row % (unsigned)A.gamma);
+    const int prev = k == 0 ? A.x0[b] : A.draft[(size_t)b * A.gamma + k - 1];
+    if (prev < 0 || prev >= A.V) {   // no token before this position (undrawn)
+        if (lane == 0) A.c[row] = 0.0f;
+        return;
+    }
+    float acc;
+    if constexpr (VEC) {
+        acc = lane_dot_vec<HB>(A.h, row * (size_t)A.d, A.w, A.d, lane) +
+              lane_dot_vec<WB>(A.W1, (size_t)prev * A.r, A.w + A.d, A.r, lane);
+    } else {
+        acc = lane_dot_any<HB>(A.h, row * (size_t)A.d, A.w, A.d, lane) +
+              lane_dot_any<WB>(A.W1, (size_t)prev * A.r, A.w + A.d, A.r, lane);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    if (lane == 0) A.c[row] = 1.0f / (1.0f + expf(-acc));
+}
+
+template <bool HB, bool WB>
+static void launch_conf_t(const ConfArgs& a, bool vec, hipStream_t s) {
+    const size_t rows = (size_t)a.R * a.gamma;
+    const unsigned grid = (unsigned)((rows + kConfThreads / kWave - 1) / (kConfThreads / kWave));
+    if (vec) hipLaunchKernelGGL((confidence_rows<HB, WB, true>), dim3(grid), dim3(kConfThreads), 0, s, a);
+    else hipLaunchKernelGGL((confidence_rows<HB, WB, false>), dim3(grid), dim3(kConfThreads), 0, s, a);
+}
+
+hipError_t confidence_launch(const ConfArgs& a, hipStream_t s) {
+    if ((size_t)a.R * a.gamma == 0) return hipSuccess;
+    auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+    // 16-byte vectors: both row lengths multiples of 8 and every base aligned
+    const bool vec = a.d % 8 == 0 && a.r % 8 == 0 && al16(a.h) && al16(a.W1) && al16(a.w) &&
+                     al16(a.w + a.d);
+    if (a.h_bf16 && a.w_bf16) launch_conf_t<true, true>(a, vec, s);
+    else if (a.h_bf16) launch_conf_t<true, false>(a, vec, s);
+    else if (a.w_bf16) launch_conf_t<false, true>(a, vec, s);
+    else launch_conf_t<false, false>(a, vec, s);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Prefix scheduler
+// ---------------------------------------------------------------------------
+
+constexpr int kSchedThreads = 1024;
+constexpr int kSchedPerThread = kSchedMax / kSchedThreads;   // 8
+constexpr double kTwo48 = 281474976710656.0;
+
+__device__ __forceinline__ int64_t shfl_up_i64(int64_t x, int d) {
+    const int lo = __shfl_up((int)(uint32_t)(uint64_t)x, d);
+    const int hi = __shfl_up((int)(uint32_t)((uint64_t)x >> 32), d);
+    return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// Theta_t for the integer prefix S_t of t admitted candidates.
+__device__ __forceinline__ double sched_theta(int R, int t, int64_t S, const double* sps, int nsps) {
+    const double tau = (double)((int64_t)R * (int64_t)kTwo48 + S) / kTwo48;
+    const int B = R + t;
+    return tau * (B < nsps ? sps[B] : 0.0);
+}
+
+__global__ __launch_bounds__(kSchedThreads)
+void prefix_schedule_kernel(SchedArgs A) {
+    __shared__ uint64_t keys[kSchedMax];    // sort buffer; later the per-request counts
+    __shared__ int64_t wave_tot[kSchedThreads / kWave];
+    __shared__ int stop_t;
+    __shared__ int64_t S_stop;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int R = A.R, G = A.gamma, N = R * G;
+    int P = 1;
+    while (P < N) P <<= 1;
+
+    // 1-2. survival products and keys; pads sort last
+    for (int r = tid; r < R; r += kSchedThreads) {
+        float a = 1.0f;
+        for (int j = 0; j < G; ++j) {
+            a = a * A.c[(size_t)r * G + j];
+            // -0 (and, outside the domain, negatives and NaN) keys as +0
+            const uint32_t bits = a > 0.0f ? __float_as_uint(a) : 0u;
+            keys[r * G + j] = ((uint64_t)(~bits) << 32) | (uint32_t)(r * G + j);
+        }
+    }
+    for (int i = N + tid; i < P; i += kSchedThreads) keys[i] = ~0ull;
+    if (tid == 0) stop_t = INT_MAX;
+    __syncthreads();
+
+    // bitonic sort, ascending
+    for (int k = 2; k <= P; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = tid; i < (P >> 1); i += kSchedThreads) {
+                const int lo = ((i & ~(j - 1)) << 1) | (i & (j - 1));
+                const int hi = lo | j;
+                const uint64_t x = keys[lo], y = keys[hi];
+                const bool up = (lo & k) == 0;
+                if ((x > y) == up) {
+                    keys[lo] = y;
+                    keys[hi] = x;
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    // 3. integer prefix sums of the cut survival values; each thread owns the
+    //    candidates [tid * E, tid * E + E) of the sorted order
+    const int E = (N + kSchedThreads - 1) / kSchedThreads;
+    const int base = tid * E;
+    uint64_t kk[kSchedPerThread];
+    int64_t q[kSchedPerThread];
+    int64_t mine = 0;
+#pragma unroll
+    for (int e = 0; e < kSchedPerThread; ++e) {
+        kk[e] = 0;
+        q[e] = 0;
+        if (e < E && base + e < N) {
+            kk[e] = keys[base + e];
+            float a = __uint_as_float(~(uint32_t)(kk[e] >> 32));
+            a = fminf(a, 1.0f);   // inputs above 1 do not cut above 2^48
+            q[e] = (int64_t)((double)a * kTwo48);
+            mine += q[e];
+        }
+    }
+    // block-wide exclusive scan of the per-thread totals
+    int64_t incl = mine;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int64_t o = shfl_up_i64(incl, d);
+        if (lane >= d) incl += o;
+    }
+    if (lane == kWave - 1) wave_tot[wave] = incl;
+    __syncthreads();
+    int64_t excl = incl - mine;
+    for (int w = 0; w < wave; ++w) excl += wave_tot[w];
+
+    // first fall of Theta: the smallest t >= 1 with Theta_t < Theta_{t-1}
+    {
+        int64_t S = excl;
+        double prev = sched_theta(R, base, S, A.sps, A.nsps);
+#pragma unroll
+        for (int e = 0; e < kSchedPerThread; ++e) {
+            if (e < E && base + e < N) {
+                S += q[e];
+                const int t = base + e + 1;
+                const double th = sched_theta(R, t, S, A.sps, A.nsps);
+                if (th < prev) {
+                    atomicMin(&stop_t, t);
+                    break;
+                }
+                prev = th;
+            }
+        }
+    }
+    __syncthreads();
+    const int admitted = stop_t == INT_MAX ? N : stop_t - 1;
+    // S at the admitted count: owned by the thread whose range ends it
+    {
+        int64_t S = excl;
+        if (admitted == 0 && tid == 0) S_stop = 0;
+#pragma unroll
+        for (int e = 0; e < kSchedPerThread; ++e) {
+            if (e < E && base + e < N) {
+                S += q[e];
+                if (base + e + 1 == admitted) S_stop = S;
+            }
+        }
+    }
+    // 4. per-request counts of the admitted candidates (keys buffer reused)
+    int* cnt = reinterpret_cast<int*>(keys);
+    for (int r = tid; r < R; r += kSchedThreads) cnt[r] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < kSchedPerThread; ++e)
+        if (e < E && base + e < admitted) atomicAdd(&cnt[(int)(uint32_t)kk[e] / G], 1);
+    __syncthreads();
+    for (int r = tid; r < R; r += kSchedThreads) A.lens[r] = cnt[r];
+    if (tid == 0) {
+        if (A.B_out) A.B_out[0] = R + admitted;
+        if (A.tau_out) A.tau_out[0] = (double)((int64_t)R * (int64_t)kTwo48 + S_stop) / kTwo48;
+    }
+}
+
+hipError_t prefix_schedule_launch(const SchedArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL(prefix_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace specdec

@@ -431,6 +431,62 @@ spec_status_t spec_acceptance_rate(const void* P, int p_dtype, const void* Q, in
     return e == hipSuccess ? SPEC_OK : hip_fail(e, "acceptance_rate");
 }
 
+spec_status_t spec_confidence_head(const void* h, int h_dtype, int d, const int32_t* x0,
+                                   const int32_t* draft, const void* W1, int w_dtype, int r,
+                                   const float* w, int R, int gamma, int V, float* c,
+                                   void* stream) {
+    g_err.clear();
+    if (R < 0 || gamma < 0) return fail(SPEC_ERR_INVALID, "R and gamma must be >= 0");
+    if (d <= 0 || r <= 0 || V <= 0) return fail(SPEC_ERR_INVALID, "d, r and V must be > 0");
+    if (!dtype_ok(h_dtype) || !dtype_ok(w_dtype)) return fail(SPEC_ERR_UNSUPPORTED, "dtype must be SPEC_F32 or SPEC_BF16");
+    if ((int64_t)R * gamma > INT32_MAX) return fail(SPEC_ERR_UNSUPPORTED, "R * gamma too large");
+    if (R == 0 || gamma == 0) return SPEC_OK;
+    if (!h || !x0 || !draft || !W1 || !w || !c) return fail(SPEC_ERR_INVALID, "null pointer (h, x0, draft, W1, w, c)");
+    ConfArgs a{};
+    a.h = h;
+    a.h_bf16 = h_dtype == SPEC_BF16;
+    a.d = d;
+    a.x0 = x0;
+    a.draft = draft;
+    a.W1 = W1;
+    a.w_bf16 = w_dtype == SPEC_BF16;
+    a.r = r;
+    a.w = w;
+    a.R = R;
+    a.gamma = gamma;
+    a.V = V;
+    a.c = c;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* t = prof_begin("confidence_head", s);
+    hipError_t e = confidence_launch(a, s);
+    prof_end(t, s);
+    return e == hipSuccess ? SPEC_OK : hip_fail(e, "confidence_head");
+}
+
+spec_status_t spec_prefix_schedule(const float* c, int R, int gamma, const double* sps, int nsps,
+                                   int32_t* lens, int32_t* B_out, double* tau_out, void* stream) {
+    g_err.clear();
+    if (R < 0 || gamma < 0 || nsps < 0) return fail(SPEC_ERR_INVALID, "R, gamma and nsps must be >= 0");
+    if (nsps > 0 && !sps) return fail(SPEC_ERR_INVALID, "null sps with nsps > 0");
+    if ((int64_t)R * gamma > kSchedMax || R > kSchedMax)
+        return fail(SPEC_ERR_UNSUPPORTED, "R and R * gamma must be <= 8192");
+    if (R > 0 && (!lens || (gamma > 0 && !c))) return fail(SPEC_ERR_INVALID, "null c or lens");
+    SchedArgs a{};
+    a.c = c;
+    a.R = R;
+    a.gamma = gamma;
+    a.sps = sps;
+    a.nsps = nsps;
+    a.lens = lens;
+    a.B_out = B_out;
+    a.tau_out = tau_out;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* t = prof_begin("prefix_schedule", s);
+    hipError_t e = prefix_schedule_launch(a, s);
+    prof_end(t, s);
+    return e == hipSuccess ? SPEC_OK : hip_fail(e, "prefix_schedule");
+}
+
 size_t spec_pack_w2_bytes(int r, int V) {
     if (r <= 0 || V <= 0 || V > kMaxV) return 0;
     return w2p_bytes(r, V);

@@ -307,6 +307,65 @@ spec_status_t spec_acceptance_rate(const void *P, int p_dtype, const void *Q, in
 
 /*
  * ---------------------------------------------------------------------------
+ * Confidence head  [DSpark §2.1 "Confidence Head", head equation]
+ * ---------------------------------------------------------------------------
+ * For every request b < R and drafted position k < gamma:
+ *     prev    = (k == 0) ? x0[b] : draft[b, k-1]
+ *     c[b, k] = sigmoid( sum_i w[i] h[b, k, i] + sum_j w[d + j] W1[prev, j] )
+ * an estimate of the chance that the draft token at position k is accepted.
+ *
+ * h     [R, gamma, d]  backbone hidden state at each drafted position, h_dtype
+ * x0    [R]            int32 anchor tokens; draft [R, gamma] int32 draft tokens
+ *                      (draft[b, gamma-1] is not read)
+ * W1    [V, r]         the Markov head's embedding table, w_dtype
+ * w     [d + r]        fp32 head weights (hidden block first)
+ * c     [R, gamma]     out: fp32 confidences; 0 where prev is outside [0, V)
+ *                      (e.g. after an undrawn token -1)
+ * Dot products in fp32 (per-lane sums, then a wave tree), sigmoid in fp32.
+ * All pointers are device memory, stream-ordered; nothing is kept.
+ * Errors: SPEC_ERR_INVALID for null pointers, R, gamma < 0, d, r, V <= 0;
+ * SPEC_ERR_UNSUPPORTED for other dtypes; R * gamma == 0 does nothing.
+ */
+spec_status_t spec_confidence_head(const void *h, int h_dtype, int d, const int32_t *x0,
+                                   const int32_t *draft, const void *W1, int w_dtype, int r,
+                                   const float *w, int R, int gamma, int V, float *c,
+                                   void *stream);
+
+/*
+ * ---------------------------------------------------------------------------
+ * Hardware-aware prefix scheduler  [DSpark §2.2, survival products,
+ * B and tau, Theta = tau * SPS(B), global greedy admission, early stop]
+ * ---------------------------------------------------------------------------
+ * Chooses how many drafted tokens l_r in [0, gamma] each request sends to
+ * verification:
+ *     a[r, j]  = c[r, 0] * ... * c[r, j]   (fp32, left to right)
+ *     candidates (r, j) in order of a descending (ties: lower r, then lower j)
+ *     are admitted one at a time; after t admissions B_t = R + t and
+ *     tau_t = R + sum of the admitted a, each a cut to a multiple of 2^-48
+ *     and summed exactly in integers; Theta_t = tau_t * sps[B_t] in double
+ *     (0 for B_t >= nsps).  The search stops at the first t with
+ *     Theta_t < Theta_{t-1}; that candidate is not admitted.
+ * Because a is non-increasing along a request, the admitted set is a prefix
+ * of every request.
+ *
+ * c       [R, gamma]  fp32 confidences, each in [0, 1] (other values give
+ *                     unspecified lengths; the call still completes)
+ * sps     [nsps]      double steps per second of the engine at batch size B
+ *                     (index B); may be NULL when nsps == 0
+ * lens    [R]         out: int32 l_r
+ * B_out   [1]         out (optional): int32 chosen batch size R + sum l_r
+ * tau_out [1]         out (optional): double tau at that size
+ * One workgroup; all pointers device memory, stream-ordered.
+ * Errors: SPEC_ERR_INVALID for null c or lens (R > 0), R, gamma, nsps < 0,
+ * null sps with nsps > 0; SPEC_ERR_UNSUPPORTED for R > 8192 or
+ * R * gamma > 8192.
+ */
+spec_status_t spec_prefix_schedule(const float *c, int R, int gamma, const double *sps,
+                                   int nsps, int32_t *lens, int32_t *B_out, double *tau_out,
+                                   void *stream);
+
+/*
+ * ---------------------------------------------------------------------------
  * Kernel timing (benchmarking aid; not needed for correct use)
  * ---------------------------------------------------------------------------
  * spec_profile_enable(name) starts a fresh record: from then on every launch
@@ -314,7 +373,8 @@ spec_status_t spec_acceptance_rate(const void *P, int p_dtype, const void *Q, in
  * "draft_persist", "rnn_hidden_proj",
  * "rnn_gates", "w2_transpose", "verify_rows_p", "verify_rows_q",
  * "verify_decide", "verify_residual_rows", "verify_final_partials",
- * "verify_final_draw", "verify_resid", "acceptance_rate", or "*" for all) is bracketed
+ * "verify_final_draw", "verify_resid", "acceptance_rate", "confidence_head",
+ * "prefix_schedule", or "*" for all) is bracketed
  * by two hipEvents recorded on its launch stream.  NULL or "" stops timing.
  * spec_profile_read waits for the recorded events and returns the number of
  * timed launches and their summed duration in milliseconds.  Process-wide

@@ -36,7 +36,8 @@ def test_header_declares_the_boundary():
               "spec_verify_workspace_size", "spec_philox_uniforms", "spec_last_error",
               "spec_version", "spec_pack_w2", "spec_pack_w2_bytes", "spec_verify_markov",
               "spec_verify_markov_workspace_size", "spec_draft_set_persistent",
-              "spec_draft_set_poll_limit", "spec_acceptance_rate"):
+              "spec_draft_set_poll_limit", "spec_acceptance_rate", "spec_confidence_head",
+              "spec_prefix_schedule"):
         assert n in names
 
 
@@ -208,6 +209,50 @@ def test_acceptance_rate_validation(lib):
     assert call(pd=7) == SPEC_ERR_UNSUPPORTED
     assert call(B=0, P=None) == SPEC_OK        # nothing to do
     assert call(G=0, P=None) == SPEC_OK
+
+
+def test_confidence_head_validation(lib):
+    """Argument checks of spec_confidence_head happen before any launch."""
+    fake = ctypes.c_void_p(4096)
+    f = lib.spec_confidence_head
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    f.argtypes = [vp, i, i, vp, vp, vp, i, i, vp, i, i, i, vp, vp]
+    f.restype = i
+
+    def call(h=fake, hd=1, d=64, x0=fake, draft=fake, W1=fake, wd=1, r=16, w=fake, R=2, G=3,
+             V=100, c=fake):
+        return f(h, hd, d, x0, draft, W1, wd, r, w, R, G, V, c, None)
+    for k in ("h", "x0", "draft", "W1", "w", "c"):
+        assert call(**{k: None}) == SPEC_ERR_INVALID, k
+    assert call(R=-1) == SPEC_ERR_INVALID
+    assert call(d=0) == SPEC_ERR_INVALID
+    assert call(r=0) == SPEC_ERR_INVALID
+    assert call(V=0) == SPEC_ERR_INVALID
+    assert call(hd=5) == SPEC_ERR_UNSUPPORTED
+    assert call(wd=5) == SPEC_ERR_UNSUPPORTED
+    assert call(R=0, h=None) == SPEC_OK        # nothing to do
+    assert call(G=0, h=None) == SPEC_OK
+
+
+def test_prefix_schedule_validation(lib):
+    """Argument checks of spec_prefix_schedule happen before any launch."""
+    fake = ctypes.c_void_p(4096)
+    f = lib.spec_prefix_schedule
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    f.argtypes = [vp, i, i, vp, i, vp, vp, vp, vp]
+    f.restype = i
+
+    def call(c=fake, R=4, G=3, sps=fake, nsps=10, lens=fake):
+        return f(c, R, G, sps, nsps, lens, None, None, None)
+    assert call(c=None) == SPEC_ERR_INVALID
+    assert call(lens=None) == SPEC_ERR_INVALID
+    assert call(sps=None) == SPEC_ERR_INVALID
+    assert call(R=-1) == SPEC_ERR_INVALID
+    assert call(G=-1) == SPEC_ERR_INVALID
+    assert call(nsps=-1) == SPEC_ERR_INVALID
+    assert call(R=1025, G=8) == SPEC_ERR_UNSUPPORTED
+    assert call(R=8193, G=1) == SPEC_ERR_UNSUPPORTED
+    assert call(R=8193, G=0) == SPEC_ERR_UNSUPPORTED
 
 
 def test_draft_poll_limit(lib):

@@ -7,8 +7,10 @@ from .gen import (  # noqa: F401
     bf16_bits_to_f32,
     f32_to_bf16_bits,
     as_f64,
+    make_confidence,
     make_markov,
     make_rnn,
+    make_schedule,
     make_verify_only,
     packed_offsets,
 )

@@ -199,3 +199,39 @@ def make_verify_only(B, gamma, V, seed, dtype="f32", scale=4.0, zipf=1.1, sigma=
     g = _rng(seed, _S_GLOBAL, 7)
     draft = g.integers(0, V, size=(B, gamma), dtype=np.int64).astype(np.int32)
     return dict(B=B, gamma=gamma, V=V, logit_dtype=dtype, Q=U, P=P, draft=draft, lens=lens)
+
+
+# Stream ids of the confidence-head and scheduler inputs.
+_S_CONF, _S_SCHED = 4, 5
+
+
+def make_confidence(R, gamma, V, r, d, seed, h_dtype="bf16", w_dtype="bf16", w_std=0.02,
+                    z_std=1.5):
+    """Confidence-head inputs: hidden states h ~ N(0, 1) [R, gamma, d], an
+    embedding table W1 ~ N(0, w_std^2) [V, r], anchors and draft tokens
+    uniform on [0, V), and fp32 head weights w [d + r] scaled so that each
+    block's dot product has standard deviation about z_std / sqrt(2)."""
+    g = _rng(seed, _S_CONF)
+    h = _store(g.standard_normal((R, gamma, d), dtype=np.float32), h_dtype)
+    W1 = _store(g.standard_normal((V, r), dtype=np.float32) * np.float32(w_std), w_dtype)
+    x0 = g.integers(0, V, size=R, dtype=np.int64).astype(np.int32)
+    draft = g.integers(0, V, size=(R, gamma), dtype=np.int64).astype(np.int32)
+    s = z_std / np.sqrt(2.0)
+    w = np.concatenate([g.standard_normal(d) * (s / np.sqrt(d)),
+                        g.standard_normal(r) * (s / (np.sqrt(r) * w_std))]).astype(np.float32)
+    return dict(R=R, gamma=gamma, V=V, r=r, d=d, h_dtype=h_dtype, w_dtype=w_dtype, h=h, W1=W1,
+                x0=x0, draft=draft, w=w)
+
+
+def make_schedule(R, gamma, seed, knee=None, beta=(4.0, 1.2)):
+    """Scheduler inputs: confidences c ~ Beta(beta) in fp32 [R, gamma] (mean
+    about 0.77), and a steps-per-second table over batch sizes
+    B = 0 .. R (gamma + 1) of an engine whose step time is flat up to `knee`
+    tokens (memory-bound) and grows linearly beyond it (compute-bound):
+    sps(B) = 1 / (1 + max(0, B - knee) / knee)."""
+    g = _rng(seed, _S_SCHED)
+    c = g.beta(beta[0], beta[1], size=(R, gamma)).astype(np.float32)
+    knee = 4 * R if knee is None else knee
+    B = np.arange(R * (gamma + 1) + 1, dtype=np.float64)
+    sps = 1.0 / (1.0 + np.maximum(0.0, B - knee) / knee)
+    return dict(R=R, gamma=gamma, c=c, sps=sps, knee=knee)
