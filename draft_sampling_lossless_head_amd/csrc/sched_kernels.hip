@@ -10,9 +10,11 @@
 // prefix_schedule: one workgroup of 1024 threads for the whole batch.
 //   1. survival a_{r,j} = c_{r,0} * ... * c_{r,j}: one thread per request,
 //      float32 products left to right;
-//   2. one 64-bit key per candidate, (~bits(a) << 32) | (r * gamma + j):
-//      for a in [0, 1] ascending keys mean descending a, ties broken by the
-//      lower request, then the lower position; bitonic sort in LDS;
+//   2. one key per candidate, ~bits(a): for a in [0, 1] ascending keys mean
+//      descending a; a stable sort keeps candidates of equal a in id order
+//      r * gamma + j (lower request, then lower position).  Each request's
+//      keys already ascend, so the sort merges adjacent runs level by level
+//      in LDS;
 //   3. q_t = a_t cut to a multiple of 2^-48 as an integer; inclusive integer
 //      prefix sums S_t give tau_t = R + S_t 2^-48 exactly (no dependence on
 //      the order of the sums); Theta_t = tau_t * SPS(R + t) in double for every
@@ -132,7 +134,6 @@ hipError_t confidence_launch(const ConfArgs& a, hipStream_t s) {
 // ---------------------------------------------------------------------------
 
 constexpr int kSchedThreads = 1024;
-constexpr int kSchedPerThread = kSchedMax / kSchedThreads;   // 8
 constexpr double kTwo48 = 281474976710656.0;
 
 __device__ __forceinline__ int64_t shfl_up_i64(int64_t x, int d) {
@@ -141,70 +142,133 @@ __device__ __forceinline__ int64_t shfl_up_i64(int64_t x, int d) {
     return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
 }
 
-// Theta_t for the integer prefix S_t of t admitted candidates.
-__device__ __forceinline__ double sched_theta(int R, int t, int64_t S, const double* sps, int nsps) {
+// Theta_t for the integer prefix S_t of t admitted candidates, given
+// SPS(R + t) (0 past the end of the table).
+__device__ __forceinline__ double sched_theta(int R, int64_t S, double sps_B) {
     const double tau = (double)((int64_t)R * (int64_t)kTwo48 + S) / kTwo48;
-    const int B = R + t;
-    return tau * (B < nsps ? sps[B] : 0.0);
+    return tau * sps_B;
 }
 
+// Stable ascending sort of the N 32-bit keys val (with their candidate ids
+// idx alongside), which arrive as ascending runs of length G (one per
+// request: survival falls along a request) in id order.  Pairs of adjacent
+// runs are merged level by level; every key finds its place in the merged run
+// from its own rank plus the number of keys of the other run before it (left
+// run: keys of the right run below it; right run: keys of the left run at or
+// below it, so equal keys keep id order).  That count is a branch-free binary
+// search with the same number of steps on every lane, the E keys of a thread
+// searched together.
+template <int E>
+__device__ __forceinline__ void merge_runs(uint32_t* val, int* idx, int N, int G, int tid) {
+    for (int s = G; s < N; s <<= 1) {
+        const int top = 1 << (31 - __builtin_clz(s));   // highest power of two <= s
+        uint32_t x[E];
+        int id[E], lo[E], n[E], cnt[E], own[E];
+        bool right[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int i = tid * E + e;
+            x[e] = 0;
+            id[e] = 0;
+            lo[e] = 0;
+            n[e] = 0;
+            cnt[e] = 0;
+            own[e] = -1;
+            right[e] = false;
+            if (i < N) {
+                x[e] = val[i];
+                id[e] = idx[i];
+                const int p0 = (i / (2 * s)) * (2 * s);   // start of the pair
+                const int mid = min(p0 + s, N), end = min(p0 + 2 * s, N);
+                if (i < mid) {
+                    lo[e] = mid;
+                    n[e] = end - mid;
+                    own[e] = i;
+                } else {
+                    lo[e] = p0;
+                    n[e] = mid - p0;
+                    own[e] = p0 + (i - mid);
+                    right[e] = true;
+                }
+            }
+        }
+        for (int b = top; b > 0; b >>= 1) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int probe = cnt[e] + b;
+                if (probe <= n[e]) {
+                    const uint32_t y = val[lo[e] + probe - 1];
+                    if (y < x[e] || (right[e] && y == x[e])) cnt[e] = probe;
+                }
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            if (own[e] >= 0) {
+                val[own[e] + cnt[e]] = x[e];
+                idx[own[e] + cnt[e]] = id[e];
+            }
+        }
+        __syncthreads();
+    }
+}
+
+template <int E>
 __global__ __launch_bounds__(kSchedThreads)
 void prefix_schedule_kernel(SchedArgs A) {
-    __shared__ uint64_t keys[kSchedMax];    // sort buffer; later the per-request counts
+    __shared__ uint32_t val[kSchedMax];     // sort keys ~bits(a), sorted in place; later the counts
+    __shared__ int idx[kSchedMax];          // candidate id r * gamma + j of each key
+    __shared__ float cl[kSchedMax];         // the confidences, staged
     __shared__ int64_t wave_tot[kSchedThreads / kWave];
     __shared__ int stop_t;
     __shared__ int64_t S_stop;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int R = A.R, G = A.gamma, N = R * G;
-    int P = 1;
-    while (P < N) P <<= 1;
 
-    // 1-2. survival products and keys; pads sort last
+    // the SPS entries this thread's sorted range will need, fetched now so
+    // their latency hides behind the sort
+    const int base = tid * E;
+    double sp[E + 1];
+#pragma unroll
+    for (int e = 0; e <= E; ++e) {
+        const int Bt = R + base + e;
+        sp[e] = (base + e <= N && Bt < A.nsps) ? A.sps[Bt] : 0.0;
+    }
+
+    // 1-2. survival products (staged through LDS so each request's chain
+    //      reads LDS, not HBM) and keys.  Values outside [0, 1] are clamped
+    //      (NaN to 0) so that every request's run stays sorted.
+    for (int i = tid; i < N; i += kSchedThreads) cl[i] = fminf(fmaxf(A.c[i], 0.0f), 1.0f);
+    if (tid == 0) stop_t = INT_MAX;
+    __syncthreads();
     for (int r = tid; r < R; r += kSchedThreads) {
         float a = 1.0f;
         for (int j = 0; j < G; ++j) {
-            a = a * A.c[(size_t)r * G + j];
-            // -0 (and, outside the domain, negatives and NaN) keys as +0
-            const uint32_t bits = a > 0.0f ? __float_as_uint(a) : 0u;
-            keys[r * G + j] = ((uint64_t)(~bits) << 32) | (uint32_t)(r * G + j);
+            a = a * cl[r * G + j];
+            const uint32_t bits = a > 0.0f ? __float_as_uint(a) : 0u;   // -0 keys as +0
+            val[r * G + j] = ~bits;
+            idx[r * G + j] = r * G + j;
         }
     }
-    for (int i = N + tid; i < P; i += kSchedThreads) keys[i] = ~0ull;
-    if (tid == 0) stop_t = INT_MAX;
     __syncthreads();
-
-    // bitonic sort, ascending
-    for (int k = 2; k <= P; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = tid; i < (P >> 1); i += kSchedThreads) {
-                const int lo = ((i & ~(j - 1)) << 1) | (i & (j - 1));
-                const int hi = lo | j;
-                const uint64_t x = keys[lo], y = keys[hi];
-                const bool up = (lo & k) == 0;
-                if ((x > y) == up) {
-                    keys[lo] = y;
-                    keys[hi] = x;
-                }
-            }
-            __syncthreads();
-        }
+    merge_runs<E>(val, idx, N, G, tid);
+    uint32_t kv[E];
+    int kid[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        kv[e] = base + e < N ? val[base + e] : ~0u;
+        kid[e] = base + e < N ? idx[base + e] : 0;
     }
 
-    // 3. integer prefix sums of the cut survival values; each thread owns the
-    //    candidates [tid * E, tid * E + E) of the sorted order
-    const int E = (N + kSchedThreads - 1) / kSchedThreads;
-    const int base = tid * E;
-    uint64_t kk[kSchedPerThread];
-    int64_t q[kSchedPerThread];
+    // 3. integer prefix sums of the cut survival values over the sorted order
+    int64_t q[E];
     int64_t mine = 0;
 #pragma unroll
-    for (int e = 0; e < kSchedPerThread; ++e) {
-        kk[e] = 0;
+    for (int e = 0; e < E; ++e) {
         q[e] = 0;
-        if (e < E && base + e < N) {
-            kk[e] = keys[base + e];
-            float a = __uint_as_float(~(uint32_t)(kk[e] >> 32));
-            a = fminf(a, 1.0f);   // inputs above 1 do not cut above 2^48
+        if (base + e < N) {
+            const float a = __uint_as_float(~kv[e]);
             q[e] = (int64_t)((double)a * kTwo48);
             mine += q[e];
         }
@@ -219,18 +283,20 @@ void prefix_schedule_kernel(SchedArgs A) {
     if (lane == kWave - 1) wave_tot[wave] = incl;
     __syncthreads();
     int64_t excl = incl - mine;
-    for (int w = 0; w < wave; ++w) excl += wave_tot[w];
+#pragma unroll
+    for (int w = 0; w < kSchedThreads / kWave; ++w)
+        if (w < wave) excl += wave_tot[w];
 
     // first fall of Theta: the smallest t >= 1 with Theta_t < Theta_{t-1}
-    {
+    if (base < N) {
         int64_t S = excl;
-        double prev = sched_theta(R, base, S, A.sps, A.nsps);
+        double prev = sched_theta(R, S, sp[0]);
 #pragma unroll
-        for (int e = 0; e < kSchedPerThread; ++e) {
-            if (e < E && base + e < N) {
+        for (int e = 0; e < E; ++e) {
+            if (base + e < N) {
                 S += q[e];
                 const int t = base + e + 1;
-                const double th = sched_theta(R, t, S, A.sps, A.nsps);
+                const double th = sched_theta(R, S, sp[e + 1]);
                 if (th < prev) {
                     atomicMin(&stop_t, t);
                     break;
@@ -246,20 +312,20 @@ void prefix_schedule_kernel(SchedArgs A) {
         int64_t S = excl;
         if (admitted == 0 && tid == 0) S_stop = 0;
 #pragma unroll
-        for (int e = 0; e < kSchedPerThread; ++e) {
-            if (e < E && base + e < N) {
+        for (int e = 0; e < E; ++e) {
+            if (base + e < N) {
                 S += q[e];
                 if (base + e + 1 == admitted) S_stop = S;
             }
         }
     }
-    // 4. per-request counts of the admitted candidates (keys buffer reused)
-    int* cnt = reinterpret_cast<int*>(keys);
+    // 4. per-request counts of the admitted candidates (key buffer reused)
+    int* cnt = reinterpret_cast<int*>(val);
     for (int r = tid; r < R; r += kSchedThreads) cnt[r] = 0;
     __syncthreads();
 #pragma unroll
-    for (int e = 0; e < kSchedPerThread; ++e)
-        if (e < E && base + e < admitted) atomicAdd(&cnt[(int)(uint32_t)kk[e] / G], 1);
+    for (int e = 0; e < E; ++e)
+        if (base + e < admitted) atomicAdd(&cnt[min(kid[e] / G, R - 1)], 1);
     __syncthreads();
     for (int r = tid; r < R; r += kSchedThreads) A.lens[r] = cnt[r];
     if (tid == 0) {
@@ -269,7 +335,12 @@ void prefix_schedule_kernel(SchedArgs A) {
 }
 
 hipError_t prefix_schedule_launch(const SchedArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL(prefix_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, s, a);
+    const int N = a.R * a.gamma;
+    const dim3 g(1), b(kSchedThreads);
+    if (N <= kSchedThreads) hipLaunchKernelGGL(prefix_schedule_kernel<1>, g, b, 0, s, a);
+    else if (N <= 2 * kSchedThreads) hipLaunchKernelGGL(prefix_schedule_kernel<2>, g, b, 0, s, a);
+    else if (N <= 4 * kSchedThreads) hipLaunchKernelGGL(prefix_schedule_kernel<4>, g, b, 0, s, a);
+    else hipLaunchKernelGGL(prefix_schedule_kernel<8>, g, b, 0, s, a);
     return hipGetLastError();
 }
 

@@ -348,8 +348,8 @@ spec_status_t spec_confidence_head(const void *h, int h_dtype, int d, const int3
  * Because a is non-increasing along a request, the admitted set is a prefix
  * of every request.
  *
- * c       [R, gamma]  fp32 confidences, each in [0, 1] (other values give
- *                     unspecified lengths; the call still completes)
+ * c       [R, gamma]  fp32 confidences, each in [0, 1] (other values are
+ *                     clamped into [0, 1], NaN to 0)
  * sps     [nsps]      double steps per second of the engine at batch size B
  *                     (index B); may be NULL when nsps == 0
  * lens    [R]         out: int32 l_r
