@@ -24,4 +24,5 @@ from .binding import (  # noqa: F401
     verify,
     confidence,
     prefix_schedule,
+    tree_select,
 )

@@ -33,6 +33,10 @@ PINS = {
                        "throughput; admitted set is the global top-t; constant SPS admits all; "
                        "SPS that vanishes past R admits none; hand-worked example; early stop at "
                        "the first fall even when a later size would be higher",
+    "tree_select": "brute force over every prefix-closed node set of the budget on tiny trees "
+                   "(the chosen set is one of them and reaches the best summed survival); chain "
+                   "gives its first n nodes; star gives numpy's stable top-n of c; all-ones gives "
+                   "breadth-first order; a forest of chains matches the prefix scheduler's order",
 }
 
 
@@ -94,6 +98,8 @@ def _L():
         lib.orc_prefix_schedule.argtypes = [f, ctypes.c_int, ctypes.c_int, d, ctypes.c_int, i,
                                             d, d]
         lib.orc_prefix_schedule.restype = ctypes.c_int
+        lib.orc_tree_select.argtypes = [i, f, ctypes.c_int, ctypes.c_int, i, d]
+        lib.orc_tree_select.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -311,3 +317,18 @@ def prefix_schedule(c, sps):
     if st != 0:
         raise MemoryError("orc_prefix_schedule")
     return lens, int(B.value), tau.value
+
+
+def tree_select(parent, c, n):
+    """Top-n nodes of one draft tree by survival probability: (sel int32 [n],
+    score).  parent int32 [M] with parent[v] in [-1, v); c float32 [M]."""
+    parent = _i32(parent)
+    c = np.ascontiguousarray(c, dtype=np.float32)
+    M = parent.size
+    sel = np.full(max(n, 0), -1, dtype=np.int32)
+    score = ctypes.c_double()
+    st = _L().orc_tree_select(_ip(parent), c.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), M,
+                              n, _ip(sel), ctypes.byref(score))
+    if st != 0:
+        return sel, float("nan")
+    return sel, score.value

@@ -22,6 +22,8 @@
  *   [P1] also §2.1 "Confidence Head" (c_k = sigma(w^T [h_k; W1[x_{k-1}]]))
  *        and §2.2 "Hardware-Aware Prefix Scheduler" (survival products,
  *        B and tau, Theta = tau * SPS(B), global greedy order, early stop).
+ *   [P2] also section "γ 재배분: 체인 대신 트리" (tree drafts: the top-n nodes by
+ *        survival probability, ties to the shallower node).
  *   [PX] Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as
  *        1, 2, 3", SC'11 -- Philox4x32 with 10 rounds.
  *
@@ -43,6 +45,10 @@
  *     integers; B = R + admitted; SPS(B) = 0 past the end of its table; the
  *     search stops at the first admission that lowers tau * SPS(B) (ties
  *     continue), and that admission is not made.
+ *   - tree selection: nodes come parents first (parent[v] < v, -1 = a child
+ *     of the root, the last accepted token); a_v = c_v * a_parent in float32
+ *     (root 1); order a descending, then depth ascending, then node id; the
+ *     score sums the chosen a cut to multiples of 2^-48, as the scheduler.
  */
 #include <math.h>
 #include <stdint.h>
@@ -558,5 +564,59 @@ int orc_prefix_schedule(const float *c, int R, int gamma, const double *sps, int
     *B_out = (double)(R + admitted);
     *tau_out = tau;
     free(cand);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* [P2] Tree drafts: top-n nodes by survival probability.                    */
+/* ------------------------------------------------------------------------ */
+
+typedef struct { float a; int depth, v; } orc_node;
+
+static int orc_node_cmp(const void *x, const void *y)
+{
+    const orc_node *p = (const orc_node *)x, *q = (const orc_node *)y;
+    if (p->a != q->a) return p->a > q->a ? -1 : 1;            /* higher survival first */
+    if (p->depth != q->depth) return p->depth < q->depth ? -1 : 1;   /* then shallower */
+    return p->v < q->v ? -1 : (p->v > q->v);
+}
+
+/* One tree of M candidate nodes: parent[v] in [-1, v) (-1: child of the
+ * root), c[v] = chance that v is accepted once its parent is.  Survival
+ * a_v = c_v * a_parent (root 1) in float32.  Writes the n nodes of highest
+ * survival (ties: shallower, then lower id) to sel[0 .. n-1] in that order,
+ * -1 past M, and their summed survival (each cut to a multiple of 2^-48,
+ * summed exactly) to *score.  Returns 0; -1 for a parent outside [-1, v)
+ * (sel all -1, score NaN) or when memory runs out. */
+int orc_tree_select(const int *parent, const float *c, int M, int n, int *sel, double *score)
+{
+    orc_node *nd = (orc_node *)malloc(sizeof(orc_node) * (size_t)(M > 0 ? M : 1));
+    float *a = (float *)malloc(sizeof(float) * (size_t)(M > 0 ? M : 1));
+    int *depth = (int *)malloc(sizeof(int) * (size_t)(M > 0 ? M : 1));
+    const double scale = 281474976710656.0;   /* 2^48 */
+    int64_t sum_q = 0;
+    int v, i;
+    if (!nd || !a || !depth) { free(nd); free(a); free(depth); return -1; }
+    for (i = 0; i < n; i++) sel[i] = -1;
+    for (v = 0; v < M; v++) {
+        const int p = parent[v];
+        if (p < -1 || p >= v) {
+            *score = NAN;
+            free(nd); free(a); free(depth);
+            return -1;
+        }
+        a[v] = (p < 0 ? 1.0f : a[p]) * c[v];
+        depth[v] = p < 0 ? 1 : depth[p] + 1;
+        nd[v].a = a[v];
+        nd[v].depth = depth[v];
+        nd[v].v = v;
+    }
+    qsort(nd, (size_t)M, sizeof(orc_node), orc_node_cmp);
+    for (i = 0; i < n && i < M; i++) {
+        sel[i] = nd[i].v;
+        sum_q += (int64_t)((double)nd[i].a * scale);
+    }
+    *score = (double)sum_q / scale;
+    free(nd); free(a); free(depth);
     return 0;
 }
