@@ -23,6 +23,7 @@ from .api import (  # noqa: F401
     spec_prefix_schedule,
     spec_profile_enable,
     spec_profile_read,
+    spec_tree_select,
     spec_verify,
     spec_verify_markov,
     spec_version,

@@ -77,6 +77,8 @@ def load_library():
     lib.spec_confidence_head.restype = i32
     lib.spec_prefix_schedule.argtypes = [vp, i32, i32, vp, i32, vp, vp, vp, vp]
     lib.spec_prefix_schedule.restype = i32
+    lib.spec_tree_select.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
+    lib.spec_tree_select.restype = i32
     lib.spec_draft_set_poll_limit.argtypes = [u32]
     lib.spec_draft_set_poll_limit.restype = u32
     lib.spec_profile_enable.argtypes = [ctypes.c_char_p]
@@ -394,6 +396,27 @@ def spec_prefix_schedule(c, sps, *, out=None, stream=None):
     st = lib.spec_prefix_schedule(_ptr(c), R, gamma, _ptr(sps), sps.numel(), _ptr(out["lens"]),
                                   _ptr(out.get("B")), _ptr(out.get("tau")), _stream(stream))
     _check(st, "spec_prefix_schedule")
+    return out
+
+
+def spec_tree_select(parent, c, n, *, out=None, stream=None):
+    """Top-n nodes of R draft trees by survival probability.  parent int32
+    [R, M] (parents first, -1: child of the root), c float32 [R, M].  Returns
+    dict(sel int32 [R, n], score float64 [R])."""
+    lib = load_library()
+    _dev(parent, "parent")
+    _dev(c, "c")
+    if parent.dtype != torch.int32 or parent.dim() != 2:
+        raise SpecError("parent must be int32 [R, M]")
+    if c.dtype != torch.float32 or c.shape != parent.shape:
+        raise SpecError("c must be float32 [R, M]")
+    R, M = parent.shape
+    if out is None:
+        out = dict(sel=torch.empty((R, n), dtype=torch.int32, device=c.device),
+                   score=torch.empty(R, dtype=torch.float64, device=c.device))
+    st = lib.spec_tree_select(_ptr(parent), _ptr(c), R, M, int(n), _ptr(out["sel"]),
+                              _ptr(out.get("score")), _stream(stream))
+    _check(st, "spec_tree_select")
     return out
 
 

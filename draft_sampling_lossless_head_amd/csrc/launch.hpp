@@ -260,6 +260,17 @@ struct SchedArgs {
 };
 hipError_t prefix_schedule_launch(const SchedArgs& a, hipStream_t s);
 
+// Top-n nodes of R draft trees of M <= kTreeMax nodes each.
+constexpr int kTreeMax = 4096;
+struct TreeArgs {
+    const int32_t* parent;      // [R, M] parent ids in [-1, v)
+    const float* c;             // [R, M] confidences in [0, 1]
+    int R, M, n;
+    int32_t* sel;               // [R, n] out
+    double* score;              // [R] out or null
+};
+hipError_t tree_select_launch(const TreeArgs& a, hipStream_t s);
+
 hipError_t philox_uniforms_launch(uint64_t seed, uint32_t offset, uint32_t stream, int B, int K,
                                   float* out, hipStream_t s);
 

@@ -344,4 +344,132 @@ hipError_t prefix_schedule_launch(const SchedArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Tree drafts: the n nodes of highest survival ("Speculative Decoding Part 1",
+// section "γ 재배분: 체인 대신 트리")
+// ---------------------------------------------------------------------------
+//
+// One workgroup per tree of M <= 4096 candidate nodes listed parents first.
+//   1. survival a_v = c_v * a_parent (root 1, float32) and depth, level by
+//      level: in round t a node whose parent was finished in an earlier round
+//      takes its value and is stamped t, so no node reads a value written in
+//      the same round;
+//   2. key (~bits(a) << 32) | (depth << 16) | v: ascending keys are higher
+//      survival first, then shallower, then lower id; bitonic sort in LDS;
+//   3. the first n ids out (-1 past M) and the exact sum of their survival
+//      cut to multiples of 2^-48.
+
+constexpr int kTreeThreads = 1024;
+
+__global__ __launch_bounds__(kTreeThreads)
+void tree_select_kernel(TreeArgs A) {
+    __shared__ uint64_t keys[kTreeMax];   // first: parent ids and confidences
+    __shared__ float av[kTreeMax];
+    __shared__ int stamp[kTreeMax];       // round in which the node was finished (0: not yet)
+    __shared__ int depth[kTreeMax];
+    __shared__ int flag_bad;
+    __shared__ int64_t part[kTreeThreads / kWave];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int M = A.M, n = A.n;
+    const size_t t = blockIdx.x;
+    int* par = reinterpret_cast<int*>(keys);
+    float* cc = reinterpret_cast<float*>(keys) + kTreeMax;
+    if (tid == 0) flag_bad = 0;
+    __syncthreads();
+    for (int v = tid; v < M; v += kTreeThreads) {
+        const int p = A.parent[t * M + v];
+        if (p < -1 || p >= v) flag_bad = 1;
+        par[v] = p;
+        cc[v] = fminf(fmaxf(A.c[t * M + v], 0.0f), 1.0f);   // NaN to 0
+        stamp[v] = 0;
+    }
+    __syncthreads();
+    if (flag_bad) {
+        for (int i = tid; i < n; i += kTreeThreads) A.sel[t * n + i] = -1;
+        if (tid == 0 && A.score) A.score[t] = NAN;
+        return;
+    }
+
+    // 1. survival and depth, one level per round
+    for (int round = 1;; ++round) {
+        int left = 0;
+        for (int v = tid; v < M; v += kTreeThreads) {
+            if (stamp[v] != 0) continue;
+            const int p = par[v];
+            if (p < 0) {
+                av[v] = cc[v];
+                depth[v] = 1;
+                stamp[v] = round;
+            } else {
+                const int sp = stamp[p];
+                if (sp != 0 && sp < round) {
+                    av[v] = av[p] * cc[v];
+                    depth[v] = depth[p] + 1;
+                    stamp[v] = round;
+                } else {
+                    left = 1;
+                }
+            }
+        }
+        if (!__syncthreads_or(left)) break;   // also the barrier between rounds
+    }
+
+    // 2. keys and the sort (parents and confidences are no longer needed)
+    int P = 1;
+    while (P < M) P <<= 1;
+    for (int v = tid; v < P; v += kTreeThreads) {
+        uint64_t key = ~0ull;
+        if (v < M) {
+            const uint32_t bits = av[v] > 0.0f ? __float_as_uint(av[v]) : 0u;   // -0 keys as +0
+            key = ((uint64_t)(~bits) << 32) | ((uint32_t)depth[v] << 16) | (uint32_t)v;
+        }
+        keys[v] = key;
+    }
+    __syncthreads();
+    for (int k = 2; k <= P; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = tid; i < (P >> 1); i += kTreeThreads) {
+                const int lo = ((i & ~(j - 1)) << 1) | (i & (j - 1));
+                const int hi = lo | j;
+                const uint64_t x = keys[lo], y = keys[hi];
+                if ((x > y) == ((lo & k) == 0)) {
+                    keys[lo] = y;
+                    keys[hi] = x;
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    // 3. the first n nodes and their summed survival
+    int64_t sum = 0;
+    for (int i = tid; i < n; i += kTreeThreads) {
+        int v = -1;
+        if (i < M) {
+            v = (int)(keys[i] & 0xFFFFu);
+            sum += (int64_t)((double)av[v] * kTwo48);
+        }
+        A.sel[t * n + i] = v;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const int lo = __shfl_xor((int)(uint32_t)(uint64_t)sum, off);
+        const int hi = __shfl_xor((int)(uint32_t)((uint64_t)sum >> 32), off);
+        sum += (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+    }
+    if (lane == 0) part[wave] = sum;
+    __syncthreads();
+    if (tid == 0 && A.score) {
+        int64_t tot = 0;
+        for (int w = 0; w < kTreeThreads / kWave; ++w) tot += part[w];
+        A.score[t] = (double)tot / kTwo48;
+    }
+}
+
+hipError_t tree_select_launch(const TreeArgs& a, hipStream_t s) {
+    if (a.R == 0) return hipSuccess;
+    hipLaunchKernelGGL(tree_select_kernel, dim3(a.R), dim3(kTreeThreads), 0, s, a);
+    return hipGetLastError();
+}
+
 }  // namespace specdec

@@ -487,6 +487,29 @@ spec_status_t spec_prefix_schedule(const float* c, int R, int gamma, const doubl
     return e == hipSuccess ? SPEC_OK : hip_fail(e, "prefix_schedule");
 }
 
+spec_status_t spec_tree_select(const int32_t* parent, const float* c, int R, int M, int n,
+                               int32_t* sel, double* score, void* stream) {
+    g_err.clear();
+    if (R < 0 || M < 0 || n < 0) return fail(SPEC_ERR_INVALID, "R, M and n must be >= 0");
+    if (M > kTreeMax) return fail(SPEC_ERR_UNSUPPORTED, "M must be <= 4096");
+    if ((int64_t)R * M > INT32_MAX || (int64_t)R * n > INT32_MAX) return fail(SPEC_ERR_UNSUPPORTED, "R * M or R * n too large");
+    if (R == 0) return SPEC_OK;
+    if ((M > 0 && (!parent || !c)) || (n > 0 && !sel)) return fail(SPEC_ERR_INVALID, "null parent, c or sel");
+    TreeArgs a{};
+    a.parent = parent;
+    a.c = c;
+    a.R = R;
+    a.M = M;
+    a.n = n;
+    a.sel = sel;
+    a.score = score;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* t = prof_begin("tree_select", s);
+    hipError_t e = tree_select_launch(a, s);
+    prof_end(t, s);
+    return e == hipSuccess ? SPEC_OK : hip_fail(e, "tree_select");
+}
+
 size_t spec_pack_w2_bytes(int r, int V) {
     if (r <= 0 || V <= 0 || V > kMaxV) return 0;
     return w2p_bytes(r, V);

@@ -366,6 +366,33 @@ spec_status_t spec_prefix_schedule(const float *c, int R, int gamma, const doubl
 
 /*
  * ---------------------------------------------------------------------------
+ * Tree drafts: top-n nodes by survival probability  [VESSL "Speculative
+ * Decoding Part 1", section "γ 재배분: 체인 대신 트리"]
+ * ---------------------------------------------------------------------------
+ * For each of R candidate trees of M nodes listed parents first:
+ *     a_v = c_v * a_parent(v)   (fp32; a child of the root has a = c_v)
+ *     sel[t, 0 .. n-1] = the n nodes of highest a_v, ties to the shallower
+ *     node, then the lower id; -1 past M.  Because a never grows down a
+ *     branch, the chosen set contains the parent of every chosen node.
+ *     score[t] = the sum of the chosen a_v, each cut to a multiple of
+ *     2^-48 and summed exactly (the expected number of accepted nodes).
+ *
+ * parent [R, M]  int32 parent ids, parent[t, v] in [-1, v) (-1: a child of
+ *                the root, the last accepted token)
+ * c      [R, M]  fp32 chance that node v is accepted once its parent is, in
+ *                [0, 1] (other values are clamped into [0, 1], NaN to 0)
+ * sel    [R, n]  out: int32 node ids in selection order
+ * score  [R]     out (optional): fp64
+ * A tree with a parent id outside [-1, v) gets sel -1 and score NaN.
+ * One workgroup per tree; all pointers device memory, stream-ordered.
+ * Errors: SPEC_ERR_INVALID for R, M, n < 0 or null parent, c (M > 0) or sel
+ * (n > 0); SPEC_ERR_UNSUPPORTED for M > 4096.
+ */
+spec_status_t spec_tree_select(const int32_t *parent, const float *c, int R, int M, int n,
+                               int32_t *sel, double *score, void *stream);
+
+/*
+ * ---------------------------------------------------------------------------
  * Kernel timing (benchmarking aid; not needed for correct use)
  * ---------------------------------------------------------------------------
  * spec_profile_enable(name) starts a fresh record: from then on every launch
@@ -374,7 +401,7 @@ spec_status_t spec_prefix_schedule(const float *c, int R, int gamma, const doubl
  * "rnn_gates", "w2_transpose", "verify_rows_p", "verify_rows_q",
  * "verify_decide", "verify_residual_rows", "verify_final_partials",
  * "verify_final_draw", "verify_resid", "acceptance_rate", "confidence_head",
- * "prefix_schedule", or "*" for all) is bracketed
+ * "prefix_schedule", "tree_select", or "*" for all) is bracketed
  * by two hipEvents recorded on its launch stream.  NULL or "" stops timing.
  * spec_profile_read waits for the recorded events and returns the number of
  * timed launches and their summed duration in milliseconds.  Process-wide

@@ -37,7 +37,7 @@ def test_header_declares_the_boundary():
               "spec_version", "spec_pack_w2", "spec_pack_w2_bytes", "spec_verify_markov",
               "spec_verify_markov_workspace_size", "spec_draft_set_persistent",
               "spec_draft_set_poll_limit", "spec_acceptance_rate", "spec_confidence_head",
-              "spec_prefix_schedule"):
+              "spec_prefix_schedule", "spec_tree_select"):
         assert n in names
 
 
@@ -253,6 +253,26 @@ def test_prefix_schedule_validation(lib):
     assert call(R=1025, G=8) == SPEC_ERR_UNSUPPORTED
     assert call(R=8193, G=1) == SPEC_ERR_UNSUPPORTED
     assert call(R=8193, G=0) == SPEC_ERR_UNSUPPORTED
+
+
+def test_tree_select_validation(lib):
+    """Argument checks of spec_tree_select happen before any launch."""
+    fake = ctypes.c_void_p(4096)
+    f = lib.spec_tree_select
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    f.argtypes = [vp, vp, i, i, i, vp, vp, vp]
+    f.restype = i
+
+    def call(parent=fake, c=fake, R=2, M=10, n=4, sel=fake):
+        return f(parent, c, R, M, n, sel, None, None)
+    assert call(parent=None) == SPEC_ERR_INVALID
+    assert call(c=None) == SPEC_ERR_INVALID
+    assert call(sel=None) == SPEC_ERR_INVALID
+    assert call(R=-1) == SPEC_ERR_INVALID
+    assert call(M=-1) == SPEC_ERR_INVALID
+    assert call(n=-1) == SPEC_ERR_INVALID
+    assert call(M=4097) == SPEC_ERR_UNSUPPORTED
+    assert call(R=0, parent=None) == SPEC_OK   # nothing to do
 
 
 def test_draft_poll_limit(lib):
