@@ -470,6 +470,23 @@ def main():
                                           chosen_batch=int(s_out["B"].item()),
                                           tau=round(float(s_out["tau"].item()), 3),
                                           mean_len=round(float(s_out["lens"].float().mean().item()), 3))
+    # Tree drafts: the top 64 of 1024 candidate nodes per request by survival
+    # probability, for every request of the batch (not part of the cycle).
+    tw = workloads.make_trees(B, 1024, 1234)
+    par_d, tc_d = to_dev(tw["parent"]), to_dev(tw["c"])
+    t_out = dict(sel=torch.empty((B, 64), dtype=torch.int32, device=dev),
+                 score=torch.empty(B, dtype=torch.float64, device=dev))
+    for i in range(3):
+        step(args.warmup + i)
+    sd.spec_profile_enable("tree_select")
+    for i in range(args.steps):
+        sd.spec_tree_select(par_d, tc_d, 64, out=t_out)
+    n, ms = sd.spec_profile_read()
+    sd.spec_profile_enable(None)
+    if n:
+        result_extra["tree_select"] = dict(avg_us=round(ms * 1e3 / n, 2), trees=B, nodes=1024,
+                                           budget=64,
+                                           mean_score=round(float(t_out["score"].mean().item()), 3))
     tdraft = sum(kernels[k]["us_per_step"] for k in kernels if k.startswith("draft")
                  or k == "w2_pack")
     tver = sum(kernels[k]["us_per_step"] for k in kernels if k.startswith("verify"))

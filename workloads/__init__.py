@@ -11,6 +11,7 @@ from .gen import (  # noqa: F401
     make_markov,
     make_rnn,
     make_schedule,
+    make_trees,
     make_verify_only,
     packed_offsets,
 )

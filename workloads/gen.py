@@ -202,7 +202,7 @@ def make_verify_only(B, gamma, V, seed, dtype="f32", scale=4.0, zipf=1.1, sigma=
 
 
 # Stream ids of the confidence-head and scheduler inputs.
-_S_CONF, _S_SCHED = 4, 5
+_S_CONF, _S_SCHED, _S_TREE = 4, 5, 6
 
 
 def make_confidence(R, gamma, V, r, d, seed, h_dtype="bf16", w_dtype="bf16", w_std=0.02,
@@ -235,3 +235,16 @@ def make_schedule(R, gamma, seed, knee=None, beta=(4.0, 1.2)):
     B = np.arange(R * (gamma + 1) + 1, dtype=np.float64)
     sps = 1.0 / (1.0 + np.maximum(0.0, B - knee) / knee)
     return dict(R=R, gamma=gamma, c=c, sps=sps, knee=knee)
+
+
+def make_trees(R, M, seed, reach=8, beta=(4.0, 1.2)):
+    """Candidate draft trees, parents first: node v's parent is uniform on
+    [max(-1, v - reach), v) (-1: a child of the root), so trees are a few
+    nodes wide at each depth; acceptance chances c ~ Beta(beta) in fp32."""
+    g = _rng(seed, _S_TREE)
+    parent = np.empty((R, M), dtype=np.int32)
+    for v in range(M):
+        lo = max(-1, v - reach)
+        parent[:, v] = g.integers(lo, v, size=R) if v > 0 else -1
+    c = g.beta(beta[0], beta[1], size=(R, M)).astype(np.float32)
+    return dict(R=R, M=M, parent=parent, c=c)
