@@ -237,14 +237,21 @@ def make_schedule(R, gamma, seed, knee=None, beta=(4.0, 1.2)):
     return dict(R=R, gamma=gamma, c=c, sps=sps, knee=knee)
 
 
-def make_trees(R, M, seed, reach=8, beta=(4.0, 1.2)):
-    """Candidate draft trees, parents first: node v's parent is uniform on
-    [max(-1, v - reach), v) (-1: a child of the root), so trees are a few
-    nodes wide at each depth; acceptance chances c ~ Beta(beta) in fp32."""
+def make_trees(R, M, seed, levels=16, beta=(4.0, 1.2)):
+    """Candidate draft trees in breadth-first order (parents first): M nodes
+    spread evenly over `levels` depths (a block of gamma positions, each a few
+    dozen candidates wide); a node's parent is uniform over the nodes one
+    level up (the root for the first level); acceptance chances
+    c ~ Beta(beta) in fp32."""
     g = _rng(seed, _S_TREE)
+    bounds = [(M * d) // levels for d in range(levels + 1)]
     parent = np.empty((R, M), dtype=np.int32)
-    for v in range(M):
-        lo = max(-1, v - reach)
-        parent[:, v] = g.integers(lo, v, size=R) if v > 0 else -1
+    for d in range(levels):
+        lo, hi = bounds[d], bounds[d + 1]
+        if d == 0:
+            parent[:, lo:hi] = -1
+        else:
+            plo, phi = bounds[d - 1], bounds[d]
+            parent[:, lo:hi] = g.integers(plo, max(phi, plo + 1), size=(R, hi - lo)) if phi > plo else -1
     c = g.beta(beta[0], beta[1], size=(R, M)).astype(np.float32)
     return dict(R=R, M=M, parent=parent, c=c)
