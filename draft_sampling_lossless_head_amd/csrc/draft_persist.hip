@@ -13,7 +13,10 @@
 //   1. wait for the tokens x_{k-1} of the block's rows (token words written by
 //      the finalize workgroups; the anchors x_0 at k = 0);
 //   2. E = W1[x_{k-1}] of the 64 rows gathered into LDS (direct loads, chunk c
-//      of row n stored in slot c ^ (n & 7): conflict-free B reads);
+//      of row n stored in slot c ^ (n & 7): conflict-free B reads).  The
+//      block's first units of U are already in flight: U does not depend on
+//      the tokens, so each wave issues them as soon as the previous block's
+//      summaries are out;
 //   3. per wave, units (32 rows x one of its 32-token blocks): U_k of the unit
 //      streams through a wave-private LDS ring (direct loads, D units ahead),
 //      16 (r = 256) 32x32x16 MFMAs against the resident W2 operands, then the
@@ -288,6 +291,32 @@ void draft_persist(PersistArgs P) {
     };
 
     const uint16_t* ninf = reinterpret_cast<const uint16_t*>(P.bar + kBarNegInf);
+    const uint16_t* usrc[2];
+    int utok[2], urow[2];
+    int rows_b = 0;
+    const size_t rg_step = (size_t)32 * G * (size_t)V;
+    int ci = 0, cj = 0, cs = 0;
+    size_t coff = 0;
+    // U cursor of row block rbb at position kk: row group, block, ring slot,
+    // and the U offset of (ci, cj) from the lane's unit-0 address.
+    auto setup_cursor = [&](int kk, int rbb) {
+        int ln = lane0;
+        asm volatile("" : "+v"(ln));
+        const int rr0 = rbb * kPersistRows;
+        rows_b = min(kPersistRows, B - rr0);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int m = 16 * q + (ln >> 2);
+            const int c = (ln & 3) ^ uswz(m);
+            urow[q] = m;
+            utok[q] = kStreamSeg * (blo + wave) + 8 * c;
+            usrc[q] = F.U + ((size_t)(rr0 + m) * G + kk) * (size_t)V + utok[q];
+        }
+        ci = 0;
+        cj = 0;
+        cs = 0;
+        coff = 0;
+    };
     for (int k = 0; k < G; ++k) {
         for (int rb = 0; rb < nrb; ++rb) {
             // Per-lane values below are recomputed for every row block from an
@@ -311,7 +340,8 @@ void draft_persist(PersistArgs P) {
                                     &ok_s)) {
                 return;
             }
-            // 2. E rows into LDS, then the first D units of U.
+            // 2. E rows into LDS.  The first D units of U were issued at the end of
+            //    the previous row block (here only for the launch's first block).
 #pragma unroll
             for (int q = 0; q < NCH / 4; ++q) {
                 const int pc = q * kPersistWaves + wave;
@@ -330,22 +360,6 @@ void draft_persist(PersistArgs P) {
             // units in order; past the last unit it issues the same two loads
             // of the -inf chunk into the slot just freed, so every wait allows
             // the same count.
-            const uint16_t* usrc[2];
-            int utok[2], urow[2];
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int m = 16 * q + (lane >> 2);
-                const int c = (lane & 3) ^ uswz(m);
-                urow[q] = m;
-                utok[q] = kStreamSeg * (blo + wave) + 8 * c;
-                usrc[q] = F.U + ((size_t)(r0 + m) * G + k) * (size_t)V + utok[q];
-            }
-            const int rows_b = rows;
-            const size_t rg_step = (size_t)32 * G * (size_t)V;
-            // issue cursor: row group, block, ring slot, and the U offset of
-            // (ci, cj) from the lane's unit-0 address (ci * rg_step + 128 cj)
-            int ci = 0, cj = 0, cs = 0;
-            size_t coff = 0;
             auto issue_next = [&]() {
                 char* dst = ring + (wave * NR + cs) * kPersistUnit;
                 const int rlim = rows_b - 32 * ci;   // rows of the group present (<= 0 past the last)
@@ -364,12 +378,13 @@ void draft_persist(PersistArgs P) {
                 }
                 if (++cs == NR) cs = 0;
             };
-            if (nj > 0) {
+            if (nj > 0 && k == 0 && rb == 0) {
+                setup_cursor(k, rb);
 #pragma unroll
                 for (int u = 0; u < D; ++u) issue_next();
                 wait_vm<2 * D>();                      // this wave's E loads have landed
             } else {
-                wait_vm<0>();
+                wait_vm<0>();                          // E (and the U issued before it)
             }
             asm volatile("s_barrier" ::: "memory");    // ... and every wave's
 
@@ -498,7 +513,19 @@ void draft_persist(PersistArgs P) {
                 flush_reset(rgp);
             }
             wait_vm<0>();      // this wave's segment summaries are out (written through)
-            __syncthreads();
+            // The next row block's first units: U does not depend on the tokens.
+            // The barriers below wait for LDS only, so these loads stay in flight
+            // while the share summaries go out and the next tokens are awaited.
+            {
+                const int rbn = rb + 1 < nrb ? rb + 1 : 0;
+                const int kn = rb + 1 < nrb ? k : k + 1;
+                if (nj > 0 && kn < G) {
+                    setup_cursor(kn, rbn);
+#pragma unroll
+                    for (int u = 0; u < D; ++u) issue_next();
+                }
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // xsum written
             // 4. one summary per (share, row): merge the waves' runs, tagged with
             // k + 1 in both words (read by the finalize without a grid barrier).
             if (tid < rows && xprev[tid] >= 0) {
@@ -525,7 +552,7 @@ void draft_persist(PersistArgs P) {
                 coh_store<true>(e64, tag | __float_as_uint(m));
                 coh_store<true>(e64 + 1, tag | (GREEDY ? (uint32_t)a : __float_as_uint(s)));
             }
-            __syncthreads();   // LDS (E, ring, xsum) is reused by the next row block
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // LDS (E, xsum) is reused by the next row block
         }
     }
 }
