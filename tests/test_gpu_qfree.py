@@ -49,6 +49,8 @@ DRAFT_CASES = [
     (4, 2, 153600, 256, "bf16", 1.0),   # 20 blocks per workgroup: all register blocks in use
     (3, 1, 153608, 256, "bf16", 1.0),   # one block more than fits: per-position kernels
     (130, 3, 8192, 128, "bf16", 1.0),   # three 64-row blocks, the last one of 2 rows
+    (65, 4, 9000, 256, "bf16", 1.0),    # a one-row second block: U of each block issued early
+    (128, 5, 30000, 64, "bf16", 0.0),   # two full blocks at r = 64, greedy
 ]
 
 
