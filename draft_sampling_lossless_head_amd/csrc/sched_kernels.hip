@@ -46,7 +46,8 @@ template <bool BF16>
 __device__ __forceinline__ float lane_dot_vec(const void* x, size_t x0, const float* w, int n,
                                               int lane) {
     float acc = 0.0f;
-    for (int i = lane * 8; i < n; i += kWave * 8) {
+#pragma unroll 4
+    for (int i = lane * 8; i < n; i += kWave * 8) {   // four 16-byte loads in flight per lane
         float v[8];
         if constexpr (BF16) {
             const u32x4_t q = __builtin_nontemporal_load(
