@@ -559,13 +559,14 @@ void draft_persist(PersistArgs P) {
 
 // Blocks per wave held in registers (320 VGPRs of W2 operands) and U ring
 // slots per wave (LDS: E rows + rings + tokens + run summaries <= 160 KB).
-// At r = 256 a shallow ring (four units ahead) is faster than a deep one: a
-// row block's first prefetch is issued by every CU at once and queues behind
-// the whole chip's, and fewer loads in flight also shorten the unit loop.
+// Shallow rings are faster (measured): the units' 64-byte row pieces stream
+// worse the more of them the chip has in flight, and with each row block's
+// first units issued at the end of the previous block, two (r = 256) or
+// three (r = 128, 64) units ahead keep the loop fed.
 template <int NKS> struct PersistShape;
-template <> struct PersistShape<16> { static constexpr int NB = 5, NR = 6; };
-template <> struct PersistShape<8> { static constexpr int NB = 10, NR = 15; };
-template <> struct PersistShape<4> { static constexpr int NB = 20, NR = 16; };
+template <> struct PersistShape<16> { static constexpr int NB = 5, NR = 4; };
+template <> struct PersistShape<8> { static constexpr int NB = 10, NR = 5; };
+template <> struct PersistShape<4> { static constexpr int NB = 20, NR = 5; };
 
 template <int NKS>
 static size_t persist_lds() {
