@@ -470,6 +470,45 @@ def main():
                                           chosen_batch=int(s_out["B"].item()),
                                           tau=round(float(s_out["tau"].item()), 3),
                                           mean_len=round(float(s_out["lens"].float().mean().item()), 3))
+        # DSpark's whole step: draft gamma positions, score them with the
+        # confidence head, schedule the lengths, verify only the scheduled
+        # prefixes (ragged lengths).  Emitted = sum of (accepted + 1).
+        if qfree:
+            v2 = dict(accepted=torch.empty(B, dtype=torch.int32, device=dev),
+                      out_tokens=torch.empty((B, g + 1), dtype=torch.int32, device=dev))
+
+            def dstep(i):
+                sd.spec_draft_sample_markov(U, x0, W1, None, T, W2T=W2T, seed=seed, offset=i,
+                                            out=d_out, workspace=ws_d)
+                sd.spec_confidence_head(h_d, x0, d_out["tokens"], W1, w_d, out=c_d)
+                sd.spec_prefix_schedule(c_d, sps_d, out=s_out)
+                sd.spec_verify_markov(P, U, x0, W1, None, d_out["tokens"], d_out["q_logZ"],
+                                      d_out["q_tok_prob"], T, W2T=W2T, lens=s_out["lens"],
+                                      seed=seed, offset=i, out=v2, workspace=ws_v)
+
+            emitted = torch.zeros((), dtype=torch.int64, device=dev)
+            lens_sum = torch.zeros((), dtype=torch.int64, device=dev)
+            for i in range(3):   # warm-up, including torch's first (lazily loaded) sums
+                dstep(i)
+                emitted += v2["accepted"].sum() + B
+                lens_sum += s_out["lens"].sum()
+            torch.cuda.synchronize()
+            emitted.zero_()
+            lens_sum.zero_()
+            torch.cuda.synchronize()
+            t0d = time.perf_counter()
+            for i in range(args.steps):
+                dstep(args.warmup + i)
+                emitted += v2["accepted"].sum() + B
+                lens_sum += s_out["lens"].sum()
+            torch.cuda.synchronize()
+            dt = (time.perf_counter() - t0d) / args.steps
+            result_extra["dspark_cycle"] = dict(
+                ms_per_step=round(dt * 1e3, 4), drafted=B * g,
+                mean_len=round(float(lens_sum.item()) / (B * args.steps), 3),
+                emitted_per_step=round(float(emitted.item()) / args.steps, 2),
+                emitted_per_s=round(float(emitted.item()) / args.steps / dt, 1),
+                sps_table="synthetic: flat to 4B tokens, then 1/B")
     # Tree drafts: the top 64 of 1024 candidate nodes per request by survival
     # probability, for every request of the batch (not part of the cycle).
     tw = workloads.make_trees(B, 1024, 1234)
