@@ -75,7 +75,9 @@ def load_library():
     lib.spec_confidence_head.argtypes = [vp, i32, i32, vp, vp, vp, i32, i32, vp, i32, i32, i32,
                                          vp, vp]
     lib.spec_confidence_head.restype = i32
-    lib.spec_prefix_schedule.argtypes = [vp, i32, i32, vp, i32, vp, vp, vp, vp]
+    lib.spec_prefix_schedule_workspace_size.argtypes = [i32, i32]
+    lib.spec_prefix_schedule_workspace_size.restype = sz
+    lib.spec_prefix_schedule.argtypes = [vp, i32, i32, vp, i32, vp, vp, vp, vp, sz, vp]
     lib.spec_prefix_schedule.restype = i32
     lib.spec_tree_select.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
     lib.spec_tree_select.restype = i32
@@ -376,7 +378,7 @@ def spec_confidence_head(h, x0, draft, W1, w, *, out=None, stream=None):
     return out
 
 
-def spec_prefix_schedule(c, sps, *, out=None, stream=None):
+def spec_prefix_schedule(c, sps, *, out=None, workspace=None, stream=None):
     """Acceptance lengths l [R] (int32) from confidences c float32 [R, gamma]
     and the steps-per-second table sps float64 [nsps] (index = batch size).
     Returns dict(lens, B, tau) of device tensors (B int32 [1], tau float64
@@ -393,8 +395,10 @@ def spec_prefix_schedule(c, sps, *, out=None, stream=None):
         out = dict(lens=torch.empty(R, dtype=torch.int32, device=c.device),
                    B=torch.empty(1, dtype=torch.int32, device=c.device),
                    tau=torch.empty(1, dtype=torch.float64, device=c.device))
+    ws, nws = _workspace(lib.spec_prefix_schedule_workspace_size(R, gamma), c.device, workspace)
     st = lib.spec_prefix_schedule(_ptr(c), R, gamma, _ptr(sps), sps.numel(), _ptr(out["lens"]),
-                                  _ptr(out.get("B")), _ptr(out.get("tau")), _stream(stream))
+                                  _ptr(out.get("B")), _ptr(out.get("tau")), _ptr(ws), nws,
+                                  _stream(stream))
     _check(st, "spec_prefix_schedule")
     return out
 

@@ -257,7 +257,10 @@ struct SchedArgs {
     int32_t* lens;              // [R] out
     int32_t* B_out;             // [1] out or null
     double* tau_out;            // [1] out or null
+    uint32_t* ws_val;           // [R * gamma] workspace: keys in sorted order
+    int32_t* ws_id;             // [R * gamma] workspace: their candidate ids
 };
+size_t prefix_schedule_ws_bytes(int R, int gamma);
 hipError_t prefix_schedule_launch(const SchedArgs& a, hipStream_t s);
 
 // Top-n nodes of R draft trees of M <= kTreeMax nodes each.

@@ -7,14 +7,16 @@
 //   c = sigmoid(w_h . h_k + w_e . W1[x_{k-1}]).  HBM-bound on h (d values per
 //   position); w is a few KB and stays in L2.
 //
-// prefix_schedule: one workgroup of 1024 threads for the whole batch.
+// prefix schedule: two launches.
 //   1. survival a_{r,j} = c_{r,0} * ... * c_{r,j}: one thread per request,
 //      float32 products left to right;
 //   2. one key per candidate, ~bits(a): for a in [0, 1] ascending keys mean
-//      descending a; a stable sort keeps candidates of equal a in id order
-//      r * gamma + j (lower request, then lower position).  Each request's
-//      keys already ascend, so the sort merges adjacent runs level by level
-//      in LDS;
+//      descending a, ties kept in id order r * gamma + j (lower request,
+//      then lower position).  Each request's keys already ascend, so a
+//      candidate's rank is its position in its own run plus binary-search
+//      counts in every other run; many workgroups rank slices of the
+//      candidates and scatter them, sorted, into the workspace;
+//   (then one workgroup of 1024 threads:)
 //   3. q_t = a_t cut to a multiple of 2^-48 as an integer; inclusive integer
 //      prefix sums S_t give tau_t = R + S_t 2^-48 exactly (no dependence on
 //      the order of the sums); Theta_t = tau_t * SPS(R + t) in double for every
@@ -150,85 +152,90 @@ __device__ __forceinline__ double sched_theta(int R, int64_t S, double sps_B) {
     return tau * sps_B;
 }
 
-// Stable ascending sort of the N 32-bit keys val (with their candidate ids
-// idx alongside), which arrive as ascending runs of length G (one per
-// request: survival falls along a request) in id order.  Pairs of adjacent
-// runs are merged level by level; every key finds its place in the merged run
-// from its own rank plus the number of keys of the other run before it (left
-// run: keys of the right run below it; right run: keys of the left run at or
-// below it, so equal keys keep id order).  That count is a branch-free binary
-// search with the same number of steps on every lane, the E keys of a thread
-// searched together.
-template <int E>
-__device__ __forceinline__ void merge_runs(uint32_t* val, int* idx, int N, int G, int tid) {
-    for (int s = G; s < N; s <<= 1) {
-        const int top = 1 << (31 - __builtin_clz(s));   // highest power of two <= s
-        uint32_t x[E];
-        int id[E], lo[E], n[E], cnt[E], own[E];
-        bool right[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const int i = tid * E + e;
-            x[e] = 0;
-            id[e] = 0;
-            lo[e] = 0;
-            n[e] = 0;
-            cnt[e] = 0;
-            own[e] = -1;
-            right[e] = false;
-            if (i < N) {
-                x[e] = val[i];
-                id[e] = idx[i];
-                const int p0 = (i / (2 * s)) * (2 * s);   // start of the pair
-                const int mid = min(p0 + s, N), end = min(p0 + 2 * s, N);
-                if (i < mid) {
-                    lo[e] = mid;
-                    n[e] = end - mid;
-                    own[e] = i;
-                } else {
-                    lo[e] = p0;
-                    n[e] = mid - p0;
-                    own[e] = p0 + (i - mid);
-                    right[e] = true;
-                }
-            }
+// Survival keys of every candidate in LDS: one thread per request forms the
+// float32 products left to right from the staged confidences (clamped into
+// [0, 1], NaN to 0, so that every request's keys ascend).
+__device__ __forceinline__ void survival_keys(const float* c, int R, int G, float* cl,
+                                              uint32_t* val, int tid, int nthreads) {
+    const int N = R * G;
+#pragma unroll 8
+    for (int i = tid; i < N; i += nthreads) cl[i] = fminf(fmaxf(c[i], 0.0f), 1.0f);
+    __syncthreads();
+    for (int r = tid; r < R; r += nthreads) {
+        float a = 1.0f;
+        for (int j = 0; j < G; ++j) {
+            a = a * cl[r * G + j];
+            const uint32_t bits = a > 0.0f ? __float_as_uint(a) : 0u;   // -0 keys as +0
+            val[r * G + j] = ~bits;
         }
-        for (int b = top; b > 0; b >>= 1) {
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const int probe = cnt[e] + b;
-                if (probe <= n[e]) {
-                    const uint32_t y = val[lo[e] + probe - 1];
-                    if (y < x[e] || (right[e] && y == x[e])) cnt[e] = probe;
-                }
-            }
+    }
+    __syncthreads();
+}
+
+// Keys of the ascending run val[lo, lo + n) below x (or at or below x when
+// le): a branch-free binary search, top = the highest power of two <= n.
+__device__ __forceinline__ int run_count(const uint32_t* val, int lo, int n, int top, uint32_t x,
+                                         bool le) {
+    int pos = 0;
+    for (int b = top; b > 0; b >>= 1) {
+        const int probe = pos + b;
+        if (probe <= n) {
+            const uint32_t y = val[lo + probe - 1];
+            if (y < x || (le && y == x)) pos = probe;
         }
-        __syncthreads();
+    }
+    return pos;
+}
+
+// 1-2. The rank of each candidate in the order (key ascending, then id): its
+// position j in its own request's run, plus, over the other requests, the
+// keys at or below its key (earlier requests) or below it (later ones).
+// The searches total R * gamma * R * log2(gamma) steps, so they are spread
+// wide: every workgroup forms all keys (cheap, and redundant by design), then
+// its 256 threads rank 16 candidates, 16 threads per candidate splitting the
+// requests.  The candidates land sorted in the workspace.
+constexpr int kRankThreads = 256;
+constexpr int kRankSplit = 16;
+constexpr int kRankPerWg = kRankThreads / kRankSplit;
+
+__global__ __launch_bounds__(kRankThreads)
+void schedule_rank_kernel(SchedArgs A) {
+    __shared__ uint32_t val[kSchedMax];
+    __shared__ float cl[kSchedMax];
+    const int tid = threadIdx.x;
+    const int R = A.R, G = A.gamma, N = R * G;
+    survival_keys(A.c, R, G, cl, val, tid, kRankThreads);
+    const int cand = blockIdx.x * kRankPerWg + tid / kRankSplit, sub = tid % kRankSplit;
+    int cnt = 0;
+    uint32_t x = 0;
+    if (cand < N) {
+        x = val[cand];
+        const int rc = cand / G;
+        const int top = 1 << (31 - __builtin_clz(G));
+#pragma unroll 2
+        for (int r = sub; r < R; r += kRankSplit)
+            if (r != rc) cnt += run_count(val, r * G, G, top, x, r < rc);
+        if (sub == 0) cnt += cand - rc * G;   // j: the earlier positions of its own request
+    }
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            if (own[e] >= 0) {
-                val[own[e] + cnt[e]] = x[e];
-                idx[own[e] + cnt[e]] = id[e];
-            }
-        }
-        __syncthreads();
+    for (int off = 1; off < kRankSplit; off <<= 1) cnt += __shfl_xor(cnt, off);
+    if (cand < N && sub == 0) {
+        A.ws_val[cnt] = x;
+        A.ws_id[cnt] = cand;
     }
 }
 
+// 3-4. One workgroup over the sorted candidates: thread t owns sorted
+// positions t E .. t E + E - 1.
 template <int E>
 __global__ __launch_bounds__(kSchedThreads)
-void prefix_schedule_kernel(SchedArgs A) {
-    __shared__ uint32_t val[kSchedMax];     // sort keys ~bits(a), sorted in place; later the counts
-    __shared__ int idx[kSchedMax];          // candidate id r * gamma + j of each key
-    __shared__ float cl[kSchedMax];         // the confidences, staged
+void schedule_scan_kernel(SchedArgs A) {
+    __shared__ int cnt_r[kSchedMax];        // per-request admitted counts
     __shared__ int64_t wave_tot[kSchedThreads / kWave];
     __shared__ int stop_t;
     __shared__ int64_t S_stop;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int R = A.R, G = A.gamma, N = R * G;
-
-    // the SPS entries this thread's sorted range will need, fetched now so
-    // their latency hides behind the sort
     const int base = tid * E;
     double sp[E + 1];
 #pragma unroll
@@ -236,31 +243,15 @@ void prefix_schedule_kernel(SchedArgs A) {
         const int Bt = R + base + e;
         sp[e] = (base + e <= N && Bt < A.nsps) ? A.sps[Bt] : 0.0;
     }
-
-    // 1-2. survival products (staged through LDS so each request's chain
-    //      reads LDS, not HBM) and keys.  Values outside [0, 1] are clamped
-    //      (NaN to 0) so that every request's run stays sorted.
-    for (int i = tid; i < N; i += kSchedThreads) cl[i] = fminf(fmaxf(A.c[i], 0.0f), 1.0f);
-    if (tid == 0) stop_t = INT_MAX;
-    __syncthreads();
-    for (int r = tid; r < R; r += kSchedThreads) {
-        float a = 1.0f;
-        for (int j = 0; j < G; ++j) {
-            a = a * cl[r * G + j];
-            const uint32_t bits = a > 0.0f ? __float_as_uint(a) : 0u;   // -0 keys as +0
-            val[r * G + j] = ~bits;
-            idx[r * G + j] = r * G + j;
-        }
-    }
-    __syncthreads();
-    merge_runs<E>(val, idx, N, G, tid);
     uint32_t kv[E];
     int kid[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-        kv[e] = base + e < N ? val[base + e] : ~0u;
-        kid[e] = base + e < N ? idx[base + e] : 0;
+        kv[e] = base + e < N ? A.ws_val[base + e] : ~0u;
+        kid[e] = base + e < N ? A.ws_id[base + e] : 0;
     }
+    for (int r = tid; r < R; r += kSchedThreads) cnt_r[r] = 0;
+    if (tid == 0) stop_t = INT_MAX;
 
     // 3. integer prefix sums of the cut survival values over the sorted order
     int64_t q[E];
@@ -320,28 +311,33 @@ void prefix_schedule_kernel(SchedArgs A) {
             }
         }
     }
-    // 4. per-request counts of the admitted candidates (key buffer reused)
-    int* cnt = reinterpret_cast<int*>(val);
-    for (int r = tid; r < R; r += kSchedThreads) cnt[r] = 0;
-    __syncthreads();
+    // 4. per-request counts of the admitted candidates
 #pragma unroll
     for (int e = 0; e < E; ++e)
-        if (base + e < admitted) atomicAdd(&cnt[min(kid[e] / G, R - 1)], 1);
+        if (base + e < admitted) atomicAdd(&cnt_r[min(kid[e] / G, R - 1)], 1);
     __syncthreads();
-    for (int r = tid; r < R; r += kSchedThreads) A.lens[r] = cnt[r];
+    for (int r = tid; r < R; r += kSchedThreads) A.lens[r] = cnt_r[r];
     if (tid == 0) {
         if (A.B_out) A.B_out[0] = R + admitted;
         if (A.tau_out) A.tau_out[0] = (double)((int64_t)R * (int64_t)kTwo48 + S_stop) / kTwo48;
     }
 }
 
+size_t prefix_schedule_ws_bytes(int R, int gamma) {
+    const size_t n = (size_t)R * gamma;
+    return 2 * ((n * 4 + 255) / 256 * 256);
+}
+
 hipError_t prefix_schedule_launch(const SchedArgs& a, hipStream_t s) {
     const int N = a.R * a.gamma;
+    if (N > 0)
+        hipLaunchKernelGGL(schedule_rank_kernel, dim3((N + kRankPerWg - 1) / kRankPerWg),
+                           dim3(kRankThreads), 0, s, a);
     const dim3 g(1), b(kSchedThreads);
-    if (N <= kSchedThreads) hipLaunchKernelGGL(prefix_schedule_kernel<1>, g, b, 0, s, a);
-    else if (N <= 2 * kSchedThreads) hipLaunchKernelGGL(prefix_schedule_kernel<2>, g, b, 0, s, a);
-    else if (N <= 4 * kSchedThreads) hipLaunchKernelGGL(prefix_schedule_kernel<4>, g, b, 0, s, a);
-    else hipLaunchKernelGGL(prefix_schedule_kernel<8>, g, b, 0, s, a);
+    if (N <= kSchedThreads) hipLaunchKernelGGL(schedule_scan_kernel<1>, g, b, 0, s, a);
+    else if (N <= 2 * kSchedThreads) hipLaunchKernelGGL(schedule_scan_kernel<2>, g, b, 0, s, a);
+    else if (N <= 4 * kSchedThreads) hipLaunchKernelGGL(schedule_scan_kernel<4>, g, b, 0, s, a);
+    else hipLaunchKernelGGL(schedule_scan_kernel<8>, g, b, 0, s, a);
     return hipGetLastError();
 }
 

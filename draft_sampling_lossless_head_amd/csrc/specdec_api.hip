@@ -463,15 +463,26 @@ spec_status_t spec_confidence_head(const void* h, int h_dtype, int d, const int3
     return e == hipSuccess ? SPEC_OK : hip_fail(e, "confidence_head");
 }
 
+size_t spec_prefix_schedule_workspace_size(int R, int gamma) {
+    if (R < 0 || gamma < 0 || (int64_t)R * gamma > kSchedMax) return 0;
+    return prefix_schedule_ws_bytes(R, gamma);
+}
+
 spec_status_t spec_prefix_schedule(const float* c, int R, int gamma, const double* sps, int nsps,
-                                   int32_t* lens, int32_t* B_out, double* tau_out, void* stream) {
+                                   int32_t* lens, int32_t* B_out, double* tau_out, void* ws,
+                                   size_t ws_bytes, void* stream) {
     g_err.clear();
     if (R < 0 || gamma < 0 || nsps < 0) return fail(SPEC_ERR_INVALID, "R, gamma and nsps must be >= 0");
     if (nsps > 0 && !sps) return fail(SPEC_ERR_INVALID, "null sps with nsps > 0");
     if ((int64_t)R * gamma > kSchedMax || R > kSchedMax)
         return fail(SPEC_ERR_UNSUPPORTED, "R and R * gamma must be <= 8192");
     if (R > 0 && (!lens || (gamma > 0 && !c))) return fail(SPEC_ERR_INVALID, "null c or lens");
+    const size_t need = prefix_schedule_ws_bytes(R, gamma);
+    if ((int64_t)R * gamma > 0 && (!ws || ws_bytes < need || !aligned16(ws)))
+        return fail(SPEC_ERR_WORKSPACE, "workspace missing, unaligned or smaller than spec_prefix_schedule_workspace_size");
     SchedArgs a{};
+    a.ws_val = static_cast<uint32_t*>(ws);
+    a.ws_id = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + need / 2);
     a.c = c;
     a.R = R;
     a.gamma = gamma;

@@ -355,14 +355,20 @@ spec_status_t spec_confidence_head(const void *h, int h_dtype, int d, const int3
  * lens    [R]         out: int32 l_r
  * B_out   [1]         out (optional): int32 chosen batch size R + sum l_r
  * tau_out [1]         out (optional): double tau at that size
- * One workgroup; all pointers device memory, stream-ordered.
+ * ws      [ws_bytes]  caller workspace, 16-byte aligned, at least
+ *                     spec_prefix_schedule_workspace_size(R, gamma) bytes (the
+ *                     candidates in sorted order); unused when R * gamma == 0
+ * Two launches: workgroups that rank slices of the candidates, then one
+ * workgroup that scans them.  All pointers device memory, stream-ordered.
  * Errors: SPEC_ERR_INVALID for null c or lens (R > 0), R, gamma, nsps < 0,
  * null sps with nsps > 0; SPEC_ERR_UNSUPPORTED for R > 8192 or
- * R * gamma > 8192.
+ * R * gamma > 8192; SPEC_ERR_WORKSPACE for a missing, unaligned or short
+ * workspace.
  */
+size_t spec_prefix_schedule_workspace_size(int R, int gamma);
 spec_status_t spec_prefix_schedule(const float *c, int R, int gamma, const double *sps,
                                    int nsps, int32_t *lens, int32_t *B_out, double *tau_out,
-                                   void *stream);
+                                   void *ws, size_t ws_bytes, void *stream);
 
 /*
  * ---------------------------------------------------------------------------

@@ -37,7 +37,7 @@ def test_header_declares_the_boundary():
               "spec_version", "spec_pack_w2", "spec_pack_w2_bytes", "spec_verify_markov",
               "spec_verify_markov_workspace_size", "spec_draft_set_persistent",
               "spec_draft_set_poll_limit", "spec_acceptance_rate", "spec_confidence_head",
-              "spec_prefix_schedule", "spec_tree_select"):
+              "spec_prefix_schedule", "spec_prefix_schedule_workspace_size", "spec_tree_select"):
         assert n in names
 
 
@@ -238,12 +238,19 @@ def test_prefix_schedule_validation(lib):
     """Argument checks of spec_prefix_schedule happen before any launch."""
     fake = ctypes.c_void_p(4096)
     f = lib.spec_prefix_schedule
-    vp, i = ctypes.c_void_p, ctypes.c_int
-    f.argtypes = [vp, i, i, vp, i, vp, vp, vp, vp]
+    vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    f.argtypes = [vp, i, i, vp, i, vp, vp, vp, vp, sz, vp]
     f.restype = i
+    lib.spec_prefix_schedule_workspace_size.argtypes = [i, i]
+    lib.spec_prefix_schedule_workspace_size.restype = sz
+    need = lib.spec_prefix_schedule_workspace_size(4, 3)
+    assert need > 0 and lib.spec_prefix_schedule_workspace_size(0, 3) == 0
 
-    def call(c=fake, R=4, G=3, sps=fake, nsps=10, lens=fake):
-        return f(c, R, G, sps, nsps, lens, None, None, None)
+    def call(c=fake, R=4, G=3, sps=fake, nsps=10, lens=fake, ws=fake, nws=None):
+        return f(c, R, G, sps, nsps, lens, None, None, ws, need if nws is None else nws, None)
+    assert call(ws=None) == SPEC_ERR_WORKSPACE
+    assert call(nws=need - 1) == SPEC_ERR_WORKSPACE
+    assert call(ws=ctypes.c_void_p(4100)) == SPEC_ERR_WORKSPACE   # unaligned
     assert call(c=None) == SPEC_ERR_INVALID
     assert call(lens=None) == SPEC_ERR_INVALID
     assert call(sps=None) == SPEC_ERR_INVALID
