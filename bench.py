@@ -224,7 +224,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="markov-152k-b128")
     ap.add_argument("--path", choices=("qfree", "materialized"), default="qfree",
                     help="q-free cycle (no draft-logit tensor) or materialized draft logits")
