@@ -259,7 +259,7 @@ def main():
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): the method's requests are "
               "independent, so several GPUs would each run this same step on their own share of "
-              "the batch with no exchange; multi-GPU runs are not part of this build.",
+              "the batch with no exchange; this benchmark does not launch several GPUs.",
               file=sys.stderr)
         sys.exit(2)
 
