@@ -24,9 +24,13 @@ PINS = {
     "argmax": "lowest index on ties vs numpy.argmax; top-2 gap brute force",
     "draft_markov": "bias equals W1[x]@W2 (numpy); W2=0 reduces to i.i.d. softmax(U) draws",
     "draft_rnn": "gate limits (sigmoid->1 keeps s=0; ->0 gives s=tanh(Wc z)); Wo=0 gives no bias; hand-derived r=1 case",
-    "verify": "exact output law by brute-force enumeration equals p (lossless theorem); "
-              "acceptance frequency equals sum min(p,q); E[tau] closed form; T=0 top-1 match",
-    "alpha_tv": "sum min(p,q) == 1 - D_TV identity; MC acceptance frequency",
+    "verify": "exact output law by brute-force enumeration equals softmax(P/T) at T in "
+              "{0.5, 0.7, 1, 1.3, 2} (lossless theorem); normalisers equal scipy logsumexp(row/T); "
+              "min(1, p/q) equals numpy's ratio at T; acceptance frequency equals sum min(p,q); "
+              "E[tau] closed form; T=0 top-1 match",
+    "residual_weights": "equal numpy max(0, softmax(lp/T) - softmax(lq/T)) at T != 1; mass = D_TV",
+    "alpha_tv": "sum min(p,q) == 1 - D_TV identity; equals numpy's sums at T != 1; MC acceptance "
+                "frequency",
     "confidence": "w=0 gives 1/2; one-hot weights on either block give scipy expit of that "
                   "input; c(-w) = 1 - c(w); logits add over disjoint weight supports",
     "prefix_schedule": "brute force over every length assignment on tiny cases with unimodal "
