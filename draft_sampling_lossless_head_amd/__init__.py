@@ -17,6 +17,7 @@ from .api import (  # noqa: F401
     spec_draft_sample_rnn,
     spec_draft_set_persistent,
     spec_draft_set_poll_limit,
+    spec_draft_status,
     spec_pack_w2,
     spec_pack_w2_bytes,
     spec_philox_uniforms,

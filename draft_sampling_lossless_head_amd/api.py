@@ -4,7 +4,9 @@ Argument marshalling only: shape checks, output/workspace allocation when the
 caller does not pass them, and the current torch stream.  Every step of the
 method runs in the library's HIP kernels.
 """
+import contextlib
 import ctypes
+import functools
 import os
 
 import torch
@@ -81,6 +83,8 @@ def load_library():
     lib.spec_prefix_schedule.restype = i32
     lib.spec_tree_select.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
     lib.spec_tree_select.restype = i32
+    lib.spec_draft_status.argtypes = [vp, sz, i32, i32, i32, i32, vp, vp]
+    lib.spec_draft_status.restype = i32
     lib.spec_draft_set_poll_limit.argtypes = [u32]
     lib.spec_draft_set_poll_limit.restype = u32
     lib.spec_profile_enable.argtypes = [ctypes.c_char_p]
@@ -118,6 +122,20 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on_stream(fn):
+    """Run a wrapper with its `stream` as torch's current stream, so that the
+    outputs and the workspace it allocates belong to the stream the library
+    enqueues on: torch's caching allocator then hands their memory to a later
+    allocation only in that stream's order (a workspace freed when the wrapper
+    returns is not reused by another stream while the kernels still run)."""
+    @functools.wraps(fn)
+    def wrapped(*args, stream=None, **kw):
+        ctx = contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+        with ctx:
+            return fn(*args, stream=stream, **kw)
+    return wrapped
+
+
 def _check(st, what):
     if st != 0:
         msg = load_library().spec_last_error().decode()
@@ -149,6 +167,7 @@ def _workspace(nbytes, device, ws):
     return ws, ws.numel()
 
 
+@_on_stream
 def spec_philox_uniforms(seed, offset, stream_id, B, K, device="cuda", out=None, stream=None):
     """[B, K] float32 uniforms u(seed, offset, b, k, stream_id)."""
     lib = load_library()
@@ -173,6 +192,7 @@ def spec_pack_w2_bytes(r, V):
     return load_library().spec_pack_w2_bytes(r, V)
 
 
+@_on_stream
 def spec_pack_w2(W2, out=None, stream=None):
     """W2 [r, V] bf16 -> packed image (uint8 [spec_pack_w2_bytes(r, V)]);
     pack once per model load and pass as W2T=."""
@@ -196,11 +216,15 @@ def _check_w2t(W2T, r, V):
         raise SpecError("W2T must be a packed image from spec_pack_w2 (too small)")
 
 
+@_on_stream
 def spec_draft_sample_markov(U, x0, W1, W2, T=1.0, *, W2T=None, q_free=False, uniforms=None,
-                             seed=0, offset=0, out=None, workspace=None, stream=None):
+                             seed=0, offset=0, out=None, workspace=None, status=None,
+                             stream=None):
     """Markov-head draft.  U [B, gamma, V], x0 [B] int32, W1 [V, r], W2 [r, V]
     (or None with W2T, the packed image from spec_pack_w2).  q_free=True writes no q
-    logits (verify with spec_verify_markov)."""
+    logits (verify with spec_verify_markov).  status: optional int32 [1] device
+    tensor that receives spec_draft_status right after the draft (0: every draw
+    happened; 1: the persistent engine's waits gave up)."""
     lib = load_library()
     for t, n in ((U, "U"), (x0, "x0"), (W1, "W1")):
         _dev(t, n)
@@ -226,9 +250,31 @@ def spec_draft_sample_markov(U, x0, W1, W2, T=1.0, *, W2T=None, q_free=False, un
         _ptr(o["tokens"]), _ptr(o.get("q_logits")), _ptr(o.get("q_logZ")),
         _ptr(o.get("q_tok_prob")), _ptr(ws), nws, _stream(stream))
     _check(st, "spec_draft_sample_markov")
+    if status is not None:
+        _draft_status(ws, nws, B, gamma, V, r, status, stream)
     return o
 
 
+def _draft_status(ws, nws, B, gamma, V, r, status, stream):
+    _dev(status, "status")
+    if status.dtype != torch.int32 or status.numel() < 1:
+        raise SpecError("status must be an int32 device tensor with one element")
+    _check(load_library().spec_draft_status(_ptr(ws), nws, B, gamma, V, r, _ptr(status),
+                                            _stream(stream)), "spec_draft_status")
+
+
+@_on_stream
+def spec_draft_status(workspace, B, gamma, V, r, *, out=None, stream=None):
+    """Completion word of the last draft made with `workspace` (a uint8 device
+    tensor passed as workspace= to that draft): int32 [1], 0 when every draw
+    happened, 1 when the persistent engine's waits gave up."""
+    if out is None:
+        out = torch.empty(1, dtype=torch.int32, device=workspace.device)
+    _draft_status(workspace, workspace.numel(), B, gamma, V, r, out, stream)
+    return out
+
+
+@_on_stream
 def spec_draft_sample_rnn(U, x0, h, W1, W2, Wg, Wc, Wo, T=1.0, *, W2T=None, uniforms=None,
                           seed=0, offset=0, out=None, workspace=None, stream=None):
     """RNN-head draft.  h [B, gamma, d]; Wg, Wc, Wo [r, 2r + d]."""
@@ -256,6 +302,7 @@ def spec_draft_sample_rnn(U, x0, h, W1, W2, Wg, Wc, Wo, T=1.0, *, W2T=None, unif
     return o
 
 
+@_on_stream
 def spec_verify(P, Q, draft, T=1.0, *, gamma_max=None, lens=None, p_row_off=None, q_row_off=None,
                 uniforms=None, seed=0, offset=0, diagnostics=True, out=None, workspace=None,
                 stream=None):
@@ -307,6 +354,7 @@ def spec_verify(P, Q, draft, T=1.0, *, gamma_max=None, lens=None, p_row_off=None
     return out
 
 
+@_on_stream
 def spec_acceptance_rate(P, Q, T=1.0, *, gamma_max=None, lens=None, p_row_off=None,
                          q_row_off=None, want_tv=True, out=None, stream=None):
     """Acceptance rate alpha[b, k] = sum min(p_k, q_k) (and the total variation
@@ -352,6 +400,7 @@ def spec_acceptance_rate(P, Q, T=1.0, *, gamma_max=None, lens=None, p_row_off=No
     return out
 
 
+@_on_stream
 def spec_confidence_head(h, x0, draft, W1, w, *, out=None, stream=None):
     """Confidence c[b, k] = sigmoid(w[:d] . h[b, k] + w[d:] . W1[prev]) of every
     drafted position (prev = x0[b] at k = 0, else draft[b, k-1]).  h [R, gamma,
@@ -378,6 +427,7 @@ def spec_confidence_head(h, x0, draft, W1, w, *, out=None, stream=None):
     return out
 
 
+@_on_stream
 def spec_prefix_schedule(c, sps, *, out=None, workspace=None, stream=None):
     """Acceptance lengths l [R] (int32) from confidences c float32 [R, gamma]
     and the steps-per-second table sps float64 [nsps] (index = batch size).
@@ -403,6 +453,7 @@ def spec_prefix_schedule(c, sps, *, out=None, workspace=None, stream=None):
     return out
 
 
+@_on_stream
 def spec_tree_select(parent, c, n, *, out=None, stream=None):
     """Top-n nodes of R draft trees by survival probability.  parent int32
     [R, M] (parents first, -1: child of the root), c float32 [R, M].  Returns
@@ -457,6 +508,7 @@ def spec_profile_read():
     return n.value, ms.value
 
 
+@_on_stream
 def spec_verify_markov(P, U, x0, W1, W2, draft, q_logZ, q_tok_prob, T=1.0, *, W2T=None,
                        gamma_max=None, lens=None, p_row_off=None, uniforms=None, seed=0,
                        offset=0, diagnostics=True, out=None, workspace=None, stream=None):

@@ -17,6 +17,8 @@
 // positions at once, bf16 MFMA) and rnn_gates (per position: the s_{k-1} and
 // W1[x_{k-1}] parts, the gated state update and o = tanh(W_o z_k)).
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 #include <climits>
 
 #include "device_common.hpp"
@@ -1422,33 +1424,34 @@ int draft_num_segments(const DraftArgs& a) {
 int draft_max_segments(int V) { return (V + kStreamItem - 1) / kStreamItem; }
 
 static int cu_count() {
-    static int n[64] = {0};
+    // per-device cache; concurrent first calls store the same value
+    static std::atomic<int> n[64];
     int dev = 0;
     (void)hipGetDevice(&dev);
     if (dev < 0 || dev >= 64) dev = 0;
-    if (!n[dev]) {
-        int c = 0;
+    int c = n[dev].load(std::memory_order_relaxed);
+    if (!c) {
         if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             c <= 0)
             c = 256;
-        n[dev] = c;
+        n[dev].store(c, std::memory_order_relaxed);
     }
-    return n[dev];
+    return c;
 }
 
 template <int NKS>
 static hipError_t launch_stream(const TileParams& p, hipStream_t s) {
     constexpr int STAGE = kStreamItem * NKS * 16 * 2 + kStreamRows * kStreamItem * 2;
     const size_t lds = (size_t)kStreamStages * STAGE;
-    static bool attr_set = false;
-    if (!attr_set) {
+    // raise the dynamic LDS limit once per process (thread-safe)
+    static std::once_flag attr_once;
+    std::call_once(attr_once, [&] {
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&draft_tile_stream<NKS, false>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&draft_tile_stream<NKS, true>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         (void)hipGetLastError();
-        attr_set = true;
-    }
+    });
     const int nitem_v = (p.V + kStreamItem - 1) / kStreamItem;
     const int nrb = (p.B + kStreamRows - 1) / kStreamRows;
     const int ws = stream_shares(p.B, p.V);
@@ -1469,15 +1472,15 @@ static hipError_t launch_tile(const TileParams& p, bool u_bf16, hipStream_t s) {
     const size_t lds = std::max((size_t)kTileV * (p.r + kLdsPad) * sizeof(uint16_t),
                                 (size_t)32 * WB * kOutLd * sizeof(float));
     // r = 256 needs 66 KB of LDS per workgroup (gfx950 has 160 KB per CU)
-    static bool attr_set = false;
-    if (!attr_set) {
+    // raise the dynamic LDS limit once per process (thread-safe)
+    static std::once_flag attr_once;
+    std::call_once(attr_once, [&] {
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&draft_tile_mfma<WB, MODE, true, OUT>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&draft_tile_mfma<WB, MODE, false, OUT>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         (void)hipGetLastError();
-        attr_set = true;
-    }
+    });
     if (u_bf16)
         hipLaunchKernelGGL((draft_tile_mfma<WB, MODE, true, OUT>), grid, dim3(256), lds, s, p);
     else
@@ -1490,15 +1493,15 @@ static hipError_t launch_stats(const TileParams& p, bool u_bf16, hipStream_t s) 
     constexpr int RT = 32 * WB;
     dim3 grid((p.V + kTileV - 1) / kTileV, (p.B + RT - 1) / RT);
     const size_t lds = (size_t)256 * p.r;   // the packed W2 tile
-    static bool attr_set = false;
-    if (!attr_set) {
+    // raise the dynamic LDS limit once per process (thread-safe)
+    static std::once_flag attr_once;
+    std::call_once(attr_once, [&] {
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&draft_tile_stats<WB, true>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&draft_tile_stats<WB, false>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
         (void)hipGetLastError();
-        attr_set = true;
-    }
+    });
     if (u_bf16)
         hipLaunchKernelGGL((draft_tile_stats<WB, true>), grid, dim3(256), lds, s, p);
     else

@@ -41,6 +41,8 @@
 // complete within the poll limit the workgroup sets an abort word and every
 // other workgroup leaves at its next poll, so the launch always ends.
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 #include <climits>
 
 #include "device_common.hpp"
@@ -585,39 +587,43 @@ static int persist_nb(int r) {
     }
 }
 
-// 0: per-position kernels; 1: persistent, plain launch; 2: persistent,
+// The two process-wide settings of the persistent draft (spec_draft_set_persistent,
+// spec_draft_set_poll_limit).  Atomic: a call reads each once, when it
+// launches, so a change made by another thread applies from the next call on.
+// Engine: 0 per-position kernels; 1 persistent, plain launch; 2 persistent,
 // cooperative launch.
-static int g_persist_mode = 1;
-
-static unsigned g_poll_limit = kBarrierPolls;
+static std::atomic<int> g_persist_mode{1};
+static std::atomic<unsigned> g_poll_limit{kBarrierPolls};
 
 unsigned persist_set_poll_limit(unsigned polls) {
-    const unsigned was = g_poll_limit;
-    g_poll_limit = polls == 0 ? kBarrierPolls : polls;
-    return was;
+    return g_poll_limit.exchange(polls == 0 ? kBarrierPolls : polls);
 }
 
 int persist_set_mode(int mode) {
     if (mode < 0 || mode > 2) return -1;
-    const int was = g_persist_mode;
-    g_persist_mode = mode;
-    return was;
+    return g_persist_mode.exchange(mode);
 }
 
+int persist_mode() { return g_persist_mode.load(); }
+
 static int persist_device_ok() {
-    static int ok[64] = {0};   // 0 unknown, 1 yes, -1 no
+    // per-device cache: CUs if the device can run the persistent draft, -1 if
+    // not, 0 unknown; concurrent first calls store the same value
+    static std::atomic<int> ok[64];
     int dev = 0;
     (void)hipGetDevice(&dev);
     if (dev < 0 || dev >= 64) return 0;
-    if (!ok[dev]) {
+    int v = ok[dev].load(std::memory_order_relaxed);
+    if (!v) {
         int coop = 0, cus = 0;
         if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess)
             coop = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             cus = 0;
-        ok[dev] = coop && cus > 0 ? cus : -1;
+        v = coop && cus > 0 ? cus : -1;
+        ok[dev].store(v, std::memory_order_relaxed);
     }
-    return ok[dev] > 0 ? ok[dev] : 0;
+    return v > 0 ? v : 0;
 }
 
 // Workgroups of the persistent draft, one per CU: kPersistFinWgs finalize
@@ -634,8 +640,8 @@ static int persist_grid(int V, int* nu_out) {
     return nu + nf;
 }
 
-bool draft_persists(const DraftArgs& a) {
-    if (g_persist_mode == 0) return false;
+bool draft_persists(const DraftArgs& a, int mode) {
+    if (mode == 0) return false;
     if (!(a.head == kHeadMarkov && a.w_bf16 && a.u_bf16 && !a.q_logits && (a.V % 8) == 0 &&
           persist_nks(a.r) != 0 && a.B > 0 && a.gamma > 0))
         return false;
@@ -646,20 +652,21 @@ bool draft_persists(const DraftArgs& a) {
 }
 
 template <int NKS>
-static hipError_t launch_persist(const PersistArgs& p, int ng, bool greedy, hipStream_t s) {
+static hipError_t launch_persist(const PersistArgs& p, int ng, bool greedy, bool coop,
+                                 hipStream_t s) {
     constexpr int NB = PersistShape<NKS>::NB, NR = PersistShape<NKS>::NR;
     const void* fn = greedy ? reinterpret_cast<const void*>(&draft_persist<NKS, NB, NR, true>)
                             : reinterpret_cast<const void*>(&draft_persist<NKS, NB, NR, false>);
     const size_t lds = persist_lds<NKS>();
-    static bool attr_set = false;
-    if (!attr_set) {
+    // raise the dynamic LDS limit once per process (thread-safe)
+    static std::once_flag attr_once;
+    std::call_once(attr_once, [&] {
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&draft_persist<NKS, NB, NR, true>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&draft_persist<NKS, NB, NR, false>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         (void)hipGetLastError();
-        attr_set = true;
-    }
+    });
     PersistArgs arg = p;
     void* args[] = {&arg};
     // Every workgroup must be resident at once (one per CU, grid <= CUs).  A
@@ -667,13 +674,19 @@ static hipError_t launch_persist(const PersistArgs& p, int ng, bool greedy, hipS
     // costs ~10 us of idle device on each side of the launch; a plain launch
     // gets it whenever no other kernel holds CUs meanwhile, and otherwise the
     // bounded waits give up (abort word set, tokens left at -1).
-    if (g_persist_mode == 2)
+    if (coop)
         return hipLaunchCooperativeKernel(fn, dim3(ng), dim3(kPersistWaves * 64), args,
                                           (unsigned)lds, s);
     return hipLaunchKernel(fn, dim3(ng), dim3(kPersistWaves * 64), args, (unsigned)lds, s);
 }
 
-hipError_t draft_persist_launch(const DraftArgs& a, unsigned* bar, hipStream_t s) {
+hipError_t persist_clear_abort(unsigned* bar, hipStream_t s) {
+    hipLaunchKernelGGL(persist_bar_reset, dim3(1), dim3(64), 0, s, bar, nullptr, 0, nullptr,
+                       (size_t)0, nullptr, (size_t)0);
+    return hipGetLastError();
+}
+
+hipError_t draft_persist_launch(const DraftArgs& a, unsigned* bar, int mode, hipStream_t s) {
     int nu = 0;
     const int ng = persist_grid(a.V, &nu);
     if (ng <= 0 || !bar || !a.tflag || !a.W2T) return hipErrorInvalidValue;
@@ -705,7 +718,7 @@ hipError_t draft_persist_launch(const DraftArgs& a, unsigned* bar, hipStream_t s
     f.r = a.r;
     f.tflag = a.tflag;
     f.abort_word = bar + kBarAbort;
-    f.poll_limit = g_poll_limit;
+    f.poll_limit = g_poll_limit.load();
     p.segm = reinterpret_cast<float*>(a.stats);
     p.gsums = a.gsums;
     p.sup = a.sup;
@@ -725,9 +738,9 @@ hipError_t draft_persist_launch(const DraftArgs& a, unsigned* bar, hipStream_t s
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     switch (persist_nks(a.r)) {
-    case 16: return launch_persist<16>(p, ng, a.greedy != 0, s);
-    case 8: return launch_persist<8>(p, ng, a.greedy != 0, s);
-    case 4: return launch_persist<4>(p, ng, a.greedy != 0, s);
+    case 16: return launch_persist<16>(p, ng, a.greedy != 0, mode == 2, s);
+    case 8: return launch_persist<8>(p, ng, a.greedy != 0, mode == 2, s);
+    case 4: return launch_persist<4>(p, ng, a.greedy != 0, mode == 2, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -119,16 +119,24 @@ int draft_segment_len(const DraftArgs& a);
 int draft_max_segments(int V);
 hipError_t draft_tile_launch(const DraftArgs& a, int k, hipStream_t s);
 hipError_t draft_finalize_launch(const DraftArgs& a, int k, hipStream_t s);
-// Persistent q-free Markov draft: all positions in one cooperative launch.
-constexpr size_t kPersistBarBytes = 2048;   // abort word, -inf chunk, 256 arrival flags
-bool draft_persists(const DraftArgs& a);
-hipError_t draft_persist_launch(const DraftArgs& a, unsigned* bar, hipStream_t s);
+constexpr size_t kPersistBarBytes = 2048;   // abort word and the -inf chunk (room to spare)
+// Persistent q-free Markov draft.  mode: the engine setting read once per call
+// (0 per-position, 1 persistent with a plain launch, 2 persistent with a
+// cooperative launch).
+bool draft_persists(const DraftArgs& a, int mode);
+hipError_t draft_persist_launch(const DraftArgs& a, unsigned* bar, int mode, hipStream_t s);
+// Clears the persistent draft's abort word (a call that runs another engine
+// leaves it at 0, so spec_draft_status reads "complete").
+hipError_t persist_clear_abort(unsigned* bar, hipStream_t s);
 int persist_set_mode(int mode);
-unsigned persist_set_poll_limit(unsigned polls);   // 0: the default   // 0 per-position, 1 persistent, 2 persistent (cooperative launch)
+int persist_mode();
+unsigned persist_set_poll_limit(unsigned polls);   // 0: the default
 // W2 [r, V] bf16 -> packed image of w2p_bytes(r, V) bytes.
 hipError_t w2_pack_launch(const uint16_t* W2, uint16_t* W2P, int r, int V, hipStream_t s);
-// Recompute the logits of row b at position row_pos[b] (bit-identical to the
-// draft's tile kernel) into out [B, V].
+// Recompute the logits of row b at position row_pos[b] into out [B, V] with the
+// materialised draft's tile kernel (draft_tile_mfma in residual mode).  They
+// equal the logits a q-free draft engine sampled from to fp32 rounding (the
+// engines sum the contraction in other orders).
 hipError_t residual_rows_launch(const TileParams& p, bool u_bf16, hipStream_t s);
 hipError_t rnn_hidden_proj_launch(const DraftArgs& a, hipStream_t s);
 hipError_t rnn_gates_launch(const DraftArgs& a, int k, hipStream_t s);

@@ -13,6 +13,7 @@
 //                          8 rebuilt weights.  A residual without mass after
 //                          rounding falls back to p_n (exact two-pass scan).
 #include <algorithm>
+#include <mutex>
 #include <climits>
 
 #include "device_common.hpp"
@@ -408,13 +409,13 @@ bool resid_streams(int B, int V, int r) {
 template <int NKS>
 static void launch_resid_stream(const ResidArgs& A, int nitem_v, int nrb, int ws, hipStream_t s) {
     constexpr int STAGE = kStreamItem * NKS * 16 * 2 + 2 * kStreamRows * kStreamItem * 2;
-    static bool attr_set = false;
-    if (!attr_set) {
+    // raise the dynamic LDS limit once per process (thread-safe)
+    static std::once_flag attr_once;
+    std::call_once(attr_once, [&] {
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&verify_resid_stream<NKS>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         (void)hipGetLastError();
-        attr_set = true;
-    }
+    });
     hipLaunchKernelGGL((verify_resid_stream<NKS>), dim3(nrb * ws), dim3(kStreamWaves * 64),
                        (size_t)kResidStages * STAGE, s, A, nitem_v, nrb, ws);
 }

@@ -171,12 +171,17 @@ spec_status_t run_draft(DraftArgs& a, void* stream) {
         prof_end(t, s);
         if (e != hipSuccess) return hip_fail(e, "rnn_hidden_proj");
     }
-    if (draft_persists(a)) {
+    const int mode = persist_mode();
+    if (draft_persists(a, mode)) {
         t = prof_begin("draft_persist", s);
-        e = draft_persist_launch(a, a.bar, s);
+        e = draft_persist_launch(a, a.bar, mode, s);
         prof_end(t, s);
         if (e != hipSuccess) return hip_fail(e, "draft_persist");
         return SPEC_OK;
+    }
+    if (a.bar) {
+        e = persist_clear_abort(a.bar, s);
+        if (e != hipSuccess) return hip_fail(e, "persist_clear_abort");
     }
     for (int k = 0; k < a.gamma; ++k) {
         if (a.head == kHeadRnn) {
@@ -208,6 +213,21 @@ const char* spec_last_error(void) { return g_err.c_str(); }
 int spec_draft_set_persistent(int mode) { return persist_set_mode(mode); }
 
 unsigned spec_draft_set_poll_limit(unsigned polls) { return persist_set_poll_limit(polls); }
+
+spec_status_t spec_draft_status(const void* ws, size_t ws_bytes, int B, int gamma, int V, int r,
+                                int32_t* status, void* stream) {
+    g_err.clear();
+    if (!status) return fail(SPEC_ERR_INVALID, "status is null");
+    if (B <= 0 || gamma <= 0 || V <= 0 || V > kMaxDraftV || r <= 0)
+        return fail(SPEC_ERR_INVALID, "B, gamma, V and r must be those of a draft call");
+    const DraftLayout L = draft_layout(false, B, gamma, V, r);   // same prefix for the RNN head
+    if (spec_status_t st = check_ws(const_cast<void*>(ws), ws_bytes, L.bar + kPersistBarBytes))
+        return st;
+    const char* word = static_cast<const char*>(ws) + L.bar;   // the abort word leads the block
+    hipError_t e = hipMemcpyAsync(status, word, sizeof(int32_t), hipMemcpyDeviceToDevice,
+                                  static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SPEC_OK : hip_fail(e, "spec_draft_status");
+}
 
 spec_status_t spec_philox_uniforms(uint64_t seed, uint32_t offset, uint32_t stream, int B, int K,
                                    float* out, void* stream_handle) {

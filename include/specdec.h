@@ -20,9 +20,16 @@
  * ---------------------------------------
  * - All tensor arguments are DEVICE pointers to caller-owned, contiguous,
  *   row-major buffers on the current HIP device.  The library never
- *   allocates or frees caller memory and keeps no state between calls; the
- *   only scratch is the caller's workspace (size from the *_workspace_size
- *   query, alignment 256 bytes).  Concurrent calls need distinct workspaces.
+ *   allocates or frees caller memory; the only scratch is the caller's
+ *   workspace (size from the *_workspace_size query, alignment 256 bytes).
+ *   Concurrent calls need distinct workspaces.  A call keeps nothing after it
+ *   returns except in its workspace and in these process-wide settings, each
+ *   atomic and read once per call when the call launches its kernels:
+ *     spec_draft_set_persistent  engine of the q-free Markov draft (default 1);
+ *     spec_draft_set_poll_limit  wait limit of the persistent draft;
+ *     spec_profile_enable        kernel timing (off by default; a mutex);
+ *   plus per-device caches of device attributes (CU count, cooperative
+ *   launch support) and each kernel's LDS limit, set once per process.
  * - `stream` is a hipStream_t passed as void* (NULL = default stream).
  *   All work is enqueued asynchronously on it; outputs are valid once the
  *   stream has been synchronised.
@@ -160,18 +167,40 @@ spec_status_t spec_pack_w2(const void *W2, void *W2T, int r, int V, void *stream
  *   1: plain launch.  Residency holds when no other kernel keeps CUs busy
  *      during the draft (e.g. the draft and the target model on one
  *      stream).  If it does not hold, the draft's bounded waits give up
- *      after about a second and the rows not drawn keep token -1 (the
- *      verification then marks those requests invalid).
+ *      after about a second and the rows not drawn keep token -1: the call
+ *      has still returned SPEC_OK (it only enqueues).  spec_draft_status
+ *      reports that case after the fact, and the verification marks the
+ *      requests holding a -1 token invalid (accepted -1).
  *   2: cooperative launch: the runtime guarantees residency by running the
  *      launch alone on the device, at the cost of ~20 us of idle device per
- *      call.  For callers that run other kernels concurrently.
+ *      call.  For callers that run other kernels concurrently.  One
+ *      rocprofv3 counter run of a benchmark in this mode ended with a
+ *      segmentation fault in the process's exit handlers after every result
+ *      was written; its cause is not known (the library registers no exit
+ *      work of its own), so this mode is not the default.
  * 0: two launches per position (streaming tile + finalize).
  *
  * All modes give the same draws up to the rounding of the sums (1 and 2 are
- * the same kernel and give identical results).  Process-wide; returns the
- * previous mode, or -1 (nothing changed) for a mode outside 0..2.
+ * the same kernel and give identical results).  Process-wide and atomic
+ * (read once per draft call); returns the previous mode, or -1 (nothing
+ * changed) for a mode outside 0..2.
  */
 int spec_draft_set_persistent(int mode);
+
+/*
+ * Completion of the last Markov or RNN draft call made with the workspace
+ * `ws` (same B, gamma, V, r as that call).  Enqueues on `stream` a copy of
+ * the call's completion word into status[0] (device int32): 0 when every
+ * draw of the call happened; 1 when the persistent engine's bounded waits
+ * gave up (mode 1 without residency, or the poll limit reached), in which
+ * case the rows not drawn hold token -1 from their first undrawn position
+ * on.  Engines without waits always leave 0.  Stream-ordered after the draft
+ * when enqueued on the draft's stream; read status after synchronising.
+ * Errors: SPEC_ERR_INVALID for a null status or bad sizes,
+ * SPEC_ERR_WORKSPACE for a workspace smaller than the draft's.
+ */
+spec_status_t spec_draft_status(const void *ws, size_t ws_bytes, int B, int gamma, int V, int r,
+                                int32_t *status, void *stream);
 
 /*
  * ---------------------------------------------------------------------------
@@ -256,9 +285,15 @@ spec_status_t spec_verify(
  * The same acceptance rule as spec_verify, for a block drafted with
  * q_logits == NULL.  q_k(x_k) and the normaliser of q_k come from the draft
  * (q_tok_prob, q_logZ); the draft row that feeds a correction is rebuilt as
- * l_n = U[b, n] + W1[x_{n-1}] W2 with the draft's own tile kernel, so it is
- * bit-identical to the logits the draft sampled from.  Only target rows are
- * streamed.
+ * l_n = U[b, n] + W1[x_{n-1}] W2 in fp32 by other kernels than the draft's:
+ * with bf16 P and U, T > 0 and gamma_max > 0 by a streaming kernel that keeps
+ * the rebuilt row in registers and sums the residual weights per 8-token group
+ * (verify_resid_stream, then verify_resid_finalize descends to the token);
+ * otherwise the rebuilt rows are written to the workspace and drawn from.  The
+ * rebuild sums the contraction in another order than the draft engine, so it
+ * matches the logits the draft sampled from to fp32 rounding (about 1e-6
+ * relative), not bit for bit; draws differ only inside the 1e-6 boundary band
+ * of a CDF interval.  Only target rows are streamed in full.
  * U, x0, W1, W2/W2T, w_dtype, r  as passed to spec_draft_sample_markov
  * (U dense [B, gamma_max, V]); draft [B, gamma_max] = the draft's tokens;
  * q_logZ, q_tok_prob [B, gamma_max] = the draft's outputs (same T).
@@ -422,9 +457,10 @@ spec_status_t spec_profile_read(int *launches, double *total_ms);
  * words of its rows, a finalize wave for the share summaries of its row) is a
  * poll that gives up after `polls` polls (about 1 us each on an idle device):
  * it sets the launch's abort word, every workgroup leaves at its next poll,
- * and the rows not drawn keep token -1.  0 restores the default (2^20 polls).
- * Lets a test force that path from the host.  Process-wide; applies to later
- * launches; returns the previous limit.
+ * and the rows not drawn keep token -1 (spec_draft_status reports 1).  0
+ * restores the default (2^20 polls).  Lets a test force that path from the
+ * host.  Process-wide and atomic; applies to later launches; returns the
+ * previous limit.
  */
 unsigned spec_draft_set_poll_limit(unsigned polls);
 

@@ -37,7 +37,8 @@ def test_header_declares_the_boundary():
               "spec_version", "spec_pack_w2", "spec_pack_w2_bytes", "spec_verify_markov",
               "spec_verify_markov_workspace_size", "spec_draft_set_persistent",
               "spec_draft_set_poll_limit", "spec_acceptance_rate", "spec_confidence_head",
-              "spec_prefix_schedule", "spec_prefix_schedule_workspace_size", "spec_tree_select"):
+              "spec_prefix_schedule", "spec_prefix_schedule_workspace_size", "spec_tree_select",
+              "spec_draft_status"):
         assert n in names
 
 
@@ -305,3 +306,17 @@ def test_draft_engine_switch(lib):
     assert lib.spec_draft_set_persistent(7) == -1
     assert lib.spec_draft_set_persistent(-1) == -1
     assert lib.spec_draft_set_persistent(was) == 2
+
+
+def test_draft_status_validation(lib):
+    fake = ctypes.c_void_p(4096)
+    i32, sz = ctypes.c_int, ctypes.c_size_t
+    need = lib.spec_draft_markov_workspace_size(128, 16, 151936, 256)
+    # null status, bad sizes, missing or short workspace: rejected before any copy
+    assert lib.spec_draft_status(fake, need, 128, 16, 151936, 256, None, None) == SPEC_ERR_INVALID
+    assert lib.spec_draft_status(fake, need, 0, 16, 151936, 256, fake, None) == SPEC_ERR_INVALID
+    assert lib.spec_draft_status(fake, need, 128, 16, 1 << 20, 256, fake, None) == SPEC_ERR_INVALID
+    assert lib.spec_draft_status(None, need, 128, 16, 151936, 256, fake, None) == SPEC_ERR_WORKSPACE
+    assert lib.spec_draft_status(fake, 64, 128, 16, 151936, 256, fake, None) == SPEC_ERR_WORKSPACE
+    assert lib.spec_draft_status(ctypes.c_void_p(4096 + 16), need, 128, 16, 151936, 256, fake,
+                                 None) == SPEC_ERR_WORKSPACE

@@ -201,18 +201,24 @@ def test_persistent_draft_gives_up_cleanly():
     W1, W2 = dev(wl["W1"], "bf16"), dev(wl["W2"], "bf16")
     was_mode = sd.spec_draft_set_persistent(1)
     try:
-        ref = host(sd.spec_draft_sample_markov(U, x0, W1, W2, 1.0, q_free=True, seed=3))
+        st_ref, st_bad, st_again = (torch.full((1,), 7, dtype=torch.int32, device="cuda")
+                                    for _ in range(3))
+        ref = host(sd.spec_draft_sample_markov(U, x0, W1, W2, 1.0, q_free=True, seed=3,
+                                               status=st_ref))
         sd.spec_draft_set_poll_limit(2)
-        d = sd.spec_draft_sample_markov(U, x0, W1, W2, 1.0, q_free=True, seed=3)
+        d = sd.spec_draft_sample_markov(U, x0, W1, W2, 1.0, q_free=True, seed=3, status=st_bad)
         torch.cuda.synchronize()
         sd.spec_draft_set_poll_limit(0)
         bad = host(d)
-        again = host(sd.spec_draft_sample_markov(U, x0, W1, W2, 1.0, q_free=True, seed=3))
+        again = host(sd.spec_draft_sample_markov(U, x0, W1, W2, 1.0, q_free=True, seed=3,
+                                                 status=st_again))
         v = host(sd.spec_verify_markov(dev(wl["P"], "bf16"), U, x0, W1, W2, d["tokens"],
                                        d["q_logZ"], d["q_tok_prob"], 1.0, seed=3))
     finally:
         sd.spec_draft_set_poll_limit(0)
         sd.spec_draft_set_persistent(was_mode)
+    # the completion word reports the give-up, and only it
+    assert (int(st_ref.item()), int(st_bad.item()), int(st_again.item())) == (0, 1, 0)
     tok = bad["tokens"]
     assert np.all((tok == -1) | ((tok >= 0) & (tok < V)))
     assert (tok == -1).any()
@@ -222,6 +228,43 @@ def test_persistent_draft_gives_up_cleanly():
     assert np.all(v["accepted"][~undrawn] >= 0)
     for k in ("tokens", "q_logZ", "q_tok_prob"):
         np.testing.assert_array_equal(ref[k], again[k], err_msg=k)
+
+
+def test_draft_status_other_engines():
+    """The per-position engine and the materialised draft have no waits: after
+    a persistent call that gave up, a call on either engine with the same
+    workspace reads complete (0) again."""
+    sd = require_gpu()
+    B, gamma, V, r = 70, 3, 8192, 128
+    cfg = dict(workloads.CONFIGS["markov-152k-b128"])
+    wl = workloads.make_markov(cfg, B=B, gamma=gamma, V=V, r=r)
+    U, x0 = dev(wl["U"], "bf16"), dev(wl["x0"])
+    W1, W2 = dev(wl["W1"], "bf16"), dev(wl["W2"], "bf16")
+    ws = torch.empty(sd.workspace_bytes("markov", B=B, gamma=gamma, V=V, r=r), dtype=torch.uint8,
+                     device="cuda")
+    st = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    was = sd.spec_draft_set_persistent(1)
+    try:
+        sd.spec_draft_set_poll_limit(2)
+        sd.spec_draft_sample_markov(U, x0, W1, W2, 1.0, q_free=True, workspace=ws, status=st)
+        sd.spec_draft_set_poll_limit(0)
+        assert int(st.item()) == 1
+        sd.spec_draft_set_persistent(0)
+        d = sd.spec_draft_sample_markov(U, x0, W1, W2, 1.0, q_free=True, workspace=ws, status=st)
+        assert int(st.item()) == 0
+        assert bool((d["tokens"] >= 0).all())
+        sd.spec_draft_set_persistent(1)
+        sd.spec_draft_set_poll_limit(2)
+        sd.spec_draft_sample_markov(U, x0, W1, W2, 1.0, q_free=True, workspace=ws, status=st)
+        sd.spec_draft_set_poll_limit(0)
+        assert int(st.item()) == 1
+        sd.spec_draft_sample_markov(U, x0, W1, W2, 1.0, workspace=ws, status=st)   # q logits
+        assert int(st.item()) == 0
+        st2 = sd.spec_draft_status(ws, B, gamma, V, r)
+        assert int(st2.item()) == 0
+    finally:
+        sd.spec_draft_set_poll_limit(0)
+        sd.spec_draft_set_persistent(was)
 
 
 def test_qfree_draft_packed_w2_and_uniforms(orc):
