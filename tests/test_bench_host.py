@@ -25,13 +25,26 @@ def test_more_than_one_gpu_is_refused():
 
 
 def test_algorithmic_bytes_of_the_metric_workload():
+    """Only the method's inputs and outputs count: U, W2 once, the gathered W1
+    rows, the anchors, and the tokens, log Z and q(x) written; the kernel's own
+    softmax summaries (scratch it writes and reads back) do not."""
     B, g, V, r = 128, 16, 151936, 256
-    segs = (V + 31) // 32
-    per_position = B * V * 2 + B * segs * (4 + 16) + B * 256 * 16 + B * r * 2
-    want = g * per_position + r * V * 2   # U_k, summaries, W1 rows per position; W2 once
+    want = B * g * V * 2 + r * V * 2 + B * g * r * 2 + B * 4 + B * g * 12
     kb = bench.kernel_bytes(METRIC_SHAPE)
-    assert kb["draft_persist"] == want == 904036352
+    assert kb["draft_persist"] == want == 701194752
     assert kb["verify_rows_p"] == B * (g + 1) * V * 2 == 661225472
+    # the streamed final draw: two rows per residual draw, one per bonus draw
+    kb = bench.kernel_bytes(METRIC_SHAPE, n_resid=100)
+    assert kb["verify_resid"] == 100 * V * 4 + 28 * V * 2 + r * V * 2 + 100 * r * 2
+    # the q-free cycle: draft + target rows + final draw
+    assert bench.cycle_bytes(METRIC_SHAPE, "qfree", 100) == \
+        701194752 + 661225472 + kb["verify_resid"]
+
+
+def test_algorithmic_bytes_of_ragged_lengths():
+    shape = dict(METRIC_SHAPE, B=4, lens=[1, 16, 3, 0])
+    kb = bench.kernel_bytes(shape)
+    assert kb["verify_rows_p"] == (20 + 4) * 151936 * 2
 
 
 def test_bias_flops_of_the_metric_workload():
