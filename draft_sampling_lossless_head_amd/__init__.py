@@ -27,6 +27,8 @@ from .api import (  # noqa: F401
     spec_tree_select,
     spec_verify,
     spec_verify_markov,
+    spec_verify_noalloc,
+    spec_verify_noalloc_max_bytes,
     spec_version,
     workspace_bytes,
 )

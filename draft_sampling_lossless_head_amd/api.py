@@ -59,6 +59,11 @@ def load_library():
     lib.spec_verify.argtypes = [vp, i32, vp, i32, vp, vp, vp, vp, i32, i32, i32, f32, vp, u64,
                                 u32, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.spec_verify.restype = i32
+    lib.spec_verify_noalloc_max_bytes.argtypes = []
+    lib.spec_verify_noalloc_max_bytes.restype = sz
+    lib.spec_verify_noalloc.argtypes = [vp, i32, vp, i32, vp, vp, vp, vp, i32, i32, i32, f32, vp,
+                                        u64, u32, vp, vp, vp, vp, vp, vp]
+    lib.spec_verify_noalloc.restype = i32
     lib.spec_pack_w2_bytes.argtypes = [i32, i32]
     lib.spec_pack_w2_bytes.restype = sz
     lib.spec_pack_w2.argtypes = [vp, vp, i32, i32, vp]
@@ -310,6 +315,65 @@ def spec_verify(P, Q, draft, T=1.0, *, gamma_max=None, lens=None, p_row_off=None
     draft [B, gamma].  Packed: P [rows, V] with p_row_off, Q [rows, V] with
     q_row_off, lens [B] int32, gamma_max given."""
     lib = load_library()
+    B, gamma_max, V = _verify_shapes(P, Q, draft, gamma_max, lens, p_row_off, q_row_off, uniforms)
+    dev = P.device
+    if out is None:
+        out = dict(accepted=torch.empty(B, dtype=torch.int32, device=dev),
+                   out_tokens=torch.empty((B, gamma_max + 1), dtype=torch.int32, device=dev))
+        if diagnostics:
+            out["p_logZ"] = torch.empty((B, gamma_max + 1), dtype=torch.float32, device=dev)
+            out["q_logZ"] = torch.empty((B, gamma_max), dtype=torch.float32, device=dev)
+            out["accept_prob"] = torch.empty((B, gamma_max), dtype=torch.float32, device=dev)
+    ws, nws = _workspace(lib.spec_verify_workspace_size(B, gamma_max, V), dev, workspace)
+    st = lib.spec_verify(
+        _ptr(P), _dtype_code(P, "P"), _ptr(Q), _dtype_code(Q, "Q") if Q is not None else SPEC_F32,
+        _ptr(draft), _ptr(lens), _ptr(p_row_off), _ptr(q_row_off), B, gamma_max, V, float(T),
+        _ptr(uniforms), seed, offset, _ptr(out["accepted"]), _ptr(out["out_tokens"]),
+        _ptr(out.get("p_logZ")), _ptr(out.get("q_logZ")), _ptr(out.get("accept_prob")), _ptr(ws),
+        nws, _stream(stream))
+    _check(st, "spec_verify")
+    return out
+
+
+def spec_verify_noalloc_max_bytes():
+    """Scratch bytes spec_verify_noalloc holds per GPU (its size limit)."""
+    return int(load_library().spec_verify_noalloc_max_bytes())
+
+
+def spec_verify_noalloc(P, Q, draft, out, T=1.0, *, gamma_max=None, lens=None, p_row_off=None,
+                        q_row_off=None, uniforms=None, seed=0, offset=0, stream=None):
+    """spec_verify for callers that cannot allocate: the library's fixed device
+    scratch stands in for the workspace, and the caller passes every output in
+    `out` (accepted int32 [B], out_tokens int32 [B, gamma_max + 1], and
+    optionally p_logZ, q_logZ, accept_prob).  Neither this wrapper nor the
+    library allocates device memory.  Calls that overlap on one GPU share the
+    scratch and race."""
+    lib = load_library()
+    B, gamma_max, V = _verify_shapes(P, Q, draft, gamma_max, lens, p_row_off, q_row_off, uniforms)
+    for n, dt, shp in (("accepted", torch.int32, (B,)), ("out_tokens", torch.int32, (B, gamma_max + 1)),
+                       ("p_logZ", torch.float32, (B, gamma_max + 1)),
+                       ("q_logZ", torch.float32, (B, gamma_max)),
+                       ("accept_prob", torch.float32, (B, gamma_max))):
+        t = out.get(n)
+        if t is None:
+            if n in ("accepted", "out_tokens"):
+                raise SpecError(f"out[{n!r}] is required")
+            continue
+        _dev(t, n)
+        if t.dtype != dt or tuple(t.shape) != shp or not t.is_contiguous():
+            raise SpecError(f"out[{n!r}] must be contiguous {dt} {list(shp)}")
+    st = lib.spec_verify_noalloc(
+        _ptr(P), _dtype_code(P, "P"), _ptr(Q), _dtype_code(Q, "Q") if Q is not None else SPEC_F32,
+        _ptr(draft), _ptr(lens), _ptr(p_row_off), _ptr(q_row_off), B, gamma_max, V, float(T),
+        _ptr(uniforms), seed, offset, _ptr(out["accepted"]), _ptr(out["out_tokens"]),
+        _ptr(out.get("p_logZ")), _ptr(out.get("q_logZ")), _ptr(out.get("accept_prob")),
+        _stream(stream))
+    _check(st, "spec_verify_noalloc")
+    return out
+
+
+def _verify_shapes(P, Q, draft, gamma_max, lens, p_row_off, q_row_off, uniforms):
+    """Shape and dtype checks of spec_verify's arguments; returns (B, gamma_max, V)."""
     _dev(P, "P")
     _dev(draft, "draft")
     B = draft.shape[0]
@@ -335,23 +399,7 @@ def spec_verify(P, Q, draft, T=1.0, *, gamma_max=None, lens=None, p_row_off=None
     if uniforms is not None and (uniforms.dtype != torch.float32
                                  or uniforms.shape != (B, gamma_max + 1)):
         raise SpecError("uniforms must be float32 [B, gamma_max + 1]")
-    dev = P.device
-    if out is None:
-        out = dict(accepted=torch.empty(B, dtype=torch.int32, device=dev),
-                   out_tokens=torch.empty((B, gamma_max + 1), dtype=torch.int32, device=dev))
-        if diagnostics:
-            out["p_logZ"] = torch.empty((B, gamma_max + 1), dtype=torch.float32, device=dev)
-            out["q_logZ"] = torch.empty((B, gamma_max), dtype=torch.float32, device=dev)
-            out["accept_prob"] = torch.empty((B, gamma_max), dtype=torch.float32, device=dev)
-    ws, nws = _workspace(lib.spec_verify_workspace_size(B, gamma_max, V), dev, workspace)
-    st = lib.spec_verify(
-        _ptr(P), _dtype_code(P, "P"), _ptr(Q), _dtype_code(Q, "Q") if Q is not None else SPEC_F32,
-        _ptr(draft), _ptr(lens), _ptr(p_row_off), _ptr(q_row_off), B, gamma_max, V, float(T),
-        _ptr(uniforms), seed, offset, _ptr(out["accepted"]), _ptr(out["out_tokens"]),
-        _ptr(out.get("p_logZ")), _ptr(out.get("q_logZ")), _ptr(out.get("accept_prob")), _ptr(ws),
-        nws, _stream(stream))
-    _check(st, "spec_verify")
-    return out
+    return B, gamma_max, V
 
 
 @_on_stream

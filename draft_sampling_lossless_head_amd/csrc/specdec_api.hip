@@ -3,6 +3,8 @@
 #include <cmath>
 #include <cstdint>
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 #include <string>
 
 #include "device_common.hpp"
@@ -366,13 +368,45 @@ size_t spec_verify_workspace_size(int B, int gamma_max, int V) {
     return verify_layout(B, gamma_max, V).total;
 }
 
-spec_status_t spec_verify(const void* P, int p_dtype, const void* Q, int q_dtype,
-                          const int32_t* draft, const int32_t* lens, const int64_t* p_row_off,
-                          const int64_t* q_row_off, int B, int gamma_max, int V, float T,
-                          const float* uniforms, uint64_t seed, uint32_t offset,
-                          int32_t* accepted, int32_t* out_tokens, float* p_logZ, float* q_logZ,
-                          float* accept_prob, void* ws, size_t ws_bytes, void* stream) {
-    g_err.clear();
+// Scratch of spec_verify_noalloc: a file-scope device array, one copy per GPU
+// the library runs on, held until the process ends.  Host code never passes
+// the array's name to a kernel (on the host it is only a stand-in symbol);
+// it passes the device address hipGetSymbolAddress returns for the current
+// device, looked up once per device.
+static constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kNoAllocMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kNoAllocMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's scratch address, or an error status.
+spec_status_t noalloc_scratch(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kNoAllocMaxDevices) return fail(SPEC_ERR_UNSUPPORTED, "device ordinal beyond 63");
+    void* ptr = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!ptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        ptr = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!ptr) {
+            e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || !ptr) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+            g_scratch_addr[dev].store(ptr, std::memory_order_release);
+        }
+    }
+    *out = ptr;
+    return SPEC_OK;
+}
+
+// Argument checks shared by spec_verify and spec_verify_noalloc (everything
+// but the workspace).
+spec_status_t verify_check(const void* P, int p_dtype, const void* Q, int q_dtype,
+                           const int32_t* draft, int B, int gamma_max, int V, float T,
+                           const int32_t* accepted, const int32_t* out_tokens) {
     if (B < 0 || gamma_max < 0) return fail(SPEC_ERR_INVALID, "B and gamma_max must be >= 0");
     if (V <= 0 || V > kMaxV) return fail(SPEC_ERR_INVALID, "V must be in [1, 2^28]");
     if (spec_status_t st = check_T(T)) return st;
@@ -384,8 +418,15 @@ spec_status_t spec_verify(const void* P, int p_dtype, const void* Q, int q_dtype
         return fail(SPEC_ERR_INVALID, "null required pointer (Q, draft)");
     if (!aligned16(P) || (Q && !aligned16(Q)))
         return fail(SPEC_ERR_UNSUPPORTED, "P and Q must be 16-byte aligned");
-    const VerifyLayout L = verify_layout(B, gamma_max, V);
-    if (spec_status_t st = check_ws(ws, ws_bytes, L.total)) return st;
+    return SPEC_OK;
+}
+
+spec_status_t verify_run(const void* P, int p_dtype, const void* Q, int q_dtype,
+                         const int32_t* draft, const int32_t* lens, const int64_t* p_row_off,
+                         const int64_t* q_row_off, int B, int gamma_max, int V, float T,
+                         const float* uniforms, uint64_t seed, uint32_t offset,
+                         int32_t* accepted, int32_t* out_tokens, float* p_logZ, float* q_logZ,
+                         float* accept_prob, void* ws, const VerifyLayout& L, void* stream) {
     char* w = static_cast<char*>(ws);
     VerifyArgs a{};
     a.P = P;
@@ -416,6 +457,51 @@ spec_status_t spec_verify(const void* P, int p_dtype, const void* Q, int q_dtype
     hipError_t e = verify_launch(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SPEC_OK : hip_fail(e, "verify");
 }
+
+}  // namespace
+
+spec_status_t spec_verify(const void* P, int p_dtype, const void* Q, int q_dtype,
+                          const int32_t* draft, const int32_t* lens, const int64_t* p_row_off,
+                          const int64_t* q_row_off, int B, int gamma_max, int V, float T,
+                          const float* uniforms, uint64_t seed, uint32_t offset,
+                          int32_t* accepted, int32_t* out_tokens, float* p_logZ, float* q_logZ,
+                          float* accept_prob, void* ws, size_t ws_bytes, void* stream) {
+    g_err.clear();
+    if (spec_status_t st = verify_check(P, p_dtype, Q, q_dtype, draft, B, gamma_max, V, T, accepted, out_tokens))
+        return st;
+    if (B == 0) return SPEC_OK;
+    const VerifyLayout L = verify_layout(B, gamma_max, V);
+    if (spec_status_t st = check_ws(ws, ws_bytes, L.total)) return st;
+    return verify_run(P, p_dtype, Q, q_dtype, draft, lens, p_row_off, q_row_off, B, gamma_max, V, T,
+                      uniforms, seed, offset, accepted, out_tokens, p_logZ, q_logZ, accept_prob, ws, L,
+                      stream);
+}
+
+size_t spec_verify_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+spec_status_t spec_verify_noalloc(const void* P, int p_dtype, const void* Q, int q_dtype,
+                                  const int32_t* draft, const int32_t* lens,
+                                  const int64_t* p_row_off, const int64_t* q_row_off, int B,
+                                  int gamma_max, int V, float T, const float* uniforms,
+                                  uint64_t seed, uint32_t offset, int32_t* accepted,
+                                  int32_t* out_tokens, float* p_logZ, float* q_logZ,
+                                  float* accept_prob, void* stream) {
+    g_err.clear();
+    if (spec_status_t st = verify_check(P, p_dtype, Q, q_dtype, draft, B, gamma_max, V, T, accepted, out_tokens))
+        return st;
+    if (B == 0) return SPEC_OK;
+    const VerifyLayout L = verify_layout(B, gamma_max, V);
+    if (L.total > kNoAllocScratchBytes)
+        return fail(SPEC_ERR_WORKSPACE, "spec_verify_noalloc: B, gamma_max and V need " + std::to_string(L.total) +
+                                            " bytes of scratch, more than its fixed " +
+                                            std::to_string(kNoAllocScratchBytes) + " (use spec_verify)");
+    void* ws = nullptr;
+    if (spec_status_t st = noalloc_scratch(&ws)) return st;
+    return verify_run(P, p_dtype, Q, q_dtype, draft, lens, p_row_off, q_row_off, B, gamma_max, V, T,
+                      uniforms, seed, offset, accepted, out_tokens, p_logZ, q_logZ, accept_prob, ws, L,
+                      stream);
+}
+
 
 spec_status_t spec_acceptance_rate(const void* P, int p_dtype, const void* Q, int q_dtype,
                                    const int32_t* lens, const int64_t* p_row_off,

@@ -278,6 +278,31 @@ spec_status_t spec_verify(
     void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * spec_verify without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, outputs, kernels and results as
+ * spec_verify; the scratch is a fixed array of spec_verify_noalloc_max_bytes()
+ * (16 MiB) in the library's device image, one per GPU, held until the process
+ * ends; its address on the current device is looked up on the first call
+ * there.  The call allocates nothing (no hipMalloc or hipFree); calls whose
+ * spec_verify_workspace_size(B, gamma_max, V) exceeds the limit return
+ * SPEC_ERR_WORKSPACE before any launch.  Every call on one GPU uses the same
+ * array, so calls that overlap on one GPU (other streams, other threads)
+ * race and give wrong results: serialise them.  Nothing in the array must
+ * start at zero; each call writes every word it reads.
+ */
+size_t spec_verify_noalloc_max_bytes(void);
+
+spec_status_t spec_verify_noalloc(
+    const void *P, int p_dtype, const void *Q, int q_dtype,
+    const int32_t *draft, const int32_t *lens,
+    const int64_t *p_row_off, const int64_t *q_row_off,
+    int B, int gamma_max, int V, float T,
+    const float *uniforms, uint64_t seed, uint32_t offset,
+    int32_t *accepted, int32_t *out_tokens,
+    float *p_logZ, float *q_logZ, float *accept_prob, void *stream);
+
+/*
  * ---------------------------------------------------------------------------
  * Lossless verification of a q-free Markov draft
  * [VESSL "알고리즘", "수락 규칙"; DSpark §1.2 Markov-head eq.]
