@@ -9,6 +9,7 @@ from .gen import (  # noqa: F401
     as_f64,
     make_confidence,
     make_markov,
+    make_repeated_markov,
     make_rnn,
     make_schedule,
     make_trees,

@@ -255,3 +255,34 @@ def make_trees(R, M, seed, levels=16, beta=(4.0, 1.2)):
             parent[:, lo:hi] = g.integers(plo, max(phi, plo + 1), size=(R, hi - lo)) if phi > plo else -1
     c = g.beta(beta[0], beta[1], size=(R, M)).astype(np.float32)
     return dict(R=R, M=M, parent=parent, c=c)
+
+
+# Stream id of the repeated-request workload.
+_S_REPEAT = 7
+
+
+def make_repeated_markov(B, gamma, V, r, seed, scale=2.0, sigma=1.0, w_std=0.3, w1_zero=False,
+                         dtype="bf16"):
+    """One request's logits repeated over a batch of B requests, for statistical
+    checks that use the batch as the trial axis: draft base logits
+    U[k] = scale * N(0, 1) (k < gamma), target logits P[k] = U[k] + sigma *
+    N(0, 1) (k < gamma) and P[gamma] = scale * N(0, 1), identical in every row;
+    W1 [V, r] and W2 [r, V] ~ N(0, w_std**2) (W1 all zero with w1_zero, so the
+    draft rows do not depend on the previous token); anchors x0 ~ U{0..V-1}
+    per row.  Logits and weights are rounded to bf16 (dtype "bf16")."""
+    g = _rng(seed, _S_REPEAT)
+    U1 = (scale * g.standard_normal((gamma, V))).astype(np.float32)
+    P1 = np.empty((gamma + 1, V), dtype=np.float32)
+    P1[:gamma] = U1 + (sigma * g.standard_normal((gamma, V))).astype(np.float32)
+    P1[gamma] = (scale * g.standard_normal(V)).astype(np.float32)
+    W1 = (w_std * g.standard_normal((V, r))).astype(np.float32)
+    if w1_zero:
+        W1[:] = 0.0
+    W2 = (w_std * g.standard_normal((r, V))).astype(np.float32)
+    x0 = g.integers(0, V, size=B, dtype=np.int64).astype(np.int32)
+    U = np.broadcast_to(U1, (B, gamma, V))
+    P = np.broadcast_to(P1, (B, gamma + 1, V))
+    return dict(B=B, gamma=gamma, V=V, r=r, logit_dtype=dtype, w_dtype=dtype,
+                U=_store(np.ascontiguousarray(U), dtype), P=_store(np.ascontiguousarray(P), dtype),
+                W1=_store(W1, dtype), W2=_store(W2, dtype), x0=x0,
+                U1=_store(U1, dtype), P1=_store(P1, dtype))
