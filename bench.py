@@ -630,6 +630,52 @@ def around_the_cycle(sd, torch, cyc, warmup, steps):
     return out
 
 
+def gemm_only(torch, steps, warmup):
+    """GEMM-only measurement of the draft's bias contraction, for comparison
+    with the fused draft: one position's product [M, r] x [r, V] (M = 128
+    requests, r = 256, V = 151936; bf16 inputs and output, fp32 accumulation)
+    by the library GEMM (torch.mm, i.e. hipBLASLt), with the weight warm: the
+    same W2 every call, so its 78 MB stay in the Infinity Cache.  Two weight
+    layouts (W2 [r, V] row-major, and W2^T [V, r] as a linear layer's weight)
+    and, for scale, M = 2048 (all 16 positions' rows at once, which the
+    sequential draft cannot do).  Each call is timed with hipEvents on the
+    stream it runs on.  Prints one JSON line."""
+    K, N = 256, 151936
+    g = torch.Generator(device="cuda").manual_seed(5)
+    W = (0.02 * torch.randn(K, N, device="cuda", generator=g)).to(torch.bfloat16)
+    WT = W.t().contiguous()
+    res = {}
+    for M in (128, 2048):
+        A = torch.randn(M, K, device="cuda", generator=g).to(torch.bfloat16)
+        out = torch.empty(M, N, device="cuda", dtype=torch.bfloat16)
+        for lay, rhs in (("W2[r,V]", W), ("W2T[V,r]", WT.t())):
+            for _ in range(warmup):
+                torch.mm(A, rhs, out=out)
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(steps)]
+            for a, b in ev:
+                a.record()
+                torch.mm(A, rhs, out=out)
+                b.record()
+            torch.cuda.synchronize()
+            us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+            avg = sum(us) / len(us)
+            flops = 2.0 * M * K * N
+            out_bytes = M * N * 2
+            res[f"M{M} {lay}"] = dict(
+                avg_us=round(avg, 2), median_us=round(us[len(us) // 2], 2), min_us=round(us[0], 2),
+                tflops=round(flops / (avg * 1e-6) / 1e12, 1),
+                mfma_frac=round(flops / (avg * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS, 4),
+                mfma_floor_us=round(flops / (MFMA_PEAK_TFLOPS * 1e12) * 1e6, 2),
+                out_write_floor_us=round(out_bytes / (HBM_PEAK_GBS * 1e9) * 1e6, 2))
+            log(f"gemm-only M={M} {lay}: {avg:.2f} us avg, {res[f'M{M} {lay}']['tflops']} TFLOP/s")
+        del A, out
+    print(json.dumps({"metric": "bias contraction GEMM-only (library GEMM, W2 warm)",
+                      "unit": "TFLOP/s", "dtype": "bf16", "peak": MFMA_PEAK_TFLOPS,
+                      "shape": {"K": K, "N": N}, "steps": steps, "warmup": warmup,
+                      "variants": res}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -659,6 +705,9 @@ def main():
     ap.add_argument("--mfma-from", metavar="SQ_CSV",
                     help="no GPU run: turn a rocprofv3 --pmc run with SQ_VALU_MFMA_BUSY_CYCLES and "
                          "SQ_WAVE_CYCLES into the matrix-core record of --traffic-kernel")
+    ap.add_argument("--gemm-only", action="store_true",
+                    help="only the GEMM-only measurement of the bias contraction (library GEMM, "
+                         "W2 warm); prints its own JSON line")
     ap.add_argument("--traffic-kernel", default="draft_persist<16, 5, 4, false>")
     ap.add_argument("--traffic-label", default="draft_persist")
     args = ap.parse_args()
@@ -678,6 +727,10 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.gemm_only:
+        gemm_only(torch, args.steps, min(args.warmup, 20))
+        return
 
     import draft_sampling_lossless_head_amd as sd
 
