@@ -22,6 +22,8 @@ from .binding import (  # noqa: F401
     draft_markov,
     draft_rnn,
     verify,
+    tree_uniforms,
+    verify_tree,
     confidence,
     prefix_schedule,
     tree_select,

@@ -37,6 +37,11 @@ PINS = {
                        "throughput; admitted set is the global top-t; constant SPS admits all; "
                        "SPS that vanishes past R admits none; hand-worked example; early stop at "
                        "the first fall even when a later size would be higher",
+    "verify_tree": "exact output law (draft tokens enumerated with their draft probabilities, "
+                   "uniforms integrated by bisecting the oracle's monotone decisions) equals the "
+                   "target's autoregressive law at every emitted position, on five tree shapes at "
+                   "T = 1 and 0.7; a chain-shaped tree equals orc_verify exactly (T = 1, 0.7, 0); "
+                   "T = 0 emits the target's greedy sequence; q = p passes the lowest-index child",
     "tree_select": "brute force over every prefix-closed node set of the budget on tiny trees "
                    "(the chosen set is one of them and reaches the best summed survival); chain "
                    "gives its first n nodes; star gives numpy's stable top-n of c; all-ones gives "
@@ -96,6 +101,9 @@ def _L():
                                    d, d, i, d, ctypes.c_double,
                                    i, i, d, d, d, d, d, d, i]
         lib.orc_verify.restype = ctypes.c_int
+        lib.orc_verify_tree.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_double, i, i,
+                                        d, d, d, ctypes.c_double, i, i, i, d, d, d, i]
+        lib.orc_verify_tree.restype = ctypes.c_int
         lib.orc_confidence.argtypes = [d, ctypes.c_int, d, ctypes.c_int, d]
         lib.orc_confidence.restype = ctypes.c_double
         f = ctypes.POINTER(ctypes.c_float)
@@ -292,6 +300,46 @@ def verify(P, Q, draft, T, u_test, u_final):
     return dict(n=n.value, out=out, logZp=logZp, logZq=logZq[:L], accept_prob=ap[:L],
                 test_margin=tm[:L], final_thr=fthr.value, final_margin=fmar.value,
                 fallback=fb.value)
+
+
+def tree_uniforms(seed, offset, B, M):
+    """[B, M + 1]: the ratio-test uniform of node v (stream 3, index v) at
+    v < M and the final-draw uniform (stream 3, index M) in slot M."""
+    L = _L()
+    out = np.empty((B, M + 1), dtype=np.float64)
+    for b in range(B):
+        for v in range(M + 1):
+            out[b, v] = L.orc_uniform(seed, offset, b, v, 3)
+    return out
+
+
+def verify_tree(P, Q, parent, tok, T, u_node, u_final):
+    """One request's tree: P, Q [M + 1, V] logits (row 0 the root, row 1 + v
+    node v), parent [M] (parents first, -1 = child of the root), tok [M]
+    draft tokens, u_node [M] ratio-test uniforms, u_final.  Returns None for
+    an invalid tree or token."""
+    P, Q = _f64(P), _f64(Q)
+    par, tk = _i32(parent), _i32(tok)
+    M = len(par)
+    V = P.shape[1]
+    assert P.shape == (M + 1, V) and Q.shape == (M + 1, V) and len(tk) == M
+    un = _f64(u_node) if M > 0 else np.zeros(1)
+    n = ctypes.c_int()
+    path = np.zeros(max(M, 1), dtype=np.int32)
+    out = np.zeros(M + 1, dtype=np.int32)
+    ratio = np.zeros(max(M, 1))
+    fthr, fmar = ctypes.c_double(), ctypes.c_double()
+    fb = ctypes.c_int()
+    st = _L().orc_verify_tree(V, M, float(T), _ip(par if M else np.zeros(1, np.int32)),
+                              _ip(tk if M else np.zeros(1, np.int32)), _dp(P), _dp(Q), _dp(un),
+                              float(u_final), ctypes.byref(n), _ip(path), _ip(out), _dp(ratio),
+                              ctypes.byref(fthr), ctypes.byref(fmar), ctypes.byref(fb))
+    if st == -1:
+        return None
+    if st != 0:
+        raise ValueError(f"oracle verify_tree failed with status {st}")
+    return dict(n=n.value, path=path[:M], out=out, test_ratio=ratio[:M], final_thr=fthr.value,
+                final_margin=fmar.value, fallback=fb.value)
 
 
 # --------------------------------------------------------------------------

@@ -38,13 +38,19 @@
  *     [s_{k-1}; W1[x_{k-1}]; h_k]; the bias uses W_o z_k; s_0 = 0.
  *   - uniforms: Philox4x32-10, key = (seed lo, seed hi), counter =
  *     (request b, position k, stream, call offset); u = (word0 >> 8) * 2^-24.
- *     stream 0 = draft sample, 1 = ratio test, 2 = final (corrected/bonus).
+ *     stream 0 = draft sample, 1 = ratio test, 2 = final (corrected/bonus),
+ *     3 = tree verification (index v < M: node v's ratio test; index M: the
+ *     final draw).
  *   - scheduler: survival a_{r,j} is the float32 product of c_{r,0..j} taken
  *     left to right; candidates are ordered by a descending, then request,
  *     then position; tau sums each a cut to a multiple of 2^-48 in exact
  *     integers; B = R + admitted; SPS(B) = 0 past the end of its table; the
  *     search stops at the first admission that lowers tau * SPS(B) (ties
  *     continue), and that admission is not made.
+ *   - tree verification: siblings are tested in increasing index against a
+ *     running residual r (p, then normalize(max(0, r - q)) after each
+ *     failure); the first passing child is descended into; no pass: final
+ *     token from r; a leaf: bonus from its p (see orc_verify_tree).
  *   - tree selection: nodes come parents first (parent[v] < v, -1 = a child
  *     of the root, the last accepted token); a_v = c_v * a_parent in float32
  *     (root 1); order a descending, then depth ascending, then node id; the
@@ -457,6 +463,136 @@ int orc_verify(int V, int L, double T,
     *n_acc = n;
     free(w);
     return status;
+}
+
+/* ------------------------------------------------------------------------ */
+/* [P2] "γ 재배분: 체인 대신 트리": verification of a tree of draft             */
+/* continuations in one target pass, under the acceptance rule of "수락 규칙". */
+/* ------------------------------------------------------------------------ */
+
+/* Nodes 0..M-1 come parents first (parent[v] < v; -1 = a child of the root,
+ * the last accepted token).  Row 0 of P and Q belongs to the root and row
+ * 1 + v to node v: the P row holds the target's next-token logits after the
+ * path to that node; the Q row holds the draft logits its children were drawn
+ * from (one independent draw per child).  tok[v] is node v's draft token.
+ *
+ * Reading (recursive rejection over siblings): the walk starts at the root
+ * with target law r = p (softmax of the node's P row at T).  The node's
+ * children are tested in increasing index; child c with token x passes iff
+ * u_node[c] * q(x) < r(x) (q = softmax of the node's Q row).  A pass emits x
+ * and moves the walk to c, with r = p of c.  A failure replaces r by
+ * normalize(max(0, r - q)) and tests the next child.  When every child has
+ * failed the final token is drawn from r by the inverse CDF with u_final; at
+ * a node without children it is drawn from that node's p (bonus token).  If a
+ * residual has no mass after rounding, the walk stops there and the final
+ * token is drawn from that node's p (*fallback = 1).
+ * T == 0: a child passes iff its token is the argmax of the node's P row
+ * (lowest id on ties); the final token is that argmax.
+ *
+ * Outputs: *n_acc = number of accepted nodes; path[0..n-1] their ids (-1
+ * after); out[0..n-1] their tokens, out[n] the final token (-1 after;
+ * out has M + 1 entries); test_ratio[c] = r(x)/q(x) (capped at 1) of every
+ * tested child c, NaN for children never tested; *final_thr, *final_margin
+ * as orc_inverse_cdf (T == 0: the argmax's logit gap).
+ * Returns 0; -1 for an invalid tree (parent out of range), a token outside
+ * [0, V) or a tested row without a finite logit (then n_acc = -1 and every
+ * output -1). */
+int orc_verify_tree(int V, int M, double T, const int *parent, const int *tok,
+                    const double *P, const double *Q, const double *u_node, double u_final,
+                    int *n_acc, int *path, int *out, double *test_ratio,
+                    double *final_thr, double *final_margin, int *fallback)
+{
+    double *r = (double *)malloc(sizeof(double) * (size_t)(V > 0 ? V : 1));
+    double *q = (double *)malloc(sizeof(double) * (size_t)(V > 0 ? V : 1));
+    double *w = (double *)malloc(sizeof(double) * (size_t)(V > 0 ? V : 1));
+    int v, c, node = -1, n = 0, final_tok = -1, bad = 0;
+    if (!r || !q || !w) { free(r); free(q); free(w); return -2; }
+    *fallback = 0;
+    *final_thr = 0.0;
+    *final_margin = 0.0;
+    *n_acc = -1;
+    for (v = 0; v <= M; v++) out[v] = -1;
+    for (v = 0; v < M; v++) { path[v] = -1; test_ratio[v] = NAN; }
+    for (v = 0; v < M; v++) {
+        if (parent[v] < -1 || parent[v] >= v) bad = 1;
+        if (tok[v] < 0 || tok[v] >= V) bad = 1;
+    }
+    if (bad) { free(r); free(q); free(w); return -1; }
+
+    for (;;) {
+        const double *pl = P + (size_t)(node + 1) * V;   /* the node's target row */
+        const double *ql = Q + (size_t)(node + 1) * V;   /* its children's draft row */
+        int accepted = -1, stop_fallback = 0;
+        if (T == 0.0) {
+            double gap;
+            int a = orc_argmax(pl, V, &gap);
+            if (pl[a] == -INFINITY) { bad = 1; break; }
+            for (c = node + 1; c < M; c++) {
+                if (parent[c] != node) continue;
+                test_ratio[c] = (tok[c] == a) ? 1.0 : 0.0;
+                if (tok[c] == a) { accepted = c; break; }
+            }
+            if (accepted < 0) { final_tok = a; *final_margin = gap; break; }
+        } else {
+            double Zp, Zq, Zr, lzp, lzq;
+            int has_child = 0;
+            lzp = orc_softmax_weights(pl, V, T, r, &Zp);
+            if (lzp == -INFINITY) { bad = 1; break; }
+            for (v = 0; v < V; v++) r[v] /= Zp;               /* r = p */
+            for (c = node + 1; c < M; c++) if (parent[c] == node) has_child = 1;
+            if (has_child) {
+                lzq = orc_softmax_weights(ql, V, T, q, &Zq);
+                if (lzq == -INFINITY) { bad = 1; break; }
+                for (v = 0; v < V; v++) q[v] /= Zq;           /* q of the children */
+            }
+            for (c = node + 1; c < M && has_child; c++) {
+                int x;
+                double rx, qx;
+                if (parent[c] != node) continue;
+                x = tok[c];
+                rx = r[x];
+                qx = q[x];
+                test_ratio[c] = qx > 0.0 ? (rx / qx < 1.0 ? rx / qx : 1.0) : (rx > 0.0 ? 1.0 : 0.0);
+                if (u_node[c] * qx < rx) { accepted = c; break; }
+                /* failure: r <- normalize(max(0, r - q)) */
+                Zr = 0.0;
+                for (v = 0; v < V; v++) {
+                    double d = r[v] - q[v];
+                    r[v] = d > 0.0 ? d : 0.0;
+                    Zr += r[v];
+                }
+                if (!(Zr > 0.0)) { stop_fallback = 1; break; }
+                for (v = 0; v < V; v++) r[v] /= Zr;
+            }
+            if (accepted < 0) {
+                double Z;
+                if (stop_fallback) {
+                    *fallback = 1;
+                    orc_softmax_weights(pl, V, T, w, &Z);
+                    final_tok = orc_inverse_cdf(w, V, Z, u_final, final_thr, final_margin);
+                } else {
+                    Z = 0.0;
+                    for (v = 0; v < V; v++) { w[v] = r[v]; Z += w[v]; }
+                    final_tok = orc_inverse_cdf(w, V, Z, u_final, final_thr, final_margin);
+                }
+                break;
+            }
+        }
+        path[n] = accepted;
+        out[n] = tok[accepted];
+        n++;
+        node = accepted;
+    }
+    if (bad) {
+        for (v = 0; v <= M; v++) out[v] = -1;
+        for (v = 0; v < M; v++) path[v] = -1;
+        free(r); free(q); free(w);
+        return -1;
+    }
+    out[n] = final_tok;
+    *n_acc = n;
+    free(r); free(q); free(w);
+    return 0;
 }
 
 /* ------------------------------------------------------------------------ */
