@@ -88,6 +88,9 @@ def load_library():
     lib.spec_prefix_schedule.restype = i32
     lib.spec_tree_select.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
     lib.spec_tree_select.restype = i32
+    lib.spec_verify_tree.argtypes = [vp, i32, vp, i32, vp, vp, vp, i32, i32, i32, f32, vp, u64,
+                                     u32, vp, vp, vp, vp]
+    lib.spec_verify_tree.restype = i32
     lib.spec_draft_status.argtypes = [vp, sz, i32, i32, i32, i32, vp, vp]
     lib.spec_draft_status.restype = i32
     lib.spec_draft_set_poll_limit.argtypes = [u32]
@@ -520,6 +523,51 @@ def spec_tree_select(parent, c, n, *, out=None, stream=None):
     st = lib.spec_tree_select(_ptr(parent), _ptr(c), R, M, int(n), _ptr(out["sel"]),
                               _ptr(out.get("score")), _stream(stream))
     _check(st, "spec_tree_select")
+    return out
+
+
+@_on_stream
+def spec_verify_tree(P, Q, parent, tokens, T=1.0, *, n_nodes=None, uniforms=None, seed=0,
+                     offset=0, want_path=True, out=None, stream=None):
+    """Verification of tree drafts.  P, Q [B, M + 1, V] (row 0 the root, row
+    1 + v node v), parent and tokens int32 [B, M] (parents first, -1: child of
+    the root), n_nodes int32 [B] or None.  Returns dict(accepted int32 [B],
+    out_tokens int32 [B, M + 1], path int32 [B, M])."""
+    lib = load_library()
+    _dev(P, "P")
+    if P.dim() != 3:
+        raise SpecError("P must be [B, M + 1, V]")
+    B, M1, V = P.shape
+    M = M1 - 1
+    if M > 0:
+        for t, n in ((Q, "Q"), (parent, "parent"), (tokens, "tokens")):
+            if t is None:
+                raise SpecError(f"{n} is required when M > 0")
+            _dev(t, n)
+        if Q.shape != P.shape:
+            raise SpecError("Q must be [B, M + 1, V] like P")
+        for t, n in ((parent, "parent"), (tokens, "tokens")):
+            if t.dtype != torch.int32 or t.shape != (B, M):
+                raise SpecError(f"{n} must be int32 [B, M]")
+    if n_nodes is not None:
+        _dev(n_nodes, "n_nodes")
+        if n_nodes.dtype != torch.int32 or n_nodes.shape != (B,):
+            raise SpecError("n_nodes must be int32 [B]")
+    if uniforms is not None and (uniforms.dtype != torch.float32 or uniforms.shape != (B, M + 1)):
+        raise SpecError("uniforms must be float32 [B, M + 1]")
+    dev = P.device
+    if out is None:
+        out = dict(accepted=torch.empty(B, dtype=torch.int32, device=dev),
+                   out_tokens=torch.empty((B, M + 1), dtype=torch.int32, device=dev))
+        if want_path:
+            out["path"] = torch.empty((B, max(M, 1)), dtype=torch.int32, device=dev)
+    st = lib.spec_verify_tree(
+        _ptr(P), _dtype_code(P, "P"), _ptr(Q) if M > 0 else None,
+        _dtype_code(Q, "Q") if M > 0 else SPEC_F32, _ptr(parent) if M > 0 else None,
+        _ptr(tokens) if M > 0 else None, _ptr(n_nodes), B, M, V, float(T), _ptr(uniforms),
+        seed, offset, _ptr(out["accepted"]), _ptr(out["out_tokens"]), _ptr(out.get("path")),
+        _stream(stream))
+    _check(st, "spec_verify_tree")
     return out
 
 

@@ -15,7 +15,7 @@ LIB = os.path.join(HERE, "libspecdec.so")
 OBJDIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["draft_kernels.hip", "draft_persist.hip", "verify_kernels.hip", "residual_kernels.hip",
-           "alpha_kernels.hip", "sched_kernels.hip",
+           "alpha_kernels.hip", "sched_kernels.hip", "tree_verify.hip",
            "specdec_api.hip",
            "profile.hip"]
 

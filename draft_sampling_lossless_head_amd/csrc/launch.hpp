@@ -282,6 +282,29 @@ struct TreeArgs {
 };
 hipError_t tree_select_launch(const TreeArgs& a, hipStream_t s);
 
+// Verification of R tree drafts of M <= kTreeVerifyMaxNodes nodes over
+// V <= kTreeVerifyMaxV tokens (tree_verify.hip).
+constexpr int kTreeVerifyMaxNodes = 1024;
+constexpr int kTreeVerifyMaxV = 1 << 20;
+struct TreeVerifyArgs {
+    const void* P;              // [B, M + 1, V] target logits (row 0 the root, 1 + v node v)
+    const void* Q;              // [B, M + 1, V] draft logits of each node's children
+    int p_bf16, q_bf16;
+    const int32_t* parent;      // [B, M] parents first, -1 = a child of the root
+    const int32_t* tokens;      // [B, M] draft token of each node
+    const int32_t* n_nodes;     // [B] nodes in use (<= M), or null for M
+    int B, M, V;
+    float invT;
+    int greedy;
+    const float* uniforms;      // [B, M + 1] or null (Philox stream 3)
+    uint64_t seed;
+    uint32_t offset;
+    int32_t* accepted;          // [B] out
+    int32_t* out_tokens;        // [B, M + 1] out
+    int32_t* path;              // [B, M] out or null
+};
+hipError_t verify_tree_launch(const TreeVerifyArgs& a, hipStream_t s);
+
 hipError_t philox_uniforms_launch(uint64_t seed, uint32_t offset, uint32_t stream, int B, int K,
                                   float* out, hipStream_t s);
 

@@ -503,6 +503,50 @@ spec_status_t spec_verify_noalloc(const void* P, int p_dtype, const void* Q, int
 }
 
 
+spec_status_t spec_verify_tree(const void* P, int p_dtype, const void* Q, int q_dtype,
+                               const int32_t* parent, const int32_t* tokens, const int32_t* n_nodes,
+                               int B, int M, int V, float T, const float* uniforms, uint64_t seed,
+                               uint32_t offset, int32_t* accepted, int32_t* out_tokens,
+                               int32_t* path, void* stream) {
+    g_err.clear();
+    if (B < 0 || M < 0) return fail(SPEC_ERR_INVALID, "B and M must be >= 0");
+    if (V <= 0 || V > kTreeVerifyMaxV) return fail(SPEC_ERR_INVALID, "V must be in [1, 2^20]");
+    if (M > kTreeVerifyMaxNodes) return fail(SPEC_ERR_UNSUPPORTED, "M must be <= 1024");
+    if (spec_status_t st = check_T(T)) return st;
+    if (!dtype_ok(p_dtype) || !dtype_ok(q_dtype)) return fail(SPEC_ERR_UNSUPPORTED, "dtype must be SPEC_F32 or SPEC_BF16");
+    if (B == 0) return SPEC_OK;
+    if (!P || !accepted || !out_tokens)
+        return fail(SPEC_ERR_INVALID, "null required pointer (P, accepted, out_tokens)");
+    if (M > 0 && (!Q || !parent || !tokens))
+        return fail(SPEC_ERR_INVALID, "null required pointer (Q, parent, tokens)");
+    if (!aligned16(P) || (Q && !aligned16(Q)))
+        return fail(SPEC_ERR_UNSUPPORTED, "P and Q must be 16-byte aligned");
+    TreeVerifyArgs a{};
+    a.P = P;
+    a.p_bf16 = p_dtype == SPEC_BF16;
+    a.Q = Q;
+    a.q_bf16 = q_dtype == SPEC_BF16;
+    a.parent = parent;
+    a.tokens = tokens;
+    a.n_nodes = n_nodes;
+    a.B = B;
+    a.M = M;
+    a.V = V;
+    a.greedy = T == 0.0f;
+    a.invT = a.greedy ? 1.0f : 1.0f / T;
+    a.uniforms = uniforms;
+    a.seed = seed;
+    a.offset = offset;
+    a.accepted = accepted;
+    a.out_tokens = out_tokens;
+    a.path = path;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* t = prof_begin("verify_tree", s);
+    hipError_t e = verify_tree_launch(a, s);
+    prof_end(t, s);
+    return e == hipSuccess ? SPEC_OK : hip_fail(e, "verify_tree");
+}
+
 spec_status_t spec_acceptance_rate(const void* P, int p_dtype, const void* Q, int q_dtype,
                                    const int32_t* lens, const int64_t* p_row_off,
                                    const int64_t* q_row_off, int B, int gamma_max, int V, float T,

@@ -1,0 +1,372 @@
+// Verification of a tree draft ("Speculative Decoding Part 1", section on
+// spending the draft budget on a tree instead of a chain: the branches of a
+// tree of continuations are verified in one target pass; the acceptance rule
+// of the section on the acceptance rule keeps the output lossless).
+//
+// Recursive rejection over siblings: the walk starts at the root with target
+// law r = p; the children of the current node are tested in increasing index,
+// child c (token x) passing iff u_c q(x) < r(x) with q the draft law the
+// children were drawn from.  A pass emits x and moves the walk to c (r = p of
+// c); a failure sets r <- normalize(max(0, r - q)) and tests the next child.
+// When every child has failed the final token is drawn from r; a node without
+// children draws a bonus token from its p.  T == 0: the first child holding
+// the argmax of p passes; the final token is that argmax.
+//
+// After j failures the residual is r_j = max(0, p - c_j q) / W_j with c_0 = 0,
+// W_0 = 1, c_{j+1} = c_j + W_j and W_{j+1} = sum_v max(0, p(v) - c_{j+1} q(v))
+// (the same law as the repeated normalisation, one pass over the vocabulary per
+// failure and no stored row).
+//
+// One workgroup of 512 threads per request.  Every pass over a row reads it in
+// 8-token vectors spread over the threads; sums are fp64 per lane, the
+// normalisers' (max, sum) pairs fp32 per lane as in the chain's verification.
+// The final draw is a two-level inverse CDF: sums of 512-token segments (one
+// wave each), the segment holding u * W by one wave, then the token inside it.
+#include <cfloat>
+#include <climits>
+
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace specdec {
+
+namespace {
+
+constexpr int kTvThreads = 512;
+constexpr int kTvWaves = kTvThreads / 64;
+constexpr int kTvSeg = 512;                        // tokens per segment of the final draw
+constexpr int kTvMaxSegs = kTreeVerifyMaxV / kTvSeg;
+
+// Eight consecutive logits v0 .. v0 + 7 of a row (fp32); -inf past V.
+template <bool BF>
+__device__ __forceinline__ void load8(const void* base, size_t row_off, int v0, int V, bool vec,
+                                      float x[8]) {
+    if (vec && v0 + 8 <= V) {
+        if constexpr (BF) {
+            const uint4 w = *reinterpret_cast<const uint4*>(
+                static_cast<const uint16_t*>(base) + row_off + v0);
+            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                x[2 * h] = __uint_as_float(ww[h] << 16);
+                x[2 * h + 1] = __uint_as_float(ww[h] & 0xFFFF0000u);
+            }
+        } else {
+            const float* p = static_cast<const float*>(base) + row_off + v0;
+            const float4 a = *reinterpret_cast<const float4*>(p);
+            const float4 b = *reinterpret_cast<const float4*>(p + 4);
+            x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+            x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int v = v0 + e;
+            if (v < V) {
+                if constexpr (BF)
+                    x[e] = __uint_as_float((uint32_t)static_cast<const uint16_t*>(base)[row_off + v] << 16);
+                else
+                    x[e] = static_cast<const float*>(base)[row_off + v];
+            } else {
+                x[e] = -INFINITY;
+            }
+        }
+    }
+}
+
+template <bool BF>
+__device__ __forceinline__ float load1(const void* base, size_t idx) {
+    if constexpr (BF) return __uint_as_float((uint32_t)static_cast<const uint16_t*>(base)[idx] << 16);
+    else return static_cast<const float*>(base)[idx];
+}
+
+struct TvShared {
+    int parent[kTreeVerifyMaxNodes];
+    int tok[kTreeVerifyMaxNodes];
+    double segsum[kTvMaxSegs];
+    float red_m[2][kTvWaves];
+    float red_s[2][kTvWaves];
+    int red_i[kTvWaves];
+    double red_d[kTvWaves];
+};
+
+// exp(y - lz) with the fp64 normaliser lz carried as a (hi, lo) float pair.
+__device__ __forceinline__ float exp_rel(float y, float hi, float lo) {
+    return __expf((y - hi) - lo);
+}
+
+// Block-wide sum of one fp64 value per thread; every thread gets the total
+// (the partials are merged in the same order in every thread).
+__device__ __forceinline__ double block_sum(TvShared& sh, double x) {
+    x = wave_sum_f64(x);
+    const int wave = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) sh.red_d[wave] = x;
+    __syncthreads();
+    double t = 0.0;
+#pragma unroll
+    for (int w = 0; w < kTvWaves; ++w) t += sh.red_d[w];
+    return t;
+}
+
+template <bool PB, bool QB>
+__global__ __launch_bounds__(kTvThreads) void verify_tree_kernel(TreeVerifyArgs a) {
+    __shared__ TvShared sh;
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int M = a.M, V = a.V;
+    const float invT = a.invT;
+    int32_t* out = a.out_tokens + (size_t)b * (M + 1);
+    int32_t* path = a.path ? a.path + (size_t)b * M : nullptr;
+    const int nn = a.n_nodes ? a.n_nodes[b] : M;
+
+    // The tree into LDS, checked: parents first, tokens in range.
+    bool bad = nn < 0 || nn > M;
+    for (int v = tid; v < M && !bad; v += kTvThreads) {
+        const int pa = a.parent[(size_t)b * M + v];
+        const int tk = a.tokens[(size_t)b * M + v];
+        sh.parent[v] = pa;
+        sh.tok[v] = tk;
+        if (v < nn && (pa < -1 || pa >= v || tk < 0 || tk >= V)) bad = true;
+    }
+    bad = __syncthreads_or(bad);
+
+    const size_t rows_b = (size_t)b * (M + 1);
+    const bool pvec = PB ? (V % 8 == 0) : (V % 4 == 0);
+    const bool qvec = QB ? (V % 8 == 0) : (V % 4 == 0);
+    const int nvec = (V + 7) / 8;
+
+    int node = -1, n = 0, final_tok = -1;
+    while (!bad) {
+        const size_t prow = (rows_b + (size_t)(node + 1)) * V;
+        const size_t qrow = prow;   // Q has the same [B, M + 1, V] layout
+        bool has_child = false;
+        for (int c = node + 1; c < nn; ++c)
+            if (sh.parent[c] == node) { has_child = true; break; }
+
+        if (a.greedy) {
+            // argmax of the node's target row, lowest id on ties
+            float m = -INFINITY;
+            int idx = INT_MAX;
+            for (int i = tid; i < nvec; i += kTvThreads) {
+                float x[8];
+                load8<PB>(a.P, prow, 8 * i, V, pvec, x);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) merge_arg(m, idx, x[e], 8 * i + e);
+            }
+            wave_argmax_dpp(m, idx);
+            __syncthreads();
+            if (lane == 0) { sh.red_m[0][wave] = m; sh.red_i[wave] = idx; }
+            __syncthreads();
+            m = sh.red_m[0][0];
+            idx = sh.red_i[0];
+            for (int w = 1; w < kTvWaves; ++w) merge_arg(m, idx, sh.red_m[0][w], sh.red_i[w]);
+            if (m == -INFINITY) { bad = true; break; }
+            int acc = -1;
+            for (int c = node + 1; c < nn; ++c)
+                if (sh.parent[c] == node && sh.tok[c] == idx) { acc = c; break; }
+            if (acc < 0) { final_tok = idx; break; }
+            if (tid == 0 && path) path[n] = acc;
+            if (tid == 0) out[n] = sh.tok[acc];
+            ++n;
+            node = acc;
+            continue;
+        }
+
+        // Normalisers of the node's target row and, with children, draft row.
+        float mp = -INFINITY, sp = 0.0f, mq = -INFINITY, sq = 0.0f;
+        for (int i = tid; i < nvec; i += kTvThreads) {
+            float x[8];
+            load8<PB>(a.P, prow, 8 * i, V, pvec, x);
+            float m8 = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) m8 = fmaxf(m8, x[e] * invT);
+            if (m8 != -INFINITY) {
+                float s8 = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s8 += __expf(x[e] * invT - m8);
+                merge_ms(mp, sp, m8, s8, 1.0f);
+            }
+            if (has_child) {
+                load8<QB>(a.Q, qrow, 8 * i, V, qvec, x);
+                m8 = -INFINITY;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) m8 = fmaxf(m8, x[e] * invT);
+                if (m8 != -INFINITY) {
+                    float s8 = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) s8 += __expf(x[e] * invT - m8);
+                    merge_ms(mq, sq, m8, s8, 1.0f);
+                }
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            merge_ms(mp, sp, __shfl_xor(mp, off), __shfl_xor(sp, off), 1.0f);
+            merge_ms(mq, sq, __shfl_xor(mq, off), __shfl_xor(sq, off), 1.0f);
+        }
+        __syncthreads();
+        if (lane == 0) {
+            sh.red_m[0][wave] = mp; sh.red_s[0][wave] = sp;
+            sh.red_m[1][wave] = mq; sh.red_s[1][wave] = sq;
+        }
+        __syncthreads();
+        mp = sh.red_m[0][0]; sp = sh.red_s[0][0];
+        mq = sh.red_m[1][0]; sq = sh.red_s[1][0];
+        for (int w = 1; w < kTvWaves; ++w) {
+            merge_ms(mp, sp, sh.red_m[0][w], sh.red_s[0][w], 1.0f);
+            merge_ms(mq, sq, sh.red_m[1][w], sh.red_s[1][w], 1.0f);
+        }
+        if (mp == -INFINITY || (has_child && mq == -INFINITY)) { bad = true; break; }
+        const double lzp = (double)mp + log((double)sp);
+        const double lzq = has_child ? (double)mq + log((double)sq) : 0.0;
+        const float lzp_hi = (float)lzp, lzp_lo = (float)(lzp - (double)lzp_hi);
+        const float lzq_hi = (float)lzq, lzq_lo = (float)(lzq - (double)lzq_hi);
+
+        // Ratio tests of the children in index order against r = max(0, p - c q) / W.
+        double cc = 0.0, W = 1.0;
+        int acc = -1;
+        bool fallback = false;
+        for (int ch = node + 1; ch < nn && has_child; ++ch) {
+            if (sh.parent[ch] != node) continue;
+            const int x = sh.tok[ch];
+            const double px = exp((double)load1<PB>(a.P, prow + x) * (double)invT - lzp);
+            const double qx = exp((double)load1<QB>(a.Q, qrow + x) * (double)invT - lzq);
+            const double rx = fmax(0.0, px - cc * qx) / W;
+            const float u = a.uniforms ? a.uniforms[rows_b + ch]
+                                       : counter_uniform(a.seed, a.offset, (uint32_t)b, (uint32_t)ch, 3);
+            if ((double)u * qx < rx) { acc = ch; break; }
+            // failure: the residual's next mass
+            cc += W;
+            const float cf = (float)cc;
+            double part = 0.0;
+            for (int i = tid; i < nvec; i += kTvThreads) {
+                float xp[8], xq[8];
+                load8<PB>(a.P, prow, 8 * i, V, pvec, xp);
+                load8<QB>(a.Q, qrow, 8 * i, V, qvec, xq);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float d = exp_rel(xp[e] * invT, lzp_hi, lzp_lo) -
+                                    cf * exp_rel(xq[e] * invT, lzq_hi, lzq_lo);
+                    part += d > 0.0f ? (double)d : 0.0;
+                }
+            }
+            W = block_sum(sh, part);
+            if (!(W > 0.0)) { fallback = true; break; }
+        }
+        if (acc >= 0) {
+            if (tid == 0 && path) path[n] = acc;
+            if (tid == 0) out[n] = sh.tok[acc];
+            ++n;
+            node = acc;
+            continue;
+        }
+
+        // Final draw: weights max(0, p - c q) (residual after failures) or p.
+        const bool resid = has_child && !fallback && cc > 0.0;
+        const float cf = resid ? (float)cc : 0.0f;
+        const float uf = a.uniforms ? a.uniforms[rows_b + M]
+                                    : counter_uniform(a.seed, a.offset, (uint32_t)b, (uint32_t)M, 3);
+        auto weights8 = [&](int v0, float w[8]) {
+            float xp[8], xq[8];
+            load8<PB>(a.P, prow, v0, V, pvec, xp);
+            if (resid) load8<QB>(a.Q, qrow, v0, V, qvec, xq);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float d = exp_rel(xp[e] * invT, lzp_hi, lzp_lo);
+                if (resid) d -= cf * exp_rel(xq[e] * invT, lzq_hi, lzq_lo);
+                w[e] = (v0 + e < V && d > 0.0f) ? d : 0.0f;
+            }
+        };
+        const int nseg = (V + kTvSeg - 1) / kTvSeg;
+        for (int sg = wave; sg < nseg; sg += kTvWaves) {
+            float w[8];
+            weights8(sg * kTvSeg + 8 * lane, w);
+            double t = 0.0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) t += (double)w[e];
+            t = wave_sum_f64(t);
+            if (lane == 0) sh.segsum[sg] = t;
+        }
+        __syncthreads();
+        if (wave == 0) {
+            // segments per lane, contiguous: lane l holds segments l*per .. l*per + per - 1
+            const int per = (nseg + 63) / 64;
+            double ls = 0.0;
+            for (int j = 0; j < per; ++j) {
+                const int sg = lane * per + j;
+                if (sg < nseg) ls += sh.segsum[sg];
+            }
+            const double total = readlane_f64(wave_inclusive_scan_f64(ls), 63);
+            const double thr = (double)uf * total;
+            double rem;
+            const int L = wave_pick(ls, thr, rem);
+            // walk lane L's segments (uniform: every lane reads the same LDS words)
+            int sel = -1, lastpos = -1;
+            for (int j = 0; j < per; ++j) {
+                const int sg = L * per + j;
+                if (sg >= nseg) break;
+                const double sv = sh.segsum[sg];
+                if (sv > 0.0) {
+                    lastpos = sg;
+                    if (rem < sv) { sel = sg; break; }
+                    rem -= sv;
+                }
+            }
+            if (sel < 0) { sel = lastpos < 0 ? 0 : lastpos; rem = INFINITY; }
+            float w[8];
+            weights8(sel * kTvSeg + 8 * lane, w);
+            double t = 0.0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) t += (double)w[e];
+            double rem2;
+            const int L2 = wave_pick(t, rem, rem2);
+            // the 8 weights of lane L2, uniform
+            int tok = -1, lastp = -1;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const double we = (double)readlane_f32(w[e], L2);
+                if (we > 0.0) {
+                    lastp = e;
+                    if (tok < 0) {
+                        if (rem2 < we) tok = e;
+                        else rem2 -= we;
+                    }
+                }
+            }
+            if (tok < 0) tok = lastp < 0 ? 0 : lastp;
+            if (lane == 0) sh.red_i[0] = min(sel * kTvSeg + 8 * L2 + tok, V - 1);
+        }
+        __syncthreads();
+        final_tok = sh.red_i[0];
+        break;
+    }
+
+    if (bad) {
+        for (int j = tid; j <= M; j += kTvThreads) out[j] = -1;
+        if (path) for (int j = tid; j < M; j += kTvThreads) path[j] = -1;
+        if (tid == 0) a.accepted[b] = -1;
+        return;
+    }
+    __syncthreads();   // the path's writes by thread 0 precede the tail
+    for (int j = n + 1 + tid; j <= M; j += kTvThreads) out[j] = -1;
+    if (path) for (int j = n + tid; j < M; j += kTvThreads) path[j] = -1;
+    if (tid == 0) {
+        out[n] = final_tok;
+        a.accepted[b] = n;
+    }
+}
+
+}  // namespace
+
+hipError_t verify_tree_launch(const TreeVerifyArgs& a, hipStream_t s) {
+    if (a.B == 0) return hipSuccess;
+    const dim3 grid((unsigned)a.B), block(kTvThreads);
+    if (a.p_bf16 && a.q_bf16) hipLaunchKernelGGL((verify_tree_kernel<true, true>), grid, block, 0, s, a);
+    else if (a.p_bf16) hipLaunchKernelGGL((verify_tree_kernel<true, false>), grid, block, 0, s, a);
+    else if (a.q_bf16) hipLaunchKernelGGL((verify_tree_kernel<false, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((verify_tree_kernel<false, false>), grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace specdec

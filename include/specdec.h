@@ -339,6 +339,57 @@ spec_status_t spec_verify_markov(
 
 /*
  * ---------------------------------------------------------------------------
+ * Verification of a tree draft  [VESSL "Speculative Decoding Part 1",
+ * section "γ 재배분: 체인 대신 트리" (a tree of continuations verified in one
+ * target pass), with the acceptance rule of section "수락 규칙"]
+ * ---------------------------------------------------------------------------
+ * Request b holds a tree of n = n_nodes ? n_nodes[b] : M draft nodes, listed
+ * parents first: parent[b, v] in [-1, v) (-1: a child of the root, the last
+ * accepted token), tokens[b, v] its draft token in [0, V).  Row 0 of P and Q
+ * belongs to the root and row 1 + v to node v (rows of unused nodes are not
+ * read): the P row is the target's next-token logits after the path to that
+ * node, the Q row the draft logits its children were drawn from (one
+ * independent draw per child).  With p = softmax(P row / T) and q =
+ * softmax(Q row / T) of the current node, starting at the root with r = p:
+ *     test the node's children in increasing index; child c (token x) passes
+ *     iff u_c * q(x) < r(x): emit x, move to c, r = p of c, repeat;
+ *     on a failure r <- normalize(max(0, r - q)) and test the next child;
+ *     no child passes: final ~ r (inverse CDF with u_final); a node without
+ *     children: final ~ p of that node (bonus token).
+ * T == 0: the first child whose token is the argmax of p passes (lowest id
+ * on ties); the final token is that argmax.  If a residual has no mass after
+ * rounding the final token is drawn from the node's p.  Every emitted token
+ * follows the target's law given the tokens before it; a chain-shaped tree
+ * (parent[v] = v - 1) is spec_verify's rule.
+ *
+ * P, Q       [B, M + 1, V] dtype p_dtype / q_dtype (f32 or bf16), 16-byte
+ *            aligned.  Q may be NULL when M == 0.
+ * parent, tokens  [B, M] int32 (NULL allowed when M == 0)
+ * n_nodes    [B] int32 in [0, M], or NULL for M
+ * uniforms   [B, M + 1] optional: column v < M is node v's ratio test,
+ *            column M the final draw; NULL: Philox stream 3 (index v, and M
+ *            for the final draw)
+ * accepted   [B] out int32: number of accepted nodes (-1 for a request with
+ *            a parent out of range, a token outside [0, V), n_nodes outside
+ *            [0, M] or a row on the walk without a finite logit)
+ * out_tokens [B, M + 1] out int32: the accepted nodes' tokens, the final
+ *            token, then -1 (all -1 for an invalid request)
+ * path       [B, M] optional out int32: the accepted node ids, then -1
+ * One workgroup per request; every tested sibling after the first costs
+ * one pass over the node's two rows.  No workspace.
+ * Errors: SPEC_ERR_INVALID (null required pointers, B or M < 0, V outside
+ * [1, 2^20], T < 0 or NaN), SPEC_ERR_UNSUPPORTED (dtype, M > 1024,
+ * misaligned P or Q), SPEC_ERR_HIP (launch).
+ */
+spec_status_t spec_verify_tree(const void *P, int p_dtype, const void *Q, int q_dtype,
+                               const int32_t *parent, const int32_t *tokens,
+                               const int32_t *n_nodes, int B, int M, int V, float T,
+                               const float *uniforms, uint64_t seed, uint32_t offset,
+                               int32_t *accepted, int32_t *out_tokens, int32_t *path,
+                               void *stream);
+
+/*
+ * ---------------------------------------------------------------------------
  * Acceptance rate per drafted position  [VESSL "Speculative Decoding Part 1",
  * section "수락 규칙": a token drawn from q passes the ratio test with
  * probability alpha = sum_v min(p(v), q(v)) = 1 - D_TV(p, q)]

@@ -102,7 +102,7 @@ def _L():
                                    i, i, d, d, d, d, d, d, i]
         lib.orc_verify.restype = ctypes.c_int
         lib.orc_verify_tree.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_double, i, i,
-                                        d, d, d, ctypes.c_double, i, i, i, d, d, d, i]
+                                        d, d, d, ctypes.c_double, i, i, i, d, d, d, i, d]
         lib.orc_verify_tree.restype = ctypes.c_int
         lib.orc_confidence.argtypes = [d, ctypes.c_int, d, ctypes.c_int, d]
         lib.orc_confidence.restype = ctypes.c_double
@@ -313,7 +313,7 @@ def tree_uniforms(seed, offset, B, M):
     return out
 
 
-def verify_tree(P, Q, parent, tok, T, u_node, u_final):
+def verify_tree(P, Q, parent, tok, T, u_node, u_final, want_weights=False):
     """One request's tree: P, Q [M + 1, V] logits (row 0 the root, row 1 + v
     node v), parent [M] (parents first, -1 = child of the root), tok [M]
     draft tokens, u_node [M] ratio-test uniforms, u_final.  Returns None for
@@ -330,16 +330,18 @@ def verify_tree(P, Q, parent, tok, T, u_node, u_final):
     ratio = np.zeros(max(M, 1))
     fthr, fmar = ctypes.c_double(), ctypes.c_double()
     fb = ctypes.c_int()
+    fw = np.zeros(V) if want_weights else None
     st = _L().orc_verify_tree(V, M, float(T), _ip(par if M else np.zeros(1, np.int32)),
                               _ip(tk if M else np.zeros(1, np.int32)), _dp(P), _dp(Q), _dp(un),
                               float(u_final), ctypes.byref(n), _ip(path), _ip(out), _dp(ratio),
-                              ctypes.byref(fthr), ctypes.byref(fmar), ctypes.byref(fb))
+                              ctypes.byref(fthr), ctypes.byref(fmar), ctypes.byref(fb),
+                              _dp(fw) if want_weights else None)
     if st == -1:
         return None
     if st != 0:
         raise ValueError(f"oracle verify_tree failed with status {st}")
     return dict(n=n.value, path=path[:M], out=out, test_ratio=ratio[:M], final_thr=fthr.value,
-                final_margin=fmar.value, fallback=fb.value)
+                final_margin=fmar.value, fallback=fb.value, final_w=fw)
 
 
 # --------------------------------------------------------------------------

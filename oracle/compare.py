@@ -152,3 +152,67 @@ def compare_verify_request(P, Q, draft, T, u_test, u_final, gpu, what, tally):
     _check_draw(w, final_o, final_g, u_final, f"{what} final draw (n={n_o})")
     tally.boundary += 1
     return False
+
+
+def compare_tree_request(P, Q, parent, tok, T, u_node, u_final, gpu, what, tally):
+    """Compare one request's tree verification.  P, Q [M + 1, V] float64 (the
+    exact values both sides received), parent / tok the nodes in use; gpu:
+    dict with accepted (int), out_tokens [M + 1], path [M].
+
+    The walks must agree node by node.  Where they part, the first sibling
+    decided differently must have been a boundary test: its uniform within
+    BAND of the oracle's ratio r(x)/q(x) (T = 0: the node's top-2 logit gap
+    within the fp32 tolerance).  On the same walk the final token must match,
+    or lie within BAND of the oracle's CDF boundary."""
+    M = len(parent)
+    o = orc.verify_tree(P, Q, parent, tok, T, u_node, u_final, want_weights=True)
+    tally.requests += 1
+    out_g = np.asarray(gpu["out_tokens"])
+    n_g = int(gpu["accepted"])
+    if o is None:
+        if n_g != -1 or np.any(out_g != -1):
+            raise AssertionError(f"{what}: invalid tree, GPU accepted {n_g} (expected -1, all -1)")
+        return True
+    tally.fallbacks += o["fallback"]
+    n_o = o["n"]
+    path_g = np.asarray(gpu["path"])[: max(n_g, 0)] if n_g >= 0 else np.zeros(0, np.int64)
+    path_o = o["path"][:n_o]
+    tally.draws += 1
+    if n_g < 0:
+        raise AssertionError(f"{what}: GPU marked a valid tree invalid")
+    k = 0
+    while k < min(n_g, n_o) and path_g[k] == path_o[k]:
+        k += 1
+    if k < n_g or k < n_o:
+        # the walks part after k common nodes: the first sibling decided
+        # differently is the smaller of the two next nodes (or the one side's)
+        nxt = [int(x) for x in (path_g[k] if k < n_g else M, path_o[k] if k < n_o else M)]
+        c = min(nxt)
+        node = int(path_o[k - 1]) if k > 0 else -1
+        if T == 0:
+            l = P[node + 1]
+            top = np.sort(l)[::-1]
+            if not (top[0] - top[1] <= TOL_REL * max(1.0, abs(top[0]))):
+                raise AssertionError(f"{what}: greedy walks part after {k} nodes, logit gap "
+                                     f"{top[0] - top[1]:.3e}")
+        else:
+            ratio = o["test_ratio"][c] if c < M else np.nan
+            if not np.isfinite(ratio) or abs(u_node[c] - ratio) > BAND:
+                raise AssertionError(f"{what}: walks part after {k} nodes at node {c}: uniform "
+                                     f"{u_node[c] if c < M else u_final} vs oracle ratio {ratio}")
+        tally.boundary += 1
+        return False
+    if not np.array_equal(out_g[:n_o], np.asarray(tok)[path_o]):
+        raise AssertionError(f"{what}: emitted tokens are not the accepted nodes' tokens")
+    if np.any(out_g[n_o + 1:] != -1) or np.any(np.asarray(gpu["path"])[n_o:M] != -1):
+        raise AssertionError(f"{what}: slots after the final token / path must be -1")
+    final_g, final_o = int(out_g[n_o]), int(o["out"][n_o])
+    if final_g == final_o:
+        return True
+    last = int(path_o[n_o - 1]) if n_o > 0 else -1
+    if T == 0:
+        _check_greedy(P[last + 1], final_o, final_g, f"{what} greedy final")
+    else:
+        _check_draw(o["final_w"], final_o, final_g, u_final, f"{what} final draw (n={n_o})")
+    tally.boundary += 1
+    return False

@@ -493,14 +493,15 @@ int orc_verify(int V, int L, double T,
  * after); out[0..n-1] their tokens, out[n] the final token (-1 after;
  * out has M + 1 entries); test_ratio[c] = r(x)/q(x) (capped at 1) of every
  * tested child c, NaN for children never tested; *final_thr, *final_margin
- * as orc_inverse_cdf (T == 0: the argmax's logit gap).
+ * as orc_inverse_cdf (T == 0: the argmax's logit gap); final_w (V entries,
+ * or NULL) receives the weights the final token was drawn from (T > 0).
  * Returns 0; -1 for an invalid tree (parent out of range), a token outside
  * [0, V) or a tested row without a finite logit (then n_acc = -1 and every
  * output -1). */
 int orc_verify_tree(int V, int M, double T, const int *parent, const int *tok,
                     const double *P, const double *Q, const double *u_node, double u_final,
                     int *n_acc, int *path, int *out, double *test_ratio,
-                    double *final_thr, double *final_margin, int *fallback)
+                    double *final_thr, double *final_margin, int *fallback, double *final_w)
 {
     double *r = (double *)malloc(sizeof(double) * (size_t)(V > 0 ? V : 1));
     double *q = (double *)malloc(sizeof(double) * (size_t)(V > 0 ? V : 1));
@@ -575,6 +576,8 @@ int orc_verify_tree(int V, int M, double T, const int *parent, const int *tok,
                     for (v = 0; v < V; v++) { w[v] = r[v]; Z += w[v]; }
                     final_tok = orc_inverse_cdf(w, V, Z, u_final, final_thr, final_margin);
                 }
+                if (final_w)
+                    for (v = 0; v < V; v++) final_w[v] = w[v];
                 break;
             }
         }

@@ -38,7 +38,8 @@ def test_header_declares_the_boundary():
               "spec_verify_markov_workspace_size", "spec_draft_set_persistent",
               "spec_draft_set_poll_limit", "spec_acceptance_rate", "spec_confidence_head",
               "spec_prefix_schedule", "spec_prefix_schedule_workspace_size", "spec_tree_select",
-              "spec_draft_status"):
+              "spec_draft_status", "spec_verify_tree", "spec_verify_noalloc",
+              "spec_verify_noalloc_max_bytes"):
         assert n in names
 
 
@@ -320,3 +321,51 @@ def test_draft_status_validation(lib):
     assert lib.spec_draft_status(fake, 64, 128, 16, 151936, 256, fake, None) == SPEC_ERR_WORKSPACE
     assert lib.spec_draft_status(ctypes.c_void_p(4096 + 16), need, 128, 16, 151936, 256, fake,
                                  None) == SPEC_ERR_WORKSPACE
+
+
+def test_verify_tree_validation(lib):
+    fake = ctypes.c_void_p(4096)
+    base = dict(P=fake, p_dtype=1, Q=fake, q_dtype=1, parent=fake, tokens=fake, n_nodes=None,
+                B=2, M=5, V=1000, T=1.0, uniforms=None, seed=0, offset=0, accepted=fake,
+                out=fake, path=None, stream=None)
+
+    def call(**kw):
+        a = dict(base)
+        a.update(kw)
+        return lib.spec_verify_tree(*a.values())
+
+    assert call(P=None) == SPEC_ERR_INVALID
+    assert call(Q=None) == SPEC_ERR_INVALID
+    assert call(parent=None) == SPEC_ERR_INVALID
+    assert call(tokens=None) == SPEC_ERR_INVALID
+    assert call(accepted=None) == SPEC_ERR_INVALID
+    assert call(B=-1) == SPEC_ERR_INVALID
+    assert call(M=-1) == SPEC_ERR_INVALID
+    assert call(V=0) == SPEC_ERR_INVALID
+    assert call(V=(1 << 20) + 1) == SPEC_ERR_INVALID
+    assert call(T=-1.0) == SPEC_ERR_INVALID
+    assert call(M=1025) == SPEC_ERR_UNSUPPORTED
+    assert call(p_dtype=5) == SPEC_ERR_UNSUPPORTED
+    assert call(Q=ctypes.c_void_p(4100)) == SPEC_ERR_UNSUPPORTED
+    assert call(B=0) == SPEC_OK
+
+
+def test_verify_noalloc_validation(lib):
+    fake = ctypes.c_void_p(4096)
+    base = dict(P=fake, p_dtype=1, Q=fake, q_dtype=0, draft=fake, lens=None, p_off=None,
+                q_off=None, B=2, G=3, V=1000, T=1.0, uniforms=None, seed=0, offset=0,
+                accepted=fake, out=fake, p_logZ=None, q_logZ=None, ap=None, stream=None)
+
+    def call(**kw):
+        a = dict(base)
+        a.update(kw)
+        return lib.spec_verify_noalloc(*a.values())
+
+    assert lib.spec_verify_noalloc_max_bytes() == 16 << 20
+    assert call(P=None) == SPEC_ERR_INVALID
+    assert call(G=-1) == SPEC_ERR_INVALID
+    assert call(q_dtype=3) == SPEC_ERR_UNSUPPORTED
+    assert call(B=0) == SPEC_OK
+    # more scratch than the fixed array: refused on the host, nothing launched
+    assert call(B=65536, G=8, V=262144) == SPEC_ERR_WORKSPACE
+    assert "spec_verify_noalloc" in lib.spec_last_error().decode()

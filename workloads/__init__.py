@@ -13,6 +13,7 @@ from .gen import (  # noqa: F401
     make_rnn,
     make_schedule,
     make_trees,
+    make_tree_verify,
     make_verify_only,
     packed_offsets,
 )

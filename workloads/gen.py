@@ -286,3 +286,38 @@ def make_repeated_markov(B, gamma, V, r, seed, scale=2.0, sigma=1.0, w_std=0.3, 
                 U=_store(np.ascontiguousarray(U), dtype), P=_store(np.ascontiguousarray(P), dtype),
                 W1=_store(W1, dtype), W2=_store(W2, dtype), x0=x0,
                 U1=_store(U1, dtype), P1=_store(P1, dtype))
+
+
+# Stream id of the tree-verification workload.
+_S_TREEV = 8
+
+
+def make_tree_verify(B, M, V, seed, dtype="bf16", scale=4.0, zipf=1.1, sigma=1.0, levels=4,
+                     n_nodes=False):
+    """Tree drafts with their logit rows: per request, M nodes parents first
+    over `levels` depths (a node's parent uniform over the level above, the
+    root for the first level), one Zipf+Gaussian draft row Q per node (row 0
+    the root, row 1 + v node v; the recipe of the chain workloads) and a target
+    row P = Q + sigma * N(0, 1); random draft tokens (tests replace them with
+    draws from the parent's draft row); with n_nodes, a count of nodes in use
+    uniform on 0..M."""
+    g = _rng(seed, _S_TREEV)
+    zb = _zipf_bias(V, zipf)
+    bounds = [(M * d) // levels for d in range(levels + 1)]
+    parent = np.empty((B, M), dtype=np.int32)
+    for d in range(levels):
+        lo, hi = bounds[d], bounds[d + 1]
+        if d == 0 or bounds[d - 1] == bounds[d]:
+            parent[:, lo:hi] = -1
+        else:
+            parent[:, lo:hi] = g.integers(bounds[d - 1], bounds[d], size=(B, hi - lo))
+    Q = np.empty((B, M + 1, V), dtype=np.uint16 if dtype == "bf16" else np.float32)
+    P = np.empty_like(Q)
+    for b in range(B):
+        gb = _rng(seed, _S_TREEV, b + 1)
+        G = gb.standard_normal((M + 1, V), dtype=np.float32) * np.float32(scale) + zb
+        Q[b] = _store(G, dtype)
+        P[b] = _store(G + np.float32(sigma) * gb.standard_normal((M + 1, V), dtype=np.float32), dtype)
+    tok = g.integers(0, V, size=(B, M), dtype=np.int64).astype(np.int32)
+    nn = g.integers(0, M + 1, size=B, dtype=np.int64).astype(np.int32) if n_nodes else None
+    return dict(B=B, M=M, V=V, logit_dtype=dtype, parent=parent, P=P, Q=Q, tokens=tok, n_nodes=nn)
