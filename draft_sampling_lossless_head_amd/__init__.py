@@ -28,6 +28,7 @@ from .api import (  # noqa: F401
     spec_verify,
     spec_verify_markov,
     spec_verify_noalloc,
+    spec_verify_rnn,
     spec_verify_noalloc_max_bytes,
     spec_verify_tree,
     spec_version,

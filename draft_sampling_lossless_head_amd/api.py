@@ -88,6 +88,13 @@ def load_library():
     lib.spec_prefix_schedule.restype = i32
     lib.spec_tree_select.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
     lib.spec_tree_select.restype = i32
+    lib.spec_draft_rnn_cond_offset.argtypes = [i32, i32, i32, i32, i32]
+    lib.spec_draft_rnn_cond_offset.restype = sz
+    lib.spec_verify_rnn_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.spec_verify_rnn_workspace_size.restype = sz
+    lib.spec_verify_rnn.argtypes = [vp, i32, vp, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp, i32,
+                                    i32, i32, f32, vp, u64, u32, vp, vp, vp, vp, vp, sz, vp]
+    lib.spec_verify_rnn.restype = i32
     lib.spec_verify_tree.argtypes = [vp, i32, vp, i32, vp, vp, vp, i32, i32, i32, f32, vp, u64,
                                      u32, vp, vp, vp, vp]
     lib.spec_verify_tree.restype = i32
@@ -283,13 +290,19 @@ def spec_draft_status(workspace, B, gamma, V, r, *, out=None, stream=None):
 
 
 @_on_stream
-def spec_draft_sample_rnn(U, x0, h, W1, W2, Wg, Wc, Wo, T=1.0, *, W2T=None, uniforms=None,
-                          seed=0, offset=0, out=None, workspace=None, stream=None):
-    """RNN-head draft.  h [B, gamma, d]; Wg, Wc, Wo [r, 2r + d]."""
+def spec_draft_sample_rnn(U, x0, h, W1, W2, Wg, Wc, Wo, T=1.0, *, W2T=None, q_free=False,
+                          uniforms=None, seed=0, offset=0, out=None, workspace=None, stream=None):
+    """RNN-head draft.  h [B, gamma, d]; Wg, Wc, Wo [r, 2r + d].  q_free=True
+    writes no q logits; the result then also holds `cond`, the conditioning
+    rows [B, gamma, 3, r] (bf16 bits as int16) inside the draft's workspace
+    (kept alive by the result), for spec_verify_rnn."""
     lib = load_library()
-    for t, n in ((U, "U"), (x0, "x0"), (h, "h"), (W1, "W1"), (W2, "W2"), (Wg, "Wg"), (Wc, "Wc"),
-                 (Wo, "Wo")):
+    for t, n in ((U, "U"), (x0, "x0"), (h, "h"), (W1, "W1"), (Wg, "Wg"), (Wc, "Wc"), (Wo, "Wo")):
         _dev(t, n)
+    if W2 is not None:
+        _dev(W2, "W2")
+    elif W2T is None:
+        raise SpecError("W2 or W2T is required")
     B, gamma, V = U.shape
     r = W1.shape[1]
     d = h.shape[2]
@@ -298,16 +311,75 @@ def spec_draft_sample_rnn(U, x0, h, W1, W2, Wg, Wc, Wo, T=1.0, *, W2T=None, unif
     for t, n in ((Wg, "Wg"), (Wc, "Wc"), (Wo, "Wo")):
         if t.shape != (r, 2 * r + d):
             raise SpecError(f"{n} must be [r, 2r + d]")
-    o = _draft_outputs(B, gamma, V, U.device, out)
+    if W2T is not None:
+        _check_w2t(W2T, r, V)
+    o = _draft_outputs(B, gamma, V, U.device, out, q_free=q_free)
     ws, nws = _workspace(lib.spec_draft_rnn_workspace_size(B, gamma, V, r, d), U.device, workspace)
     st = lib.spec_draft_sample_rnn(
         _ptr(U), _dtype_code(U, "U"), _ptr(x0), _ptr(h), _dtype_code(h, "h"), d, _ptr(W1),
         _ptr(W2), _ptr(W2T), _ptr(Wg), _ptr(Wc), _ptr(Wo), _dtype_code(W1, "W1"), r, B, gamma, V,
         float(T),
-        _ptr(uniforms), seed, offset, _ptr(o["tokens"]), _ptr(o["q_logits"]), _ptr(o.get("q_logZ")),
-        _ptr(o.get("q_tok_prob")), _ptr(ws), nws, _stream(stream))
+        _ptr(uniforms), seed, offset, _ptr(o["tokens"]), _ptr(o.get("q_logits")),
+        _ptr(o.get("q_logZ")), _ptr(o.get("q_tok_prob")), _ptr(ws), nws, _stream(stream))
     _check(st, "spec_draft_sample_rnn")
+    if q_free:
+        off = lib.spec_draft_rnn_cond_offset(B, gamma, V, r, d)
+        nb = B * gamma * 3 * r * 2
+        o["cond"] = ws.view(torch.uint8).reshape(-1)[off:off + nb].view(torch.int16).view(
+            B, gamma, 3, r)
     return o
+
+
+@_on_stream
+def spec_verify_rnn(P, U, cond, W2, draft, q_logZ, q_tok_prob, T=1.0, *, W2T=None,
+                    gamma_max=None, lens=None, p_row_off=None, uniforms=None, seed=0, offset=0,
+                    diagnostics=True, out=None, workspace=None, stream=None):
+    """Verification of a q-free RNN draft: P target logits (dense [B, gamma+1, V]
+    or packed with p_row_off), U and W2 (or W2T) as given to the draft, cond
+    the draft's conditioning rows (the `cond` of spec_draft_sample_rnn's
+    result), the draft's tokens, q_logZ and q_tok_prob [B, gamma]."""
+    lib = load_library()
+    for t, n in ((P, "P"), (U, "U"), (cond, "cond"), (draft, "draft"), (q_logZ, "q_logZ"),
+                 (q_tok_prob, "q_tok_prob")):
+        _dev(t, n)
+    B = draft.shape[0]
+    gamma_max = draft.shape[1] if gamma_max is None else gamma_max
+    V = P.shape[-1]
+    if cond.dim() != 4 or cond.shape[:3] != (B, gamma_max, 3) or cond.element_size() != 2:
+        raise SpecError("cond must be [B, gamma_max, 3, r] 16-bit")
+    r = cond.shape[3]
+    if U.shape != (B, gamma_max, V):
+        raise SpecError("U must be dense [B, gamma_max, V]")
+    for t, n in ((q_logZ, "q_logZ"), (q_tok_prob, "q_tok_prob")):
+        if t.dtype != torch.float32 or t.shape != (B, gamma_max):
+            raise SpecError(f"{n} must be float32 [B, gamma_max]")
+    if draft.dtype != torch.int32 or draft.shape != (B, gamma_max):
+        raise SpecError("draft must be int32 [B, gamma_max]")
+    for t, n, dt in ((lens, "lens", torch.int32), (p_row_off, "p_row_off", torch.int64)):
+        if t is not None:
+            _dev(t, n)
+            if t.dtype != dt or t.shape != (B,):
+                raise SpecError(f"{n} must be {dt} [B]")
+    if W2 is not None:
+        _dev(W2, "W2")
+    if W2T is not None:
+        _check_w2t(W2T, r, V)
+    dev = P.device
+    if out is None:
+        out = dict(accepted=torch.empty(B, dtype=torch.int32, device=dev),
+                   out_tokens=torch.empty((B, gamma_max + 1), dtype=torch.int32, device=dev))
+        if diagnostics:
+            out["p_logZ"] = torch.empty((B, gamma_max + 1), dtype=torch.float32, device=dev)
+            out["accept_prob"] = torch.empty((B, gamma_max), dtype=torch.float32, device=dev)
+    ws, nws = _workspace(lib.spec_verify_rnn_workspace_size(B, gamma_max, V, r), dev, workspace)
+    st = lib.spec_verify_rnn(
+        _ptr(P), _dtype_code(P, "P"), _ptr(U), _dtype_code(U, "U"), _ptr(cond), _ptr(W2),
+        _ptr(W2T), r, _ptr(draft), _ptr(q_logZ), _ptr(q_tok_prob), _ptr(lens), _ptr(p_row_off),
+        B, gamma_max, V, float(T), _ptr(uniforms), seed, offset, _ptr(out["accepted"]),
+        _ptr(out["out_tokens"]), _ptr(out.get("p_logZ")), _ptr(out.get("accept_prob")),
+        _ptr(ws), nws, _stream(stream))
+    _check(st, "spec_verify_rnn")
+    return out
 
 
 @_on_stream

@@ -232,9 +232,10 @@ void draft_tile_mfma(TileParams P) {
     // 4) the contraction (RNN: three bf16 terms of o against the same tile).
 #pragma unroll
     for (int split = 0; split < NS; ++split) {
-        const uint16_t* erow = (MODE == kHeadMarkov)
-                                   ? P.W1 + (size_t)prev * r
-                                   : P.Erows + ((size_t)(b < B ? b : 0) * 3 + split) * r;
+        const uint16_t* erow =
+            (MODE == kHeadMarkov)
+                ? P.W1 + (size_t)prev * r
+                : P.Erows + (((size_t)(b < B ? b : 0) * gamma + (bpos > 0 ? bpos : 0)) * 3 + split) * r;
         bf16x8_t e[16];
 #pragma unroll
         for (int ks = 0; ks < 16; ++ks) {
@@ -1001,6 +1002,9 @@ struct RebuildArgs {
     const uint16_t* W1;     // [V, r]
     const uint16_t* W2T;    // [V, r]
     int r;
+    // RNN head: the conditioning rows [B, gamma, 3, r] (three bf16 terms of
+    // o_k) stand in for W1[prev]; null for the Markov head
+    const uint16_t* erows;
 };
 
 __global__ __launch_bounds__(256)
@@ -1152,7 +1156,8 @@ void draft_finalize(const SegStat* __restrict__ stats, int nseg, int seg_len,
 
     if (q_logits == nullptr) {
         // q-free draft: locate the 8-token group from the tile's group sums,
-        // then rebuild that group's logits l = U + W1[prev] . W2[:, v].
+        // then rebuild that group's logits l = U + e . W2[:, v], e = W1[prev]
+        // (Markov) or the three bf16 terms of o_k (RNN).
         const float mseg = st[(size_t)seg * sj].m;
         const double scale = (double)expf((mseg - M) * invT);   // as the tile weight
         const double wg = lane < rb.gps
@@ -1175,8 +1180,10 @@ void draft_finalize(const SegStat* __restrict__ stats, int nseg, int seg_len,
         const int vt = seg * seg_len + grp * 8 + t;
         const int span = rb.r / 8;
         float part = 0.0f;
-        if (vt < V) {
-            const uint16_t* w1 = rb.W1 + (size_t)prev * rb.r;
+        const int nterm = rb.erows ? 3 : 1;
+        for (int term = 0; term < nterm && vt < V; ++term) {
+            const uint16_t* w1 = rb.erows ? rb.erows + (outi * 3 + term) * (size_t)rb.r
+                                          : rb.W1 + (size_t)prev * rb.r;
             if ((span & 7) == 0) {   // whole 16-byte chunks: span / 8 <= 4 of them
                 const int nswz = w2p_swizzle(vt & (kPackTile - 1), rb.r >> 3);
 #pragma unroll
@@ -1326,7 +1333,8 @@ void rnn_hidden_proj(const uint16_t* __restrict__ h, const uint16_t* __restrict_
 
 // Per position k: pre-activations = hidden part + W[:, 0:r] s_{k-1} +
 // W[:, r:2r] W1[x_{k-1}] for W = W_g, W_c, W_o; gated state update; o split
-// into three bf16 terms (hi, mid, lo) whose sum equals o to ~2^-25.
+// into three bf16 terms (hi, mid, lo) whose sum equals o to ~2^-25, stored as
+// the conditioning rows of (b, k) in Erows [B, gamma, 3, r].
 __global__ __launch_bounds__(256)
 void rnn_gates(const float* __restrict__ hproj, const uint16_t* __restrict__ Wg,
                const uint16_t* __restrict__ Wc, const uint16_t* __restrict__ Wo,
@@ -1378,7 +1386,7 @@ void rnn_gates(const float* __restrict__ hproj, const uint16_t* __restrict__ Wg,
         const uint32_t mid = float_to_bf16_bits(r1);
         const float r2 = r1 - bf16_bits_to_float(mid);
         const uint32_t lo = float_to_bf16_bits(r2);
-        uint16_t* er = Erows + (size_t)b * 3 * r;
+        uint16_t* er = Erows + ((size_t)b * gamma + k) * 3 * r;
         er[i] = (uint16_t)hi;
         er[r + i] = (uint16_t)mid;
         er[2 * r + i] = (uint16_t)lo;
@@ -1575,10 +1583,12 @@ hipError_t draft_tile_launch(const DraftArgs& a, int k, hipStream_t s) {
         if (wb == 2) return launch_stats<2>(p, a.u_bf16, s);
         return launch_stats<4>(p, a.u_bf16, s);
     }
-    return launch_tile_b<kHeadRnn, kOutQ>(p, a.u_bf16, s);
+    if (a.q_logits) return launch_tile_b<kHeadRnn, kOutQ>(p, a.u_bf16, s);
+    return launch_tile_b<kHeadRnn, kOutStats>(p, a.u_bf16, s);
 }
 
 hipError_t residual_rows_launch(const TileParams& p, bool u_bf16, hipStream_t s) {
+    if (p.Erows) return launch_tile_b<kHeadRnn, kOutResidual>(p, u_bf16, s);
     return launch_tile_b<kHeadMarkov, kOutResidual>(p, u_bf16, s);
 }
 
@@ -1630,6 +1640,7 @@ hipError_t draft_finalize_launch(const DraftArgs& a, int k, hipStream_t s) {
     rb.W1 = (const uint16_t*)a.W1;
     rb.W2T = a.W2T;
     rb.r = a.r;
+    rb.erows = a.head == kHeadRnn ? a.Erows : nullptr;
     hipLaunchKernelGGL(draft_finalize, dim3(a.B), dim3(256), 0, s, a.stats, nseg, seg, a.q_logits,
                        a.x0, a.tokens, a.q_logZ, a.q_tok, a.uniforms, a.seed, a.offset, a.B,
                        a.gamma, a.V, k, a.invT, a.greedy, rb);

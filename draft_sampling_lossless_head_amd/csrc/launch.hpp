@@ -77,7 +77,7 @@ struct DraftArgs {
     SegStat* stats;      // [B, nseg]
     float* hproj;        // RNN: [B * gamma, 3r]
     float* state;        // RNN: [2, B, r]
-    uint16_t* Erows;     // RNN: [B, 3, r]
+    uint16_t* Erows;     // RNN: [B, gamma, 3, r] conditioning rows of every position
     const uint16_t* W2T; // bf16 weights: packed W2 image
     uint16_t* W2T_ws;    // workspace for that image when the caller passes none
     float* gsums;        // q-free draft: [B, nseg, 16] 8-token group sums
@@ -98,7 +98,7 @@ struct TileParams {
     const void* U;            // [B, gamma, V]
     const uint16_t* W1;       // [V, r]
     const uint16_t* W2T;      // packed W2 image
-    const uint16_t* Erows;    // RNN: [B, 3, r]
+    const uint16_t* Erows;    // RNN: [B, gamma, 3, r]; residual rows: non-null selects the RNN head
     const int32_t* x0;        // [B]
     const int32_t* tokens;    // [B, gamma] conditioning tokens (draft outputs)
     const int32_t* row_pos;   // kOutResidual: position per row (-1: inactive)

@@ -66,8 +66,8 @@ DraftLayout draft_layout(bool rnn, int B, int gamma, int V, int r) {
         off += align_up((size_t)B * gamma * 3 * r * sizeof(float));
         L.state = off;
         off += align_up((size_t)2 * B * r * sizeof(float));
-        L.erows = off;
-        off += align_up((size_t)B * 3 * r * sizeof(uint16_t));
+        L.erows = off;   // conditioning rows of every position [B, gamma, 3, r]
+        off += align_up((size_t)B * gamma * 3 * r * sizeof(uint16_t));
     }
     L.total = off;
     return L;
@@ -310,8 +310,6 @@ spec_status_t spec_draft_sample_rnn(const void* U, int U_dtype, const int32_t* x
     if (spec_status_t st = check_draft_common(U, U_dtype, x0, W1, W2, w_dtype, r, B, gamma, V, T,
                                               tokens, q_logits, q_logZ, q_tok_prob, W2T))
         return st;
-    if (B > 0 && gamma > 0 && !q_logits)
-        return fail(SPEC_ERR_UNSUPPORTED, "the RNN head needs q_logits");
     if (d < 0) return fail(SPEC_ERR_INVALID, "hidden size d must be >= 0");
     if (!dtype_ok(h_dtype)) return fail(SPEC_ERR_UNSUPPORTED, "dtype must be SPEC_F32 or SPEC_BF16");
     if (B == 0 || gamma == 0) return SPEC_OK;
@@ -692,6 +690,47 @@ size_t spec_verify_markov_workspace_size(int B, int gamma_max, int V, int r) {
     return verify_layout(B, gamma_max, V, r).total;
 }
 
+size_t spec_draft_rnn_cond_offset(int B, int gamma, int V, int r, int d) {
+    (void)d;
+    if (B <= 0 || gamma <= 0 || V <= 0 || V > kMaxDraftV || r <= 0) return 0;
+    return draft_layout(true, B, gamma, V, r).erows;
+}
+
+size_t spec_verify_rnn_workspace_size(int B, int gamma_max, int V, int r) {
+    return spec_verify_markov_workspace_size(B, gamma_max, V, r);
+}
+
+// Verification of a q-free draft: the Markov head (cond == NULL: rows
+// rebuilt from W1[x_{n-1}]) or the RNN head (cond: the draft's conditioning
+// rows [B, gamma, 3, r]).
+static spec_status_t verify_qfree(const void* P, int p_dtype, const void* U, int U_dtype,
+                                  const int32_t* x0, const void* W1, const uint16_t* cond,
+                                  const void* W2, const void* W2T, int w_dtype, int r,
+                                  const int32_t* draft, const float* q_logZ,
+                                  const float* q_tok_prob, const int32_t* lens,
+                                  const int64_t* p_row_off, int B, int gamma_max, int V, float T,
+                                  const float* uniforms, uint64_t seed, uint32_t offset,
+                                  int32_t* accepted, int32_t* out_tokens, float* p_logZ,
+                                  float* accept_prob, void* ws, size_t ws_bytes, void* stream);
+
+spec_status_t spec_verify_rnn(const void* P, int p_dtype, const void* U, int U_dtype,
+                              const void* cond, const void* W2, const void* W2T, int r,
+                              const int32_t* draft, const float* q_logZ, const float* q_tok_prob,
+                              const int32_t* lens, const int64_t* p_row_off, int B, int gamma_max,
+                              int V, float T, const float* uniforms, uint64_t seed,
+                              uint32_t offset, int32_t* accepted, int32_t* out_tokens,
+                              float* p_logZ, float* accept_prob, void* ws, size_t ws_bytes,
+                              void* stream) {
+    g_err.clear();
+    if (B > 0 && gamma_max > 0 && !cond)
+        return fail(SPEC_ERR_INVALID, "null required pointer (cond)");
+    if (!aligned16(cond)) return fail(SPEC_ERR_UNSUPPORTED, "cond must be 16-byte aligned");
+    return verify_qfree(P, p_dtype, U, U_dtype, nullptr, nullptr, static_cast<const uint16_t*>(cond),
+                        W2, W2T, SPEC_BF16, r, draft, q_logZ, q_tok_prob, lens, p_row_off, B,
+                        gamma_max, V, T, uniforms, seed, offset, accepted, out_tokens, p_logZ,
+                        accept_prob, ws, ws_bytes, stream);
+}
+
 spec_status_t spec_verify_markov(const void* P, int p_dtype, const void* U, int U_dtype,
                                  const int32_t* x0, const void* W1, const void* W2,
                                  const void* W2T, int w_dtype, int r, const int32_t* draft,
@@ -702,6 +741,24 @@ spec_status_t spec_verify_markov(const void* P, int p_dtype, const void* U, int 
                                  int32_t* out_tokens, float* p_logZ, float* accept_prob,
                                  void* ws, size_t ws_bytes, void* stream) {
     g_err.clear();
+    if (B > 0 && gamma_max > 0 && (!x0 || !W1))
+        return fail(SPEC_ERR_INVALID, "null required pointer (x0, W1)");
+    return verify_qfree(P, p_dtype, U, U_dtype, x0, W1, nullptr, W2, W2T, w_dtype, r, draft,
+                        q_logZ, q_tok_prob, lens, p_row_off, B, gamma_max, V, T, uniforms, seed,
+                        offset, accepted, out_tokens, p_logZ, accept_prob, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+static spec_status_t verify_qfree(const void* P, int p_dtype, const void* U, int U_dtype,
+                                  const int32_t* x0, const void* W1, const uint16_t* cond,
+                                  const void* W2, const void* W2T, int w_dtype, int r,
+                                  const int32_t* draft, const float* q_logZ,
+                                  const float* q_tok_prob, const int32_t* lens,
+                                  const int64_t* p_row_off, int B, int gamma_max, int V, float T,
+                                  const float* uniforms, uint64_t seed, uint32_t offset,
+                                  int32_t* accepted, int32_t* out_tokens, float* p_logZ,
+                                  float* accept_prob, void* ws, size_t ws_bytes, void* stream) {
     if (B < 0 || gamma_max < 0) return fail(SPEC_ERR_INVALID, "B and gamma_max must be >= 0");
     if (V <= 0 || V > kMaxDraftV) return fail(SPEC_ERR_INVALID, "V must be in [1, 262144]");
     if (r <= 0) return fail(SPEC_ERR_INVALID, "rank r must be > 0");
@@ -712,8 +769,8 @@ spec_status_t spec_verify_markov(const void* P, int p_dtype, const void* U, int 
     if ((int64_t)B * gamma_max > INT32_MAX) return fail(SPEC_ERR_UNSUPPORTED, "B * gamma_max too large");
     if (B == 0) return SPEC_OK;
     if (!P || !accepted || !out_tokens) return fail(SPEC_ERR_INVALID, "null required pointer (P, accepted, out_tokens)");
-    if (gamma_max > 0 && (!U || !x0 || !W1 || !(W2 || W2T) || !draft || !q_logZ || !q_tok_prob))
-        return fail(SPEC_ERR_INVALID, "null required pointer (U, x0, W1, W2 or W2T, draft, q_logZ, q_tok_prob)");
+    if (gamma_max > 0 && (!U || !(W2 || W2T) || !draft || !q_logZ || !q_tok_prob))
+        return fail(SPEC_ERR_INVALID, "null required pointer (U, W2 or W2T, draft, q_logZ, q_tok_prob)");
     if (!aligned16(P) || !aligned16(U) || !aligned16(W1) || !aligned16(W2) || !aligned16(W2T))
         return fail(SPEC_ERR_UNSUPPORTED, "P, U, W1, W2 and W2T must be 16-byte aligned");
     const VerifyLayout L = verify_layout(B, gamma_max, V, r);
@@ -752,7 +809,7 @@ spec_status_t spec_verify_markov(const void* P, int p_dtype, const void* U, int 
     a.chunk_sums = reinterpret_cast<double*>(w + L.chunks);
     hipError_t e = verify_rows_decide_launch(a, s);
     if (e != hipSuccess) return hip_fail(e, "verify");
-    if (!a.greedy && gamma_max > 0 && p_dtype == SPEC_BF16 && U_dtype == SPEC_BF16 &&
+    if (!cond && !a.greedy && gamma_max > 0 && p_dtype == SPEC_BF16 && U_dtype == SPEC_BF16 &&
         resid_streams(B, V, r)) {
         // streamed final draw: residual rows rebuilt in registers, never stored
         // (gamma_max == 0 has no residual: the bonus draw below serves it)
@@ -803,6 +860,7 @@ spec_status_t spec_verify_markov(const void* P, int p_dtype, const void* U, int 
         TileParams tp{};
         tp.U = U;
         tp.W1 = static_cast<const uint16_t*>(W1);
+        tp.Erows = cond;   // RNN head: the draft's conditioning rows
         tp.W2T = w2t;
         tp.x0 = x0;
         tp.tokens = draft;
@@ -823,5 +881,3 @@ spec_status_t spec_verify_markov(const void* P, int p_dtype, const void* U, int 
     e = verify_final_launch(a, s);
     return e == hipSuccess ? SPEC_OK : hip_fail(e, "verify");
 }
-
-}  // extern "C"

@@ -215,10 +215,18 @@ spec_status_t spec_draft_status(const void *ws, size_t ws_bytes, int B, int gamm
  * Wg, Wc, Wo [r, 2r + d]  gate matrices, dtype w_dtype (BF16), no bias terms
  * The state s and o are kept in fp32; o enters the W2 contraction as an
  * exact three-term bf16 split so the bf16 MFMA path keeps fp32 accuracy.
- * Other arguments, outputs and errors as spec_draft_sample_markov, except that
- * q_logits is required (no q-free RNN draft).
+ * Other arguments, outputs and errors as spec_draft_sample_markov.  With
+ * q_logits == NULL the draft is q-free, as the Markov head's per-position
+ * engine: only tokens, q_logZ and q_tok_prob are written; the group of the
+ * draw is rebuilt from U, W2 and the three bf16 terms of o_k.  After either
+ * mode the workspace holds the conditioning rows of every position: the
+ * three bf16 terms of o_k, [B, gamma, 3, r], at byte offset
+ * spec_draft_rnn_cond_offset(B, gamma, V, r, d).  spec_verify_rnn reads them
+ * from there, so a q-free RNN cycle keeps the draft's workspace (unchanged)
+ * until its verification has run.
  */
 size_t spec_draft_rnn_workspace_size(int B, int gamma, int V, int r, int d);
+size_t spec_draft_rnn_cond_offset(int B, int gamma, int V, int r, int d);
 
 spec_status_t spec_draft_sample_rnn(
     const void *U, int U_dtype, const int32_t *x0,
@@ -330,6 +338,34 @@ size_t spec_verify_markov_workspace_size(int B, int gamma_max, int V, int r);
 spec_status_t spec_verify_markov(
     const void *P, int p_dtype, const void *U, int U_dtype, const int32_t *x0,
     const void *W1, const void *W2, const void *W2T, int w_dtype, int r,
+    const int32_t *draft, const float *q_logZ, const float *q_tok_prob,
+    const int32_t *lens, const int64_t *p_row_off,
+    int B, int gamma_max, int V, float T,
+    const float *uniforms, uint64_t seed, uint32_t offset,
+    int32_t *accepted, int32_t *out_tokens, float *p_logZ, float *accept_prob,
+    void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * ---------------------------------------------------------------------------
+ * Lossless verification of a q-free RNN draft
+ * [VESSL "알고리즘", "수락 규칙"; DSpark §1.2 RNN-head eq.]
+ * ---------------------------------------------------------------------------
+ * spec_verify_markov's rule and outputs for a block drafted by
+ * spec_draft_sample_rnn with q_logits == NULL.  q_k(x_k) and the normaliser
+ * of q_k come from the draft (q_tok_prob, q_logZ); the draft row of a
+ * rejected position n is rebuilt as l_n = U[b, n] + W2^T o_n from the draft's
+ * conditioning rows cond = (char *)draft_ws + spec_draft_rnn_cond_offset(...)
+ * ([B, gamma, 3, r] bf16, the three bf16 terms of o_n), written to this
+ * call's workspace and drawn from (fp32, same summation as the draft's tile:
+ * the rebuilt logits match the draft's to fp32 rounding).
+ * P, U, W2 / W2T (bf16, r % 16 == 0, r <= 256), draft, q_logZ, q_tok_prob,
+ * lens, p_row_off, uniforms, outputs and errors as spec_verify_markov.
+ */
+size_t spec_verify_rnn_workspace_size(int B, int gamma_max, int V, int r);
+
+spec_status_t spec_verify_rnn(
+    const void *P, int p_dtype, const void *U, int U_dtype, const void *cond,
+    const void *W2, const void *W2T, int r,
     const int32_t *draft, const float *q_logZ, const float *q_tok_prob,
     const int32_t *lens, const int64_t *p_row_off,
     int B, int gamma_max, int V, float T,

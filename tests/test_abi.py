@@ -39,7 +39,8 @@ def test_header_declares_the_boundary():
               "spec_draft_set_poll_limit", "spec_acceptance_rate", "spec_confidence_head",
               "spec_prefix_schedule", "spec_prefix_schedule_workspace_size", "spec_tree_select",
               "spec_draft_status", "spec_verify_tree", "spec_verify_noalloc",
-              "spec_verify_noalloc_max_bytes"):
+              "spec_verify_noalloc_max_bytes", "spec_verify_rnn",
+              "spec_verify_rnn_workspace_size", "spec_draft_rnn_cond_offset"):
         assert n in names
 
 
@@ -137,7 +138,11 @@ def test_rnn_validation(lib):
     assert call(d=-1) == SPEC_ERR_INVALID
     assert call(d=12) == SPEC_ERR_UNSUPPORTED
     assert call(w_dtype=0) == SPEC_ERR_UNSUPPORTED
-    assert call(q_logits=None, q_logZ=fake, q_tok=fake) == SPEC_ERR_UNSUPPORTED
+    assert call(q_logits=None) == SPEC_ERR_INVALID                    # q-free needs q_logZ, q(x)
+    assert call(q_logits=None, q_logZ=fake, q_tok=fake) == SPEC_ERR_WORKSPACE   # q-free RNN draft
+    assert lib.spec_draft_rnn_cond_offset(2, 2, 500, 32, 64) % 256 == 0
+    assert lib.spec_draft_rnn_cond_offset(2, 2, 500, 32, 64) + 2 * 2 * 3 * 32 * 2 <= \
+        lib.spec_draft_rnn_workspace_size(2, 2, 500, 32, 64)
     assert call() == SPEC_ERR_WORKSPACE
 
 
@@ -369,3 +374,25 @@ def test_verify_noalloc_validation(lib):
     # more scratch than the fixed array: refused on the host, nothing launched
     assert call(B=65536, G=8, V=262144) == SPEC_ERR_WORKSPACE
     assert "spec_verify_noalloc" in lib.spec_last_error().decode()
+
+
+def test_verify_rnn_validation(lib):
+    fake = ctypes.c_void_p(4096)
+    base = dict(P=fake, p_dtype=1, U=fake, U_dtype=1, cond=fake, W2=fake, W2T=None, r=64,
+                draft=fake, q_logZ=fake, q_tok=fake, lens=None, p_off=None, B=2, G=3, V=1000,
+                T=1.0, uniforms=None, seed=0, offset=0, accepted=fake, out=fake, p_logZ=None,
+                ap=None, ws=None, ws_bytes=0, stream=None)
+
+    def call(**kw):
+        a = dict(base)
+        a.update(kw)
+        return lib.spec_verify_rnn(*a.values())
+
+    assert call(cond=None) == SPEC_ERR_INVALID
+    assert call(cond=ctypes.c_void_p(4100)) == SPEC_ERR_UNSUPPORTED
+    assert call(q_logZ=None) == SPEC_ERR_INVALID
+    assert call(r=40) == SPEC_ERR_UNSUPPORTED
+    assert call() == SPEC_ERR_WORKSPACE
+    assert call(B=0) == SPEC_OK
+    assert lib.spec_verify_rnn_workspace_size(2, 3, 1000, 64) == \
+        lib.spec_verify_markov_workspace_size(2, 3, 1000, 64)
