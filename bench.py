@@ -92,10 +92,12 @@ def cycle_bytes(wl, path, n_resid=None):
     kb = kernel_bytes(wl, n_resid)
     B, g, V, r = wl["B"], wl["gamma"], wl["V"], wl["r"]
     lb, wb = _nbytes(wl["logit_dtype"]), _nbytes(wl["w_dtype"])
+    # the RNN head also reads the hidden states and its three gate matrices
+    head = (B * g * wl["d"] * 2 + 3 * r * (2 * r + wl["d"]) * wb) if wl.get("head") == "rnn" else 0
     if path == "qfree":
-        return kb["draft_persist"] + kb["verify_rows_p"] + kb["verify_resid"]
+        return kb["draft_persist"] + head + kb["verify_rows_p"] + kb["verify_resid"]
     q = B * g * V * 4
-    return (B * g * V * lb + q + r * V * wb + B * g * r * wb) + kb["verify_rows_p"] + q
+    return (B * g * V * lb + q + r * V * wb + B * g * r * wb) + head + kb["verify_rows_p"] + q
 
 
 def bias_flops(wl):
@@ -225,10 +227,11 @@ def traffic_from_pmc(fetch_csv, write_csv, kernel_substr, label, workload, probe
 # ---------------------------------------------------------------------------
 
 class Cycle:
-    """Device copies of one workload and the step that runs its cycle:
+    """Device copies of one workload and the step that runs its cycle: the
     Markov head q-free (persistent or per-position engine) or materialised,
-    RNN head materialised; ragged lengths verify only the first L_b
-    positions of each request from packed target rows."""
+    the RNN head q-free (spec_verify_rnn) or materialised; ragged lengths
+    verify only the first L_b positions of each request from packed target
+    rows."""
 
     def __init__(self, sd, torch, wl, path, seed=0):
         import numpy as np
@@ -256,7 +259,6 @@ class Cycle:
         if self.rnn:
             self.H = to_dev(wl["H"], wl["h_dtype"])
             self.Wg, self.Wc, self.Wo = (to_dev(wl[k], wbt) for k in ("Wg", "Wc", "Wo"))
-            self.path = path = "materialized"
         lens = wl.get("lens")
         self.lens = None if lens is None else to_dev(lens)
         self.p_off = None if lens is None else to_dev(workloads.packed_offsets(lens + 1))
@@ -283,8 +285,9 @@ class Cycle:
         sd = self.sd
         if self.rnn:
             sd.spec_draft_sample_rnn(self.U, self.x0, self.H, self.W1, self.W2dev, self.Wg, self.Wc,
-                                     self.Wo, self.T, W2T=self.W2T, seed=self.seed, offset=i,
-                                     out=self.d_out, workspace=self.ws_d)
+                                     self.Wo, self.T, W2T=self.W2T, q_free=self.qfree,
+                                     seed=self.seed, offset=i, out=self.d_out,
+                                     workspace=self.ws_d)
         else:
             sd.spec_draft_sample_markov(self.U, self.x0, self.W1, self.W2, self.T, W2T=self.W2T,
                                         seed=self.seed, offset=i, out=self.d_out,
@@ -294,7 +297,12 @@ class Cycle:
         sd, d = self.sd, self.d_out
         lens = self.lens if lens is None else lens
         out = self.v_out if out is None else out
-        if self.qfree:
+        if self.qfree and self.rnn:
+            sd.spec_verify_rnn(self.P, self.U, d["cond"], self.W2, d["tokens"], d["q_logZ"],
+                               d["q_tok_prob"], self.T, W2T=self.W2T, lens=lens,
+                               p_row_off=self.p_off, seed=self.seed, offset=i, out=out,
+                               workspace=self.ws_v, diagnostics=False)
+        elif self.qfree:
             sd.spec_verify_markov(self.P, self.U, self.x0, self.W1, self.W2, d["tokens"],
                                   d["q_logZ"], d["q_tok_prob"], self.T, W2T=self.W2T, lens=lens,
                                   p_row_off=self.p_off, seed=self.seed, offset=i, out=out,
@@ -464,7 +472,8 @@ SWEEP = [
     ("markov-152k-b128-sigma0.3", "markov-152k-b128", dict(sigma=0.3), "qfree"),
     ("markov-32k-b32", "markov-32k-b32", dict(), "qfree"),
     ("markov-32k-b32-greedy", "markov-32k-b32", dict(T=0.0), "qfree"),
-    ("rnn-32k-b64", "rnn-32k-b64", dict(), "materialized"),
+    ("rnn-32k-b64", "rnn-32k-b64", dict(), "qfree"),
+    ("rnn-32k-b64-materialized", "rnn-32k-b64", dict(), "materialized"),
     ("ragged-128k-b256", "ragged-128k-b256", dict(), "qfree"),
 ]
 
@@ -796,7 +805,8 @@ def main():
                                   for k, v in kernels.items()}))
     # One more step at offset 0, kept for the oracle check of the CPU baseline.
     cyc.step(0)
-    gpu_out = dict(d={k: v.cpu().numpy() for k, v in cyc.d_out.items() if k != "q_logits"},
+    gpu_out = dict(d={k: v.cpu().numpy() for k, v in cyc.d_out.items()
+                      if k not in ("q_logits", "cond")},
                    v={k: v.cpu().numpy() for k, v in cyc.v_out.items()})
 
     result = {

@@ -1283,23 +1283,29 @@ void draft_finalize_stream(FinStreamArgs A, int k) { finalize_row_stream<false>(
 // RNN head.
 // ---------------------------------------------------------------------------
 
-// out[m][n] = sum_t h[m][t] * Wcat[n][2r + t], m < M = B * gamma, n < 3r,
-// Wcat = [W_g; W_c; W_o].  One wave per 32 x 32 output block, operands read
-// straight from global memory in 16-byte runs along t.
+// Hidden part of the pre-activations, split over kHprojSplit ranges of the
+// hidden size: part[s][m][n] = sum_{t in range s} h[m][t] * Wcat[n][2r + t],
+// m < M = B * gamma, n < 3r, Wcat = [W_g; W_c; W_o] (the gates kernel sums
+// the kHprojSplit partials).  One wave per 32 x 32 output block and range,
+// operands straight from global memory in 16-byte runs along t, the next
+// 64-wide chunk loaded while the current one is multiplied.
 __global__ __launch_bounds__(256)
 void rnn_hidden_proj(const uint16_t* __restrict__ h, const uint16_t* __restrict__ Wg,
                      const uint16_t* __restrict__ Wc, const uint16_t* __restrict__ Wo,
-                     float* __restrict__ out, int M, int r, int d) {
+                     float* __restrict__ part, int M, int r, int d) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int m0 = blockIdx.y * 64 + (wave >> 1) * 32;
     const int n0 = blockIdx.x * 64 + (wave & 1) * 32;
+    const int sp = blockIdx.z;
     const int ld = 2 * r + d;
     const int kgrp = lane >> 5;
     const int m = m0 + (lane & 31);
     const int n = n0 + (lane & 31);
     const bool mok = m < M;
     const bool nok = n < 3 * r;
+    const int span = (d + kHprojSplit * 64 - 1) / (kHprojSplit * 64) * 64;
+    const int t_lo = min(d, sp * span), t_hi = min(d, t_lo + span);
     const uint16_t* arow = h + (size_t)(mok ? m : 0) * d + kgrp * 8;
     const uint16_t* wsel = n < r ? Wg : (n < 2 * r ? Wc : Wo);
     const uint16_t* brow = wsel + (size_t)(nok ? n % r : 0) * ld + 2 * r + kgrp * 8;
@@ -1309,20 +1315,35 @@ void rnn_hidden_proj(const uint16_t* __restrict__ h, const uint16_t* __restrict_
     bf16x8_t zero;
 #pragma unroll
     for (int t = 0; t < 8; ++t) zero[t] = (__bf16)0.0f;
-    for (int t0 = 0; t0 < d; t0 += 64) {
-        bf16x8_t a[4], bb[4];
+    bf16x8_t a[2][4], bb[2][4];
+    // Branch-free loads: an address outside the operands is clamped to a valid
+    // one and the value zeroed after the load.
+    auto load = [&](int buf, int t0) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int t = t0 + 16 * u;
-            const bool in = t + kgrp * 8 + 8 <= d;   // d % 8 == 0: whole 8-runs only
-            a[u] = (mok && in) ? *reinterpret_cast<const bf16x8_t*>(arow + t) : zero;
-            bb[u] = (nok && in) ? *reinterpret_cast<const bf16x8_t*>(brow + t) : zero;
+            const bool in = t + kgrp * 8 + 8 <= t_hi;   // d % 8 == 0: whole 8-runs only
+            const int tc = in ? t : t_lo - kgrp * 8;     // a valid run of this range
+            a[buf][u] = *reinterpret_cast<const bf16x8_t*>(arow + tc);
+            bb[buf][u] = *reinterpret_cast<const bf16x8_t*>(brow + tc);
+            if (!(mok && in)) a[buf][u] = zero;
+            if (!(nok && in)) bb[buf][u] = zero;
         }
+    };
+    auto mul = [&](int buf) {
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], bb[u], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[buf][u], bb[buf][u], acc, 0, 0, 0);
+    };
+    if (t_lo < t_hi) load(0, t_lo);
+    for (int t0 = t_lo; t0 < t_hi; t0 += 128) {
+        if (t0 + 64 < t_hi) load(1, t0 + 64);
+        mul(0);
+        if (t0 + 128 < t_hi) load(0, t0 + 128);
+        if (t0 + 64 < t_hi) mul(1);
     }
     if (nok) {
+        float* out = part + (size_t)sp * M * 3 * r;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int mm = m0 + 8 * (i >> 2) + 4 * kgrp + (i & 3);
@@ -1331,65 +1352,162 @@ void rnn_hidden_proj(const uint16_t* __restrict__ h, const uint16_t* __restrict_
     }
 }
 
-// Per position k: pre-activations = hidden part + W[:, 0:r] s_{k-1} +
-// W[:, r:2r] W1[x_{k-1}] for W = W_g, W_c, W_o; gated state update; o split
-// into three bf16 terms (hi, mid, lo) whose sum equals o to ~2^-25, stored as
-// the conditioning rows of (b, k) in Erows [B, gamma, 3, r].
+// Per position k: pre-activations = hidden part (the kHprojSplit partials) +
+// W[:, 0:r] s_{k-1} + W[:, r:2r] W1[x_{k-1}] for W = W_g, W_c, W_o; gated
+// state update; o split into three bf16 terms (hi, mid, lo) whose sum equals
+// o to ~2^-25, stored as the conditioning rows of (b, k) in Erows
+// [B, gamma, 3, r].
+// One workgroup per 32 requests x 32 features; its four waves split the
+// contraction: waves 0 and 1 take halves of the state columns W[:, 0:r] and
+// multiply each weight operand by the hi, mid and lo bf16 terms of the fp32
+// state (their sum is s to ~2^-25, so the products keep fp32 accuracy);
+// waves 2 and 3 take halves of the embedding columns W[:, r:2r].  Every
+// weight is loaded once per workgroup, all of a wave's loads go out before
+// its first MFMA (32x32x16 bf16), the four partial accumulators meet in LDS,
+// and each wave finishes a quarter of the outputs.
 __global__ __launch_bounds__(256)
-void rnn_gates(const float* __restrict__ hproj, const uint16_t* __restrict__ Wg,
+void rnn_gates(const float* __restrict__ hpart, const uint16_t* __restrict__ Wg,
                const uint16_t* __restrict__ Wc, const uint16_t* __restrict__ Wo,
                const uint16_t* __restrict__ W1, const int32_t* __restrict__ x0,
                const int32_t* __restrict__ tokens, const float* __restrict__ s_in,
-               float* __restrict__ s_out, uint16_t* __restrict__ Erows, int gamma, int V, int r,
-               int d, int k) {
-    extern __shared__ float z[];   // [2r]: s_{k-1}, then W1[x_{k-1}]
-    const int b = blockIdx.x;
-    const int tid = threadIdx.x;
-    const int prev = (k == 0) ? x0[b] : tokens[(size_t)b * gamma + k - 1];
-    const bool ok = prev >= 0 && prev < V;
-    for (int t = tid; t < r; t += blockDim.x) {
-        z[t] = (k == 0) ? 0.0f : s_in[(size_t)b * r + t];
-        z[r + t] = ok ? bf16_bits_to_float(W1[(size_t)prev * r + t]) : 0.0f;
-    }
-    __syncthreads();
+               float* __restrict__ s_out, uint16_t* __restrict__ Erows, int B, int gamma, int V,
+               int r, int d, int k) {
+    __shared__ float red[4][3][16][64];
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int kgrp = lane >> 5;
+    const int n0 = blockIdx.x * 32, m0 = blockIdx.y * 32;
+    const int b = m0 + (lane & 31);
+    const int n = n0 + (lane & 31);
+    const bool bok = b < B, nok = n < r;
+    const int bc = bok ? b : 0;
     const int ld = 2 * r + d;
-    const float* hp = hproj + ((size_t)b * gamma + k) * 3 * r;
-    for (int i = tid; i < r; i += blockDim.x) {
-        float ag = hp[i], ac = hp[r + i], ao = hp[2 * r + i];
-        const uint16_t* gr = Wg + (size_t)i * ld;
-        const uint16_t* cr = Wc + (size_t)i * ld;
-        const uint16_t* orow = Wo + (size_t)i * ld;
-        for (int t = 0; t < 2 * r; t += 8) {
-            const uint4 wg = *reinterpret_cast<const uint4*>(gr + t);
-            const uint4 wc = *reinterpret_cast<const uint4*>(cr + t);
-            const uint4 wo = *reinterpret_cast<const uint4*>(orow + t);
-            const uint32_t g4[4] = {wg.x, wg.y, wg.z, wg.w};
-            const uint32_t c4[4] = {wc.x, wc.y, wc.z, wc.w};
-            const uint32_t o4[4] = {wo.x, wo.y, wo.z, wo.w};
+    const int prev = (k == 0) ? x0[bc] : tokens[(size_t)bc * gamma + k - 1];
+    const bool pok = bok && prev >= 0 && prev < V;
+    const int pc = pok ? prev : 0;
+    bf16x8_t zero;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float z0 = z[t + 2 * q], z1 = z[t + 2 * q + 1];
-                ag = fmaf(bf16_bits_to_float(g4[q] & 0xFFFFu), z0, ag);
-                ag = fmaf(bf16_bits_to_float(g4[q] >> 16), z1, ag);
-                ac = fmaf(bf16_bits_to_float(c4[q] & 0xFFFFu), z0, ac);
-                ac = fmaf(bf16_bits_to_float(c4[q] >> 16), z1, ac);
-                ao = fmaf(bf16_bits_to_float(o4[q] & 0xFFFFu), z0, ao);
-                ao = fmaf(bf16_bits_to_float(o4[q] >> 16), z1, ao);
+    for (int t = 0; t < 8; ++t) zero[t] = (__bf16)0.0f;
+    f32x16_t acc[3];
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[q][i] = 0.0f;
+    const uint16_t* wr[3] = {Wg + (size_t)(nok ? n : 0) * ld, Wc + (size_t)(nok ? n : 0) * ld,
+                             Wo + (size_t)(nok ? n : 0) * ld};
+    // This wave's rank steps (16 columns each) of its half: state half for
+    // waves 0-1, embedding half for waves 2-3; at most 8 steps (r <= 256).
+    const int nsteps = r / 16;
+    const int half = (nsteps + 1) / 2;
+    const bool state = w < 2;
+    const int s_lo = (w & 1) ? half : 0;
+    const int s_n = (w & 1) ? nsteps - half : half;
+    // No branches among the loads: addresses are clamped to valid memory and
+    // the values zeroed afterwards.
+    const char* abase = state ? reinterpret_cast<const char*>(s_in + (size_t)bc * r)
+                              : reinterpret_cast<const char*>(W1 + (size_t)pc * r);
+    const int astride = state ? 4 : 2;
+    const int ahi = state ? 16 : 0;
+    const bool azero = state ? (!bok || k == 0) : !pok;
+    const int col0 = state ? 0 : r;
+    constexpr int KB = 8;
+    uint4 ra[KB][2];
+    bf16x8_t bq[KB][3];
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+        const int ks = min(s_lo + min(j, max(s_n - 1, 0)), nsteps - 1);   // inside the row
+        const int t = ks * 16 + kgrp * 8;
+        const char* ap = abase + (size_t)t * astride;
+        ra[j][0] = *reinterpret_cast<const uint4*>(ap);
+        ra[j][1] = *reinterpret_cast<const uint4*>(ap + ahi);
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+            bq[j][q] = *reinterpret_cast<const bf16x8_t*>(wr[q] + col0 + t);
+    }
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+        if (j >= s_n) break;
+        bf16x8_t bv[3];
+#pragma unroll
+        for (int q = 0; q < 3; ++q) bv[q] = nok ? bq[j][q] : zero;
+        if (state) {
+            const uint32_t raw[8] = {ra[j][0].x, ra[j][0].y, ra[j][0].z, ra[j][0].w,
+                                     ra[j][1].x, ra[j][1].y, ra[j][1].z, ra[j][1].w};
+            bf16x8_t th, tm, tl;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float sv = azero ? 0.0f : __uint_as_float(raw[e]);
+                const uint32_t hi = float_to_bf16_bits(sv);
+                const float r1 = sv - bf16_bits_to_float(hi);
+                const uint32_t mid = float_to_bf16_bits(r1);
+                const uint32_t lo = float_to_bf16_bits(r1 - bf16_bits_to_float(mid));
+                th[e] = __builtin_bit_cast(__bf16, (uint16_t)hi);
+                tm[e] = __builtin_bit_cast(__bf16, (uint16_t)mid);
+                tl[e] = __builtin_bit_cast(__bf16, (uint16_t)lo);
             }
+#pragma unroll
+            for (int q = 0; q < 3; ++q) {
+                acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(th, bv[q], acc[q], 0, 0, 0);
+                acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tm, bv[q], acc[q], 0, 0, 0);
+                acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl, bv[q], acc[q], 0, 0, 0);
+            }
+        } else {
+            bf16x8_t a = __builtin_bit_cast(bf16x8_t, ra[j][0]);
+            if (azero) a = zero;
+#pragma unroll
+            for (int q = 0; q < 3; ++q)
+                acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bv[q], acc[q], 0, 0, 0);
         }
-        const float g = 1.0f / (1.0f + expf(-ag));
-        const float c = tanhf(ac);
-        const float o = tanhf(ao);
-        s_out[(size_t)b * r + i] = g * z[i] + (1.0f - g) * c;
+    }
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) red[w][q][i][lane] = acc[q][i];
+    __syncthreads();
+    const size_t M = (size_t)B * gamma;
+    // wave w finishes accumulator elements 4w .. 4w + 3: requests m0 + 8w +
+    // 4 * kgrp + 0..3 of feature n; their loads go out first
+    const int nc = nok ? n : 0;
+    float hpv[4][3][kHprojSplit], sold[4];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+        const int m = m0 + 8 * w + 4 * kgrp + ii;
+        const size_t row = (size_t)(m < B ? m : 0) * gamma + k;
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+#pragma unroll
+            for (int sp = 0; sp < kHprojSplit; ++sp)
+                hpv[ii][q][sp] = hpart[((size_t)sp * M + row) * 3 * r + (size_t)q * r + nc];
+        sold[ii] = (k == 0) ? 0.0f : s_in[(size_t)(m < B ? m : 0) * r + nc];
+    }
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+        const int i = 4 * w + ii;
+        const int m = m0 + 8 * w + 4 * kgrp + ii;
+        if (m >= B || !nok) continue;
+        const size_t row = (size_t)m * gamma + k;
+        float pre[3];
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            float hp = 0.0f;
+#pragma unroll
+            for (int sp = 0; sp < kHprojSplit; ++sp) hp += hpv[ii][q][sp];
+            pre[q] = hp + ((red[0][q][i][lane] + red[1][q][i][lane]) +
+                           (red[2][q][i][lane] + red[3][q][i][lane]));
+        }
+        const float g = 1.0f / (1.0f + expf(-pre[0]));
+        const float c = tanhf(pre[1]);
+        const float o = tanhf(pre[2]);
+        s_out[(size_t)m * r + n] = g * sold[ii] + (1.0f - g) * c;
         const uint32_t hi = float_to_bf16_bits(o);
         const float r1 = o - bf16_bits_to_float(hi);
         const uint32_t mid = float_to_bf16_bits(r1);
         const float r2 = r1 - bf16_bits_to_float(mid);
         const uint32_t lo = float_to_bf16_bits(r2);
-        uint16_t* er = Erows + ((size_t)b * gamma + k) * 3 * r;
-        er[i] = (uint16_t)hi;
-        er[r + i] = (uint16_t)mid;
-        er[2 * r + i] = (uint16_t)lo;
+        uint16_t* er = Erows + row * 3 * r;
+        er[n] = (uint16_t)hi;
+        er[r + n] = (uint16_t)mid;
+        er[2 * r + n] = (uint16_t)lo;
     }
 }
 
@@ -1649,7 +1767,7 @@ hipError_t draft_finalize_launch(const DraftArgs& a, int k, hipStream_t s) {
 
 hipError_t rnn_hidden_proj_launch(const DraftArgs& a, hipStream_t s) {
     const int M = a.B * a.gamma;
-    dim3 grid((3 * a.r + 63) / 64, (M + 63) / 64);
+    dim3 grid((3 * a.r + 63) / 64, (M + 63) / 64, kHprojSplit);
     hipLaunchKernelGGL(rnn_hidden_proj, grid, dim3(256), 0, s, (const uint16_t*)a.h,
                        (const uint16_t*)a.Wg, (const uint16_t*)a.Wc, (const uint16_t*)a.Wo,
                        a.hproj, M, a.r, a.d);
@@ -1659,10 +1777,10 @@ hipError_t rnn_hidden_proj_launch(const DraftArgs& a, hipStream_t s) {
 hipError_t rnn_gates_launch(const DraftArgs& a, int k, hipStream_t s) {
     const float* s_in = a.state + (size_t)((k + 1) & 1) * a.B * a.r;
     float* s_out = a.state + (size_t)(k & 1) * a.B * a.r;
-    hipLaunchKernelGGL(rnn_gates, dim3(a.B), dim3(256), 2 * a.r * sizeof(float), s, a.hproj,
-                       (const uint16_t*)a.Wg, (const uint16_t*)a.Wc, (const uint16_t*)a.Wo,
-                       (const uint16_t*)a.W1, a.x0, a.tokens, s_in, s_out, a.Erows, a.gamma, a.V,
-                       a.r, a.d, k);
+    hipLaunchKernelGGL(rnn_gates, dim3((a.r + 31) / 32, (a.B + 31) / 32), dim3(256), 0, s,
+                       a.hproj, (const uint16_t*)a.Wg, (const uint16_t*)a.Wc,
+                       (const uint16_t*)a.Wo, (const uint16_t*)a.W1, a.x0, a.tokens, s_in, s_out,
+                       a.Erows, a.B, a.gamma, a.V, a.r, a.d, k);
     return hipGetLastError();
 }
 

@@ -138,6 +138,9 @@ hipError_t w2_pack_launch(const uint16_t* W2, uint16_t* W2P, int r, int V, hipSt
 // equal the logits a q-free draft engine sampled from to fp32 rounding (the
 // engines sum the contraction in other orders).
 hipError_t residual_rows_launch(const TileParams& p, bool u_bf16, hipStream_t s);
+// Ranges of the hidden size the RNN head's hidden projection is split over
+// (the gates kernel sums the partials).
+constexpr int kHprojSplit = 8;
 hipError_t rnn_hidden_proj_launch(const DraftArgs& a, hipStream_t s);
 hipError_t rnn_gates_launch(const DraftArgs& a, int k, hipStream_t s);
 

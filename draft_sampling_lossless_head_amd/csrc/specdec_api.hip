@@ -62,8 +62,8 @@ DraftLayout draft_layout(bool rnn, int B, int gamma, int V, int r) {
     L.w2t = off;   // packed bf16 W2 when the caller passes none
     off += align_up(w2p_bytes(r, V));
     if (rnn) {
-        L.hproj = off;
-        off += align_up((size_t)B * gamma * 3 * r * sizeof(float));
+        L.hproj = off;   // hidden-part partials [kHprojSplit][B * gamma][3r]
+        off += align_up((size_t)kHprojSplit * B * gamma * 3 * r * sizeof(float));
         L.state = off;
         off += align_up((size_t)2 * B * r * sizeof(float));
         L.erows = off;   // conditioning rows of every position [B, gamma, 3, r]
