@@ -251,6 +251,10 @@ def draft_markov(U, W1, W2, x0, T, u, forced=None, want_logits=True):
                                _dp(o["logZ"]), _dp(o["q_tok"]), _dp(o["thr"]), _dp(o["margin"]))
     if st != 0:
         raise ValueError(f"oracle draft_markov failed with status {st}")
+    # the inputs of each position's logits, for the comparison's error bound:
+    # W1, W2 and the token each position conditioned on
+    prev = np.concatenate([[int(x0)], (o["tokens"] if f is None else f)[: gamma - 1]])
+    o["markov"] = dict(W1=W1, W2=W2, prev=prev.astype(np.int64))
     return o
 
 

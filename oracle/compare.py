@@ -5,12 +5,16 @@ GPU and never receives anything the GPU produced.  The bar:
 
 * token ids and accepted counts match exactly, except a draw whose uniform
   lies within BAND (1e-6) of the oracle's CDF boundary between the oracle's
-  choice and the GPU's (or, at T = 0, whose top-2 logit gap is within the
-  fp32 accumulation tolerance).  Such draws are counted and reported.  After
+  choice and the GPU's, or, at T = 0, a draft argmax whose two logits differ
+  by no more than the error bounds of their fp32 computation (Markov head:
+  gamma_{r+1} (|U| + |W1[x]| . |W2|) per logit; the RNN head, whose o carries
+  the gates' own rounding, keeps the fixed band 1e-5 * max(1, |l|)).
+  Verification's greedy choices take the argmax of given rows and are exact.  Such draws are counted and reported.  After
   a boundary draw in a draft chain the rest of that request conditions on a
   different prefix and is not compared.
 * normalisers (log Z): |delta| <= 1e-5; probabilities q(x), min(1, p/q):
-  relative 1e-5; draft logits: |delta| <= 1e-5 * max(1, |l|).
+  relative 1e-5; draft logits: within the same per-logit bound (Markov
+  head) or 1e-5 * max(1, |l|) (RNN head).
 """
 import numpy as np
 
@@ -19,6 +23,24 @@ from . import binding as orc
 BAND = 1e-6
 TOL_LOGZ = 1e-5
 TOL_REL = 1e-5
+U32 = 2.0 ** -24     # unit roundoff of fp32
+
+
+def _gamma(n):
+    """gamma_n = n u / (1 - n u) (Higham, Accuracy and Stability of Numerical
+    Algorithms, §3.1): |fl(x^T y) - x^T y| <= gamma_n |x|^T |y| for a dot
+    product of n terms summed in any order with each operation rounded."""
+    return n * U32 / (1.0 - n * U32)
+
+
+def markov_logit_bound(U_k, W1, W2, prev):
+    """Bound on |fl(l) - l| for the fp32 kernels' Markov-head logits
+    l = U_k + W1[prev] . W2 (r products and one add, every input exact in fp32:
+    bf16 or fp32 values): gamma_{r+1} (|U_k| + |W1[prev]| . |W2|)."""
+    r = W1.shape[1]
+    if prev < 0 or prev >= W1.shape[0]:
+        return np.full(U_k.shape, np.inf)
+    return _gamma(r + 1) * (np.abs(U_k) + np.abs(W1[prev]) @ np.abs(W2))
 
 
 class Tally:
@@ -59,11 +81,16 @@ def _check_draw(w, orc_tok, gpu_tok, u, what):
     return True
 
 
-def _check_greedy(l, orc_tok, gpu_tok, what):
+def _check_greedy(l, orc_tok, gpu_tok, what, err=None):
+    """A greedy mismatch is a tie within the GPU's arithmetic: the two exact
+    logits differ by at most the sum of their computed values' error bounds
+    (err, per token; without it the fixed band TOL_REL * max(1, |l|))."""
     if gpu_tok == orc_tok:
         return False
+    if gpu_tok < 0 or gpu_tok >= len(l):
+        raise AssertionError(f"{what}: greedy GPU token {gpu_tok} out of range")
     gap = l[orc_tok] - l[gpu_tok]
-    tol = TOL_REL * max(1.0, abs(l[orc_tok]))
+    tol = (err[orc_tok] + err[gpu_tok]) if err is not None else TOL_REL * max(1.0, abs(l[orc_tok]))
     if not (0 <= gap <= tol):
         raise AssertionError(f"{what}: greedy GPU token {gpu_tok} != oracle {orc_tok}, "
                              f"logit gap {gap:.3e} > {tol:.1e}")
@@ -86,18 +113,20 @@ def compare_draft_request(orc_out, U, gpu, T, u, what, tally, check_logits=True)
     (tokens [gamma], q_logits [gamma, V], q_logZ, q_tok_prob); u: uniforms."""
     gamma = len(orc_out["tokens"])
     tally.requests += 1
+    mk = orc_out.get("markov")   # Markov head: the derived per-logit error bound
     for k in range(gamma):
         l = orc_out["q_logits"][k]
         gt, ot = int(gpu["tokens"][k]), int(orc_out["tokens"][k])
+        err = markov_logit_bound(U[k], mk["W1"], mk["W2"], int(mk["prev"][k])) if mk else None
         if check_logits:
-            _close(gpu["q_logits"][k], l, TOL_REL * np.maximum(1.0, np.abs(l)), 0.0,
-                   f"{what} q_logits[k={k}]")
+            tol = err + 1e-12 * np.abs(l) if err is not None else TOL_REL * np.maximum(1.0, np.abs(l))
+            _close(gpu["q_logits"][k], l, tol, 0.0, f"{what} q_logits[k={k}]")
         if T > 0:
             _close(gpu["q_logZ"][k], orc_out["logZ"][k], TOL_LOGZ, 0.0, f"{what} q_logZ[k={k}]")
         tally.draws += 1
         tally.compared_positions += 1
         if T == 0:
-            boundary = _check_greedy(l, ot, gt, f"{what} k={k}")
+            boundary = _check_greedy(l, ot, gt, f"{what} k={k}", err)
         else:
             w, Z, _ = orc.softmax_weights(l, T)
             boundary = _check_draw(w, ot, gt, u[k], f"{what} k={k}")
