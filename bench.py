@@ -400,12 +400,13 @@ def roofline_of(cyc, kernels, workload_name):
 # CPU baseline: the oracle as it stands, and a sampled check of one GPU step
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(wl, seed, offset, nsample, threads, gpu=None):
+def cpu_baseline(wl, seed, offset, nsample, threads, gpu=None, min_seconds=10.0, max_steps=40):
     """The fp64 oracle (as it stands) on the first nsample requests: draft then
-    verify of each request, requests spread over `threads` host threads, with
-    the uniforms of step `offset`.  gpu: host copies of that GPU step's draft
-    and verification outputs; the oracle's results are then compared request
-    by request (draws within 1e-6 of a CDF boundary are counted, not failed)."""
+    verify of each request, requests spread over `threads` host threads, step
+    after step (the uniforms of steps offset, offset + 1, ...) until about
+    min_seconds of wall time (at most max_steps).  gpu: host copies of the GPU
+    step at `offset`; the oracle's first step is compared with it request by
+    request (draws within 1e-6 of a CDF boundary are counted, not failed)."""
     import concurrent.futures
 
     import numpy as np
@@ -418,24 +419,33 @@ def cpu_baseline(wl, seed, offset, nsample, threads, gpu=None):
     lb, wbt = wl["logit_dtype"], wl["w_dtype"]
     W1 = workloads.as_f64(wl["W1"], wbt)
     W2 = workloads.as_f64(wl["W2"], wbt)
-    ud = oracle.draft_uniforms(seed, offset, nsample, g)
-    uv = oracle.verify_uniforms(seed, offset, nsample, g)
     U = [workloads.as_f64(wl["U"][b], lb) for b in range(nsample)]
     P = [workloads.as_f64(wl["P"][b], lb) for b in range(nsample)]
     T = wl["T"]
 
-    def one(b):
-        d = oracle.draft_markov(U[b], W1, W2, int(wl["x0"][b]), T, ud[b])
-        v = oracle.verify(P[b], d["q_logits"], d["tokens"], T, uv[b, :g], uv[b, g])
-        return d, v
+    def step(off):
+        ud = oracle.draft_uniforms(seed, off, nsample, g)
+        uv = oracle.verify_uniforms(seed, off, nsample, g)
+
+        def one(b):
+            d = oracle.draft_markov(U[b], W1, W2, int(wl["x0"][b]), T, ud[b])
+            v = oracle.verify(P[b], d["q_logits"], d["tokens"], T, uv[b, :g], uv[b, g])
+            return d, v
+
+        with concurrent.futures.ThreadPoolExecutor(max_workers=threads) as ex:
+            return list(ex.map(one, range(nsample))), ud, uv
 
     t0 = time.perf_counter()
-    with concurrent.futures.ThreadPoolExecutor(max_workers=threads) as ex:
-        res = list(ex.map(one, range(nsample)))
+    res, ud, uv = step(offset)          # the step compared with the GPU's
+    steps = 1
+    while time.perf_counter() - t0 < min_seconds and steps < max_steps:
+        step(offset + steps)
+        steps += 1
     dt = time.perf_counter() - t0
-    out = dict(value=nsample * g / dt, unit="tokens/s", cores=threads, kind="oracle",
-               sample=f"first {nsample} of {B} requests of the same workload (draft + verify, "
-                      f"fp64, {threads} threads), {dt:.2f} s wall",
+    out = dict(value=steps * nsample * g / dt, unit="tokens/s", cores=threads, kind="oracle",
+               sample=f"first {nsample} of {B} requests of the same workload, {steps} steps "
+                      f"(uniforms of steps {offset}..{offset + steps - 1}; draft + verify, fp64, "
+                      f"{threads} threads), {dt:.2f} s wall",
                mean_tau=float(np.mean([v["n"] for _, v in res])) + 1.0)
     if gpu is not None:
         td, tv = compare.Tally(), compare.Tally()
@@ -636,6 +646,36 @@ def around_the_cycle(sd, torch, cyc, warmup, steps):
     if n:
         out["tree_select"] = dict(avg_us=round(ms * 1e3 / n, 2), trees=B, nodes=1024, budget=64,
                                   mean_score=round(float(t_out["score"].mean().item()), 3))
+    # tree verification: 32 requests, 16-node trees over 4 levels, the
+    # workload's vocabulary (bf16 rows); the children of a node hold the
+    # highest tokens of its draft row, first child the argmax
+    import numpy as np
+    BT, MT = 32, 16
+    tvw = workloads.make_tree_verify(BT, MT, V, seed=1234, dtype="bf16", sigma=1.0, levels=4)
+    Qf = workloads.bf16_bits_to_f32(tvw["Q"])
+    tok = np.empty((BT, MT), dtype=np.int32)
+    for b in range(BT):
+        seen = {}
+        for v in range(MT):
+            pa = int(tvw["parent"][b, v])
+            k = seen.get(pa, 0)
+            seen[pa] = k + 1
+            row = Qf[b, pa + 1]
+            tok[b, v] = int(np.argpartition(-row, k)[k]) if k else int(np.argmax(row))
+    Pt, Qt = cyc.to_dev(tvw["P"], "bf16"), cyc.to_dev(tvw["Q"], "bf16")
+    part, tokt = cyc.to_dev(tvw["parent"]), cyc.to_dev(tok)
+    tv_out = sd.spec_verify_tree(Pt, Qt, part, tokt, T, seed=5)
+    for i in range(3):
+        cyc.step(warmup + i)
+    sd.spec_profile_enable("verify_tree")
+    for i in range(steps):
+        sd.spec_verify_tree(Pt, Qt, part, tokt, T, seed=5, offset=i, out=tv_out)
+    n, ms = sd.spec_profile_read()
+    sd.spec_profile_enable(None)
+    if n:
+        out["verify_tree"] = dict(avg_us=round(ms * 1e3 / n, 2), trees=BT, nodes=MT, V=V,
+                                  mean_accepted=round(float(tv_out["accepted"].float().mean().item()), 3))
+    del Pt, Qt
     return out
 
 
@@ -698,7 +738,8 @@ def main():
                     help="q-free draft: one persistent launch (plain, or cooperative), or two "
                          "launches per position")
     ap.add_argument("--sigma", type=float, default=None, help="override target/draft noise")
-    ap.add_argument("--cpu-sample", type=int, default=64, help="requests timed on the oracle")
+    ap.add_argument("--cpu-sample", type=int, default=128,
+                    help="requests per oracle step (steps repeat for about 10 s)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true",
                     help="only the headline workload (no per-configuration lines)")

@@ -74,6 +74,61 @@ __device__ __forceinline__ void load8(const void* base, size_t row_off, int v0, 
     }
 }
 
+// Eight logits of vector i (< nvec) of a row of a multiple of 8 tokens: one
+// or two 16-byte loads, no branch.
+template <bool BF>
+__device__ __forceinline__ void load8v(const void* base, size_t row_off, int i, float x[8]) {
+    if constexpr (BF) {
+        const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + row_off +
+                                                        8 * (size_t)i);
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            x[2 * h] = __uint_as_float(ww[h] << 16);
+            x[2 * h + 1] = __uint_as_float(ww[h] & 0xFFFF0000u);
+        }
+    } else {
+        const float* p = static_cast<const float*>(base) + row_off + 8 * (size_t)i;
+        const float4 a = *reinterpret_cast<const float4*>(p);
+        const float4 b = *reinterpret_cast<const float4*>(p + 4);
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    }
+}
+
+// A pass over the row's vectors: f(i, xp, xq) for every vector i < nvec of
+// this thread (xq only with Q).  Aligned rows go in batches of kTvBatch
+// vectors per thread whose loads all issue before the first is used (a
+// clamped index past the end re-reads the last vector, skipped); other rows
+// one vector at a time with bounds checks.
+constexpr int kTvBatch = 8;
+template <bool PB, bool QB, bool WITHQ, typename F>
+__device__ __forceinline__ void row_pass(const TreeVerifyArgs& a, size_t prow, size_t qrow,
+                                         int nvec, bool vec, F&& f) {
+    const int tid = threadIdx.x;
+    if (vec) {
+        for (int i0 = tid; i0 < nvec; i0 += kTvThreads * kTvBatch) {
+            float xp[kTvBatch][8], xq[kTvBatch][8];
+#pragma unroll
+            for (int j = 0; j < kTvBatch; ++j) {
+                const int i = min(i0 + j * kTvThreads, nvec - 1);
+                load8v<PB>(a.P, prow, i, xp[j]);
+                if constexpr (WITHQ) load8v<QB>(a.Q, qrow, i, xq[j]);
+            }
+#pragma unroll
+            for (int j = 0; j < kTvBatch; ++j)
+                if (i0 + j * kTvThreads < nvec) f(i0 + j * kTvThreads, xp[j], xq[j]);
+        }
+    } else {
+        for (int i = tid; i < nvec; i += kTvThreads) {
+            float xp[8], xq[8];
+            load8<PB>(a.P, prow, 8 * i, a.V, false, xp);
+            if constexpr (WITHQ) load8<QB>(a.Q, qrow, 8 * i, a.V, false, xq);
+            f(i, xp, xq);
+        }
+    }
+}
+
 template <bool BF>
 __device__ __forceinline__ float load1(const void* base, size_t idx) {
     if constexpr (BF) return __uint_as_float((uint32_t)static_cast<const uint16_t*>(base)[idx] << 16);
@@ -132,8 +187,10 @@ __global__ __launch_bounds__(kTvThreads) void verify_tree_kernel(TreeVerifyArgs 
     bad = __syncthreads_or(bad);
 
     const size_t rows_b = (size_t)b * (M + 1);
-    const bool pvec = PB ? (V % 8 == 0) : (V % 4 == 0);
-    const bool qvec = QB ? (V % 8 == 0) : (V % 4 == 0);
+    // whole 8-token vectors, each 16-byte aligned (the rows start 16-byte
+    // aligned and hold a multiple of 8 tokens)
+    const bool pvec = V % 8 == 0;
+    const bool qvec = pvec;
     const int nvec = (V + 7) / 8;
 
     int node = -1, n = 0, final_tok = -1;
@@ -148,12 +205,11 @@ __global__ __launch_bounds__(kTvThreads) void verify_tree_kernel(TreeVerifyArgs 
             // argmax of the node's target row, lowest id on ties
             float m = -INFINITY;
             int idx = INT_MAX;
-            for (int i = tid; i < nvec; i += kTvThreads) {
-                float x[8];
-                load8<PB>(a.P, prow, 8 * i, V, pvec, x);
+            row_pass<PB, QB, false>(a, prow, qrow, nvec, pvec, [&](int i, float* x, float*) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) merge_arg(m, idx, x[e], 8 * i + e);
-            }
+                for (int e = 0; e < 8; ++e)
+                    if (8 * i + e < V) merge_arg(m, idx, x[e], 8 * i + e);
+            });
             wave_argmax_dpp(m, idx);
             __syncthreads();
             if (lane == 0) { sh.red_m[0][wave] = m; sh.red_i[wave] = idx; }
@@ -175,9 +231,7 @@ __global__ __launch_bounds__(kTvThreads) void verify_tree_kernel(TreeVerifyArgs 
 
         // Normalisers of the node's target row and, with children, draft row.
         float mp = -INFINITY, sp = 0.0f, mq = -INFINITY, sq = 0.0f;
-        for (int i = tid; i < nvec; i += kTvThreads) {
-            float x[8];
-            load8<PB>(a.P, prow, 8 * i, V, pvec, x);
+        auto absorb = [&](const float* x, float& m, float& sm) {
             float m8 = -INFINITY;
 #pragma unroll
             for (int e = 0; e < 8; ++e) m8 = fmaxf(m8, x[e] * invT);
@@ -185,21 +239,17 @@ __global__ __launch_bounds__(kTvThreads) void verify_tree_kernel(TreeVerifyArgs 
                 float s8 = 0.0f;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) s8 += __expf(x[e] * invT - m8);
-                merge_ms(mp, sp, m8, s8, 1.0f);
+                merge_ms(m, sm, m8, s8, 1.0f);
             }
-            if (has_child) {
-                load8<QB>(a.Q, qrow, 8 * i, V, qvec, x);
-                m8 = -INFINITY;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) m8 = fmaxf(m8, x[e] * invT);
-                if (m8 != -INFINITY) {
-                    float s8 = 0.0f;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) s8 += __expf(x[e] * invT - m8);
-                    merge_ms(mq, sq, m8, s8, 1.0f);
-                }
-            }
-        }
+        };
+        if (has_child)
+            row_pass<PB, QB, true>(a, prow, qrow, nvec, pvec && qvec, [&](int, float* xp, float* xq) {
+                absorb(xp, mp, sp);
+                absorb(xq, mq, sq);
+            });
+        else
+            row_pass<PB, QB, false>(a, prow, qrow, nvec, pvec,
+                                    [&](int, float* xp, float*) { absorb(xp, mp, sp); });
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) {
             merge_ms(mp, sp, __shfl_xor(mp, off), __shfl_xor(sp, off), 1.0f);
@@ -240,17 +290,14 @@ __global__ __launch_bounds__(kTvThreads) void verify_tree_kernel(TreeVerifyArgs 
             cc += W;
             const float cf = (float)cc;
             double part = 0.0;
-            for (int i = tid; i < nvec; i += kTvThreads) {
-                float xp[8], xq[8];
-                load8<PB>(a.P, prow, 8 * i, V, pvec, xp);
-                load8<QB>(a.Q, qrow, 8 * i, V, qvec, xq);
+            row_pass<PB, QB, true>(a, prow, qrow, nvec, pvec && qvec, [&](int i, float* xp, float* xq) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float d = exp_rel(xp[e] * invT, lzp_hi, lzp_lo) -
                                     cf * exp_rel(xq[e] * invT, lzq_hi, lzq_lo);
-                    part += d > 0.0f ? (double)d : 0.0;
+                    part += (d > 0.0f && 8 * i + e < V) ? (double)d : 0.0;
                 }
-            }
+            });
             W = block_sum(sh, part);
             if (!(W > 0.0)) { fallback = true; break; }
         }

@@ -120,3 +120,40 @@ def test_rnn_32k_sampled(orc):
                                            o["tokens"], 1.0, uv[b, :gamma], uv[b, gamma],
                                            {k: x[b] for k, x in gv.items()}, f"verify b={b}", tv)
     note(f"  draft {td.as_dict()}\n  verify {tv.as_dict()}")
+
+
+def test_rnn_32k_qfree_sampled(orc):
+    """The RNN workload at full size on the q-free path (the benchmark's
+    cycle): q-free draft, then spec_verify_rnn; requests spread over the
+    batch compared with the oracle's draft and verification."""
+    sd = require_gpu()
+    wl = workloads.make_rnn(workloads.CONFIGS["rnn-32k-b64"])
+    B, gamma, V = wl["B"], wl["gamma"], wl["V"]
+    note(f"rnn-32k q-free B={B}")
+    lb = wl["logit_dtype"]
+    U, W2 = dev(wl["U"], lb), dev(wl["W2"], "bf16")
+    d = sd.spec_draft_sample_rnn(U, dev(wl["x0"]), dev(wl["H"], "bf16"), dev(wl["W1"], "bf16"),
+                                 W2, dev(wl["Wg"], "bf16"), dev(wl["Wc"], "bf16"),
+                                 dev(wl["Wo"], "bf16"), 1.0, q_free=True, seed=7)
+    v = sd.spec_verify_rnn(dev(wl["P"], lb), U, d["cond"], W2, d["tokens"], d["q_logZ"],
+                           d["q_tok_prob"], 1.0, seed=7, offset=1)
+    gd = host({k: x for k, x in d.items() if k != "cond"})
+    gv = host(v)
+    _check_properties(gd, gv, V, None, gamma)
+    f = {n: workloads.as_f64(wl[n], "bf16") for n in ("W1", "W2", "Wg", "Wc", "Wo")}
+    ud = orc.draft_uniforms(7, 0, B, gamma)
+    uv = orc.verify_uniforms(7, 1, B, gamma)
+    td, tv = compare.Tally(), compare.Tally()
+    for b in [0, 9, 31, 50, 63]:
+        Ub = workloads.as_f64(wl["U"][b], lb)
+        o = orc.draft_rnn(Ub, workloads.as_f64(wl["H"][b], "bf16"), f["W1"], f["W2"], f["Wg"],
+                          f["Wc"], f["Wo"], wl["x0"][b], 1.0, ud[b])
+        if compare.compare_draft_request(o, Ub, {k: x[b] for k, x in gd.items()}, 1.0, ud[b],
+                                         f"draft b={b}", td, check_logits=False):
+            gvb = {k: x[b] for k, x in gv.items()}
+            gvb["q_logZ"] = gd["q_logZ"][b]
+            compare.compare_verify_request(workloads.as_f64(wl["P"][b], lb), o["q_logits"],
+                                           o["tokens"], 1.0, uv[b, :gamma], uv[b, gamma], gvb,
+                                           f"verify b={b}", tv)
+    note(f"  draft {td.as_dict()}\n  verify {tv.as_dict()}")
+    assert tv.requests >= 4
