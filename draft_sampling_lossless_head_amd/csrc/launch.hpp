@@ -159,7 +159,8 @@ struct alignas(16) FinalInfo {
     double logZq;   // normaliser of the draft row (residual mode)
     int n;          // accepted count, or -1 for an invalid request
     int mode;       // 0 none (greedy or invalid), 1 residual, 2 bonus
-    int pad0, pad1;
+    int prev;       // draft token x_{n-1} that conditions q_n (n >= 1), else -1
+    int pad1;
 };
 
 struct VerifyArgs {

@@ -13,6 +13,7 @@
 //                          8 rebuilt weights.  A residual without mass after
 //                          rounding falls back to p_n (exact two-pass scan).
 #include <algorithm>
+#include <type_traits>
 #include <mutex>
 #include <climits>
 
@@ -21,7 +22,8 @@
 
 namespace specdec {
 
-constexpr int kResidStages = 2;
+constexpr int kResidStages = 4;   // W2 ring: items i+1 .. i+3 stream in while item i is used
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 
 // What one request row contributes: mode 1 residual (n < L), 2 bonus (n = L),
@@ -32,14 +34,13 @@ struct RowInfo {
     float lzp_hi, lzp_lo, lzq_hi, lzq_lo;
 };
 
-__device__ __forceinline__ RowInfo resid_row(const ResidArgs& A, int b) {
+__device__ __forceinline__ RowInfo resid_row_of(const ResidArgs& A, int b, const FinalInfo& f) {
     RowInfo ri;
     ri.mode = 0;
     ri.n = 0;
     ri.prow = ri.urow = 0;
     ri.lzp_hi = ri.lzp_lo = ri.lzq_hi = ri.lzq_lo = 0.0f;
     if (b >= A.B) return ri;
-    const FinalInfo f = A.fin[b];
     if (f.mode != 1 && f.mode != 2) return ri;
     ri.mode = f.mode;
     ri.n = f.n;
@@ -52,6 +53,10 @@ __device__ __forceinline__ RowInfo resid_row(const ResidArgs& A, int b) {
     return ri;
 }
 
+__device__ __forceinline__ RowInfo resid_row(const ResidArgs& A, int b) {
+    return resid_row_of(A, b, A.fin[min(b, A.B - 1)]);
+}
+
 // Weight of one token: p = exp(lp / T - logZp), q = exp(lq / T - logZq), the
 // normalisers applied as fp32 (hi, lo) pairs.
 __device__ __forceinline__ float resid_weight(const RowInfo& ri, float lp, float lq, float invT) {
@@ -61,57 +66,115 @@ __device__ __forceinline__ float resid_weight(const RowInfo& ri, float lp, float
     return fmaxf(p - q, 0.0f);
 }
 
-// Work split, stage layout and wave mapping as the streaming draft tile: a
-// work item is a 64-token slice x 128 rows; each stage holds the packed W2
-// slice, the U_n slice and the P_n slice (16-byte chunk c of row bl in slot
-// bl*8 + (c ^ ((bl>>1)&7))); wave w owns rows 32 (w & 3) .. + 31 and tokens
-// 32 (w >> 2) .. + 31 on 32x32x16 MFMAs.  Two stages: item i+1 streams in while
-// item i is contracted.
-template <int NKS>
+// Normalisers of one row as exp2 offsets: p = 2^(lp a + cp), q = 2^(lq a + cq)
+// with a = log2(e) / T and c = -logZ log2(e) as fp32 (hi, lo) pairs; q = 0
+// (cq = -inf) for rows without a residual, so max(0, p - q) = p for bonus rows.
+struct RowExp2 {
+    float cp_hi, cp_lo, cq_hi, cq_lo;
+};
+
+__device__ __forceinline__ RowExp2 row_exp2(const FinalInfo& f, int mode) {
+    RowExp2 x;
+    x.cp_hi = x.cp_lo = 0.0f;
+    x.cq_hi = -INFINITY;
+    x.cq_lo = 0.0f;
+    if (mode == 0) return x;
+    const double l2e = 1.4426950408889634;
+    const double cp = -f.logZp * l2e;
+    x.cp_hi = (float)cp;
+    x.cp_lo = (float)(cp - (double)x.cp_hi);
+    if (mode == 1) {
+        const double cq = -f.logZq * l2e;
+        x.cq_hi = (float)cq;
+        x.cq_lo = (float)(cq - (double)x.cq_hi);
+    }
+    return x;
+}
+
+// Weight of one token in both kernels, with the same operations in the same
+// order, so that the rebuild of a group reproduces the streamed weights
+// exactly when it reproduces the logits: max(0, p - q), p for bonus rows.
+__device__ __forceinline__ float resid_w(float lp, float lq, float a2, const RowExp2& cz) {
+    const float p = __builtin_amdgcn_exp2f(fmaf(lp, a2, cz.cp_hi) + cz.cp_lo);
+    const float q = __builtin_amdgcn_exp2f(fmaf(lq, a2, cz.cq_hi) + cz.cq_lo);
+    return fmaxf(p - q, 0.0f);
+}
+
+__device__ __forceinline__ float exp2_scale(float invT) { return invT * 1.4426950408889634f; }
+
+// One persistent workgroup per (row block, share) of 64-token items x 128
+// rows.  Wave w owns rows 16w .. 16w + 15 and all 64 tokens of an item on
+// 16x16x32 MFMAs: A is the packed W2 slice from LDS (tile m, operand row i is
+// token 32 (m >> 1) + 8 (i >> 2) + 4 (m & 1) + (i & 3)), B is the row's
+// conditioning embedding from registers.  Lane (n, kq) = (lane & 15, lane >> 4)
+// then holds, for row 16w + n, the 8-token groups kq of both 32-token
+// segments of the item, in token order: the U_n and P_n values it needs are
+// two 16-byte loads each, straight into registers (a wave's load covers 64
+// contiguous bytes of 16 rows), its accumulators start at U_n, and its group
+// sums need no exchange.  Only W2 goes through LDS, in a ring of four stages;
+// item i+3's loads go out before item i is used, so three items (~190 KB per
+// CU) are in flight.  Every load is issued for every item, with addresses
+// clamped for items past the share, so the wait counts are fixed.
+template <int NK>
 __global__ __launch_bounds__(kStreamWaves * 64, 1)
 void verify_resid_stream(ResidArgs A, int nitem_v, int nrb, int ws) {
-    constexpr int R = NKS * 16;
-    constexpr int W2B = kStreamItem * R * 2;
-    constexpr int SB = kStreamRows * kStreamItem * 2;   // U or P slice bytes
-    constexpr int STAGE = W2B + 2 * SB;
-    constexpr int W2P = W2B / 1024 / kStreamWaves;
-    constexpr int SP = SB / 1024 / kStreamWaves;
+    constexpr int R = NK * 32;
+    constexpr int W2B = kStreamItem * R * 2;           // packed W2 slice of one item
+    constexpr int W2P = W2B / 1024 / kStreamWaves;     // 1 KB direct-load pieces per wave
     constexpr int NCH = R / 8;
-    static_assert(W2P >= 1 && SP == 2, "piece split");
+    constexpr int LD = W2P + 4;                        // loads per item and wave
+    constexpr int NS = kResidStages;                   // stages = register sets = lookahead + 1
+    static_assert(W2P >= 1 && kStreamWaves * 16 == kStreamRows && 2 * LD < 64, "piece split");
+    static_assert(NS == 4, "the loop below is unrolled for four stages");
     extern __shared__ __align__(16) char smem_r[];
     const int V = A.V;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int h = lane >> 5;
-    const int rg = wave & 3, th = wave >> 2;
+    const int n16 = lane & 15, kq = lane >> 4;
     const int rb0 = (int)blockIdx.x / ws;
     const int jw = (int)blockIdx.x % ws;
     const int lo = (int)((long long)jw * nitem_v / ws);
     const int hi = (int)((long long)(jw + 1) * nitem_v / ws);
     const int my_n = hi - lo;
+    if (my_n <= 0) return;   // whole workgroup: no share (the launch keeps ws <= nitem_v)
     const size_t bpad = (size_t)nrb * kStreamRows;
-    const uint16_t* Ubase = A.U;   // any readable chunk, for rows without a residual
 
-    // This lane's U and P pieces: row bl, chunk c of every slice.
-    size_t uoff[SP], poff[SP];
-    int uc8[SP];
-    bool uok[SP], pok[SP];
+    const int bl = 16 * wave + n16;
+    const int b = rb0 * kStreamRows + bl;
+    // The decision and the anchor token load together; the conditioning token
+    // of q_n is the anchor (n = 0) or the draft token the decide pass recorded.
+    const int bc = min(b, A.B - 1);
+    const FinalInfo fi = A.fin[bc];
+    const int x0b = A.x0[bc];
+    const RowInfo me = resid_row_of(A, b, fi);
+    const RowExp2 cz = row_exp2(fi, me.mode);
+    const float a2 = exp2_scale(A.invT);
+    // B operand: E = W1[x_{n-1}], k = 32 kk + 8 kq .. + 7 (row 0 of W1 for
+    // rows without a residual, whose q is not used).  Issued before the first
+    // items, so waiting for item 0 covers it.
+    bf16x8_t e[NK];
+    {
+        int prev = me.n == 0 ? x0b : fi.prev;
+        prev = (me.mode == 1 && prev >= 0 && prev < V) ? prev : 0;   // verify_decide has checked it
+        const uint16_t* erow = A.W1 + (size_t)prev * R + 8 * kq;
 #pragma unroll
-    for (int q = 0; q < SP; ++q) {
-        const int sl = (q * kStreamWaves + wave) * 64 + lane;
-        const int bl = sl >> 3;
-        const int c = (sl & 7) ^ ((bl >> 1) & 7);
-        const RowInfo ri = resid_row(A, rb0 * kStreamRows + bl);
-        uc8[q] = c * 8;
-        uok[q] = ri.mode == 1;
-        pok[q] = ri.mode != 0;
-        uoff[q] = ri.urow + c * 8;
-        poff[q] = ri.prow + c * 8;
+        for (int kk = 0; kk < NK; ++kk) e[kk] = *reinterpret_cast<const bf16x8_t*>(erow + 32 * kk);
     }
-    auto issue = [&](int i) {
-        const int iv = lo + i;
-        char* st = smem_r + (i % kResidStages) * STAGE;
+    const bool uok = me.mode == 1, pok = me.mode != 0;
+    const uint16_t* ubase = A.U + me.urow + 8 * kq;
+    const uint16_t* pbase = A.P + me.prow + 8 * kq;
+
+    // A operand rows of this lane: token tm[m] of the item; its chunk swizzle
+    // depends on the token's place in its 128-token pack tile.
+    int tm[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) tm[m] = 32 * (m >> 1) + 8 * (n16 >> 2) + 4 * (m & 1) + (n16 & 3);
+
+    u32x4_t uv[NS][2], pv[NS][2];
+    auto issue_w2 = [&](int i) {
+        const int iv = lo + min(i, my_n - 1);
+        char* st = smem_r + (i % NS) * W2B;
         const char* wsrc = reinterpret_cast<const char*>(A.W2P) + (size_t)iv * W2B;
 #pragma unroll
         for (int q = 0; q < W2P; ++q) {
@@ -119,119 +182,123 @@ void verify_resid_stream(ResidArgs A, int nitem_v, int nrb, int ws) {
             __builtin_amdgcn_global_load_lds(wsrc + pc * 1024 + lane * 16,
                                              (lds_ptr_t)(st + pc * 1024), 16, 0, 0);
         }
-        const int tok = iv * kStreamItem;
+    };
+    auto issue_up = [&](auto S, int i) {
+        constexpr int s_ = decltype(S)::value;
+        const int t = (lo + min(i, my_n - 1)) * kStreamItem;
 #pragma unroll
-        for (int q = 0; q < SP; ++q) {
-            const int pc = q * kStreamWaves + wave;
-            const bool in = tok + uc8[q] < V;
-            const uint16_t* us = (uok[q] && in) ? A.U + uoff[q] + tok : Ubase;
-            const uint16_t* ps = (pok[q] && in) ? A.P + poff[q] + tok : A.P;
-            __builtin_amdgcn_global_load_lds(us, (lds_ptr_t)(st + W2B + pc * 1024), 16, 0, kCpolNT);
-            __builtin_amdgcn_global_load_lds(ps, (lds_ptr_t)(st + W2B + SB + pc * 1024), 16, 0,
-                                             kCpolNT);
+        for (int sg = 0; sg < 2; ++sg) {
+            const bool in = t + 32 * sg + 8 * kq < V;
+            const uint16_t* us = (uok && in) ? ubase + t + 32 * sg : A.U;
+            uv[s_][sg] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(us));
+        }
+#pragma unroll
+        for (int sg = 0; sg < 2; ++sg) {
+            const bool in = t + 32 * sg + 8 * kq < V;
+            const uint16_t* ps = (pok && in) ? pbase + t + 32 * sg : A.P;
+            pv[s_][sg] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(ps));
         }
     };
 
-    // This lane's compute row: its decision and conditioning row E = W1[x_{n-1}].
-    const int bl = 32 * rg + (lane & 31);
-    const int b = rb0 * kStreamRows + bl;
-    const RowInfo me = resid_row(A, b);
-    bf16x8_t e[NKS];
-    {
-        int prev = 0;
-        if (me.mode == 1) {
-            prev = me.n == 0 ? A.x0[b] : A.draft[(size_t)b * A.G + me.n - 1];
-            prev = (prev >= 0 && prev < V) ? prev : 0;   // verify_decide has checked it
-        }
-        const uint16_t* erow = A.W1 + (size_t)prev * R;
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            if (me.mode == 1) {
-                e[ks] = *reinterpret_cast<const bf16x8_t*>(erow + ks * 16 + h * 8);
-            } else {
-#pragma unroll
-                for (int t = 0; t < 8; ++t) e[ks][t] = (__bf16)0.0f;
-            }
-        }
-    }
-    wait_vmcnt_le(0);   // nothing but direct loads may be pending in the loop
-    issue(0);
-
-    int atok, arow;
-    {
-        const int i = lane & 31;
-        const int g = i >> 3, hh = (i >> 2) & 1, c = i & 3;
-        atok = 32 * th + 16 * hh + 8 * (g & 1) + 4 * (g >> 1) + c;
-        arow = atok * R;
-    }
-    int uslot[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) uslot[q] = bl * 8 + ((4 * th + 2 * h + q) ^ ((bl >> 1) & 7));
-
-    float run = 0.0f;   // this wave's half of the share's weight for the lane's row
-    for (int i = 0; i < my_n; ++i) {
+    float run = 0.0f;   // this lane's part of the share's weight for its row
+    auto step = [&](auto S, int i) {
+        constexpr int s_ = decltype(S)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm<(NS - 2) * LD>();                  // item i: items i+1, i+2 may be pending
+        asm volatile("s_barrier" ::: "memory");    // every wave's W2 pieces of item i; item
+        issue_w2(i + NS - 1);                      // i-1's stage and registers are free
+        __builtin_amdgcn_sched_barrier(0);
+        issue_up(std::integral_constant<int, (s_ + NS - 1) % NS>{}, i + NS - 1);
+        __builtin_amdgcn_sched_barrier(0);
         const int iv = lo + i;
-        wait_vmcnt_le(0);                         // item i (and item i-1's stores)
-        asm volatile("s_barrier" ::: "memory");   // every wave's pieces; stage (i+1)%2 is free
-        if (i + 1 < my_n) issue(i + 1);
-
-        const char* st = smem_r + (i % kResidStages) * STAGE;
-        const uint16_t* w2s = reinterpret_cast<const uint16_t*>(st);
-        const int sw = w2p_swizzle((iv & 1) * 64 + atok, NCH);
-        bf16x8_t afr[NKS];
+        const uint16_t* w2s = reinterpret_cast<const uint16_t*>(smem_r + (i % NS) * W2B);
+        // accumulators start at U_n: acc[2 sg + (j >> 2)][j & 3] is token
+        // iv*64 + 32 sg + 8 kq + j
+        f32x4_t acc[4];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-            afr[ks] = *reinterpret_cast<const bf16x8_t*>(w2s + arow + (((2 * ks + h) ^ sw) << 3));
-        const u32x4_t* us = reinterpret_cast<const u32x4_t*>(st + W2B);
-        const u32x4_t* ps = reinterpret_cast<const u32x4_t*>(st + W2B + SB);
-        u32x4_t uf[2], pf[2];
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            uf[q] = us[uslot[q]];
-            pf[q] = ps[uslot[q]];
-        }
-        f32x16_t acc;
-#pragma unroll
-        for (int t = 0; t < 16; ++t) acc[t] = 0.0f;
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[ks], e[ks], acc, 0, 0, 0);
-
-        // accumulator idx = 4g + c holds run position 8 (g & 1) + 4 (g >> 1) + c
-        const int v0 = iv * kStreamItem + 32 * th + 16 * h;
-        float g0 = 0.0f, g1 = 0.0f;
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
+        for (int m = 0; m < 4; ++m)
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const int pos = 8 * (g & 1) + 4 * (g >> 1) + c;
-                const uint32_t wu = uf[pos >> 3][(pos & 7) >> 1];
-                const uint32_t wp = pf[pos >> 3][(pos & 7) >> 1];
-                const float lq = acc[4 * g + c] + ((pos & 1) ? __uint_as_float(wu & 0xFFFF0000u)
-                                                             : __uint_as_float(wu << 16));
-                const float lp = (pos & 1) ? __uint_as_float(wp & 0xFFFF0000u)
-                                           : __uint_as_float(wp << 16);
-                float w = resid_weight(me, lp, lq, A.invT);
-                w = v0 + pos < V ? w : 0.0f;
-                if (pos < 8) g0 += w;
-                else g1 += w;
+                const int j = 4 * (m & 1) + c;
+                const uint32_t wu = uv[s_][m >> 1][j >> 1];
+                acc[m][c] = (j & 1) ? __uint_as_float(wu & 0xFFFF0000u) : __uint_as_float(wu << 16);
             }
-        if (me.mode != 0) {
-            const size_t si = (2 * (size_t)iv + th) * bpad + b;
-            *reinterpret_cast<float2*>(A.gsums + si * 4 + 2 * h) = make_float2(g0, g1);
+        // operand (m, kk): chunk 4 kk + kq of token row tm[m], slot (4 kk + kq) ^ sw
+        int abase[4], c0[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            abase[m] = tm[m] * R;
+            c0[m] = kq ^ w2p_swizzle((iv & 1) * kStreamItem + tm[m], NCH);
         }
-        float tot = g0 + g1;
-        tot += __shfl_xor(tot, 32);
-        run += tot;
-    }
+        auto lda = [&](int m, int kk) {
+            return *reinterpret_cast<const bf16x8_t*>(w2s + abase[m] + (((4 * kk) ^ c0[m]) << 3));
+        };
+        bf16x8_t a0[4], a1[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) a0[m] = lda(m, 0);
+#pragma unroll
+        for (int kk = 0; kk < NK; kk += 2) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) a1[m] = lda(m, kk + 1);
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[m], e[kk], acc[m], 0, 0, 0);
+            if (kk + 2 < NK) {
+#pragma unroll
+                for (int m = 0; m < 4; ++m) a0[m] = lda(m, kk + 2);
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[m], e[kk + 1], acc[m], 0, 0, 0);
+        }
+#pragma unroll
+        for (int sg = 0; sg < 2; ++sg) {
+            float g = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t wp = pv[s_][sg][j >> 1];
+                const float lp = (j & 1) ? __uint_as_float(wp & 0xFFFF0000u) : __uint_as_float(wp << 16);
+                g += resid_w(lp, acc[2 * sg + (j >> 2)][j & 3], a2, cz);
+            }
+            g = iv * kStreamItem + 32 * sg + 8 * kq < V ? g : 0.0f;
+            A.gsums[((2 * (size_t)iv + sg) * bpad + b) * 4 + kq] = g;
+            run += g;
+        }
+    };
 
-    // Share sums: the token-half-1 waves hand theirs to the half-0 waves.
-    float* xs = reinterpret_cast<float*>(smem_r);   // the stages are idle now
-    wait_vmcnt_le(0);
-    __syncthreads();
-    if (th == 1 && h == 0) xs[bl] = run;
-    __syncthreads();
-    if (th == 0 && h == 0 && me.mode != 0) A.sup[(size_t)jw * bpad + b] = run + xs[bl];
+    // Issue order E, W2(0) UP(0) .. W2(2) UP(2), then per step W2(i+3) UP(i+3):
+    // after item i's last load come exactly items i+1 and i+2 (stores aside).
+    __builtin_amdgcn_sched_barrier(0);
+    issue_w2(0);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_up(std::integral_constant<int, 0>{}, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_w2(1);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_up(std::integral_constant<int, 1>{}, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_w2(2);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_up(std::integral_constant<int, 2>{}, 2);
+    // Whole rounds of four steps, then the last zero to three steps outside the
+    // loop (an exit from inside a round would let the compiler merge
+    // pending-load states at the loop head and drain every load there).
+    int i = 0;
+    for (; i + NS - 1 < my_n; i += NS) {
+        step(std::integral_constant<int, 0>{}, i);
+        step(std::integral_constant<int, 1>{}, i + 1);
+        step(std::integral_constant<int, 2>{}, i + 2);
+        step(std::integral_constant<int, 3>{}, i + 3);
+    }
+    if (i < my_n) step(std::integral_constant<int, 0>{}, i);
+    if (i + 1 < my_n) step(std::integral_constant<int, 1>{}, i + 1);
+    if (i + 2 < my_n) step(std::integral_constant<int, 2>{}, i + 2);
+    wait_vm<0>();   // no direct load into LDS outlives the workgroup
+
+    // Share sum of the row: the four lanes kq of row n.
+    run += __shfl_xor(run, 16);
+    run += __shfl_xor(run, 32);
+    if (kq == 0 && me.mode != 0) A.sup[(size_t)jw * bpad + b] = run;
 }
 
 __global__ __launch_bounds__(64)
@@ -392,7 +459,7 @@ void verify_resid_finalize(ResidArgs A, int nitem, int ws, int bpad) {
     part += __shfl_xor(part, 1);
     part += __shfl_xor(part, 2);
     part += __shfl_xor(part, 4);
-    const float wt = vt < V ? resid_weight(ri, lp, lq + part, invT) : 0.0f;
+    const float wt = vt < V ? resid_w(lp, lq + part, exp2_scale(invT), row_exp2(A.fin[b], ri.mode)) : 0.0f;
     const float w8 = __shfl(wt, (lane & 7) * 8);
     double trem;
     const int tsel = wave_pick(lane < 8 ? (double)w8 : 0.0, grem, trem);
@@ -406,17 +473,17 @@ bool resid_streams(int B, int V, int r) {
     return 2 * ((nitem_v + ws - 1) / ws) <= 64;
 }
 
-template <int NKS>
+template <int NK>
 static void launch_resid_stream(const ResidArgs& A, int nitem_v, int nrb, int ws, hipStream_t s) {
-    constexpr int STAGE = kStreamItem * NKS * 16 * 2 + 2 * kStreamRows * kStreamItem * 2;
+    constexpr int STAGE = kStreamItem * NK * 32 * 2;
     // raise the dynamic LDS limit once per process (thread-safe)
     static std::once_flag attr_once;
     std::call_once(attr_once, [&] {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&verify_resid_stream<NKS>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&verify_resid_stream<NK>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         (void)hipGetLastError();
     });
-    hipLaunchKernelGGL((verify_resid_stream<NKS>), dim3(nrb * ws), dim3(kStreamWaves * 64),
+    hipLaunchKernelGGL((verify_resid_stream<NK>), dim3(nrb * ws), dim3(kStreamWaves * 64),
                        (size_t)kResidStages * STAGE, s, A, nitem_v, nrb, ws);
 }
 
@@ -426,9 +493,9 @@ hipError_t verify_resid_launch(const ResidArgs& A, hipStream_t s) {
     const int nitem_v = (A.V + kStreamItem - 1) / kStreamItem;
     const int nrb = (A.B + kStreamRows - 1) / kStreamRows;
     const int ws = stream_shares(A.B, A.V);
-    if (A.r == 256) launch_resid_stream<16>(A, nitem_v, nrb, ws, s);
-    else if (A.r == 128) launch_resid_stream<8>(A, nitem_v, nrb, ws, s);
-    else launch_resid_stream<4>(A, nitem_v, nrb, ws, s);
+    if (A.r == 256) launch_resid_stream<8>(A, nitem_v, nrb, ws, s);
+    else if (A.r == 128) launch_resid_stream<4>(A, nitem_v, nrb, ws, s);
+    else launch_resid_stream<2>(A, nitem_v, nrb, ws, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(verify_resid_finalize, dim3(A.B), dim3(64), 0, s, A, nitem_v, ws,

@@ -465,7 +465,8 @@ void verify_decide(VerifyArgs a) {
             f.logZq = 0.0;
             f.n = -1;
             f.mode = 0;
-            f.pad0 = f.pad1 = 0;
+            f.prev = -1;
+            f.pad1 = 0;
             a.fin[b] = f;
         }
         return;
@@ -484,7 +485,8 @@ void verify_decide(VerifyArgs a) {
         f.logZq = lzq_n;
         f.n = n;
         f.mode = a.greedy ? 0 : (n < L ? 1 : 2);
-        f.pad0 = f.pad1 = 0;
+        f.prev = n > 0 ? dr[n - 1] : -1;
+        f.pad1 = 0;
         a.fin[b] = f;
     }
 }
