@@ -599,6 +599,8 @@ unsigned persist_set_poll_limit(unsigned polls) {
     return g_poll_limit.exchange(polls == 0 ? kBarrierPolls : polls);
 }
 
+unsigned persist_poll_limit() { return g_poll_limit.load(); }
+
 int persist_set_mode(int mode) {
     if (mode < 0 || mode > 2) return -1;
     return g_persist_mode.exchange(mode);

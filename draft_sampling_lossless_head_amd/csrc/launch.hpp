@@ -131,6 +131,7 @@ hipError_t persist_clear_abort(unsigned* bar, hipStream_t s);
 int persist_set_mode(int mode);
 int persist_mode();
 unsigned persist_set_poll_limit(unsigned polls);   // 0: the default
+unsigned persist_poll_limit();                     // also the split tree walk's wait limit
 // W2 [r, V] bf16 -> packed image of w2p_bytes(r, V) bytes.
 hipError_t w2_pack_launch(const uint16_t* W2, uint16_t* W2P, int r, int V, hipStream_t s);
 // Recompute the logits of row b at position row_pos[b] into out [B, V] with the
@@ -306,6 +307,9 @@ struct TreeVerifyArgs {
     int32_t* accepted;          // [B] out
     int32_t* out_tokens;        // [B, M + 1] out
     int32_t* path;              // [B, M] out or null
+    int split;                  // workgroups per request (set by the launcher)
+    uint32_t epoch;             // tag of this call's exchange words (set by the launcher)
+    unsigned poll_limit;        // polls before an exchange wait gives up
 };
 hipError_t verify_tree_launch(const TreeVerifyArgs& a, hipStream_t s);
 

@@ -538,6 +538,7 @@ spec_status_t spec_verify_tree(const void* P, int p_dtype, const void* Q, int q_
     a.accepted = accepted;
     a.out_tokens = out_tokens;
     a.path = path;
+    a.poll_limit = persist_poll_limit();
     hipStream_t s = static_cast<hipStream_t>(stream);
     void* t = prof_begin("verify_tree", s);
     hipError_t e = verify_tree_launch(a, s);

@@ -26,10 +26,14 @@
  *   returns except in its workspace and in these process-wide settings, each
  *   atomic and read once per call when the call launches its kernels:
  *     spec_draft_set_persistent  engine of the q-free Markov draft (default 1);
- *     spec_draft_set_poll_limit  wait limit of the persistent draft;
+ *     spec_draft_set_poll_limit  wait limit of the persistent draft and of
+ *                                the split tree walk;
  *     spec_profile_enable        kernel timing (off by default; a mutex);
  *   plus per-device caches of device attributes (CU count, cooperative
- *   launch support) and each kernel's LDS limit, set once per process.
+ *   launch support) and each kernel's LDS limit, set once per process, and
+ *   two areas of static device memory per device: the exchange words of the
+ *   split tree walk (spec_verify_tree, 64 KB) and the scratch of
+ *   spec_verify_noalloc.
  * - `stream` is a hipStream_t passed as void* (NULL = default stream).
  *   All work is enqueued asynchronously on it; outputs are valid once the
  *   stream has been synchronised.
@@ -411,8 +415,16 @@ spec_status_t spec_verify_rnn(
  * out_tokens [B, M + 1] out int32: the accepted nodes' tokens, the final
  *            token, then -1 (all -1 for an invalid request)
  * path       [B, M] optional out int32: the accepted node ids, then -1
- * One workgroup per request; every tested sibling after the first costs
- * one pass over the node's two rows.  No workspace.
+ * W workgroups per request, W = min(8, CUs / B, ceil(V / 512)) (one when the
+ * batch fills the device): each covers a range of the vocabulary, every
+ * tested sibling after the first costs one pass over the node's two rows,
+ * and the workgroups of a request exchange each pass's partial sums through
+ * the library's static exchange area (device memory, tagged per call).  No
+ * workspace.  With W > 1 all of a call's workgroups must be resident at once,
+ * which an otherwise idle device gives; calls that overlap on one device
+ * (other streams) are not supported then.  Every wait of the walk is bounded
+ * (spec_draft_set_poll_limit): when one gives up, the requests not finished
+ * report accepted -1 with all-(-1) out_tokens and path.
  * Errors: SPEC_ERR_INVALID (null required pointers, B or M < 0, V outside
  * [1, 2^20], T < 0 or NaN), SPEC_ERR_UNSUPPORTED (dtype, M > 1024,
  * misaligned P or Q), SPEC_ERR_HIP (launch).
@@ -569,10 +581,11 @@ spec_status_t spec_profile_read(int *launches, double *total_ms);
  * words of its rows, a finalize wave for the share summaries of its row) is a
  * poll that gives up after `polls` polls (about 1 us each on an idle device):
  * it sets the launch's abort word, every workgroup leaves at its next poll,
- * and the rows not drawn keep token -1 (spec_draft_status reports 1).  0
- * restores the default (2^20 polls).  Lets a test force that path from the
- * host.  Process-wide and atomic; applies to later launches; returns the
- * previous limit.
+ * and the rows not drawn keep token -1 (spec_draft_status reports 1).  The
+ * exchange waits of the split tree walk (spec_verify_tree with more than one
+ * workgroup per request) use the same limit.  0 restores the default (2^20
+ * polls).  Lets a test force that path from the host.  Process-wide and
+ * atomic; applies to later launches; returns the previous limit.
  */
 unsigned spec_draft_set_poll_limit(unsigned polls);
 

@@ -186,3 +186,50 @@ def test_tree_verify_root_token_law(orc):
          f"mean accepted {g['accepted'].float().mean().item():.3f}")
     assert p_target > 1e-4
     assert p_draft < 1e-8
+
+
+def test_tree_verify_bench_shape_split(orc):
+    """The bench's tree workload (32 trees x 16 nodes x 151936 tokens, bf16):
+    eight workgroups per request on a 256-CU device, every request against the
+    oracle."""
+    sd = require_gpu()
+    B, M, V = 32, 16, 151936
+    note(f"tree verify split walk B={B} M={M} V={V} bf16")
+    wl = workloads.make_tree_verify(B, M, V, seed=1234, dtype="bf16", sigma=1.0, levels=4)
+    tok = _drawn_tokens(orc, wl, 1.0, np.random.default_rng(9))
+    g = _run(sd, wl, tok, 1.0, 31)
+    u = orc.tree_uniforms(31, 5, B, M)
+    tally = _compare_all(orc, wl, tok, 1.0, g, u, "bench shape")
+    note(f"  {tally.as_dict()} accepted={g['accepted'].tolist()}")
+    assert g["accepted"].min() >= 0
+
+
+def test_tree_verify_split_gives_up_cleanly(orc):
+    """With a wait limit of two polls (set from the host) the split walk's
+    exchanges give up: the launch still ends, every request is either valid
+    (and agrees with the oracle) or reports accepted -1 with all-(-1) outputs,
+    and the next call with the default limit agrees with the oracle again."""
+    sd = require_gpu()
+    B, M, V = 16, 12, 40000
+    note(f"tree verify split walk, wait limit 2: B={B} M={M} V={V}")
+    wl = workloads.make_tree_verify(B, M, V, seed=77, dtype="bf16", sigma=0.8, levels=3)
+    tok = _drawn_tokens(orc, wl, 1.0, np.random.default_rng(3))
+    u = orc.tree_uniforms(8, 5, B, M)
+    try:
+        sd.spec_draft_set_poll_limit(2)
+        bad = _run(sd, wl, tok, 1.0, 8)
+    finally:
+        sd.spec_draft_set_poll_limit(0)
+    again = _run(sd, wl, tok, 1.0, 8)
+    gave_up = bad["accepted"] == -1
+    note(f"  requests that gave up: {int(gave_up.sum())} of {B}")
+    assert np.all(bad["out_tokens"][gave_up] == -1)
+    assert np.all(bad["path"][gave_up] == -1)
+    keep = np.flatnonzero(~gave_up)
+    if len(keep):
+        sub = dict(wl, B=len(keep), P=wl["P"][keep], Q=wl["Q"][keep], parent=wl["parent"][keep])
+        gk = {k: v[keep] for k, v in bad.items()}
+        _compare_all(orc, sub, tok[keep], 1.0, gk, u[keep], "kept")
+    tally = _compare_all(orc, wl, tok, 1.0, again, u, "again")
+    assert again["accepted"].min() >= 0
+    note(f"  again: {tally.as_dict()}")
