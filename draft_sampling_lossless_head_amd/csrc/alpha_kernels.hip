@@ -6,8 +6,9 @@
 // row p_k and the draft row q_k:
 //   1. per row the max of the logits and sum exp((l - max) / T) (greedy: the
 //      argmax, lowest id on ties);
-//   2. sum_v min(p(v), q(v)) and sum_v |p(v) - q(v)| with p = exp((l_p - m_p)
-//      / T) / Z_p and q likewise.
+//   2. sum_v min(p(v), q(v)) with p = exp((l_p - m_p) / T) / Z_p and q
+//      likewise, as one exponential of the smaller exponent per token; the
+//      total variation is 1 - alpha.
 // Per-thread sums are fp32 (a few hundred terms each), the workgroup sums
 // fp64.  At T = 0 both distributions are one-hot at their argmax, so alpha is
 // 1 when the two argmaxes agree and 0 otherwise.
@@ -179,17 +180,23 @@ void acceptance_rate_rows(AlphaArgs A) {
         return;
     }
 
-    // 2. sum min(p, q) and sum |p - q|
-    const float rzp = 1.0f / P.s, rzq = 1.0f / Q.s;
-    float amin = 0.0f, adiff = 0.0f;
+    // 2. alpha = sum_v min(p(v), q(v)) with min(2^a, 2^b) = 2^min(a, b): one
+    //    exponential per token, the exponents a = l_p sc - (m_p sc + log2 Z_p)
+    //    with the offset as an fp32 (hi, lo) pair (the same rounded sc scales
+    //    the logits and the row max, so its rounding cancels in l - m).  TV is
+    //    1 - alpha (sum |p - q| = sum p + sum q - 2 sum min(p, q)).
+    const double op = (double)P.m * (double)sc + log2((double)P.s);
+    const double oq = (double)Q.m * (double)sc + log2((double)Q.s);
+    const float op_hi = (float)op, op_lo = (float)(op - (double)op_hi);
+    const float oq_hi = (float)oq, oq_lo = (float)(oq - (double)oq_hi);
+    float amin = 0.0f;
     auto add8 = [&](int n) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             if (j < n) {
-                const float pv = __builtin_amdgcn_exp2f((x[j] - P.m) * sc) * rzp;
-                const float qv = __builtin_amdgcn_exp2f((y[j] - Q.m) * sc) * rzq;
-                amin += fminf(pv, qv);
-                adiff += fabsf(pv - qv);
+                const float ea = fmaf(x[j], sc, -op_hi) - op_lo;
+                const float eb = fmaf(y[j], sc, -oq_hi) - oq_lo;
+                amin += __builtin_amdgcn_exp2f(fminf(ea, eb));
             }
         }
     };
@@ -211,10 +218,9 @@ void acceptance_rate_rows(AlphaArgs A) {
         }
     }
     const double smin = block_sum_f64((double)amin, lds_d);
-    const double sdiff = block_sum_f64((double)adiff, lds_d);
     if (tid == 0) {
         A.alpha[oi] = (float)smin;
-        if (A.tv) A.tv[oi] = (float)(0.5 * sdiff);
+        if (A.tv) A.tv[oi] = (float)(1.0 - smin);
     }
 }
 

@@ -445,7 +445,8 @@ spec_status_t spec_verify_tree(const void *P, int p_dtype, const void *Q, int q_
  * For every request b and position k < L_b (L_b = lens[b], or gamma_max when
  * lens is NULL): p_k = softmax(P row / T), q_k = softmax(Q row / T),
  *   alpha[b, k] = sum_v min(p_k(v), q_k(v)),
- *   tv[b, k]    = 1/2 sum_v |p_k(v) - q_k(v)|   (optional; equals 1 - alpha).
+ *   tv[b, k]    = 1/2 sum_v |p_k(v) - q_k(v)|   (optional; returned as
+ *                 1 - alpha, which it equals).
  * T = 0: both are one-hot at their argmax (lowest id on ties), so alpha is 1
  * when the argmaxes agree and 0 otherwise.  The row layout is spec_verify's:
  * P dense [B, gamma_max + 1, V] or packed rows from p_row_off[b] on (position
