@@ -758,7 +758,7 @@ def main():
     ap.add_argument("--gemm-only", action="store_true",
                     help="only the GEMM-only measurement of the bias contraction (library GEMM, "
                          "W2 warm); prints its own JSON line")
-    ap.add_argument("--traffic-kernel", default="draft_persist<16, 5, 4, false>")
+    ap.add_argument("--traffic-kernel", default="draft_persist<16, 5, 4, false, false>")
     ap.add_argument("--traffic-label", default="draft_persist")
     args = ap.parse_args()
     if args.mfma_from:

@@ -1731,7 +1731,8 @@ hipError_t draft_finalize_launch(const DraftArgs& a, int k, hipStream_t s) {
         f.V = a.V;
         f.invT = a.invT;
         f.greedy = a.greedy;
-        f.U = static_cast<const uint16_t*>(a.U);
+        f.U = a.U;
+        f.u_f32 = 0;   // the streaming tile takes bf16 U only
         f.W1 = static_cast<const uint16_t*>(a.W1);
         f.W2P = a.W2T;
         f.r = a.r;

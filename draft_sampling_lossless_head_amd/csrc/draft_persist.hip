@@ -54,7 +54,7 @@ namespace specdec {
 constexpr int kPersistWaves = 4;             // one wave per SIMD
 constexpr int kPersistRows = 64;             // request rows of one row block
 constexpr int kPersistFinWgs = 16;           // workgroups that only finalize
-constexpr int kPersistUnit = 2048;           // U bytes of one unit: 32 rows x 32 tokens
+constexpr int kPersistUnit = 2048;           // bf16 U bytes of one unit: 32 rows x 32 tokens
 constexpr unsigned kBarrierPolls = 1u << 20; // polls (with s_sleep) before a wait gives up
 
 // Both values of a lane pair (l, l ^ 32), one in each result: swapping the
@@ -81,6 +81,8 @@ __device__ __forceinline__ void pair_argmax32(float& m, int& a) {
 // Chunk swizzle of a U ring slot (32 rows x 64 bytes): conflict-free reads of
 // chunks 2h and 2h + 1 of row m by lane (m, h), in groups of 8 or 16 lanes.
 __device__ __forceinline__ int uswz(int m) { return ((m >> 1) ^ (m >> 2)) & 3; }
+// The same for fp32 U (32 rows x 128 bytes): chunks 4h .. 4h + 3 of row m.
+__device__ __forceinline__ int uswz8(int m) { return m & 7; }
 
 struct PersistArgs {
     FinStreamArgs fin;   // finalize inputs and outputs (tokens, q_logZ, q_tok, ...)
@@ -94,10 +96,11 @@ struct PersistArgs {
 };
 
 // Layout of the synchronisation words (unsigned, in the workspace): the abort
-// word and eight bf16 -inf values.
+// word, eight bf16 -inf values and four fp32 -inf values.
 constexpr int kBarAbort = 0;
 constexpr int kBarNegInf = 4;     // [4, 8)
-constexpr int kBarWords = 8;
+constexpr int kBarNegInfF = 8;    // [8, 12)
+constexpr int kBarWords = 12;
 static_assert(kBarWords * sizeof(unsigned) <= kPersistBarBytes, "barrier words");
 
 // Launch preamble: clears the abort word, the token words [B] and the tagged
@@ -108,7 +111,8 @@ __global__ void persist_bar_reset(unsigned* bar, uint64_t* tflag, int B, uint64_
                                   size_t ns, int32_t* tokens, size_t ntok) {
     const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     const size_t stride = (size_t)gridDim.x * blockDim.x;
-    if (t < (size_t)kBarWords) bar[t] = (t >= (size_t)kBarNegInf) ? 0xFF80FF80u : 0u;
+    if (t < (size_t)kBarWords)
+        bar[t] = t >= (size_t)kBarNegInfF ? 0xFF800000u : (t >= (size_t)kBarNegInf ? 0xFF80FF80u : 0u);
     if (t < (size_t)B) tflag[t] = 0u;
     for (size_t i = t; i < 2 * ns; i += stride) sup64[i] = 0u;
     for (size_t i = t; i < ntok; i += stride) tokens[i] = -1;
@@ -152,21 +156,33 @@ __device__ __forceinline__ bool rows_tokens(unsigned* bar, const uint64_t* tflag
     return *ok_s != 0;
 }
 
-template <int NKS, int NB, int NR, bool GREEDY>
-__global__ __launch_bounds__(kPersistWaves * 64, 1)
-void draft_persist(PersistArgs P) {
+// Per U element type: value bytes, unit bytes, direct loads per unit and
+// wave, 16-byte chunks per unit row.
+template <bool UF> struct PersistU {
+    static constexpr int ES = UF ? 4 : 2;
+    static constexpr int UNIT = kPersistUnit * ES / 2;
+    static constexpr int LU = UF ? 4 : 2;
+    static constexpr int CPR = UF ? 8 : 4;
+};
+
+// The kernel's body, a device function so that the host pass, which only
+// needs the kernel's entry stub, never instantiates it (its instantiation
+// there silently failed once the body depended on UF).
+template <int NKS, int NB, int NR, bool GREEDY, bool UF>
+__device__ __forceinline__ void draft_persist_body(const PersistArgs& P) {
     constexpr int R = NKS * 16;
     constexpr int NCH = R / 8;                  // 16-byte chunks per rank row
     constexpr int D = NR - 2;                   // units in flight per wave
     constexpr int EB = kPersistRows * R * 2;    // E rows of one row block
+    using UT = PersistU<UF>;
     static_assert(NCH >= 8 && NCH % 2 == 0, "rank");
-    static_assert(2 * D <= 32, "vmcnt waits");
+    static_assert(UT::LU * D <= 32, "vmcnt waits");
     static_assert(NKS >= 4, "the U read follows the stages that use the previous unit's U");
     extern __shared__ __align__(16) char smem_p[];
     __shared__ int ok_s;
     char* e_lds = smem_p;
     char* ring = smem_p + EB;
-    int* xprev = reinterpret_cast<int*>(ring + kPersistWaves * NR * kPersistUnit);
+    int* xprev = reinterpret_cast<int*>(ring + kPersistWaves * NR * UT::UNIT);
     float* xsum = reinterpret_cast<float*>(xprev + kPersistRows);  // [wave][row][3]
 
     const FinStreamArgs& F = P.fin;
@@ -240,13 +256,18 @@ void draft_persist(PersistArgs P) {
         int am;
     };
     // vb: the first of this lane's 16 tokens (greedy only).
-    auto stage = [&](Reducer& R, const f32x16_t& ac, const u32x4_t (&uf)[2], int vb, int st) {
+    auto stage = [&](Reducer& R, const f32x16_t& ac, const auto& uf, int vb, int st) {
         if (st < 4) {
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const int pos = 8 * (st & 1) + 4 * (st >> 1) + c;
-                const uint32_t w = uf[pos >> 3][(pos & 7) >> 1];
-                const float uv = (pos & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
+                float uv;
+                if constexpr (UF) {
+                    uv = __uint_as_float(uf[pos >> 2][pos & 3]);
+                } else {
+                    const uint32_t w = uf[pos >> 3][(pos & 7) >> 1];
+                    uv = (pos & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
+                }
                 R.x[pos] = ac[4 * st + c] + uv;
             }
         } else if (st == 4) {
@@ -285,16 +306,17 @@ void draft_persist(PersistArgs P) {
         o.am = GREEDY ? R.am : 0;
         return o;
     };
-    auto reduce = [&](const f32x16_t& ac, const u32x4_t (&uf)[2], int vb) -> Red {
+    auto reduce = [&](const f32x16_t& ac, const auto& uf, int vb) -> Red {
         Reducer R;
 #pragma unroll
         for (int st = 0; st < 15; ++st) stage(R, ac, uf, vb, st);
         return finish(R);
     };
 
-    const uint16_t* ninf = reinterpret_cast<const uint16_t*>(P.bar + kBarNegInf);
-    const uint16_t* usrc[2];
-    int utok[2], urow[2];
+    const char* ninf = reinterpret_cast<const char*>(P.bar + (UF ? kBarNegInfF : kBarNegInf));
+    const char* ubase = reinterpret_cast<const char*>(F.U);
+    const char* usrc[4];   // the first UT::LU used
+    int utok[4], urow[4];
     int rows_b = 0;
     const size_t rg_step = (size_t)32 * G * (size_t)V;
     int ci = 0, cj = 0, cs = 0;
@@ -307,12 +329,13 @@ void draft_persist(PersistArgs P) {
         const int rr0 = rbb * kPersistRows;
         rows_b = min(kPersistRows, B - rr0);
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int m = 16 * q + (ln >> 2);
-            const int c = (ln & 3) ^ uswz(m);
+        for (int q = 0; q < UT::LU; ++q) {
+            // load q covers rows (32 / UT::LU) q .. + 32 / UT::LU - 1, UT::CPR lanes per row
+            const int m = (32 / UT::LU) * q + ln / UT::CPR;
+            const int c = UF ? ((ln & 7) ^ uswz8(m)) : ((ln & 3) ^ uswz(m));
             urow[q] = m;
-            utok[q] = kStreamSeg * (blo + wave) + 8 * c;
-            usrc[q] = F.U + ((size_t)(rr0 + m) * G + kk) * (size_t)V + utok[q];
+            utok[q] = kStreamSeg * (blo + wave) + (16 / UT::ES) * c;
+            usrc[q] = ubase + (((size_t)(rr0 + m) * G + kk) * (size_t)V + utok[q]) * UT::ES;
         }
         ci = 0;
         cj = 0;
@@ -363,13 +386,13 @@ void draft_persist(PersistArgs P) {
             // of the -inf chunk into the slot just freed, so every wait allows
             // the same count.
             auto issue_next = [&]() {
-                char* dst = ring + (wave * NR + cs) * kPersistUnit;
+                char* dst = ring + (wave * NR + cs) * UT::UNIT;
                 const int rlim = rows_b - 32 * ci;   // rows of the group present (<= 0 past the last)
                 const int vlim = V - 128 * cj;
 #pragma unroll
-                for (int q = 0; q < 2; ++q) {
+                for (int q = 0; q < UT::LU; ++q) {
                     const bool ok = urow[q] < rlim && utok[q] < vlim;
-                    __builtin_amdgcn_global_load_lds(ok ? usrc[q] + coff : ninf,
+                    __builtin_amdgcn_global_load_lds(ok ? usrc[q] + coff * UT::ES : ninf,
                                                      (lds_ptr_t)(dst + q * 1024), 16, 0, 0);
                 }
                 coff += 128;
@@ -384,7 +407,7 @@ void draft_persist(PersistArgs P) {
                 setup_cursor(k, rb);
 #pragma unroll
                 for (int u = 0; u < D; ++u) issue_next();
-                wait_vm<2 * D>();                      // this wave's E loads have landed
+                wait_vm<UT::LU * D>();                     // this wave's E loads have landed
             } else {
                 wait_vm<0>();                          // E (and the U issued before it)
             }
@@ -438,8 +461,11 @@ void draft_persist(PersistArgs P) {
             f32x16_t accp;
 #pragma unroll
             for (int q = 0; q < 16; ++q) accp[q] = 0.0f;
-            const u32x4_t ninf4 = u32x4_t{0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u};
-            u32x4_t ufp[2] = {ninf4, ninf4};
+            const uint32_t ni = UF ? 0xFF800000u : 0xFF80FF80u;
+            const u32x4_t ninf4 = u32x4_t{ni, ni, ni, ni};
+            u32x4_t ufp[4];
+#pragma unroll
+            for (int q = 0; q < UT::LU; ++q) ufp[q] = ninf4;
             Red redh;
             redh.m = -INFINITY;
             redh.g0 = redh.g1 = 0.0f;
@@ -485,11 +511,13 @@ void draft_persist(PersistArgs P) {
                                 // U of this unit for the next reduction (the stages that
                                 // read the previous unit's U are done): D newer units are
                                 // in flight.
-                                wait_vm<2 * D>();
+                                wait_vm<UT::LU * D>();
                                 const u32x4_t* us = reinterpret_cast<const u32x4_t*>(
-                                    ring + (wave * NR + cu) * kPersistUnit);
-                                ufp[0] = us[4 * n + ((2 * h) ^ uswz(n))];
-                                ufp[1] = us[4 * n + ((2 * h + 1) ^ uswz(n))];
+                                    ring + (wave * NR + cu) * UT::UNIT);
+#pragma unroll
+                                for (int q = 0; q < UT::LU; ++q)
+                                    ufp[q] = UF ? us[UT::CPR * n + ((4 * h + q) ^ uswz8(n))]
+                                                : us[UT::CPR * n + ((2 * h + q) ^ uswz(n))];
                             }
                             __builtin_amdgcn_sched_barrier(0);
                         }
@@ -559,6 +587,12 @@ void draft_persist(PersistArgs P) {
     }
 }
 
+template <int NKS, int NB, int NR, bool GREEDY, bool UF>
+__global__ __launch_bounds__(kPersistWaves * 64, 1)
+void draft_persist(PersistArgs P) {
+    draft_persist_body<NKS, NB, NR, GREEDY, UF>(P);
+}
+
 // Blocks per wave held in registers (320 VGPRs of W2 operands) and U ring
 // slots per wave (LDS: E rows + rings + tokens + run summaries <= 160 KB).
 // Shallow rings are faster (measured): the units' 64-byte row pieces stream
@@ -570,9 +604,10 @@ template <> struct PersistShape<16> { static constexpr int NB = 5, NR = 4; };
 template <> struct PersistShape<8> { static constexpr int NB = 10, NR = 5; };
 template <> struct PersistShape<4> { static constexpr int NB = 20, NR = 5; };
 
-template <int NKS>
+template <int NKS, bool UF>
 static size_t persist_lds() {
-    return (size_t)kPersistRows * NKS * 16 * 2 + (size_t)kPersistWaves * PersistShape<NKS>::NR * kPersistUnit +
+    return (size_t)kPersistRows * NKS * 16 * 2 +
+           (size_t)kPersistWaves * PersistShape<NKS>::NR * kPersistUnit * (UF ? 2 : 1) +
            kPersistRows * sizeof(int) + (size_t)kPersistWaves * kPersistRows * 3 * sizeof(float);
 }
 
@@ -644,7 +679,7 @@ static int persist_grid(int V, int* nu_out) {
 
 bool draft_persists(const DraftArgs& a, int mode) {
     if (mode == 0) return false;
-    if (!(a.head == kHeadMarkov && a.w_bf16 && a.u_bf16 && !a.q_logits && (a.V % 8) == 0 &&
+    if (!(a.head == kHeadMarkov && a.w_bf16 && !a.q_logits && (a.V % 8) == 0 &&
           persist_nks(a.r) != 0 && a.B > 0 && a.gamma > 0))
         return false;
     int nu = 0;
@@ -653,19 +688,19 @@ bool draft_persists(const DraftArgs& a, int mode) {
     return (nblk + nu - 1) / nu <= kPersistWaves * persist_nb(a.r);   // <= 20 blocks per share
 }
 
-template <int NKS>
+template <int NKS, bool UF>
 static hipError_t launch_persist(const PersistArgs& p, int ng, bool greedy, bool coop,
                                  hipStream_t s) {
     constexpr int NB = PersistShape<NKS>::NB, NR = PersistShape<NKS>::NR;
-    const void* fn = greedy ? reinterpret_cast<const void*>(&draft_persist<NKS, NB, NR, true>)
-                            : reinterpret_cast<const void*>(&draft_persist<NKS, NB, NR, false>);
-    const size_t lds = persist_lds<NKS>();
+    const void* fn = greedy ? reinterpret_cast<const void*>(&draft_persist<NKS, NB, NR, true, UF>)
+                            : reinterpret_cast<const void*>(&draft_persist<NKS, NB, NR, false, UF>);
+    const size_t lds = persist_lds<NKS, UF>();
     // raise the dynamic LDS limit once per process (thread-safe)
     static std::once_flag attr_once;
     std::call_once(attr_once, [&] {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&draft_persist<NKS, NB, NR, true>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&draft_persist<NKS, NB, NR, true, UF>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&draft_persist<NKS, NB, NR, false>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&draft_persist<NKS, NB, NR, false, UF>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         (void)hipGetLastError();
     });
@@ -714,7 +749,8 @@ hipError_t draft_persist_launch(const DraftArgs& a, unsigned* bar, int mode, hip
     f.V = a.V;
     f.invT = a.invT;
     f.greedy = a.greedy;
-    f.U = static_cast<const uint16_t*>(a.U);
+    f.U = a.U;
+    f.u_f32 = a.u_bf16 ? 0 : 1;
     f.W1 = static_cast<const uint16_t*>(a.W1);
     f.W2P = a.W2T;
     f.r = a.r;
@@ -739,10 +775,11 @@ hipError_t draft_persist_launch(const DraftArgs& a, unsigned* bar, int mode, hip
                        reinterpret_cast<uint64_t*>(a.sup), ns, a.tokens, ntok);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    const bool g = a.greedy != 0, c = mode == 2;
     switch (persist_nks(a.r)) {
-    case 16: return launch_persist<16>(p, ng, a.greedy != 0, mode == 2, s);
-    case 8: return launch_persist<8>(p, ng, a.greedy != 0, mode == 2, s);
-    case 4: return launch_persist<4>(p, ng, a.greedy != 0, mode == 2, s);
+    case 16: return a.u_bf16 ? launch_persist<16, false>(p, ng, g, c, s) : launch_persist<16, true>(p, ng, g, c, s);
+    case 8: return a.u_bf16 ? launch_persist<8, false>(p, ng, g, c, s) : launch_persist<8, true>(p, ng, g, c, s);
+    case 4: return a.u_bf16 ? launch_persist<4, false>(p, ng, g, c, s) : launch_persist<4, true>(p, ng, g, c, s);
     default: return hipErrorInvalidValue;
     }
 }

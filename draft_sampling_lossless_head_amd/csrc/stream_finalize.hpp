@@ -39,7 +39,8 @@ struct FinStreamArgs {
     int gamma, V;
     float invT;
     int greedy;
-    const uint16_t* U;      // bf16 [B, gamma, V]
+    const void* U;          // [B, gamma, V], bf16 or (u_f32) fp32
+    int u_f32;
     const uint16_t* W1;     // [V, r]
     const uint16_t* W2P;    // packed W2 image
     int r;
@@ -267,7 +268,8 @@ __device__ __forceinline__ bool finalize_row_stream(const FinStreamArgs& A, int 
                 part = fmaf(bf16_bits_to_float(w1[j]),
                             bf16_bits_to_float(A.W2P[w2p_index(vt, j, A.r)]), part);
         }
-        ut = bf16_bits_to_float(A.U[outi * (size_t)V + vt]);
+        ut = A.u_f32 ? static_cast<const float*>(A.U)[outi * (size_t)V + vt]
+                     : bf16_bits_to_float(static_cast<const uint16_t*>(A.U)[outi * (size_t)V + vt]);
     }
     part = row8_sum(part);
     const float lt = ut + part;

@@ -159,7 +159,8 @@ size_t spec_pack_w2_bytes(int r, int V);
 spec_status_t spec_pack_w2(const void *W2, void *W2T, int r, int V, void *stream);
 
 /*
- * Engine of the q-free Markov draft (bf16 U and weights, q_logits == NULL).
+ * Engine of the q-free Markov draft (bf16 weights, q_logits == NULL; U bf16
+ * or fp32).
  *
  * 1 (the default) and 2: where the shape allows it (V % 8 == 0, r in {64,
  * 128, 256}, the device's share of packed W2 fitting in registers: V <= 153600
@@ -182,7 +183,8 @@ spec_status_t spec_pack_w2(const void *W2, void *W2T, int r, int V, void *stream
  *      segmentation fault in the process's exit handlers after every result
  *      was written; its cause is not known (the library registers no exit
  *      work of its own), so this mode is not the default.
- * 0: two launches per position (streaming tile + finalize).
+ * 0: two launches per position (a tile + finalize; the streaming tile when U
+ *    is bf16 and B > 64).
  *
  * All modes give the same draws up to the rounding of the sums (1 and 2 are
  * the same kernel and give identical results).  Process-wide and atomic

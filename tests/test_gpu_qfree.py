@@ -42,6 +42,11 @@ DRAFT_CASES = [
     (100, 3, 40000, 128, "bf16", 1.0),  # three items per workgroup: full pipeline
     (200, 2, 20008, 64, "bf16", 0.9),   # row block changes inside a workgroup; 40-token tail
     (80, 3, 16384, 256, "bf16", 0.0),   # greedy
+    # fp32 U on the persistent engine (4 KB units, 8 lanes per row piece):
+    (32, 7, 32000, 256, "f32", 1.0),    # the 32k-vocabulary configuration's shape
+    (130, 2, 3000, 128, "f32", 0.9),    # two row blocks
+    (70, 3, 20008, 64, "f32", 1.0),     # 40-token tail, r = 64
+    (9, 3, 3000, 256, "f32", 0.0),      # greedy
     # persistent draft (bf16 U, V % 8 == 0, r in {64, 128, 256}, W2 share fits):
     (1, 3, 5000, 64, "bf16", 1.0),      # one row: 31 absent rows in its group
     (33, 2, 8, 64, "bf16", 1.0),        # V = 8: one block, one workgroup
@@ -58,7 +63,7 @@ def persist_eligible(B, gamma, V, r, udt):
     """Shapes the library runs as one persistent launch (256 CUs, 16 of them
     finalizing: at most 20 / 40 / 80 blocks of 32 tokens per unit workgroup
     for r = 256 / 128 / 64)."""
-    if udt != "bf16" or V % 8 or r not in (64, 128, 256) or B < 1 or gamma < 1:
+    if udt not in ("bf16", "f32") or V % 8 or r not in (64, 128, 256) or B < 1 or gamma < 1:
         return False
     nblk = (V + 31) // 32
     ng = min(240, nblk)
