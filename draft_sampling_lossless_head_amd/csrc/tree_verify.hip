@@ -223,16 +223,15 @@ __device__ __forceinline__ bool tv_exchange(TvShared& sh, TvGroup& g, uint32_t v
         int ok = 1;
         for (unsigned polls = 0;; ++polls) {
             bool up = true;
-            uint64_t word = 0;
-            if (j < g.W) {
-                word = coh_load<true>(g.slots + ((size_t)j * 2 + par) * 4 + w);
-                up = (uint32_t)(word >> 32) == tag;
-            }
+            // the abort word is read with the exchange words: one round trip a poll
+            const uint64_t word = j < g.W ? coh_load<true>(g.slots + ((size_t)j * 2 + par) * 4 + w) : 0;
+            const uint64_t ab = coh_load<true>(tv_xchg + kTvAbortWord);
+            if (j < g.W) up = (uint32_t)(word >> 32) == tag;
             if (__all(up)) {
                 if (j < g.W) sh.xv[j][w] = (uint32_t)word;
                 break;
             }
-            if (coh_load<true>(tv_xchg + kTvAbortWord) == (uint64_t)g.epoch || polls > g.limit) {
+            if (ab == (uint64_t)g.epoch || polls > g.limit) {
                 if (tid == 0) coh_store<true>(tv_xchg + kTvAbortWord, (uint64_t)g.epoch);
                 ok = 0;
                 break;
