@@ -184,8 +184,9 @@ __device__ __forceinline__ double block_sum(TvShared& sh, double x) {
 
 // Exchange words of the split walk: [workgroup][parity][4] 64-bit words
 // (tag << 32 | value), and one abort word.  Zero at load; a tag is
-// (epoch << 12) | exchange number with a nonzero epoch per call, so words of
-// earlier calls never match.  Exchange s of a workgroup uses parity s & 1: it
+// (epoch << 12) | exchange number with a nonzero epoch per call, and the area
+// is zeroed again whenever the epoch counter restarts, so words of earlier
+// calls never match.  Exchange s of a workgroup uses parity s & 1: it
 // can only write exchange s + 2 after every workgroup of its request wrote
 // s + 1, which each does after reading all of exchange s.
 __device__ uint64_t tv_xchg[kTreeXchgWgs * 2 * 4 + 1];
@@ -613,12 +614,21 @@ static int tree_split(int B, int V) {
 
 static std::atomic<uint32_t> g_tree_epoch{0};
 
+// Zeroes the exchange area (tag 0 matches no epoch) at the start of each epoch
+// cycle.
+__global__ void verify_tree_xchg_clear() {
+    constexpr int n = (int)(sizeof(tv_xchg) / sizeof(tv_xchg[0]));
+    for (int e = (int)(blockIdx.x * blockDim.x + threadIdx.x); e < n; e += (int)(gridDim.x * blockDim.x))
+        tv_xchg[e] = 0;
+}
+
 hipError_t verify_tree_launch(const TreeVerifyArgs& a, hipStream_t s) {
     if (a.B == 0) return hipSuccess;
     TreeVerifyArgs x = a;
     x.split = tree_split(a.B, a.V);
-    // 20-bit nonzero epoch: exchange words of earlier calls never match
+    // 20-bit nonzero epoch; the area is cleared when the counter restarts
     x.epoch = g_tree_epoch.fetch_add(1, std::memory_order_relaxed) % 0xFFFFFu + 1u;
+    if (x.epoch == 1u) hipLaunchKernelGGL(verify_tree_xchg_clear, dim3(32), dim3(256), 0, s);
     if (x.poll_limit == 0) x.poll_limit = kTreePollLimit;
     const dim3 grid((unsigned)((size_t)a.B * x.split)), block(kTvThreads);
     if (a.p_bf16 && a.q_bf16) hipLaunchKernelGGL((verify_tree_kernel<true, true>), grid, block, 0, s, x);

@@ -61,6 +61,61 @@ def test_alpha_dense_parity(orc, B, gamma, V, pdt, qdt, T):
             assert abs(g["alpha"][b, k] + g["tv"][b, k] - 1.0) <= 2e-6
 
 
+@pytest.mark.parametrize("B,gamma,V,T", [
+    (4, 5, 3000, 1.3),
+    (61, 13, 3000, 1.0),     # 793 positions
+    (3, 2, 64, 0.7),
+    (2, 3, 8, 1.0),          # one 8-token vector per row
+    (5, 7, 184320, 1.0),
+])
+def test_alpha_bf16_pairs_parity(orc, B, gamma, V, T):
+    """bf16 P and Q rows under sampling: every position against the oracle,
+    and against the same values given as fp32 Q rows (a second kernel
+    instantiation)."""
+    sd = require_gpu()
+    note(f"acceptance rate bf16 pairs B={B} gamma={gamma} V={V} T={T}")
+    (Ph, Pd), (Qh, Qd) = _rows(B, gamma, V, 90 + V, "bf16", "bf16")
+    g = host(sd.spec_acceptance_rate(Pd, Qd, T))
+    g2 = host(sd.spec_acceptance_rate(Pd, Qd.float().contiguous(), T))
+    for b in range(B):
+        for k in range(gamma):
+            a, t = _want(orc, Ph[b, k].astype(np.float64), Qh[b, k].astype(np.float64), T)
+            assert abs(g["alpha"][b, k] - a) <= _tol(a), (b, k, g["alpha"][b, k], a)
+            assert abs(g["tv"][b, k] - t) <= _tol(t), (b, k, g["tv"][b, k], t)
+            assert abs(g["alpha"][b, k] - g2["alpha"][b, k]) <= 2 * _tol(a), (b, k)
+
+
+def test_alpha_bf16_packed_ragged(orc):
+    """Packed bf16 P and Q rows with per-request lengths (0, gamma_max and one
+    out of range): positions with no rows are NaN (the last request has none,
+    so its offsets point at the end of both tensors)."""
+    sd = require_gpu()
+    B, G, V, T = 9, 6, 6000, 1.0
+    lens = np.array([3, 0, 6, 1, 9, 5, 2, 6, 0], dtype=np.int32)   # lens[4] > G: invalid
+    (Ph, _), (Qh, _) = _rows(B, G, V, 78, "f32", "f32")
+    prow, qrow, p_off, q_off = [], [], [], []
+    for b in range(B):
+        L = int(lens[b]) if lens[b] <= G else 0
+        p_off.append(len(prow))
+        q_off.append(len(qrow))
+        prow += [Ph[b, k] for k in range(L + 1 if L else 0)]
+        qrow += [Qh[b, k] for k in range(L)]
+    Pb = workloads.f32_to_bf16_bits(np.stack(prow).astype(np.float32))
+    Qb = workloads.f32_to_bf16_bits(np.stack(qrow).astype(np.float32))
+    g = host(sd.spec_acceptance_rate(
+        dev(Pb, "bf16"), dev(Qb, "bf16"), T, gamma_max=G, lens=dev(lens),
+        p_row_off=dev(np.array(p_off, np.int64)), q_row_off=dev(np.array(q_off, np.int64))))
+    P64, Q64 = workloads.as_f64(Pb, "bf16"), workloads.as_f64(Qb, "bf16")
+    for b in range(B):
+        for k in range(G):
+            if lens[b] > G or k >= lens[b]:
+                assert np.isnan(g["alpha"][b, k]) and np.isnan(g["tv"][b, k]), (b, k)
+                continue
+            a, t = _want(orc, P64[p_off[b] + k], Q64[q_off[b] + k], T)
+            assert abs(g["alpha"][b, k] - a) <= _tol(a), (b, k)
+            assert abs(g["tv"][b, k] - t) <= _tol(t), (b, k)
+
+
 def test_alpha_packed_ragged(orc):
     """Packed rows with per-request lengths (0 and gamma_max included, one
     out of range): positions past L_b and the bad request are NaN."""
