@@ -1410,6 +1410,24 @@ void rnn_gates(const float* __restrict__ hpart, const uint16_t* __restrict__ Wg,
     const int ahi = state ? 16 : 0;
     const bool azero = state ? (!bok || k == 0) : !pok;
     const int col0 = state ? 0 : r;
+    const size_t M = (size_t)B * gamma;
+    // wave w finishes accumulator elements 4w .. 4w + 3: requests m0 + 8w +
+    // 4 * kgrp + 0..3 of feature n.  Their hidden parts and old states depend
+    // on nothing in this kernel, so they are loaded first, together with the
+    // operands, instead of one round trip after the contraction.
+    const int nc = nok ? n : 0;
+    float hpv[4][3][kHprojSplit], sold[4];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+        const int m = m0 + 8 * w + 4 * kgrp + ii;
+        const size_t row = (size_t)(m < B ? m : 0) * gamma + k;
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+#pragma unroll
+            for (int sp = 0; sp < kHprojSplit; ++sp)
+                hpv[ii][q][sp] = hpart[((size_t)sp * M + row) * 3 * r + (size_t)q * r + nc];
+        sold[ii] = (k == 0) ? 0.0f : s_in[(size_t)(m < B ? m : 0) * r + nc];
+    }
     constexpr int KB = 8;
     uint4 ra[KB][2];
     bf16x8_t bq[KB][3];
@@ -1464,22 +1482,6 @@ void rnn_gates(const float* __restrict__ hpart, const uint16_t* __restrict__ Wg,
 #pragma unroll
         for (int i = 0; i < 16; ++i) red[w][q][i][lane] = acc[q][i];
     __syncthreads();
-    const size_t M = (size_t)B * gamma;
-    // wave w finishes accumulator elements 4w .. 4w + 3: requests m0 + 8w +
-    // 4 * kgrp + 0..3 of feature n; their loads go out first
-    const int nc = nok ? n : 0;
-    float hpv[4][3][kHprojSplit], sold[4];
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-        const int m = m0 + 8 * w + 4 * kgrp + ii;
-        const size_t row = (size_t)(m < B ? m : 0) * gamma + k;
-#pragma unroll
-        for (int q = 0; q < 3; ++q)
-#pragma unroll
-            for (int sp = 0; sp < kHprojSplit; ++sp)
-                hpv[ii][q][sp] = hpart[((size_t)sp * M + row) * 3 * r + (size_t)q * r + nc];
-        sold[ii] = (k == 0) ? 0.0f : s_in[(size_t)(m < B ? m : 0) * r + nc];
-    }
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
         const int i = 4 * w + ii;
