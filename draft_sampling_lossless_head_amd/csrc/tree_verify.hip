@@ -160,6 +160,7 @@ struct TvShared {
     double red_d[kTvWaves];
     uint32_t xv[kTreeSplitMax][4];   // exchanged values, by workgroup
     int xok;
+    int xlast;   // this workgroup finished the split call last
     float clp[kTvThreads], clq[kTvThreads], cu[kTvThreads];   // children's logits and uniforms
 };
 
@@ -183,14 +184,17 @@ __device__ __forceinline__ double block_sum(TvShared& sh, double x) {
 }
 
 // Exchange words of the split walk: [workgroup][parity][4] 64-bit words
-// (tag << 32 | value), and one abort word.  Zero at load; a tag is
-// (epoch << 12) | exchange number with a nonzero epoch per call, and the area
-// is zeroed again whenever the epoch counter restarts, so words of earlier
-// calls never match.  Exchange s of a workgroup uses parity s & 1: it
-// can only write exchange s + 2 after every workgroup of its request wrote
+// (tag << 32 | value), and one abort word.  Zero at load, and zeroed again by
+// the last workgroup of every split call (tv_release), so each call starts
+// from zeros, whether it is launched directly or replayed from a captured
+// graph.  A tag is (epoch << 12) | exchange number with epoch >= 1, so a
+// cleared word never matches.  Exchange s of a workgroup uses parity s & 1:
+// it can only write exchange s + 2 after every workgroup of its request wrote
 // s + 1, which each does after reading all of exchange s.
 __device__ uint64_t tv_xchg[kTreeXchgWgs * 2 * 4 + 1];
 constexpr int kTvAbortWord = kTreeXchgWgs * 2 * 4;
+// Workgroups of the running split call that are done with the area.
+__device__ unsigned tv_done;
 
 struct TvGroup {
     int W, i;          // workgroups of the request, this one's index
@@ -203,7 +207,7 @@ struct TvGroup {
 // Publishes this workgroup's four values for the next exchange and leaves
 // every workgroup's values in sh.xv[0 .. W); false when a wait gave up (past
 // the poll limit, or another workgroup of the launch gave up: the abort word
-// holds this call's epoch).
+// holds the epoch).
 __device__ __forceinline__ bool tv_exchange(TvShared& sh, TvGroup& g, uint32_t v0, uint32_t v1,
                                               uint32_t v2, uint32_t v3) {
     const int tid = threadIdx.x;
@@ -254,8 +258,7 @@ __device__ __forceinline__ uint32_t f64_lo(double x) { return (uint32_t)__double
 __device__ __forceinline__ uint32_t f64_hi(double x) { return (uint32_t)__double2hiint(x); }
 
 template <bool PB, bool QB>
-__global__ __launch_bounds__(kTvThreads) void verify_tree_kernel(TreeVerifyArgs a) {
-    __shared__ TvShared sh;
+__device__ __forceinline__ void tree_walk(const TreeVerifyArgs& a, TvShared& sh) {
     const int W = a.split;
     const int b = (int)blockIdx.x / W;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -589,6 +592,34 @@ __global__ __launch_bounds__(kTvThreads) void verify_tree_kernel(TreeVerifyArgs 
     }
 }
 
+// End of a split call, in every workgroup: the count of finished workgroups
+// is an acquire-release add, so the last one to finish sees every other
+// workgroup's accesses to the area completed; it zeroes the words the call
+// used, the abort word and the count.
+__device__ __forceinline__ void tv_release(TvShared& sh, const TreeVerifyArgs& a) {
+    __syncthreads();   // every thread of this workgroup is done with the area
+    if (threadIdx.x == 0) {
+        const unsigned d = __hip_atomic_fetch_add(&tv_done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        sh.xlast = d == gridDim.x - 1 ? 1 : 0;
+    }
+    __syncthreads();
+    if (sh.xlast) {
+        const int nw = a.B * a.split * 2 * 4;
+        for (int e = (int)threadIdx.x; e < nw; e += kTvThreads) coh_store<true>(tv_xchg + e, (uint64_t)0);
+        if (threadIdx.x == 0) {
+            coh_store<true>(tv_xchg + kTvAbortWord, (uint64_t)0);
+            coh_store<true>(&tv_done, 0u);
+        }
+    }
+}
+
+template <bool PB, bool QB>
+__global__ __launch_bounds__(kTvThreads) void verify_tree_kernel(TreeVerifyArgs a) {
+    __shared__ TvShared sh;
+    tree_walk<PB, QB>(a, sh);
+    if (a.split > 1) tv_release(sh, a);
+}
+
 }  // namespace
 
 // Workgroups per request: all of them must be resident at once (the split
@@ -612,23 +643,13 @@ static int tree_split(int B, int V) {
     return std::max(w, 1);
 }
 
-static std::atomic<uint32_t> g_tree_epoch{0};
-
-// Zeroes the exchange area (tag 0 matches no epoch) at the start of each epoch
-// cycle.
-__global__ void verify_tree_xchg_clear() {
-    constexpr int n = (int)(sizeof(tv_xchg) / sizeof(tv_xchg[0]));
-    for (int e = (int)(blockIdx.x * blockDim.x + threadIdx.x); e < n; e += (int)(gridDim.x * blockDim.x))
-        tv_xchg[e] = 0;
-}
-
 hipError_t verify_tree_launch(const TreeVerifyArgs& a, hipStream_t s) {
     if (a.B == 0) return hipSuccess;
     TreeVerifyArgs x = a;
     x.split = tree_split(a.B, a.V);
-    // 20-bit nonzero epoch; the area is cleared when the counter restarts
-    x.epoch = g_tree_epoch.fetch_add(1, std::memory_order_relaxed) % 0xFFFFFu + 1u;
-    if (x.epoch == 1u) hipLaunchKernelGGL(verify_tree_xchg_clear, dim3(32), dim3(256), 0, s);
+    // every split call starts from a zeroed area (the last workgroup of the
+    // previous one cleared it), so one fixed nonzero epoch serves all calls
+    x.epoch = 1u;
     if (x.poll_limit == 0) x.poll_limit = kTreePollLimit;
     const dim3 grid((unsigned)((size_t)a.B * x.split)), block(kTvThreads);
     if (a.p_bf16 && a.q_bf16) hipLaunchKernelGGL((verify_tree_kernel<true, true>), grid, block, 0, s, x);

@@ -421,10 +421,11 @@ spec_status_t spec_verify_rnn(
  * batch fills the device): each covers a range of the vocabulary, every
  * tested sibling after the first costs one pass over the node's two rows,
  * and the workgroups of a request exchange each pass's partial sums through
- * the library's static exchange area (device memory, tagged per call).  No
- * workspace.  With W > 1 all of a call's workgroups must be resident at once,
- * which an otherwise idle device gives; calls that overlap on one device
- * (other streams) are not supported then.  Every wait of the walk is bounded
+ * the library's static exchange area (device memory; the last workgroup of
+ * each call zeroes what the call used, so the call can also be captured in a
+ * graph and replayed).  No workspace.  With W > 1 all of a call's
+ * workgroups must be resident at once, which an otherwise idle device gives;
+ * calls that overlap on one device (other streams) are not supported then.  Every wait of the walk is bounded
  * (spec_draft_set_poll_limit): when one gives up, the requests not finished
  * report accepted -1 with all-(-1) out_tokens and path.
  * Errors: SPEC_ERR_INVALID (null required pointers, B or M < 0, V outside

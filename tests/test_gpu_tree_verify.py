@@ -233,3 +233,49 @@ def test_tree_verify_split_gives_up_cleanly(orc):
     tally = _compare_all(orc, wl, tok, 1.0, again, u, "again")
     assert again["accepted"].min() >= 0
     note(f"  again: {tally.as_dict()}")
+
+
+def test_tree_verify_split_graph_replays(orc):
+    """The split walk captured in a HIP graph and replayed three times, with
+    direct calls on other uniforms between the replays: every replay and every
+    direct call gives the direct call's result for its uniforms (each split
+    call leaves the exchange area zeroed for the next, so a replay cannot see
+    words of the one before), and the first agrees with the oracle."""
+    sd = require_gpu()
+    B, M, V = 16, 12, 40000
+    note(f"tree verify split walk under graph replay: B={B} M={M} V={V}")
+    wl = workloads.make_tree_verify(B, M, V, seed=91, dtype="bf16", sigma=0.8, levels=3)
+    tok = _drawn_tokens(orc, wl, 1.0, np.random.default_rng(4))
+    Pd, Qd = dev(wl["P"], "bf16"), dev(wl["Q"], "bf16")
+    pard, tokd = dev(wl["parent"]), dev(tok)
+
+    def call(seed, out=None):
+        return sd.spec_verify_tree(Pd, Qd, pard, tokd, 1.0, seed=seed, offset=5, out=out)
+
+    def host_of(g):
+        torch.cuda.synchronize()
+        return {k: v.cpu().numpy() for k, v in g.items()}
+
+    want_a = host_of(call(21))
+    want_b = host_of(call(22))
+    _compare_all(orc, wl, tok, 1.0, want_a, orc.tree_uniforms(21, 5, B, M), "direct")
+    out = {k: torch.empty((B,) if k == "accepted" else (B, M + (k == "out_tokens")),
+                          dtype=torch.int32, device="cuda") for k in ("accepted", "out_tokens", "path")}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(21, out)   # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(21, out)
+    for rep in range(3):
+        for v in out.values():
+            v.fill_(-7)
+        graph.replay()
+        got = host_of(out)
+        for k in want_a:
+            assert np.array_equal(got[k], want_a[k]), (rep, k)
+        between = host_of(call(22))
+        for k in want_b:
+            assert np.array_equal(between[k], want_b[k]), (rep, k)
