@@ -36,7 +36,12 @@
  *   spec_verify_noalloc.
  * - `stream` is a hipStream_t passed as void* (NULL = default stream).
  *   All work is enqueued asynchronously on it; outputs are valid once the
- *   stream has been synchronised.
+ *   stream has been synchronised.  No entry point reads results back to the
+ *   host or records a memset, and every word a call reads from its workspace
+ *   or the static areas is written or reset by that call, so a sequence of
+ *   calls can be captured in a HIP graph and replayed (the process-wide
+ *   settings are then those at capture time); the GPU tests replay the
+ *   q-free Markov cycle and the split tree walk this way.
  * - Argument validation is synchronous and happens before any launch; a
  *   non-SPEC_OK status means nothing was enqueued.  Checks that need device
  *   data (token ids, lengths) are done by the kernels: an offending request

@@ -245,3 +245,58 @@ def test_side_stream_allocations():
                **{k: x.cpu().numpy() for k, x in v.items()}}
         for k in ("tokens", "q_logZ", "q_tok_prob", "accepted", "out_tokens"):
             np.testing.assert_array_equal(got[k], ref[k], err_msg=k)
+
+
+def test_cycle_graph_replays():
+    """One q-free cycle (persistent draft with the packed W2 image, then
+    spec_verify_markov) captured in a HIP graph and replayed three times, with
+    direct cycles on other uniforms between the replays: every replay gives
+    the direct cycle's tokens, normalisers and verdicts bit for bit (every
+    word a call reads is written or reset inside the call), and the draft
+    status stays 0."""
+    sd = require_gpu()
+    B, G, V, r = 96, 6, 40000, 128
+    note(f"graph-replayed draft + verify B={B} gamma={G} V={V} r={r}")
+    cfg = dict(workloads.CONFIGS["markov-152k-b128"])
+    wl = workloads.make_markov(cfg, B=B, gamma=G, V=V, r=r)
+    U, P = dev(wl["U"], "bf16"), dev(wl["P"], "bf16")
+    W1, W2, x0 = dev(wl["W1"], "bf16"), dev(wl["W2"], "bf16"), dev(wl["x0"])
+    W2T = sd.spec_pack_w2(W2)
+    status = torch.full((1,), -3, dtype=torch.int32, device="cuda")
+
+    def cycle(seed):
+        d = sd.spec_draft_sample_markov(U, x0, W1, None, 1.0, W2T=W2T, q_free=True, seed=seed,
+                                        status=status)
+        v = sd.spec_verify_markov(P, U, x0, W1, W2, d["tokens"], d["q_logZ"], d["q_tok_prob"],
+                                  1.0, seed=seed)
+        return d, v
+
+    def host_of(d, v):
+        torch.cuda.synchronize()
+        return {**{k: x.cpu().numpy() for k, x in d.items()},
+                **{k: x.cpu().numpy() for k, x in v.items()}}
+
+    keys = ("tokens", "q_logZ", "q_tok_prob", "accepted", "out_tokens")
+    ref_a = host_of(*cycle(8))
+    ref_b = host_of(*cycle(9))
+    assert not np.array_equal(ref_a["tokens"], ref_b["tokens"])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        cycle(8)   # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gd, gv = cycle(8)
+    for rep in range(3):
+        for t in (*gd.values(), *gv.values()):
+            t.fill_(-5)
+        status.fill_(-3)
+        graph.replay()
+        got = host_of(gd, gv)
+        assert int(status.cpu()[0]) == 0, rep
+        for k in keys:
+            np.testing.assert_array_equal(got[k], ref_a[k], err_msg=f"replay {rep}: {k}")
+        between = host_of(*cycle(9))
+        for k in keys:
+            np.testing.assert_array_equal(between[k], ref_b[k], err_msg=f"direct {rep}: {k}")
