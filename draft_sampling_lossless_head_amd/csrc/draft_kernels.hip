@@ -213,6 +213,30 @@ void draft_tile_mfma(TileParams P) {
         prev = (bpos == 0) ? P.x0[b] : P.tokens[(size_t)b * gamma + bpos - 1];
         erow_ok = prev >= 0 && prev < V;
     }
+    auto load_e = [&](int split, bf16x8_t (&e)[16]) {
+        const uint16_t* erow =
+            (MODE == kHeadMarkov)
+                ? P.W1 + (size_t)prev * r
+                : P.Erows + (((size_t)(b < B ? b : 0) * gamma + (bpos > 0 ? bpos : 0)) * 3 + split) * r;
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) {
+            if (ks < nks) {
+                if (erow_ok) {
+                    e[ks] = *reinterpret_cast<const bf16x8_t*>(erow + ks * 16 + kgrp * 8);
+                } else {
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) e[ks][t] = (__bf16)0.0f;
+                }
+            }
+        }
+    };
+    // With up to 64 rows per tile the registers hold two sets of B operands:
+    // the first set is loaded here, in flight with the W2 tile and U, and each
+    // later RNN term is loaded while the previous one is multiplied (with
+    // 128 rows each set is loaded just before its MFMAs).
+    constexpr bool EPRE = WB <= 2;
+    bf16x8_t e0[16], e1[16];
+    if constexpr (EPRE) load_e(0, e0);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int c = tid + i * 256;
@@ -230,24 +254,7 @@ void draft_tile_mfma(TileParams P) {
     __syncthreads();
 
     // 4) the contraction (RNN: three bf16 terms of o against the same tile).
-#pragma unroll
-    for (int split = 0; split < NS; ++split) {
-        const uint16_t* erow =
-            (MODE == kHeadMarkov)
-                ? P.W1 + (size_t)prev * r
-                : P.Erows + (((size_t)(b < B ? b : 0) * gamma + (bpos > 0 ? bpos : 0)) * 3 + split) * r;
-        bf16x8_t e[16];
-#pragma unroll
-        for (int ks = 0; ks < 16; ++ks) {
-            if (ks < nks) {
-                if (erow_ok) {
-                    e[ks] = *reinterpret_cast<const bf16x8_t*>(erow + ks * 16 + kgrp * 8);
-                } else {
-#pragma unroll
-                    for (int t = 0; t < 8; ++t) e[ks][t] = (__bf16)0.0f;
-                }
-            }
-        }
+    auto contract = [&](const bf16x8_t (&e)[16]) {
 #pragma unroll
         for (int ks = 0; ks < 16; ++ks) {
             if (ks < nks) {
@@ -259,6 +266,22 @@ void draft_tile_mfma(TileParams P) {
                     acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, e[ks], acc[mb], 0, 0, 0);
                 }
             }
+        }
+    };
+    // term t uses set t % 2; with EPRE, term t + 1 goes into the other set first
+    if constexpr (EPRE) {
+        if constexpr (NS > 1) load_e(1, e1);
+        contract(e0);
+        if constexpr (NS > 1) {
+            if constexpr (NS > 2) load_e(2, e0);
+            contract(e1);
+        }
+        if constexpr (NS > 2) contract(e0);
+    } else {
+#pragma unroll
+        for (int sp = 0; sp < NS; ++sp) {
+            load_e(sp, e0);
+            contract(e0);
         }
     }
 
