@@ -352,11 +352,32 @@ hipError_t prefix_schedule_launch(const SchedArgs& a, hipStream_t s) {
 //      takes its value and is stamped t, so no node reads a value written in
 //      the same round;
 //   2. key (~bits(a) << 32) | (depth << 16) | v: ascending keys are higher
-//      survival first, then shallower, then lower id; bitonic sort in LDS;
+//      survival first, then shallower, then lower id; bitonic sort (one key
+//      per thread, shuffles within a wave, for up to 1024 nodes; in LDS for
+//      larger trees);
 //   3. the first n ids out (-1 past M) and the exact sum of their survival
 //      cut to multiples of 2^-48.
 
 constexpr int kTreeThreads = 1024;
+
+// The tree's score: every thread's part (a_v cut to multiples of 2^-48, as
+// integers) summed exactly over the workgroup.
+__device__ __forceinline__ void tree_score(const TreeArgs& A, size_t t, int64_t sum, int64_t* part) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const int lo = __shfl_xor((int)(uint32_t)(uint64_t)sum, off);
+        const int hi = __shfl_xor((int)(uint32_t)((uint64_t)sum >> 32), off);
+        sum += (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+    }
+    if (lane == 0) part[wave] = sum;
+    __syncthreads();
+    if (threadIdx.x == 0 && A.score) {
+        int64_t tot = 0;
+        for (int w = 0; w < kTreeThreads / kWave; ++w) tot += part[w];
+        A.score[t] = (double)tot / kTwo48;
+    }
+}
 
 __global__ __launch_bounds__(kTreeThreads)
 void tree_select_kernel(TreeArgs A) {
@@ -412,16 +433,58 @@ void tree_select_kernel(TreeArgs A) {
     }
 
     // 2. keys and the sort (parents and confidences are no longer needed)
+    auto key_of = [&](int v) -> uint64_t {
+        if (v >= M) return ~0ull;   // past the tree: after every node
+        const uint32_t bits = av[v] > 0.0f ? __float_as_uint(av[v]) : 0u;   // -0 keys as +0
+        return ((uint64_t)(~bits) << 32) | ((uint32_t)depth[v] << 16) | (uint32_t)v;
+    };
+    if (M <= kTreeThreads) {
+        // One key per thread, a bitonic sort of kTreeThreads keys: a compare
+        // step whose partner is in the same wave (distance j < 64) is a
+        // shuffle; only the steps with j >= 64 go through LDS, into one of two
+        // buffers in turn, so one barrier per such step keeps the reads of a
+        // buffer ahead of its next write.
+        uint64_t key = key_of(tid);
+        uint64_t* xb = keys;   // [2][kTreeThreads], over the parents and confidences
+        int nb = 0;
+        for (int k = 2; k <= kTreeThreads; k <<= 1) {
+            for (int j = k >> 1; j > 0; j >>= 1) {
+                uint64_t other;
+                if (j >= kWave) {
+                    uint64_t* buf = xb + nb * kTreeThreads;
+                    nb ^= 1;
+                    buf[tid] = key;
+                    __syncthreads();
+                    other = buf[tid ^ j];
+                } else {
+                    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)key, j);
+                    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(key >> 32), j);
+                    other = ((uint64_t)hi << 32) | lo;
+                }
+                // ascending runs where bit k of the index is clear; the lower
+                // index of a pair keeps the smaller key there, the larger one
+                // in the descending runs
+                const bool up = (tid & k) == 0, lower = (tid & j) == 0;
+                const uint64_t mn = key < other ? key : other, mx = key < other ? other : key;
+                key = (lower == up) ? mn : mx;
+            }
+        }
+        // 3. the first n nodes (thread i holds the i-th key) and their summed survival
+        int64_t sum = 0;
+        for (int i = tid; i < n; i += kTreeThreads) {
+            int v = -1;
+            if (i < M) {
+                v = (int)(key & 0xFFFFu);
+                sum += (int64_t)((double)av[v] * kTwo48);
+            }
+            A.sel[t * n + i] = v;
+        }
+        tree_score(A, t, sum, part);
+        return;
+    }
     int P = 1;
     while (P < M) P <<= 1;
-    for (int v = tid; v < P; v += kTreeThreads) {
-        uint64_t key = ~0ull;
-        if (v < M) {
-            const uint32_t bits = av[v] > 0.0f ? __float_as_uint(av[v]) : 0u;   // -0 keys as +0
-            key = ((uint64_t)(~bits) << 32) | ((uint32_t)depth[v] << 16) | (uint32_t)v;
-        }
-        keys[v] = key;
-    }
+    for (int v = tid; v < P; v += kTreeThreads) keys[v] = key_of(v);
     __syncthreads();
     for (int k = 2; k <= P; k <<= 1) {
         for (int j = k >> 1; j > 0; j >>= 1) {
@@ -448,19 +511,7 @@ void tree_select_kernel(TreeArgs A) {
         }
         A.sel[t * n + i] = v;
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const int lo = __shfl_xor((int)(uint32_t)(uint64_t)sum, off);
-        const int hi = __shfl_xor((int)(uint32_t)((uint64_t)sum >> 32), off);
-        sum += (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
-    }
-    if (lane == 0) part[wave] = sum;
-    __syncthreads();
-    if (tid == 0 && A.score) {
-        int64_t tot = 0;
-        for (int w = 0; w < kTreeThreads / kWave; ++w) tot += part[w];
-        A.score[t] = (double)tot / kTwo48;
-    }
+    tree_score(A, t, sum, part);
 }
 
 hipError_t tree_select_launch(const TreeArgs& a, hipStream_t s) {
