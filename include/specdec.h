@@ -32,7 +32,8 @@
  *   plus per-device caches of device attributes (CU count, cooperative
  *   launch support) and each kernel's LDS limit, set once per process, and
  *   two areas of static device memory per device: the exchange words of the
- *   split tree walk (spec_verify_tree, 64 KB) and the scratch of
+ *   split tree walk (spec_verify_tree, 64 KB, with its count of finished
+ *   workgroups; each call leaves both zeroed) and the scratch of
  *   spec_verify_noalloc.
  * - `stream` is a hipStream_t passed as void* (NULL = default stream).
  *   All work is enqueued asynchronously on it; outputs are valid once the
